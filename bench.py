@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA forward hot path on one MI355X.
+
+One step = one chunkwise prefill (``kda_chunk_fwd``) of the long-context
+workload (B=1, H=32, T=131072, d_k=d_v=128, C=64, bf16 storage) with every
+input already resident in HBM.  The same run also times the batched decode
+step (``kda_decode_step``: 128 sessions x 32 heads, 268 MB fp32 state updated
+in place) and the fp64 CPU oracle on a bounded sample of the prefill workload.
+
+Prints ONE JSON line.  ``value`` is prefill tokens/s; the ``decode`` object
+carries the decode state bandwidth.  Roofline fractions use the algorithmic
+bytes of the operator (inputs read once, outputs written once) over measured
+time, against MI355X's 8 TB/s HBM.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill tokens/s + decode state GB/s (KDA, H=32, d=128) and % of roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def prefill_alg_bytes(T_total, H, dk, dv, n_seqs, has_s0=True):
+    """q, k, v (bf16), g (fp32), beta (fp32) read once, o (bf16) written once,
+    plus the fp32 initial state read and final state written once."""
+    per_th = 2 * dk + 2 * dk + 2 * dv + 4 * dk + 4 + 2 * dv
+    state = n_seqs * H * dk * dv * 4
+    return T_total * H * per_th + state * (2 if has_s0 else 1)
+
+
+def prefill_alg_flops(T_total, H, C, d):
+    """Dense chunk contractions per token-head: A, H, W, U, H Z (C^2 d terms)
+    and W S, Qbar S, Ktil^T Z (C d^2 terms): 2 (5 C d + 3 d^2)."""
+    return T_total * H * 2 * (5 * C * d + 3 * d * d)
+
+
+def decode_alg_bytes(N, H, dk, dv):
+    """Per (session, head): state read + write (fp32), q, k, v, o (bf16), g
+    (fp32), beta (fp32)."""
+    return N * H * (2 * dk * dv * 4 + 2 * dk + 2 * dk + 2 * dv + 4 * dk + 4 + 2 * dv)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=32768)
+    ap.add_argument("--skip-decode", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build runs the whole KDA path on a single "
+              "MI355X (no sharding or collectives); --gpus %d is not supported" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_80_amd as K
+    import kda_workloads as W
+
+    K.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    w5 = W.WORKLOADS[5]
+    print("[bench] generating %s" % w5.description, file=sys.stderr, flush=True)
+    inp = W.make_workload(5)
+    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    B, T, H, dk = d["q"].shape
+    dv = d["v"].shape[-1]
+    N = inp["n_seqs"]
+    ws = torch.empty(K.workspace_bytes(B, T, H, dk, dv, w5.chunk, N), dtype=torch.uint8,
+                     device=dev)
+    o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+    fs = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+
+    def step():
+        K.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], scale=d["scale"],
+                    initial_state=d["initial_state"], chunk_size=w5.chunk, workspace=ws, out=o,
+                    final_state=fs)
+
+    print("[bench] prefill warmup %d, timed %d" % (args.warmup, args.steps), file=sys.stderr,
+          flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_per_step = wall * 1e3 / args.steps
+    avg_launch_ms = sum(launch_ms) / len(launch_ms)
+    T_total = B * T
+    tokens_per_s = T_total / (ms_per_step * 1e-3)
+    alg_bytes = prefill_alg_bytes(T_total, H, dk, dv, N)
+    alg_flops = prefill_alg_flops(T_total, H, w5.chunk, dk)
+    achieved = alg_bytes / (avg_launch_ms * 1e-3) / 1e9
+    ok = bool(torch.isfinite(o.float()).all().item()) and bool(torch.isfinite(fs).all().item())
+
+    result = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "precision": "bf16 storage; fp16 MFMA operands with fp32 accumulation; fp32 state",
+        "data": "synthetic",
+        "config": {"workload": "long-context prefill B=1 H=32 T=131072 d_k=d_v=128 C=64 bf16, "
+                               "z~U(4,12), S0~N(0,0.01^2)",
+                   "global_batch": B, "seq_len": T, "heads": H, "d_k": dk, "d_v": dv,
+                   "chunk": w5.chunk, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "kda_chunk_fwd (intra + inter launches)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "alg_bytes_per_launch": alg_bytes,
+                     "avg_launch_ms": round(avg_launch_ms, 4),
+                     "mfma_frac_alg": round(alg_flops / (avg_launch_ms * 1e-3) / 1e12
+                                            / BF16_MFMA_PEAK_TFLOPS, 4)},
+        "outputs_finite": ok,
+    }
+
+    if not args.skip_decode:
+        w3 = W.WORKLOADS[3]
+        print("[bench] decode: %s" % w3.description, file=sys.stderr, flush=True)
+        state = W.make_decode_state(w3).to(dev)
+        n_tok = 8
+        toks = [{k: (v.to(dev) if isinstance(v, torch.Tensor) else v)
+                 for k, v in W.make_decode_step(s, w3).items()} for s in range(n_tok)]
+        od = torch.empty((w3.n_sessions, w3.H, w3.dv), dtype=torch.bfloat16, device=dev)
+
+        def dstep(i):
+            t = toks[i % n_tok]
+            K.decode_step(t["q"], t["k"], t["v"], t["g"], t["beta"], state, scale=w3.scale,
+                          out=od)
+
+        for i in range(8):
+            dstep(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.decode_steps):
+            dstep(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dms = e0.elapsed_time(e1) / args.decode_steps
+        dbytes = decode_alg_bytes(w3.n_sessions, w3.H, w3.dk, w3.dv)
+        dgbs = dbytes / (dms * 1e-3) / 1e9
+        result["decode"] = {
+            "value": round(dgbs, 1), "unit": "GB/s", "ms_per_step": round(dms, 5),
+            "steps": args.decode_steps,
+            "config": {"workload": "batched decode 128 sessions x 32 heads d=128, fp32 state "
+                                   "268 MB in place, bf16 tokens"},
+            "roofline": {"bound": "hbm", "kernel": "kda_decode_kernel<128,128,bf16>",
+                         "achieved": round(dgbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(dgbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "alg_bytes_per_launch": dbytes},
+        }
+        del state, toks
+
+    if not args.no_cpu_baseline:
+        import numpy as np
+        import oracle
+        S = min(args.cpu_sample_tokens, T)
+        print("[bench] cpu oracle on the first %d tokens x %d heads" % (S, H), file=sys.stderr,
+              flush=True)
+        a = {n: W.to64(inp[n][:, :S]).reshape(S, H, -1) for n in ("q", "k", "v", "g")}
+        bta = W.to64(inp["beta"][:, :S]).reshape(S, H)
+        s0 = W.to64(inp["initial_state"])
+        threads = len(os.sched_getaffinity(0))
+        oracle.load_c_oracle()
+        t0 = time.perf_counter()
+        oracle.prefill(a["q"], a["k"], a["v"], a["g"], bta, inp["scale"], s0, [0, S],
+                       col_block=32, n_threads=threads)
+        cpu_s = time.perf_counter() - t0
+        result["cpu_baseline"] = {
+            "value": round(S / cpu_s, 1), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "first %d tokens of the long-context prefill workload, all %d heads, "
+                      "fp64 token recurrence, %.1f s" % (S, H, cpu_s),
+            "cpu": cpu_model()}
+        del np
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,194 @@
+"""Kimi Delta Attention (KDA) forward pass on MI355X (gfx950).
+
+A thin binding over the C ABI of ``libkda.so`` (declared in ``include/kda.h``).
+Every step of the computation runs in the library's HIP kernels; this module
+only checks shapes, allocates outputs and workspace with torch, and passes
+device pointers and the current HIP stream.  There is no fallback: if the
+library is missing or cannot be loaded, every call raises.
+
+  chunk_fwd(q, k, v, g, beta, ...)      chunkwise prefill  -> (o, final_state)
+  decode_step(q, k, v, g, beta, state)  one recurrent step -> o (state in place)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["chunk_fwd", "decode_step", "workspace_bytes", "lib", "KdaError", "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
+
+KDA_F32, KDA_BF16 = 0, 1
+STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
+          3: "KDA_ERR_WORKSPACE_TOO_SMALL", 4: "KDA_ERR_HIP"}
+
+
+class KdaError(RuntimeError):
+    """A non-OK status from the C ABI."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__("%s: %s" % (STATUS.get(status, status), message))
+        self.status = status
+
+
+class KdaShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32),
+                ("num_heads", ctypes.c_int32), ("d_k", ctypes.c_int32),
+                ("d_v", ctypes.c_int32), ("chunk_size", ctypes.c_int32),
+                ("num_seqs", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded ``libkda.so`` (ctypes), with argument types declared."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libkda.so is not built (%s); run __graft_entry__.build() or "
+                          "python gated_delta_rule_80_amd/build.py" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    vp, fp, ip = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+    L.kda_abi_version.restype = ctypes.c_int
+    L.kda_abi_version.argtypes = []
+    L.kda_status_string.restype = ctypes.c_char_p
+    L.kda_status_string.argtypes = [ctypes.c_int]
+    L.kda_last_error.restype = ctypes.c_char_p
+    L.kda_last_error.argtypes = []
+    L.kda_chunk_fwd_workspace_bytes.restype = ctypes.c_size_t
+    L.kda_chunk_fwd_workspace_bytes.argtypes = [ctypes.POINTER(KdaShape)]
+    L.kda_chunk_fwd.restype = ctypes.c_int
+    L.kda_chunk_fwd.argtypes = [ctypes.POINTER(KdaShape), vp, vp, vp, fp, fp, ctypes.c_float,
+                                fp, ip, vp, fp, vp, ctypes.c_size_t, vp]
+    L.kda_decode_step.restype = ctypes.c_int
+    L.kda_decode_step.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                  ctypes.c_int32, ctypes.c_int, vp, vp, vp, fp, fp,
+                                  ctypes.c_float, fp, vp, vp]
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != 0:
+        raise KdaError(status, lib().kda_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError("q, k, v must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def make_shape(batch, seqlen, heads, d_k, d_v, chunk_size, num_seqs, dtype_code) -> KdaShape:
+    return KdaShape(batch, seqlen, heads, d_k, d_v, chunk_size, num_seqs, dtype_code)
+
+
+def workspace_bytes(batch, seqlen, heads, d_k, d_v, chunk_size, num_seqs,
+                    dtype=torch.bfloat16) -> int:
+    """Workspace kda_chunk_fwd needs for this problem (0 if unsupported)."""
+    code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
+    sh = make_shape(batch, seqlen, heads, d_k, d_v, chunk_size, num_seqs, code)
+    return int(lib().kda_chunk_fwd_workspace_bytes(ctypes.byref(sh)))
+
+
+def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+              beta: torch.Tensor, scale: Optional[float] = None,
+              initial_state: Optional[torch.Tensor] = None,
+              cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = 64,
+              output_final_state: bool = True, workspace: Optional[torch.Tensor] = None,
+              out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None
+              ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunkwise KDA prefill.
+
+    q, k: [B, T, H, d_k]; v: [B, T, H, d_v] (bf16 or fp32, same dtype);
+    g: [B, T, H, d_k] fp32 per-token log-decay; beta: [B, T, H] fp32;
+    initial_state: [N, H, d_k, d_v] fp32 or None; cu_seqlens: [N+1] int32 on
+    the device (then B == 1) or None.  Returns (o [B, T, H, d_v], final_state
+    [N, H, d_k, d_v] fp32 or None).
+    """
+    _need(q.dim() == 4 and k.shape == q.shape and v.dim() == 4 and v.shape[:3] == q.shape[:3],
+          "q, k must be [B, T, H, d_k] and v [B, T, H, d_v]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    _need(g.shape == q.shape and g.dtype == torch.float32, "g must be fp32 [B, T, H, d_k]")
+    _need(beta.shape == (B, T, H) and beta.dtype == torch.float32, "beta must be fp32 [B, T, H]")
+    _need(q.dtype == k.dtype == v.dtype, "q, k, v must share one dtype")
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
+        _need(t.is_cuda and t.is_contiguous(), "%s must be a contiguous device tensor" % name)
+    code = _dtype_code(q)
+    if cu_seqlens is not None:
+        _need(cu_seqlens.dtype == torch.int32 and cu_seqlens.is_cuda and cu_seqlens.dim() == 1,
+              "cu_seqlens must be an int32 device tensor [N+1]")
+        _need(B == 1, "cu_seqlens needs batch 1")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if initial_state is not None:
+        _need(initial_state.shape == (N, H, dk, dv) and initial_state.dtype == torch.float32
+              and initial_state.is_cuda and initial_state.is_contiguous(),
+              "initial_state must be a contiguous fp32 device tensor [N, H, d_k, d_v]")
+    scale = 1.0 / math.sqrt(dk) if scale is None else float(scale)
+    sh = make_shape(B, T, H, dk, dv, chunk_size, N, code)
+    need = int(lib().kda_chunk_fwd_workspace_bytes(ctypes.byref(sh)))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    o = out if out is not None else torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+    fs = None
+    if output_final_state:
+        fs = final_state if final_state is not None else torch.empty(
+            (N, H, dk, dv), dtype=torch.float32, device=q.device)
+    st = lib().kda_chunk_fwd(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                             ctypes.c_float(scale), _ptr(initial_state), _ptr(cu_seqlens),
+                             _ptr(o), _ptr(fs), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+                             _stream())
+    _check(st)
+    return o, fs
+
+
+def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                beta: torch.Tensor, state: torch.Tensor, scale: Optional[float] = None,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One recurrent KDA step; ``state`` [N, H, d_k, d_v] fp32 is updated in place.
+
+    q, k: [N, H, d_k]; v: [N, H, d_v] (bf16 or fp32); g: [N, H, d_k] fp32;
+    beta: [N, H] fp32.  Returns o [N, H, d_v] in the dtype of v.
+    """
+    _need(q.dim() == 3 and k.shape == q.shape and v.dim() == 3 and v.shape[:2] == q.shape[:2],
+          "q, k must be [N, H, d_k] and v [N, H, d_v]")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    _need(g.shape == q.shape and g.dtype == torch.float32, "g must be fp32 [N, H, d_k]")
+    _need(beta.shape == (N, H) and beta.dtype == torch.float32, "beta must be fp32 [N, H]")
+    _need(state.shape == (N, H, dk, dv) and state.dtype == torch.float32,
+          "state must be fp32 [N, H, d_k, d_v]")
+    _need(q.dtype == k.dtype == v.dtype, "q, k, v must share one dtype")
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("state", state)):
+        _need(t.is_cuda and t.is_contiguous(), "%s must be a contiguous device tensor" % name)
+    code = _dtype_code(q)
+    scale = 1.0 / math.sqrt(dk) if scale is None else float(scale)
+    o = out if out is not None else torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
+    st = lib().kda_decode_step(N, H, dk, dv, code, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                               ctypes.c_float(scale), _ptr(state), _ptr(o), _stream())
+    _check(st)
+    return o

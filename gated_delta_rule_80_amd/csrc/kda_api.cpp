@@ -1,0 +1,199 @@
+// kda_api.cpp -- the C ABI of libkda: validation, workspace sizing, dispatch.
+//
+// Every argument is checked on the host before anything is enqueued; an
+// invalid call returns a status and leaves every buffer untouched.  Messages
+// for the last failure are kept per thread.
+#include "../../include/kda.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "kda_internal.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+kda_status fail(kda_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+kda_status hip_fail(hipError_t e, const char *what) {
+    return fail(KDA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Checks the fields every prefill call needs; on success fills the token count.
+kda_status check_shape(const kda_shape *s, int64_t *total_tokens) {
+    if (!s) return fail(KDA_ERR_INVALID_ARGUMENT, "shape is NULL");
+    if (s->dtype != KDA_F32 && s->dtype != KDA_BF16)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)s->dtype);
+    if (s->batch <= 0 || s->seqlen < 0 || s->num_heads <= 0 || s->d_k <= 0 || s->d_v <= 0 ||
+        s->chunk_size <= 0 || s->num_seqs <= 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT,
+                    "non-positive size (batch %d seqlen %d heads %d d_k %d d_v %d chunk %d "
+                    "num_seqs %d)",
+                    s->batch, s->seqlen, s->num_heads, s->d_k, s->d_v, s->chunk_size,
+                    s->num_seqs);
+    const bool bf16 = s->dtype == KDA_BF16;
+    if (!kda::mfma_path_supported(s->d_k, s->d_v, s->chunk_size, bf16) &&
+        !kda::f32_path_supported(s->d_k, s->d_v, s->chunk_size, bf16))
+        return fail(KDA_ERR_UNSUPPORTED,
+                    "no kernel for d_k %d d_v %d chunk %d dtype %s (built: 128/128/64 bf16; "
+                    "d in {16,32,64} with chunk in {16,32,64} fp32)",
+                    s->d_k, s->d_v, s->chunk_size, bf16 ? "bf16" : "f32");
+    *total_tokens = (int64_t)s->batch * s->seqlen;
+    if (*total_tokens > INT32_MAX / 2)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "too many tokens (%lld)",
+                    (long long)*total_tokens);
+    if ((int64_t)s->num_seqs * s->num_heads > INT32_MAX / 4)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "too many sequences x heads");
+    return KDA_OK;
+}
+
+// The workspace is sized for the packed-sequence chunk bound T/C + N, which
+// is never below the equal-rows count B * ceil(T/C); one size fits both.
+size_t workspace_for(const kda_shape *s, int64_t total) {
+    const bool bf16 = s->dtype == KDA_BF16;
+    if (kda::mfma_path_supported(s->d_k, s->d_v, s->chunk_size, bf16))
+        return kda::mfma_workspace_bytes(total, s->num_seqs, s->num_heads, s->chunk_size);
+    return kda::f32_workspace_bytes(total, s->num_seqs, s->num_heads, s->chunk_size);
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char *kda_status_string(kda_status status) {
+    switch (status) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_INVALID_ARGUMENT: return "KDA_ERR_INVALID_ARGUMENT";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+    case KDA_ERR_WORKSPACE_TOO_SMALL: return "KDA_ERR_WORKSPACE_TOO_SMALL";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP";
+    }
+    return "KDA_ERR_UNKNOWN";
+}
+
+const char *kda_last_error(void) { return g_last_error; }
+
+size_t kda_chunk_fwd_workspace_bytes(const kda_shape *shape) {
+    int64_t total = 0;
+    char saved[sizeof(g_last_error)];
+    memcpy(saved, g_last_error, sizeof(saved));
+    const kda_status st = check_shape(shape, &total);
+    memcpy(g_last_error, saved, sizeof(saved));
+    if (st != KDA_OK) return 0;
+    return workspace_for(shape, total);
+}
+
+kda_status kda_chunk_fwd(const kda_shape *shape, const void *q, const void *k, const void *v,
+                         const float *g_log_decay, const float *beta, float scale,
+                         const float *initial_state, const int32_t *cu_seqlens, void *o,
+                         float *final_state, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+    g_last_error[0] = '\0';
+    const bool varlen = cu_seqlens != nullptr;
+    int64_t total = 0;
+    kda_status st = check_shape(shape, &total);
+    if (st != KDA_OK) return st;
+    if (varlen && shape->batch != 1)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens needs batch == 1 (got %d)",
+                    shape->batch);
+    if (!varlen && shape->num_seqs != shape->batch)
+        return fail(KDA_ERR_INVALID_ARGUMENT,
+                    "without cu_seqlens num_seqs must equal batch (%d vs %d)", shape->num_seqs,
+                    shape->batch);
+    if (total > 0 && (!q || !k || !v || !g_log_decay || !beta || !o))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "a required tensor pointer is NULL");
+    const void *ptrs[] = {q, k, v, g_log_decay, o, initial_state, final_state};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "tensor pointer %p is not 16-byte aligned", p);
+    if ((beta && !aligned4(beta)) || (cu_seqlens && !aligned4(cu_seqlens)))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "beta / cu_seqlens must be 4-byte aligned");
+    if (o && (o == q || o == k || o == v || o == (const void *)g_log_decay ||
+              o == (const void *)beta))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "o must not alias an input");
+    const size_t need = workspace_for(shape, total);
+    if (need > 0 && !workspace)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "workspace is NULL (%zu bytes needed)", need);
+    if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+    if (workspace_bytes < need)
+        return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed",
+                    workspace_bytes, need);
+
+    kda::ChunkProblem p;
+    p.n_seqs = shape->num_seqs;
+    p.batch = shape->batch;
+    p.seqlen = shape->seqlen;
+    p.heads = shape->num_heads;
+    p.dk = shape->d_k;
+    p.dv = shape->d_v;
+    p.chunk = shape->chunk_size;
+    p.bf16 = shape->dtype == KDA_BF16;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.g = g_log_decay;
+    p.beta = beta;
+    p.scale = scale;
+    p.s0 = initial_state;
+    p.cu = cu_seqlens;
+    p.o = o;
+    p.s_final = final_state;
+    p.workspace = workspace;
+    p.workspace_bytes = workspace_bytes;
+    p.stream = static_cast<hipStream_t>(stream);
+
+    hipError_t e = kda::mfma_path_supported(p.dk, p.dv, p.chunk, p.bf16)
+                       ? kda::launch_chunk_fwd_mfma(p)
+                       : kda::launch_chunk_fwd_f32(p);
+    if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd launch");
+    return KDA_OK;
+}
+
+kda_status kda_decode_step(int32_t num_sessions, int32_t num_heads, int32_t d_k, int32_t d_v,
+                           kda_dtype dtype, const void *q, const void *k, const void *v,
+                           const float *g, const float *beta, float scale, float *state_inout,
+                           void *o, void *stream) {
+    g_last_error[0] = '\0';
+    if (dtype != KDA_F32 && dtype != KDA_BF16)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)dtype);
+    if (num_sessions <= 0 || num_heads <= 0 || d_k <= 0 || d_v <= 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "non-positive size (sessions %d heads %d d_k %d "
+                    "d_v %d)", num_sessions, num_heads, d_k, d_v);
+    if (!kda::decode_supported(d_k, d_v))
+        return fail(KDA_ERR_UNSUPPORTED, "no decode kernel for d_k %d d_v %d (built: d_k == "
+                    "d_v in {16, 32, 64, 128})", d_k, d_v);
+    const int64_t pairs = (int64_t)num_sessions * num_heads;
+    if (pairs > INT32_MAX) return fail(KDA_ERR_INVALID_ARGUMENT, "too many pairs");
+    if (!q || !k || !v || !g || !beta || !state_inout || !o)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "a required tensor pointer is NULL");
+    const void *ptrs[] = {q, k, v, g, state_inout, o};
+    for (const void *p : ptrs)
+        if (!aligned16(p))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "tensor pointer %p is not 16-byte aligned", p);
+    if (!aligned4(beta))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "beta must be 4-byte aligned");
+    if (o == (void *)state_inout)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "o must not alias state_inout");
+    hipError_t e = kda::launch_decode((int)pairs, d_k, d_v, dtype == KDA_BF16, q, k, v, g, beta,
+                                      scale, state_inout, o, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "kda_decode_step launch");
+    return KDA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,707 @@
+// kda_chunk_mfma.hip -- chunkwise KDA prefill on gfx950 MFMA, d_k = d_v = 128,
+// C = 64, bf16 storage, fp16 MFMA operands with fp32 accumulation.
+//
+// The chunk algebra is that of "Understanding Kimi Delta Attention"
+// (A. Flores), sections "The triangular system" and "Putting the chunks
+// together", written with the opposite sign for the coupling matrix
+// (A here = -A there, so the solve is (I + A) T = I):
+//   G_i    = sum_{r <= i} g_r                     (inclusive, per channel)
+//   A_ij   = beta_i k_i^T Diag(e^{G_i - G_j}) k_j  (j < i)
+//   T      = (I + A)^{-1}
+//   W      = T Diag(beta) (K . e^{G})    U = T Diag(beta) V
+//   H_ij   = s q_i^T Diag(e^{G_i - G_j}) k_j     (j <= i)
+//   Qbar   = s Q . e^{G}                          Ktil = K . e^{G_C - G}
+// and, carried across chunks with the state S (d_k x d_v, fp32):
+//   Z = U - W S,   O = Qbar S + H Z,   S <- Diag(e^{G_C}) S + Ktil^T Z.
+// The decay is folded into the vectors ("Kimi Delta Attention: a half-life
+// per channel", section "What changes in the kernel"), but against a
+// reference row m inside the chunk (K e^{G - G_m} and K e^{G_m - G}) so no
+// factor ever divides by the decay of the whole chunk; exponents are
+// differences of cumulative logs as the derivation recommends.
+//
+// Kernels
+//   kda_chunk_index  packed sequences -> chunk table (device side, no sync)
+//   kda_intra        one workgroup per (chunk, head), fully parallel: the
+//                    cumulative decay, A and H on MFMA, (I + A)^{-1} (diagonal
+//                    16x16 blocks by forward substitution, off-diagonal blocks
+//                    by fp32 MFMA), then W and U on MFMA.  Its outputs go to
+//                    the workspace already in the register-fragment order the
+//                    inter kernel consumes.
+//   kda_inter        one workgroup per (sequence, head, 32-column value
+//                    tile): the sequential chunk loop with the fp32 state
+//                    resident in registers.  Columns of the value space evolve
+//                    independently, so value tiles need no communication.
+//
+// MFMA fragments (v_mfma_f32_16x16x32_f16): lane l gives row/column l % 16
+// and 8 reduction values for group l / 16; it receives output column l % 16,
+// rows 4 (l / 16) .. +3.  The reduction index inside a fragment may be any
+// permutation as long as both operands use the same one.  All fragments here
+// that contract over 32 channels or 32 tokens use the permutation
+//   slot s < 4  -> index 4 (l/16) + s,   slot s >= 4 -> index 16 + 4 (l/16) + s - 4
+// which is exactly what two vertically adjacent 16x16 accumulator tiles hold,
+// so an MFMA result feeds the next MFMA without leaving registers.
+#include "kda_common.hpp"
+#include "kda_internal.hpp"
+
+namespace kda {
+namespace mfma_path {
+
+constexpr int C = 64, DK = 128, DV = 128;
+constexpr int DVT = 32;               // value columns per inter workgroup
+constexpr int NCT = DVT / 16;         // 16-column tiles per inter wave
+constexpr int NTILES = DV / DVT;      // inter workgroups per (sequence, head)
+
+// One chunk-head record in the workspace (bytes).  Fragment index -> 1 KB
+// (64 lanes x 16 B) unless noted.
+constexpr int REC_W = 0;        // W   A-frags [token tile 4][channel block 4]
+constexpr int REC_Q = 16384;    // Qbar A-frags [token tile 4][channel block 4]
+constexpr int REC_K = 32768;    // Ktil^T A-frags [channel tile 8][token block 2]
+constexpr int REC_U = 49152;    // U accumulator tiles [token tile 4][value tile 8], 512 B each
+constexpr int REC_H = 65536;    // H A-frags, 6 nonzero (token tile, token block) pairs
+constexpr int REC_GE = 71680;   // e^{G_C} fp32 [128]
+constexpr int REC_BYTES = 72192;
+static_assert(REC_BYTES % 256 == 0, "record alignment");
+
+// H fragment slot of (token tile it, token block kb), kb <= it / 2.
+__device__ __forceinline__ int h_slot(int it, int kb) { return it < 2 ? it : 2 * it - 2 + kb; }
+
+struct Chunk {
+    int seq, t0, len;
+};
+
+// Chunk c of the problem: equal rows (table == nullptr) or the device table.
+__device__ __forceinline__ Chunk chunk_at(int c, const int4 *table, int row_len, int ncr) {
+    if (!table) {
+        const int b = c / ncr, j = c - b * ncr;
+        return {b, b * row_len + j * C, min(C, row_len - j * C)};
+    }
+    const int4 e = table[c];
+    return {e.x, e.y, e.z};
+}
+
+__device__ __forceinline__ float bf(uint16_t x) { return bf16_to_f32(x); }
+
+// Inclusive prefix sum across the 16 lanes of each DPP row.
+__device__ __forceinline__ float row_scan16(float x) {
+#define KDA_SHR(N)                                                                              \
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + (N), 0xf, 0xf, \
+                                                    true));
+    KDA_SHR(1) KDA_SHR(2) KDA_SHR(4) KDA_SHR(8)
+#undef KDA_SHR
+    return x;
+}
+
+// ------------------------------------------------------------------------------------
+// Chunk table for packed sequences.  One workgroup; writes off[0..N] (chunk
+// offsets, off[N] = number of chunks) and table[c] = {seq, first token, len}.
+// Boundaries are sanitised first -- b'_0 = 0, b'_n = max(b'_{n-1}, clamp(cu[n],
+// 0, T)) -- so that even a malformed cu_seqlens yields disjoint in-range
+// sequences and at most T / C + N chunks: every later access stays in bounds.
+// For a valid cu_seqlens (starting at 0, non-decreasing, ending at T) b' = cu.
+// ------------------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void kda_chunk_index_kernel(const int32_t *__restrict__ cu,
+                                                               int n_seqs, int total_tokens,
+                                                               int32_t *__restrict__ off,
+                                                               int4 *__restrict__ table) {
+    __shared__ int s_max[1024], s_cnt[1024];
+    const int t = threadIdx.x;
+    const int per = (n_seqs + 1023) / 1024;
+    const int s0 = min(n_seqs, t * per), s1 = min(n_seqs, s0 + per);
+    auto clampT = [&](int x) { return min(total_tokens, max(0, x)); };
+    int mx = 0;
+    for (int n = s0; n < s1; ++n) mx = max(mx, clampT(cu[n + 1]));
+    s_max[t] = mx;
+    __syncthreads();
+    if (t == 0) {
+        int run = 0;
+        for (int i = 0; i < 1024; ++i) {
+            const int x = s_max[i];
+            s_max[i] = run;
+            run = max(run, x);
+        }
+    }
+    __syncthreads();
+    const int start = s_max[t];   // b'_{s0}
+    int a = start, cnt = 0;
+    for (int n = s0; n < s1; ++n) {
+        const int b = max(a, clampT(cu[n + 1]));
+        cnt += (b - a + C - 1) / C;
+        a = b;
+    }
+    s_cnt[t] = cnt;
+    __syncthreads();
+    if (t == 0) {
+        int run = 0;
+        for (int i = 0; i < 1024; ++i) {
+            const int x = s_cnt[i];
+            s_cnt[i] = run;
+            run += x;
+        }
+        off[n_seqs] = run;
+    }
+    __syncthreads();
+    int run = s_cnt[t];
+    a = start;
+    for (int n = s0; n < s1; ++n) {
+        const int b = max(a, clampT(cu[n + 1])), L = b - a;
+        off[n] = run;
+        for (int j = 0; j * C < L; ++j) table[run + j] = make_int4(n, a + j * C, min(C, L - j * C), 0);
+        run += (L + C - 1) / C;
+        a = b;
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// Intra-chunk kernel.
+// ------------------------------------------------------------------------------------
+// LDS map (bytes).  Stages 1-2: fragment buffers and the transposed Ktil.
+constexpr int L_KP = 0, L_KM = 16384, L_QP = 32768, L_KT = 49152;   // + 18432 -> 67584
+// Stages 3-6 (the fragment buffers are dead by then).
+constexpr int L_A = 0;            // fp32 [64][65]   16640
+constexpr int L_BL = 16640;       // fp16 [128][72]  18432  (beta L)^T
+constexpr int L_BV = 35072;       // fp16 [128][72]  18432  (beta V)^T
+constexpr int L_TF = 53504;       // fp32 [64][65]   16640  T
+constexpr int L_T16 = 0;          // fp16 [64][72]    9216  T (after A is dead)
+constexpr int L_BETA = 70144;     // fp32 [64]
+constexpr int L_BYTES = 70400;
+constexpr int TP = 72;            // fp16 pitch of transposed [channel][token] buffers
+constexpr int AP = 65;            // fp32 pitch of A and T
+
+// Block column J of T = (I + A)^{-1} below the diagonal, by one wave:
+//   X_J = T_JJ;  X_b = -T_bb sum_{k=J}^{b-1} A_bk X_k  for b > J.
+// X_k stays in accumulator registers (rows 4 (l/16) .. +3 of column l % 16)
+// and is fed back as the B operand of v_mfma_f32_16x16x4f32 with the
+// reduction index permuted accordingly (step s uses rows 4 (l/16) + s).
+template <int J>
+__device__ __forceinline__ void offdiag_column(const float *sA, float *sTf, int g4, int i16) {
+    float4v X[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) X[J][e] = sTf[(16 * J + 4 * g4 + e) * AP + 16 * J + i16];
+#pragma unroll
+    for (int b = J + 1; b < 4; ++b) {
+        float4v Y = {0, 0, 0, 0};
+#pragma unroll
+        for (int kk = J; kk < b; ++kk) {
+            const float *arow = sA + (16 * b + i16) * AP + 16 * kk + 4 * g4;
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                Y = __builtin_amdgcn_mfma_f32_16x16x4f32(arow[s], X[kk][s], Y, 0, 0, 0);
+        }
+        float4v Xb = {0, 0, 0, 0};
+        const float *trow = sTf + (16 * b + i16) * AP + 16 * b + 4 * g4;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            Xb = __builtin_amdgcn_mfma_f32_16x16x4f32(trow[s], Y[s], Xb, 0, 0, 0);
+        X[b] = -Xb;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sTf[(16 * b + 4 * g4 + e) * AP + 16 * J + i16] = X[b][e];
+    }
+}
+
+__global__ __launch_bounds__(256, 2) void kda_intra_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+    const uint16_t *__restrict__ v, const float *__restrict__ g,
+    const float *__restrict__ beta, float scale, int H, int row_len, int ncr,
+    const int4 *__restrict__ table, const int32_t *__restrict__ n_chunks, int nc_max,
+    uint8_t *__restrict__ recs) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[L_BYTES];
+    const int c = blockIdx.x, h = blockIdx.y;
+    if (table && c >= *n_chunks) return;
+    const Chunk ch = chunk_at(c, table, row_len, ncr);
+    uint8_t *rec = recs + ((size_t)h * nc_max + c) * REC_BYTES;
+
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4, i16 = l & 15;
+    const int len = ch.len;
+    const int ca = 32 * w + 4 * g4, cb = ca + 16;   // this lane's 8 channels: ca..ca+3, cb..cb+3
+
+    half8 *sKp = reinterpret_cast<half8 *>(smem + L_KP);
+    half8 *sKm = reinterpret_cast<half8 *>(smem + L_KM);
+    half8 *sQp = reinterpret_cast<half8 *>(smem + L_QP);
+    _Float16 *sKt = reinterpret_cast<_Float16 *>(smem + L_KT);
+    float *sBeta = reinterpret_cast<float *>(smem + L_BETA);
+
+    // ---- stage 1: cumulative decay and the decay-scaled operands -------------------
+    float G[4][8], kf[4][8], qf[4][8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int i = 16 * r + i16;
+        const bool ok = i < len;
+        const size_t base = ((size_t)(ch.t0 + (ok ? i : 0)) * H + h) * DK;
+        float4v ga = {0, 0, 0, 0}, gb = {0, 0, 0, 0};
+        uint2 ka = {0, 0}, kb2 = {0, 0}, qa = {0, 0}, qb = {0, 0};
+        if (ok) {
+            ga = *reinterpret_cast<const float4v *>(g + base + ca);
+            gb = *reinterpret_cast<const float4v *>(g + base + cb);
+            ka = *reinterpret_cast<const uint2 *>(k + base + ca);
+            kb2 = *reinterpret_cast<const uint2 *>(k + base + cb);
+            qa = *reinterpret_cast<const uint2 *>(q + base + ca);
+            qb = *reinterpret_cast<const uint2 *>(q + base + cb);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            G[r][e] = ga[e];
+            G[r][4 + e] = gb[e];
+        }
+        const uint32_t kw[4] = {ka.x, ka.y, kb2.x, kb2.y}, qw[4] = {qa.x, qa.y, qb.x, qb.y};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            kf[r][2 * e] = bf(kw[e] & 0xffff);
+            kf[r][2 * e + 1] = bf(kw[e] >> 16);
+            qf[r][2 * e] = bf(qw[e] & 0xffff);
+            qf[r][2 * e + 1] = bf(qw[e] >> 16);
+        }
+    }
+    if (tid < C) {
+        const int i = tid;
+        sBeta[i] = i < len ? beta[(size_t)(ch.t0 + i) * H + h] : 0.f;
+    }
+    // Inclusive cumsum along tokens: scan inside each 16-token tile, carry across tiles.
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        float carry = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float x = row_scan16(G[r][j]);
+            G[r][j] = carry + x;
+            carry += __shfl(x, (l & 48) | 15, 64);
+        }
+    }
+    // Reference row m (middle of the valid rows) and the chunk's last row.
+    const int m = (len - 1) >> 1, rm = m >> 4, im = m & 15;
+    float Gm[8], Em[8], ECm[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        float x = G[0][j];
+#pragma unroll
+        for (int r = 1; r < 4; ++r) x = (rm == r) ? G[r][j] : x;
+        Gm[j] = __shfl(x, (l & 48) | im, 64);
+        const float gl = __shfl(G[3][j], (l & 48) | 15, 64);   // padding rows add 0
+        Em[j] = fast_exp(Gm[j]);
+        ECm[j] = fast_exp(gl - Gm[j]);
+        // e^{G_C} for the state decay, written by one lane per channel group
+        if (i16 == 0) {
+            float *ge = reinterpret_cast<float *>(rec + REC_GE);
+            ge[(j < 4 ? ca + j : cb + j - 4)] = fast_exp(gl);
+        }
+    }
+    float Kp[4][8];   // kept for (beta L)^T in stage 3
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        half8 hkp, hkm, hqp, hqb;
+        const int i = 16 * r + i16;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float e1 = fast_exp(G[r][j] - Gm[j]);
+            const float e2 = fast_exp(Gm[j] - G[r][j]);
+            const float kp = kf[r][j] * e1, km = kf[r][j] * e2, qp = scale * qf[r][j] * e1;
+            Kp[r][j] = kp;
+            hkp[j] = (_Float16)kp;
+            hkm[j] = (_Float16)km;
+            hqp[j] = (_Float16)qp;
+            hqb[j] = (_Float16)(qp * Em[j]);
+            const int cc = j < 4 ? ca + j : cb + j - 4;
+            sKt[cc * TP + i] = (_Float16)(km * ECm[j]);
+        }
+        sKp[(r * 4 + w) * 64 + l] = hkp;
+        sKm[(r * 4 + w) * 64 + l] = hkm;
+        sQp[(r * 4 + w) * 64 + l] = hqp;
+        reinterpret_cast<half8 *>(rec + REC_Q)[(r * 4 + w) * 64 + l] = hqb;
+    }
+    __syncthreads();
+
+    // ---- stage 2: A (10 tiles) and H^T (10 tiles) on MFMA; Ktil^T fragments out ---
+    // Tile t in 0..9 is the t-th (row, col) pair with col <= row in row-major order;
+    // list entries 0..9 are A(row, col), 10..19 are H^T(col, row).  Wave w takes
+    // entries w, w+4, w+8, w+12, w+16: slots 0 and 1 are always A tiles, slot 2 is an
+    // A tile for w < 2, slots 3 and 4 are always H^T tiles.
+    float4v accA[3];
+#pragma unroll
+    for (int s = 0; s < 5; ++s) {
+        const int t = w + 4 * s;
+        const bool is_a = t < 10;
+        const int u = is_a ? t : t - 10;
+        const int r = u >= 6 ? 3 : (u >= 3 ? 2 : (u >= 1 ? 1 : 0));
+        const int j = u - (r * (r + 1)) / 2;
+        float4v acc = {0, 0, 0, 0};
+        if (is_a) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                acc = mfma16(sKp[(r * 4 + kb) * 64 + l], sKm[(j * 4 + kb) * 64 + l], acc);
+            // A_ij = beta_i * acc for j < i (rows i = 16r + 4 g4 + e, col j = 16 j + i16)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int ii = 16 * r + 4 * g4 + e, jj = 16 * j + i16;
+                acc[e] = (jj < ii) ? acc[e] * sBeta[ii] : 0.f;
+            }
+            if (s < 3) accA[s < 3 ? s : 0] = acc;
+        } else {
+            const int it = r, jt = j;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                acc = mfma16(sKm[(jt * 4 + kb) * 64 + l], sQp[(it * 4 + kb) * 64 + l], acc);
+            // H^T rows j = 16 jt + 4 g4 + e, column i = 16 it + i16; H_ij needs j <= i.
+            half4 hv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int jj = 16 * jt + 4 * g4 + e, ii = 16 * it + i16;
+                hv[e] = (_Float16)((jj <= ii) ? acc[e] : 0.f);
+            }
+            uint8_t *dst = rec + REC_H + (h_slot(it, jt >> 1) * 64 + l) * 16;
+            *reinterpret_cast<half4 *>(dst + (jt & 1) * 8) = hv;
+            if (jt == it && !(jt & 1)) {
+                const half4 z = {0, 0, 0, 0};
+                *reinterpret_cast<half4 *>(dst + 8) = z;
+            }
+        }
+    }
+    // Ktil^T fragments: channel tiles 2w, 2w+1, token blocks 0, 1.
+#pragma unroll
+    for (int cl = 0; cl < 2; ++cl) {
+        const int ct = 2 * w + cl;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const _Float16 *row = sKt + (16 * ct + i16) * TP + 32 * kb + 4 * g4;
+            const half4 lo = *reinterpret_cast<const half4 *>(row);
+            const half4 hi = *reinterpret_cast<const half4 *>(row + 16);
+            half8 f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                f[e] = lo[e];
+                f[4 + e] = hi[e];
+            }
+            reinterpret_cast<half8 *>(rec + REC_K)[(ct * 2 + kb) * 64 + l] = f;
+        }
+    }
+    __syncthreads();
+
+    // ---- stage 3: A to LDS; (beta L)^T and (beta V)^T transposed into LDS ---------
+    float *sA = reinterpret_cast<float *>(smem + L_A);
+    _Float16 *sBL = reinterpret_cast<_Float16 *>(smem + L_BL);
+    _Float16 *sBV = reinterpret_cast<_Float16 *>(smem + L_BV);
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+        const int t = w + 4 * s;
+        if (t < 10) {
+            const int r = t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0));
+            const int j = t - (r * (r + 1)) / 2;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sA[(16 * r + 4 * g4 + e) * AP + 16 * j + i16] = accA[s][e];
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int i = 16 * r + i16;
+        const bool ok = i < len;
+        const float b = sBeta[i];
+        uint2 va = {0, 0}, vb = {0, 0};
+        if (ok) {
+            const size_t base = ((size_t)(ch.t0 + i) * H + h) * DV;
+            va = *reinterpret_cast<const uint2 *>(v + base + ca);
+            vb = *reinterpret_cast<const uint2 *>(v + base + cb);
+        }
+        const uint32_t vw[4] = {va.x, va.y, vb.x, vb.y};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int cc = j < 4 ? ca + j : cb + j - 4;
+            sBL[cc * TP + i] = (_Float16)(b * Kp[r][j] * Em[j]);
+            const float vv = bf((j & 1) ? (vw[j >> 1] >> 16) : (vw[j >> 1] & 0xffff));
+            sBV[cc * TP + i] = (_Float16)(b * vv);
+        }
+    }
+    __syncthreads();
+
+    // ---- stage 4: inverses of the four diagonal 16x16 blocks of (I + A) ------------
+    float *sTf = reinterpret_cast<float *>(smem + L_TF);
+    if (w == 0) {
+        const int b = l >> 4, jc = l & 15;   // block b, column jc
+        float X[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float s = (i == jc) ? 1.f : 0.f;
+            const float *arow = sA + (16 * b + i) * AP + 16 * b;
+#pragma unroll
+            for (int kk = 0; kk < i; ++kk) s -= arow[kk] * X[kk];
+            X[i] = s;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sTf[(16 * b + i) * AP + 16 * b + jc] = X[i];
+    }
+    __syncthreads();
+
+    // ---- stage 5: off-diagonal blocks, block column j by wave j (fp32 MFMA) ---------
+    switch (w) {
+    case 0: offdiag_column<0>(sA, sTf, g4, i16); break;
+    case 1: offdiag_column<1>(sA, sTf, g4, i16); break;
+    case 2: offdiag_column<2>(sA, sTf, g4, i16); break;
+    default: break;
+    }
+    __syncthreads();
+
+    // ---- stage 6: T to fp16, then W^T = (beta L)^T T^T and U = T (beta V) -----------
+    _Float16 *sT16 = reinterpret_cast<_Float16 *>(smem + L_T16);
+    for (int e = tid; e < C * C; e += 256) {
+        const int i = e >> 6, jj = e & 63;
+        sT16[i * TP + jj] = (_Float16)((jj <= i) ? sTf[i * AP + jj] : 0.f);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int cl = 0; cl < 2; ++cl) {
+        const int ct = 2 * w + cl;   // channel tile for W^T, value tile for U
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            float4v aw = {0, 0, 0, 0}, au = {0, 0, 0, 0};
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                if (kb > (it >> 1)) continue;
+                const half8 tfrag =
+                    *reinterpret_cast<const half8 *>(sT16 + (16 * it + i16) * TP + 32 * kb + 8 * g4);
+                const half8 lfrag =
+                    *reinterpret_cast<const half8 *>(sBL + (16 * ct + i16) * TP + 32 * kb + 8 * g4);
+                const half8 vfrag =
+                    *reinterpret_cast<const half8 *>(sBV + (16 * ct + i16) * TP + 32 * kb + 8 * g4);
+                aw = mfma16(lfrag, tfrag, aw);   // rows: channels, cols: tokens
+                au = mfma16(tfrag, vfrag, au);   // rows: tokens, cols: value columns
+            }
+            half4 hw, hu;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                hw[e] = (_Float16)aw[e];
+                hu[e] = (_Float16)au[e];
+            }
+            // W A-frag (token tile it, channel block w): channel tile 2w -> bytes 0..7,
+            // channel tile 2w+1 -> bytes 8..15.
+            *reinterpret_cast<half4 *>(rec + REC_W + ((it * 4 + w) * 64 + l) * 16 + cl * 8) = hw;
+            reinterpret_cast<half4 *>(rec + REC_U)[(it * 8 + ct) * 64 + l] = hu;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// Inter-chunk kernel: the sequential chunk loop for one (sequence, head, value tile).
+// ------------------------------------------------------------------------------------
+struct InterOperands {
+    half8 W[4], Q[4], K[4], H[2];
+    half4 U[NCT];
+    float4v ge[2];
+};
+
+__device__ __forceinline__ void load_operands(InterOperands &op, const uint8_t *rec, int w, int l,
+                                              int tile) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        op.W[kb] = reinterpret_cast<const half8 *>(rec + REC_W)[(w * 4 + kb) * 64 + l];
+        op.Q[kb] = reinterpret_cast<const half8 *>(rec + REC_Q)[(w * 4 + kb) * 64 + l];
+    }
+#pragma unroll
+    for (int cl = 0; cl < 2; ++cl)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+            op.K[cl * 2 + kb] =
+                reinterpret_cast<const half8 *>(rec + REC_K)[((2 * w + cl) * 2 + kb) * 64 + l];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+        op.H[kb] = (kb <= (w >> 1))
+                       ? reinterpret_cast<const half8 *>(rec + REC_H)[h_slot(w, kb) * 64 + l]
+                       : half8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+        op.U[ct] = reinterpret_cast<const half4 *>(rec + REC_U)[(w * 8 + tile * NCT + ct) * 64 + l];
+    const float *ge = reinterpret_cast<const float *>(rec + REC_GE);
+    const int g4 = l >> 4;
+#pragma unroll
+    for (int cl = 0; cl < 2; ++cl)
+        op.ge[cl] = *reinterpret_cast<const float4v *>(ge + 16 * (2 * w + cl) + 4 * g4);
+}
+
+__global__ __launch_bounds__(256, 1) void kda_inter_kernel(
+    const int32_t *__restrict__ off, int n_pairs, int H, int row_len, int ncr,
+    const int4 *__restrict__ table, int nc_max, const uint8_t *__restrict__ recs,
+    const float *__restrict__ s0, float *__restrict__ s_final, uint16_t *__restrict__ o) {
+    __shared__ half8 sS[4 * NCT * 64];   // S as fp16 B-fragments [channel block][col tile]
+    __shared__ half8 sZ[2 * NCT * 64];   // Z as fp16 B-fragments [token block][col tile]
+
+    // Block id -> (pair, tile) so the value tiles of one (sequence, head) run on one XCD
+    // (consecutive ids go round-robin over the 8 XCDs) and share its L2.
+    const int bid = blockIdx.x;
+    const int lane8 = bid & 7, rest = bid >> 3;
+    const int tile = rest % NTILES, grp = rest / NTILES;
+    const int pair = grp * 8 + lane8;
+    if (pair >= n_pairs) return;
+    const int n = pair / H, h = pair - n * H;
+
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4, i16 = l & 15;
+    const int col0 = tile * DVT;
+
+    // State rows (channels) 32w + 16 cl + 4 g4 + e, columns col0 + 16 ct + i16.
+    float4v S[2][NCT];
+    const size_t sbase = (size_t)pair * DK * DV;
+#pragma unroll
+    for (int cl = 0; cl < 2; ++cl)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                S[cl][ct][e] = s0 ? s0[sbase + (size_t)(32 * w + 16 * cl + 4 * g4 + e) * DV + col0 +
+                                       16 * ct + i16]
+                                  : 0.f;
+
+    int cs, ce;
+    if (table) {
+        cs = off[n];
+        ce = off[n + 1];
+    } else {
+        cs = n * ncr;
+        ce = cs + ncr;
+    }
+    const uint8_t *rbase = recs + (size_t)h * nc_max * REC_BYTES;
+
+    InterOperands cur, nxt;
+    if (cs < ce) load_operands(cur, rbase + (size_t)cs * REC_BYTES, w, l, tile);
+
+    for (int c = cs; c < ce; ++c) {
+        if (c + 1 < ce) load_operands(nxt, rbase + (size_t)(c + 1) * REC_BYTES, w, l, tile);
+        const Chunk ch = chunk_at(c, table, row_len, ncr);
+
+        // 1. S -> fp16 B-fragments (channel block w).
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            half8 f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                f[e] = (_Float16)S[0][ct][e];
+                f[4 + e] = (_Float16)S[1][ct][e];
+            }
+            sS[(w * NCT + ct) * 64 + l] = f;
+        }
+        __syncthreads();
+
+        // 2. Token tile w: Z = U - W S (rows: tokens), O^T = S^T Qbar^T (rows: value cols).
+        float4v Z[NCT], O[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            float4v p = {0, 0, 0, 0}, oq = {0, 0, 0, 0};
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const half8 sf = sS[(kb * NCT + ct) * 64 + l];
+                p = mfma16(cur.W[kb], sf, p);
+                oq = mfma16(sf, cur.Q[kb], oq);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Z[ct][e] = (float)cur.U[ct][e] - p[e];
+            O[ct] = oq;
+            half4 zh;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) zh[e] = (_Float16)Z[ct][e];
+            *reinterpret_cast<half4 *>(reinterpret_cast<uint8_t *>(&sZ[((w >> 1) * NCT + ct) * 64 + l]) +
+                                       (w & 1) * 8) = zh;
+        }
+        __syncthreads();
+
+        // 3. O^T += Z^T H^T over token blocks <= w/2; store this token tile.
+        half8 zf[2][NCT];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) zf[kb][ct] = sZ[(kb * NCT + ct) * 64 + l];
+        const int tok = 16 * w + i16;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                if (kb <= (w >> 1)) O[ct] = mfma16(zf[kb][ct], cur.H[kb], O[ct]);
+            if (tok < ch.len) {
+                const size_t ob = ((size_t)(ch.t0 + tok) * H + h) * DV + col0 + 16 * ct + 4 * g4;
+                uint2 pk;
+                pk.x = (uint32_t)f32_to_bf16(O[ct][0]) | ((uint32_t)f32_to_bf16(O[ct][1]) << 16);
+                pk.y = (uint32_t)f32_to_bf16(O[ct][2]) | ((uint32_t)f32_to_bf16(O[ct][3]) << 16);
+                *reinterpret_cast<uint2 *>(o + ob) = pk;
+            }
+        }
+
+        // 4. S <- Diag(e^{G_C}) S + Ktil^T Z for channel rows 32w .. 32w+31.
+#pragma unroll
+        for (int cl = 0; cl < 2; ++cl)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                float4v acc = S[cl][ct] * cur.ge[cl];
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) acc = mfma16(cur.K[cl * 2 + kb], zf[kb][ct], acc);
+                S[cl][ct] = acc;
+            }
+        cur = nxt;
+    }
+
+    if (s_final) {
+#pragma unroll
+        for (int cl = 0; cl < 2; ++cl)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    s_final[sbase + (size_t)(32 * w + 16 * cl + 4 * g4 + e) * DV + col0 + 16 * ct +
+                            i16] = S[cl][ct][e];
+    }
+}
+
+// Workspace: [off int32 (N+1), 256-aligned][table int4 x nc_max, 256-aligned][records].
+struct WsLayout {
+    size_t off, table, recs, total;
+    int64_t nc_max;
+};
+
+static WsLayout ws_layout(int64_t total_tokens, int64_t n_seqs, int heads) {
+    WsLayout L;
+    L.nc_max = max_chunks(total_tokens, n_seqs, C);
+    auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+    L.off = 0;
+    L.table = up((size_t)(n_seqs + 1) * 4);
+    L.recs = L.table + up((size_t)L.nc_max * 16);
+    L.total = L.recs + (size_t)heads * L.nc_max * REC_BYTES;
+    return L;
+}
+
+}  // namespace mfma_path
+
+bool mfma_path_supported(int dk, int dv, int chunk, bool bf16) {
+    return bf16 && dk == mfma_path::DK && dv == mfma_path::DV && chunk == mfma_path::C;
+}
+
+size_t mfma_workspace_bytes(int64_t total_tokens, int64_t n_seqs, int heads, int /*chunk*/) {
+    return mfma_path::ws_layout(total_tokens, n_seqs, heads).total;
+}
+
+hipError_t launch_chunk_fwd_mfma(const ChunkProblem &p) {
+    using namespace mfma_path;
+    const bool varlen = p.cu != nullptr;
+    const int64_t total = (int64_t)p.batch * p.seqlen;
+    const WsLayout L = ws_layout(total, p.n_seqs, p.heads);
+    uint8_t *ws = static_cast<uint8_t *>(p.workspace);
+    int32_t *off = reinterpret_cast<int32_t *>(ws + L.off);
+    int4 *table = varlen ? reinterpret_cast<int4 *>(ws + L.table) : nullptr;
+    uint8_t *recs = ws + L.recs;
+    const int ncr = (p.seqlen + C - 1) / C;
+    const int n_pairs = p.n_seqs * p.heads;
+
+    if (varlen) {
+        hipLaunchKernelGGL(kda_chunk_index_kernel, dim3(1), dim3(1024), 0, p.stream, p.cu,
+                           p.n_seqs, (int)total, off, table);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int grid_chunks = varlen ? (int)L.nc_max : p.batch * ncr;
+    if (grid_chunks > 0 && total > 0) {
+        hipLaunchKernelGGL(kda_intra_kernel, dim3(grid_chunks, p.heads), dim3(256), 0, p.stream,
+                           static_cast<const uint16_t *>(p.q), static_cast<const uint16_t *>(p.k),
+                           static_cast<const uint16_t *>(p.v), p.g, p.beta, p.scale, p.heads,
+                           p.seqlen, ncr, table, off + p.n_seqs, (int)L.nc_max, recs);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int groups = (n_pairs + 7) / 8;
+    hipLaunchKernelGGL(kda_inter_kernel, dim3(groups * 8 * NTILES), dim3(256), 0, p.stream, off,
+                       n_pairs, p.heads, p.seqlen, ncr, table, (int)L.nc_max, recs, p.s0,
+                       p.s_final, static_cast<uint16_t *>(p.o));
+    return hipGetLastError();
+}
+
+}  // namespace kda

@@ -1,0 +1,54 @@
+// kda_internal.hpp -- host-side declarations shared by the C ABI and the
+// kernel launchers (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+// ---- decode -----------------------------------------------------------------
+bool decode_supported(int dk, int dv);
+hipError_t launch_decode(int n_pairs, int dk, int dv, bool bf16, const void *q, const void *k,
+                         const void *v, const float *g, const float *beta, float scale,
+                         float *state, void *o, hipStream_t stream);
+
+// ---- chunked prefill ----------------------------------------------------------
+// Everything a prefill launch needs, already validated by the C ABI layer.
+struct ChunkProblem {
+    int n_seqs;        // N
+    int batch;         // B rows (1 with cu_seqlens)
+    int seqlen;        // tokens per row (packed total with cu_seqlens)
+    int heads;         // H
+    int dk, dv, chunk; // d_k, d_v, C
+    bool bf16;         // storage type of q, k, v, o
+    const void *q, *k, *v;
+    const float *g, *beta;
+    float scale;
+    const float *s0;       // may be null (zeros)
+    const int32_t *cu;     // may be null (equal rows)
+    void *o;
+    float *s_final;        // may be null
+    void *workspace;
+    size_t workspace_bytes;
+    hipStream_t stream;
+};
+
+// Upper bound on the number of chunks over all sequences: each sequence of
+// L tokens has ceil(L / C) <= L / C + 1 chunks.
+inline int64_t max_chunks(int64_t total_tokens, int64_t n_seqs, int64_t chunk) {
+    return total_tokens / chunk + n_seqs;
+}
+
+// MFMA path: (128, 128, 64) with bf16 storage.
+bool mfma_path_supported(int dk, int dv, int chunk, bool bf16);
+size_t mfma_workspace_bytes(int64_t total_tokens, int64_t n_seqs, int heads, int chunk);
+hipError_t launch_chunk_fwd_mfma(const ChunkProblem &p);
+
+// fp32 path: d_k == d_v in {16, 32, 64}, C in {16, 32, 64}, fp32 storage.
+bool f32_path_supported(int dk, int dv, int chunk, bool bf16);
+size_t f32_workspace_bytes(int64_t total_tokens, int64_t n_seqs, int heads, int chunk);
+hipError_t launch_chunk_fwd_f32(const ChunkProblem &p);
+
+}  // namespace kda

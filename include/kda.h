@@ -1,0 +1,169 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention forward library.
+ *
+ * The operator, per head, with key-by-value state S (d_k x d_v, row r = key
+ * channel r), per-token log-decay g_t = log a_t (<= 0), write strength beta_t
+ * and query scale s:
+ *
+ *   S_bar = Diag(exp(g_t)) S_{t-1}                 (retain)
+ *   S_t   = S_bar + beta_t k_t (v_t - S_bar^T k_t)^T (predict, correct)
+ *   o_t   = S_t^T (s q_t)                          (read the updated state)
+ *
+ * Defined in "Understanding Kimi Delta Attention" (A. Flores), section
+ * "Learning what to forget", box "KDA: retain, predict, correct"; the query
+ * scale d_k^{-1/2} in the read is from "Demystifying Kimi Delta Attention"
+ * (J. Dborin), section "The Complexity of Modern Linear Attention".
+ *
+ * kda_chunk_fwd evaluates a whole sequence chunk by chunk in the WY / UT form
+ * of "Understanding Kimi Delta Attention", sections "The triangular system"
+ * and "Putting the chunks together" (one triangular system per chunk, one
+ * state crossing each chunk boundary).  kda_decode_step applies the recurrence
+ * once to each (session, head) pair.
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller, dense,
+ *     row-major and contiguous in the layouts stated below; the library never
+ *     allocates, frees or retains them.  They must stay valid until the work
+ *     enqueued on `stream` has completed.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  All work is
+ *     enqueued on it in order; calls return without synchronising.
+ *   - Arguments are validated on the host before anything is enqueued.  On any
+ *     error nothing is enqueued, no output is touched, and a status other than
+ *     KDA_OK is returned; kda_last_error() then describes the cause (the text
+ *     is thread-local and valid until the next call on the same thread).
+ *   - Device-side faults, if any, surface at the caller's next
+ *     synchronisation, as for any HIP kernel.
+ *   - No C++ exception crosses this boundary.  The library holds no global
+ *     mutable state; concurrent calls on different streams are safe.
+ *   - Values are not checked: NaN / Inf in, NaN / Inf out.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARGUMENT = 1,    /* NULL / misaligned pointer, bad size   */
+    KDA_ERR_UNSUPPORTED = 2,         /* (d_k, d_v, chunk, dtype) not built    */
+    KDA_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes below the query        */
+    KDA_ERR_HIP = 4                  /* a HIP launch or runtime call failed   */
+} kda_status;
+
+/* Storage type of q, k, v and o.  g, beta and every state are always fp32. */
+typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/*
+ * Problem description for kda_chunk_fwd.
+ *   batch      rows B of the q/k/v/g/beta/o tensors (must be 1 with cu_seqlens)
+ *   seqlen     tokens per row T; with cu_seqlens, the packed total cu_seqlens[N]
+ *   num_heads  H
+ *   d_k, d_v   key and value widths
+ *   chunk_size C, tokens per chunk
+ *   num_seqs   N: number of sequences (== batch without cu_seqlens)
+ *   dtype      storage type of q, k, v, o
+ * Built combinations (d_k, d_v, C, dtype):
+ *   (128, 128, 64, KDA_BF16)  MFMA path (fp16 operands, fp32 accumulation)
+ *   (d, d, C, KDA_F32) with d in {16, 32, 64}, C in {16, 32, 64}: fp32 path
+ * Everything else returns KDA_ERR_UNSUPPORTED.
+ */
+typedef struct kda_shape {
+    int32_t batch;
+    int32_t seqlen;
+    int32_t num_heads;
+    int32_t d_k;
+    int32_t d_v;
+    int32_t chunk_size;
+    int32_t num_seqs;
+    kda_dtype dtype;
+} kda_shape;
+
+/* ABI version of the loaded library (KDA_ABI_VERSION it was built with). */
+int kda_abi_version(void);
+
+/* Static text for a status code. */
+const char *kda_status_string(kda_status status);
+
+/* Detail of the last failed call on this thread ("" if none). */
+const char *kda_last_error(void);
+
+/*
+ * Bytes of device workspace kda_chunk_fwd needs for `shape`, or 0 if the
+ * shape is invalid or unsupported (kda_chunk_fwd then reports why).  The
+ * workspace holds the per-chunk WY factors between the intra-chunk and the
+ * inter-chunk kernels, and the chunk table of packed sequences.
+ */
+size_t kda_chunk_fwd_workspace_bytes(const kda_shape *shape);
+
+/*
+ * Chunkwise KDA prefill ("Understanding Kimi Delta Attention", sections "The
+ * triangular system" and "Putting the chunks together").
+ *
+ *   q, k          [B, T, H, d_k]  dtype          (q, k not normalised here)
+ *   v             [B, T, H, d_v]  dtype
+ *   g_log_decay   [B, T, H, d_k]  fp32: per-token log a_t (<= 0), NOT a
+ *                 cumulative sum; the kernel accumulates it per chunk.
+ *   beta          [B, T, H]       fp32
+ *   scale         query scale s, usually d_k^{-1/2}
+ *   initial_state [N, H, d_k, d_v] fp32, or NULL for zeros
+ *   cu_seqlens    [N+1] int32 on the device, or NULL.  With it, B must be 1,
+ *                 T = cu_seqlens[N] and sequence n owns packed tokens
+ *                 [cu_seqlens[n], cu_seqlens[n+1]).  It must start at 0 and be
+ *                 non-decreasing (not checked on the device).  Zero-length
+ *                 sequences are allowed: their final state is their initial
+ *                 state.  Without it, row b is sequence b.
+ *   o             [B, T, H, d_v]  dtype (written for every token); must not
+ *                 alias any input.
+ *   final_state   [N, H, d_k, d_v] fp32, or NULL (not written).  May equal
+ *                 initial_state (in-place continuation).
+ *   workspace     device buffer of at least
+ *                 kda_chunk_fwd_workspace_bytes(shape) bytes, 256-byte aligned.
+ * Each sequence is cut into chunks of C tokens from its first token; the last
+ * chunk may be shorter.  Chunks never straddle sequences.
+ * Supported decay range: on the MFMA path the cumulative log-decay of every
+ * channel over one chunk must stay above -16 (the decay-scaled fp16 operands
+ * keep full precision there; the standard workloads stay above -8.1).  Keys
+ * and queries are expected L2-normalised (|k|, |q| <= 1) and |v| well below
+ * the fp16 range, as the layer that calls this operator produces them.
+ * Pointers to q, k, v, o, g and the states must be 16-byte aligned; beta and
+ * cu_seqlens 4-byte aligned.
+ */
+kda_status kda_chunk_fwd(const kda_shape *shape, const void *q, const void *k,
+                         const void *v, const float *g_log_decay,
+                         const float *beta, float scale,
+                         const float *initial_state, const int32_t *cu_seqlens,
+                         void *o, float *final_state, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
+/*
+ * One recurrent decode step for num_sessions x num_heads independent pairs
+ * ("Understanding Kimi Delta Attention", box "KDA: retain, predict, correct";
+ * the fixed-size state is what a decode step reads and rewrites).
+ *
+ *   q, k          [N, H, d_k]  dtype      v, o  [N, H, d_v]  dtype
+ *   g             [N, H, d_k]  fp32 log a (<= 0)
+ *   beta          [N, H]       fp32
+ *   state_inout   [N, H, d_k, d_v] fp32, read and overwritten in place with
+ *                 the state after this token; must not alias o.
+ * Built combinations (d_k, d_v): (128, 128) for KDA_BF16 and KDA_F32, and
+ * (d, d) with d in {16, 32, 64} for both dtypes.
+ * Pointers must be 16-byte aligned, except beta (4-byte aligned).
+ */
+kda_status kda_decode_step(int32_t num_sessions, int32_t num_heads, int32_t d_k,
+                           int32_t d_v, kda_dtype dtype, const void *q,
+                           const void *k, const void *v, const float *g,
+                           const float *beta, float scale, float *state_inout,
+                           void *o, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

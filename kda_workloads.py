@@ -19,11 +19,13 @@ Distributions (the five standard workloads)
           (sigma is a standard deviation).
   lengths integers uniform on [lo, hi], both ends included.
 
-Generation uses ``numpy.random.default_rng`` with the workload's seed (1000+i
-for workload i; decode step s of workload 3 uses ``default_rng([1003, s])``)
-and a fixed draw order: lengths, q, k, v, beta-logits, z, S0.  Large tensors
-are drawn in float32 in fixed token blocks so host memory stays bounded; the
-stream is deterministic for a given seed.
+Generation uses ``numpy.random.default_rng`` streams keyed by the workload's
+seed (1000+i for workload i), the tensor (lengths 0, q 1, k 2, v 3,
+beta-logits 4, z 5, S0 6) and the block of BLOCK_TOKENS tokens: block b of
+tensor j comes from ``default_rng([seed, j, b])``; decode step s of workload 3
+uses ``default_rng([1003, 1000 + s, j, 0])``.  Blocks are independent, so they
+are drawn in parallel threads, and the result is deterministic for a given
+seed.  Normal draws are float32; host memory stays bounded by the block size.
 """
 from __future__ import annotations
 
@@ -94,34 +96,82 @@ def torch_dtype(name: str):
     return {"f32": torch.float32, "bf16": torch.bfloat16}[name]
 
 
-def _normal_rows(rng, n_tok, H, d, normalize, out_dtype):
-    """[n_tok, H, d] N(0,1) drawn in token blocks, optionally L2-normalised."""
+_POOL = None
+
+
+def _pool():
+    global _POOL
+    if _POOL is None:
+        import concurrent.futures as cf
+        import os
+        _POOL = cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 4))
+    return _POOL
+
+
+def _blocks(n_tok):
+    return [(b, t0, min(n_tok, t0 + BLOCK_TOKENS))
+            for b, t0 in enumerate(range(0, n_tok, BLOCK_TOKENS))]
+
+
+TENSOR_ID = dict(lengths=0, q=1, k=2, v=3, beta=4, z=5, s0=6)
+
+
+def _normal_rows(key, n_tok, H, d, normalize, out_dtype):
+    """[n_tok, H, d] N(0,1) (float32 draws), optionally L2-normalised per row
+    (float64 norms), rounded to ``out_dtype``.  ``key`` = [seed, tensor id]."""
     out = torch.empty((n_tok, H, d), dtype=out_dtype)
-    for t0 in range(0, n_tok, BLOCK_TOKENS):
-        t1 = min(n_tok, t0 + BLOCK_TOKENS)
-        x = rng.standard_normal((t1 - t0, H, d), dtype=np.float32)
+
+    def fill(blk):
+        b, t0, t1 = blk
+        x = torch.from_numpy(np.random.default_rng(key + [b]).standard_normal(
+            (t1 - t0, H, d), dtype=np.float32))
         if normalize:
-            x64 = x.astype(np.float64)
-            x64 /= np.sqrt(np.sum(x64 * x64, axis=-1, keepdims=True))
-            x = x64.astype(np.float32)
-        out[t0:t1] = torch.from_numpy(x).to(out_dtype)
+            x64 = x.double()
+            x = (x64 / torch.linalg.vector_norm(x64, dim=-1, keepdim=True)).float()
+        out[t0:t1] = x.to(out_dtype)
+
+    list(_pool().map(fill, _blocks(n_tok)))
     return out
 
 
-def _log_decay(rng, n_tok, H, dk, z_range):
-    """[n_tok, H, dk] fp32 log sigmoid(z), z ~ U(z_lo, z_hi)."""
+def _log_decay(key, n_tok, H, dk, z_range):
+    """[n_tok, H, dk] fp32 log sigmoid(z) = -log1p(exp(-z)) in fp64, z ~ U(z_lo, z_hi)."""
     out = torch.empty((n_tok, H, dk), dtype=torch.float32)
     lo, hi = z_range
-    for t0 in range(0, n_tok, BLOCK_TOKENS):
-        t1 = min(n_tok, t0 + BLOCK_TOKENS)
-        z = rng.uniform(lo, hi, size=(t1 - t0, H, dk))
-        out[t0:t1] = torch.from_numpy((-np.log1p(np.exp(-z))).astype(np.float32))
+
+    def fill(blk):
+        b, t0, t1 = blk
+        z = torch.from_numpy(np.random.default_rng(key + [b]).uniform(lo, hi, size=(t1 - t0, H, dk)))
+        out[t0:t1] = torch.log1p(torch.exp(-z)).neg_().float()
+
+    list(_pool().map(fill, _blocks(n_tok)))
     return out
 
 
-def _beta(rng, n_tok, H):
-    x = rng.standard_normal((n_tok, H))
-    return torch.from_numpy((1.0 / (1.0 + np.exp(-x))).astype(np.float32))
+def _beta(key, n_tok, H):
+    """[n_tok, H] fp32 sigmoid(N(0, 1))."""
+    out = torch.empty((n_tok, H), dtype=torch.float32)
+    for b, t0, t1 in _blocks(n_tok):
+        x = torch.from_numpy(np.random.default_rng(key + [b]).standard_normal((t1 - t0, H)))
+        out[t0:t1] = torch.sigmoid(x).float()
+    return out
+
+
+def _s0(key, n, H, dk, dv, std):
+    x = np.random.default_rng(key + [0]).standard_normal((n, H, dk, dv), dtype=np.float32)
+    return torch.from_numpy(x * np.float32(std))
+
+
+def _draw(seed_key, total, H, dk, dv, dtype, z_range):
+    """q, k, v, beta, g for ``total`` packed tokens; seed_key = [seed] or [seed, step]."""
+    td = torch_dtype(dtype)
+    T = TENSOR_ID
+    q = _normal_rows(seed_key + [T["q"]], total, H, dk, True, td)
+    k = _normal_rows(seed_key + [T["k"]], total, H, dk, True, td)
+    v = _normal_rows(seed_key + [T["v"]], total, H, dv, False, td)
+    beta = _beta(seed_key + [T["beta"]], total, H)
+    g = _log_decay(seed_key + [T["z"]], total, H, dk, z_range)
+    return q, k, v, beta, g
 
 
 def make_prefill(*, H, dk, dv, dtype, z_range, seed, B=1, T=0, lengths=None,
@@ -133,8 +183,6 @@ def make_prefill(*, H, dk, dv, dtype, z_range, seed, B=1, T=0, lengths=None,
     [1, sum(lengths), H, d] plus ``cu_seqlens`` int32 [N+1]).
     Returns a dict of CPU tensors plus metadata.
     """
-    rng = np.random.default_rng(seed)
-    td = torch_dtype(dtype)
     if lengths is not None:
         lengths = [int(x) for x in lengths]
         total = sum(lengths)
@@ -145,15 +193,8 @@ def make_prefill(*, H, dk, dv, dtype, z_range, seed, B=1, T=0, lengths=None,
         total, rows, row_len = B * T, B, T
         cu = None
         n_seqs = B
-    q = _normal_rows(rng, total, H, dk, True, td)
-    k = _normal_rows(rng, total, H, dk, True, td)
-    v = _normal_rows(rng, total, H, dv, False, td)
-    beta = _beta(rng, total, H)
-    g = _log_decay(rng, total, H, dk, z_range)
-    s0 = None
-    if s0_std is not None:
-        s0 = torch.from_numpy(
-            (rng.standard_normal((n_seqs, H, dk, dv), dtype=np.float32) * np.float32(s0_std)))
+    q, k, v, beta, g = _draw([seed], total, H, dk, dv, dtype, z_range)
+    s0 = None if s0_std is None else _s0([seed, TENSOR_ID["s0"]], n_seqs, H, dk, dv, s0_std)
     shape4 = lambda x: x.reshape(rows, row_len, *x.shape[1:])  # noqa: E731
     return dict(q=shape4(q), k=shape4(k), v=shape4(v), g=shape4(g), beta=shape4(beta),
                 initial_state=s0, cu_seqlens=cu, scale=1.0 / math.sqrt(dk),
@@ -161,8 +202,8 @@ def make_prefill(*, H, dk, dv, dtype, z_range, seed, B=1, T=0, lengths=None,
 
 
 def varlen_lengths(w: Workload):
-    """Seeded sequence lengths of a varlen workload (first draw of its stream)."""
-    rng = np.random.default_rng(w.seed)
+    """Seeded sequence lengths of a varlen workload."""
+    rng = np.random.default_rng([w.seed, TENSOR_ID["lengths"]])
     lo, hi = w.len_range
     return [int(x) for x in rng.integers(lo, hi + 1, size=w.n_seqs)]
 
@@ -173,43 +214,24 @@ def make_workload(idx: int):
     if w.kind != "prefill":
         raise ValueError("workload %d is a decode workload; use make_decode_state/step" % idx)
     if w.n_seqs:
-        # lengths are the first draw of the same stream; regenerate the whole
-        # stream so that the draw order is lengths, q, k, v, beta, z, S0.
-        rng = np.random.default_rng(w.seed)
-        lo, hi = w.len_range
-        lengths = [int(x) for x in rng.integers(lo, hi + 1, size=w.n_seqs)]
-        return _make_prefill_from_rng(rng, w, lengths)
+        return make_prefill(H=w.H, dk=w.dk, dv=w.dv, dtype=w.dtype, z_range=w.z_range,
+                            seed=w.seed, lengths=varlen_lengths(w), s0_std=w.s0_std)
     return make_prefill(H=w.H, dk=w.dk, dv=w.dv, dtype=w.dtype, z_range=w.z_range,
                         seed=w.seed, B=w.B, T=w.T, s0_std=w.s0_std)
-
-
-def _make_prefill_from_rng(rng, w: Workload, lengths):
-    td = torch_dtype(w.dtype)
-    total = sum(lengths)
-    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32))
-    q = _normal_rows(rng, total, w.H, w.dk, True, td)
-    k = _normal_rows(rng, total, w.H, w.dk, True, td)
-    v = _normal_rows(rng, total, w.H, w.dv, False, td)
-    beta = _beta(rng, total, w.H)
-    g = _log_decay(rng, total, w.H, w.dk, w.z_range)
-    s0 = None
-    if w.s0_std is not None:
-        s0 = torch.from_numpy(rng.standard_normal((len(lengths), w.H, w.dk, w.dv),
-                                                  dtype=np.float32) * np.float32(w.s0_std))
-    one = lambda x: x.reshape(1, total, *x.shape[1:])  # noqa: E731
-    return dict(q=one(q), k=one(k), v=one(v), g=one(g), beta=one(beta), initial_state=s0,
-                cu_seqlens=cu, scale=w.scale, n_seqs=len(lengths), dtype=w.dtype)
 
 
 def make_decode_state(w: Workload = WORKLOADS[3], n_sessions=None, H=None):
     """Initial decode state [N, H, d_k, d_v] fp32 ~ N(0, state_std^2)."""
     N = n_sessions or w.n_sessions
     Hh = H or w.H
-    rng = np.random.default_rng(w.seed)
     st = torch.empty((N, Hh, w.dk, w.dv), dtype=torch.float32)
-    for n in range(N):
-        st[n] = torch.from_numpy(rng.standard_normal((Hh, w.dk, w.dv), dtype=np.float32)
-                                 * np.float32(w.state_std))
+
+    def fill(n):
+        x = np.random.default_rng([w.seed, TENSOR_ID["s0"], n]).standard_normal(
+            (Hh, w.dk, w.dv), dtype=np.float32)
+        st[n] = torch.from_numpy(x * np.float32(w.state_std))
+
+    list(_pool().map(fill, range(N)))
     return st
 
 
@@ -217,13 +239,7 @@ def make_decode_step(step: int, w: Workload = WORKLOADS[3], n_sessions=None, H=N
     """Fresh seeded tokens of decode step ``step``: q, k, v [N, H, d], g, beta."""
     N = n_sessions or w.n_sessions
     Hh = H or w.H
-    rng = np.random.default_rng([w.seed, step])
-    td = torch_dtype(w.dtype)
-    q = _normal_rows(rng, N, Hh, w.dk, True, td)
-    k = _normal_rows(rng, N, Hh, w.dk, True, td)
-    v = _normal_rows(rng, N, Hh, w.dv, False, td)
-    beta = _beta(rng, N, Hh)
-    g = _log_decay(rng, N, Hh, w.dk, w.z_range)
+    q, k, v, beta, g = _draw([w.seed, 1000 + step], N, Hh, w.dk, w.dv, w.dtype, w.z_range)
     return dict(q=q, k=k, v=v, g=g, beta=beta, scale=w.scale)
 
 
@@ -231,5 +247,4 @@ def to64(t):
     """Exact up-cast of a stored tensor to a float64 numpy array."""
     if t is None:
         return None
-    return t.detach().to("cpu", torch.float32).numpy().astype(np.float64) if t.dtype == torch.bfloat16 \
-        else t.detach().to("cpu").numpy().astype(np.float64)
+    return t.detach().to("cpu", torch.float64).numpy()

@@ -1,0 +1,133 @@
+"""The C ABI library on the host: it loads, exports every declared symbol, and
+rejects bad arguments before touching the GPU (no compute call is made)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch  # noqa: F401  (load torch's HIP runtime first, as the binding does)
+
+import gated_delta_rule_80_amd as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_workspace_bytes",
+              "kda_status_string", "kda_abi_version", "kda_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", K.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    lib = K.lib()
+    for n in declared_functions():
+        assert getattr(lib, n) is not None
+
+
+def test_abi_version_and_status_strings():
+    lib = K.lib()
+    assert lib.kda_abi_version() == 1
+    for code, name in K.STATUS.items():
+        assert lib.kda_status_string(code).decode() == name
+
+
+def shape(**kw):
+    base = dict(batch=1, seqlen=2048, heads=32, d_k=128, d_v=128, chunk_size=64, num_seqs=1,
+                dtype_code=K.KDA_BF16)
+    base.update(kw)
+    return K.make_shape(base["batch"], base["seqlen"], base["heads"], base["d_k"], base["d_v"],
+                        base["chunk_size"], base["num_seqs"], base["dtype_code"])
+
+
+def ws(sh):
+    return K.lib().kda_chunk_fwd_workspace_bytes(ctypes.byref(sh))
+
+
+def test_workspace_query():
+    # records of 72192 bytes per (chunk, head) plus chunk table and offsets
+    n = ws(shape())
+    assert n >= 32 * (2048 // 64) * 72192
+    assert ws(shape(seqlen=131072)) >= 32 * 2048 * 72192
+    assert ws(shape(d_k=64)) == 0                       # unsupported
+    assert ws(shape(batch=0)) == 0                      # invalid
+    assert ws(shape(d_k=16, d_v=16, chunk_size=16, dtype_code=K.KDA_F32)) == 0  # fp32 path: none
+    # varlen bound T/C + N chunks never below B * ceil(T/C)
+    for B, T in [(1, 1), (3, 65), (2, 64), (5, 127)]:
+        assert ws(shape(batch=B, seqlen=T, num_seqs=B)) >= B * ((T + 63) // 64) * 32 * 72192
+
+
+FAKE = ctypes.c_void_p(0x100000)   # aligned, never dereferenced: validation fails first
+
+
+def call_chunk(sh, **over):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, scale=ctypes.c_float(0.1), s0=None,
+                cu=None, o=ctypes.c_void_p(0x200000), fs=None, ws=ctypes.c_void_p(0x300000),
+                wsb=ctypes.c_size_t(1 << 40), stream=None)
+    args.update(over)
+    return K.lib().kda_chunk_fwd(ctypes.byref(sh) if sh is not None else None, args["q"],
+                                 args["k"], args["v"], args["g"], args["beta"], args["scale"],
+                                 args["s0"], args["cu"], args["o"], args["fs"], args["ws"],
+                                 args["wsb"], args["stream"])
+
+
+def test_chunk_fwd_rejects_bad_arguments():
+    lib = K.lib()
+    assert call_chunk(None) == 1
+    assert call_chunk(shape(heads=0)) == 1
+    assert call_chunk(shape(d_k=96, d_v=96)) == 2
+    assert call_chunk(shape(chunk_size=32)) == 2
+    assert call_chunk(shape(dtype_code=7)) == 1
+    assert call_chunk(shape(batch=2, num_seqs=3)) == 1                 # N must equal B
+    assert call_chunk(shape(batch=2, num_seqs=2), cu=FAKE) == 1        # varlen needs B == 1
+    assert call_chunk(shape(), q=None) == 1
+    assert call_chunk(shape(), q=ctypes.c_void_p(0x100004)) == 1       # misaligned
+    assert call_chunk(shape(), o=FAKE) == 1                            # o aliases an input
+    assert call_chunk(shape(), ws=None) == 1
+    assert call_chunk(shape(), ws=ctypes.c_void_p(0x300010)) == 1      # workspace alignment
+    assert call_chunk(shape(), wsb=ctypes.c_size_t(1024)) == 3
+    assert b"workspace" in lib.kda_last_error()
+
+
+def test_decode_rejects_bad_arguments():
+    lib = K.lib()
+    P = ctypes.c_void_p(0x100000)
+    O = ctypes.c_void_p(0x200000)
+    f = ctypes.c_float(0.1)
+    assert lib.kda_decode_step(0, 32, 128, 128, K.KDA_BF16, P, P, P, P, P, f, P, O, None) == 1
+    assert lib.kda_decode_step(4, 32, 96, 96, K.KDA_BF16, P, P, P, P, P, f, P, O, None) == 2
+    assert lib.kda_decode_step(4, 32, 128, 64, K.KDA_BF16, P, P, P, P, P, f, P, O, None) == 2
+    assert lib.kda_decode_step(4, 32, 128, 128, 5, P, P, P, P, P, f, P, O, None) == 1
+    assert lib.kda_decode_step(4, 32, 128, 128, K.KDA_BF16, None, P, P, P, P, f, P, O, None) == 1
+    assert lib.kda_decode_step(4, 32, 128, 128, K.KDA_BF16, P, P, P, P, P, f, P, P, None) == 1
+    assert lib.kda_decode_step(4, 32, 128, 128, K.KDA_BF16, P, P, P, P, P, f, P,
+                               ctypes.c_void_p(0x200008), None) == 1
+    assert b"aligned" in lib.kda_last_error()
+
+
+def test_last_error_is_cleared_on_entry():
+    lib = K.lib()
+    call_chunk(shape(heads=0))
+    assert lib.kda_last_error() != b""
+    # a call that fails later in validation overwrites the message
+    call_chunk(shape(d_k=96, d_v=96))
+    assert b"no kernel" in lib.kda_last_error()
+
+
+def test_binding_refuses_host_tensors():
+    q = torch.zeros(1, 64, 1, 16)
+    with pytest.raises(ValueError):
+        K.chunk_fwd(q, q, q, q.float(), torch.zeros(1, 64, 1), chunk_size=16)
