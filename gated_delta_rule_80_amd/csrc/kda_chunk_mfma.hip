@@ -47,9 +47,17 @@ namespace kda {
 namespace mfma_path {
 
 constexpr int C = 64, DK = 128, DV = 128;
-constexpr int DVT = 32;               // value columns per inter workgroup
-constexpr int NCT = DVT / 16;         // 16-column tiles per inter wave
+#ifndef KDA_INTER_NG
+#define KDA_INTER_NG 1
+#endif
+#ifndef KDA_INTER_PF
+#define KDA_INTER_PF 2
+#endif
+constexpr int NG = KDA_INTER_NG;      // 16-column groups per inter workgroup (4 waves each)
+constexpr int PF = KDA_INTER_PF;      // chunk records in flight per inter wave
+constexpr int DVT = 16 * NG;          // value columns per inter workgroup
 constexpr int NTILES = DV / DVT;      // inter workgroups per (sequence, head)
+constexpr int INTER_THREADS = 256 * NG;
 
 // One chunk-head record in the workspace (bytes).  Fragment index -> 1 KB
 // (64 lanes x 16 B) unless noted.
@@ -205,12 +213,15 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
     const int4 *__restrict__ table, const int32_t *__restrict__ n_chunks, int nc_max,
     uint8_t *__restrict__ recs) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[L_BYTES];
-    const int c = blockIdx.x, h = blockIdx.y;
+    // Heads vary fastest across consecutive workgroups, so the 32 heads of one
+    // chunk -- which share every token row of q, k, v, g -- are read together.
+    const int h = blockIdx.x % H, c = blockIdx.x / H;
     if (table && c >= *n_chunks) return;
     const Chunk ch = chunk_at(c, table, row_len, ncr);
     uint8_t *rec = recs + ((size_t)h * nc_max + c) * REC_BYTES;
 
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4, i16 = l & 15;
+    const int tid = threadIdx.x, l = tid & 63, g4 = l >> 4, i16 = l & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
     const int len = ch.len;
     const int ca = 32 * w + 4 * g4, cb = ca + 16;   // this lane's 8 channels: ca..ca+3, cb..cb+3
 
@@ -222,13 +233,17 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
 
     // ---- stage 1: cumulative decay and the decay-scaled operands -------------------
     float G[4][8], kf[4][8], qf[4][8];
+    uint2 vra[4], vrb[4];   // this lane's v values (value channels ca.., cb..), used in stage 3
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int i = 16 * r + i16;
         const bool ok = i < len;
         const size_t base = ((size_t)(ch.t0 + (ok ? i : 0)) * H + h) * DK;
+        const size_t vbase = ((size_t)(ch.t0 + (ok ? i : 0)) * H + h) * DV;
         float4v ga = {0, 0, 0, 0}, gb = {0, 0, 0, 0};
         uint2 ka = {0, 0}, kb2 = {0, 0}, qa = {0, 0}, qb = {0, 0};
+        vra[r] = uint2{0, 0};
+        vrb[r] = uint2{0, 0};
         if (ok) {
             ga = *reinterpret_cast<const float4v *>(g + base + ca);
             gb = *reinterpret_cast<const float4v *>(g + base + cb);
@@ -236,6 +251,8 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
             kb2 = *reinterpret_cast<const uint2 *>(k + base + cb);
             qa = *reinterpret_cast<const uint2 *>(q + base + ca);
             qb = *reinterpret_cast<const uint2 *>(q + base + cb);
+            vra[r] = *reinterpret_cast<const uint2 *>(v + vbase + ca);
+            vrb[r] = *reinterpret_cast<const uint2 *>(v + vbase + cb);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -307,7 +324,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
         sQp[(r * 4 + w) * 64 + l] = hqp;
         reinterpret_cast<half8 *>(rec + REC_Q)[(r * 4 + w) * 64 + l] = hqb;
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- stage 2: A (10 tiles) and H^T (10 tiles) on MFMA; Ktil^T fragments out ---
     // Tile t in 0..9 is the t-th (row, col) pair with col <= row in row-major order;
@@ -372,7 +389,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
             reinterpret_cast<half8 *>(rec + REC_K)[(ct * 2 + kb) * 64 + l] = f;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- stage 3: A to LDS; (beta L)^T and (beta V)^T transposed into LDS ---------
     float *sA = reinterpret_cast<float *>(smem + L_A);
@@ -392,14 +409,8 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
     for (int r = 0; r < 4; ++r) {
         const int i = 16 * r + i16;
         const bool ok = i < len;
-        const float b = sBeta[i];
-        uint2 va = {0, 0}, vb = {0, 0};
-        if (ok) {
-            const size_t base = ((size_t)(ch.t0 + i) * H + h) * DV;
-            va = *reinterpret_cast<const uint2 *>(v + base + ca);
-            vb = *reinterpret_cast<const uint2 *>(v + base + cb);
-        }
-        const uint32_t vw[4] = {va.x, va.y, vb.x, vb.y};
+        const float b = ok ? sBeta[i] : 0.f;
+        const uint32_t vw[4] = {vra[r].x, vra[r].y, vrb[r].x, vrb[r].y};
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int cc = j < 4 ? ca + j : cb + j - 4;
@@ -408,7 +419,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
             sBV[cc * TP + i] = (_Float16)(b * vv);
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- stage 4: inverses of the four diagonal 16x16 blocks of (I + A) ------------
     float *sTf = reinterpret_cast<float *>(smem + L_TF);
@@ -426,7 +437,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) sTf[(16 * b + i) * AP + 16 * b + jc] = X[i];
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- stage 5: off-diagonal blocks, block column j by wave j (fp32 MFMA) ---------
     switch (w) {
@@ -435,7 +446,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
     case 2: offdiag_column<2>(sA, sTf, g4, i16); break;
     default: break;
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- stage 6: T to fp16, then W^T = (beta L)^T T^T and U = T (beta V) -----------
     _Float16 *sT16 = reinterpret_cast<_Float16 *>(smem + L_T16);
@@ -443,7 +454,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
         const int i = e >> 6, jj = e & 63;
         sT16[i * TP + jj] = (_Float16)((jj <= i) ? sTf[i * AP + jj] : 0.f);
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int cl = 0; cl < 2; ++cl) {
         const int ct = 2 * w + cl;   // channel tile for W^T, value tile for U
@@ -479,46 +490,110 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
 // ------------------------------------------------------------------------------------
 // Inter-chunk kernel: the sequential chunk loop for one (sequence, head, value tile).
 // ------------------------------------------------------------------------------------
+// One wave's share of a chunk record: token tile t of W, Qbar and H, channel
+// tiles 2t, 2t+1 of Ktil^T, the U tile of its 16 columns and e^{G_C} for its
+// channel rows.  Waves of one token tile in different column groups load the
+// same addresses (except U) in step, so L1 serves all but the first.
 struct InterOperands {
     half8 W[4], Q[4], K[4], H[2];
-    half4 U[NCT];
+    half4 U;
     float4v ge[2];
 };
 
-__device__ __forceinline__ void load_operands(InterOperands &op, const uint8_t *rec, int w, int l,
-                                              int tile) {
+__device__ __forceinline__ void load_operands(InterOperands &op, const uint8_t *rec, int t, int l,
+                                              int vt) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-        op.W[kb] = reinterpret_cast<const half8 *>(rec + REC_W)[(w * 4 + kb) * 64 + l];
-        op.Q[kb] = reinterpret_cast<const half8 *>(rec + REC_Q)[(w * 4 + kb) * 64 + l];
+        op.W[kb] = reinterpret_cast<const half8 *>(rec + REC_W)[(t * 4 + kb) * 64 + l];
+        op.Q[kb] = reinterpret_cast<const half8 *>(rec + REC_Q)[(t * 4 + kb) * 64 + l];
     }
 #pragma unroll
     for (int cl = 0; cl < 2; ++cl)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
             op.K[cl * 2 + kb] =
-                reinterpret_cast<const half8 *>(rec + REC_K)[((2 * w + cl) * 2 + kb) * 64 + l];
+                reinterpret_cast<const half8 *>(rec + REC_K)[((2 * t + cl) * 2 + kb) * 64 + l];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
-        op.H[kb] = (kb <= (w >> 1))
-                       ? reinterpret_cast<const half8 *>(rec + REC_H)[h_slot(w, kb) * 64 + l]
+        op.H[kb] = (kb <= (t >> 1))
+                       ? reinterpret_cast<const half8 *>(rec + REC_H)[h_slot(t, kb) * 64 + l]
                        : half8{0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-        op.U[ct] = reinterpret_cast<const half4 *>(rec + REC_U)[(w * 8 + tile * NCT + ct) * 64 + l];
+    op.U = reinterpret_cast<const half4 *>(rec + REC_U)[(t * 8 + vt) * 64 + l];
     const float *ge = reinterpret_cast<const float *>(rec + REC_GE);
     const int g4 = l >> 4;
 #pragma unroll
     for (int cl = 0; cl < 2; ++cl)
-        op.ge[cl] = *reinterpret_cast<const float4v *>(ge + 16 * (2 * w + cl) + 4 * g4);
+        op.ge[cl] = *reinterpret_cast<const float4v *>(ge + 16 * (2 * t + cl) + 4 * g4);
 }
 
-__global__ __launch_bounds__(256, 1) void kda_inter_kernel(
+// One chunk step of the recurrence for wave (token tile t, column group cg):
+// token tile t of the outputs and channel rows 32t .. 32t+31 of the state, for
+// the 16 value columns of the group.
+__device__ __forceinline__ void inter_step(float4v (&S)[2], const InterOperands &op, half8 *sS,
+                                           half8 *sZ, const Chunk &ch, int H, int h, int col,
+                                           int t, int cg, int l, uint16_t *__restrict__ o) {
+    const int g4 = l >> 4, i16 = l & 15;
+    // 1. S -> fp16 B-fragment of channel block t.
+    {
+        half8 f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            f[e] = (_Float16)S[0][e];
+            f[4 + e] = (_Float16)S[1][e];
+        }
+        sS[(t * NG + cg) * 64 + l] = f;
+    }
+    lds_barrier();
+
+    // 2. Z = U - W S (rows: tokens), O^T = S^T Qbar^T (rows: value columns).
+    float4v p = {0, 0, 0, 0}, O = {0, 0, 0, 0};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        const half8 sf = sS[(kb * NG + cg) * 64 + l];
+        p = mfma16(op.W[kb], sf, p);
+        O = mfma16(sf, op.Q[kb], O);
+    }
+    {
+        half4 zh;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) zh[e] = (_Float16)((float)op.U[e] - p[e]);
+        *reinterpret_cast<half4 *>(reinterpret_cast<uint8_t *>(&sZ[((t >> 1) * NG + cg) * 64 + l]) +
+                                   (t & 1) * 8) = zh;
+    }
+    lds_barrier();
+
+    // 3. O^T += Z^T H^T over token blocks <= t/2; store this token tile.
+    half8 zf[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) zf[kb] = sZ[(kb * NG + cg) * 64 + l];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+        if (kb <= (t >> 1)) O = mfma16(zf[kb], op.H[kb], O);
+    const int tok = 16 * t + i16;
+    if (tok < ch.len) {
+        const size_t ob = ((size_t)(ch.t0 + tok) * H + h) * DV + col + 4 * g4;
+        uint2 pk;
+        pk.x = pack_bf16x2(O[0], O[1]);
+        pk.y = pack_bf16x2(O[2], O[3]);
+        *reinterpret_cast<uint2 *>(o + ob) = pk;
+    }
+
+    // 4. S <- Diag(e^{G_C}) S + Ktil^T Z for channel rows 32t .. 32t+31.
+#pragma unroll
+    for (int cl = 0; cl < 2; ++cl) {
+        float4v acc = S[cl] * op.ge[cl];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) acc = mfma16(op.K[cl * 2 + kb], zf[kb], acc);
+        S[cl] = acc;
+    }
+}
+
+__global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
     const int32_t *__restrict__ off, int n_pairs, int H, int row_len, int ncr,
     const int4 *__restrict__ table, int nc_max, const uint8_t *__restrict__ recs,
     const float *__restrict__ s0, float *__restrict__ s_final, uint16_t *__restrict__ o) {
-    __shared__ half8 sS[4 * NCT * 64];   // S as fp16 B-fragments [channel block][col tile]
-    __shared__ half8 sZ[2 * NCT * 64];   // Z as fp16 B-fragments [token block][col tile]
+    __shared__ half8 sS[4 * NG * 64];   // S as fp16 B-fragments [channel block][column group]
+    __shared__ half8 sZ[2 * NG * 64];   // Z as fp16 B-fragments [token block][column group]
 
     // Block id -> (pair, tile) so the value tiles of one (sequence, head) run on one XCD
     // (consecutive ids go round-robin over the 8 XCDs) and share its L2.
@@ -529,21 +604,21 @@ __global__ __launch_bounds__(256, 1) void kda_inter_kernel(
     if (pair >= n_pairs) return;
     const int n = pair / H, h = pair - n * H;
 
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4, i16 = l & 15;
-    const int col0 = tile * DVT;
+    const int tid = threadIdx.x, l = tid & 63, g4 = l >> 4, i16 = l & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
+    const int t = w & 3, cg = w >> 2;                          // token tile, column group
+    const int vt = tile * NG + cg;                             // 16-column value tile
+    const int col = 16 * vt;
 
-    // State rows (channels) 32w + 16 cl + 4 g4 + e, columns col0 + 16 ct + i16.
-    float4v S[2][NCT];
+    // State rows (channels) 32t + 16 cl + 4 g4 + e, column col + i16.
+    float4v S[2];
     const size_t sbase = (size_t)pair * DK * DV;
 #pragma unroll
     for (int cl = 0; cl < 2; ++cl)
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                S[cl][ct][e] = s0 ? s0[sbase + (size_t)(32 * w + 16 * cl + 4 * g4 + e) * DV + col0 +
-                                       16 * ct + i16]
-                                  : 0.f;
+        for (int e = 0; e < 4; ++e)
+            S[cl][e] = s0 ? s0[sbase + (size_t)(32 * t + 16 * cl + 4 * g4 + e) * DV + col + i16]
+                          : 0.f;
 
     int cs, ce;
     if (table) {
@@ -555,91 +630,35 @@ __global__ __launch_bounds__(256, 1) void kda_inter_kernel(
     }
     const uint8_t *rbase = recs + (size_t)h * nc_max * REC_BYTES;
 
-    InterOperands cur, nxt;
-    if (cs < ce) load_operands(cur, rbase + (size_t)cs * REC_BYTES, w, l, tile);
-
-    for (int c = cs; c < ce; ++c) {
-        if (c + 1 < ce) load_operands(nxt, rbase + (size_t)(c + 1) * REC_BYTES, w, l, tile);
-        const Chunk ch = chunk_at(c, table, row_len, ncr);
-
-        // 1. S -> fp16 B-fragments (channel block w).
+    // Register ring of PF chunk records: chunk c + PF is requested while chunk c
+    // is being processed.  The loads are unconditional -- past the last chunk
+    // they re-read the last record (in bounds, unused) -- so the compiler's
+    // wait-count tracking stays exact across the loop.
+    InterOperands buf[PF];
+    const int clast = max(cs, ce - 1);
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            half8 f;
+    for (int j = 0; j < PF; ++j)
+        load_operands(buf[j], rbase + (size_t)min(cs + j, clast) * REC_BYTES, t, l, vt);
+
+    for (int c = cs; c < ce; c += PF) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                f[e] = (_Float16)S[0][ct][e];
-                f[4 + e] = (_Float16)S[1][ct][e];
+        for (int j = 0; j < PF; ++j) {
+            const int cj = c + j;
+            if (cj < ce) {
+                const Chunk ch = chunk_at(cj, table, row_len, ncr);
+                inter_step(S, buf[j], sS, sZ, ch, H, h, col, t, cg, l, o);
             }
-            sS[(w * NCT + ct) * 64 + l] = f;
+            load_operands(buf[j], rbase + (size_t)min(cj + PF, clast) * REC_BYTES, t, l, vt);
         }
-        __syncthreads();
-
-        // 2. Token tile w: Z = U - W S (rows: tokens), O^T = S^T Qbar^T (rows: value cols).
-        float4v Z[NCT], O[NCT];
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            float4v p = {0, 0, 0, 0}, oq = {0, 0, 0, 0};
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const half8 sf = sS[(kb * NCT + ct) * 64 + l];
-                p = mfma16(cur.W[kb], sf, p);
-                oq = mfma16(sf, cur.Q[kb], oq);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Z[ct][e] = (float)cur.U[ct][e] - p[e];
-            O[ct] = oq;
-            half4 zh;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) zh[e] = (_Float16)Z[ct][e];
-            *reinterpret_cast<half4 *>(reinterpret_cast<uint8_t *>(&sZ[((w >> 1) * NCT + ct) * 64 + l]) +
-                                       (w & 1) * 8) = zh;
-        }
-        __syncthreads();
-
-        // 3. O^T += Z^T H^T over token blocks <= w/2; store this token tile.
-        half8 zf[2][NCT];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) zf[kb][ct] = sZ[(kb * NCT + ct) * 64 + l];
-        const int tok = 16 * w + i16;
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                if (kb <= (w >> 1)) O[ct] = mfma16(zf[kb][ct], cur.H[kb], O[ct]);
-            if (tok < ch.len) {
-                const size_t ob = ((size_t)(ch.t0 + tok) * H + h) * DV + col0 + 16 * ct + 4 * g4;
-                uint2 pk;
-                pk.x = (uint32_t)f32_to_bf16(O[ct][0]) | ((uint32_t)f32_to_bf16(O[ct][1]) << 16);
-                pk.y = (uint32_t)f32_to_bf16(O[ct][2]) | ((uint32_t)f32_to_bf16(O[ct][3]) << 16);
-                *reinterpret_cast<uint2 *>(o + ob) = pk;
-            }
-        }
-
-        // 4. S <- Diag(e^{G_C}) S + Ktil^T Z for channel rows 32w .. 32w+31.
-#pragma unroll
-        for (int cl = 0; cl < 2; ++cl)
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                float4v acc = S[cl][ct] * cur.ge[cl];
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) acc = mfma16(cur.K[cl * 2 + kb], zf[kb][ct], acc);
-                S[cl][ct] = acc;
-            }
-        cur = nxt;
     }
 
     if (s_final) {
 #pragma unroll
         for (int cl = 0; cl < 2; ++cl)
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    s_final[sbase + (size_t)(32 * w + 16 * cl + 4 * g4 + e) * DV + col0 + 16 * ct +
-                            i16] = S[cl][ct][e];
+            for (int e = 0; e < 4; ++e)
+                s_final[sbase + (size_t)(32 * t + 16 * cl + 4 * g4 + e) * DV + col + i16] =
+                    S[cl][e];
     }
 }
 
@@ -690,7 +709,7 @@ hipError_t launch_chunk_fwd_mfma(const ChunkProblem &p) {
     }
     const int grid_chunks = varlen ? (int)L.nc_max : p.batch * ncr;
     if (grid_chunks > 0 && total > 0) {
-        hipLaunchKernelGGL(kda_intra_kernel, dim3(grid_chunks, p.heads), dim3(256), 0, p.stream,
+        hipLaunchKernelGGL(kda_intra_kernel, dim3(p.heads * grid_chunks), dim3(256), 0, p.stream,
                            static_cast<const uint16_t *>(p.q), static_cast<const uint16_t *>(p.k),
                            static_cast<const uint16_t *>(p.v), p.g, p.beta, p.scale, p.heads,
                            p.seqlen, ncr, table, off + p.n_seqs, (int)L.nc_max, recs);
@@ -698,7 +717,8 @@ hipError_t launch_chunk_fwd_mfma(const ChunkProblem &p) {
         if (e != hipSuccess) return e;
     }
     const int groups = (n_pairs + 7) / 8;
-    hipLaunchKernelGGL(kda_inter_kernel, dim3(groups * 8 * NTILES), dim3(256), 0, p.stream, off,
+    hipLaunchKernelGGL(kda_inter_kernel, dim3(groups * 8 * NTILES), dim3(INTER_THREADS), 0,
+                       p.stream, off,
                        n_pairs, p.heads, p.seqlen, ncr, table, (int)L.nc_max, recs, p.s0,
                        p.s_final, static_cast<uint16_t *>(p.o));
     return hipGetLastError();

@@ -57,6 +57,25 @@ __device__ __forceinline__ float4v mfma16(half8 a, half8 b, float4v c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// Two fp32 values -> packed bf16 pair (low half = a), round to nearest even
+// (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    bf2 v;
+    v[0] = (__bf16)a;
+    v[1] = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Workgroup barrier for LDS traffic only: wait for this wave's LDS operations,
+// then meet at s_barrier.  __syncthreads() also carries a global-memory fence,
+// which on CDNA waits for every outstanding global load AND store (both are
+// counted in vmcnt); that would drain prefetches and output stores at every
+// barrier.  Use this where only LDS data is exchanged between the waves.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
