@@ -40,6 +40,9 @@
 //   slot s < 4  -> index 4 (l/16) + s,   slot s >= 4 -> index 16 + 4 (l/16) + s - 4
 // which is exactly what two vertically adjacent 16x16 accumulator tiles hold,
 // so an MFMA result feeds the next MFMA without leaving registers.
+#include <algorithm>
+#include <mutex>
+
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
@@ -47,17 +50,20 @@ namespace kda {
 namespace mfma_path {
 
 constexpr int C = 64, DK = 128, DV = 128;
-#ifndef KDA_INTER_NG
-#define KDA_INTER_NG 1
+#ifndef KDA_INTER_NCT
+#define KDA_INTER_NCT 1
 #endif
 #ifndef KDA_INTER_PF
-#define KDA_INTER_PF 2
+#define KDA_INTER_PF 3
 #endif
-constexpr int NG = KDA_INTER_NG;      // 16-column groups per inter workgroup (4 waves each)
+#ifndef KDA_SEGMENTS
+#define KDA_SEGMENTS 1
+#endif
+constexpr int NCT = KDA_INTER_NCT;    // 16-column value tiles per inter workgroup
 constexpr int PF = KDA_INTER_PF;      // chunk records in flight per inter wave
-constexpr int DVT = 16 * NG;          // value columns per inter workgroup
+constexpr int DVT = 16 * NCT;         // value columns per inter workgroup
 constexpr int NTILES = DV / DVT;      // inter workgroups per (sequence, head)
-constexpr int INTER_THREADS = 256 * NG;
+constexpr int INTER_THREADS = 512;    // 4 state waves + 4 output waves
 
 // One chunk-head record in the workspace (bytes).  Fragment index -> 1 KB
 // (64 lanes x 16 B) unless noted.
@@ -206,17 +212,29 @@ __device__ __forceinline__ void offdiag_column(const float *sA, float *sTf, int 
     }
 }
 
+// Grid: one workgroup per (head, chunk).  With a chunk table (packed sequences)
+// block b covers global chunk b / H.  Without one (B equal rows of ncr chunks)
+// it covers local chunk jlo + (b / H) % jn of row (b / H) / jn, so a launch can
+// produce one segment [jlo, jlo + jn) of every row.  Heads vary fastest, so the
+// 32 heads of one chunk -- which share every token row of q, k, v, g -- are
+// read together.
 __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const float *__restrict__ g,
     const float *__restrict__ beta, float scale, int H, int row_len, int ncr,
-    const int4 *__restrict__ table, const int32_t *__restrict__ n_chunks, int nc_max,
-    uint8_t *__restrict__ recs) {
+    const int4 *__restrict__ table, const int32_t *__restrict__ n_chunks, int nc_max, int jlo,
+    int jn, uint8_t *__restrict__ recs) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[L_BYTES];
-    // Heads vary fastest across consecutive workgroups, so the 32 heads of one
-    // chunk -- which share every token row of q, k, v, g -- are read together.
-    const int h = blockIdx.x % H, c = blockIdx.x / H;
-    if (table && c >= *n_chunks) return;
+    const int h = blockIdx.x % H, b = blockIdx.x / H;
+    int c;
+    if (table) {
+        c = b;
+        if (c >= *n_chunks) return;
+    } else {
+        const int row = b / jn, j = jlo + (b - row * jn);
+        if (j >= ncr) return;
+        c = row * ncr + j;
+    }
     const Chunk ch = chunk_at(c, table, row_len, ncr);
     uint8_t *rec = recs + ((size_t)h * nc_max + c) * REC_BYTES;
 
@@ -490,110 +508,151 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
 // ------------------------------------------------------------------------------------
 // Inter-chunk kernel: the sequential chunk loop for one (sequence, head, value tile).
 // ------------------------------------------------------------------------------------
-// One wave's share of a chunk record: token tile t of W, Qbar and H, channel
-// tiles 2t, 2t+1 of Ktil^T, the U tile of its 16 columns and e^{G_C} for its
-// channel rows.  Waves of one token tile in different column groups load the
-// same addresses (except U) in step, so L1 serves all but the first.
-struct InterOperands {
-    half8 W[4], Q[4], K[4], H[2];
-    half4 U;
+// Eight waves, two per SIMD, in two roles that share no operand:
+//   state wave t (0..3)   owns channel rows 32t..32t+31 of the state (fp32, in
+//                         registers) and, for token tile t, Z = U - W S; it then
+//                         applies S <- Diag(e^{G_C}) S + Ktil^T Z.  This is the
+//                         serial chain from chunk to chunk.
+//   output wave t (0..3)  computes token tile t of O = Qbar S + H Z and stores it,
+//                         off the chain.
+// S (fp16) and Z (fp16) are exchanged through LDS with two barriers per chunk.
+// Each operand fragment is reused for the NCT 16-column tiles of the workgroup,
+// and each byte of a chunk record is loaded by exactly one wave of the CU.
+struct StateOps {
+    half8 W[4], K[4];
+    half4 U[NCT];
     float4v ge[2];
 };
+struct OutOps {
+    half8 Q[4], H[2];
+};
 
-__device__ __forceinline__ void load_operands(InterOperands &op, const uint8_t *rec, int t, int l,
-                                              int vt) {
+// Refills are split by the step that consumes each piece, so a buffer is
+// reloaded for the chunk PF ahead right after each piece's last use.
+__device__ __forceinline__ void load_wu(StateOps &op, const uint8_t *rec, int t, int l, int vt0) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < 4; ++kb)
         op.W[kb] = reinterpret_cast<const half8 *>(rec + REC_W)[(t * 4 + kb) * 64 + l];
-        op.Q[kb] = reinterpret_cast<const half8 *>(rec + REC_Q)[(t * 4 + kb) * 64 + l];
-    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+        op.U[ct] = reinterpret_cast<const half4 *>(rec + REC_U)[(t * 8 + vt0 + ct) * 64 + l];
+}
+__device__ __forceinline__ void load_kg(StateOps &op, const uint8_t *rec, int t, int l) {
 #pragma unroll
     for (int cl = 0; cl < 2; ++cl)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
             op.K[cl * 2 + kb] =
                 reinterpret_cast<const half8 *>(rec + REC_K)[((2 * t + cl) * 2 + kb) * 64 + l];
+    const float *ge = reinterpret_cast<const float *>(rec + REC_GE);
+#pragma unroll
+    for (int cl = 0; cl < 2; ++cl)
+        op.ge[cl] = *reinterpret_cast<const float4v *>(ge + 16 * (2 * t + cl) + 4 * (l >> 4));
+}
+__device__ __forceinline__ void load_q(OutOps &op, const uint8_t *rec, int t, int l) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+        op.Q[kb] = reinterpret_cast<const half8 *>(rec + REC_Q)[(t * 4 + kb) * 64 + l];
+}
+__device__ __forceinline__ void load_h(OutOps &op, const uint8_t *rec, int t, int l) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
         op.H[kb] = (kb <= (t >> 1))
                        ? reinterpret_cast<const half8 *>(rec + REC_H)[h_slot(t, kb) * 64 + l]
                        : half8{0, 0, 0, 0, 0, 0, 0, 0};
-    op.U = reinterpret_cast<const half4 *>(rec + REC_U)[(t * 8 + vt) * 64 + l];
-    const float *ge = reinterpret_cast<const float *>(rec + REC_GE);
-    const int g4 = l >> 4;
-#pragma unroll
-    for (int cl = 0; cl < 2; ++cl)
-        op.ge[cl] = *reinterpret_cast<const float4v *>(ge + 16 * (2 * t + cl) + 4 * g4);
 }
 
-// One chunk step of the recurrence for wave (token tile t, column group cg):
-// token tile t of the outputs and channel rows 32t .. 32t+31 of the state, for
-// the 16 value columns of the group.
-__device__ __forceinline__ void inter_step(float4v (&S)[2], const InterOperands &op, half8 *sS,
-                                           half8 *sZ, const Chunk &ch, int H, int h, int col,
-                                           int t, int cg, int l, uint16_t *__restrict__ o) {
-    const int g4 = l >> 4, i16 = l & 15;
-    // 1. S -> fp16 B-fragment of channel block t.
-    {
+// Chunk step of a state wave (token tile / channel block t).
+__device__ __forceinline__ void state_step(float4v (&S)[2][NCT], StateOps &op, half8 *sS,
+                                           half8 *sZ, int t, int l, int vt0,
+                                           const uint8_t *next) {
+    // S -> fp16 B-fragments of channel block t.
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
         half8 f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            f[e] = (_Float16)S[0][e];
-            f[4 + e] = (_Float16)S[1][e];
+            f[e] = (_Float16)S[0][ct][e];
+            f[4 + e] = (_Float16)S[1][ct][e];
         }
-        sS[(t * NG + cg) * 64 + l] = f;
+        sS[(t * NCT + ct) * 64 + l] = f;
     }
     lds_barrier();
-
-    // 2. Z = U - W S (rows: tokens), O^T = S^T Qbar^T (rows: value columns).
-    float4v p = {0, 0, 0, 0}, O = {0, 0, 0, 0};
+    // Z = U - W S for token tile t (rows: tokens).
+    float4v p[NCT];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-        const half8 sf = sS[(kb * NG + cg) * 64 + l];
-        p = mfma16(op.W[kb], sf, p);
-        O = mfma16(sf, op.Q[kb], O);
-    }
-    {
+    for (int ct = 0; ct < NCT; ++ct) p[ct] = float4v{0, 0, 0, 0};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) p[ct] = mfma16(op.W[kb], sS[(kb * NCT + ct) * 64 + l], p[ct]);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
         half4 zh;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) zh[e] = (_Float16)((float)op.U[e] - p[e]);
-        *reinterpret_cast<half4 *>(reinterpret_cast<uint8_t *>(&sZ[((t >> 1) * NG + cg) * 64 + l]) +
+        for (int e = 0; e < 4; ++e) zh[e] = (_Float16)((float)op.U[ct][e] - p[ct][e]);
+        *reinterpret_cast<half4 *>(reinterpret_cast<uint8_t *>(&sZ[((t >> 1) * NCT + ct) * 64 + l]) +
                                    (t & 1) * 8) = zh;
     }
+    load_wu(op, next, t, l, vt0);
     lds_barrier();
-
-    // 3. O^T += Z^T H^T over token blocks <= t/2; store this token tile.
-    half8 zf[2];
+    // S <- Diag(e^{G_C}) S + Ktil^T Z for channel rows 32t .. 32t+31.
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) zf[kb] = sZ[(kb * NG + cg) * 64 + l];
+    for (int ct = 0; ct < NCT; ++ct) {
+        const half8 z0 = sZ[(0 * NCT + ct) * 64 + l], z1 = sZ[(1 * NCT + ct) * 64 + l];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-        if (kb <= (t >> 1)) O = mfma16(zf[kb], op.H[kb], O);
-    const int tok = 16 * t + i16;
-    if (tok < ch.len) {
-        const size_t ob = ((size_t)(ch.t0 + tok) * H + h) * DV + col + 4 * g4;
-        uint2 pk;
-        pk.x = pack_bf16x2(O[0], O[1]);
-        pk.y = pack_bf16x2(O[2], O[3]);
-        *reinterpret_cast<uint2 *>(o + ob) = pk;
+        for (int cl = 0; cl < 2; ++cl) {
+            float4v acc = S[cl][ct] * op.ge[cl];
+            acc = mfma16(op.K[cl * 2 + 0], z0, acc);
+            acc = mfma16(op.K[cl * 2 + 1], z1, acc);
+            S[cl][ct] = acc;
+        }
     }
-
-    // 4. S <- Diag(e^{G_C}) S + Ktil^T Z for channel rows 32t .. 32t+31.
-#pragma unroll
-    for (int cl = 0; cl < 2; ++cl) {
-        float4v acc = S[cl] * op.ge[cl];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) acc = mfma16(op.K[cl * 2 + kb], zf[kb], acc);
-        S[cl] = acc;
-    }
+    load_kg(op, next, t, l);
 }
 
+// Chunk step of an output wave (token tile t): O^T = S^T Qbar^T + Z^T H^T.
+__device__ __forceinline__ void output_step(OutOps &op, const half8 *sS, const half8 *sZ,
+                                            const Chunk &ch, int H, int h, int t, int l, int vt0,
+                                            const uint8_t *next, uint16_t *__restrict__ o) {
+    const int g4 = l >> 4, i16 = l & 15;
+    lds_barrier();
+    float4v O[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) O[ct] = float4v{0, 0, 0, 0};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) O[ct] = mfma16(sS[(kb * NCT + ct) * 64 + l], op.Q[kb], O[ct]);
+    load_q(op, next, t, l);
+    lds_barrier();
+    const int tok = 16 * t + i16;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+            if (kb <= (t >> 1)) O[ct] = mfma16(sZ[(kb * NCT + ct) * 64 + l], op.H[kb], O[ct]);
+        if (tok < ch.len) {
+            const size_t ob = ((size_t)(ch.t0 + tok) * H + h) * DV + 16 * (vt0 + ct) + 4 * g4;
+            uint2 pk;
+            pk.x = pack_bf16x2(O[ct][0], O[ct][1]);
+            pk.y = pack_bf16x2(O[ct][2], O[ct][3]);
+            *reinterpret_cast<uint2 *>(o + ob) = pk;
+        }
+    }
+    load_h(op, next, t, l);
+}
+
+// Processes local chunks [jlo, jhi) of every (sequence, head, value tile): the
+// state is read from s_in (NULL = zeros) and written to s_out (NULL = not
+// written).  s_out may equal s_in: each lane reads its state elements before
+// it writes them, and no other lane touches them.
 __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
     const int32_t *__restrict__ off, int n_pairs, int H, int row_len, int ncr,
-    const int4 *__restrict__ table, int nc_max, const uint8_t *__restrict__ recs,
-    const float *__restrict__ s0, float *__restrict__ s_final, uint16_t *__restrict__ o) {
-    __shared__ half8 sS[4 * NG * 64];   // S as fp16 B-fragments [channel block][column group]
-    __shared__ half8 sZ[2 * NG * 64];   // Z as fp16 B-fragments [token block][column group]
+    const int4 *__restrict__ table, int nc_max, const uint8_t *__restrict__ recs, int jlo,
+    int jhi, const float *s_in, float *s_out, uint16_t *__restrict__ o) {
+    __shared__ half8 sS[4 * NCT * 64];   // S as fp16 B-fragments [channel block][column tile]
+    __shared__ half8 sZ[2 * NCT * 64];   // Z as fp16 B-fragments [token block][column tile]
 
     // Block id -> (pair, tile) so the value tiles of one (sequence, head) run on one XCD
     // (consecutive ids go round-robin over the 8 XCDs) and share its L2.
@@ -606,19 +665,9 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
 
     const int tid = threadIdx.x, l = tid & 63, g4 = l >> 4, i16 = l & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
-    const int t = w & 3, cg = w >> 2;                          // token tile, column group
-    const int vt = tile * NG + cg;                             // 16-column value tile
-    const int col = 16 * vt;
-
-    // State rows (channels) 32t + 16 cl + 4 g4 + e, column col + i16.
-    float4v S[2];
-    const size_t sbase = (size_t)pair * DK * DV;
-#pragma unroll
-    for (int cl = 0; cl < 2; ++cl)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            S[cl][e] = s0 ? s0[sbase + (size_t)(32 * t + 16 * cl + 4 * g4 + e) * DV + col + i16]
-                          : 0.f;
+    const int t = w & 3;
+    const bool state_role = w < 4;
+    const int vt0 = tile * NCT;
 
     int cs, ce;
     if (table) {
@@ -628,43 +677,75 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
         cs = n * ncr;
         ce = cs + ncr;
     }
+    ce = min(ce, cs + jhi);
+    cs = min(ce, cs + jlo);
     const uint8_t *rbase = recs + (size_t)h * nc_max * REC_BYTES;
-
-    // Register ring of PF chunk records: chunk c + PF is requested while chunk c
-    // is being processed.  The loads are unconditional -- past the last chunk
-    // they re-read the last record (in bounds, unused) -- so the compiler's
-    // wait-count tracking stays exact across the loop.
-    InterOperands buf[PF];
     const int clast = max(cs, ce - 1);
-#pragma unroll
-    for (int j = 0; j < PF; ++j)
-        load_operands(buf[j], rbase + (size_t)min(cs + j, clast) * REC_BYTES, t, l, vt);
+    const size_t sbase = (size_t)pair * DK * DV;
 
-    for (int c = cs; c < ce; c += PF) {
-#pragma unroll
-        for (int j = 0; j < PF; ++j) {
-            const int cj = c + j;
-            if (cj < ce) {
-                const Chunk ch = chunk_at(cj, table, row_len, ncr);
-                inter_step(S, buf[j], sS, sZ, ch, H, h, col, t, cg, l, o);
-            }
-            load_operands(buf[j], rbase + (size_t)min(cj + PF, clast) * REC_BYTES, t, l, vt);
-        }
-    }
-
-    if (s_final) {
+    // The loads are unconditional -- past the last chunk they re-read the last
+    // record (in bounds, unused) -- so the compiler's wait-count tracking stays
+    // exact across the loop.  Each ring slot is refilled for the chunk PF ahead.
+    if (state_role) {
+        // State rows (channels) 32t + 16 cl + 4 g4 + e, columns 16 (vt0 + ct) + i16.
+        float4v S[2][NCT];
 #pragma unroll
         for (int cl = 0; cl < 2; ++cl)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                s_final[sbase + (size_t)(32 * t + 16 * cl + 4 * g4 + e) * DV + col + i16] =
-                    S[cl][e];
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    S[cl][ct][e] = s_in ? s_in[sbase + (size_t)(32 * t + 16 * cl + 4 * g4 + e) * DV +
+                                               16 * (vt0 + ct) + i16]
+                                        : 0.f;
+        StateOps buf[PF];
+#pragma unroll
+        for (int j = 0; j < PF; ++j) {
+            const uint8_t *rec = rbase + (size_t)min(cs + j, clast) * REC_BYTES;
+            load_wu(buf[j], rec, t, l, vt0);
+            load_kg(buf[j], rec, t, l);
+        }
+        for (int c = cs; c < ce; c += PF) {
+#pragma unroll
+            for (int j = 0; j < PF; ++j)
+                if (c + j < ce)
+                    state_step(S, buf[j], sS, sZ, t, l, vt0,
+                               rbase + (size_t)min(c + j + PF, clast) * REC_BYTES);
+        }
+        if (s_out) {
+#pragma unroll
+            for (int cl = 0; cl < 2; ++cl)
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        s_out[sbase + (size_t)(32 * t + 16 * cl + 4 * g4 + e) * DV +
+                              16 * (vt0 + ct) + i16] = S[cl][ct][e];
+        }
+    } else {
+        OutOps buf[PF];
+#pragma unroll
+        for (int j = 0; j < PF; ++j) {
+            const uint8_t *rec = rbase + (size_t)min(cs + j, clast) * REC_BYTES;
+            load_q(buf[j], rec, t, l);
+            load_h(buf[j], rec, t, l);
+        }
+        for (int c = cs; c < ce; c += PF) {
+#pragma unroll
+            for (int j = 0; j < PF; ++j)
+                if (c + j < ce) {
+                    const Chunk ch = chunk_at(c + j, table, row_len, ncr);
+                    output_step(buf[j], sS, sZ, ch, H, h, t, l, vt0,
+                                rbase + (size_t)min(c + j + PF, clast) * REC_BYTES, o);
+                }
+        }
     }
 }
 
-// Workspace: [off int32 (N+1), 256-aligned][table int4 x nc_max, 256-aligned][records].
+// Workspace: [off int32 (N+1)][chunk table int4 x nc_max][carried state fp32
+// N x H x d_k x d_v][records], each region 256-byte aligned.
 struct WsLayout {
-    size_t off, table, recs, total;
+    size_t off, table, state, recs, total;
     int64_t nc_max;
 };
 
@@ -674,7 +755,8 @@ static WsLayout ws_layout(int64_t total_tokens, int64_t n_seqs, int heads) {
     auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
     L.off = 0;
     L.table = up((size_t)(n_seqs + 1) * 4);
-    L.recs = L.table + up((size_t)L.nc_max * 16);
+    L.state = L.table + up((size_t)L.nc_max * 16);
+    L.recs = L.state + up((size_t)n_seqs * heads * DK * DV * 4);
     L.total = L.recs + (size_t)heads * L.nc_max * REC_BYTES;
     return L;
 }
@@ -689,6 +771,42 @@ size_t mfma_workspace_bytes(int64_t total_tokens, int64_t n_seqs, int heads, int
     return mfma_path::ws_layout(total_tokens, n_seqs, heads).total;
 }
 
+// Per device: one helper stream (default priority) and a ring of events, made
+// on first use and kept until the process ends.  The helper stream runs the
+// intra-chunk kernels of segment s + 1 while the caller's stream runs the
+// inter-chunk kernel of segment s.
+namespace {
+constexpr int kMaxDevices = 64, kEvents = 64;
+struct Aux {
+    bool ready = false;
+    hipStream_t helper = nullptr;
+    hipEvent_t ev[kEvents];
+    int next = 0;
+};
+std::mutex g_aux_mu;
+Aux g_aux[kMaxDevices];
+
+// Returns false if the helper resources cannot be made (then run serially).
+bool get_aux(int n_events, hipStream_t *helper, hipEvent_t *evs) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return false;
+    std::lock_guard<std::mutex> lk(g_aux_mu);
+    Aux &a = g_aux[dev];
+    if (!a.ready) {
+        if (hipStreamCreateWithFlags(&a.helper, hipStreamNonBlocking) != hipSuccess) return false;
+        for (int i = 0; i < kEvents; ++i)
+            if (hipEventCreateWithFlags(&a.ev[i], hipEventDisableTiming) != hipSuccess) return false;
+        a.ready = true;
+    }
+    *helper = a.helper;
+    for (int i = 0; i < n_events; ++i) {
+        evs[i] = a.ev[a.next];
+        a.next = (a.next + 1) % kEvents;
+    }
+    return true;
+}
+}  // namespace
+
 hipError_t launch_chunk_fwd_mfma(const ChunkProblem &p) {
     using namespace mfma_path;
     const bool varlen = p.cu != nullptr;
@@ -697,31 +815,71 @@ hipError_t launch_chunk_fwd_mfma(const ChunkProblem &p) {
     uint8_t *ws = static_cast<uint8_t *>(p.workspace);
     int32_t *off = reinterpret_cast<int32_t *>(ws + L.off);
     int4 *table = varlen ? reinterpret_cast<int4 *>(ws + L.table) : nullptr;
+    float *carry = reinterpret_cast<float *>(ws + L.state);
     uint8_t *recs = ws + L.recs;
     const int ncr = (p.seqlen + C - 1) / C;
     const int n_pairs = p.n_seqs * p.heads;
+    const int inter_grid = (n_pairs + 7) / 8 * 8 * NTILES;
+    uint16_t *o = static_cast<uint16_t *>(p.o);
+    hipError_t e;
 
-    if (varlen) {
-        hipLaunchKernelGGL(kda_chunk_index_kernel, dim3(1), dim3(1024), 0, p.stream, p.cu,
-                           p.n_seqs, (int)total, off, table);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    const int grid_chunks = varlen ? (int)L.nc_max : p.batch * ncr;
-    if (grid_chunks > 0 && total > 0) {
-        hipLaunchKernelGGL(kda_intra_kernel, dim3(p.heads * grid_chunks), dim3(256), 0, p.stream,
+    auto intra = [&](hipStream_t st, int jlo, int jn, int grid) {
+        hipLaunchKernelGGL(kda_intra_kernel, dim3(grid), dim3(256), 0, st,
                            static_cast<const uint16_t *>(p.q), static_cast<const uint16_t *>(p.k),
                            static_cast<const uint16_t *>(p.v), p.g, p.beta, p.scale, p.heads,
-                           p.seqlen, ncr, table, off + p.n_seqs, (int)L.nc_max, recs);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+                           p.seqlen, ncr, table, off + p.n_seqs, (int)L.nc_max, jlo, jn, recs);
+        return hipGetLastError();
+    };
+    auto inter = [&](int jlo, int jhi, const float *s_in, float *s_out) {
+        hipLaunchKernelGGL(kda_inter_kernel, dim3(inter_grid), dim3(INTER_THREADS), 0, p.stream,
+                           off, n_pairs, p.heads, p.seqlen, ncr, table, (int)L.nc_max, recs, jlo,
+                           jhi, s_in, s_out, o);
+        return hipGetLastError();
+    };
+
+    if (varlen || total == 0) {
+        // Packed sequences: chunk table, all intra-chunk work, then the chunk chain.
+        if (varlen) {
+            hipLaunchKernelGGL(kda_chunk_index_kernel, dim3(1), dim3(1024), 0, p.stream, p.cu,
+                               p.n_seqs, (int)total, off, table);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            if (L.nc_max > 0 && (e = intra(p.stream, 0, 0, p.heads * (int)L.nc_max)) != hipSuccess)
+                return e;
+        }
+        return inter(0, INT32_MAX / 2, p.s0, p.s_final);
     }
-    const int groups = (n_pairs + 7) / 8;
-    hipLaunchKernelGGL(kda_inter_kernel, dim3(groups * 8 * NTILES), dim3(INTER_THREADS), 0,
-                       p.stream, off,
-                       n_pairs, p.heads, p.seqlen, ncr, table, (int)L.nc_max, recs, p.s0,
-                       p.s_final, static_cast<uint16_t *>(p.o));
-    return hipGetLastError();
+
+    // Equal rows: S segments of local chunks; intra(s + 1) overlaps inter(s).
+    const int S = KDA_SEGMENTS <= 1 ? 1 : std::min(ncr, std::min(16, KDA_SEGMENTS));
+    const int M = (ncr + S - 1) / S;
+    hipStream_t helper = nullptr;
+    hipEvent_t ev[17];
+    const bool overlap = S > 1 && get_aux(S + 1, &helper, ev);
+    if (!overlap) {
+        if ((e = intra(p.stream, 0, ncr, p.heads * p.batch * ncr)) != hipSuccess) return e;
+        return inter(0, ncr, p.s0, p.s_final);
+    }
+    // The helper stream starts once everything the caller queued before us is done.
+    if ((e = hipEventRecord(ev[S], p.stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(helper, ev[S], 0)) != hipSuccess) return e;
+    for (int s = 0; s < S; ++s) {
+        const int jlo = s * M, jn = std::min(M, ncr - jlo);
+        if (jn <= 0) break;
+        if ((e = intra(helper, jlo, jn, p.heads * p.batch * jn)) != hipSuccess) return e;
+        if ((e = hipEventRecord(ev[s], helper)) != hipSuccess) return e;
+    }
+    // The state crosses segments through final_state when given, else through
+    // the workspace (final_state may alias initial_state: see the inter kernel).
+    float *state = p.s_final ? p.s_final : carry;
+    for (int s = 0; s < S; ++s) {
+        const int jlo = s * M, jhi = std::min(ncr, jlo + M);
+        if (jhi <= jlo) break;
+        if ((e = hipStreamWaitEvent(p.stream, ev[s], 0)) != hipSuccess) return e;
+        const bool last = jhi >= ncr;
+        if ((e = inter(jlo, jhi, s == 0 ? p.s0 : state, last ? p.s_final : state)) != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace kda

@@ -83,6 +83,54 @@ def test_ragged_lengths(T):
     check_prefill(small(T=T), 64)
 
 
+@pytest.mark.parametrize("T,B,s0", [(529, 1, True), (1000, 2, False), (4100, 1, True),
+                                    (8192 + 33, 1, True)])
+def test_segmented_overlap_path(T, B, s0):
+    """Rows of >= 8 chunks run as overlapped segments (intra-chunk kernels on a
+    helper stream, the chunk chain on the caller's stream, the state carried
+    between segments)."""
+    check_prefill(small(T=T, B=B, H=2, s0_std=0.05 if s0 else None), 64)
+
+
+def test_segmented_in_place_state_and_no_final():
+    import gated_delta_rule_80_amd as K
+    inp = small(T=1500, H=2)
+    d = to_dev(inp)
+    o_ref, s_ref = oracle_prefill(inp)
+    st = d["initial_state"].clone()
+    o, _ = K.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=st,
+                       final_state=st)
+    o2, none = K.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                           initial_state=d["initial_state"], output_final_state=False)
+    torch.cuda.synchronize()
+    assert none is None
+    o64 = o.double().cpu().numpy().reshape(-1, 2, 128)
+    assert rel_err(o64, o_ref) <= TOL["bf16"]
+    assert rel_err(st.double().cpu().numpy(), s_ref) <= TOL["bf16"]
+    assert torch.equal(o, o2)
+
+
+def test_back_to_back_calls_reuse_workspace():
+    """Consecutive calls on one stream share a workspace: the second call's
+    intra-chunk work must not overwrite records the first call still reads."""
+    import gated_delta_rule_80_amd as K
+    a, b = small(T=2000, H=2, seed=21), small(T=2000, H=2, seed=22)
+    da, db = to_dev(a), to_dev(b)
+    ws = torch.empty(K.workspace_bytes(1, 2000, 2, 128, 128, 64, 1), dtype=torch.uint8,
+                     device="cuda")
+    outs = []
+    for _ in range(3):
+        for dd in (da, db):
+            o, f = K.chunk_fwd(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"],
+                               initial_state=dd["initial_state"], workspace=ws)
+            outs.append((o, f))
+    torch.cuda.synchronize()
+    for i in range(2, 6):
+        assert torch.equal(outs[i][0], outs[i % 2][0]) and torch.equal(outs[i][1], outs[i % 2][1])
+    o_ref, s_ref = oracle_prefill(a)
+    assert rel_err(outs[0][0].double().cpu().numpy().reshape(-1, 2, 128), o_ref) <= TOL["bf16"]
+
+
 def test_equal_rows_batch():
     check_prefill(small(B=3, T=150, H=2), 64)
 
