@@ -776,7 +776,8 @@ size_t mfma_workspace_bytes(int64_t total_tokens, int64_t n_seqs, int heads, int
 // intra-chunk kernels of segment s + 1 while the caller's stream runs the
 // inter-chunk kernel of segment s.
 namespace {
-constexpr int kMaxDevices = 64, kEvents = 64;
+constexpr int kMaxDevices = 64, kEvents = 160;
+constexpr int kMaxSegments = 128;
 struct Aux {
     bool ready = false;
     hipStream_t helper = nullptr;
@@ -850,10 +851,10 @@ hipError_t launch_chunk_fwd_mfma(const ChunkProblem &p) {
     }
 
     // Equal rows: S segments of local chunks; intra(s + 1) overlaps inter(s).
-    const int S = KDA_SEGMENTS <= 1 ? 1 : std::min(ncr, std::min(16, KDA_SEGMENTS));
+    const int S = KDA_SEGMENTS <= 1 ? 1 : std::min(ncr, std::min(kMaxSegments, KDA_SEGMENTS));
     const int M = (ncr + S - 1) / S;
     hipStream_t helper = nullptr;
-    hipEvent_t ev[17];
+    hipEvent_t ev[kMaxSegments + 1];
     const bool overlap = S > 1 && get_aux(S + 1, &helper, ev);
     if (!overlap) {
         if ((e = intra(p.stream, 0, ncr, p.heads * p.batch * ncr)) != hipSuccess) return e;
