@@ -59,11 +59,19 @@ constexpr int C = 64, DK = 128, DV = 128;
 #ifndef KDA_SEGMENTS
 #define KDA_SEGMENTS 1
 #endif
+#ifndef KDA_INTER_L2D
+#define KDA_INTER_L2D 4
+#endif
+#ifndef KDA_INTER_L2R
+#define KDA_INTER_L2R 4
+#endif
 constexpr int NCT = KDA_INTER_NCT;    // 16-column value tiles per inter workgroup
 constexpr int PF = KDA_INTER_PF;      // chunk records in flight per inter wave
 constexpr int DVT = 16 * NCT;         // value columns per inter workgroup
 constexpr int NTILES = DV / DVT;      // inter workgroups per (sequence, head)
-constexpr int INTER_THREADS = 512;    // 4 state waves + 4 output waves
+constexpr int L2D = KDA_INTER_L2D;    // L2 prefetch distance in chunks (0: no prefetch wave)
+constexpr int L2R = KDA_INTER_L2R;    // chunks a prefetch load may stay in flight
+constexpr int INTER_THREADS = L2D > 0 ? 576 : 512;   // 4 state + 4 output (+ 1 prefetch) waves
 
 // One chunk-head record in the workspace (bytes).  Fragment index -> 1 KB
 // (64 lanes x 16 B) unless noted.
@@ -722,7 +730,7 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
                         s_out[sbase + (size_t)(32 * t + 16 * cl + 4 * g4 + e) * DV +
                               16 * (vt0 + ct) + i16] = S[cl][ct][e];
         }
-    } else {
+    } else if (w < 8) {
         OutOps buf[PF];
 #pragma unroll
         for (int j = 0; j < PF; ++j) {
@@ -739,6 +747,48 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
                                 rbase + (size_t)min(c + j + PF, clast) * REC_BYTES, o);
                 }
         }
+    } else if (L2D > 0) {
+        // Prefetch wave: touches this tile's share of the 128-byte lines of the
+        // record L2D chunks ahead, so that the record sits in L2 when the other
+        // waves' register rings load it (the value tiles of a pair share that
+        // L2).  A touch is consumed -- waited for -- L2R chunks after it was
+        // issued, so this wave never stalls the chunk barriers on memory.
+        constexpr int LINES = REC_BYTES / 128;
+#ifdef KDA_INTER_L2ALL
+        constexpr int SHARE = LINES;
+        const int tile0 = 0;
+#else
+        constexpr int SHARE = (LINES + NTILES - 1) / NTILES;
+        const int tile0 = tile;
+#endif
+        constexpr int NLD = (SHARE + 63) / 64;
+        int lofs[NLD];
+#pragma unroll
+        for (int i = 0; i < NLD; ++i)
+            lofs[i] = min(tile0 * SHARE + min(64 * i + l, SHARE - 1), LINES - 1) * 128;
+        uint32_t ring[L2R][NLD];
+#pragma unroll
+        for (int j = 0; j < L2R; ++j)
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) ring[j][i] = 0;
+        for (int c = cs; c < ce; c += L2R) {
+#pragma unroll
+            for (int j = 0; j < L2R; ++j)
+                if (c + j < ce) {
+                    lds_barrier();
+                    const uint8_t *rec = rbase + (size_t)min(c + j + L2D, clast) * REC_BYTES;
+#pragma unroll
+                    for (int i = 0; i < NLD; ++i) {
+                        asm volatile("" ::"v"(ring[j][i]));
+                        ring[j][i] = *reinterpret_cast<const uint32_t *>(rec + lofs[i]);
+                    }
+                    lds_barrier();
+                }
+        }
+#pragma unroll
+        for (int j = 0; j < L2R; ++j)
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) asm volatile("" ::"v"(ring[j][i]));
     }
 }
 
