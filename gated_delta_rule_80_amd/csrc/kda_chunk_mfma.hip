@@ -180,8 +180,8 @@ __global__ __launch_bounds__(1024) void kda_chunk_index_kernel(const int32_t *__
 constexpr int L_KP = 0, L_KM = 16384, L_QP = 32768, L_KT = 49152;   // + 18432 -> 67584
 // Stages 3-6 (the fragment buffers are dead by then).
 constexpr int L_A = 0;            // fp32 [64][65]   16640
-constexpr int L_BL = 16640;       // fp16 [128][72]  18432  (beta L)^T
-constexpr int L_BV = 35072;       // fp16 [128][72]  18432  (beta V)^T
+constexpr int L_BL = 16640;       // fp16 [128][72]  18432  L^T = (K e^{G})^T
+constexpr int L_BV = 35072;       // fp16 [128][72]  18432  V^T
 constexpr int L_TF = 53504;       // fp32 [64][65]   16640  T
 constexpr int L_T16 = 0;          // fp16 [64][72]    9216  T (after A is dead)
 constexpr int L_BETA = 70144;     // fp32 [64]
@@ -280,10 +280,11 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
             vra[r] = *reinterpret_cast<const uint2 *>(v + vbase + ca);
             vrb[r] = *reinterpret_cast<const uint2 *>(v + vbase + cb);
         }
+        // Log-decays are kept in base 2 (g log2 e), so every factor below is one exp2.
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            G[r][e] = ga[e];
-            G[r][4 + e] = gb[e];
+            G[r][e] = ga[e] * 1.4426950408889634f;
+            G[r][4 + e] = gb[e] * 1.4426950408889634f;
         }
         const uint32_t kw[4] = {ka.x, ka.y, kb2.x, kb2.y}, qw[4] = {qa.x, qa.y, qb.x, qb.y};
 #pragma unroll
@@ -319,12 +320,12 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
         for (int r = 1; r < 4; ++r) x = (rm == r) ? G[r][j] : x;
         Gm[j] = __shfl(x, (l & 48) | im, 64);
         const float gl = __shfl(G[3][j], (l & 48) | 15, 64);   // padding rows add 0
-        Em[j] = fast_exp(Gm[j]);
-        ECm[j] = fast_exp(gl - Gm[j]);
+        Em[j] = __builtin_amdgcn_exp2f(Gm[j]);
+        ECm[j] = __builtin_amdgcn_exp2f(gl - Gm[j]);
         // e^{G_C} for the state decay, written by one lane per channel group
         if (i16 == 0) {
             float *ge = reinterpret_cast<float *>(rec + REC_GE);
-            ge[(j < 4 ? ca + j : cb + j - 4)] = fast_exp(gl);
+            ge[(j < 4 ? ca + j : cb + j - 4)] = __builtin_amdgcn_exp2f(gl);
         }
     }
     float Kp[4][8];   // kept for (beta L)^T in stage 3
@@ -334,8 +335,8 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
         const int i = 16 * r + i16;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const float e1 = fast_exp(G[r][j] - Gm[j]);
-            const float e2 = fast_exp(Gm[j] - G[r][j]);
+            const float e1 = __builtin_amdgcn_exp2f(G[r][j] - Gm[j]);
+            const float e2 = __builtin_amdgcn_exp2f(Gm[j] - G[r][j]);
             const float kp = kf[r][j] * e1, km = kf[r][j] * e2, qp = scale * qf[r][j] * e1;
             Kp[r][j] = kp;
             hkp[j] = (_Float16)kp;
@@ -417,7 +418,9 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
     }
     lds_barrier();
 
-    // ---- stage 3: A to LDS; (beta L)^T and (beta V)^T transposed into LDS ---------
+    // ---- stage 3: A to LDS; L^T and V^T transposed into LDS --------------------------
+    // beta is applied to the columns of T in stage 6 (W = (T Diag(beta)) L and
+    // U = (T Diag(beta)) V), so L and V go to LDS unscaled.
     float *sA = reinterpret_cast<float *>(smem + L_A);
     _Float16 *sBL = reinterpret_cast<_Float16 *>(smem + L_BL);
     _Float16 *sBV = reinterpret_cast<_Float16 *>(smem + L_BV);
@@ -433,16 +436,14 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const int i = 16 * r + i16;
-        const bool ok = i < len;
-        const float b = ok ? sBeta[i] : 0.f;
+        const int i = 16 * r + i16;   // rows past the end hold zeros (masked loads)
         const uint32_t vw[4] = {vra[r].x, vra[r].y, vrb[r].x, vrb[r].y};
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int cc = j < 4 ? ca + j : cb + j - 4;
-            sBL[cc * TP + i] = (_Float16)(b * Kp[r][j] * Em[j]);
+            sBL[cc * TP + i] = (_Float16)(Kp[r][j] * Em[j]);
             const float vv = bf((j & 1) ? (vw[j >> 1] >> 16) : (vw[j >> 1] & 0xffff));
-            sBV[cc * TP + i] = (_Float16)(b * vv);
+            sBV[cc * TP + i] = (_Float16)vv;
         }
     }
     lds_barrier();
@@ -474,11 +475,11 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
     }
     lds_barrier();
 
-    // ---- stage 6: T to fp16, then W^T = (beta L)^T T^T and U = T (beta V) -----------
+    // ---- stage 6: T Diag(beta) to fp16, then W^T = L^T (T B)^T and U = (T B) V -------
     _Float16 *sT16 = reinterpret_cast<_Float16 *>(smem + L_T16);
     for (int e = tid; e < C * C; e += 256) {
         const int i = e >> 6, jj = e & 63;
-        sT16[i * TP + jj] = (_Float16)((jj <= i) ? sTf[i * AP + jj] : 0.f);
+        sT16[i * TP + jj] = (_Float16)((jj <= i) ? sTf[i * AP + jj] * sBeta[jj] : 0.f);
     }
     lds_barrier();
 #pragma unroll
