@@ -212,6 +212,52 @@ def test_strong_decay_within_documented_range():
     check_prefill(inp, 64)
 
 
+# ---------------------------------------------------------------- degenerate cases of the method
+def test_no_decay_is_deltanet():
+    """a = 1 (g = 0): the delta rule without forgetting, through the same kernels."""
+    inp = small(T=300, H=2)
+    inp["g"] = torch.zeros_like(inp["g"])
+    check_prefill(inp, 64)
+
+
+def test_scalar_gate_per_head():
+    """One decay value shared by every channel of a head (a scalar gate)."""
+    inp = small(T=300, H=2, B=2)
+    inp["g"] = inp["g"][..., :1].expand_as(inp["g"]).contiguous()
+    check_prefill(inp, 64)
+
+
+def test_zero_beta_is_pure_decay():
+    """beta = 0: no writes, so S_T = Diag(e^{sum g}) S_0 and o_t reads the decayed S_0."""
+    inp = small(T=200, H=2)
+    inp["beta"] = torch.zeros_like(inp["beta"])
+    check_prefill(inp, 64)
+    _, fs = gpu_prefill(inp, 64)
+    decay = np.exp(W.to64(inp["g"])[0].sum(axis=0))        # [H, d_k]
+    expect = decay[:, :, None] * W.to64(inp["initial_state"])[0]
+    assert rel_err(fs[0], expect) <= TOL["bf16"]
+
+
+def test_zero_keys_leave_state_decaying_only():
+    """k = 0 on every token: A, W, U's coupling and every write vanish."""
+    inp = small(T=130, H=2)
+    inp["k"] = torch.zeros_like(inp["k"])
+    check_prefill(inp, 64)
+
+
+# ---------------------------------------------------------------- shapes
+@pytest.mark.parametrize("H,B,T", [(5, 2, 300), (1, 1, 64), (3, 4, 1), (12, 1, 513)])
+def test_head_and_batch_shapes(H, B, T):
+    """Head counts that do not fill the inter kernel's groups of 8 pairs, single
+    tokens, and rows that are exactly one chunk."""
+    check_prefill(small(H=H, B=B, T=T), 64)
+
+
+def test_many_short_packed_sequences():
+    lengths = np.random.default_rng(77).integers(0, 150, size=40).tolist()
+    check_prefill(small(H=3, lengths=lengths), 64)
+
+
 # ---------------------------------------------------------------- fp32 path
 @pytest.mark.parametrize("d,C,T", [(16, 16, 64), (16, 32, 77), (16, 64, 130), (32, 16, 50),
                                    (32, 32, 96), (32, 64, 150), (64, 16, 40), (64, 64, 129)])
