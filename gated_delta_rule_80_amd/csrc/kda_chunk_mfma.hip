@@ -714,13 +714,21 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
             load_wu(buf[j], rec, t, l, vt0);
             load_kg(buf[j], rec, t, l);
         }
-        for (int c = cs; c < ce; c += PF) {
+        // Whole groups of PF chunks run without per-step conditions, so the
+        // compiler's wait counts see the same load sequence on every path and
+        // wait only for the ring slot in use; the last < PF chunks follow.
+        int c = cs;
+        for (; c + PF <= ce; c += PF) {
 #pragma unroll
             for (int j = 0; j < PF; ++j)
-                if (c + j < ce)
-                    state_step(S, buf[j], sS, sZ, t, l, vt0,
-                               rbase + (size_t)min(c + j + PF, clast) * REC_BYTES);
+                state_step(S, buf[j], sS, sZ, t, l, vt0,
+                           rbase + (size_t)min(c + j + PF, clast) * REC_BYTES);
         }
+#pragma unroll
+        for (int j = 0; j < PF - 1; ++j)
+            if (c + j < ce)
+                state_step(S, buf[j], sS, sZ, t, l, vt0,
+                           rbase + (size_t)min(c + j + PF, clast) * REC_BYTES);
         if (s_out) {
 #pragma unroll
             for (int cl = 0; cl < 2; ++cl)
@@ -739,15 +747,18 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
             load_q(buf[j], rec, t, l);
             load_h(buf[j], rec, t, l);
         }
-        for (int c = cs; c < ce; c += PF) {
+        int c = cs;
+        for (; c + PF <= ce; c += PF) {
 #pragma unroll
             for (int j = 0; j < PF; ++j)
-                if (c + j < ce) {
-                    const Chunk ch = chunk_at(c + j, table, row_len, ncr);
-                    output_step(buf[j], sS, sZ, ch, H, h, t, l, vt0,
-                                rbase + (size_t)min(c + j + PF, clast) * REC_BYTES, o);
-                }
+                output_step(buf[j], sS, sZ, chunk_at(c + j, table, row_len, ncr), H, h, t, l,
+                            vt0, rbase + (size_t)min(c + j + PF, clast) * REC_BYTES, o);
         }
+#pragma unroll
+        for (int j = 0; j < PF - 1; ++j)
+            if (c + j < ce)
+                output_step(buf[j], sS, sZ, chunk_at(c + j, table, row_len, ncr), H, h, t, l,
+                            vt0, rbase + (size_t)min(c + j + PF, clast) * REC_BYTES, o);
     } else if (L2D > 0) {
         // Prefetch wave: touches this tile's share of the 128-byte lines of the
         // record L2D chunks ahead, so that the record sits in L2 when the other
@@ -772,20 +783,24 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
         for (int j = 0; j < L2R; ++j)
 #pragma unroll
             for (int i = 0; i < NLD; ++i) ring[j][i] = 0;
-        for (int c = cs; c < ce; c += L2R) {
+        auto touch = [&](int j, int cc) {
+            lds_barrier();
+            const uint8_t *rec = rbase + (size_t)min(cc + L2D, clast) * REC_BYTES;
 #pragma unroll
-            for (int j = 0; j < L2R; ++j)
-                if (c + j < ce) {
-                    lds_barrier();
-                    const uint8_t *rec = rbase + (size_t)min(c + j + L2D, clast) * REC_BYTES;
+            for (int i = 0; i < NLD; ++i) {
+                asm volatile("" ::"v"(ring[j][i]));
+                ring[j][i] = *reinterpret_cast<const uint32_t *>(rec + lofs[i]);
+            }
+            lds_barrier();
+        };
+        int c = cs;
+        for (; c + L2R <= ce; c += L2R) {
 #pragma unroll
-                    for (int i = 0; i < NLD; ++i) {
-                        asm volatile("" ::"v"(ring[j][i]));
-                        ring[j][i] = *reinterpret_cast<const uint32_t *>(rec + lofs[i]);
-                    }
-                    lds_barrier();
-                }
+            for (int j = 0; j < L2R; ++j) touch(j, c + j);
         }
+#pragma unroll
+        for (int j = 0; j < L2R - 1; ++j)
+            if (c + j < ce) touch(j, c + j);
 #pragma unroll
         for (int j = 0; j < L2R; ++j)
 #pragma unroll
