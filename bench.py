@@ -37,6 +37,13 @@ def prefill_alg_bytes(T_total, H, dk, dv, n_seqs, has_s0=True):
     return T_total * H * per_th + state * (2 if has_s0 else 1)
 
 
+def scalar_gate_alg_bytes(T_total, H, dk, dv, n_seqs, has_s0=True):
+    """As prefill_alg_bytes with one fp32 log-decay per (token, head)."""
+    per_th = 2 * dk + 2 * dk + 2 * dv + 4 + 4 + 2 * dv
+    state = n_seqs * H * dk * dv * 4
+    return T_total * H * per_th + state * (2 if has_s0 else 1)
+
+
 def prefill_alg_flops(T_total, H, C, d):
     """Dense chunk contractions per token-head: A, H, W, U, H Z (C^2 d terms)
     and W S, Qbar S, Ktil^T Z (C d^2 terms): 2 (5 C d + 3 d^2)."""
@@ -86,6 +93,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=32768)
     ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--skip-scalar-gate", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="finally run a plain device copy kernel over this many MiB three times: "
                          "the known-size reference for hardware byte counters")
@@ -214,6 +222,41 @@ def main():
                          "alg_bytes_per_launch": dbytes},
         }
         del state, toks
+
+    if not args.skip_scalar_gate:
+        # The same long-context prefill through the scalar-gate entry point, gated
+        # by the first channel's log-decay of every (token, head).
+        gs = d["g"][..., 0].contiguous()
+        print("[bench] scalar-gate prefill", file=sys.stderr, flush=True)
+
+        def sstep():
+            K.chunk_fwd_scalar_gate(d["q"], d["k"], d["v"], gs, d["beta"], scale=d["scale"],
+                                    initial_state=d["initial_state"], chunk_size=w5.chunk,
+                                    workspace=ws, out=o, final_state=fs)
+
+        for _ in range(3):
+            sstep()
+        torch.cuda.synchronize()
+        n_s = max(1, args.steps // 2)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n_s):
+            sstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        sms = e0.elapsed_time(e1) / n_s
+        sbytes = scalar_gate_alg_bytes(T_total, H, dk, dv, N)
+        sgbs = sbytes / (sms * 1e-3) / 1e9
+        result["scalar_gate"] = {
+            "value": round(T_total / (sms * 1e-3), 1), "unit": "tokens/s",
+            "ms_per_step": round(sms, 4), "steps": n_s,
+            "config": {"workload": "long-context prefill B=1 H=32 T=131072 d=128 C=64 bf16 "
+                                   "with one log-decay per (token, head)"},
+            "roofline": {"bound": "hbm", "kernel": "kda_chunk_fwd_scalar_gate",
+                         "achieved": round(sgbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(sgbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "alg_bytes_per_launch": sbytes}}
+        del gs
 
     if not args.no_cpu_baseline:
         import numpy as np

@@ -8,6 +8,10 @@ library is missing or cannot be loaded, every call raises.
 
   chunk_fwd(q, k, v, g, beta, ...)      chunkwise prefill  -> (o, final_state)
   decode_step(q, k, v, g, beta, state)  one recurrent step -> o (state in place)
+  chunk_fwd_scalar_gate, decode_step_scalar_gate
+                                        the same with one log-decay per (token,
+                                        head) shared by all key channels, or
+                                        g=None for no decay
 """
 from __future__ import annotations
 
@@ -18,7 +22,8 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["chunk_fwd", "decode_step", "workspace_bytes", "lib", "KdaError", "LIB_PATH"]
+__all__ = ["chunk_fwd", "decode_step", "chunk_fwd_scalar_gate", "decode_step_scalar_gate",
+           "workspace_bytes", "lib", "KdaError", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
@@ -66,10 +71,14 @@ def lib():
     L.kda_chunk_fwd.restype = ctypes.c_int
     L.kda_chunk_fwd.argtypes = [ctypes.POINTER(KdaShape), vp, vp, vp, fp, fp, ctypes.c_float,
                                 fp, ip, vp, fp, vp, ctypes.c_size_t, vp]
+    L.kda_chunk_fwd_scalar_gate.restype = ctypes.c_int
+    L.kda_chunk_fwd_scalar_gate.argtypes = L.kda_chunk_fwd.argtypes
     L.kda_decode_step.restype = ctypes.c_int
     L.kda_decode_step.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                   ctypes.c_int32, ctypes.c_int, vp, vp, vp, fp, fp,
                                   ctypes.c_float, fp, vp, vp]
+    L.kda_decode_step_scalar_gate.restype = ctypes.c_int
+    L.kda_decode_step_scalar_gate.argtypes = L.kda_decode_step.argtypes
     _lib = L
     return L
 
@@ -112,30 +121,22 @@ def workspace_bytes(batch, seqlen, heads, d_k, d_v, chunk_size, num_seqs,
     return int(lib().kda_chunk_fwd_workspace_bytes(ctypes.byref(sh)))
 
 
-def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
-              beta: torch.Tensor, scale: Optional[float] = None,
-              initial_state: Optional[torch.Tensor] = None,
-              cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = 64,
-              output_final_state: bool = True, workspace: Optional[torch.Tensor] = None,
-              out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None
-              ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Chunkwise KDA prefill.
-
-    q, k: [B, T, H, d_k]; v: [B, T, H, d_v] (bf16 or fp32, same dtype);
-    g: [B, T, H, d_k] fp32 per-token log-decay; beta: [B, T, H] fp32;
-    initial_state: [N, H, d_k, d_v] fp32 or None; cu_seqlens: [N+1] int32 on
-    the device (then B == 1) or None.  Returns (o [B, T, H, d_v], final_state
-    [N, H, d_k, d_v] fp32 or None).
-    """
+def _prefill(entry, scalar_gate, q, k, v, g, beta, scale, initial_state, cu_seqlens,
+             chunk_size, output_final_state, workspace, out, final_state):
     _need(q.dim() == 4 and k.shape == q.shape and v.dim() == 4 and v.shape[:3] == q.shape[:3],
           "q, k must be [B, T, H, d_k] and v [B, T, H, d_v]")
     B, T, H, dk = q.shape
     dv = v.shape[-1]
-    _need(g.shape == q.shape and g.dtype == torch.float32, "g must be fp32 [B, T, H, d_k]")
+    if scalar_gate:
+        _need(g is None or (g.shape == (B, T, H) and g.dtype == torch.float32),
+              "g must be fp32 [B, T, H] or None")
+    else:
+        _need(g.shape == q.shape and g.dtype == torch.float32, "g must be fp32 [B, T, H, d_k]")
     _need(beta.shape == (B, T, H) and beta.dtype == torch.float32, "beta must be fp32 [B, T, H]")
     _need(q.dtype == k.dtype == v.dtype, "q, k, v must share one dtype")
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
-        _need(t.is_cuda and t.is_contiguous(), "%s must be a contiguous device tensor" % name)
+        _need(t is None or (t.is_cuda and t.is_contiguous()),
+              "%s must be a contiguous device tensor" % name)
     code = _dtype_code(q)
     if cu_seqlens is not None:
         _need(cu_seqlens.dtype == torch.int32 and cu_seqlens.is_cuda and cu_seqlens.dim() == 1,
@@ -158,37 +159,92 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     if output_final_state:
         fs = final_state if final_state is not None else torch.empty(
             (N, H, dk, dv), dtype=torch.float32, device=q.device)
-    st = lib().kda_chunk_fwd(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                             ctypes.c_float(scale), _ptr(initial_state), _ptr(cu_seqlens),
-                             _ptr(o), _ptr(fs), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
-                             _stream())
+    st = entry(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+               ctypes.c_float(scale), _ptr(initial_state), _ptr(cu_seqlens), _ptr(o), _ptr(fs),
+               _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream())
     _check(st)
     return o, fs
 
 
-def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
-                beta: torch.Tensor, state: torch.Tensor, scale: Optional[float] = None,
-                out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """One recurrent KDA step; ``state`` [N, H, d_k, d_v] fp32 is updated in place.
+def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+              beta: torch.Tensor, scale: Optional[float] = None,
+              initial_state: Optional[torch.Tensor] = None,
+              cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = 64,
+              output_final_state: bool = True, workspace: Optional[torch.Tensor] = None,
+              out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None
+              ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunkwise KDA prefill (``kda_chunk_fwd``).
 
-    q, k: [N, H, d_k]; v: [N, H, d_v] (bf16 or fp32); g: [N, H, d_k] fp32;
-    beta: [N, H] fp32.  Returns o [N, H, d_v] in the dtype of v.
+    q, k: [B, T, H, d_k]; v: [B, T, H, d_v] (bf16 or fp32, same dtype);
+    g: [B, T, H, d_k] fp32 per-token log-decay; beta: [B, T, H] fp32;
+    initial_state: [N, H, d_k, d_v] fp32 or None; cu_seqlens: [N+1] int32 on
+    the device (then B == 1) or None.  Returns (o [B, T, H, d_v], final_state
+    [N, H, d_k, d_v] fp32 or None).
     """
+    return _prefill(lib().kda_chunk_fwd, False, q, k, v, g, beta, scale, initial_state,
+                    cu_seqlens, chunk_size, output_final_state, workspace, out, final_state)
+
+
+def chunk_fwd_scalar_gate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                          g: Optional[torch.Tensor], beta: torch.Tensor,
+                          scale: Optional[float] = None,
+                          initial_state: Optional[torch.Tensor] = None,
+                          cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = 64,
+                          output_final_state: bool = True,
+                          workspace: Optional[torch.Tensor] = None,
+                          out: Optional[torch.Tensor] = None,
+                          final_state: Optional[torch.Tensor] = None
+                          ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunkwise prefill with a scalar gate (``kda_chunk_fwd_scalar_gate``):
+    g is [B, T, H] fp32, one log-decay per (token, head) for all key channels,
+    or None for no decay.  Everything else as ``chunk_fwd``."""
+    return _prefill(lib().kda_chunk_fwd_scalar_gate, True, q, k, v, g, beta, scale,
+                    initial_state, cu_seqlens, chunk_size, output_final_state, workspace, out,
+                    final_state)
+
+
+def _decode(entry, scalar_gate, q, k, v, g, beta, state, scale, out):
     _need(q.dim() == 3 and k.shape == q.shape and v.dim() == 3 and v.shape[:2] == q.shape[:2],
           "q, k must be [N, H, d_k] and v [N, H, d_v]")
     N, H, dk = q.shape
     dv = v.shape[-1]
-    _need(g.shape == q.shape and g.dtype == torch.float32, "g must be fp32 [N, H, d_k]")
+    if scalar_gate:
+        _need(g is None or (g.shape == (N, H) and g.dtype == torch.float32),
+              "g must be fp32 [N, H] or None")
+    else:
+        _need(g.shape == q.shape and g.dtype == torch.float32, "g must be fp32 [N, H, d_k]")
     _need(beta.shape == (N, H) and beta.dtype == torch.float32, "beta must be fp32 [N, H]")
     _need(state.shape == (N, H, dk, dv) and state.dtype == torch.float32,
           "state must be fp32 [N, H, d_k, d_v]")
     _need(q.dtype == k.dtype == v.dtype, "q, k, v must share one dtype")
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("state", state)):
-        _need(t.is_cuda and t.is_contiguous(), "%s must be a contiguous device tensor" % name)
+        _need(t is None or (t.is_cuda and t.is_contiguous()),
+              "%s must be a contiguous device tensor" % name)
     code = _dtype_code(q)
     scale = 1.0 / math.sqrt(dk) if scale is None else float(scale)
     o = out if out is not None else torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
-    st = lib().kda_decode_step(N, H, dk, dv, code, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                               ctypes.c_float(scale), _ptr(state), _ptr(o), _stream())
+    st = entry(N, H, dk, dv, code, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+               ctypes.c_float(scale), _ptr(state), _ptr(o), _stream())
     _check(st)
     return o
+
+
+def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                beta: torch.Tensor, state: torch.Tensor, scale: Optional[float] = None,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One recurrent KDA step (``kda_decode_step``); ``state`` [N, H, d_k, d_v]
+    fp32 is updated in place.
+
+    q, k: [N, H, d_k]; v: [N, H, d_v] (bf16 or fp32); g: [N, H, d_k] fp32;
+    beta: [N, H] fp32.  Returns o [N, H, d_v] in the dtype of v.
+    """
+    return _decode(lib().kda_decode_step, False, q, k, v, g, beta, state, scale, out)
+
+
+def decode_step_scalar_gate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                            g: Optional[torch.Tensor], beta: torch.Tensor, state: torch.Tensor,
+                            scale: Optional[float] = None,
+                            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One recurrent step with a scalar gate (``kda_decode_step_scalar_gate``):
+    g is [N, H] fp32 or None for no decay.  Everything else as ``decode_step``."""
+    return _decode(lib().kda_decode_step_scalar_gate, True, q, k, v, g, beta, state, scale, out)

@@ -69,6 +69,116 @@ size_t workspace_for(const kda_shape *s, int64_t total) {
     return kda::f32_workspace_bytes(total, s->num_seqs, s->num_heads, s->chunk_size);
 }
 
+// Shared body of the two prefill entry points.  With Gate::PerChannel, g is
+// [B, T, H, d_k] and required; with Gate::Scalar it is [B, T, H] and NULL
+// means no decay (Gate::None).
+kda_status chunk_fwd(kda::Gate gate, const kda_shape *shape, const void *q, const void *k,
+                     const void *v, const float *g, const float *beta, float scale,
+                     const float *initial_state, const int32_t *cu_seqlens, void *o,
+                     float *final_state, void *workspace, size_t workspace_bytes, void *stream) {
+    g_last_error[0] = '\0';
+    if (gate == kda::Gate::Scalar && !g) gate = kda::Gate::None;
+    const bool varlen = cu_seqlens != nullptr;
+    int64_t total = 0;
+    kda_status st = check_shape(shape, &total);
+    if (st != KDA_OK) return st;
+    if (varlen && shape->batch != 1)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens needs batch == 1 (got %d)",
+                    shape->batch);
+    if (!varlen && shape->num_seqs != shape->batch)
+        return fail(KDA_ERR_INVALID_ARGUMENT,
+                    "without cu_seqlens num_seqs must equal batch (%d vs %d)", shape->num_seqs,
+                    shape->batch);
+    if (total > 0 && (!q || !k || !v || !beta || !o || (gate == kda::Gate::PerChannel && !g)))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "a required tensor pointer is NULL");
+    const void *g16 = gate == kda::Gate::PerChannel ? g : nullptr;
+    const void *ptrs[] = {q, k, v, g16, o, initial_state, final_state};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "tensor pointer %p is not 16-byte aligned", p);
+    if ((beta && !aligned4(beta)) || (cu_seqlens && !aligned4(cu_seqlens)) ||
+        (gate == kda::Gate::Scalar && !aligned4(g)))
+        return fail(KDA_ERR_INVALID_ARGUMENT,
+                    "beta / cu_seqlens / a scalar gate must be 4-byte aligned");
+    if (o && (o == q || o == k || o == v || (g && o == (const void *)g) ||
+              o == (const void *)beta))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "o must not alias an input");
+    const size_t need = workspace_for(shape, total);
+    if (need > 0 && !workspace)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "workspace is NULL (%zu bytes needed)", need);
+    if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+    if (workspace_bytes < need)
+        return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed",
+                    workspace_bytes, need);
+
+    kda::ChunkProblem p;
+    p.n_seqs = shape->num_seqs;
+    p.batch = shape->batch;
+    p.seqlen = shape->seqlen;
+    p.heads = shape->num_heads;
+    p.dk = shape->d_k;
+    p.dv = shape->d_v;
+    p.chunk = shape->chunk_size;
+    p.bf16 = shape->dtype == KDA_BF16;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.gate = gate;
+    p.g = gate == kda::Gate::None ? nullptr : g;
+    p.beta = beta;
+    p.scale = scale;
+    p.s0 = initial_state;
+    p.cu = cu_seqlens;
+    p.o = o;
+    p.s_final = final_state;
+    p.workspace = workspace;
+    p.workspace_bytes = workspace_bytes;
+    p.stream = static_cast<hipStream_t>(stream);
+
+    hipError_t e = kda::mfma_path_supported(p.dk, p.dv, p.chunk, p.bf16)
+                       ? kda::launch_chunk_fwd_mfma(p)
+                       : kda::launch_chunk_fwd_f32(p);
+    if (e != hipSuccess) return hip_fail(e, "chunk prefill launch");
+    return KDA_OK;
+}
+
+// Shared body of the two decode entry points (gate layouts as for chunk_fwd,
+// per pair instead of per token).
+kda_status decode_step(kda::Gate gate, int32_t num_sessions, int32_t num_heads, int32_t d_k,
+                       int32_t d_v, kda_dtype dtype, const void *q, const void *k, const void *v,
+                       const float *g, const float *beta, float scale, float *state_inout,
+                       void *o, void *stream) {
+    g_last_error[0] = '\0';
+    if (gate == kda::Gate::Scalar && !g) gate = kda::Gate::None;
+    if (dtype != KDA_F32 && dtype != KDA_BF16)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)dtype);
+    if (num_sessions <= 0 || num_heads <= 0 || d_k <= 0 || d_v <= 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "non-positive size (sessions %d heads %d d_k %d "
+                    "d_v %d)", num_sessions, num_heads, d_k, d_v);
+    if (!kda::decode_supported(d_k, d_v))
+        return fail(KDA_ERR_UNSUPPORTED, "no decode kernel for d_k %d d_v %d (built: d_k == "
+                    "d_v in {16, 32, 64, 128})", d_k, d_v);
+    const int64_t pairs = (int64_t)num_sessions * num_heads;
+    if (pairs > INT32_MAX) return fail(KDA_ERR_INVALID_ARGUMENT, "too many pairs");
+    if (!q || !k || !v || !beta || !state_inout || !o || (gate == kda::Gate::PerChannel && !g))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "a required tensor pointer is NULL");
+    const void *g16 = gate == kda::Gate::PerChannel ? g : q;
+    const void *ptrs[] = {q, k, v, g16, state_inout, o};
+    for (const void *p : ptrs)
+        if (!aligned16(p))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "tensor pointer %p is not 16-byte aligned", p);
+    if (!aligned4(beta) || (gate == kda::Gate::Scalar && !aligned4(g)))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "beta / a scalar gate must be 4-byte aligned");
+    if (o == (void *)state_inout)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "o must not alias state_inout");
+    hipError_t e = kda::launch_decode((int)pairs, d_k, d_v, dtype == KDA_BF16, gate, q, k, v,
+                                      gate == kda::Gate::None ? nullptr : g, beta, scale,
+                                      state_inout, o, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "decode step launch");
+    return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -103,97 +213,35 @@ kda_status kda_chunk_fwd(const kda_shape *shape, const void *q, const void *k, c
                          const float *initial_state, const int32_t *cu_seqlens, void *o,
                          float *final_state, void *workspace, size_t workspace_bytes,
                          void *stream) {
-    g_last_error[0] = '\0';
-    const bool varlen = cu_seqlens != nullptr;
-    int64_t total = 0;
-    kda_status st = check_shape(shape, &total);
-    if (st != KDA_OK) return st;
-    if (varlen && shape->batch != 1)
-        return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens needs batch == 1 (got %d)",
-                    shape->batch);
-    if (!varlen && shape->num_seqs != shape->batch)
-        return fail(KDA_ERR_INVALID_ARGUMENT,
-                    "without cu_seqlens num_seqs must equal batch (%d vs %d)", shape->num_seqs,
-                    shape->batch);
-    if (total > 0 && (!q || !k || !v || !g_log_decay || !beta || !o))
-        return fail(KDA_ERR_INVALID_ARGUMENT, "a required tensor pointer is NULL");
-    const void *ptrs[] = {q, k, v, g_log_decay, o, initial_state, final_state};
-    for (const void *p : ptrs)
-        if (p && !aligned16(p))
-            return fail(KDA_ERR_INVALID_ARGUMENT, "tensor pointer %p is not 16-byte aligned", p);
-    if ((beta && !aligned4(beta)) || (cu_seqlens && !aligned4(cu_seqlens)))
-        return fail(KDA_ERR_INVALID_ARGUMENT, "beta / cu_seqlens must be 4-byte aligned");
-    if (o && (o == q || o == k || o == v || o == (const void *)g_log_decay ||
-              o == (const void *)beta))
-        return fail(KDA_ERR_INVALID_ARGUMENT, "o must not alias an input");
-    const size_t need = workspace_for(shape, total);
-    if (need > 0 && !workspace)
-        return fail(KDA_ERR_INVALID_ARGUMENT, "workspace is NULL (%zu bytes needed)", need);
-    if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u))
-        return fail(KDA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
-    if (workspace_bytes < need)
-        return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed",
-                    workspace_bytes, need);
+    return chunk_fwd(kda::Gate::PerChannel, shape, q, k, v, g_log_decay, beta, scale,
+                     initial_state, cu_seqlens, o, final_state, workspace, workspace_bytes,
+                     stream);
+}
 
-    kda::ChunkProblem p;
-    p.n_seqs = shape->num_seqs;
-    p.batch = shape->batch;
-    p.seqlen = shape->seqlen;
-    p.heads = shape->num_heads;
-    p.dk = shape->d_k;
-    p.dv = shape->d_v;
-    p.chunk = shape->chunk_size;
-    p.bf16 = shape->dtype == KDA_BF16;
-    p.q = q;
-    p.k = k;
-    p.v = v;
-    p.g = g_log_decay;
-    p.beta = beta;
-    p.scale = scale;
-    p.s0 = initial_state;
-    p.cu = cu_seqlens;
-    p.o = o;
-    p.s_final = final_state;
-    p.workspace = workspace;
-    p.workspace_bytes = workspace_bytes;
-    p.stream = static_cast<hipStream_t>(stream);
-
-    hipError_t e = kda::mfma_path_supported(p.dk, p.dv, p.chunk, p.bf16)
-                       ? kda::launch_chunk_fwd_mfma(p)
-                       : kda::launch_chunk_fwd_f32(p);
-    if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd launch");
-    return KDA_OK;
+kda_status kda_chunk_fwd_scalar_gate(const kda_shape *shape, const void *q, const void *k,
+                                     const void *v, const float *g_log_decay, const float *beta,
+                                     float scale, const float *initial_state,
+                                     const int32_t *cu_seqlens, void *o, float *final_state,
+                                     void *workspace, size_t workspace_bytes, void *stream) {
+    return chunk_fwd(kda::Gate::Scalar, shape, q, k, v, g_log_decay, beta, scale, initial_state,
+                     cu_seqlens, o, final_state, workspace, workspace_bytes, stream);
 }
 
 kda_status kda_decode_step(int32_t num_sessions, int32_t num_heads, int32_t d_k, int32_t d_v,
                            kda_dtype dtype, const void *q, const void *k, const void *v,
                            const float *g, const float *beta, float scale, float *state_inout,
                            void *o, void *stream) {
-    g_last_error[0] = '\0';
-    if (dtype != KDA_F32 && dtype != KDA_BF16)
-        return fail(KDA_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)dtype);
-    if (num_sessions <= 0 || num_heads <= 0 || d_k <= 0 || d_v <= 0)
-        return fail(KDA_ERR_INVALID_ARGUMENT, "non-positive size (sessions %d heads %d d_k %d "
-                    "d_v %d)", num_sessions, num_heads, d_k, d_v);
-    if (!kda::decode_supported(d_k, d_v))
-        return fail(KDA_ERR_UNSUPPORTED, "no decode kernel for d_k %d d_v %d (built: d_k == "
-                    "d_v in {16, 32, 64, 128})", d_k, d_v);
-    const int64_t pairs = (int64_t)num_sessions * num_heads;
-    if (pairs > INT32_MAX) return fail(KDA_ERR_INVALID_ARGUMENT, "too many pairs");
-    if (!q || !k || !v || !g || !beta || !state_inout || !o)
-        return fail(KDA_ERR_INVALID_ARGUMENT, "a required tensor pointer is NULL");
-    const void *ptrs[] = {q, k, v, g, state_inout, o};
-    for (const void *p : ptrs)
-        if (!aligned16(p))
-            return fail(KDA_ERR_INVALID_ARGUMENT, "tensor pointer %p is not 16-byte aligned", p);
-    if (!aligned4(beta))
-        return fail(KDA_ERR_INVALID_ARGUMENT, "beta must be 4-byte aligned");
-    if (o == (void *)state_inout)
-        return fail(KDA_ERR_INVALID_ARGUMENT, "o must not alias state_inout");
-    hipError_t e = kda::launch_decode((int)pairs, d_k, d_v, dtype == KDA_BF16, q, k, v, g, beta,
-                                      scale, state_inout, o, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "kda_decode_step launch");
-    return KDA_OK;
+    return decode_step(kda::Gate::PerChannel, num_sessions, num_heads, d_k, d_v, dtype, q, k, v,
+                       g, beta, scale, state_inout, o, stream);
+}
+
+kda_status kda_decode_step_scalar_gate(int32_t num_sessions, int32_t num_heads, int32_t d_k,
+                                       int32_t d_v, kda_dtype dtype, const void *q,
+                                       const void *k, const void *v, const float *g,
+                                       const float *beta, float scale, float *state_inout,
+                                       void *o, void *stream) {
+    return decode_step(kda::Gate::Scalar, num_sessions, num_heads, d_k, d_v, dtype, q, k, v, g,
+                       beta, scale, state_inout, o, stream);
 }
 
 }  // extern "C"

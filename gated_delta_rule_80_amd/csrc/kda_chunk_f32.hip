@@ -39,9 +39,9 @@ __host__ __device__ inline Lds lds_layout(int dk, int dv, int C) {
 
 __global__ __launch_bounds__(THREADS) void kda_chunk_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
-    const float *__restrict__ g, const float *__restrict__ beta, float scale, int H, int dk,
-    int dv, int C, int row_len, const int32_t *__restrict__ cu, const float *__restrict__ s0,
-    float *__restrict__ s_final, float *__restrict__ o) {
+    const float *__restrict__ g, int gate, const float *__restrict__ beta, float scale, int H,
+    int dk, int dv, int C, int row_len, const int32_t *__restrict__ cu,
+    const float *__restrict__ s0, float *__restrict__ s_final, float *__restrict__ o) {
     extern __shared__ float sm[];
     const Lds L = lds_layout(dk, dv, C);
     float *sq = sm + L.q, *sk = sm + L.k, *sG = sm + L.G, *sv = sm + L.v, *sb = sm + L.beta;
@@ -74,7 +74,9 @@ __global__ __launch_bounds__(THREADS) void kda_chunk_f32_kernel(
             const size_t a = ((size_t)(t0 + i) * H + h) * dk + c;
             sq[e] = ok ? q[a] : 0.f;
             sk[e] = ok ? k[a] : 0.f;
-            sG[e] = ok ? g[a] : 0.f;
+            // gate 0: log-decay per channel; 1: one per (token, head); 2: none
+            const float gv = gate == 0 ? g[a] : (gate == 1 ? g[(size_t)(t0 + i) * H + h] : 0.f);
+            sG[e] = ok ? gv : 0.f;
         }
         for (int e = tid; e < C * dv; e += THREADS) {
             const int i = e / dv, c = e - i * dv;
@@ -190,8 +192,9 @@ hipError_t launch_chunk_fwd_f32(const ChunkProblem &p) {
     }
     hipLaunchKernelGGL(kda_chunk_f32_kernel, dim3(p.n_seqs * p.heads), dim3(THREADS), lds,
                        p.stream, static_cast<const float *>(p.q), static_cast<const float *>(p.k),
-                       static_cast<const float *>(p.v), p.g, p.beta, p.scale, p.heads, p.dk, p.dv,
-                       p.chunk, p.seqlen, p.cu, p.s0, p.s_final, static_cast<float *>(p.o));
+                       static_cast<const float *>(p.v), p.g, (int)p.gate, p.beta, p.scale, p.heads,
+                       p.dk, p.dv, p.chunk, p.seqlen, p.cu, p.s0, p.s_final,
+                       static_cast<float *>(p.o));
     return hipGetLastError();
 }
 

@@ -225,7 +225,10 @@ __device__ __forceinline__ void offdiag_column(const float *sA, float *sTf, int 
 // it covers local chunk jlo + (b / H) % jn of row (b / H) / jn, so a launch can
 // produce one segment [jlo, jlo + jn) of every row.  Heads vary fastest, so the
 // 32 heads of one chunk -- which share every token row of q, k, v, g -- are
-// read together.
+// read together.  GATE says how g is laid out: [tokens, H, d_k] (one log-decay
+// per channel), [tokens, H] (one per token and head, shared by its channels) or
+// absent (no decay).
+template <Gate GATE>
 __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const float *__restrict__ g,
@@ -271,8 +274,14 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
         vra[r] = uint2{0, 0};
         vrb[r] = uint2{0, 0};
         if (ok) {
-            ga = *reinterpret_cast<const float4v *>(g + base + ca);
-            gb = *reinterpret_cast<const float4v *>(g + base + cb);
+            if constexpr (GATE == Gate::PerChannel) {
+                ga = *reinterpret_cast<const float4v *>(g + base + ca);
+                gb = *reinterpret_cast<const float4v *>(g + base + cb);
+            } else if constexpr (GATE == Gate::Scalar) {
+                const float gs = g[(size_t)(ch.t0 + i) * H + h];
+                ga = float4v{gs, gs, gs, gs};
+                gb = ga;
+            }
             ka = *reinterpret_cast<const uint2 *>(k + base + ca);
             kb2 = *reinterpret_cast<const uint2 *>(k + base + cb);
             qa = *reinterpret_cast<const uint2 *>(q + base + ca);
@@ -891,7 +900,10 @@ hipError_t launch_chunk_fwd_mfma(const ChunkProblem &p) {
     hipError_t e;
 
     auto intra = [&](hipStream_t st, int jlo, int jn, int grid) {
-        hipLaunchKernelGGL(kda_intra_kernel, dim3(grid), dim3(256), 0, st,
+        auto kern = p.gate == Gate::PerChannel ? kda_intra_kernel<Gate::PerChannel>
+                    : p.gate == Gate::Scalar   ? kda_intra_kernel<Gate::Scalar>
+                                               : kda_intra_kernel<Gate::None>;
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st,
                            static_cast<const uint16_t *>(p.q), static_cast<const uint16_t *>(p.k),
                            static_cast<const uint16_t *>(p.v), p.g, p.beta, p.scale, p.heads,
                            p.seqlen, ncr, table, off + p.n_seqs, (int)L.nc_max, jlo, jn, recs);

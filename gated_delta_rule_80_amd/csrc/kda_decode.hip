@@ -9,11 +9,15 @@
 // state is written from registers: the fp32 state crosses HBM exactly once
 // in each direction, which is the whole cost of a decode step.
 //
+// The decay is given per key channel (KDA), once per pair (a scalar gate:
+// every channel decays by the same a), or not at all (a = 1).
+//
 // Layout: one workgroup per pair; thread (rg, cq) owns the float4 column
 // quad cq of rows rg, rg + NRG, rg + 2 NRG, ...  Each wave's loads and
 // stores cover whole 512-byte state rows (fully coalesced, nontemporal: the
 // state is streamed, never re-read within a step).
 #include "kda_common.hpp"
+#include "kda_internal.hpp"
 
 namespace kda {
 
@@ -28,7 +32,7 @@ struct DecodeCfg {
     static_assert(64 % NQ == 0 || NQ % 64 == 0, "column quads per wave");
 };
 
-template <int DK, int DV, typename T>
+template <int DK, int DV, typename T, Gate GATE>
 __global__ __launch_bounds__((DecodeCfg<DK, DV>::THREADS)) void kda_decode_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, float scale,
@@ -58,7 +62,9 @@ __global__ __launch_bounds__((DecodeCfg<DK, DV>::THREADS)) void kda_decode_kerne
     for (int i = tid; i < DK; i += THREADS) {
         const size_t gi = pair * DK + i;
         float kk = io<T>::load(k, gi), sq = scale * io<T>::load(q, gi);
-        s_a[i] = fast_exp(g[gi]);
+        s_a[i] = GATE == Gate::PerChannel ? fast_exp(g[gi])
+                 : GATE == Gate::Scalar   ? fast_exp(g[pair])
+                                          : 1.f;
         s_k[i] = kk;
         s_sq[i] = sq;
         kq += kk * sq;
@@ -122,27 +128,45 @@ __global__ __launch_bounds__((DecodeCfg<DK, DV>::THREADS)) void kda_decode_kerne
     }
 }
 
-template <int DK, int DV, typename T>
-static hipError_t launch_decode_t(int n_pairs, const void *q, const void *k, const void *v,
+template <int DK, int DV, typename T, Gate GATE>
+static hipError_t launch_decode_g(int n_pairs, const void *q, const void *k, const void *v,
                                   const float *g, const float *beta, float scale, float *state,
                                   void *o, hipStream_t stream) {
     using Cfg = DecodeCfg<DK, DV>;
-    hipLaunchKernelGGL((kda_decode_kernel<DK, DV, T>), dim3(n_pairs), dim3(Cfg::THREADS), 0,
-                       stream, static_cast<const T *>(q), static_cast<const T *>(k),
+    hipLaunchKernelGGL((kda_decode_kernel<DK, DV, T, GATE>), dim3(n_pairs), dim3(Cfg::THREADS),
+                       0, stream, static_cast<const T *>(q), static_cast<const T *>(k),
                        static_cast<const T *>(v), g, beta, scale, state, static_cast<T *>(o));
     return hipGetLastError();
 }
 
+template <int DK, int DV, typename T>
+static hipError_t launch_decode_t(Gate gate, int n_pairs, const void *q, const void *k,
+                                  const void *v, const float *g, const float *beta, float scale,
+                                  float *state, void *o, hipStream_t stream) {
+    switch (gate) {
+    case Gate::PerChannel:
+        return launch_decode_g<DK, DV, T, Gate::PerChannel>(n_pairs, q, k, v, g, beta, scale,
+                                                            state, o, stream);
+    case Gate::Scalar:
+        return launch_decode_g<DK, DV, T, Gate::Scalar>(n_pairs, q, k, v, g, beta, scale, state,
+                                                        o, stream);
+    case Gate::None:
+        return launch_decode_g<DK, DV, T, Gate::None>(n_pairs, q, k, v, g, beta, scale, state, o,
+                                                      stream);
+    }
+    return hipErrorInvalidValue;
+}
+
 // Returns hipErrorInvalidValue for a (d_k, d_v) that is not instantiated.
-hipError_t launch_decode(int n_pairs, int dk, int dv, bool bf16, const void *q, const void *k,
-                         const void *v, const float *g, const float *beta, float scale,
-                         float *state, void *o, hipStream_t stream) {
+hipError_t launch_decode(int n_pairs, int dk, int dv, bool bf16, Gate gate, const void *q,
+                         const void *k, const void *v, const float *g, const float *beta,
+                         float scale, float *state, void *o, hipStream_t stream) {
 #define KDA_DECODE_CASE(D)                                                                   \
     if (dk == D && dv == D)                                                                  \
-        return bf16 ? launch_decode_t<D, D, bf16_t>(n_pairs, q, k, v, g, beta, scale, state, \
-                                                    o, stream)                               \
-                    : launch_decode_t<D, D, float>(n_pairs, q, k, v, g, beta, scale, state,  \
-                                                   o, stream);
+        return bf16 ? launch_decode_t<D, D, bf16_t>(gate, n_pairs, q, k, v, g, beta, scale,  \
+                                                    state, o, stream)                        \
+                    : launch_decode_t<D, D, float>(gate, n_pairs, q, k, v, g, beta, scale,   \
+                                                   state, o, stream);
     KDA_DECODE_CASE(128)
     KDA_DECODE_CASE(64)
     KDA_DECODE_CASE(32)

@@ -8,11 +8,16 @@
 
 namespace kda {
 
+// How the per-token decay a_t = exp(g_t) is given: one log-decay per key
+// channel (KDA), one per (token, head) shared by all channels (a scalar gate,
+// as in Gated DeltaNet), or none (a_t = 1: DeltaNet).
+enum class Gate : int { PerChannel = 0, Scalar = 1, None = 2 };
+
 // ---- decode -----------------------------------------------------------------
 bool decode_supported(int dk, int dv);
-hipError_t launch_decode(int n_pairs, int dk, int dv, bool bf16, const void *q, const void *k,
-                         const void *v, const float *g, const float *beta, float scale,
-                         float *state, void *o, hipStream_t stream);
+hipError_t launch_decode(int n_pairs, int dk, int dv, bool bf16, Gate gate, const void *q,
+                         const void *k, const void *v, const float *g, const float *beta,
+                         float scale, float *state, void *o, hipStream_t stream);
 
 // ---- chunked prefill ----------------------------------------------------------
 // Everything a prefill launch needs, already validated by the C ABI layer.
@@ -24,6 +29,7 @@ struct ChunkProblem {
     int dk, dv, chunk; // d_k, d_v, C
     bool bf16;         // storage type of q, k, v, o
     const void *q, *k, *v;
+    Gate gate;             // layout of g (null when gate == Gate::None)
     const float *g, *beta;
     float scale;
     const float *s0;       // may be null (zeros)

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 typedef enum kda_status {
     KDA_OK = 0,
@@ -143,6 +143,31 @@ kda_status kda_chunk_fwd(const kda_shape *shape, const void *q, const void *k,
                          size_t workspace_bytes, void *stream);
 
 /*
+ * The same prefill with a scalar gate: one log-decay per (token, head), shared
+ * by every key channel of the head, i.e. Diag(a_t) = a_t I.  This is the
+ * coarser gate that "Understanding Kimi Delta Attention", section "Learning
+ * what to forget", contrasts with KDA's per-channel one (the gate of Gated
+ * DeltaNet); with no gate at all (a_t = 1) the operator is the plain delta
+ * rule of the sections before it (DeltaNet).
+ *
+ *   g_log_decay   [B, T, H] fp32 per-token log a_t (<= 0), not cumulative, or
+ *                 NULL for a_t = 1.  4-byte aligned.
+ * Every other argument, the workspace (kda_chunk_fwd_workspace_bytes, same
+ * shape), the built combinations, the decay range and the alignment rules are
+ * those of kda_chunk_fwd.  The kernels are the same ones; only the gate is
+ * read differently, so a scalar gate g gives bit-for-bit the result of
+ * kda_chunk_fwd with g repeated over the d_k channels.
+ */
+kda_status kda_chunk_fwd_scalar_gate(const kda_shape *shape, const void *q,
+                                     const void *k, const void *v,
+                                     const float *g_log_decay,
+                                     const float *beta, float scale,
+                                     const float *initial_state,
+                                     const int32_t *cu_seqlens, void *o,
+                                     float *final_state, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
+/*
  * One recurrent decode step for num_sessions x num_heads independent pairs
  * ("Understanding Kimi Delta Attention", box "KDA: retain, predict, correct";
  * the fixed-size state is what a decode step reads and rewrites).
@@ -161,6 +186,20 @@ kda_status kda_decode_step(int32_t num_sessions, int32_t num_heads, int32_t d_k,
                            const void *k, const void *v, const float *g,
                            const float *beta, float scale, float *state_inout,
                            void *o, void *stream);
+
+/*
+ * kda_decode_step with a scalar gate (see kda_chunk_fwd_scalar_gate):
+ *   g             [N, H] fp32 log a (<= 0), one per pair, or NULL for a = 1.
+ *                 4-byte aligned.
+ * Everything else as kda_decode_step.
+ */
+kda_status kda_decode_step_scalar_gate(int32_t num_sessions, int32_t num_heads,
+                                       int32_t d_k, int32_t d_v, kda_dtype dtype,
+                                       const void *q, const void *k,
+                                       const void *v, const float *g,
+                                       const float *beta, float scale,
+                                       float *state_inout, void *o,
+                                       void *stream);
 
 #ifdef __cplusplus
 }

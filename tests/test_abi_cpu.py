@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = K.lib()
-    assert lib.kda_abi_version() == 1
+    assert lib.kda_abi_version() == 2
     for code, name in K.STATUS.items():
         assert lib.kda_status_string(code).decode() == name
 
@@ -131,3 +131,41 @@ def test_binding_refuses_host_tensors():
     q = torch.zeros(1, 64, 1, 16)
     with pytest.raises(ValueError):
         K.chunk_fwd(q, q, q, q.float(), torch.zeros(1, 64, 1), chunk_size=16)
+
+
+def call_chunk_sg(sh, **over):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, scale=ctypes.c_float(0.1), s0=None,
+                cu=None, o=ctypes.c_void_p(0x200000), fs=None, ws=ctypes.c_void_p(0x300000),
+                wsb=ctypes.c_size_t(1 << 40), stream=None)
+    args.update(over)
+    return K.lib().kda_chunk_fwd_scalar_gate(
+        ctypes.byref(sh) if sh is not None else None, args["q"], args["k"], args["v"],
+        args["g"], args["beta"], args["scale"], args["s0"], args["cu"], args["o"], args["fs"],
+        args["ws"], args["wsb"], args["stream"])
+
+
+def test_scalar_gate_entry_points_validate_like_the_others():
+    lib = K.lib()
+    P, O, f = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000), ctypes.c_float(0.1)
+    assert call_chunk_sg(shape(heads=0)) == 1
+    assert call_chunk_sg(shape(d_k=96, d_v=96)) == 2
+    assert call_chunk_sg(shape(), q=None) == 1
+    assert call_chunk_sg(shape(), g=ctypes.c_void_p(0x100002)) == 1       # 4-byte alignment
+    assert b"scalar gate" in lib.kda_last_error()
+    assert call_chunk_sg(shape(), wsb=ctypes.c_size_t(1024)) == 3
+    # a NULL gate (no decay) passes validation up to the workspace check
+    assert call_chunk_sg(shape(), g=None, wsb=ctypes.c_size_t(1024)) == 3
+    # the per-channel entry still needs its gate
+    assert call_chunk(shape(), g=None) == 1
+    dsg = lib.kda_decode_step_scalar_gate
+    assert dsg(0, 32, 128, 128, K.KDA_BF16, P, P, P, P, P, f, P, O, None) == 1
+    assert dsg(4, 32, 96, 96, K.KDA_BF16, P, P, P, P, P, f, P, O, None) == 2
+    assert dsg(4, 32, 128, 128, K.KDA_BF16, P, P, P, ctypes.c_void_p(0x100001), P, f, P, O,
+               None) == 1
+    assert lib.kda_decode_step(4, 32, 128, 128, K.KDA_BF16, P, P, P, None, P, f, P, O, None) == 1
+
+
+def test_binding_scalar_gate_shape_checks():
+    q = torch.zeros(1, 64, 2, 16)
+    with pytest.raises(ValueError):     # per-channel gate shape given to the scalar entry
+        K.chunk_fwd_scalar_gate(q, q, q, q.float(), torch.zeros(1, 64, 2), chunk_size=16)
