@@ -12,6 +12,10 @@ library is missing or cannot be loaded, every call raises.
                                         the same with one log-decay per (token,
                                         head) shared by all key channels, or
                                         g=None for no decay
+  chunk_fwd_ex, decode_step_ex          any gate layout, and the layer's last
+                                        elementwise input steps (q/k L2 norm,
+                                        logit gates, logit beta) done in-kernel
+  output_rmsnorm_gate(o, gate, weight)  RMS norm x weight x sigmoid gate
 """
 from __future__ import annotations
 
@@ -23,7 +27,8 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["chunk_fwd", "decode_step", "chunk_fwd_scalar_gate", "decode_step_scalar_gate",
-           "workspace_bytes", "lib", "KdaError", "LIB_PATH"]
+           "chunk_fwd_ex", "decode_step_ex", "output_rmsnorm_gate", "workspace_bytes", "lib",
+           "KdaError", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
@@ -46,6 +51,14 @@ class KdaShape(ctypes.Structure):
                 ("d_v", ctypes.c_int32), ("chunk_size", ctypes.c_int32),
                 ("num_seqs", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
+
+class KdaInputsForm(ctypes.Structure):
+    _fields_ = [("gate_layout", ctypes.c_int32), ("gate_is_logit", ctypes.c_int32),
+                ("beta_is_logit", ctypes.c_int32), ("l2norm_qk", ctypes.c_int32),
+                ("eps", ctypes.c_float)]
+
+
+GATE_LAYOUTS = {"per_channel": 0, "scalar": 1, "none": 2}
 
 _lib = None
 
@@ -79,6 +92,17 @@ def lib():
                                   ctypes.c_float, fp, vp, vp]
     L.kda_decode_step_scalar_gate.restype = ctypes.c_int
     L.kda_decode_step_scalar_gate.argtypes = L.kda_decode_step.argtypes
+    L.kda_chunk_fwd_ex.restype = ctypes.c_int
+    L.kda_chunk_fwd_ex.argtypes = [ctypes.POINTER(KdaShape), ctypes.POINTER(KdaInputsForm), vp, vp,
+                                   vp, fp, fp, ctypes.c_float, fp, ip, vp, fp, vp, ctypes.c_size_t,
+                                   vp]
+    L.kda_decode_step_ex.restype = ctypes.c_int
+    L.kda_decode_step_ex.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_int32, ctypes.c_int, ctypes.POINTER(KdaInputsForm),
+                                     vp, vp, vp, fp, fp, ctypes.c_float, fp, vp, vp]
+    L.kda_output_rmsnorm_gate.restype = ctypes.c_int
+    L.kda_output_rmsnorm_gate.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int, vp, vp, fp,
+                                          ctypes.c_float, vp, vp]
     _lib = L
     return L
 
@@ -121,17 +145,20 @@ def workspace_bytes(batch, seqlen, heads, d_k, d_v, chunk_size, num_seqs,
     return int(lib().kda_chunk_fwd_workspace_bytes(ctypes.byref(sh)))
 
 
-def _prefill(entry, scalar_gate, q, k, v, g, beta, scale, initial_state, cu_seqlens,
-             chunk_size, output_final_state, workspace, out, final_state):
+def _prefill(entry, gate, q, k, v, g, beta, scale, initial_state, cu_seqlens,
+             chunk_size, output_final_state, workspace, out, final_state, form=None):
     _need(q.dim() == 4 and k.shape == q.shape and v.dim() == 4 and v.shape[:3] == q.shape[:3],
           "q, k must be [B, T, H, d_k] and v [B, T, H, d_v]")
     B, T, H, dk = q.shape
     dv = v.shape[-1]
-    if scalar_gate:
+    if gate == "scalar":
         _need(g is None or (g.shape == (B, T, H) and g.dtype == torch.float32),
               "g must be fp32 [B, T, H] or None")
+    elif gate == "none":
+        _need(g is None, "g must be None without a gate")
     else:
-        _need(g.shape == q.shape and g.dtype == torch.float32, "g must be fp32 [B, T, H, d_k]")
+        _need(g is not None and g.shape == q.shape and g.dtype == torch.float32,
+              "g must be fp32 [B, T, H, d_k]")
     _need(beta.shape == (B, T, H) and beta.dtype == torch.float32, "beta must be fp32 [B, T, H]")
     _need(q.dtype == k.dtype == v.dtype, "q, k, v must share one dtype")
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
@@ -159,7 +186,8 @@ def _prefill(entry, scalar_gate, q, k, v, g, beta, scale, initial_state, cu_seql
     if output_final_state:
         fs = final_state if final_state is not None else torch.empty(
             (N, H, dk, dv), dtype=torch.float32, device=q.device)
-    st = entry(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+    extra = () if form is None else (ctypes.byref(form),)
+    st = entry(ctypes.byref(sh), *extra, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                ctypes.c_float(scale), _ptr(initial_state), _ptr(cu_seqlens), _ptr(o), _ptr(fs),
                _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream())
     _check(st)
@@ -181,7 +209,7 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     the device (then B == 1) or None.  Returns (o [B, T, H, d_v], final_state
     [N, H, d_k, d_v] fp32 or None).
     """
-    return _prefill(lib().kda_chunk_fwd, False, q, k, v, g, beta, scale, initial_state,
+    return _prefill(lib().kda_chunk_fwd, "per_channel", q, k, v, g, beta, scale, initial_state,
                     cu_seqlens, chunk_size, output_final_state, workspace, out, final_state)
 
 
@@ -198,21 +226,51 @@ def chunk_fwd_scalar_gate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     """Chunkwise prefill with a scalar gate (``kda_chunk_fwd_scalar_gate``):
     g is [B, T, H] fp32, one log-decay per (token, head) for all key channels,
     or None for no decay.  Everything else as ``chunk_fwd``."""
-    return _prefill(lib().kda_chunk_fwd_scalar_gate, True, q, k, v, g, beta, scale,
+    return _prefill(lib().kda_chunk_fwd_scalar_gate, "scalar", q, k, v, g, beta, scale,
                     initial_state, cu_seqlens, chunk_size, output_final_state, workspace, out,
                     final_state)
 
 
-def _decode(entry, scalar_gate, q, k, v, g, beta, state, scale, out):
+def _form(gate, gate_is_logit, beta_is_logit, l2norm_qk, eps):
+    _need(gate in GATE_LAYOUTS, "gate must be one of %s" % sorted(GATE_LAYOUTS))
+    return KdaInputsForm(GATE_LAYOUTS[gate], int(bool(gate_is_logit)), int(bool(beta_is_logit)),
+                         int(bool(l2norm_qk)), float(eps))
+
+
+def chunk_fwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[torch.Tensor],
+                 beta: torch.Tensor, *, gate: str = "per_channel", gate_is_logit: bool = False,
+                 beta_is_logit: bool = False, l2norm_qk: bool = False, eps: float = 1e-6,
+                 scale: Optional[float] = None, initial_state: Optional[torch.Tensor] = None,
+                 cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = 64,
+                 output_final_state: bool = True, workspace: Optional[torch.Tensor] = None,
+                 out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None
+                 ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunkwise prefill with the inputs in a stated form (``kda_chunk_fwd_ex``).
+
+    gate: "per_channel" (g [B, T, H, d_k]), "scalar" (g [B, T, H]) or "none"
+    (g None).  gate_is_logit: g holds logits x and log a = log sigmoid(x).
+    beta_is_logit: beta = sigmoid(beta).  l2norm_qk: q and k are divided by
+    sqrt(sum of squares + eps) per (token, head) inside the kernel.
+    """
+    f = _form(gate, gate_is_logit, beta_is_logit, l2norm_qk, eps)
+    return _prefill(lib().kda_chunk_fwd_ex, gate, q, k, v, g, beta, scale, initial_state,
+                    cu_seqlens, chunk_size, output_final_state, workspace, out, final_state,
+                    form=f)
+
+
+def _decode(entry, gate, q, k, v, g, beta, state, scale, out, form=None):
     _need(q.dim() == 3 and k.shape == q.shape and v.dim() == 3 and v.shape[:2] == q.shape[:2],
           "q, k must be [N, H, d_k] and v [N, H, d_v]")
     N, H, dk = q.shape
     dv = v.shape[-1]
-    if scalar_gate:
+    if gate == "scalar":
         _need(g is None or (g.shape == (N, H) and g.dtype == torch.float32),
               "g must be fp32 [N, H] or None")
+    elif gate == "none":
+        _need(g is None, "g must be None without a gate")
     else:
-        _need(g.shape == q.shape and g.dtype == torch.float32, "g must be fp32 [N, H, d_k]")
+        _need(g is not None and g.shape == q.shape and g.dtype == torch.float32,
+              "g must be fp32 [N, H, d_k]")
     _need(beta.shape == (N, H) and beta.dtype == torch.float32, "beta must be fp32 [N, H]")
     _need(state.shape == (N, H, dk, dv) and state.dtype == torch.float32,
           "state must be fp32 [N, H, d_k, d_v]")
@@ -223,7 +281,8 @@ def _decode(entry, scalar_gate, q, k, v, g, beta, state, scale, out):
     code = _dtype_code(q)
     scale = 1.0 / math.sqrt(dk) if scale is None else float(scale)
     o = out if out is not None else torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
-    st = entry(N, H, dk, dv, code, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+    extra = () if form is None else (ctypes.byref(form),)
+    st = entry(N, H, dk, dv, code, *extra, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                ctypes.c_float(scale), _ptr(state), _ptr(o), _stream())
     _check(st)
     return o
@@ -238,7 +297,7 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
     q, k: [N, H, d_k]; v: [N, H, d_v] (bf16 or fp32); g: [N, H, d_k] fp32;
     beta: [N, H] fp32.  Returns o [N, H, d_v] in the dtype of v.
     """
-    return _decode(lib().kda_decode_step, False, q, k, v, g, beta, state, scale, out)
+    return _decode(lib().kda_decode_step, "per_channel", q, k, v, g, beta, state, scale, out)
 
 
 def decode_step_scalar_gate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
@@ -247,4 +306,36 @@ def decode_step_scalar_gate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                             out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """One recurrent step with a scalar gate (``kda_decode_step_scalar_gate``):
     g is [N, H] fp32 or None for no decay.  Everything else as ``decode_step``."""
-    return _decode(lib().kda_decode_step_scalar_gate, True, q, k, v, g, beta, state, scale, out)
+    return _decode(lib().kda_decode_step_scalar_gate, "scalar", q, k, v, g, beta, state, scale,
+                   out)
+
+
+def decode_step_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[torch.Tensor],
+                   beta: torch.Tensor, state: torch.Tensor, *, gate: str = "per_channel",
+                   gate_is_logit: bool = False, beta_is_logit: bool = False,
+                   l2norm_qk: bool = False, eps: float = 1e-6, scale: Optional[float] = None,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One recurrent step with the inputs in a stated form (``kda_decode_step_ex``);
+    the form arguments are those of ``chunk_fwd_ex`` (g [N, H, d_k], [N, H] or None)."""
+    f = _form(gate, gate_is_logit, beta_is_logit, l2norm_qk, eps)
+    return _decode(lib().kda_decode_step_ex, gate, q, k, v, g, beta, state, scale, out, form=f)
+
+
+def output_rmsnorm_gate(o: torch.Tensor, gate: torch.Tensor, weight: torch.Tensor,
+                        eps: float = 1e-6, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out = o / sqrt(mean(o^2 over d_v) + eps) * weight * sigmoid(gate)
+    (``kda_output_rmsnorm_gate``).  o, gate: [..., d_v] bf16 or fp32 (same);
+    weight: [d_v] fp32.  ``out`` may be ``o`` (in place)."""
+    _need(o.shape == gate.shape and o.dtype == gate.dtype, "o and gate must match")
+    dv = o.shape[-1]
+    _need(weight.shape == (dv,) and weight.dtype == torch.float32, "weight must be fp32 [d_v]")
+    for name, t in (("o", o), ("gate", gate), ("weight", weight)):
+        _need(t.is_cuda and t.is_contiguous(), "%s must be a contiguous device tensor" % name)
+    code = _dtype_code(o)
+    res = out if out is not None else torch.empty_like(o)
+    _need(res.shape == o.shape and res.dtype == o.dtype and res.is_contiguous(),
+          "out must match o")
+    st = lib().kda_output_rmsnorm_gate(o.numel() // dv, dv, code, _ptr(o), _ptr(gate), _ptr(weight),
+                                       ctypes.c_float(eps), _ptr(res), _stream())
+    _check(st)
+    return res

@@ -19,7 +19,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkda.so")
 ARCH = "gfx950"
 
-SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_chunk_mfma.hip", "kda_chunk_f32.hip"]
+SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_chunk_mfma.hip", "kda_chunk_f32.hip",
+           "kda_post.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -7,6 +7,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -72,12 +73,31 @@ size_t workspace_for(const kda_shape *s, int64_t total) {
 // Shared body of the two prefill entry points.  With Gate::PerChannel, g is
 // [B, T, H, d_k] and required; with Gate::Scalar it is [B, T, H] and NULL
 // means no decay (Gate::None).
-kda_status chunk_fwd(kda::Gate gate, const kda_shape *shape, const void *q, const void *k,
-                     const void *v, const float *g, const float *beta, float scale,
-                     const float *initial_state, const int32_t *cu_seqlens, void *o,
-                     float *final_state, void *workspace, size_t workspace_bytes, void *stream) {
-    g_last_error[0] = '\0';
+// Decodes and checks an input-form descriptor (NULL = the plain KDA form).
+kda_status read_form(const kda_inputs_form *f, kda::Gate *gate, kda::InputForm *form) {
+    *form = kda::InputForm();
+    if (!f) return KDA_OK;
+    if (f->gate_layout < KDA_GATE_PER_CHANNEL || f->gate_layout > KDA_GATE_NONE)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "unknown gate_layout %d", (int)f->gate_layout);
+    *gate = static_cast<kda::Gate>(f->gate_layout);
+    form->gate_logit = f->gate_is_logit != 0;
+    form->beta_logit = f->beta_is_logit != 0;
+    form->l2norm = f->l2norm_qk != 0;
+    form->eps = f->eps;
+    if (form->l2norm && !(std::isfinite(f->eps) && f->eps > 0.f))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "l2norm_qk needs a finite eps > 0 (got %g)",
+                    (double)f->eps);
+    return KDA_OK;
+}
+
+kda_status chunk_fwd(kda::Gate gate, kda::InputForm form, const kda_shape *shape, const void *q,
+                     const void *k, const void *v, const float *g, const float *beta,
+                     float scale, const float *initial_state, const int32_t *cu_seqlens,
+                     void *o, float *final_state, void *workspace, size_t workspace_bytes,
+                     void *stream) {
     if (gate == kda::Gate::Scalar && !g) gate = kda::Gate::None;
+    if (gate == kda::Gate::None && g)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "g must be NULL when there is no gate");
     const bool varlen = cu_seqlens != nullptr;
     int64_t total = 0;
     kda_status st = check_shape(shape, &total);
@@ -125,6 +145,7 @@ kda_status chunk_fwd(kda::Gate gate, const kda_shape *shape, const void *q, cons
     p.k = k;
     p.v = v;
     p.gate = gate;
+    p.form = form;
     p.g = gate == kda::Gate::None ? nullptr : g;
     p.beta = beta;
     p.scale = scale;
@@ -145,12 +166,14 @@ kda_status chunk_fwd(kda::Gate gate, const kda_shape *shape, const void *q, cons
 
 // Shared body of the two decode entry points (gate layouts as for chunk_fwd,
 // per pair instead of per token).
-kda_status decode_step(kda::Gate gate, int32_t num_sessions, int32_t num_heads, int32_t d_k,
-                       int32_t d_v, kda_dtype dtype, const void *q, const void *k, const void *v,
-                       const float *g, const float *beta, float scale, float *state_inout,
-                       void *o, void *stream) {
-    g_last_error[0] = '\0';
+kda_status decode_step(kda::Gate gate, kda::InputForm form, int32_t num_sessions,
+                       int32_t num_heads, int32_t d_k, int32_t d_v, kda_dtype dtype,
+                       const void *q, const void *k, const void *v, const float *g,
+                       const float *beta, float scale, float *state_inout, void *o,
+                       void *stream) {
     if (gate == kda::Gate::Scalar && !g) gate = kda::Gate::None;
+    if (gate == kda::Gate::None && g)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "g must be NULL when there is no gate");
     if (dtype != KDA_F32 && dtype != KDA_BF16)
         return fail(KDA_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)dtype);
     if (num_sessions <= 0 || num_heads <= 0 || d_k <= 0 || d_v <= 0)
@@ -172,7 +195,7 @@ kda_status decode_step(kda::Gate gate, int32_t num_sessions, int32_t num_heads, 
         return fail(KDA_ERR_INVALID_ARGUMENT, "beta / a scalar gate must be 4-byte aligned");
     if (o == (void *)state_inout)
         return fail(KDA_ERR_INVALID_ARGUMENT, "o must not alias state_inout");
-    hipError_t e = kda::launch_decode((int)pairs, d_k, d_v, dtype == KDA_BF16, gate, q, k, v,
+    hipError_t e = kda::launch_decode((int)pairs, d_k, d_v, dtype == KDA_BF16, gate, form, q, k, v,
                                       gate == kda::Gate::None ? nullptr : g, beta, scale,
                                       state_inout, o, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "decode step launch");
@@ -213,9 +236,10 @@ kda_status kda_chunk_fwd(const kda_shape *shape, const void *q, const void *k, c
                          const float *initial_state, const int32_t *cu_seqlens, void *o,
                          float *final_state, void *workspace, size_t workspace_bytes,
                          void *stream) {
-    return chunk_fwd(kda::Gate::PerChannel, shape, q, k, v, g_log_decay, beta, scale,
-                     initial_state, cu_seqlens, o, final_state, workspace, workspace_bytes,
-                     stream);
+    g_last_error[0] = '\0';
+    return chunk_fwd(kda::Gate::PerChannel, kda::InputForm(), shape, q, k, v, g_log_decay, beta,
+                     scale, initial_state, cu_seqlens, o, final_state, workspace,
+                     workspace_bytes, stream);
 }
 
 kda_status kda_chunk_fwd_scalar_gate(const kda_shape *shape, const void *q, const void *k,
@@ -223,7 +247,25 @@ kda_status kda_chunk_fwd_scalar_gate(const kda_shape *shape, const void *q, cons
                                      float scale, const float *initial_state,
                                      const int32_t *cu_seqlens, void *o, float *final_state,
                                      void *workspace, size_t workspace_bytes, void *stream) {
-    return chunk_fwd(kda::Gate::Scalar, shape, q, k, v, g_log_decay, beta, scale, initial_state,
+    g_last_error[0] = '\0';
+    return chunk_fwd(kda::Gate::Scalar, kda::InputForm(), shape, q, k, v, g_log_decay, beta,
+                     scale, initial_state, cu_seqlens, o, final_state, workspace,
+                     workspace_bytes, stream);
+}
+
+kda_status kda_chunk_fwd_ex(const kda_shape *shape, const kda_inputs_form *form, const void *q,
+                            const void *k, const void *v, const float *g_log_decay,
+                            const float *beta, float scale, const float *initial_state,
+                            const int32_t *cu_seqlens, void *o, float *final_state,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+    g_last_error[0] = '\0';
+    kda::Gate gate = kda::Gate::PerChannel;
+    kda::InputForm f;
+    const kda_status st = read_form(form, &gate, &f);
+    if (st != KDA_OK) return st;
+    if (gate == kda::Gate::Scalar && !g_log_decay)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "KDA_GATE_SCALAR needs g (use KDA_GATE_NONE)");
+    return chunk_fwd(gate, f, shape, q, k, v, g_log_decay, beta, scale, initial_state,
                      cu_seqlens, o, final_state, workspace, workspace_bytes, stream);
 }
 
@@ -231,8 +273,9 @@ kda_status kda_decode_step(int32_t num_sessions, int32_t num_heads, int32_t d_k,
                            kda_dtype dtype, const void *q, const void *k, const void *v,
                            const float *g, const float *beta, float scale, float *state_inout,
                            void *o, void *stream) {
-    return decode_step(kda::Gate::PerChannel, num_sessions, num_heads, d_k, d_v, dtype, q, k, v,
-                       g, beta, scale, state_inout, o, stream);
+    g_last_error[0] = '\0';
+    return decode_step(kda::Gate::PerChannel, kda::InputForm(), num_sessions, num_heads, d_k, d_v,
+                       dtype, q, k, v, g, beta, scale, state_inout, o, stream);
 }
 
 kda_status kda_decode_step_scalar_gate(int32_t num_sessions, int32_t num_heads, int32_t d_k,
@@ -240,8 +283,52 @@ kda_status kda_decode_step_scalar_gate(int32_t num_sessions, int32_t num_heads, 
                                        const void *k, const void *v, const float *g,
                                        const float *beta, float scale, float *state_inout,
                                        void *o, void *stream) {
-    return decode_step(kda::Gate::Scalar, num_sessions, num_heads, d_k, d_v, dtype, q, k, v, g,
-                       beta, scale, state_inout, o, stream);
+    g_last_error[0] = '\0';
+    return decode_step(kda::Gate::Scalar, kda::InputForm(), num_sessions, num_heads, d_k, d_v,
+                       dtype, q, k, v, g, beta, scale, state_inout, o, stream);
+}
+
+kda_status kda_decode_step_ex(int32_t num_sessions, int32_t num_heads, int32_t d_k, int32_t d_v,
+                              kda_dtype dtype, const kda_inputs_form *form, const void *q,
+                              const void *k, const void *v, const float *g, const float *beta,
+                              float scale, float *state_inout, void *o, void *stream) {
+    g_last_error[0] = '\0';
+    kda::Gate gate = kda::Gate::PerChannel;
+    kda::InputForm f;
+    const kda_status st = read_form(form, &gate, &f);
+    if (st != KDA_OK) return st;
+    if (gate == kda::Gate::Scalar && !g)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "KDA_GATE_SCALAR needs g (use KDA_GATE_NONE)");
+    return decode_step(gate, f, num_sessions, num_heads, d_k, d_v, dtype, q, k, v, g, beta, scale,
+                       state_inout, o, stream);
+}
+
+kda_status kda_output_rmsnorm_gate(int64_t rows, int32_t d_v, kda_dtype dtype, const void *o,
+                                   const void *gate, const float *weight, float eps, void *out,
+                                   void *stream) {
+    g_last_error[0] = '\0';
+    if (dtype != KDA_F32 && dtype != KDA_BF16)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)dtype);
+    if (rows < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "negative rows (%lld)", (long long)rows);
+    if (!kda::output_stage_supported(d_v))
+        return fail(KDA_ERR_UNSUPPORTED, "no output-stage kernel for d_v %d (built: 16, 32, 64, "
+                    "128, 256)", d_v);
+    if (!(std::isfinite(eps) && eps > 0.f))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "eps must be finite and > 0 (got %g)", (double)eps);
+    if (rows == 0) return KDA_OK;
+    if ((rows + 255) / 256 * 4 > (int64_t)INT32_MAX)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "too many rows (%lld)", (long long)rows);
+    if (!o || !gate || !weight || !out)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "a required tensor pointer is NULL");
+    const uintptr_t mask = dtype == KDA_F32 ? 15u : 7u;
+    if ((reinterpret_cast<uintptr_t>(o) & mask) || (reinterpret_cast<uintptr_t>(gate) & mask) ||
+        (reinterpret_cast<uintptr_t>(out) & mask) || !aligned16(weight))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "o / gate / out / weight are misaligned");
+    if (out == gate) return fail(KDA_ERR_INVALID_ARGUMENT, "out must not alias gate");
+    hipError_t e = kda::launch_output_rmsnorm_gate(rows, d_v, dtype == KDA_BF16, o, gate, weight,
+                                                   eps, out, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "output stage launch");
+    return KDA_OK;
 }
 
 }  // extern "C"

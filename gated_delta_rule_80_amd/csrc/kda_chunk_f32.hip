@@ -17,7 +17,7 @@ namespace f32_path {
 constexpr int THREADS = 256;
 
 struct Lds {
-    int q, k, G, v, beta, A, T, W, U, S, total;   // offsets in floats (H reuses A)
+    int q, k, G, v, beta, nrm, A, T, W, U, S, total;   // offsets in floats (H reuses A)
 };
 
 __host__ __device__ inline Lds lds_layout(int dk, int dv, int C) {
@@ -28,6 +28,7 @@ __host__ __device__ inline Lds lds_layout(int dk, int dv, int C) {
     L.G = o; o += C * dk;
     L.v = o; o += C * dv;
     L.beta = o; o += C;
+    L.nrm = o; o += 2 * C;   // inverse L2 norms of the rows of k and q
     L.A = o; o += C * C;
     L.T = o; o += C * C;
     L.W = o; o += C * dk;
@@ -39,12 +40,13 @@ __host__ __device__ inline Lds lds_layout(int dk, int dv, int C) {
 
 __global__ __launch_bounds__(THREADS) void kda_chunk_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
-    const float *__restrict__ g, int gate, const float *__restrict__ beta, float scale, int H,
-    int dk, int dv, int C, int row_len, const int32_t *__restrict__ cu,
+    const float *__restrict__ g, int gate, const float *__restrict__ beta, float scale, int form,
+    float eps, int H, int dk, int dv, int C, int row_len, const int32_t *__restrict__ cu,
     const float *__restrict__ s0, float *__restrict__ s_final, float *__restrict__ o) {
     extern __shared__ float sm[];
     const Lds L = lds_layout(dk, dv, C);
     float *sq = sm + L.q, *sk = sm + L.k, *sG = sm + L.G, *sv = sm + L.v, *sb = sm + L.beta;
+    float *snrm = sm + L.nrm;
     float *sA = sm + L.A, *sT = sm + L.T, *sW = sm + L.W, *sU = sm + L.U;
     float *sH = sA;   // H is built once T no longer needs A
     float *sS = sm + L.S;
@@ -75,15 +77,38 @@ __global__ __launch_bounds__(THREADS) void kda_chunk_f32_kernel(
             sq[e] = ok ? q[a] : 0.f;
             sk[e] = ok ? k[a] : 0.f;
             // gate 0: log-decay per channel; 1: one per (token, head); 2: none
-            const float gv = gate == 0 ? g[a] : (gate == 1 ? g[(size_t)(t0 + i) * H + h] : 0.f);
-            sG[e] = ok ? gv : 0.f;
+            float gv = 0.f;
+            if (ok && gate != 2) {
+                gv = gate == 0 ? g[a] : g[(size_t)(t0 + i) * H + h];
+                if (form & kFormGateLogit) gv = log_sigmoid(gv);
+            }
+            sG[e] = gv;
         }
         for (int e = tid; e < C * dv; e += THREADS) {
             const int i = e / dv, c = e - i * dv;
             sv[e] = i < len ? v[((size_t)(t0 + i) * H + h) * dv + c] : 0.f;
         }
-        for (int i = tid; i < C; i += THREADS) sb[i] = i < len ? beta[(size_t)(t0 + i) * H + h] : 0.f;
+        for (int i = tid; i < C; i += THREADS) {
+            float b = i < len ? beta[(size_t)(t0 + i) * H + h] : 0.f;
+            if ((form & kFormBetaLogit) && i < len) b = sigmoid(b);
+            sb[i] = b;
+        }
         __syncthreads();
+        if (form & kFormL2Norm) {   // q, k rows divided by sqrt(sum of squares + eps)
+            for (int x = tid; x < 2 * C; x += THREADS) {
+                const float *row = (x < C ? sk : sq) + (x % C) * dk;
+                float ss = 0.f;
+                for (int c = 0; c < dk; ++c) ss += row[c] * row[c];
+                snrm[x] = 1.f / sqrtf(ss + eps);
+            }
+            __syncthreads();
+            for (int e = tid; e < C * dk; e += THREADS) {
+                const int i = e / dk;
+                sk[e] *= snrm[i];
+                sq[e] *= snrm[C + i];
+            }
+            __syncthreads();
+        }
         // G: inclusive cumulative log-decay per channel.
         for (int c = tid; c < dk; c += THREADS) {
             float run = 0.f;
@@ -192,9 +217,9 @@ hipError_t launch_chunk_fwd_f32(const ChunkProblem &p) {
     }
     hipLaunchKernelGGL(kda_chunk_f32_kernel, dim3(p.n_seqs * p.heads), dim3(THREADS), lds,
                        p.stream, static_cast<const float *>(p.q), static_cast<const float *>(p.k),
-                       static_cast<const float *>(p.v), p.g, (int)p.gate, p.beta, p.scale, p.heads,
-                       p.dk, p.dv, p.chunk, p.seqlen, p.cu, p.s0, p.s_final,
-                       static_cast<float *>(p.o));
+                       static_cast<const float *>(p.v), p.g, (int)p.gate, p.beta, p.scale,
+                       p.form.flags(), p.form.eps, p.heads, p.dk, p.dv, p.chunk, p.seqlen, p.cu,
+                       p.s0, p.s_final, static_cast<float *>(p.o));
     return hipGetLastError();
 }
 

@@ -178,6 +178,7 @@ __global__ __launch_bounds__(1024) void kda_chunk_index_kernel(const int32_t *__
 // ------------------------------------------------------------------------------------
 // LDS map (bytes).  Stages 1-2: fragment buffers and the transposed Ktil.
 constexpr int L_KP = 0, L_KM = 16384, L_QP = 32768, L_KT = 49152;   // + 18432 -> 67584
+constexpr int L_NRM = 67584;      // fp32 [4 waves][64 rows][2]: partial |k|^2, |q|^2 (stage 1)
 // Stages 3-6 (the fragment buffers are dead by then).
 constexpr int L_A = 0;            // fp32 [64][65]   16640
 constexpr int L_BL = 16640;       // fp16 [128][72]  18432  L^T = (K e^{G})^T
@@ -232,9 +233,9 @@ template <Gate GATE>
 __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const float *__restrict__ g,
-    const float *__restrict__ beta, float scale, int H, int row_len, int ncr,
-    const int4 *__restrict__ table, const int32_t *__restrict__ n_chunks, int nc_max, int jlo,
-    int jn, uint8_t *__restrict__ recs) {
+    const float *__restrict__ beta, float scale, int form, float eps, int H, int row_len,
+    int ncr, const int4 *__restrict__ table, const int32_t *__restrict__ n_chunks, int nc_max,
+    int jlo, int jn, uint8_t *__restrict__ recs) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[L_BYTES];
     const int h = blockIdx.x % H, b = blockIdx.x / H;
     int c;
@@ -277,8 +278,16 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
             if constexpr (GATE == Gate::PerChannel) {
                 ga = *reinterpret_cast<const float4v *>(g + base + ca);
                 gb = *reinterpret_cast<const float4v *>(g + base + cb);
+                if (form & kFormGateLogit) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        ga[e] = log_sigmoid(ga[e]);
+                        gb[e] = log_sigmoid(gb[e]);
+                    }
+                }
             } else if constexpr (GATE == Gate::Scalar) {
-                const float gs = g[(size_t)(ch.t0 + i) * H + h];
+                float gs = g[(size_t)(ch.t0 + i) * H + h];
+                if (form & kFormGateLogit) gs = log_sigmoid(gs);
                 ga = float4v{gs, gs, gs, gs};
                 gb = ga;
             }
@@ -306,7 +315,49 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
     }
     if (tid < C) {
         const int i = tid;
-        sBeta[i] = i < len ? beta[(size_t)(ch.t0 + i) * H + h] : 0.f;
+        float b = i < len ? beta[(size_t)(ch.t0 + i) * H + h] : 0.f;
+        if ((form & kFormBetaLogit) && i < len) b = sigmoid(b);
+        sBeta[i] = b;
+    }
+    // Optional L2 normalisation of q and k over their d_k channels: each lane
+    // holds 8 channels of 4 rows; the 4 lanes of a row in a wave, then the 4
+    // waves through LDS, complete the sums of squares.
+    if (form & kFormL2Norm) {
+        float *sNrm = reinterpret_cast<float *>(smem + L_NRM);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float a = 0.f, b = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                a += kf[r][j] * kf[r][j];
+                b += qf[r][j] * qf[r][j];
+            }
+            a += __shfl_xor(a, 16, 64);
+            a += __shfl_xor(a, 32, 64);
+            b += __shfl_xor(b, 16, 64);
+            b += __shfl_xor(b, 32, 64);
+            if (g4 == 0) {
+                sNrm[(w * 64 + 16 * r + i16) * 2 + 0] = a;
+                sNrm[(w * 64 + 16 * r + i16) * 2 + 1] = b;
+            }
+        }
+        lds_barrier();
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * r + i16;
+            float a = 0.f, b = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < 4; ++ww) {
+                a += sNrm[(ww * 64 + i) * 2 + 0];
+                b += sNrm[(ww * 64 + i) * 2 + 1];
+            }
+            const float ia = rsqrtf(a + eps), ib = rsqrtf(b + eps);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                kf[r][j] *= ia;
+                qf[r][j] *= ib;
+            }
+        }
     }
     // Inclusive cumsum along tokens: scan inside each 16-token tile, carry across tiles.
 #pragma unroll
@@ -905,8 +956,9 @@ hipError_t launch_chunk_fwd_mfma(const ChunkProblem &p) {
                                                : kda_intra_kernel<Gate::None>;
         hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st,
                            static_cast<const uint16_t *>(p.q), static_cast<const uint16_t *>(p.k),
-                           static_cast<const uint16_t *>(p.v), p.g, p.beta, p.scale, p.heads,
-                           p.seqlen, ncr, table, off + p.n_seqs, (int)L.nc_max, jlo, jn, recs);
+                           static_cast<const uint16_t *>(p.v), p.g, p.beta, p.scale,
+                           p.form.flags(), p.form.eps, p.heads, p.seqlen, ncr, table,
+                           off + p.n_seqs, (int)L.nc_max, jlo, jn, recs);
         return hipGetLastError();
     };
     auto inter = [&](int jlo, int jhi, const float *s_in, float *s_out) {

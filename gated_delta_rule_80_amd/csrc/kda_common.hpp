@@ -82,6 +82,13 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
+// log(sigmoid(x)) without overflow: min(x, 0) - log(1 + e^{-|x|}).
+__device__ __forceinline__ float log_sigmoid(float x) {
+    return fminf(x, 0.f) - log1pf(__expf(-fabsf(x)));
+}
+
+__device__ __forceinline__ float sigmoid(float x) { return 1.f / (1.f + __expf(-x)); }
+
 __device__ __forceinline__ float fast_exp(float x) {
     // exp(x) = 2^(x * log2(e)) on the hardware exp2 unit.
     return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);

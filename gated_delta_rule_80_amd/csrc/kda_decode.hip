@@ -35,15 +35,15 @@ struct DecodeCfg {
 template <int DK, int DV, typename T, Gate GATE>
 __global__ __launch_bounds__((DecodeCfg<DK, DV>::THREADS)) void kda_decode_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
-    const float *__restrict__ g, const float *__restrict__ beta, float scale,
-    float *__restrict__ state, T *__restrict__ o) {
+    const float *__restrict__ g, const float *__restrict__ beta, float scale, int form,
+    float eps, float *__restrict__ state, T *__restrict__ o) {
     using Cfg = DecodeCfg<DK, DV>;
     constexpr int NQ = Cfg::NQ, NRG = Cfg::NRG, RPT = Cfg::RPT, NWAVES = Cfg::NWAVES;
     constexpr int THREADS = Cfg::THREADS;
 
     __shared__ float s_a[DK], s_k[DK], s_sq[DK], s_v[DV];
     __shared__ float4v s_red[NWAVES][2][NQ];
-    __shared__ float s_kq[NWAVES];
+    __shared__ float s_kq[NWAVES], s_kk[NWAVES], s_qq[NWAVES];
 
     const size_t pair = blockIdx.x;
     const int tid = threadIdx.x;
@@ -57,22 +57,48 @@ __global__ __launch_bounds__((DecodeCfg<DK, DV>::THREADS)) void kda_decode_kerne
     for (int i = 0; i < RPT; ++i)
         S[i] = __builtin_nontemporal_load(sp + (size_t)(rg + NRG * i) * NQ + cq);
 
-    // Token vectors: a = exp(g), k, s*q, v; plus the scalar k . (s q).
-    float kq = 0.f;
+    // Token vectors: a = exp(g) (sigmoid(g) for a logit gate), k, s*q, v; plus
+    // the scalar k . (s q) and, for L2-normalised q and k, |k|^2 and |q|^2.
+    const bool glogit = (form & kFormGateLogit) != 0;
+    float kq = 0.f, kk2 = 0.f, qq2 = 0.f;
     for (int i = tid; i < DK; i += THREADS) {
         const size_t gi = pair * DK + i;
-        float kk = io<T>::load(k, gi), sq = scale * io<T>::load(q, gi);
-        s_a[i] = GATE == Gate::PerChannel ? fast_exp(g[gi])
-                 : GATE == Gate::Scalar   ? fast_exp(g[pair])
-                                          : 1.f;
+        const float kk = io<T>::load(k, gi), qq = io<T>::load(q, gi);
+        float a = 1.f;
+        if (GATE == Gate::PerChannel) a = glogit ? sigmoid(g[gi]) : fast_exp(g[gi]);
+        if (GATE == Gate::Scalar) a = glogit ? sigmoid(g[pair]) : fast_exp(g[pair]);
+        s_a[i] = a;
         s_k[i] = kk;
-        s_sq[i] = sq;
-        kq += kk * sq;
+        s_sq[i] = scale * qq;
+        kq += kk * (scale * qq);
+        kk2 += kk * kk;
+        qq2 += qq * qq;
     }
     for (int i = tid; i < DV; i += THREADS) s_v[i] = io<T>::load(v, pair * DV + i);
     kq = wave_sum(kq);
     if (lane == 0) s_kq[wave] = kq;
+    if (form & kFormL2Norm) {
+        kk2 = wave_sum(kk2);
+        qq2 = wave_sum(qq2);
+        if (lane == 0) {
+            s_kk[wave] = kk2;
+            s_qq[wave] = qq2;
+        }
+    }
     __syncthreads();
+    // 1 / |k| and 1 / |q| when q and k are normalised here (else 1); every use
+    // of k and q below is linear in them, so the factors are applied to sums.
+    float ik = 1.f, iq = 1.f;
+    if (form & kFormL2Norm) {
+        float a = 0.f, b = 0.f;
+#pragma unroll
+        for (int w = 0; w < NWAVES; ++w) {
+            a += s_kk[w];
+            b += s_qq[w];
+        }
+        ik = rsqrtf(a + eps);
+        iq = rsqrtf(b + eps);
+    }
 
     // Retain, then both reductions over this thread's rows.
     float4v vh = {0.f, 0.f, 0.f, 0.f}, qs = {0.f, 0.f, 0.f, 0.f};
@@ -107,8 +133,11 @@ __global__ __launch_bounds__((DecodeCfg<DK, DV>::THREADS)) void kda_decode_kerne
         qs += s_red[w][1][cq];
         kq += s_kq[w];
     }
+    vh *= ik;
+    qs *= iq;
+    kq *= ik * iq;
 
-    const float b = beta[pair];
+    const float b = (form & kFormBetaLogit) ? sigmoid(beta[pair]) : beta[pair];
     float4v e;
 #pragma unroll
     for (int j = 0; j < 4; ++j) e[j] = s_v[4 * cq + j] - vh[j];
@@ -123,49 +152,52 @@ __global__ __launch_bounds__((DecodeCfg<DK, DV>::THREADS)) void kda_decode_kerne
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int r = rg + NRG * i;
-        const float bk = b * s_k[r];
+        const float bk = b * ik * s_k[r];
         __builtin_nontemporal_store(S[i] + bk * e, spw + (size_t)r * NQ + cq);
     }
 }
 
 template <int DK, int DV, typename T, Gate GATE>
-static hipError_t launch_decode_g(int n_pairs, const void *q, const void *k, const void *v,
-                                  const float *g, const float *beta, float scale, float *state,
-                                  void *o, hipStream_t stream) {
+static hipError_t launch_decode_g(int n_pairs, InputForm f, const void *q, const void *k,
+                                  const void *v, const float *g, const float *beta, float scale,
+                                  float *state, void *o, hipStream_t stream) {
     using Cfg = DecodeCfg<DK, DV>;
     hipLaunchKernelGGL((kda_decode_kernel<DK, DV, T, GATE>), dim3(n_pairs), dim3(Cfg::THREADS),
                        0, stream, static_cast<const T *>(q), static_cast<const T *>(k),
-                       static_cast<const T *>(v), g, beta, scale, state, static_cast<T *>(o));
+                       static_cast<const T *>(v), g, beta, scale, f.flags(), f.eps, state,
+                       static_cast<T *>(o));
     return hipGetLastError();
 }
 
 template <int DK, int DV, typename T>
-static hipError_t launch_decode_t(Gate gate, int n_pairs, const void *q, const void *k,
-                                  const void *v, const float *g, const float *beta, float scale,
-                                  float *state, void *o, hipStream_t stream) {
+static hipError_t launch_decode_t(Gate gate, InputForm f, int n_pairs, const void *q,
+                                  const void *k, const void *v, const float *g,
+                                  const float *beta, float scale, float *state, void *o,
+                                  hipStream_t stream) {
     switch (gate) {
     case Gate::PerChannel:
-        return launch_decode_g<DK, DV, T, Gate::PerChannel>(n_pairs, q, k, v, g, beta, scale,
+        return launch_decode_g<DK, DV, T, Gate::PerChannel>(n_pairs, f, q, k, v, g, beta, scale,
                                                             state, o, stream);
     case Gate::Scalar:
-        return launch_decode_g<DK, DV, T, Gate::Scalar>(n_pairs, q, k, v, g, beta, scale, state,
-                                                        o, stream);
+        return launch_decode_g<DK, DV, T, Gate::Scalar>(n_pairs, f, q, k, v, g, beta, scale,
+                                                        state, o, stream);
     case Gate::None:
-        return launch_decode_g<DK, DV, T, Gate::None>(n_pairs, q, k, v, g, beta, scale, state, o,
-                                                      stream);
+        return launch_decode_g<DK, DV, T, Gate::None>(n_pairs, f, q, k, v, g, beta, scale, state,
+                                                      o, stream);
     }
     return hipErrorInvalidValue;
 }
 
 // Returns hipErrorInvalidValue for a (d_k, d_v) that is not instantiated.
-hipError_t launch_decode(int n_pairs, int dk, int dv, bool bf16, Gate gate, const void *q,
-                         const void *k, const void *v, const float *g, const float *beta,
-                         float scale, float *state, void *o, hipStream_t stream) {
-#define KDA_DECODE_CASE(D)                                                                   \
-    if (dk == D && dv == D)                                                                  \
-        return bf16 ? launch_decode_t<D, D, bf16_t>(gate, n_pairs, q, k, v, g, beta, scale,  \
-                                                    state, o, stream)                        \
-                    : launch_decode_t<D, D, float>(gate, n_pairs, q, k, v, g, beta, scale,   \
+hipError_t launch_decode(int n_pairs, int dk, int dv, bool bf16, Gate gate, InputForm form,
+                         const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, float scale, float *state, void *o,
+                         hipStream_t stream) {
+#define KDA_DECODE_CASE(D)                                                                     \
+    if (dk == D && dv == D)                                                                    \
+        return bf16 ? launch_decode_t<D, D, bf16_t>(gate, form, n_pairs, q, k, v, g, beta,     \
+                                                    scale, state, o, stream)                   \
+                    : launch_decode_t<D, D, float>(gate, form, n_pairs, q, k, v, g, beta, scale, \
                                                    state, o, stream);
     KDA_DECODE_CASE(128)
     KDA_DECODE_CASE(64)

@@ -13,11 +13,29 @@ namespace kda {
 // as in Gated DeltaNet), or none (a_t = 1: DeltaNet).
 enum class Gate : int { PerChannel = 0, Scalar = 1, None = 2 };
 
+// Elementwise steps applied to the inputs as the kernels read them.
+struct InputForm {
+    bool gate_logit = false;   // g holds logits x: log a = log sigmoid(x)
+    bool beta_logit = false;   // beta holds logits x: beta = sigmoid(x)
+    bool l2norm = false;       // q, k divided by sqrt(sum of squares + eps) per row
+    float eps = 0.f;
+    // Kernel-argument encoding: bit 0 gate_logit, bit 1 beta_logit, bit 2 l2norm.
+    int flags() const { return (gate_logit ? 1 : 0) | (beta_logit ? 2 : 0) | (l2norm ? 4 : 0); }
+};
+constexpr int kFormGateLogit = 1, kFormBetaLogit = 2, kFormL2Norm = 4;
+
 // ---- decode -----------------------------------------------------------------
 bool decode_supported(int dk, int dv);
-hipError_t launch_decode(int n_pairs, int dk, int dv, bool bf16, Gate gate, const void *q,
-                         const void *k, const void *v, const float *g, const float *beta,
-                         float scale, float *state, void *o, hipStream_t stream);
+hipError_t launch_decode(int n_pairs, int dk, int dv, bool bf16, Gate gate, InputForm form,
+                         const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, float scale, float *state, void *o,
+                         hipStream_t stream);
+
+// ---- output stage: RMS norm over d_v, weight, sigmoid gate -------------------------
+bool output_stage_supported(int dv);
+hipError_t launch_output_rmsnorm_gate(int64_t rows, int dv, bool bf16, const void *o,
+                                      const void *gate, const float *weight, float eps,
+                                      void *out, hipStream_t stream);
 
 // ---- chunked prefill ----------------------------------------------------------
 // Everything a prefill launch needs, already validated by the C ABI layer.
@@ -30,6 +48,7 @@ struct ChunkProblem {
     bool bf16;         // storage type of q, k, v, o
     const void *q, *k, *v;
     Gate gate;             // layout of g (null when gate == Gate::None)
+    InputForm form;        // elementwise steps applied as q, k, g, beta are read
     const float *g, *beta;
     float scale;
     const float *s0;       // may be null (zeros)

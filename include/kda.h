@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 typedef enum kda_status {
     KDA_OK = 0,
@@ -84,6 +84,41 @@ typedef struct kda_shape {
     int32_t num_seqs;
     kda_dtype dtype;
 } kda_shape;
+
+/*
+ * How the inputs of the *_ex entry points are given.  A KDA layer produces q,
+ * k, the decay and beta from learned projections; normalising q and k and
+ * squashing the decay and write-strength logits are the last elementwise steps
+ * before the recurrence ("Kimi Delta Attention: How It Works, Step by Step",
+ * question 16; "Kimi Delta Attention: a half-life per channel", section
+ * "Promote the scalar to a diagonal", a_t = sigmoid(x_t W_a)).  The *_ex entry
+ * points apply them inside the kernels as the inputs are read, so no separate
+ * pass over q, k, g or beta is needed.
+ *   gate_layout    KDA_GATE_PER_CHANNEL: g is [.., d_k] (KDA);
+ *                  KDA_GATE_SCALAR: g is [..] (one per token and head);
+ *                  KDA_GATE_NONE: no decay, g must be NULL.
+ *   gate_is_logit  0: g holds log a (<= 0).  1: g holds logits x and
+ *                  log a = log sigmoid(x), evaluated as min(x, 0) - log1p(e^-|x|).
+ *   beta_is_logit  0: beta holds the write strength.  1: beta = sigmoid(x).
+ *   l2norm_qk      1: q and k are each divided by sqrt(sum of squares + eps)
+ *                  over their d_k channels, per (token, head).
+ *   eps            the epsilon of l2norm_qk (for example 1e-6); must be > 0
+ *                  when l2norm_qk is set.
+ * {KDA_GATE_PER_CHANNEL, 0, 0, 0, 0} is exactly kda_chunk_fwd / kda_decode_step.
+ */
+typedef enum kda_gate_layout {
+    KDA_GATE_PER_CHANNEL = 0,
+    KDA_GATE_SCALAR = 1,
+    KDA_GATE_NONE = 2
+} kda_gate_layout;
+
+typedef struct kda_inputs_form {
+    int32_t gate_layout;
+    int32_t gate_is_logit;
+    int32_t beta_is_logit;
+    int32_t l2norm_qk;
+    float eps;
+} kda_inputs_form;
 
 /* ABI version of the loaded library (KDA_ABI_VERSION it was built with). */
 int kda_abi_version(void);
@@ -200,6 +235,53 @@ kda_status kda_decode_step_scalar_gate(int32_t num_sessions, int32_t num_heads,
                                        const float *beta, float scale,
                                        float *state_inout, void *o,
                                        void *stream);
+
+/*
+ * kda_chunk_fwd with the inputs in the form `form` describes (see
+ * kda_inputs_form).  g_log_decay is [B, T, H, d_k] or [B, T, H] by
+ * form->gate_layout (NULL for KDA_GATE_NONE); beta is [B, T, H] either way.
+ * Everything else, including the workspace query, is as kda_chunk_fwd.
+ */
+kda_status kda_chunk_fwd_ex(const kda_shape *shape, const kda_inputs_form *form,
+                            const void *q, const void *k, const void *v,
+                            const float *g_log_decay, const float *beta,
+                            float scale, const float *initial_state,
+                            const int32_t *cu_seqlens, void *o,
+                            float *final_state, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/*
+ * kda_decode_step with the inputs in the form `form` describes; g is
+ * [N, H, d_k] or [N, H] by form->gate_layout (NULL for KDA_GATE_NONE).
+ */
+kda_status kda_decode_step_ex(int32_t num_sessions, int32_t num_heads,
+                              int32_t d_k, int32_t d_v, kda_dtype dtype,
+                              const kda_inputs_form *form, const void *q,
+                              const void *k, const void *v, const float *g,
+                              const float *beta, float scale,
+                              float *state_inout, void *o, void *stream);
+
+/*
+ * Output stage of a KDA layer after the recurrence: RMS normalisation of each
+ * (token, head) output row over its d_v channels, a learned per-channel
+ * weight, and a sigmoid output gate ("Understanding Kimi Delta Attention",
+ * section "From mathematics to the GPU", lists output gating and RMS
+ * normalisation among the layer's steps around the core):
+ *
+ *   out[r, c] = o[r, c] / sqrt(mean_c' o[r, c']^2 + eps) * weight[c]
+ *               * sigmoid(gate[r, c])
+ *
+ *   o, gate, out  [rows, d_v] in dtype (rows = tokens x heads, or sessions x
+ *                 heads); out may equal o (in place) but not gate.
+ *   weight        [d_v] fp32.
+ *   eps           > 0.
+ * d_v in {16, 32, 64, 128, 256}; rows >= 0 (0 enqueues nothing).  o, gate and
+ * out 16-byte aligned for fp32 and 8-byte for bf16; weight 16-byte aligned.
+ */
+kda_status kda_output_rmsnorm_gate(int64_t rows, int32_t d_v, kda_dtype dtype,
+                                   const void *o, const void *gate,
+                                   const float *weight, float eps, void *out,
+                                   void *stream);
 
 #ifdef __cplusplus
 }

@@ -11,6 +11,10 @@ Contents
   reference.py   NumPy fp64 twin of the recurrence, and the chunkwise WY / UT
                  form written step by step from the derivation, used to pin
                  the recurrence.
+  layer.py       fp64 definitions of the layer's elementwise steps around the
+                 recurrence (q/k L2 norm, log sigmoid and sigmoid of logits,
+                 RMS norm x weight x sigmoid output gate), pinned by
+                 ``tests/test_oracle_layer.py``.
   build.py       gcc build of the C oracle.
 
 Every function is pinned by ``tests/test_oracle_pins.py`` against closed
@@ -26,7 +30,7 @@ import os
 
 import numpy as np
 
-from . import reference  # noqa: F401  (re-export)
+from . import layer, reference  # noqa: F401  (re-export)
 from .reference import chunkwise, recurrent, decode_step as decode_step_np  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
