@@ -15,7 +15,10 @@
 // Layout: one workgroup per pair; thread (rg, cq) owns the float4 column
 // quad cq of rows rg, rg + NRG, rg + 2 NRG, ...  Each wave's loads and
 // stores cover whole 512-byte state rows (fully coalesced, nontemporal: the
-// state is streamed, never re-read within a step).
+// state is streamed, never re-read within a step).  Ordinary (temporal)
+// accesses look faster only while the whole state fits the 256 MB Infinity
+// Cache between steps (128 sessions x 32 heads at d = 128 nearly does); at
+// twice that they are 15% slower than streaming ones.
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
@@ -24,7 +27,9 @@ namespace kda {
 template <int DK, int DV>
 struct DecodeCfg {
     static constexpr int NQ = DV / 4;                        // column quads
-    static constexpr int THREADS = (NQ * DK < 256) ? NQ * DK : 256;
+    // 512 threads (8 state rows each at d = 128) measured faster than 256 or
+    // 1024 at 128, 256 and 512 sessions.
+    static constexpr int THREADS = (NQ * DK < 512) ? NQ * DK : 512;
     static constexpr int NRG = THREADS / NQ;                 // row groups
     static constexpr int RPT = DK / NRG;                     // rows per thread
     static constexpr int NWAVES = (THREADS + 63) / 64;
