@@ -40,9 +40,6 @@
 //   slot s < 4  -> index 4 (l/16) + s,   slot s >= 4 -> index 16 + 4 (l/16) + s - 4
 // which is exactly what two vertically adjacent 16x16 accumulator tiles hold,
 // so an MFMA result feeds the next MFMA without leaving registers.
-#include <algorithm>
-#include <mutex>
-
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
@@ -55,9 +52,6 @@ constexpr int C = 64, DK = 128, DV = 128;
 #endif
 #ifndef KDA_INTER_PF
 #define KDA_INTER_PF 3
-#endif
-#ifndef KDA_SEGMENTS
-#define KDA_SEGMENTS 1
 #endif
 #ifndef KDA_INTER_L2D
 #define KDA_INTER_L2D 4
@@ -868,10 +862,10 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
     }
 }
 
-// Workspace: [off int32 (N+1)][chunk table int4 x nc_max][carried state fp32
-// N x H x d_k x d_v][records], each region 256-byte aligned.
+// Workspace: [off int32 (N+1)][chunk table int4 x nc_max][records], each region
+// 256-byte aligned.
 struct WsLayout {
-    size_t off, table, state, recs, total;
+    size_t off, table, recs, total;
     int64_t nc_max;
 };
 
@@ -881,8 +875,7 @@ static WsLayout ws_layout(int64_t total_tokens, int64_t n_seqs, int heads) {
     auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
     L.off = 0;
     L.table = up((size_t)(n_seqs + 1) * 4);
-    L.state = L.table + up((size_t)L.nc_max * 16);
-    L.recs = L.state + up((size_t)n_seqs * heads * DK * DV * 4);
+    L.recs = L.table + up((size_t)L.nc_max * 16);
     L.total = L.recs + (size_t)heads * L.nc_max * REC_BYTES;
     return L;
 }
@@ -897,43 +890,6 @@ size_t mfma_workspace_bytes(int64_t total_tokens, int64_t n_seqs, int heads, int
     return mfma_path::ws_layout(total_tokens, n_seqs, heads).total;
 }
 
-// Per device: one helper stream (default priority) and a ring of events, made
-// on first use and kept until the process ends.  The helper stream runs the
-// intra-chunk kernels of segment s + 1 while the caller's stream runs the
-// inter-chunk kernel of segment s.
-namespace {
-constexpr int kMaxDevices = 64, kEvents = 160;
-constexpr int kMaxSegments = 128;
-struct Aux {
-    bool ready = false;
-    hipStream_t helper = nullptr;
-    hipEvent_t ev[kEvents];
-    int next = 0;
-};
-std::mutex g_aux_mu;
-Aux g_aux[kMaxDevices];
-
-// Returns false if the helper resources cannot be made (then run serially).
-bool get_aux(int n_events, hipStream_t *helper, hipEvent_t *evs) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return false;
-    std::lock_guard<std::mutex> lk(g_aux_mu);
-    Aux &a = g_aux[dev];
-    if (!a.ready) {
-        if (hipStreamCreateWithFlags(&a.helper, hipStreamNonBlocking) != hipSuccess) return false;
-        for (int i = 0; i < kEvents; ++i)
-            if (hipEventCreateWithFlags(&a.ev[i], hipEventDisableTiming) != hipSuccess) return false;
-        a.ready = true;
-    }
-    *helper = a.helper;
-    for (int i = 0; i < n_events; ++i) {
-        evs[i] = a.ev[a.next];
-        a.next = (a.next + 1) % kEvents;
-    }
-    return true;
-}
-}  // namespace
-
 hipError_t launch_chunk_fwd_mfma(const ChunkProblem &p) {
     using namespace mfma_path;
     const bool varlen = p.cu != nullptr;
@@ -942,7 +898,6 @@ hipError_t launch_chunk_fwd_mfma(const ChunkProblem &p) {
     uint8_t *ws = static_cast<uint8_t *>(p.workspace);
     int32_t *off = reinterpret_cast<int32_t *>(ws + L.off);
     int4 *table = varlen ? reinterpret_cast<int4 *>(ws + L.table) : nullptr;
-    float *carry = reinterpret_cast<float *>(ws + L.state);
     uint8_t *recs = ws + L.recs;
     const int ncr = (p.seqlen + C - 1) / C;
     const int n_pairs = p.n_seqs * p.heads;
@@ -980,37 +935,9 @@ hipError_t launch_chunk_fwd_mfma(const ChunkProblem &p) {
         return inter(0, INT32_MAX / 2, p.s0, p.s_final);
     }
 
-    // Equal rows: S segments of local chunks; intra(s + 1) overlaps inter(s).
-    const int S = KDA_SEGMENTS <= 1 ? 1 : std::min(ncr, std::min(kMaxSegments, KDA_SEGMENTS));
-    const int M = (ncr + S - 1) / S;
-    hipStream_t helper = nullptr;
-    hipEvent_t ev[kMaxSegments + 1];
-    const bool overlap = S > 1 && get_aux(S + 1, &helper, ev);
-    if (!overlap) {
-        if ((e = intra(p.stream, 0, ncr, p.heads * p.batch * ncr)) != hipSuccess) return e;
-        return inter(0, ncr, p.s0, p.s_final);
-    }
-    // The helper stream starts once everything the caller queued before us is done.
-    if ((e = hipEventRecord(ev[S], p.stream)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(helper, ev[S], 0)) != hipSuccess) return e;
-    for (int s = 0; s < S; ++s) {
-        const int jlo = s * M, jn = std::min(M, ncr - jlo);
-        if (jn <= 0) break;
-        if ((e = intra(helper, jlo, jn, p.heads * p.batch * jn)) != hipSuccess) return e;
-        if ((e = hipEventRecord(ev[s], helper)) != hipSuccess) return e;
-    }
-    // The state crosses segments through final_state when given, else through
-    // the workspace (final_state may alias initial_state: see the inter kernel).
-    float *state = p.s_final ? p.s_final : carry;
-    for (int s = 0; s < S; ++s) {
-        const int jlo = s * M, jhi = std::min(ncr, jlo + M);
-        if (jhi <= jlo) break;
-        if ((e = hipStreamWaitEvent(p.stream, ev[s], 0)) != hipSuccess) return e;
-        const bool last = jhi >= ncr;
-        if ((e = inter(jlo, jhi, s == 0 ? p.s0 : state, last ? p.s_final : state)) != hipSuccess)
-            return e;
-    }
-    return hipSuccess;
+    // Equal rows: all intra-chunk work, then the chunk chain, on the caller's stream.
+    if ((e = intra(p.stream, 0, ncr, p.heads * p.batch * ncr)) != hipSuccess) return e;
+    return inter(0, ncr, p.s0, p.s_final);
 }
 
 }  // namespace kda

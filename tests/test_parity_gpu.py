@@ -85,14 +85,12 @@ def test_ragged_lengths(T):
 
 @pytest.mark.parametrize("T,B,s0", [(529, 1, True), (1000, 2, False), (4100, 1, True),
                                     (8192 + 33, 1, True)])
-def test_segmented_overlap_path(T, B, s0):
-    """Rows of >= 8 chunks run as overlapped segments (intra-chunk kernels on a
-    helper stream, the chunk chain on the caller's stream, the state carried
-    between segments)."""
+def test_multi_chunk_rows(T, B, s0):
+    """Rows of 9 to 129 chunks, with and without an initial state, one or two rows."""
     check_prefill(small(T=T, B=B, H=2, s0_std=0.05 if s0 else None), 64)
 
 
-def test_segmented_in_place_state_and_no_final():
+def test_in_place_state_and_no_final_on_a_long_row():
     import gated_delta_rule_80_amd as K
     inp = small(T=1500, H=2)
     d = to_dev(inp)
