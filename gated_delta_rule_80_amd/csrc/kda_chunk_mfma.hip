@@ -750,6 +750,10 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
     // record (in bounds, unused) -- so the compiler's wait-count tracking stays
     // exact across the loop.  Each ring slot is refilled for the chunk PF ahead.
     if (state_role) {
+        // The state waves carry the chain from chunk to chunk: let them win
+        // instruction issue on their SIMD over the output and prefetch waves
+        // (priority 2 measured best of 0-3).
+        __builtin_amdgcn_s_setprio(2);
         // State rows (channels) 32t + 16 cl + 4 g4 + e, columns 16 (vt0 + ct) + i16.
         float4v S[2][NCT];
 #pragma unroll
