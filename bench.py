@@ -254,7 +254,8 @@ def main():
                                    "with one log-decay per (token, head)"},
             "roofline": {"bound": "hbm", "kernel": "kda_chunk_fwd_scalar_gate",
                          "achieved": round(sgbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(sgbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "frac": round(sgbs / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("kda_chunk_fwd_scalar_gate:T131072_H32"),
                          "alg_bytes_per_launch": sbytes}}
         del gs
 

@@ -14,20 +14,23 @@
 // and, carried across chunks with the state S (d_k x d_v, fp32):
 //   Z = U - W S,   O = Qbar S + H Z,   S <- Diag(e^{G_C}) S + Ktil^T Z.
 // The decay is folded into the vectors ("Kimi Delta Attention: a half-life
-// per channel", section "What changes in the kernel"), but against a
-// reference row m inside the chunk (K e^{G - G_m} and K e^{G_m - G}) so no
-// factor ever divides by the decay of the whole chunk; exponents are
-// differences of cumulative logs as the derivation recommends.
+// per channel", section "What changes in the kernel") with secondary
+// chunking: A and H are built from 16-token sub-chunk blocks, each with its
+// own reference point, so no factor ever divides by the decay of more than
+// half a sub-chunk.  Qbar, L and Ktil only ever scale by e^{x} with x <= 0.
+// Exponents are differences of cumulative logs, as the derivation
+// recommends.  Supported: per-token log-decays down to about -10.9.
 //
 // Kernels
 //   kda_chunk_index  packed sequences -> chunk table (device side, no sync)
 //   kda_intra        one workgroup per (chunk, head), fully parallel: the
-//                    cumulative decay, A and H on MFMA, (I + A)^{-1} (diagonal
+//                    cumulative decay, A and H on MFMA (fp16 for the blocks
+//                    between sub-chunks, split bf16 inside them), (I + A)^{-1} (diagonal
 //                    16x16 blocks by forward substitution, off-diagonal blocks
 //                    by fp32 MFMA), then W and U on MFMA.  Its outputs go to
 //                    the workspace already in the register-fragment order the
 //                    inter kernel consumes.
-//   kda_inter        one workgroup per (sequence, head, 32-column value
+//   kda_inter        one workgroup per (sequence, head, 16-column value
 //                    tile): the sequential chunk loop with the fp32 state
 //                    resident in registers.  Columns of the value space evolve
 //                    independently, so value tiles need no communication.
@@ -96,6 +99,26 @@ __device__ __forceinline__ Chunk chunk_at(int c, const int4 *table, int row_len,
 }
 
 __device__ __forceinline__ float bf(uint16_t x) { return bf16_to_f32(x); }
+
+// Value j of 8 bf16 packed two per word (low half first).
+__device__ __forceinline__ float bf_at(const uint32_t (&w)[4], int j) {
+    return (j & 1) ? __uint_as_float(w[j >> 1] & 0xffff0000u) : __uint_as_float(w[j >> 1] << 16);
+}
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi): about 16 significant
+// bits in two bf16 values, with the range of fp32.
+__device__ __forceinline__ void split_bf16(float x, bf16x8 &hi, bf16x8 &lo, int j) {
+    const __bf16 h = (__bf16)x;
+    hi[j] = h;
+    lo[j] = (__bf16)(x - (float)h);
+}
+
+// D = A * B + C for one 16x16 fp32 tile, K = 32 bf16, same lane layout as mfma16.
+__device__ __forceinline__ float4v mfma16_bf16(bf16x8 a, bf16x8 b, float4v c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 
 // Inclusive prefix sum across the 16 lanes of each DPP row.
 __device__ __forceinline__ float row_scan16(float x) {
@@ -170,9 +193,16 @@ __global__ __launch_bounds__(1024) void kda_chunk_index_kernel(const int32_t *__
 // ------------------------------------------------------------------------------------
 // Intra-chunk kernel.
 // ------------------------------------------------------------------------------------
-// LDS map (bytes).  Stages 1-2: fragment buffers and the transposed Ktil.
-constexpr int L_KP = 0, L_KM = 16384, L_QP = 32768, L_KT = 49152;   // + 18432 -> 67584
+// LDS map (bytes).  Stages 1-2: fp16 fragments [row tile][channel block][lane]
+// of the off-diagonal sub-chunk blocks, and the transposed Ktil.
+constexpr int L_LK = 0;           // K e^{G - E_a}      sub-chunks 1..3   12288
+constexpr int L_LQ = 12288;       // s Q e^{G - E_a}    sub-chunks 1..3   12288
+constexpr int L_RB = 24576;       // K e^{E_{b+1} - G}  sub-chunks 0..2   12288
+constexpr int L_RD = 36864;       // the same times e^{E_a - E_{b+1}}, blocks (2,0), (3,0), (3,1)
+constexpr int L_KT = 49152;       // Ktil^T fp16 [128][TP]  18432 -> 67584
 constexpr int L_NRM = 67584;      // fp32 [4 waves][64 rows][2]: partial |k|^2, |q|^2 (stage 1)
+// Stage 2b-2c: per-wave partial sums of the 8 diagonal blocks, float4 [wave][block][lane].
+constexpr int L_DP = 16640;       // 32768 -> 49408, over dead fragment buffers, clear of sA
 // Stages 3-6 (the fragment buffers are dead by then).
 constexpr int L_A = 0;            // fp32 [64][65]   16640
 constexpr int L_BL = 16640;       // fp16 [128][72]  18432  L^T = (K e^{G})^T
@@ -183,6 +213,10 @@ constexpr int L_BETA = 70144;     // fp32 [64]
 constexpr int L_BYTES = 70400;
 constexpr int TP = 72;            // fp16 pitch of transposed [channel][token] buffers
 constexpr int AP = 65;            // fp32 pitch of A and T
+static_assert(L_KT == L_RD + 12288 && L_KT + 128 * TP * 2 == L_NRM && L_NRM + 2048 <= L_BETA,
+              "stage 1 LDS map");
+static_assert(L_DP >= L_A + 64 * AP * 4 && L_DP + 32768 <= L_BV + 128 * TP * 2,
+              "diagonal partials sit clear of sA and inside the stage 3 buffers");
 
 // Block column J of T = (I + A)^{-1} below the diagonal, by one wave:
 //   X_J = T_JJ;  X_b = -T_bb sum_{k=J}^{b-1} A_bk X_k  for b > J.
@@ -230,6 +264,10 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
     const float *__restrict__ beta, float scale, int form, float eps, int H, int row_len,
     int ncr, const int4 *__restrict__ table, const int32_t *__restrict__ n_chunks, int nc_max,
     int jlo, int jn, uint8_t *__restrict__ recs) {
+    // No FMA contraction in this kernel: the compiler would fuse differently in
+    // each gate layout's instantiation, and a scalar gate would then no longer
+    // give the bits of the same gate repeated over the channels.
+#pragma clang fp contract(off)
     __shared__ __attribute__((aligned(16))) uint8_t smem[L_BYTES];
     const int h = blockIdx.x % H, b = blockIdx.x / H;
     int c;
@@ -249,15 +287,21 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
     const int len = ch.len;
     const int ca = 32 * w + 4 * g4, cb = ca + 16;   // this lane's 8 channels: ca..ca+3, cb..cb+3
 
-    half8 *sKp = reinterpret_cast<half8 *>(smem + L_KP);
-    half8 *sKm = reinterpret_cast<half8 *>(smem + L_KM);
-    half8 *sQp = reinterpret_cast<half8 *>(smem + L_QP);
+    half8 *sLK = reinterpret_cast<half8 *>(smem + L_LK);
+    half8 *sLQ = reinterpret_cast<half8 *>(smem + L_LQ);
+    half8 *sRB = reinterpret_cast<half8 *>(smem + L_RB);
+    half8 *sRD = reinterpret_cast<half8 *>(smem + L_RD);
     _Float16 *sKt = reinterpret_cast<_Float16 *>(smem + L_KT);
     float *sBeta = reinterpret_cast<float *>(smem + L_BETA);
 
     // ---- stage 1: cumulative decay and the decay-scaled operands -------------------
-    float G[4][8], kf[4][8], qf[4][8];
+    // k and q stay packed (two bf16 per word, channels in slot order) and are
+    // expanded where they are used; nk, nq are the per-row L2-norm factors.
+    float G[4][8], nk[4], nq[4];
+    uint32_t kw[4][4], qw[4][4];
     uint2 vra[4], vrb[4];   // this lane's v values (value channels ca.., cb..), used in stage 3
+    // All loads are issued before any of them is used, so the four row tiles
+    // cost one memory round trip; the gate's elementwise form is applied after.
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int i = 16 * r + i16;
@@ -272,18 +316,8 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
             if constexpr (GATE == Gate::PerChannel) {
                 ga = *reinterpret_cast<const float4v *>(g + base + ca);
                 gb = *reinterpret_cast<const float4v *>(g + base + cb);
-                if (form & kFormGateLogit) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        ga[e] = log_sigmoid(ga[e]);
-                        gb[e] = log_sigmoid(gb[e]);
-                    }
-                }
             } else if constexpr (GATE == Gate::Scalar) {
-                float gs = g[(size_t)(ch.t0 + i) * H + h];
-                if (form & kFormGateLogit) gs = log_sigmoid(gs);
-                ga = float4v{gs, gs, gs, gs};
-                gb = ga;
+                ga[0] = g[(size_t)(ch.t0 + i) * H + h];
             }
             ka = *reinterpret_cast<const uint2 *>(k + base + ca);
             kb2 = *reinterpret_cast<const uint2 *>(k + base + cb);
@@ -292,20 +326,35 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
             vra[r] = *reinterpret_cast<const uint2 *>(v + vbase + ca);
             vrb[r] = *reinterpret_cast<const uint2 *>(v + vbase + cb);
         }
-        // Log-decays are kept in base 2 (g log2 e), so every factor below is one exp2.
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            G[r][e] = ga[e] * 1.4426950408889634f;
-            G[r][4 + e] = gb[e] * 1.4426950408889634f;
+            G[r][e] = ga[e];
+            G[r][4 + e] = gb[e];
         }
-        const uint32_t kw[4] = {ka.x, ka.y, kb2.x, kb2.y}, qw[4] = {qa.x, qa.y, qb.x, qb.y};
+        kw[r][0] = ka.x, kw[r][1] = ka.y, kw[r][2] = kb2.x, kw[r][3] = kb2.y;
+        qw[r][0] = qa.x, qw[r][1] = qa.y, qw[r][2] = qb.x, qw[r][3] = qb.y;
+        nk[r] = 1.f;
+        nq[r] = 1.f;
+    }
+    // Gate as a logit: log a = log sigmoid(x) on the valid rows (padding rows
+    // keep log a = 0).  A scalar gate is broadcast over the channels.  Log-decays
+    // are then kept in base 2 (g log2 e), so every factor below is one exp2.
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            kf[r][2 * e] = bf(kw[e] & 0xffff);
-            kf[r][2 * e + 1] = bf(kw[e] >> 16);
-            qf[r][2 * e] = bf(qw[e] & 0xffff);
-            qf[r][2 * e + 1] = bf(qw[e] >> 16);
+    for (int r = 0; r < 4; ++r) {
+        const bool ok = 16 * r + i16 < len;
+        if constexpr (GATE == Gate::Scalar) {
+            float gs = G[r][0];
+            if ((form & kFormGateLogit) && ok) gs = log_sigmoid(gs);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) G[r][j] = gs;
+        } else if constexpr (GATE == Gate::PerChannel) {
+            if ((form & kFormGateLogit) && ok) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) G[r][j] = log_sigmoid(G[r][j]);
+            }
         }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) G[r][j] *= 1.4426950408889634f;
     }
     if (tid < C) {
         const int i = tid;
@@ -323,8 +372,9 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
             float a = 0.f, b = 0.f;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                a += kf[r][j] * kf[r][j];
-                b += qf[r][j] * qf[r][j];
+                const float kx = bf_at(kw[r], j), qx = bf_at(qw[r], j);
+                a += kx * kx;
+                b += qx * qx;
             }
             a += __shfl_xor(a, 16, 64);
             a += __shfl_xor(a, 32, 64);
@@ -345,111 +395,168 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
                 a += sNrm[(ww * 64 + i) * 2 + 0];
                 b += sNrm[(ww * 64 + i) * 2 + 1];
             }
-            const float ia = rsqrtf(a + eps), ib = rsqrtf(b + eps);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                kf[r][j] *= ia;
-                qf[r][j] *= ib;
-            }
+            nk[r] = rsqrtf(a + eps);
+            nq[r] = rsqrtf(b + eps);
         }
     }
-    // Inclusive cumsum along tokens: scan inside each 16-token tile, carry across tiles.
+    // Secondary chunking ("Kimi Delta Attention: a half-life per channel",
+    // section "What changes in the kernel"): the decay is folded into the
+    // vectors relative to a point inside the chunk, never across the whole
+    // chunk.  With E_a the cumulative log-decay before 16-token sub-chunk a
+    // (E_0 = 0, E_4 = G_C), for sub-chunks a > b the factor e^{G_i - G_j}
+    // (i in a, j in b) splits at the boundary before sub-chunk a:
+    //   e^{G_i - E_a} * e^{E_{b+1} - G_j} * e^{E_a - E_{b+1}},
+    // three factors that are all <= 1, so the fp16 operands cannot overflow
+    // whatever the decay.  Inside a sub-chunk the split is taken at the
+    // mid-point M_a = (E_a + E_{a+1}) / 2, so each factor lies within
+    // e^{+-(E_a - E_{a+1}) / 2}: in range for fp32 and bf16 while the decay of
+    // 16 tokens stays above about -175 (-10.9 per token).
+    // Kept per (sub-chunk, channel): M_a and the half-decay h_a = e^{(E_{a+1} -
+    // E_a) / 2}; s_a = h_a^2 is the sub-chunk's whole decay, and the other
+    // factors are products of those: e^{E_a} = s_0 .. s_{a-1}, e^{G_C - E_{a+1}}
+    // = s_{a+1} .. s_3, e^{E_a - E_{b+1}} = s_{b+1} .. s_{a-1}.  Products of
+    // factors <= 1 only underflow where the exact value is below the fp32 range.
+    float M[4][8], hf[4][8];
+    float dmax = 0.f;   // largest sub-chunk decay (log2) among this lane's channels
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        float carry = 0.f;
+        float carry = 0.f;   // inclusive cumsum: scan inside each sub-chunk, carry across
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const float x = row_scan16(G[r][j]);
+            const float ea = carry;
             G[r][j] = carry + x;
             carry += __shfl(x, (l & 48) | 15, 64);
+            M[r][j] = 0.5f * (ea + carry);
+            hf[r][j] = __builtin_amdgcn_exp2f(0.5f * (carry - ea));
+            dmax = fmaxf(dmax, ea - carry);
         }
-    }
-    // Reference row m (middle of the valid rows) and the chunk's last row.
-    const int m = (len - 1) >> 1, rm = m >> 4, im = m & 15;
-    float Gm[8], Em[8], ECm[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        float x = G[0][j];
-#pragma unroll
-        for (int r = 1; r < 4; ++r) x = (rm == r) ? G[r][j] : x;
-        Gm[j] = __shfl(x, (l & 48) | im, 64);
-        const float gl = __shfl(G[3][j], (l & 48) | 15, 64);   // padding rows add 0
-        Em[j] = __builtin_amdgcn_exp2f(Gm[j]);
-        ECm[j] = __builtin_amdgcn_exp2f(gl - Gm[j]);
         // e^{G_C} for the state decay, written by one lane per channel group
         if (i16 == 0) {
             float *ge = reinterpret_cast<float *>(rec + REC_GE);
-            ge[(j < 4 ? ca + j : cb + j - 4)] = __builtin_amdgcn_exp2f(gl);
+            ge[(j < 4 ? ca + j : cb + j - 4)] = __builtin_amdgcn_exp2f(carry);
         }
     }
-    float Kp[4][8];   // kept for (beta L)^T in stage 3
+    // Where no sub-chunk of this wave's channels decays by more than 2^-8, the
+    // mid-point factors stay within 2^{+-4} and the diagonal blocks use plain
+    // fp16 operands like the others; stronger decays take bf16 MFMA with each
+    // operand split into a high and a low bf16 part (three products, about 16
+    // significant bits).  The choice is per wave (each wave sums its own 32
+    // channels), so it needs no exchange.
+    const bool diag_fp16 = __all(dmax <= 8.f);
+    half8 hL[4];         // L = K e^{G} in fp16, kept for stage 3
+    float4v accD[8];     // diagonal blocks over this wave's 32 channels: A(r, r), then H^T(r, r)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        half8 hkp, hkm, hqp, hqb;
+        half8 hlk, hlq, hrb, hrd0, hrd1, hqb;
+        float dlk[8], dlq[8], drk[8];   // diagonal-block operands before rounding
         const int i = 16 * r + i16;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const float e1 = __builtin_amdgcn_exp2f(G[r][j] - Gm[j]);
-            const float e2 = __builtin_amdgcn_exp2f(Gm[j] - G[r][j]);
-            const float kp = kf[r][j] * e1, km = kf[r][j] * e2, qp = scale * qf[r][j] * e1;
-            Kp[r][j] = kp;
-            hkp[j] = (_Float16)kp;
-            hkm[j] = (_Float16)km;
-            hqp[j] = (_Float16)qp;
-            hqb[j] = (_Float16)(qp * Em[j]);
+            // DL = e^{G_i - M_a}, DR = e^{M_a - G_i} lie within 1 / h_a and h_a;
+            // X = e^{G_i - E_a} = DL h_a and Y = e^{E_{a+1} - G_i} = DR h_a are <= 1.
+            const float DL = __builtin_amdgcn_exp2f(G[r][j] - M[r][j]);
+            const float DR = __builtin_amdgcn_exp2f(M[r][j] - G[r][j]);
+            const float X = DL * hf[r][j], Y = DR * hf[r][j];
+            float sd[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) sd[t] = hf[t][j] * hf[t][j];
+            float P = 1.f, Qf = 1.f;                           // e^{E_a}, e^{G_C - E_{a+1}}
+#pragma unroll
+            for (int t = 0; t < r; ++t) P *= sd[t];
+#pragma unroll
+            for (int t = 3; t > r; --t) Qf *= sd[t];
+            const float kk = bf_at(kw[r], j) * nk[r], qq = scale * (bf_at(qw[r], j) * nq[r]);
+            const float eG = X * P;                            // e^{G_i}
+            hL[r][j] = (_Float16)(kk * eG);
+            hqb[j] = (_Float16)(qq * eG);
+            hlk[j] = (_Float16)(kk * X);
+            hlq[j] = (_Float16)(qq * X);
+            const float ky = kk * Y;
+            hrb[j] = (_Float16)ky;
+            // blocks (2, 0) and (3, 1) scale by the sub-chunk between them, (3, 0) by two
+            hrd0[j] = (_Float16)(ky * (r == 0 ? sd[1] : sd[2]));
+            hrd1[j] = (_Float16)(ky * (sd[1] * sd[2]));
             const int cc = j < 4 ? ca + j : cb + j - 4;
-            sKt[cc * TP + i] = (_Float16)(km * ECm[j]);
+            sKt[cc * TP + i] = (_Float16)(ky * Qf);           // Ktil = K e^{G_C - G}
+            dlk[j] = kk * DL;
+            dlq[j] = qq * DL;
+            drk[j] = kk * DR;
         }
-        sKp[(r * 4 + w) * 64 + l] = hkp;
-        sKm[(r * 4 + w) * 64 + l] = hkm;
-        sQp[(r * 4 + w) * 64 + l] = hqp;
+        if (r >= 1) {
+            sLK[((r - 1) * 4 + w) * 64 + l] = hlk;
+            sLQ[((r - 1) * 4 + w) * 64 + l] = hlq;
+        }
+        if (r <= 2) sRB[(r * 4 + w) * 64 + l] = hrb;
+        if (r == 0) {
+            sRD[(0 * 4 + w) * 64 + l] = hrd0;   // block (2, 0)
+            sRD[(1 * 4 + w) * 64 + l] = hrd1;   // block (3, 0)
+        }
+        if (r == 1) sRD[(2 * 4 + w) * 64 + l] = hrd0;   // block (3, 1)
         reinterpret_cast<half8 *>(rec + REC_Q)[(r * 4 + w) * 64 + l] = hqb;
+        // Diagonal block r: A rows i / columns j, H^T rows j / columns i.
+        float4v a = {0, 0, 0, 0}, hh = {0, 0, 0, 0};
+        if (diag_fp16) {
+            half8 fk, fq, fr;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                fk[j] = (_Float16)dlk[j];
+                fq[j] = (_Float16)dlq[j];
+                fr[j] = (_Float16)drk[j];
+            }
+            a = mfma16(fk, fr, a);
+            hh = mfma16(fr, fq, hh);
+        } else {
+            bf16x8 lk_hi, lk_lo, lq_hi, lq_lo, rk_hi, rk_lo;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                split_bf16(dlk[j], lk_hi, lk_lo, j);
+                split_bf16(dlq[j], lq_hi, lq_lo, j);
+                split_bf16(drk[j], rk_hi, rk_lo, j);
+            }
+            a = mfma16_bf16(lk_hi, rk_hi, a);
+            a = mfma16_bf16(lk_hi, rk_lo, a);
+            a = mfma16_bf16(lk_lo, rk_hi, a);
+            hh = mfma16_bf16(rk_hi, lq_hi, hh);
+            hh = mfma16_bf16(rk_lo, lq_hi, hh);
+            hh = mfma16_bf16(rk_hi, lq_lo, hh);
+        }
+        accD[r] = a;
+        accD[4 + r] = hh;
     }
     lds_barrier();
 
-    // ---- stage 2: A (10 tiles) and H^T (10 tiles) on MFMA; Ktil^T fragments out ---
-    // Tile t in 0..9 is the t-th (row, col) pair with col <= row in row-major order;
-    // list entries 0..9 are A(row, col), 10..19 are H^T(col, row).  Wave w takes
-    // entries w, w+4, w+8, w+12, w+16: slots 0 and 1 are always A tiles, slot 2 is an
-    // A tile for w < 2, slots 3 and 4 are always H^T tiles.
-    float4v accA[3];
+    // ---- stage 2: off-diagonal blocks of A and H^T on MFMA; Ktil^T fragments out ----
+    // Block u = 0..5 is the sub-chunk pair (a, b) = (1,0), (2,0), (2,1), (3,0),
+    // (3,1), (3,2); list entries 0..5 are A(a, b), 6..11 are H^T(b, a).  Wave w
+    // takes entries w, w+4, w+8: slot 0 is always an A block, slot 1 is an A
+    // block for w < 2, slot 2 is always an H^T block.
+    float4v accA[2];
 #pragma unroll
-    for (int s = 0; s < 5; ++s) {
+    for (int s = 0; s < 3; ++s) {
         const int t = w + 4 * s;
-        const bool is_a = t < 10;
-        const int u = is_a ? t : t - 10;
-        const int r = u >= 6 ? 3 : (u >= 3 ? 2 : (u >= 1 ? 1 : 0));
-        const int j = u - (r * (r + 1)) / 2;
+        const bool is_a = t < 6;
+        const int u = is_a ? t : t - 6;
+        const int a = u >= 3 ? 3 : (u >= 1 ? 2 : 1);
+        const int b = u - (a * (a - 1)) / 2;
+        const half8 *right = (a == b + 1) ? sRB + b * 256 : sRD + (u == 1 ? 0 : (u == 3 ? 1 : 2)) * 256;
+        const half8 *lk = sLK + (a - 1) * 256, *lq = sLQ + (a - 1) * 256;
         float4v acc = {0, 0, 0, 0};
         if (is_a) {
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-                acc = mfma16(sKp[(r * 4 + kb) * 64 + l], sKm[(j * 4 + kb) * 64 + l], acc);
-            // A_ij = beta_i * acc for j < i (rows i = 16r + 4 g4 + e, col j = 16 j + i16)
+            for (int kb = 0; kb < 4; ++kb) acc = mfma16(lk[kb * 64 + l], right[kb * 64 + l], acc);
+            // A_ij = beta_i * acc (rows i = 16a + 4 g4 + e, all columns j < i)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int ii = 16 * r + 4 * g4 + e, jj = 16 * j + i16;
-                acc[e] = (jj < ii) ? acc[e] * sBeta[ii] : 0.f;
-            }
-            if (s < 3) accA[s < 3 ? s : 0] = acc;
+            for (int e = 0; e < 4; ++e) acc[e] *= sBeta[16 * a + 4 * g4 + e];
+            if (s < 2) accA[s] = acc;
         } else {
-            const int it = r, jt = j;
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-                acc = mfma16(sKm[(jt * 4 + kb) * 64 + l], sQp[(it * 4 + kb) * 64 + l], acc);
-            // H^T rows j = 16 jt + 4 g4 + e, column i = 16 it + i16; H_ij needs j <= i.
+            for (int kb = 0; kb < 4; ++kb) acc = mfma16(right[kb * 64 + l], lq[kb * 64 + l], acc);
             half4 hv;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int jj = 16 * jt + 4 * g4 + e, ii = 16 * it + i16;
-                hv[e] = (_Float16)((jj <= ii) ? acc[e] : 0.f);
-            }
-            uint8_t *dst = rec + REC_H + (h_slot(it, jt >> 1) * 64 + l) * 16;
-            *reinterpret_cast<half4 *>(dst + (jt & 1) * 8) = hv;
-            if (jt == it && !(jt & 1)) {
-                const half4 z = {0, 0, 0, 0};
-                *reinterpret_cast<half4 *>(dst + 8) = z;
-            }
+            for (int e = 0; e < 4; ++e) hv[e] = (_Float16)acc[e];
+            uint8_t *dst = rec + REC_H + (h_slot(a, b >> 1) * 64 + l) * 16;
+            *reinterpret_cast<half4 *>(dst + (b & 1) * 8) = hv;
         }
     }
     // Ktil^T fragments: channel tiles 2w, 2w+1, token blocks 0, 1.
@@ -472,39 +579,44 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
     }
     lds_barrier();
 
-    // ---- stage 3: A to LDS; L^T and V^T transposed into LDS --------------------------
-    // beta is applied to the columns of T in stage 6 (W = (T Diag(beta)) L and
-    // U = (T Diag(beta)) V), so L and V go to LDS unscaled.
+    // ---- stage 2b: diagonal partial sums to LDS; off-diagonal A blocks into sA ------
     float *sA = reinterpret_cast<float *>(smem + L_A);
-    _Float16 *sBL = reinterpret_cast<_Float16 *>(smem + L_BL);
-    _Float16 *sBV = reinterpret_cast<_Float16 *>(smem + L_BV);
+    float4v *sDP = reinterpret_cast<float4v *>(smem + L_DP);
 #pragma unroll
-    for (int s = 0; s < 3; ++s) {
+    for (int d = 0; d < 8; ++d) sDP[(w * 8 + d) * 64 + l] = accD[d];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
         const int t = w + 4 * s;
-        if (t < 10) {
-            const int r = t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0));
-            const int j = t - (r * (r + 1)) / 2;
+        if (t < 6) {
+            const int a = t >= 3 ? 3 : (t >= 1 ? 2 : 1);
+            const int b = t - (a * (a - 1)) / 2;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sA[(16 * r + 4 * g4 + e) * AP + 16 * j + i16] = accA[s][e];
-        }
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int i = 16 * r + i16;   // rows past the end hold zeros (masked loads)
-        const uint32_t vw[4] = {vra[r].x, vra[r].y, vrb[r].x, vrb[r].y};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int cc = j < 4 ? ca + j : cb + j - 4;
-            sBL[cc * TP + i] = (_Float16)(Kp[r][j] * Em[j]);
-            const float vv = bf((j & 1) ? (vw[j >> 1] >> 16) : (vw[j >> 1] & 0xffff));
-            sBV[cc * TP + i] = (_Float16)vv;
+            for (int e = 0; e < 4; ++e) sA[(16 * a + 4 * g4 + e) * AP + 16 * b + i16] = accA[s][e];
         }
     }
     lds_barrier();
 
-    // ---- stage 4: inverses of the four diagonal 16x16 blocks of (I + A) ------------
+    // ---- stage 4: diagonal blocks summed in wave order; their inverses -------------
+    // Wave 0 sums the four diagonal blocks of A into sA and inverts the four
+    // diagonal 16x16 blocks of (I + A) (it alone touches sA and sTf here);
+    // waves 1-3 sum the four diagonal blocks of H^T into the record.
     float *sTf = reinterpret_cast<float *>(smem + L_TF);
     if (w == 0) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            float4v a = sDP[(0 * 8 + b) * 64 + l];
+#pragma unroll
+            for (int ww = 1; ww < 4; ++ww) a += sDP[(ww * 8 + b) * 64 + l];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int ra = 16 * b + 4 * g4 + e, cc = 16 * b + i16;
+                sA[ra * AP + cc] = (cc < ra) ? a[e] * sBeta[ra] : 0.f;
+            }
+        }
+        // The block inversion reads what other lanes of this wave just wrote:
+        // LDS executes a wave's operations in order; wait for the writes and
+        // keep the compiler from moving the reads above them.
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         const int b = l >> 4, jc = l & 15;   // block b, column jc
         float X[16];
 #pragma unroll
@@ -517,15 +629,54 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) sTf[(16 * b + i) * AP + 16 * b + jc] = X[i];
+    } else {
+        // block b of H^T for b = w - 1, and block 3 also by wave 1
+#pragma unroll
+        for (int rep = 0; rep < 2; ++rep) {
+            const int b = rep == 0 ? w - 1 : 3;
+            if (rep == 1 && w != 1) break;
+            float4v hs = sDP[(0 * 8 + 4 + b) * 64 + l];
+#pragma unroll
+            for (int ww = 1; ww < 4; ++ww) hs += sDP[(ww * 8 + 4 + b) * 64 + l];
+            half4 hv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int rj = 16 * b + 4 * g4 + e, ci = 16 * b + i16;   // H^T(rj, ci) = H(ci, rj)
+                hv[e] = (_Float16)((rj <= ci) ? hs[e] : 0.f);
+            }
+            uint8_t *dst = rec + REC_H + (h_slot(b, b >> 1) * 64 + l) * 16;
+            *reinterpret_cast<half4 *>(dst + (b & 1) * 8) = hv;
+            if (!(b & 1)) {
+                const half4 z = {0, 0, 0, 0};
+                *reinterpret_cast<half4 *>(dst + 8) = z;
+            }
+        }
     }
     lds_barrier();
 
-    // ---- stage 5: off-diagonal blocks, block column j by wave j (fp32 MFMA) ---------
+    // ---- stage 5: off-diagonal blocks of T, block column j by wave j (fp32 MFMA); ----
+    // ---- stage 3 alongside: L^T and V^T transposed into LDS (over the dead partials)
+    // beta is applied to the columns of T in stage 6 (W = (T Diag(beta)) L and
+    // U = (T Diag(beta)) V), so L and V go to LDS unscaled.
     switch (w) {
     case 0: offdiag_column<0>(sA, sTf, g4, i16); break;
     case 1: offdiag_column<1>(sA, sTf, g4, i16); break;
     case 2: offdiag_column<2>(sA, sTf, g4, i16); break;
     default: break;
+    }
+    _Float16 *sBL = reinterpret_cast<_Float16 *>(smem + L_BL);
+    _Float16 *sBV = reinterpret_cast<_Float16 *>(smem + L_BV);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int i = 16 * r + i16;   // rows past the end hold zeros (masked loads)
+        const uint32_t vw[4] = {vra[r].x, vra[r].y, vrb[r].x, vrb[r].y};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int cc = j < 4 ? ca + j : cb + j - 4;
+            sBL[cc * TP + i] = hL[r][j];
+            const float vv = bf((j & 1) ? (vw[j >> 1] >> 16) : (vw[j >> 1] & 0xffff));
+            sBV[cc * TP + i] = (_Float16)vv;
+        }
     }
     lds_barrier();
 

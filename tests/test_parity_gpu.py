@@ -201,13 +201,61 @@ def test_varlen_equals_separate_calls():
         assert np.array_equal(o1, o[a:b]) and np.array_equal(s1[0], fs[n])
 
 
-def test_strong_decay_within_documented_range():
-    # per-token log-decay about -0.23 puts a chunk's cumulative decay near -15,
-    # inside the documented bound (> -16 per 64-token chunk) of the MFMA path
+def test_moderate_decay_near_the_old_chunk_bound():
+    # per-token log-decay about -0.23: a chunk's cumulative decay near -15,
+    # where a single reference row per chunk would already leave fp16's range
     inp = small(T=256, z=(1.2, 1.5), s0_std=0.05)
     per_chunk = inp["g"].reshape(1, 4, 64, 2, 128).sum(dim=2)
-    assert float(per_chunk.min()) > -16.0
+    assert float(per_chunk.min()) < -14.0
     check_prefill(inp, 64)
+
+
+def _strong_gate(inp, lo, hi, seed, mixed=False):
+    """Replaces the log-decays by U(lo, hi) draws; with ``mixed`` every other
+    channel keeps its weak decay, so long and short memories share a head."""
+    gen = torch.Generator().manual_seed(seed)
+    g = lo + (hi - lo) * torch.rand(inp["g"].shape, generator=gen, dtype=torch.float64)
+    g = g.to(torch.float32)
+    if mixed:
+        g[..., 0::2] = inp["g"][..., 0::2]
+    inp["g"] = g.contiguous()
+    return inp
+
+
+@pytest.mark.parametrize("lo,hi,mixed", [(-5.0, 0.0, False), (-5.0, -4.0, False),
+                                         (-10.0, -9.0, False), (-10.0, 0.0, True)])
+def test_strong_decay_sub_chunks(lo, hi, mixed):
+    """Per-token log-decays down to -10 (the pages' layer bounds them at -5): a
+    chunk's cumulative decay reaches -640, far outside any single-reference
+    range, and the 16-token sub-chunks keep every factor finite."""
+    inp = _strong_gate(small(T=333, H=2, s0_std=0.05), lo, hi, seed=61, mixed=mixed)
+    check_prefill(inp, 64)
+
+
+def test_strong_decay_varlen_and_scalar_gate():
+    import gated_delta_rule_80_amd as K
+    inp = _strong_gate(small(H=2, lengths=[70, 1, 200, 64, 17], s0_std=0.05), -6.0, 0.0,
+                       seed=62)
+    check_prefill(inp, 64)
+    # one value per (token, head) through the scalar-gate entry point
+    gs = inp["g"][..., 0].contiguous()
+    inp["g"] = gs[..., None].expand(*gs.shape, 128).contiguous()
+    o_ref, s_ref = oracle_prefill(inp, None, None)
+    d = to_dev(inp)
+    o, fs = K.chunk_fwd_scalar_gate(d["q"], d["k"], d["v"], gs.cuda(), d["beta"],
+                                    scale=d["scale"], initial_state=d["initial_state"],
+                                    cu_seqlens=d["cu_seqlens"])
+    torch.cuda.synchronize()
+    o64 = o.double().cpu().numpy()
+    eo = rel_err(o64.reshape(-1, *o64.shape[2:]), o_ref)
+    es = rel_err(fs.double().cpu().numpy(), s_ref)
+    print("scalar gate, strong decay: err o %.3e  S %.3e" % (eo, es), flush=True)
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_strong_decay_fp32_path():
+    inp = _strong_gate(small(T=150, H=2, dk=64, dv=64, dtype="f32"), -10.0, 0.0, seed=63)
+    check_prefill(inp, 32)
 
 
 # ---------------------------------------------------------------- degenerate cases of the method
