@@ -597,59 +597,48 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
     lds_barrier();
 
     // ---- stage 4: diagonal blocks summed in wave order; their inverses -------------
-    // Wave 0 sums the four diagonal blocks of A into sA and inverts the four
-    // diagonal 16x16 blocks of (I + A) (it alone touches sA and sTf here);
-    // waves 1-3 sum the four diagonal blocks of H^T into the record.
+    // Wave w sums diagonal block w of A (into sA) and of H^T (into the record),
+    // then inverts diagonal block w of (I + A) with 16 lanes, one per column.
+    // It reads only what it wrote, so no barrier is needed in between.
     float *sTf = reinterpret_cast<float *>(smem + L_TF);
-    if (w == 0) {
+    {
+        float4v a = sDP[(0 * 8 + w) * 64 + l], hs = sDP[(0 * 8 + 4 + w) * 64 + l];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            float4v a = sDP[(0 * 8 + b) * 64 + l];
-#pragma unroll
-            for (int ww = 1; ww < 4; ++ww) a += sDP[(ww * 8 + b) * 64 + l];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int ra = 16 * b + 4 * g4 + e, cc = 16 * b + i16;
-                sA[ra * AP + cc] = (cc < ra) ? a[e] * sBeta[ra] : 0.f;
-            }
+        for (int ww = 1; ww < 4; ++ww) {
+            a += sDP[(ww * 8 + w) * 64 + l];
+            hs += sDP[(ww * 8 + 4 + w) * 64 + l];
         }
-        // The block inversion reads what other lanes of this wave just wrote:
-        // LDS executes a wave's operations in order; wait for the writes and
-        // keep the compiler from moving the reads above them.
+        half4 hv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int rr = 16 * w + 4 * g4 + e, cc = 16 * w + i16;
+            // A(rr, cc) for cc < rr; H^T(rr, cc) = H(cc, rr) for rr <= cc
+            sA[rr * AP + cc] = (cc < rr) ? a[e] * sBeta[rr] : 0.f;
+            hv[e] = (_Float16)((rr <= cc) ? hs[e] : 0.f);
+        }
+        uint8_t *dst = rec + REC_H + (h_slot(w, w >> 1) * 64 + l) * 16;
+        *reinterpret_cast<half4 *>(dst + (w & 1) * 8) = hv;
+        if (!(w & 1)) {
+            const half4 z = {0, 0, 0, 0};
+            *reinterpret_cast<half4 *>(dst + 8) = z;
+        }
+        // The inversion reads what other lanes of this wave just wrote: LDS
+        // executes a wave's operations in order; wait for the writes and keep
+        // the compiler from moving the reads above them.
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        const int b = l >> 4, jc = l & 15;   // block b, column jc
-        float X[16];
+        if (l < 16) {
+            const int jc = l;   // column of block w
+            float X[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float s = (i == jc) ? 1.f : 0.f;
-            const float *arow = sA + (16 * b + i) * AP + 16 * b;
+            for (int i = 0; i < 16; ++i) {
+                float sum = (i == jc) ? 1.f : 0.f;
+                const float *arow = sA + (16 * w + i) * AP + 16 * w;
 #pragma unroll
-            for (int kk = 0; kk < i; ++kk) s -= arow[kk] * X[kk];
-            X[i] = s;
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sTf[(16 * b + i) * AP + 16 * b + jc] = X[i];
-    } else {
-        // block b of H^T for b = w - 1, and block 3 also by wave 1
-#pragma unroll
-        for (int rep = 0; rep < 2; ++rep) {
-            const int b = rep == 0 ? w - 1 : 3;
-            if (rep == 1 && w != 1) break;
-            float4v hs = sDP[(0 * 8 + 4 + b) * 64 + l];
-#pragma unroll
-            for (int ww = 1; ww < 4; ++ww) hs += sDP[(ww * 8 + 4 + b) * 64 + l];
-            half4 hv;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int rj = 16 * b + 4 * g4 + e, ci = 16 * b + i16;   // H^T(rj, ci) = H(ci, rj)
-                hv[e] = (_Float16)((rj <= ci) ? hs[e] : 0.f);
+                for (int kk = 0; kk < i; ++kk) sum -= arow[kk] * X[kk];
+                X[i] = sum;
             }
-            uint8_t *dst = rec + REC_H + (h_slot(b, b >> 1) * 64 + l) * 16;
-            *reinterpret_cast<half4 *>(dst + (b & 1) * 8) = hv;
-            if (!(b & 1)) {
-                const half4 z = {0, 0, 0, 0};
-                *reinterpret_cast<half4 *>(dst + 8) = z;
-            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sTf[(16 * w + i) * AP + 16 * w + jc] = X[i];
         }
     }
     lds_barrier();

@@ -232,6 +232,33 @@ def test_strong_decay_sub_chunks(lo, hi, mixed):
     check_prefill(inp, 64)
 
 
+def test_sub_chunk_edges_in_ragged_sequences():
+    """Lengths that end inside, on and just past 16-token sub-chunk boundaries,
+    with strong decays (each sub-chunk of a chunk has its own split point)."""
+    lengths = [1, 15, 16, 17, 31, 33, 63, 65, 130]
+    inp = _strong_gate(small(H=2, lengths=lengths, s0_std=0.05), -8.0, 0.0, seed=64)
+    check_prefill(inp, 64)
+
+
+def test_weak_and_strong_channel_blocks_in_one_head():
+    """Channels 0-63 decay weakly and 64-127 strongly: the waves owning the
+    first two 32-channel blocks take the fp16 path for the diagonal sub-chunk
+    blocks, the other two the split-bf16 path, and their shares are summed."""
+    inp = small(T=200, H=2, s0_std=0.05)
+    weak = inp["g"][..., :64].clone()
+    inp = _strong_gate(inp, -7.0, -1.0, seed=65)
+    inp["g"][..., :64] = weak
+    check_prefill(inp, 64)
+
+
+@pytest.mark.parametrize("lo,hi", [(-0.40, -0.30), (-0.36, -0.34)])
+def test_decay_at_the_fp16_diagonal_threshold(lo, hi):
+    """Sub-chunk decays near 2^-8 (about -0.35 per token), where a wave's choice
+    between fp16 and split-bf16 diagonal operands flips from chunk to chunk."""
+    inp = _strong_gate(small(T=320, H=2, s0_std=0.05), lo, hi, seed=66)
+    check_prefill(inp, 64)
+
+
 def test_strong_decay_varlen_and_scalar_gate():
     import gated_delta_rule_80_amd as K
     inp = _strong_gate(small(H=2, lengths=[70, 1, 200, 64, 17], s0_std=0.05), -6.0, 0.0,
