@@ -296,7 +296,8 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
 
     // ---- stage 1: cumulative decay and the decay-scaled operands -------------------
     // k and q stay packed (two bf16 per word, channels in slot order) and are
-    // expanded where they are used; nk, nq are the per-row L2-norm factors.
+    // expanded where they are used; nk, nq are the per-row L2-norm factors
+    // (nq also carries the query scale s).
     float G[4][8], nk[4], nq[4];
     uint32_t kw[4][4], qw[4][4];
     uint2 vra[4], vrb[4];   // this lane's v values (value channels ca.., cb..), used in stage 3
@@ -334,7 +335,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
         kw[r][0] = ka.x, kw[r][1] = ka.y, kw[r][2] = kb2.x, kw[r][3] = kb2.y;
         qw[r][0] = qa.x, qw[r][1] = qa.y, qw[r][2] = qb.x, qw[r][3] = qb.y;
         nk[r] = 1.f;
-        nq[r] = 1.f;
+        nq[r] = scale;   // the query scale rides on the per-row factor
     }
     // Gate as a logit: log a = log sigmoid(x) on the valid rows (padding rows
     // keep log a = 0).  A scalar gate is broadcast over the channels.  Log-decays
@@ -396,7 +397,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
                 b += sNrm[(ww * 64 + i) * 2 + 1];
             }
             nk[r] = rsqrtf(a + eps);
-            nq[r] = rsqrtf(b + eps);
+            nq[r] = scale * rsqrtf(b + eps);
         }
     }
     // Secondary chunking ("Kimi Delta Attention: a half-life per channel",
@@ -466,12 +467,12 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
             for (int t = 0; t < r; ++t) P *= sd[t];
 #pragma unroll
             for (int t = 3; t > r; --t) Qf *= sd[t];
-            const float kk = bf_at(kw[r], j) * nk[r], qq = scale * (bf_at(qw[r], j) * nq[r]);
-            const float eG = X * P;                            // e^{G_i}
-            hL[r][j] = (_Float16)(kk * eG);
-            hqb[j] = (_Float16)(qq * eG);
-            hlk[j] = (_Float16)(kk * X);
-            hlq[j] = (_Float16)(qq * X);
+            const float kk = bf_at(kw[r], j) * nk[r], qq = bf_at(qw[r], j) * nq[r];
+            const float kX = kk * X, qX = qq * X;
+            hL[r][j] = (_Float16)(kX * P);                     // L = K e^{G}
+            hqb[j] = (_Float16)(qX * P);                       // Qbar = s Q e^{G}
+            hlk[j] = (_Float16)kX;
+            hlq[j] = (_Float16)qX;
             const float ky = kk * Y;
             hrb[j] = (_Float16)ky;
             // blocks (2, 0) and (3, 1) scale by the sub-chunk between them, (3, 0) by two
