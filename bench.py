@@ -5,7 +5,9 @@ One step = one chunkwise prefill (``kda_chunk_fwd``) of the long-context
 workload (B=1, H=32, T=131072, d_k=d_v=128, C=64, bf16 storage) with every
 input already resident in HBM.  The same run also times the batched decode
 step (``kda_decode_step``: 128 sessions x 32 heads, 268 MB fp32 state updated
-in place) and the fp64 CPU oracle on a bounded sample of the prefill workload.
+in place), the same prefill through the scalar-gate entry point, the packed
+varlen workload (8 sequences through cu_seqlens), and the fp64 CPU oracle on a
+bounded sample of the prefill workload.
 
 Prints ONE JSON line.  ``value`` is prefill tokens/s; the ``decode`` object
 carries the decode state bandwidth.  Roofline fractions use the algorithmic
@@ -94,6 +96,7 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=32768)
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-scalar-gate", action="store_true")
+    ap.add_argument("--skip-varlen", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="finally run a plain device copy kernel over this many MiB three times: "
                          "the known-size reference for hardware byte counters")
@@ -258,6 +261,52 @@ def main():
                          "traffic": measured_traffic("kda_chunk_fwd_scalar_gate:T131072_H32"),
                          "alg_bytes_per_launch": sbytes}}
         del gs
+
+    if not args.skip_varlen:
+        # The packed workload: 8 sequences of seeded lengths in one buffer with
+        # cu_seqlens, zero initial states, one final state per sequence.
+        w4 = W.WORKLOADS[4]
+        print("[bench] varlen prefill: %s" % w4.description, file=sys.stderr, flush=True)
+        inp4 = W.make_workload(4)
+        d4 = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp4.items()}
+        B4, T4, H4, dk4 = d4["q"].shape
+        N4 = inp4["n_seqs"]
+        ws4 = torch.empty(K.workspace_bytes(B4, T4, H4, dk4, dv, w4.chunk, N4), dtype=torch.uint8,
+                          device=dev)
+        o4 = torch.empty((B4, T4, H4, dv), dtype=torch.bfloat16, device=dev)
+        fs4 = torch.empty((N4, H4, dk4, dv), dtype=torch.float32, device=dev)
+
+        def vstep():
+            K.chunk_fwd(d4["q"], d4["k"], d4["v"], d4["g"], d4["beta"], scale=d4["scale"],
+                        initial_state=None, cu_seqlens=d4["cu_seqlens"], chunk_size=w4.chunk,
+                        workspace=ws4, out=o4, final_state=fs4)
+
+        for _ in range(3):
+            vstep()
+        torch.cuda.synchronize()
+        n_v = max(1, args.steps // 2)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n_v):
+            vstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        vms = e0.elapsed_time(e1) / n_v
+        vtok = B4 * T4
+        vbytes = prefill_alg_bytes(vtok, H4, dk4, dv, N4, has_s0=False)
+        vgbs = vbytes / (vms * 1e-3) / 1e9
+        lens = [int(x) for x in (inp4["cu_seqlens"][1:] - inp4["cu_seqlens"][:-1]).tolist()]
+        result["varlen"] = {
+            "value": round(vtok / (vms * 1e-3), 1), "unit": "tokens/s",
+            "ms_per_step": round(vms, 4), "steps": n_v,
+            "config": {"workload": "varlen packed prefill, 8 sequences of lengths %s (%d "
+                                   "tokens), H=32 d=128 C=64 bf16, zero initial states"
+                                   % (lens, vtok)},
+            "roofline": {"bound": "hbm", "kernel": "kda_chunk_fwd (cu_seqlens)",
+                         "achieved": round(vgbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(vgbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "alg_bytes_per_launch": vbytes}}
+        del d4, inp4, ws4, o4, fs4
 
     if not args.no_cpu_baseline:
         import numpy as np
