@@ -163,11 +163,11 @@ size_t kda_chunk_fwd_workspace_bytes(const kda_shape *shape);
  * Each sequence is cut into chunks of C tokens from its first token; the last
  * chunk may be shorter.  Chunks never straddle sequences.
  * Supported decay range: any cumulative decay; on the MFMA path every
- * per-token log-decay must be >= -10 (the kernels split each 64-token chunk
+ * per-token log-decay must be finite and >= -10 (the kernels split each 64-token chunk
  * into 16-token sub-chunks, "Kimi Delta Attention: a half-life per channel",
  * section "What changes in the kernel"; within a sub-chunk the decay-scaled
- * operands then stay inside the fp32 / bf16 range).  The fp32 path has no
- * bound.  Smaller values (a channel that forgets within one token) give
+ * operands then stay inside the fp32 / bf16 range).  The fp32 path takes any
+ * finite value.  Smaller values (a channel that forgets within one token) give
  * non-finite outputs on the MFMA path.  Keys
  * and queries are expected L2-normalised (|k|, |q| <= 1) and |v| well below
  * the fp16 range, as the layer that calls this operator produces them.

@@ -363,6 +363,37 @@ def test_decode_shapes(d, dtype):
     assert rel_err(st.double().cpu().numpy(), ref) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_with_strong_decays(dtype):
+    """Per-token log-decays in [-10, 0] (and exactly -inf for one channel: a
+    channel that forgets everything) through the decode step: it scales the
+    state by e^g directly, so any log-decay is in range."""
+    import gated_delta_rule_80_amd as K
+    w = W.Workload(3, "decode", "decode", H=3, dk=128, dv=128, dtype=dtype, z_range=(2.0, 9.0),
+                   n_sessions=6, steps=5, state_std=0.05)
+    state = W.make_decode_state(w)
+    ref = W.to64(state)
+    st = state.to("cuda")
+    gen = torch.Generator().manual_seed(67)
+    outs, refs = [], []
+    for s in range(w.steps):
+        tok = W.make_decode_step(s, w)
+        tok["g"] = (-10.0 * torch.rand(tok["g"].shape, generator=gen,
+                                       dtype=torch.float64)).to(torch.float32)
+        tok["g"][..., 5] = float("-inf")
+        dd = to_dev(tok)
+        outs.append(K.decode_step(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], st,
+                                  scale=w.scale).double().cpu().numpy())
+        o_ref, ref = oracle.decode_step(*(W.to64(tok[n]) for n in ("q", "k", "v", "g", "beta")),
+                                        w.scale, ref)
+        refs.append(o_ref)
+    torch.cuda.synchronize()
+    eo = rel_err(np.stack(outs), np.stack(refs))
+    es = rel_err(st.double().cpu().numpy(), ref)
+    print("decode, strong decays: err o %.3e  S %.3e" % (eo, es), flush=True)
+    assert np.isfinite(eo) and eo <= TOL[dtype] and es <= TOL[dtype]
+
+
 def test_decode_steps_match_prefill():
     """T decode steps on one session equal a T-token prefill (both on the GPU)."""
     import gated_delta_rule_80_amd as K
