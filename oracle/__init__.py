@@ -15,6 +15,9 @@ Contents
                  recurrence (q/k L2 norm, log sigmoid and sigmoid of logits,
                  RMS norm x weight x sigmoid output gate), pinned by
                  ``tests/test_oracle_layer.py``.
+  backward.py    gradients of the forward: autograd of the recurrence (pinned
+                 to finite differences) and the hand-derived backward of the
+                 chunkwise form (pinned to autograd), ``tests/test_oracle_backward.py``.
   build.py       gcc build of the C oracle.
 
 Every function is pinned by ``tests/test_oracle_pins.py`` against closed
@@ -30,7 +33,7 @@ import os
 
 import numpy as np
 
-from . import layer, reference  # noqa: F401  (re-export)
+from . import backward, layer, reference  # noqa: F401  (re-export)
 from .reference import chunkwise, recurrent, decode_step as decode_step_np  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
