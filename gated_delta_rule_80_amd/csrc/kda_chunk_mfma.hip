@@ -412,118 +412,176 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
     // mid-point M_a = (E_a + E_{a+1}) / 2, so each factor lies within
     // e^{+-(E_a - E_{a+1}) / 2}: in range for fp32 and bf16 while the decay of
     // 16 tokens stays above about -175 (-10.9 per token).
-    // Kept per (sub-chunk, channel): M_a and the half-decay h_a = e^{(E_{a+1} -
-    // E_a) / 2}; s_a = h_a^2 is the sub-chunk's whole decay, and the other
-    // factors are products of those: e^{E_a} = s_0 .. s_{a-1}, e^{G_C - E_{a+1}}
-    // = s_{a+1} .. s_3, e^{E_a - E_{b+1}} = s_{b+1} .. s_{a-1}.  Products of
-    // factors <= 1 only underflow where the exact value is below the fp32 range.
-    float M[4][8], hf[4][8];
-    float dmax = 0.f;   // largest sub-chunk decay (log2) among this lane's channels
+    float E[5][8];
+    float gcmin = 0.f;   // the strongest whole-chunk decay (log2) among this lane's channels
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         float carry = 0.f;   // inclusive cumsum: scan inside each sub-chunk, carry across
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const float x = row_scan16(G[r][j]);
-            const float ea = carry;
+            E[r][j] = carry;
             G[r][j] = carry + x;
             carry += __shfl(x, (l & 48) | 15, 64);
-            M[r][j] = 0.5f * (ea + carry);
-            hf[r][j] = __builtin_amdgcn_exp2f(0.5f * (carry - ea));
-            dmax = fmaxf(dmax, ea - carry);
         }
+        E[4][j] = carry;
+        gcmin = fminf(gcmin, carry);
         // e^{G_C} for the state decay, written by one lane per channel group
         if (i16 == 0) {
             float *ge = reinterpret_cast<float *>(rec + REC_GE);
             ge[(j < 4 ? ca + j : cb + j - 4)] = __builtin_amdgcn_exp2f(carry);
         }
     }
-    // Where no sub-chunk of this wave's channels decays by more than 2^-8, the
-    // mid-point factors stay within 2^{+-4} and the diagonal blocks use plain
-    // fp16 operands like the others; stronger decays take bf16 MFMA with each
-    // operand split into a high and a low bf16 part (three products, about 16
-    // significant bits).  The choice is per wave (each wave sums its own 32
-    // channels), so it needs no exchange.
-    const bool diag_fp16 = __all(dmax <= 8.f);
     half8 hL[4];         // L = K e^{G} in fp16, kept for stage 3
     float4v accD[8];     // diagonal blocks over this wave's 32 channels: A(r, r), then H^T(r, r)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        half8 hlk, hlq, hrb, hrd0, hrd1, hqb;
-        float dlk[8], dlq[8], drk[8];   // diagonal-block operands before rounding
-        const int i = 16 * r + i16;
+    // Each wave picks the split for its own 32 channels; the fragments have the
+    // same meaning either way (their products over a channel are the exact
+    // pairwise factors), so stage 2 sums waves that chose differently.
+    if (__all(gcmin >= -16.f)) {
+        // Weak decay: the whole chunk decays by at most 2^-16 on every channel
+        // of this wave.  One split point per channel, the chunk's mid-decay
+        // M = G_C / 2, serves every block: e^{+-(G_i - M)} lies within 2^{+-8},
+        // and e^{M} = e^{G_C - M} turns the split operands into Qbar, L, Ktil.
+        float Mw[8], Em[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            // DL = e^{G_i - M_a}, DR = e^{M_a - G_i} lie within 1 / h_a and h_a;
-            // X = e^{G_i - E_a} = DL h_a and Y = e^{E_{a+1} - G_i} = DR h_a are <= 1.
-            const float DL = __builtin_amdgcn_exp2f(G[r][j] - M[r][j]);
-            const float DR = __builtin_amdgcn_exp2f(M[r][j] - G[r][j]);
-            const float X = DL * hf[r][j], Y = DR * hf[r][j];
-            float sd[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) sd[t] = hf[t][j] * hf[t][j];
-            float P = 1.f, Qf = 1.f;                           // e^{E_a}, e^{G_C - E_{a+1}}
-#pragma unroll
-            for (int t = 0; t < r; ++t) P *= sd[t];
-#pragma unroll
-            for (int t = 3; t > r; --t) Qf *= sd[t];
-            const float kk = bf_at(kw[r], j) * nk[r], qq = bf_at(qw[r], j) * nq[r];
-            const float kX = kk * X, qX = qq * X;
-            hL[r][j] = (_Float16)(kX * P);                     // L = K e^{G}
-            hqb[j] = (_Float16)(qX * P);                       // Qbar = s Q e^{G}
-            hlk[j] = (_Float16)kX;
-            hlq[j] = (_Float16)qX;
-            const float ky = kk * Y;
-            hrb[j] = (_Float16)ky;
-            // blocks (2, 0) and (3, 1) scale by the sub-chunk between them, (3, 0) by two
-            hrd0[j] = (_Float16)(ky * (r == 0 ? sd[1] : sd[2]));
-            hrd1[j] = (_Float16)(ky * (sd[1] * sd[2]));
-            const int cc = j < 4 ? ca + j : cb + j - 4;
-            sKt[cc * TP + i] = (_Float16)(ky * Qf);           // Ktil = K e^{G_C - G}
-            dlk[j] = kk * DL;
-            dlq[j] = qq * DL;
-            drk[j] = kk * DR;
+            Mw[j] = 0.5f * E[4][j];
+            Em[j] = __builtin_amdgcn_exp2f(Mw[j]);
         }
-        if (r >= 1) {
-            sLK[((r - 1) * 4 + w) * 64 + l] = hlk;
-            sLQ[((r - 1) * 4 + w) * 64 + l] = hlq;
-        }
-        if (r <= 2) sRB[(r * 4 + w) * 64 + l] = hrb;
-        if (r == 0) {
-            sRD[(0 * 4 + w) * 64 + l] = hrd0;   // block (2, 0)
-            sRD[(1 * 4 + w) * 64 + l] = hrd1;   // block (3, 0)
-        }
-        if (r == 1) sRD[(2 * 4 + w) * 64 + l] = hrd0;   // block (3, 1)
-        reinterpret_cast<half8 *>(rec + REC_Q)[(r * 4 + w) * 64 + l] = hqb;
-        // Diagonal block r: A rows i / columns j, H^T rows j / columns i.
-        float4v a = {0, 0, 0, 0}, hh = {0, 0, 0, 0};
-        if (diag_fp16) {
-            half8 fk, fq, fr;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            half8 hp, hm, hq, hqb;
+            const int i = 16 * r + i16;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                fk[j] = (_Float16)dlk[j];
-                fq[j] = (_Float16)dlq[j];
-                fr[j] = (_Float16)drk[j];
+                const float e1 = __builtin_amdgcn_exp2f(G[r][j] - Mw[j]);
+                const float e2 = __builtin_amdgcn_exp2f(Mw[j] - G[r][j]);
+                const float kk = bf_at(kw[r], j) * nk[r], qq = bf_at(qw[r], j) * nq[r];
+                const float kp = kk * e1, km = kk * e2, qp = qq * e1;
+                hp[j] = (_Float16)kp;
+                hm[j] = (_Float16)km;
+                hq[j] = (_Float16)qp;
+                hL[r][j] = (_Float16)(kp * Em[j]);                 // L = K e^{G}
+                hqb[j] = (_Float16)(qp * Em[j]);                   // Qbar = s Q e^{G}
+                const int cc = j < 4 ? ca + j : cb + j - 4;
+                sKt[cc * TP + i] = (_Float16)(km * Em[j]);        // Ktil = K e^{G_C - G}
             }
-            a = mfma16(fk, fr, a);
-            hh = mfma16(fr, fq, hh);
-        } else {
-            bf16x8 lk_hi, lk_lo, lq_hi, lq_lo, rk_hi, rk_lo;
+            if (r >= 1) {
+                sLK[((r - 1) * 4 + w) * 64 + l] = hp;
+                sLQ[((r - 1) * 4 + w) * 64 + l] = hq;
+            }
+            if (r <= 2) sRB[(r * 4 + w) * 64 + l] = hm;
+            if (r == 0) {
+                sRD[(0 * 4 + w) * 64 + l] = hm;
+                sRD[(1 * 4 + w) * 64 + l] = hm;
+            }
+            if (r == 1) sRD[(2 * 4 + w) * 64 + l] = hm;
+            reinterpret_cast<half8 *>(rec + REC_Q)[(r * 4 + w) * 64 + l] = hqb;
+            float4v a = {0, 0, 0, 0}, hh = {0, 0, 0, 0};
+            accD[r] = mfma16(hp, hm, a);
+            accD[4 + r] = mfma16(hm, hq, hh);
+        }
+    } else {
+        // Sub-chunk splits.  Kept per (sub-chunk, channel): M_a and the
+        // half-decay h_a = e^{(E_{a+1} - E_a) / 2}; s_a = h_a^2 is the sub-chunk's
+        // whole decay, and the other factors are products of those: e^{E_a} =
+        // s_0 .. s_{a-1}, e^{G_C - E_{a+1}} = s_{a+1} .. s_3, e^{E_a - E_{b+1}} =
+        // s_{b+1} .. s_{a-1}.  Products of factors <= 1 only underflow where the
+        // exact value is below the fp32 range.
+        float M[4][8], hf[4][8];
+        float dmax = 0.f;   // largest sub-chunk decay (log2) among this lane's channels
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                M[r][j] = 0.5f * (E[r][j] + E[r + 1][j]);
+                hf[r][j] = __builtin_amdgcn_exp2f(0.5f * (E[r + 1][j] - E[r][j]));
+                dmax = fmaxf(dmax, E[r][j] - E[r + 1][j]);
+            }
+        // Where no sub-chunk of this wave's channels decays by more than 2^-8,
+        // the mid-point factors stay within 2^{+-4} and the diagonal blocks use
+        // plain fp16 operands like the others; stronger decays take bf16 MFMA
+        // with each operand split into a high and a low bf16 part (three
+        // products, about 16 significant bits).
+        const bool diag_fp16 = __all(dmax <= 8.f);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            half8 hlk, hlq, hrb, hrd0, hrd1, hqb;
+            float dlk[8], dlq[8], drk[8];   // diagonal-block operands before rounding
+            const int i = 16 * r + i16;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                split_bf16(dlk[j], lk_hi, lk_lo, j);
-                split_bf16(dlq[j], lq_hi, lq_lo, j);
-                split_bf16(drk[j], rk_hi, rk_lo, j);
+                // DL = e^{G_i - M_a}, DR = e^{M_a - G_i} lie within 1 / h_a and h_a;
+                // X = e^{G_i - E_a} = DL h_a and Y = e^{E_{a+1} - G_i} = DR h_a are <= 1.
+                const float DL = __builtin_amdgcn_exp2f(G[r][j] - M[r][j]);
+                const float DR = __builtin_amdgcn_exp2f(M[r][j] - G[r][j]);
+                const float X = DL * hf[r][j], Y = DR * hf[r][j];
+                float sd[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) sd[t] = hf[t][j] * hf[t][j];
+                float P = 1.f, Qf = 1.f;                           // e^{E_a}, e^{G_C - E_{a+1}}
+#pragma unroll
+                for (int t = 0; t < r; ++t) P *= sd[t];
+#pragma unroll
+                for (int t = 3; t > r; --t) Qf *= sd[t];
+                const float kk = bf_at(kw[r], j) * nk[r], qq = bf_at(qw[r], j) * nq[r];
+                const float kX = kk * X, qX = qq * X;
+                hL[r][j] = (_Float16)(kX * P);                     // L = K e^{G}
+                hqb[j] = (_Float16)(qX * P);                       // Qbar = s Q e^{G}
+                hlk[j] = (_Float16)kX;
+                hlq[j] = (_Float16)qX;
+                const float ky = kk * Y;
+                hrb[j] = (_Float16)ky;
+                // blocks (2, 0) and (3, 1) scale by the sub-chunk between them, (3, 0) by two
+                hrd0[j] = (_Float16)(ky * (r == 0 ? sd[1] : sd[2]));
+                hrd1[j] = (_Float16)(ky * (sd[1] * sd[2]));
+                const int cc = j < 4 ? ca + j : cb + j - 4;
+                sKt[cc * TP + i] = (_Float16)(ky * Qf);           // Ktil = K e^{G_C - G}
+                dlk[j] = kk * DL;
+                dlq[j] = qq * DL;
+                drk[j] = kk * DR;
             }
-            a = mfma16_bf16(lk_hi, rk_hi, a);
-            a = mfma16_bf16(lk_hi, rk_lo, a);
-            a = mfma16_bf16(lk_lo, rk_hi, a);
-            hh = mfma16_bf16(rk_hi, lq_hi, hh);
-            hh = mfma16_bf16(rk_lo, lq_hi, hh);
-            hh = mfma16_bf16(rk_hi, lq_lo, hh);
+            if (r >= 1) {
+                sLK[((r - 1) * 4 + w) * 64 + l] = hlk;
+                sLQ[((r - 1) * 4 + w) * 64 + l] = hlq;
+            }
+            if (r <= 2) sRB[(r * 4 + w) * 64 + l] = hrb;
+            if (r == 0) {
+                sRD[(0 * 4 + w) * 64 + l] = hrd0;   // block (2, 0)
+                sRD[(1 * 4 + w) * 64 + l] = hrd1;   // block (3, 0)
+            }
+            if (r == 1) sRD[(2 * 4 + w) * 64 + l] = hrd0;   // block (3, 1)
+            reinterpret_cast<half8 *>(rec + REC_Q)[(r * 4 + w) * 64 + l] = hqb;
+            // Diagonal block r: A rows i / columns j, H^T rows j / columns i.
+            float4v a = {0, 0, 0, 0}, hh = {0, 0, 0, 0};
+            if (diag_fp16) {
+                half8 fk, fq, fr;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    fk[j] = (_Float16)dlk[j];
+                    fq[j] = (_Float16)dlq[j];
+                    fr[j] = (_Float16)drk[j];
+                }
+                a = mfma16(fk, fr, a);
+                hh = mfma16(fr, fq, hh);
+            } else {
+                bf16x8 lk_hi, lk_lo, lq_hi, lq_lo, rk_hi, rk_lo;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    split_bf16(dlk[j], lk_hi, lk_lo, j);
+                    split_bf16(dlq[j], lq_hi, lq_lo, j);
+                    split_bf16(drk[j], rk_hi, rk_lo, j);
+                }
+                a = mfma16_bf16(lk_hi, rk_hi, a);
+                a = mfma16_bf16(lk_hi, rk_lo, a);
+                a = mfma16_bf16(lk_lo, rk_hi, a);
+                hh = mfma16_bf16(rk_hi, lq_hi, hh);
+                hh = mfma16_bf16(rk_lo, lq_hi, hh);
+                hh = mfma16_bf16(rk_hi, lq_lo, hh);
+            }
+            accD[r] = a;
+            accD[4 + r] = hh;
         }
-        accD[r] = a;
-        accD[4 + r] = hh;
     }
     lds_barrier();
 
