@@ -251,10 +251,12 @@ def test_weak_and_strong_channel_blocks_in_one_head():
     check_prefill(inp, 64)
 
 
-@pytest.mark.parametrize("lo,hi", [(-0.40, -0.30), (-0.36, -0.34)])
+@pytest.mark.parametrize("lo,hi", [(-0.40, -0.30), (-0.36, -0.34), (-0.19, -0.16)])
 def test_decay_at_the_fp16_diagonal_threshold(lo, hi):
     """Sub-chunk decays near 2^-8 (about -0.35 per token), where a wave's choice
-    between fp16 and split-bf16 diagonal operands flips from chunk to chunk."""
+    between fp16 and split-bf16 diagonal operands flips from chunk to chunk;
+    and whole-chunk decays near 2^-16 (about -0.17 per token), where its choice
+    between one split point per chunk and sub-chunk splits flips."""
     inp = _strong_gate(small(T=320, H=2, s0_std=0.05), lo, hi, seed=66)
     check_prefill(inp, 64)
 
