@@ -6,8 +6,9 @@ workload (B=1, H=32, T=131072, d_k=d_v=128, C=64, bf16 storage) with every
 input already resident in HBM.  The same run also times the batched decode
 step (``kda_decode_step``: 128 sessions x 32 heads, 268 MB fp32 state updated
 in place), the same prefill through the scalar-gate entry point, the packed
-varlen workload (8 sequences through cu_seqlens), and the fp64 CPU oracle on a
-bounded sample of the prefill workload.
+varlen workload (8 sequences through cu_seqlens), the backward of the fp32
+small-width path, and the fp64 CPU oracle on a bounded sample of the prefill
+workload.
 
 Prints ONE JSON line.  ``value`` is prefill tokens/s; the ``decode`` object
 carries the decode state bandwidth.  Roofline fractions use the algorithmic
@@ -75,6 +76,11 @@ def measured_traffic(key):
     return rec["hbm_bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
 
 
+def ctypes_byref_shape(K, B, T, H, d, C, N):
+    import ctypes
+    return ctypes.byref(K.make_shape(B, T, H, d, d, C, N, K.KDA_F32))
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -97,6 +103,7 @@ def main():
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-scalar-gate", action="store_true")
     ap.add_argument("--skip-varlen", action="store_true")
+    ap.add_argument("--skip-backward", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="finally run a plain device copy kernel over this many MiB three times: "
                          "the known-size reference for hardware byte counters")
@@ -307,6 +314,53 @@ def main():
                          "frac": round(vgbs / HBM_PEAK_GBS, 4), "traffic": None,
                          "alg_bytes_per_launch": vbytes}}
         del d4, inp4, ws4, o4, fs4
+
+    if not args.skip_backward:
+        # Gradients through kda_chunk_bwd: the fp32 small-width path (d = 64,
+        # C = 32), one sequence of 4096 tokens per head, 16 heads.
+        print("[bench] backward (fp32, d=64, C=32, B=1 H=16 T=4096)", file=sys.stderr, flush=True)
+        gen = torch.Generator(device=dev).manual_seed(7)
+        Tb, Hb, db = 4096, 16, 64
+        rnd = lambda *sh: torch.randn(*sh, generator=gen, device=dev)  # noqa: E731
+        qb = torch.nn.functional.normalize(rnd(1, Tb, Hb, db), dim=-1).contiguous()
+        kb = torch.nn.functional.normalize(rnd(1, Tb, Hb, db), dim=-1).contiguous()
+        vb, dob = rnd(1, Tb, Hb, db), rnd(1, Tb, Hb, db)
+        gb = (-0.05 * torch.rand(1, Tb, Hb, db, generator=gen, device=dev)).contiguous()
+        bb = torch.sigmoid(rnd(1, Tb, Hb)).contiguous()
+        s0b, dfb = 0.1 * rnd(1, Hb, db, db), rnd(1, Hb, db, db)
+        wsb = torch.empty(K.lib().kda_chunk_bwd_workspace_bytes(ctypes_byref_shape(
+            K, 1, Tb, Hb, db, 32, 1)), dtype=torch.uint8, device=dev)
+
+        def bstep():
+            return K.chunk_bwd(qb, kb, vb, gb, bb, dob, initial_state=s0b, d_final_state=dfb,
+                               chunk_size=32, workspace=wsb)
+
+        for _ in range(2):
+            bstep()
+        torch.cuda.synchronize()
+        n_b = max(1, args.steps // 4)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n_b):
+            grads = bstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        bms = e0.elapsed_time(e1) / n_b
+        # inputs q, k, v, g, d_o (fp32 d) and beta read once, gradients written
+        # once, states read (s0, d_final) and written (d_s0) once
+        bbytes = Tb * Hb * (5 * 4 * db + 4) + Tb * Hb * (4 * 4 * db + 4) + 3 * Hb * db * db * 4
+        bgbs = bbytes / (bms * 1e-3) / 1e9
+        result["backward"] = {
+            "value": round(Tb / (bms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(bms, 4),
+            "steps": n_b,
+            "config": {"workload": "gradients of the chunked prefill, B=1 H=16 T=4096 d=64 C=32 "
+                                   "fp32, log-decays U(-0.05, 0), through kda_chunk_bwd"},
+            "roofline": {"bound": "alu", "kernel": "kda_chunk_bwd_f32_kernel (fp32 VALU, "
+                         "operands in LDS; a correctness-first path)",
+                         "achieved_hbm_gbs": round(bgbs, 2), "hbm_frac": round(bgbs / HBM_PEAK_GBS, 5),
+                         "alg_bytes_per_launch": bbytes},
+            "outputs_finite": bool(all(torch.isfinite(t).all().item() for t in grads.values()))}
+        del qb, kb, vb, dob, gb, bb, s0b, dfb, wsb, grads
 
     if not args.no_cpu_baseline:
         import numpy as np

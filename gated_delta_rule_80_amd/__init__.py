@@ -100,6 +100,11 @@ def lib():
     L.kda_decode_step_ex.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_int32, ctypes.c_int, ctypes.POINTER(KdaInputsForm),
                                      vp, vp, vp, fp, fp, ctypes.c_float, fp, vp, vp]
+    L.kda_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.kda_chunk_bwd_workspace_bytes.argtypes = [ctypes.POINTER(KdaShape)]
+    L.kda_chunk_bwd.restype = ctypes.c_int
+    L.kda_chunk_bwd.argtypes = [ctypes.POINTER(KdaShape), fp, fp, fp, fp, fp, ctypes.c_float, fp,
+                                ip, fp, fp, fp, fp, fp, fp, fp, fp, vp, ctypes.c_size_t, vp]
     L.kda_output_rmsnorm_gate.restype = ctypes.c_int
     L.kda_output_rmsnorm_gate.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int, vp, vp, fp,
                                           ctypes.c_float, vp, vp]
@@ -339,3 +344,51 @@ def output_rmsnorm_gate(o: torch.Tensor, gate: torch.Tensor, weight: torch.Tenso
                                        ctypes.c_float(eps), _ptr(res), _stream())
     _check(st)
     return res
+
+
+def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+              beta: torch.Tensor, d_o: torch.Tensor, scale: Optional[float] = None,
+              initial_state: Optional[torch.Tensor] = None,
+              cu_seqlens: Optional[torch.Tensor] = None,
+              d_final_state: Optional[torch.Tensor] = None, chunk_size: int = 32,
+              workspace: Optional[torch.Tensor] = None) -> dict:
+    """Gradients of ``chunk_fwd`` (``kda_chunk_bwd``) for L = <o, d_o> +
+    <final states, d_final_state>: a dict with dq, dk, dv, dg, dbeta and, when
+    an initial state is given, dinitial_state.  fp32 tensors only, d_k = d_v =
+    d with (d, chunk_size) in {(16, 16|32|64), (32, 16|32), (64, 16|32)}."""
+    _need(q.dim() == 4 and k.shape == q.shape and v.shape == q.shape and g.shape == q.shape,
+          "q, k, v, g must be [B, T, H, d] (d_k = d_v)")
+    B, T, H, d = q.shape
+    _need(beta.shape == (B, T, H) and d_o.shape == q.shape, "beta must be [B, T, H], d_o like v")
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("d_o", d_o)):
+        _need(t.dtype == torch.float32 and t.is_cuda and t.is_contiguous(),
+              "%s must be a contiguous fp32 device tensor" % name)
+    if cu_seqlens is not None:
+        _need(cu_seqlens.dtype == torch.int32 and cu_seqlens.is_cuda and cu_seqlens.dim() == 1,
+              "cu_seqlens must be an int32 device tensor [N+1]")
+        _need(B == 1, "cu_seqlens needs batch 1")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    for name, t in (("initial_state", initial_state), ("d_final_state", d_final_state)):
+        _need(t is None or (t.shape == (N, H, d, d) and t.dtype == torch.float32 and t.is_cuda
+                            and t.is_contiguous()),
+              "%s must be a contiguous fp32 device tensor [N, H, d, d]" % name)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    sh = make_shape(B, T, H, d, d, chunk_size, N, KDA_F32)
+    need = int(lib().kda_chunk_bwd_workspace_bytes(ctypes.byref(sh)))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    out = {n: torch.empty_like(t) for n, t in (("dq", q), ("dk", k), ("dv", v), ("dg", g),
+                                               ("dbeta", beta))}
+    ds0 = None
+    if initial_state is not None:
+        ds0 = torch.empty_like(initial_state)
+        out["dinitial_state"] = ds0
+    st = lib().kda_chunk_bwd(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                             ctypes.c_float(scale), _ptr(initial_state), _ptr(cu_seqlens),
+                             _ptr(d_o), _ptr(d_final_state), _ptr(out["dq"]), _ptr(out["dk"]),
+                             _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(ds0),
+                             _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream())
+    _check(st)
+    return out

@@ -331,4 +331,94 @@ kda_status kda_output_rmsnorm_gate(int64_t rows, int32_t d_v, kda_dtype dtype, c
     return KDA_OK;
 }
 
+size_t kda_chunk_bwd_workspace_bytes(const kda_shape *shape) {
+    if (!shape || shape->batch <= 0 || shape->seqlen < 0 || shape->num_heads <= 0 ||
+        shape->d_k <= 0 || shape->chunk_size <= 0 || shape->num_seqs <= 0)
+        return 0;
+    const int64_t total = (int64_t)shape->batch * shape->seqlen;
+    return kda::bwd_f32_workspace_bytes(total, shape->num_seqs, shape->num_heads, shape->d_k,
+                                        shape->chunk_size);
+}
+
+kda_status kda_chunk_bwd(const kda_shape *shape, const float *q, const float *k, const float *v,
+                         const float *g_log_decay, const float *beta, float scale,
+                         const float *initial_state, const int32_t *cu_seqlens, const float *d_o,
+                         const float *d_final_state, float *dq, float *dk, float *dv, float *dg,
+                         float *dbeta, float *d_initial_state, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+    g_last_error[0] = '\0';
+    if (!shape) return fail(KDA_ERR_INVALID_ARGUMENT, "shape is NULL");
+    if (shape->dtype != KDA_F32)
+        return fail(KDA_ERR_UNSUPPORTED, "the backward is built for fp32 storage only");
+    if (shape->batch <= 0 || shape->seqlen < 0 || shape->num_heads <= 0 || shape->d_k <= 0 ||
+        shape->d_v <= 0 || shape->chunk_size <= 0 || shape->num_seqs <= 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "non-positive size");
+    if (!kda::bwd_f32_supported(shape->d_k, shape->d_v, shape->chunk_size))
+        return fail(KDA_ERR_UNSUPPORTED,
+                    "no backward kernel for d_k %d d_v %d chunk %d (built: d_k = d_v = 16 with "
+                    "chunk 16/32/64, 32 or 64 with chunk 16/32)",
+                    shape->d_k, shape->d_v, shape->chunk_size);
+    const int64_t total = (int64_t)shape->batch * shape->seqlen;
+    if (total > INT32_MAX / 2) return fail(KDA_ERR_INVALID_ARGUMENT, "too many tokens");
+    const bool varlen = cu_seqlens != nullptr;
+    if (varlen && shape->batch != 1)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens needs batch == 1 (got %d)",
+                    shape->batch);
+    if (!varlen && shape->num_seqs != shape->batch)
+        return fail(KDA_ERR_INVALID_ARGUMENT,
+                    "without cu_seqlens num_seqs must equal batch (%d vs %d)", shape->num_seqs,
+                    shape->batch);
+    if (total > 0 && (!q || !k || !v || !g_log_decay || !beta || !d_o || !dq || !dk || !dv ||
+                      !dg || !dbeta))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "a required tensor pointer is NULL");
+    const void *p16[] = {q, k, v, g_log_decay, d_o, dq, dk, dv, dg, initial_state,
+                         d_final_state, d_initial_state};
+    for (const void *p : p16)
+        if (p && !aligned16(p))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "tensor pointer %p is not 16-byte aligned", p);
+    if ((beta && !aligned4(beta)) || (dbeta && !aligned4(dbeta)) ||
+        (cu_seqlens && !aligned4(cu_seqlens)))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "beta / dbeta / cu_seqlens must be 4-byte aligned");
+    const void *ins[] = {q, k, v, g_log_decay, beta, d_o, initial_state, d_final_state};
+    const void *outs[] = {dq, dk, dv, dg, dbeta, d_initial_state};
+    for (const void *o : outs)
+        for (const void *in : ins)
+            if (o && o == in)
+                return fail(KDA_ERR_INVALID_ARGUMENT, "gradient outputs must not alias inputs");
+    const size_t need = kda_chunk_bwd_workspace_bytes(shape);
+    if (!workspace) return fail(KDA_ERR_INVALID_ARGUMENT, "workspace is NULL (%zu bytes needed)", need);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+    if (workspace_bytes < need)
+        return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed",
+                    workspace_bytes, need);
+    kda::ChunkBwdProblem p;
+    p.n_seqs = shape->num_seqs;
+    p.seqlen = shape->seqlen;
+    p.heads = shape->num_heads;
+    p.d = shape->d_k;
+    p.chunk = shape->chunk_size;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.g = g_log_decay;
+    p.beta = beta;
+    p.scale = scale;
+    p.s0 = initial_state;
+    p.cu = cu_seqlens;
+    p.dfinal = d_final_state;
+    p.dout = d_o;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.dg = dg;
+    p.dbeta = dbeta;
+    p.ds0 = d_initial_state;
+    p.ckpt = static_cast<float *>(workspace);
+    p.stream = static_cast<hipStream_t>(stream);
+    hipError_t e = kda::launch_chunk_bwd_f32(p);
+    if (e != hipSuccess) return hip_fail(e, "chunk backward launch");
+    return KDA_OK;
+}
+
 }  // extern "C"

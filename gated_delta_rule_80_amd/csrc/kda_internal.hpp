@@ -76,4 +76,22 @@ bool f32_path_supported(int dk, int dv, int chunk, bool bf16);
 size_t f32_workspace_bytes(int64_t total_tokens, int64_t n_seqs, int heads, int chunk);
 hipError_t launch_chunk_fwd_f32(const ChunkProblem &p);
 
+// Gradients of the chunked prefill, fp32 storage, d_k = d_v = d.
+struct ChunkBwdProblem {
+    int n_seqs, seqlen, heads, d, chunk;   // as ChunkProblem (seqlen = row length)
+    const float *q, *k, *v, *g, *beta;     // per-channel log-decays, plain inputs
+    float scale;
+    const float *s0;        // may be null (zeros)
+    const int32_t *cu;      // may be null (equal rows)
+    const float *dfinal;    // gradient of the final states; may be null (zeros)
+    const float *dout;      // gradient of o
+    float *dq, *dk, *dv, *dg, *dbeta;
+    float *ds0;             // may be null (not written)
+    float *ckpt;            // workspace: chunk-start states
+    hipStream_t stream;
+};
+bool bwd_f32_supported(int dk, int dv, int chunk);
+size_t bwd_f32_workspace_bytes(int64_t total_tokens, int n_seqs, int heads, int d, int chunk);
+hipError_t launch_chunk_bwd_f32(const ChunkBwdProblem &p);
+
 }  // namespace kda

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 
 typedef enum kda_status {
     KDA_OK = 0,
@@ -286,6 +286,42 @@ kda_status kda_output_rmsnorm_gate(int64_t rows, int32_t d_v, kda_dtype dtype,
                                    const void *o, const void *gate,
                                    const float *weight, float eps, void *out,
                                    void *stream);
+
+/*
+ * Gradients of kda_chunk_fwd (per-channel log-decays, plain inputs) for the
+ * loss L = <o, d_o> + <final states, d_final_state>.  The pages derive no
+ * gradients ("Kimi Delta Attention: How It Works, Step by Step" motivates the
+ * chunkwise form by training); this reverses the chunk algebra of
+ * "Understanding Kimi Delta Attention", sections "The triangular system" and
+ * "Putting the chunks together", step by step: a forward pass stores each
+ * chunk's start state in the workspace, then the chunks are walked in reverse
+ * carrying dL/dS across chunk boundaries.
+ *
+ *   shape         as kda_chunk_fwd; dtype KDA_F32 only, d_k = d_v = d with
+ *                 (d, chunk) in {(16, 16|32|64), (32, 16|32), (64, 16|32)}.
+ *   q, k, g_log_decay, v, beta, scale, initial_state, cu_seqlens
+ *                 the forward's inputs, same layouts (initial_state may be NULL).
+ *   d_o           [B, T, H, d_v] fp32: dL/do.
+ *   d_final_state [N, H, d_k, d_v] fp32 or NULL (zeros).
+ *   dq, dk, dv, dg, dbeta
+ *                 outputs with the layouts of q, k, v, g_log_decay, beta.
+ *   d_initial_state [N, H, d_k, d_v] fp32 or NULL (not written).
+ *   workspace     at least kda_chunk_bwd_workspace_bytes(shape) bytes,
+ *                 256-byte aligned (chunk-start states, fp32).
+ * Tensors 16-byte aligned (beta, dbeta, cu_seqlens 4-byte); outputs must not
+ * alias inputs.  Log-decays must be finite.  Asynchronous on `stream`; the
+ * library enqueues kernels only.
+ */
+size_t kda_chunk_bwd_workspace_bytes(const kda_shape *shape);
+kda_status kda_chunk_bwd(const kda_shape *shape, const float *q, const float *k,
+                         const float *v, const float *g_log_decay,
+                         const float *beta, float scale,
+                         const float *initial_state,
+                         const int32_t *cu_seqlens, const float *d_o,
+                         const float *d_final_state, float *dq, float *dk,
+                         float *dv, float *dg, float *dbeta,
+                         float *d_initial_state, void *workspace,
+                         size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

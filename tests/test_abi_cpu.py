@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = K.lib()
-    assert lib.kda_abi_version() == 3
+    assert lib.kda_abi_version() == 4
     for code, name in K.STATUS.items():
         assert lib.kda_status_string(code).decode() == name
 
@@ -169,3 +169,37 @@ def test_binding_scalar_gate_shape_checks():
     q = torch.zeros(1, 64, 2, 16)
     with pytest.raises(ValueError):     # per-channel gate shape given to the scalar entry
         K.chunk_fwd_scalar_gate(q, q, q, q.float(), torch.zeros(1, 64, 2), chunk_size=16)
+
+
+# ---------------------------------------------------------------- backward
+def call_bwd(sh, **kw):
+    lib = K.lib()
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+    args = dict(q=fake, k=fake, v=fake, g=fake, beta=fake, s0=None, cu=None, do=fake, dfin=None,
+                dq=ctypes.c_void_p(0x2000), dk=ctypes.c_void_p(0x3000), dv=ctypes.c_void_p(0x4000),
+                dg=ctypes.c_void_p(0x5000), db=ctypes.c_void_p(0x6000), ds0=None,
+                ws=ctypes.c_void_p(0x10000), wsb=ctypes.c_size_t(1 << 40))
+    args.update(kw)
+    return lib.kda_chunk_bwd(ctypes.byref(sh), args["q"], args["k"], args["v"], args["g"],
+                             args["beta"], ctypes.c_float(0.25), args["s0"], args["cu"], args["do"],
+                             args["dfin"], args["dq"], args["dk"], args["dv"], args["dg"],
+                             args["db"], args["ds0"], args["ws"], args["wsb"], None)
+
+
+def test_backward_rejects_unsupported_problems():
+    f32 = dict(d_k=32, d_v=32, chunk_size=32, dtype_code=K.KDA_F32, seqlen=64, heads=2)
+    assert call_bwd(shape(**dict(f32, dtype_code=K.KDA_BF16))) == 2
+    assert call_bwd(shape(**dict(f32, d_k=128, d_v=128))) == 2
+    assert call_bwd(shape(**dict(f32, chunk_size=64))) == 2
+    assert call_bwd(shape(**f32), dq=None) == 1
+    assert call_bwd(shape(**f32), dq=ctypes.c_void_p(0x1000)) == \
+        1   # aliases an input
+    assert call_bwd(shape(**f32), ws=None) == 1
+    assert call_bwd(shape(**f32), wsb=ctypes.c_size_t(16)) == \
+        3
+
+
+def test_backward_workspace_query():
+    sh = shape(d_k=16, d_v=16, chunk_size=16, dtype_code=K.KDA_F32, seqlen=100, heads=3)
+    # chunk-start states: (T / C + N + 1) slots of H x d x d fp32
+    assert K.lib().kda_chunk_bwd_workspace_bytes(ctypes.byref(sh)) == (100 // 16 + 1 + 1) * 3 * 16 * 16 * 4

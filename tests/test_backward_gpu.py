@@ -1,0 +1,84 @@
+"""The GPU backward (kda_chunk_bwd, fp32 small-width path) against the fp64
+autograd oracle of the recurrence (oracle/backward.py, pinned to finite
+differences), through the C ABI.  Tolerance: relative Frobenius error <= 1e-4
+on every gradient, as for the fp32 forward."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kda_harness import rel_err
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-4
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_delta_rule_80_amd as K
+    K.lib()
+
+
+def make(B, T, H, d, seed, lengths=None, g_range=(-1.0, 0.0), s0=True, dfin=True):
+    rng = np.random.default_rng(seed)
+    rows = 1 if lengths else B
+    tot = sum(lengths) if lengths else T
+    n = len(lengths) if lengths else B
+    shp = (rows, tot, H, d)
+    q = rng.normal(size=shp)
+    k = rng.normal(size=shp)
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    x = dict(q=q, k=k, v=rng.normal(size=shp), g=rng.uniform(*g_range, size=shp),
+             beta=rng.uniform(0.05, 0.95, size=shp[:3]), do=rng.normal(size=shp))
+    x = {n_: a.astype(np.float32) for n_, a in x.items()}
+    x["s0"] = (0.1 * rng.normal(size=(n, H, d, d))).astype(np.float32) if s0 else None
+    x["dfin"] = rng.normal(size=(n, H, d, d)).astype(np.float32) if dfin else None
+    x["cu"] = (np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32) if lengths else None)
+    return x
+
+
+def check(x, chunk):
+    import gated_delta_rule_80_amd as K
+    dev = {n: (torch.from_numpy(a).cuda() if a is not None else None) for n, a in x.items()}
+    got = K.chunk_bwd(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], dev["do"],
+                      initial_state=dev["s0"], cu_seqlens=dev["cu"], d_final_state=dev["dfin"],
+                      chunk_size=chunk)
+    torch.cuda.synchronize()
+    flat = lambda a: None if a is None else a.reshape(-1, *a.shape[2:]).astype(np.float64)  # noqa
+    rows, T, _, d = x["q"].shape
+    # B equal rows are B sequences for the oracle
+    cu = x["cu"].tolist() if x["cu"] is not None else list(range(0, rows * T + 1, T))
+    ref = oracle.backward.recurrent_grads(flat(x["q"]), flat(x["k"]), flat(x["v"]), flat(x["g"]),
+                                          x["beta"].reshape(-1, x["beta"].shape[-1]),
+                                          1.0 / np.sqrt(d), flat(x["do"]), x["s0"], x["dfin"], cu)
+    errs = {}
+    for name in ("dq", "dk", "dv", "dg", "dbeta"):
+        a = got[name].double().cpu().numpy()
+        errs[name] = rel_err(a.reshape(-1, *a.shape[2:]), ref[name])
+    if x["s0"] is not None:
+        errs["dinitial_state"] = rel_err(got["dinitial_state"].double().cpu().numpy(),
+                                         ref["dinitial_state"])
+    print("backward errors: " + "  ".join("%s %.2e" % kv for kv in errs.items()), flush=True)
+    for name, e in errs.items():
+        assert np.isfinite(e) and e <= TOL, (name, e)
+
+
+@pytest.mark.parametrize("d,C,T", [(16, 16, 70), (16, 64, 150), (32, 16, 47), (32, 32, 100),
+                                   (64, 16, 40), (64, 32, 65)])
+def test_backward_shapes(d, C, T):
+    check(make(2, T, 2, d, seed=100 + d + C), C)
+
+
+def test_backward_packed_sequences_with_an_empty_one():
+    check(make(1, 0, 2, 32, seed=201, lengths=[17, 0, 43, 40]), 32)
+
+
+def test_backward_strong_decays():
+    check(make(1, 90, 2, 16, seed=202, g_range=(-5.0, 0.0)), 16)
+
+
+def test_backward_without_states():
+    check(make(1, 80, 3, 16, seed=203, s0=False, dfin=False), 32)
