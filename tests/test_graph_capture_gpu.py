@@ -102,3 +102,41 @@ def test_prefill_replayed_from_a_graph(varlen):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(o, o_ref) and torch.equal(fs, fs_ref), "replay %d" % replay
+
+
+def test_backward_replayed_from_a_graph():
+    import gated_delta_rule_80_amd as K
+    gen = torch.Generator(device="cuda").manual_seed(73)
+    B, T, H, d = 1, 150, 2, 32
+    rnd = lambda *s: torch.randn(*s, generator=gen, device="cuda")  # noqa: E731
+    q = torch.nn.functional.normalize(rnd(B, T, H, d), dim=-1).contiguous()
+    k = torch.nn.functional.normalize(rnd(B, T, H, d), dim=-1).contiguous()
+    v, do = rnd(B, T, H, d), rnd(B, T, H, d)
+    g = (-0.5 * torch.rand(B, T, H, d, generator=gen, device="cuda")).contiguous()
+    beta = torch.sigmoid(rnd(B, T, H)).contiguous()
+    s0, dfin = 0.1 * rnd(1, H, d, d), rnd(1, H, d, d)
+    ws = torch.empty(1 << 22, dtype=torch.uint8, device="cuda")
+
+    def call():
+        return K.chunk_bwd(q, k, v, g, beta, do, initial_state=s0, d_final_state=dfin,
+                           chunk_size=32, workspace=ws)
+
+    ref = call()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = call()
+    for replay in range(3):
+        for t in out.values():
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name in ref:
+            assert torch.equal(out[name], ref[name]), "replay %d %s" % (replay, name)
