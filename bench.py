@@ -104,6 +104,7 @@ def main():
     ap.add_argument("--skip-scalar-gate", action="store_true")
     ap.add_argument("--skip-varlen", action="store_true")
     ap.add_argument("--skip-backward", action="store_true")
+    ap.add_argument("--skip-layer-forms", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="finally run a plain device copy kernel over this many MiB three times: "
                          "the known-size reference for hardware byte counters")
@@ -268,6 +269,61 @@ def main():
                          "traffic": measured_traffic("kda_chunk_fwd_scalar_gate:T131072_H32"),
                          "alg_bytes_per_launch": sbytes}}
         del gs
+
+    if not args.skip_layer_forms:
+        # The same long-context prefill with the layer's input steps done in the
+        # kernels (gate and beta as logits, q and k L2-normalised), then the
+        # output stage (RMS norm x weight x sigmoid gate) on its output.
+        print("[bench] prefill with every input form, then the output stage", file=sys.stderr,
+              flush=True)
+        gen = torch.Generator(device=dev).manual_seed(11)
+        z = (4.0 + 8.0 * torch.rand(d["g"].shape, generator=gen, device=dev)).contiguous()
+        bl = torch.randn(d["beta"].shape, generator=gen, device=dev).contiguous()
+        ogate = torch.randn(o.shape, generator=gen, device=dev).to(torch.bfloat16).contiguous()
+        wgt = (1.0 + 0.1 * torch.randn(dv, generator=gen, device=dev)).contiguous()
+        out_stage = torch.empty_like(o)
+
+        def fstep():
+            K.chunk_fwd_ex(d["q"], d["k"], d["v"], z, bl, gate="per_channel", gate_is_logit=True,
+                           beta_is_logit=True, l2norm_qk=True, scale=d["scale"],
+                           initial_state=d["initial_state"], chunk_size=w5.chunk, workspace=ws,
+                           out=o, final_state=fs)
+
+        def ostep():
+            K.output_rmsnorm_gate(o, ogate, wgt, eps=1e-6, out=out_stage)
+
+        for _ in range(3):
+            fstep()
+            ostep()
+        torch.cuda.synchronize()
+        n_f = max(1, args.steps // 2)
+        times = []
+        for fn in (fstep, ostep):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(n_f):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / n_f)
+        fms, oms = times
+        obytes = 3 * T_total * H * dv * 2 + dv * 4   # o and gate read, out written (bf16)
+        ogbs = obytes / (oms * 1e-3) / 1e9
+        fgbs = alg_bytes / (fms * 1e-3) / 1e9
+        result["layer_forms"] = {
+            "value": round(T_total / (fms * 1e-3), 1), "unit": "tokens/s",
+            "ms_per_step": round(fms, 4), "steps": n_f,
+            "config": {"workload": "long-context prefill as above through kda_chunk_fwd_ex with "
+                                   "logit gate, logit beta and in-kernel q/k L2 norm; then "
+                                   "kda_output_rmsnorm_gate on its output"},
+            "roofline": {"bound": "hbm", "kernel": "kda_chunk_fwd_ex", "achieved": round(fgbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(fgbs / HBM_PEAK_GBS, 4), "alg_bytes_per_launch": alg_bytes},
+            "output_stage": {"ms": round(oms, 4), "achieved": round(ogbs, 1), "unit": "GB/s",
+                             "frac": round(ogbs / HBM_PEAK_GBS, 4),
+                             "kernel": "kda_output_rmsnorm_gate_kernel",
+                             "alg_bytes_per_launch": obytes}}
+        del z, bl, ogate, wgt, out_stage
 
     if not args.skip_varlen:
         # The packed workload: 8 sequences of seeded lengths in one buffer with

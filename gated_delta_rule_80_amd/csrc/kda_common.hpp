@@ -82,9 +82,19 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
+// log(1 + x) for x >= 0 by D. Goldberg's method ("What Every Computer
+// Scientist Should Know About Floating-Point Arithmetic", 1991, Theorem 4):
+// with u = fl(1 + x), log1p(x) = log(u) * x / (u - 1), and = x when u == 1.
+// The factor x / (u - 1) undoes the rounding of 1 + x, so the result keeps a
+// few ulps of relative accuracy even where x is far below 1 (u - 1 is exact).
+__device__ __forceinline__ float log1p_nonneg(float x) {
+    const float u = 1.f + x;
+    return (u == 1.f) ? x : __logf(u) * (x * __builtin_amdgcn_rcpf(u - 1.f));
+}
+
 // log(sigmoid(x)) without overflow: min(x, 0) - log(1 + e^{-|x|}).
 __device__ __forceinline__ float log_sigmoid(float x) {
-    return fminf(x, 0.f) - log1pf(__expf(-fabsf(x)));
+    return fminf(x, 0.f) - log1p_nonneg(__expf(-fabsf(x)));
 }
 
 __device__ __forceinline__ float sigmoid(float x) { return 1.f / (1.f + __expf(-x)); }
