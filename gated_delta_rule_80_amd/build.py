@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libkda.so")
 ARCH = "gfx950"
 
 SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_chunk_mfma.hip", "kda_chunk_f32.hip",
-           "kda_chunk_bwd_f32.hip",
+           "kda_chunk_bwd.hip",
            "kda_post.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",

@@ -336,8 +336,8 @@ size_t kda_chunk_bwd_workspace_bytes(const kda_shape *shape) {
         shape->d_k <= 0 || shape->chunk_size <= 0 || shape->num_seqs <= 0)
         return 0;
     const int64_t total = (int64_t)shape->batch * shape->seqlen;
-    return kda::bwd_f32_workspace_bytes(total, shape->num_seqs, shape->num_heads, shape->d_k,
-                                        shape->chunk_size);
+    return kda::bwd_workspace_bytes(total, shape->num_seqs, shape->num_heads, shape->d_k,
+                                    shape->chunk_size);
 }
 
 kda_status kda_chunk_bwd(const kda_shape *shape, const float *q, const float *k, const float *v,
@@ -353,10 +353,10 @@ kda_status kda_chunk_bwd(const kda_shape *shape, const float *q, const float *k,
     if (shape->batch <= 0 || shape->seqlen < 0 || shape->num_heads <= 0 || shape->d_k <= 0 ||
         shape->d_v <= 0 || shape->chunk_size <= 0 || shape->num_seqs <= 0)
         return fail(KDA_ERR_INVALID_ARGUMENT, "non-positive size");
-    if (!kda::bwd_f32_supported(shape->d_k, shape->d_v, shape->chunk_size))
+    if (!kda::bwd_supported(shape->d_k, shape->d_v, shape->chunk_size))
         return fail(KDA_ERR_UNSUPPORTED,
                     "no backward kernel for d_k %d d_v %d chunk %d (built: d_k = d_v = 16 with "
-                    "chunk 16/32/64, 32 or 64 with chunk 16/32)",
+                    "chunk 16/32/64, 32 or 64 with chunk 16/32, 128 with chunk 16)",
                     shape->d_k, shape->d_v, shape->chunk_size);
     const int64_t total = (int64_t)shape->batch * shape->seqlen;
     if (total > INT32_MAX / 2) return fail(KDA_ERR_INVALID_ARGUMENT, "too many tokens");
@@ -414,9 +414,9 @@ kda_status kda_chunk_bwd(const kda_shape *shape, const float *q, const float *k,
     p.dg = dg;
     p.dbeta = dbeta;
     p.ds0 = d_initial_state;
-    p.ckpt = static_cast<float *>(workspace);
+    p.work = static_cast<float *>(workspace);
     p.stream = static_cast<hipStream_t>(stream);
-    hipError_t e = kda::launch_chunk_bwd_f32(p);
+    hipError_t e = kda::launch_chunk_bwd(p);
     if (e != hipSuccess) return hip_fail(e, "chunk backward launch");
     return KDA_OK;
 }

@@ -1,0 +1,539 @@
+// kda_chunk_bwd.hip -- gradients of the chunkwise KDA prefill in fp32, for
+// fp32 storage and d_k = d_v = d in {16, 32, 64, 128}.
+//
+// The pages derive no gradients.  These kernels reverse the chunk algebra of
+// "Understanding Kimi Delta Attention" (A. Flores), sections "The triangular
+// system" and "Putting the chunks together" (written here with A = -A_page,
+// so T = (I + A)^{-1}):
+//   R = T Diag(beta) L,  U = T Diag(beta) V,  Z = U - R S,
+//   O = Qbar S + H Z,    S' = Diag(e^{G_C}) S + Kbar^T Z,
+// one step at a time, last step first.  With dS' the gradient reaching the
+// end of a chunk:
+//   dZ = Kbar dS' + H^T dO,   dS = Diag(e^{G_C}) dS' + Qbar^T dO - R^T dZ,
+//   dR = -dZ S^T,  dT = dZ (BV)^T + dR (BL)^T,  dA = T^T dT T^T (strictly lower),
+// and the decay-weighted products behind A and H hand their gradients to k, q
+// and the cumulative log-decay G, whose reverse cumulative sum is dg.
+//
+// Two kernels.  Only S and dS are carried from chunk to chunk, and each of
+// their value columns evolves on its own (Z and dZ are column-wise too), so
+// the chain kernel runs one workgroup per (sequence, head, 16 value columns):
+// a forward sweep stores each chunk's start state and Z, a reverse sweep
+// stores each chunk's end-state gradient dS' and dZ and leaves dS_0.  Every
+// other gradient is a function of one chunk's inputs and those four stored
+// quantities, so the gradient kernel runs one workgroup per (chunk, head),
+// all in parallel.  fp32 on the vector ALUs, decay factors as e^{G_i - G_j}
+// with exponents <= 0, so any finite log-decay is in range.
+#include "kda_common.hpp"
+#include "kda_internal.hpp"
+
+namespace kda {
+namespace bwd {
+
+constexpr int THREADS = 256;
+constexpr int TV = 16;   // value columns per chain workgroup
+
+// ---- workspace ------------------------------------------------------------------
+// Per (chunk slot, head): S at the chunk start [d][d], dS' at the chunk end
+// [d][d], Z [C][d] and dZ [C][d], fp32, row-major; four regions one after another.
+__host__ __device__ inline size_t n_slots(int64_t total_tokens, int n_seqs, int chunk) {
+    return (size_t)(total_tokens / chunk + n_seqs + 1);
+}
+struct Ws {
+    float *S, *dS, *Z, *dZ;
+};
+__host__ __device__ inline Ws ws_layout(float *base, size_t slots, int heads, int d, int C) {
+    const size_t dd = (size_t)slots * heads * d * d, cd = (size_t)slots * heads * C * d;
+    return Ws{base, base + dd, base + 2 * dd, base + 2 * dd + cd};
+}
+
+// First chunk slot of sequence n: floor(start / C) + n.  Strictly increasing in
+// n, and a sequence's slots stay below the next one's first slot.
+__device__ __forceinline__ int chunk_base(int ts, int n, int C) { return ts / C + n; }
+
+__device__ __forceinline__ void seq_range(const int32_t *cu, int row_len, int n, int &ts,
+                                          int &te) {
+    if (cu) {
+        const int T = row_len;   // clamped: a malformed cu_seqlens stays inside [0, T)
+        ts = min(T, max(0, cu[n]));
+        te = min(T, max(ts, cu[n + 1]));
+    } else {
+        ts = n * row_len;
+        te = ts + row_len;
+    }
+}
+
+// ---- shared chunk steps (one workgroup, THREADS threads, operands in LDS) ----------
+// Loads rows t0 .. t0+len-1 of a [tokens, H, d] tensor into dst[C][d] (zeros below).
+__device__ __forceinline__ void load_rows(float *dst, const float *src, int t0, int len, int H,
+                                          int h, int d, int C, int tid) {
+    for (int e = tid; e < C * d; e += THREADS) {
+        const int i = e / d;
+        dst[e] = i < len ? src[((size_t)(t0 + i) * H + h) * d + (e - i * d)] : 0.f;
+    }
+}
+// In place: G[i][c] <- sum_{r <= i} g[r][c] (padding rows add zero).
+__device__ __forceinline__ void cumsum_rows(float *G, int d, int C, int tid) {
+    for (int c = tid; c < d; c += THREADS) {
+        float run = 0.f;
+        for (int i = 0; i < C; ++i) {
+            run += G[i * d + c];
+            G[i * d + c] = run;
+        }
+    }
+}
+// K~_ij = sum_c k_ic k_jc e^{G_ic - G_jc} (j < i, else 0) and
+// T = (I + Diag(beta) K~)^{-1} by forward substitution, one column per thread.
+__device__ __forceinline__ void build_T(float *Kt, float *T, const float *k, const float *G,
+                                        const float *b, int d, int C, int tid) {
+    for (int e = tid; e < C * C; e += THREADS) {
+        const int i = e / C, j = e - i * C;
+        float a = 0.f;
+        if (j < i)
+            for (int c = 0; c < d; ++c) a += k[i * d + c] * expf(G[i * d + c] - G[j * d + c]) * k[j * d + c];
+        Kt[e] = a;
+    }
+    __syncthreads();
+    for (int j = tid; j < C; j += THREADS)
+        for (int i = 0; i < C; ++i) {
+            float s = (i == j) ? 1.f : 0.f;
+            for (int m = j; m < i; ++m) s -= b[i] * Kt[i * C + m] * T[m * C + j];
+            T[i * C + j] = (i < j) ? 0.f : s;
+        }
+    __syncthreads();
+}
+// R = T Diag(beta) L with L_j = k_j e^{G_j}.
+__device__ __forceinline__ void build_R(float *R, const float *T, const float *k, const float *G,
+                                        const float *b, int d, int C, int tid) {
+    for (int e = tid; e < C * d; e += THREADS) {
+        const int i = e / d, c = e - i * d;
+        float r = 0.f;
+        for (int j = 0; j <= i; ++j) r += T[i * C + j] * b[j] * k[j * d + c] * expf(G[j * d + c]);
+        R[e] = r;
+    }
+}
+
+// ---- chain kernel ---------------------------------------------------------------
+struct ChainLds {
+    int k, G, q, R, beta, Kt, T, Hm, vt, zt, A, B, total;
+};
+__host__ __device__ inline ChainLds chain_layout(int d, int C) {
+    ChainLds L;
+    int o = 0;
+    const int cd = C * d, cc = C * C, ct = C * TV, dt = d * TV;
+    L.k = o; o += cd;
+    L.G = o; o += cd;
+    L.q = o; o += cd;
+    L.R = o; o += cd;
+    L.beta = o; o += C;
+    L.Kt = o; o += cc;
+    L.T = o; o += cc;
+    L.Hm = o; o += cc;
+    L.vt = o; o += ct;   // v tile (forward sweep) or dO tile (reverse sweep)
+    L.zt = o; o += ct;   // Z tile or dZ tile
+    L.A = o; o += dt;    // S tile or dS tile
+    L.B = o; o += dt;    // its update
+    L.total = o;
+    return L;
+}
+
+__global__ __launch_bounds__(THREADS) void kda_bwd_chain_kernel(
+    const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
+    const float *__restrict__ g, const float *__restrict__ beta, float scale, int H, int d, int C,
+    int row_len, const int32_t *__restrict__ cu, const float *__restrict__ s0,
+    const float *__restrict__ dfinal, const float *__restrict__ dout, float *__restrict__ ds0,
+    Ws ws) {
+    extern __shared__ float sm[];
+    const ChainLds L = chain_layout(d, C);
+    float *sk = sm + L.k, *sG = sm + L.G, *sq = sm + L.q, *sR = sm + L.R, *sb = sm + L.beta;
+    float *sKt = sm + L.Kt, *sT = sm + L.T, *sHm = sm + L.Hm, *svt = sm + L.vt, *szt = sm + L.zt;
+    float *sA = sm + L.A, *sB = sm + L.B;
+
+    const int nt = d / TV;
+    const int pid = blockIdx.x / nt, tile = blockIdx.x - pid * nt;
+    const int n = pid / H, h = pid - n * H;
+    const int v0 = tile * TV, tid = threadIdx.x;
+    const int dd = d * d, dt = d * TV, ct = C * TV;
+    int ts, te;
+    seq_range(cu, row_len, n, ts, te);
+    const size_t pair = (size_t)n * H + h;
+    const int nck = (te - ts + C - 1) / C;
+    const int base = chunk_base(ts, n, C);
+
+    // Chunk c's k, G (cumulative), beta and a 16-column tile of v (forward)
+    // or of dO and all of q (reverse).
+    auto load_chunk = [&](int c, bool reverse) {
+        const int t0 = ts + c * C, len = min(C, te - t0);
+        load_rows(sk, k, t0, len, H, h, d, C, tid);
+        load_rows(sG, g, t0, len, H, h, d, C, tid);
+        if (reverse) load_rows(sq, q, t0, len, H, h, d, C, tid);
+        const float *src = reverse ? dout : v;
+        for (int e = tid; e < ct; e += THREADS) {
+            const int i = e / TV;
+            svt[e] = i < len ? src[((size_t)(t0 + i) * H + h) * d + v0 + (e - i * TV)] : 0.f;
+        }
+        for (int i = tid; i < C; i += THREADS) sb[i] = i < len ? beta[(size_t)(t0 + i) * H + h] : 0.f;
+        __syncthreads();
+        cumsum_rows(sG, d, C, tid);
+        __syncthreads();
+    };
+
+    // ---- forward sweep: S at each chunk start, and Z --------------------------
+    for (int e = tid; e < dt; e += THREADS) {
+        const int r = e / TV;
+        sA[e] = s0 ? s0[pair * dd + (size_t)r * d + v0 + (e - r * TV)] : 0.f;
+    }
+    __syncthreads();
+    for (int c = 0; c < nck; ++c) {
+        const size_t slot = (size_t)(base + c) * H + h;
+        float *Sd = ws.S + slot * dd;
+        for (int e = tid; e < dt; e += THREADS) {
+            const int r = e / TV;
+            Sd[(size_t)r * d + v0 + (e - r * TV)] = sA[e];
+        }
+        load_chunk(c, false);
+        build_T(sKt, sT, sk, sG, sb, d, C, tid);
+        build_R(sR, sT, sk, sG, sb, d, C, tid);
+        __syncthreads();
+        // Z = T Diag(beta) V - R S on this tile
+        float *Zd = ws.Z + slot * C * d;
+        for (int e = tid; e < ct; e += THREADS) {
+            const int i = e / TV, j = e - i * TV;
+            float z = 0.f;
+            for (int m = 0; m <= i; ++m) z += sT[i * C + m] * sb[m] * svt[m * TV + j];
+            for (int r = 0; r < d; ++r) z -= sR[i * d + r] * sA[r * TV + j];
+            szt[e] = z;
+            Zd[(size_t)i * d + v0 + j] = z;
+        }
+        __syncthreads();
+        // S <- Diag(e^{G_C}) S + Kbar^T Z, Kbar_ir = k_ir e^{G_C,r - G_ir}
+        for (int e = tid; e < dt; e += THREADS) {
+            const int r = e / TV, j = e - r * TV;
+            const float gl = sG[(C - 1) * d + r];
+            float acc = expf(gl) * sA[e];
+            for (int i = 0; i < C; ++i) acc += sk[i * d + r] * expf(gl - sG[i * d + r]) * szt[i * TV + j];
+            sB[e] = acc;
+        }
+        __syncthreads();
+        for (int e = tid; e < dt; e += THREADS) sA[e] = sB[e];
+        __syncthreads();
+    }
+
+    // ---- reverse sweep: dS' at each chunk end, and dZ; dS_0 at the end -----------
+    for (int e = tid; e < dt; e += THREADS) {
+        const int r = e / TV;
+        sA[e] = dfinal ? dfinal[pair * dd + (size_t)r * d + v0 + (e - r * TV)] : 0.f;
+    }
+    __syncthreads();
+    for (int c = nck - 1; c >= 0; --c) {
+        const size_t slot = (size_t)(base + c) * H + h;
+        float *dSd = ws.dS + slot * dd;
+        for (int e = tid; e < dt; e += THREADS) {
+            const int r = e / TV;
+            dSd[(size_t)r * d + v0 + (e - r * TV)] = sA[e];
+        }
+        load_chunk(c, true);
+        build_T(sKt, sT, sk, sG, sb, d, C, tid);
+        build_R(sR, sT, sk, sG, sb, d, C, tid);
+        // H_ij = s sum_c q_ic k_jc e^{G_ic - G_jc} (j <= i)
+        for (int e = tid; e < C * C; e += THREADS) {
+            const int i = e / C, j = e - i * C;
+            float hh = 0.f;
+            if (j <= i)
+                for (int c2 = 0; c2 < d; ++c2)
+                    hh += sq[i * d + c2] * expf(sG[i * d + c2] - sG[j * d + c2]) * sk[j * d + c2];
+            sHm[e] = scale * hh;
+        }
+        __syncthreads();
+        // dZ = Kbar dS' + H^T dO on this tile
+        float *dZd = ws.dZ + slot * C * d;
+        for (int e = tid; e < ct; e += THREADS) {
+            const int i = e / TV, j = e - i * TV;
+            float z = 0.f;
+            for (int r = 0; r < d; ++r)
+                z += sk[i * d + r] * expf(sG[(C - 1) * d + r] - sG[i * d + r]) * sA[r * TV + j];
+            for (int i2 = i; i2 < C; ++i2) z += sHm[i2 * C + i] * svt[i2 * TV + j];
+            szt[e] = z;
+            dZd[(size_t)i * d + v0 + j] = z;
+        }
+        __syncthreads();
+        // dS = Diag(e^{G_C}) dS' + Qbar^T dO - R^T dZ, Qbar_ir = s q_ir e^{G_ir}
+        for (int e = tid; e < dt; e += THREADS) {
+            const int r = e / TV, j = e - r * TV;
+            float a = expf(sG[(C - 1) * d + r]) * sA[e];
+            for (int i = 0; i < C; ++i)
+                a += scale * sq[i * d + r] * expf(sG[i * d + r]) * svt[i * TV + j] -
+                     sR[i * d + r] * szt[i * TV + j];
+            sB[e] = a;
+        }
+        __syncthreads();
+        for (int e = tid; e < dt; e += THREADS) sA[e] = sB[e];
+        __syncthreads();
+    }
+    if (ds0)
+        for (int e = tid; e < dt; e += THREADS) {
+            const int r = e / TV;
+            ds0[pair * dd + (size_t)r * d + v0 + (e - r * TV)] = sA[e];
+        }
+}
+
+// ---- gradient kernel ------------------------------------------------------------
+__host__ __device__ inline int slice_rows(int d) { return d < 16 ? d : 16; }
+
+struct GradLds {
+    int q, k, G, v, dO, Z, dZ, dR, dL, dQb, dKb, Ssl, dSsl, beta, dbeta, Kt, Hm, T, dT, M1, gc,
+        total;
+};
+__host__ __device__ inline GradLds grad_layout(int d, int C) {
+    GradLds L;
+    int o = 0;
+    const int cd = C * d, cc = C * C, sd = slice_rows(d) * (d + 1);
+    L.q = o; o += cd;
+    L.k = o; o += cd;
+    L.G = o; o += cd;
+    L.v = o; o += cd;
+    L.dO = o; o += cd;    // later dBV
+    L.Z = o; o += cd;
+    L.dZ = o; o += cd;
+    L.dR = o; o += cd;    // later dG
+    L.dL = o; o += cd;
+    L.dQb = o; o += cd;   // dL/dQbar = dO S^T
+    L.dKb = o; o += cd;   // dL/dKbar = Z dS'^T
+    L.Ssl = o; o += sd;   // rows of S (row stride d + 1)
+    L.dSsl = o; o += sd;  // rows of dS'
+    L.beta = o; o += C;
+    L.dbeta = o; o += C;
+    L.Kt = o; o += cc;    // K~, later its gradient
+    L.Hm = o; o += cc;    // dH
+    L.T = o; o += cc;
+    L.dT = o; o += cc;
+    L.M1 = o; o += cc;    // T^T dT
+    L.gc = o; o += d;     // e^{G_C} rowsum(dS' . S)
+    L.total = o;
+    return L;
+}
+
+__global__ __launch_bounds__(THREADS) void kda_bwd_grad_kernel(
+    const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
+    const float *__restrict__ g, const float *__restrict__ beta, float scale, int H, int d, int C,
+    int row_len, const int32_t *__restrict__ cu, int n_seqs, const float *__restrict__ dout,
+    float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv,
+    float *__restrict__ dg, float *__restrict__ dbeta, Ws ws) {
+    extern __shared__ float sm[];
+    const GradLds L = grad_layout(d, C);
+    float *sq = sm + L.q, *sk = sm + L.k, *sG = sm + L.G, *sv = sm + L.v, *sdO = sm + L.dO;
+    float *sZ = sm + L.Z, *sdZ = sm + L.dZ, *sdR = sm + L.dR, *sdL = sm + L.dL;
+    float *sdQb = sm + L.dQb, *sdKb = sm + L.dKb, *sS = sm + L.Ssl, *sdS = sm + L.dSsl;
+    float *sb = sm + L.beta, *sdb = sm + L.dbeta, *sKt = sm + L.Kt, *sHm = sm + L.Hm;
+    float *sT = sm + L.T, *sdT = sm + L.dT, *sM1 = sm + L.M1, *sgc = sm + L.gc;
+    float *sdBV = sdO, *sdG = sdR;
+
+    const int slot = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
+    const int tid = threadIdx.x;
+    // The sequence owning this slot: the last n with chunk_base(n) <= slot.
+    int lo = 0, hi = n_seqs - 1, ts, te;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        seq_range(cu, row_len, mid, ts, te);
+        if (chunk_base(ts, mid, C) <= slot) lo = mid;
+        else hi = mid - 1;
+    }
+    const int n = lo;
+    seq_range(cu, row_len, n, ts, te);
+    const int c = slot - chunk_base(ts, n, C);
+    if (c >= (te - ts + C - 1) / C) return;   // a gap slot: uniform over the workgroup
+    const int t0 = ts + c * C, len = min(C, te - t0);
+    const int cd = C * d, dd = d * d, SR = slice_rows(d), sp = d + 1;
+    const size_t wslot = (size_t)slot * H + h;
+
+    load_rows(sq, q, t0, len, H, h, d, C, tid);
+    load_rows(sk, k, t0, len, H, h, d, C, tid);
+    load_rows(sG, g, t0, len, H, h, d, C, tid);
+    load_rows(sv, v, t0, len, H, h, d, C, tid);
+    load_rows(sdO, dout, t0, len, H, h, d, C, tid);
+    for (int e = tid; e < cd; e += THREADS) {
+        sZ[e] = ws.Z[wslot * cd + e];
+        sdZ[e] = ws.dZ[wslot * cd + e];
+    }
+    for (int i = tid; i < C; i += THREADS) sb[i] = i < len ? beta[(size_t)(t0 + i) * H + h] : 0.f;
+    __syncthreads();
+    cumsum_rows(sG, d, C, tid);
+    __syncthreads();
+    build_T(sKt, sT, sk, sG, sb, d, C, tid);
+
+    // The products with S and dS', SR channel rows at a time:
+    //   dR = -dZ S^T,  dQbar = dO S^T,  dKbar = Z dS'^T,  gc = e^{G_C} rowsum(dS' . S).
+    const float *Sg = ws.S + wslot * dd, *dSg = ws.dS + wslot * dd;
+    for (int r0 = 0; r0 < d; r0 += SR) {
+        for (int e = tid; e < SR * d; e += THREADS) {
+            const int rr = e / d, u = e - rr * d;
+            sS[rr * sp + u] = Sg[(size_t)r0 * d + e];
+            sdS[rr * sp + u] = dSg[(size_t)r0 * d + e];
+        }
+        __syncthreads();
+        for (int e = tid; e < C * SR; e += THREADS) {
+            const int x = e / SR, rr = e - x * SR;
+            float a = 0.f, b = 0.f, z = 0.f;
+            for (int u = 0; u < d; ++u) {
+                const float s = sS[rr * sp + u];
+                a += sdZ[x * d + u] * s;
+                b += sdO[x * d + u] * s;
+                z += sZ[x * d + u] * sdS[rr * sp + u];
+            }
+            sdR[x * d + r0 + rr] = -a;
+            sdQb[x * d + r0 + rr] = b;
+            sdKb[x * d + r0 + rr] = z;
+        }
+        for (int rr = tid; rr < SR; rr += THREADS) {
+            float a = 0.f;
+            for (int u = 0; u < d; ++u) a += sdS[rr * sp + u] * sS[rr * sp + u];
+            sgc[r0 + rr] = expf(sG[(C - 1) * d + r0 + rr]) * a;
+        }
+        __syncthreads();
+    }
+    // dT = dZ (BV)^T + dR (BL)^T;  dH = dO Z^T (j <= i)
+    for (int e = tid; e < C * C; e += THREADS) {
+        const int i = e / C, j = e - i * C;
+        float a = 0.f;
+        for (int c2 = 0; c2 < d; ++c2)
+            a += sb[j] * (sdZ[i * d + c2] * sv[j * d + c2] +
+                          sdR[i * d + c2] * sk[j * d + c2] * expf(sG[j * d + c2]));
+        sdT[e] = a;
+        float hh = 0.f;
+        if (j <= i)
+            for (int c2 = 0; c2 < d; ++c2) hh += sdO[i * d + c2] * sZ[j * d + c2];
+        sHm[e] = hh;
+    }
+    __syncthreads();
+    // dBV = T^T dZ (into dO's storage), dBL = T^T dR
+    for (int e = tid; e < cd; e += THREADS) {
+        const int j = e / d, c2 = e - j * d;
+        float bv = 0.f, bl = 0.f;
+        for (int i = j; i < C; ++i) {
+            bv += sT[i * C + j] * sdZ[i * d + c2];
+            bl += sT[i * C + j] * sdR[i * d + c2];
+        }
+        sdBV[e] = bv;
+        sdL[e] = bl;
+    }
+    __syncthreads();
+    // dbeta_j = dBV_j . v_j + dBL_j . L_j;  M1 = T^T dT
+    for (int j = tid; j < C; j += THREADS) {
+        float s = 0.f;
+        for (int c2 = 0; c2 < d; ++c2)
+            s += sdBV[j * d + c2] * sv[j * d + c2] +
+                 sdL[j * d + c2] * sk[j * d + c2] * expf(sG[j * d + c2]);
+        sdb[j] = s;
+    }
+    for (int e = tid; e < C * C; e += THREADS) {
+        const int i = e / C, j = e - i * C;
+        float a = 0.f;
+        for (int m = i; m < C; ++m) a += sT[m * C + i] * sdT[m * C + j];
+        sM1[e] = a;
+    }
+    __syncthreads();
+    // dv = beta dBV;  dL = beta dBL (in place);
+    // dA = M1 T^T (strictly lower), dbeta_i -= sum_j dA_ij K~_ij,
+    // dK~_ij = -beta_i dA_ij into K~'s storage (one thread per row)
+    for (int e = tid; e < cd; e += THREADS) {
+        const int j = e / d;
+        if (j < len) dv[((size_t)(t0 + j) * H + h) * d + (e - j * d)] = sb[j] * sdBV[e];
+        sdL[e] *= sb[j];
+    }
+    for (int i = tid; i < C; i += THREADS) {
+        float s = 0.f;
+        for (int j = 0; j < i; ++j) {
+            float a = 0.f;
+            for (int m = 0; m <= j; ++m) a += sM1[i * C + m] * sT[j * C + m];
+            s += a * sKt[i * C + j];
+            sKt[i * C + j] = -sb[i] * a;
+        }
+        for (int j = i; j < C; ++j) sKt[i * C + j] = 0.f;
+        sdb[i] -= s;
+    }
+    __syncthreads();
+    // Per (row x, channel c), with E_ij = e^{G_ic - G_jc}:
+    //   P1 = sum_{j<x} dK~_xj k_jc E_xj,  P2 = sum_{i>x} dK~_ix k_ic E_ix,
+    //   P3 = sum_{j<=x} dH_xj k_jc E_xj,  P4 = sum_{i>=x} dH_ix (s q_ic) E_ix;
+    // then the direct uses of e^{G} in Qbar, L and Kbar.
+    for (int e = tid; e < cd; e += THREADS) {
+        const int x = e / d, c2 = e - x * d;
+        const float Gx = sG[e], kx = sk[e], qx = scale * sq[e];
+        float P1 = 0.f, P2 = 0.f, P3 = 0.f, P4 = 0.f;
+        for (int j = 0; j <= x; ++j) {
+            const float E = expf(Gx - sG[j * d + c2]);
+            if (j < x) P1 += sKt[x * C + j] * sk[j * d + c2] * E;
+            P3 += sHm[x * C + j] * sk[j * d + c2] * E;
+        }
+        for (int i = x; i < C; ++i) {
+            const float E = expf(sG[i * d + c2] - Gx);
+            if (i > x) P2 += sKt[i * C + x] * sk[i * d + c2] * E;
+            P4 += sHm[i * C + x] * scale * sq[i * d + c2] * E;
+        }
+        const float dQb = sdQb[e], dKb = sdKb[e];
+        const float eG = expf(Gx), eK = expf(sG[(C - 1) * d + c2] - Gx);
+        const float dqs = P3 + dQb * eG;
+        const float dkx = P1 + P2 + P4 + sdL[e] * eG + dKb * eK;
+        const float dGx = kx * (P1 - P2 - P4) + qx * P3 + dQb * qx * eG + sdL[e] * kx * eG -
+                          dKb * kx * eK;
+        if (x < len) {
+            const size_t a = ((size_t)(t0 + x) * H + h) * d + c2;
+            dq[a] = scale * dqs;
+            dk[a] = dkx;
+        }
+        sdG[e] = dGx;
+        sdL[e] = dKb * kx * eK;   // Kbar-term of dG_C, summed over rows below
+    }
+    __syncthreads();
+    // dG_C = gc + sum_x dKbar_x Kbar_x joins the last row; dg is the reverse
+    // cumulative sum of dG over the valid rows (padding rows carry nothing).
+    for (int c2 = tid; c2 < d; c2 += THREADS) {
+        float run = sgc[c2];
+        for (int x = 0; x < C; ++x) run += sdL[x * d + c2];
+        for (int x = len - 1; x >= 0; --x) {
+            run += sdG[x * d + c2];
+            dg[((size_t)(t0 + x) * H + h) * d + c2] = run;
+        }
+    }
+    for (int j = tid; j < len; j += THREADS) dbeta[(size_t)(t0 + j) * H + h] = sdb[j];
+}
+
+}  // namespace bwd
+
+bool bwd_supported(int dk, int dv, int chunk) {
+    if (dk != dv || !(dk == 16 || dk == 32 || dk == 64 || dk == 128)) return false;
+    if (!(chunk == 16 || chunk == 32 || chunk == 64)) return false;
+    const size_t cap = 163840 / sizeof(float);
+    return (size_t)bwd::chain_layout(dk, chunk).total <= cap &&
+           (size_t)bwd::grad_layout(dk, chunk).total <= cap;
+}
+
+size_t bwd_workspace_bytes(int64_t total_tokens, int n_seqs, int heads, int d, int chunk) {
+    const size_t slots = bwd::n_slots(total_tokens, n_seqs, chunk);
+    return slots * heads * (2 * (size_t)d * d + 2 * (size_t)chunk * d) * sizeof(float);
+}
+
+hipError_t launch_chunk_bwd(const ChunkBwdProblem &p) {
+    using namespace bwd;
+    const int64_t total = p.cu ? (int64_t)p.seqlen : (int64_t)p.n_seqs * p.seqlen;
+    const size_t slots = n_slots(total, p.n_seqs, p.chunk);
+    const Ws ws = ws_layout(p.work, slots, p.heads, p.d, p.chunk);
+    const size_t lc = (size_t)chain_layout(p.d, p.chunk).total * sizeof(float);
+    const size_t lg = (size_t)grad_layout(p.d, p.chunk).total * sizeof(float);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kda_bwd_chain_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lc);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kda_bwd_grad_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lg);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kda_bwd_chain_kernel, dim3(p.n_seqs * p.heads * (p.d / TV)), dim3(THREADS),
+                       lc, p.stream, p.q, p.k, p.v, p.g, p.beta, p.scale, p.heads, p.d, p.chunk,
+                       p.seqlen, p.cu, p.s0, p.dfinal, p.dout, p.ds0, ws);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kda_bwd_grad_kernel, dim3((unsigned)(slots * p.heads)), dim3(THREADS), lg,
+                       p.stream, p.q, p.k, p.v, p.g, p.beta, p.scale, p.heads, p.d, p.chunk,
+                       p.seqlen, p.cu, p.n_seqs, p.dout, p.dq, p.dk, p.dv, p.dg, p.dbeta, ws);
+    return hipGetLastError();
+}
+
+}  // namespace kda

@@ -87,11 +87,11 @@ struct ChunkBwdProblem {
     const float *dout;      // gradient of o
     float *dq, *dk, *dv, *dg, *dbeta;
     float *ds0;             // may be null (not written)
-    float *ckpt;            // workspace: chunk-start states
+    float *work;            // workspace: per chunk S, dS', Z and dZ
     hipStream_t stream;
 };
-bool bwd_f32_supported(int dk, int dv, int chunk);
-size_t bwd_f32_workspace_bytes(int64_t total_tokens, int n_seqs, int heads, int d, int chunk);
-hipError_t launch_chunk_bwd_f32(const ChunkBwdProblem &p);
+bool bwd_supported(int dk, int dv, int chunk);
+size_t bwd_workspace_bytes(int64_t total_tokens, int n_seqs, int heads, int d, int chunk);
+hipError_t launch_chunk_bwd(const ChunkBwdProblem &p);
 
 }  // namespace kda

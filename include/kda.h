@@ -293,12 +293,16 @@ kda_status kda_output_rmsnorm_gate(int64_t rows, int32_t d_v, kda_dtype dtype,
  * gradients ("Kimi Delta Attention: How It Works, Step by Step" motivates the
  * chunkwise form by training); this reverses the chunk algebra of
  * "Understanding Kimi Delta Attention", sections "The triangular system" and
- * "Putting the chunks together", step by step: a forward pass stores each
- * chunk's start state in the workspace, then the chunks are walked in reverse
- * carrying dL/dS across chunk boundaries.
+ * "Putting the chunks together", step by step.  A chain kernel (one
+ * workgroup per sequence, head and 16 value columns) walks the chunks forward
+ * storing each chunk's start state and Z = U - R S, then in reverse carrying
+ * dL/dS across chunk boundaries and storing each chunk's end-state gradient
+ * and dZ; a second kernel (one workgroup per chunk and head) forms every
+ * other gradient from one chunk's inputs and those stored quantities.
  *
  *   shape         as kda_chunk_fwd; dtype KDA_F32 only, d_k = d_v = d with
- *                 (d, chunk) in {(16, 16|32|64), (32, 16|32), (64, 16|32)}.
+ *                 (d, chunk) in {(16, 16|32|64), (32, 16|32), (64, 16|32),
+ *                 (128, 16)}.
  *   q, k, g_log_decay, v, beta, scale, initial_state, cu_seqlens
  *                 the forward's inputs, same layouts (initial_state may be NULL).
  *   d_o           [B, T, H, d_v] fp32: dL/do.
@@ -307,7 +311,9 @@ kda_status kda_output_rmsnorm_gate(int64_t rows, int32_t d_v, kda_dtype dtype,
  *                 outputs with the layouts of q, k, v, g_log_decay, beta.
  *   d_initial_state [N, H, d_k, d_v] fp32 or NULL (not written).
  *   workspace     at least kda_chunk_bwd_workspace_bytes(shape) bytes,
- *                 256-byte aligned (chunk-start states, fp32).
+ *                 256-byte aligned: per chunk slot and head, the chunk-start
+ *                 state and end-state gradient (d x d) and Z, dZ (chunk x d),
+ *                 fp32, with T_total / chunk + N + 1 slots.
  * Tensors 16-byte aligned (beta, dbeta, cu_seqlens 4-byte); outputs must not
  * alias inputs.  Log-decays must be finite.  Asynchronous on `stream`; the
  * library enqueues kernels only.

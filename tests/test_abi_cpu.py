@@ -189,7 +189,10 @@ def call_bwd(sh, **kw):
 def test_backward_rejects_unsupported_problems():
     f32 = dict(d_k=32, d_v=32, chunk_size=32, dtype_code=K.KDA_F32, seqlen=64, heads=2)
     assert call_bwd(shape(**dict(f32, dtype_code=K.KDA_BF16))) == 2
-    assert call_bwd(shape(**dict(f32, d_k=128, d_v=128))) == 2
+    assert call_bwd(shape(**dict(f32, d_k=128, d_v=128))) == 2          # d = 128 needs chunk 16
+    assert call_bwd(shape(**dict(f32, d_k=128, d_v=128, chunk_size=64))) == 2
+    assert call_bwd(shape(**dict(f32, d_k=96, d_v=96, chunk_size=16))) == 2
+    assert call_bwd(shape(**dict(f32, d_k=64, d_v=32, chunk_size=16))) == 2
     assert call_bwd(shape(**dict(f32, chunk_size=64))) == 2
     assert call_bwd(shape(**f32), dq=None) == 1
     assert call_bwd(shape(**f32), dq=ctypes.c_void_p(0x1000)) == \
@@ -201,5 +204,11 @@ def test_backward_rejects_unsupported_problems():
 
 def test_backward_workspace_query():
     sh = shape(d_k=16, d_v=16, chunk_size=16, dtype_code=K.KDA_F32, seqlen=100, heads=3)
-    # chunk-start states: (T / C + N + 1) slots of H x d x d fp32
-    assert K.lib().kda_chunk_bwd_workspace_bytes(ctypes.byref(sh)) == (100 // 16 + 1 + 1) * 3 * 16 * 16 * 4
+    # (T / C + N + 1) chunk slots per head, each with the chunk-start state and
+    # the end-state gradient (d x d) and Z, dZ (C x d), fp32
+    slots = 100 // 16 + 1 + 1
+    assert K.lib().kda_chunk_bwd_workspace_bytes(ctypes.byref(sh)) == \
+        slots * 3 * (2 * 16 * 16 + 2 * 16 * 16) * 4
+    sh = shape(d_k=128, d_v=128, chunk_size=16, dtype_code=K.KDA_F32, seqlen=4096, heads=2)
+    assert K.lib().kda_chunk_bwd_workspace_bytes(ctypes.byref(sh)) == \
+        (4096 // 16 + 2) * 2 * (2 * 128 * 128 + 2 * 16 * 128) * 4

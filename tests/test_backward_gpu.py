@@ -1,4 +1,4 @@
-"""The GPU backward (kda_chunk_bwd, fp32 small-width path) against the fp64
+"""The GPU backward (kda_chunk_bwd, fp32 storage) against the fp64
 autograd oracle of the recurrence (oracle/backward.py, pinned to finite
 differences), through the C ABI.  Tolerance: relative Frobenius error <= 1e-4
 on every gradient, as for the fp32 forward."""
@@ -67,7 +67,7 @@ def check(x, chunk):
 
 
 @pytest.mark.parametrize("d,C,T", [(16, 16, 70), (16, 64, 150), (32, 16, 47), (32, 32, 100),
-                                   (64, 16, 40), (64, 32, 65)])
+                                   (64, 16, 40), (64, 32, 65), (128, 16, 40)])
 def test_backward_shapes(d, C, T):
     check(make(2, T, 2, d, seed=100 + d + C), C)
 
@@ -82,3 +82,11 @@ def test_backward_strong_decays():
 
 def test_backward_without_states():
     check(make(1, 80, 3, 16, seed=203, s0=False, dfin=False), 32)
+
+
+def test_backward_d128_packed_sequences():
+    check(make(1, 0, 2, 128, seed=204, lengths=[33, 0, 17, 30]), 16)
+
+
+def test_backward_d128_strong_decays_without_initial_state():
+    check(make(1, 37, 1, 128, seed=205, g_range=(-5.0, 0.0), s0=False), 16)
