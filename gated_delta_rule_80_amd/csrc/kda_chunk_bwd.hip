@@ -63,66 +63,92 @@ __device__ __forceinline__ void seq_range(const int32_t *cu, int row_len, int n,
 }
 
 // ---- shared chunk steps (one workgroup, THREADS threads, operands in LDS) ----------
-// Loads rows t0 .. t0+len-1 of a [tokens, H, d] tensor into dst[C][d] (zeros below).
+// [C][d] operands sit in LDS with row stride d + 1, so that lanes walking the
+// rows of one column hit distinct banks.
+__host__ __device__ inline int row_stride(int d) { return d + 1; }
+
+// Loads rows t0 .. t0+len-1 of a [tokens, H, d] tensor into dst[C][dp] (zeros below).
+template <int C>
 __device__ __forceinline__ void load_rows(float *dst, const float *src, int t0, int len, int H,
-                                          int h, int d, int C, int tid) {
+                                          int h, int d, int tid) {
+    const int dp = row_stride(d);
     for (int e = tid; e < C * d; e += THREADS) {
-        const int i = e / d;
-        dst[e] = i < len ? src[((size_t)(t0 + i) * H + h) * d + (e - i * d)] : 0.f;
+        const int i = e / d, c = e - i * d;
+        dst[i * dp + c] = i < len ? src[((size_t)(t0 + i) * H + h) * d + c] : 0.f;
     }
 }
 // In place: G[i][c] <- sum_{r <= i} g[r][c] (padding rows add zero).
-__device__ __forceinline__ void cumsum_rows(float *G, int d, int C, int tid) {
+template <int C> __device__ __forceinline__ void cumsum_rows(float *G, int d, int tid) {
+    const int dp = row_stride(d);
     for (int c = tid; c < d; c += THREADS) {
         float run = 0.f;
+#pragma unroll 4
         for (int i = 0; i < C; ++i) {
-            run += G[i * d + c];
-            G[i * d + c] = run;
+            run += G[i * dp + c];
+            G[i * dp + c] = run;
         }
     }
 }
-// K~_ij = sum_c k_ic k_jc e^{G_ic - G_jc} (j < i, else 0) and
-// T = (I + Diag(beta) K~)^{-1} by forward substitution, one column per thread.
-__device__ __forceinline__ void build_T(float *Kt, float *T, const float *k, const float *G,
-                                        const float *b, int d, int C, int tid) {
+// Pairwise decay-weighted products, with E_ijc = e^{G_ic - G_jc} (exponent <= 0):
+//   K~_ij = sum_c k_ic k_jc E_ijc (j < i, else 0),
+//   H_ij  = s sum_c q_ic k_jc E_ijc (j <= i, else 0; only when Hm is given).
+template <int C>
+__device__ __forceinline__ void pair_products(float *Kt, float *Hm, const float *k,
+                                              const float *q, const float *G, float scale, int d,
+                                              int tid) {
+    const int dp = row_stride(d);
     for (int e = tid; e < C * C; e += THREADS) {
         const int i = e / C, j = e - i * C;
-        float a = 0.f;
-        if (j < i)
-            for (int c = 0; c < d; ++c) a += k[i * d + c] * expf(G[i * d + c] - G[j * d + c]) * k[j * d + c];
-        Kt[e] = a;
-    }
-    __syncthreads();
-    for (int j = tid; j < C; j += THREADS)
-        for (int i = 0; i < C; ++i) {
-            float s = (i == j) ? 1.f : 0.f;
-            for (int m = j; m < i; ++m) s -= b[i] * Kt[i * C + m] * T[m * C + j];
-            T[i * C + j] = (i < j) ? 0.f : s;
+        float a = 0.f, hh = 0.f;
+        if (j <= i) {
+            if (Hm) {
+                for (int c = 0; c < d; ++c) {
+                    const float E = fast_exp(G[i * dp + c] - G[j * dp + c]) * k[j * dp + c];
+                    a += k[i * dp + c] * E;
+                    hh += q[i * dp + c] * E;
+                }
+            } else if (j < i) {
+                for (int c = 0; c < d; ++c)
+                    a += k[i * dp + c] * fast_exp(G[i * dp + c] - G[j * dp + c]) * k[j * dp + c];
+            }
         }
-    __syncthreads();
+        Kt[e] = (j < i) ? a : 0.f;
+        if (Hm) Hm[e] = scale * hh;
+    }
 }
-// R = T Diag(beta) L with L_j = k_j e^{G_j}.
-__device__ __forceinline__ void build_R(float *R, const float *T, const float *k, const float *G,
-                                        const float *b, int d, int C, int tid) {
-    for (int e = tid; e < C * d; e += THREADS) {
-        const int i = e / d, c = e - i * d;
-        float r = 0.f;
-        for (int j = 0; j <= i; ++j) r += T[i * C + j] * b[j] * k[j * d + c] * expf(G[j * d + c]);
-        R[e] = r;
+// T = (I + Diag(beta) K~)^{-1}, unit lower triangular.  Thread j < C solves
+// column j by forward substitution, keeping the column in registers:
+//   T_ij = delta_ij - beta_i sum_{j <= m < i} K~_im T_mj.
+template <int C>
+__device__ __forceinline__ void solve_T(float *T, const float *Kt, const float *b, int tid) {
+    if (tid < C) {
+        const int j = tid;
+        float col[C];
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            float s = 0.f;
+#pragma unroll
+            for (int m = 0; m < i; ++m) s += Kt[i * C + m] * col[m];
+            col[i] = (i < j) ? 0.f : ((i == j) ? 1.f : -b[i] * s);
+        }
+#pragma unroll
+        for (int i = 0; i < C; ++i) T[i * C + j] = col[i];
     }
 }
 
 // ---- chain kernel ---------------------------------------------------------------
 struct ChainLds {
-    int k, G, q, R, beta, Kt, T, Hm, vt, zt, A, B, total;
+    int k, G, q, LQ, Kb, R, beta, Kt, T, Hm, vt, zt, A, B, total;
 };
 __host__ __device__ inline ChainLds chain_layout(int d, int C) {
     ChainLds L;
     int o = 0;
-    const int cd = C * d, cc = C * C, ct = C * TV, dt = d * TV;
+    const int cd = C * row_stride(d), cc = C * C, ct = C * TV, dt = d * TV;
     L.k = o; o += cd;
     L.G = o; o += cd;
     L.q = o; o += cd;
+    L.LQ = o; o += cd;   // L = k e^{G} for R, then Qbar = s q e^{G}
+    L.Kb = o; o += cd;   // Kbar = k e^{G_C - G}
     L.R = o; o += cd;
     L.beta = o; o += C;
     L.Kt = o; o += cc;
@@ -136,36 +162,37 @@ __host__ __device__ inline ChainLds chain_layout(int d, int C) {
     return L;
 }
 
+template <int C>
 __global__ __launch_bounds__(THREADS) void kda_bwd_chain_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
-    const float *__restrict__ g, const float *__restrict__ beta, float scale, int H, int d, int C,
+    const float *__restrict__ g, const float *__restrict__ beta, float scale, int H, int d,
     int row_len, const int32_t *__restrict__ cu, const float *__restrict__ s0,
     const float *__restrict__ dfinal, const float *__restrict__ dout, float *__restrict__ ds0,
     Ws ws) {
     extern __shared__ float sm[];
     const ChainLds L = chain_layout(d, C);
-    float *sk = sm + L.k, *sG = sm + L.G, *sq = sm + L.q, *sR = sm + L.R, *sb = sm + L.beta;
-    float *sKt = sm + L.Kt, *sT = sm + L.T, *sHm = sm + L.Hm, *svt = sm + L.vt, *szt = sm + L.zt;
-    float *sA = sm + L.A, *sB = sm + L.B;
+    float *sk = sm + L.k, *sG = sm + L.G, *sq = sm + L.q, *sLQ = sm + L.LQ, *sKb = sm + L.Kb;
+    float *sR = sm + L.R, *sb = sm + L.beta, *sKt = sm + L.Kt, *sT = sm + L.T, *sHm = sm + L.Hm;
+    float *svt = sm + L.vt, *szt = sm + L.zt, *sA = sm + L.A, *sB = sm + L.B;
 
     const int nt = d / TV;
     const int pid = blockIdx.x / nt, tile = blockIdx.x - pid * nt;
     const int n = pid / H, h = pid - n * H;
     const int v0 = tile * TV, tid = threadIdx.x;
-    const int dd = d * d, dt = d * TV, ct = C * TV;
+    const int dd = d * d, dt = d * TV, ct = C * TV, dp = row_stride(d);
     int ts, te;
     seq_range(cu, row_len, n, ts, te);
     const size_t pair = (size_t)n * H + h;
     const int nck = (te - ts + C - 1) / C;
     const int base = chunk_base(ts, n, C);
 
-    // Chunk c's k, G (cumulative), beta and a 16-column tile of v (forward)
-    // or of dO and all of q (reverse).
-    auto load_chunk = [&](int c, bool reverse) {
+    // Chunk c: k, G (cumulative), beta and a 16-column tile of v (forward) or of
+    // dO and all of q (reverse); then L, Kbar, K~ (and H), and T.
+    auto prepare_chunk = [&](int c, bool reverse) {
         const int t0 = ts + c * C, len = min(C, te - t0);
-        load_rows(sk, k, t0, len, H, h, d, C, tid);
-        load_rows(sG, g, t0, len, H, h, d, C, tid);
-        if (reverse) load_rows(sq, q, t0, len, H, h, d, C, tid);
+        load_rows<C>(sk, k, t0, len, H, h, d, tid);
+        load_rows<C>(sG, g, t0, len, H, h, d, tid);
+        if (reverse) load_rows<C>(sq, q, t0, len, H, h, d, tid);
         const float *src = reverse ? dout : v;
         for (int e = tid; e < ct; e += THREADS) {
             const int i = e / TV;
@@ -173,7 +200,25 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_chain_kernel(
         }
         for (int i = tid; i < C; i += THREADS) sb[i] = i < len ? beta[(size_t)(t0 + i) * H + h] : 0.f;
         __syncthreads();
-        cumsum_rows(sG, d, C, tid);
+        cumsum_rows<C>(sG, d, tid);
+        __syncthreads();
+        for (int e = tid; e < C * d; e += THREADS) {
+            const int i = e / d, c2 = e - i * d, a = i * dp + c2;
+            const float kk = sk[a], G = sG[a];
+            sLQ[a] = kk * fast_exp(G);
+            sKb[a] = kk * fast_exp(sG[(C - 1) * dp + c2] - G);
+        }
+        pair_products<C>(sKt, reverse ? sHm : nullptr, sk, sq, sG, scale, d, tid);
+        __syncthreads();
+        solve_T<C>(sT, sKt, sb, tid);
+        __syncthreads();
+        // R = T Diag(beta) L
+        for (int e = tid; e < C * d; e += THREADS) {
+            const int i = e / d, c2 = e - i * d;
+            float r = 0.f;
+            for (int j = 0; j <= i; ++j) r += sT[i * C + j] * sb[j] * sLQ[j * dp + c2];
+            sR[i * dp + c2] = r;
+        }
         __syncthreads();
     };
 
@@ -190,27 +235,24 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_chain_kernel(
             const int r = e / TV;
             Sd[(size_t)r * d + v0 + (e - r * TV)] = sA[e];
         }
-        load_chunk(c, false);
-        build_T(sKt, sT, sk, sG, sb, d, C, tid);
-        build_R(sR, sT, sk, sG, sb, d, C, tid);
-        __syncthreads();
+        prepare_chunk(c, false);
         // Z = T Diag(beta) V - R S on this tile
         float *Zd = ws.Z + slot * C * d;
         for (int e = tid; e < ct; e += THREADS) {
             const int i = e / TV, j = e - i * TV;
             float z = 0.f;
             for (int m = 0; m <= i; ++m) z += sT[i * C + m] * sb[m] * svt[m * TV + j];
-            for (int r = 0; r < d; ++r) z -= sR[i * d + r] * sA[r * TV + j];
+            for (int r = 0; r < d; ++r) z -= sR[i * dp + r] * sA[r * TV + j];
             szt[e] = z;
             Zd[(size_t)i * d + v0 + j] = z;
         }
         __syncthreads();
-        // S <- Diag(e^{G_C}) S + Kbar^T Z, Kbar_ir = k_ir e^{G_C,r - G_ir}
+        // S <- Diag(e^{G_C}) S + Kbar^T Z
         for (int e = tid; e < dt; e += THREADS) {
             const int r = e / TV, j = e - r * TV;
-            const float gl = sG[(C - 1) * d + r];
-            float acc = expf(gl) * sA[e];
-            for (int i = 0; i < C; ++i) acc += sk[i * d + r] * expf(gl - sG[i * d + r]) * szt[i * TV + j];
+            float acc = fast_exp(sG[(C - 1) * dp + r]) * sA[e];
+#pragma unroll 4
+            for (int i = 0; i < C; ++i) acc += sKb[i * dp + r] * szt[i * TV + j];
             sB[e] = acc;
         }
         __syncthreads();
@@ -231,38 +273,29 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_chain_kernel(
             const int r = e / TV;
             dSd[(size_t)r * d + v0 + (e - r * TV)] = sA[e];
         }
-        load_chunk(c, true);
-        build_T(sKt, sT, sk, sG, sb, d, C, tid);
-        build_R(sR, sT, sk, sG, sb, d, C, tid);
-        // H_ij = s sum_c q_ic k_jc e^{G_ic - G_jc} (j <= i)
-        for (int e = tid; e < C * C; e += THREADS) {
-            const int i = e / C, j = e - i * C;
-            float hh = 0.f;
-            if (j <= i)
-                for (int c2 = 0; c2 < d; ++c2)
-                    hh += sq[i * d + c2] * expf(sG[i * d + c2] - sG[j * d + c2]) * sk[j * d + c2];
-            sHm[e] = scale * hh;
-        }
-        __syncthreads();
-        // dZ = Kbar dS' + H^T dO on this tile
+        prepare_chunk(c, true);
+        // dZ = Kbar dS' + H^T dO on this tile; L's storage takes Qbar = s q e^{G}
         float *dZd = ws.dZ + slot * C * d;
         for (int e = tid; e < ct; e += THREADS) {
             const int i = e / TV, j = e - i * TV;
             float z = 0.f;
-            for (int r = 0; r < d; ++r)
-                z += sk[i * d + r] * expf(sG[(C - 1) * d + r] - sG[i * d + r]) * sA[r * TV + j];
+            for (int r = 0; r < d; ++r) z += sKb[i * dp + r] * sA[r * TV + j];
             for (int i2 = i; i2 < C; ++i2) z += sHm[i2 * C + i] * svt[i2 * TV + j];
             szt[e] = z;
             dZd[(size_t)i * d + v0 + j] = z;
         }
+        for (int e = tid; e < C * d; e += THREADS) {
+            const int i = e / d, a = i * dp + (e - i * d);
+            sLQ[a] = scale * sq[a] * fast_exp(sG[a]);
+        }
         __syncthreads();
-        // dS = Diag(e^{G_C}) dS' + Qbar^T dO - R^T dZ, Qbar_ir = s q_ir e^{G_ir}
+        // dS = Diag(e^{G_C}) dS' + Qbar^T dO - R^T dZ
         for (int e = tid; e < dt; e += THREADS) {
             const int r = e / TV, j = e - r * TV;
-            float a = expf(sG[(C - 1) * d + r]) * sA[e];
+            float a = fast_exp(sG[(C - 1) * dp + r]) * sA[e];
+#pragma unroll 4
             for (int i = 0; i < C; ++i)
-                a += scale * sq[i * d + r] * expf(sG[i * d + r]) * svt[i * TV + j] -
-                     sR[i * d + r] * szt[i * TV + j];
+                a += sLQ[i * dp + r] * svt[i * TV + j] - sR[i * dp + r] * szt[i * TV + j];
             sB[e] = a;
         }
         __syncthreads();
@@ -286,7 +319,7 @@ struct GradLds {
 __host__ __device__ inline GradLds grad_layout(int d, int C) {
     GradLds L;
     int o = 0;
-    const int cd = C * d, cc = C * C, sd = slice_rows(d) * (d + 1);
+    const int cd = C * row_stride(d), cc = C * C, sd = slice_rows(d) * row_stride(d);
     L.q = o; o += cd;
     L.k = o; o += cd;
     L.G = o; o += cd;
@@ -298,23 +331,24 @@ __host__ __device__ inline GradLds grad_layout(int d, int C) {
     L.dL = o; o += cd;
     L.dQb = o; o += cd;   // dL/dQbar = dO S^T
     L.dKb = o; o += cd;   // dL/dKbar = Z dS'^T
-    L.Ssl = o; o += sd;   // rows of S (row stride d + 1)
+    L.Ssl = o; o += sd;   // rows of S
     L.dSsl = o; o += sd;  // rows of dS'
     L.beta = o; o += C;
     L.dbeta = o; o += C;
     L.Kt = o; o += cc;    // K~, later its gradient
     L.Hm = o; o += cc;    // dH
     L.T = o; o += cc;
-    L.dT = o; o += cc;
+    L.dT = o; o += cc;    // later dA . K~
     L.M1 = o; o += cc;    // T^T dT
     L.gc = o; o += d;     // e^{G_C} rowsum(dS' . S)
     L.total = o;
     return L;
 }
 
+template <int C>
 __global__ __launch_bounds__(THREADS) void kda_bwd_grad_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
-    const float *__restrict__ g, const float *__restrict__ beta, float scale, int H, int d, int C,
+    const float *__restrict__ g, const float *__restrict__ beta, float scale, int H, int d,
     int row_len, const int32_t *__restrict__ cu, int n_seqs, const float *__restrict__ dout,
     float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv,
     float *__restrict__ dg, float *__restrict__ dbeta, Ws ws) {
@@ -325,7 +359,7 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_grad_kernel(
     float *sdQb = sm + L.dQb, *sdKb = sm + L.dKb, *sS = sm + L.Ssl, *sdS = sm + L.dSsl;
     float *sb = sm + L.beta, *sdb = sm + L.dbeta, *sKt = sm + L.Kt, *sHm = sm + L.Hm;
     float *sT = sm + L.T, *sdT = sm + L.dT, *sM1 = sm + L.M1, *sgc = sm + L.gc;
-    float *sdBV = sdO, *sdG = sdR;
+    float *sdBV = sdO, *sdG = sdR, *sAK = sdT;
 
     const int slot = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
     const int tid = threadIdx.x;
@@ -342,51 +376,54 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_grad_kernel(
     const int c = slot - chunk_base(ts, n, C);
     if (c >= (te - ts + C - 1) / C) return;   // a gap slot: uniform over the workgroup
     const int t0 = ts + c * C, len = min(C, te - t0);
-    const int cd = C * d, dd = d * d, SR = slice_rows(d), sp = d + 1;
+    const int cd = C * d, dd = d * d, SR = slice_rows(d), dp = row_stride(d);
     const size_t wslot = (size_t)slot * H + h;
 
-    load_rows(sq, q, t0, len, H, h, d, C, tid);
-    load_rows(sk, k, t0, len, H, h, d, C, tid);
-    load_rows(sG, g, t0, len, H, h, d, C, tid);
-    load_rows(sv, v, t0, len, H, h, d, C, tid);
-    load_rows(sdO, dout, t0, len, H, h, d, C, tid);
+    load_rows<C>(sq, q, t0, len, H, h, d, tid);
+    load_rows<C>(sk, k, t0, len, H, h, d, tid);
+    load_rows<C>(sG, g, t0, len, H, h, d, tid);
+    load_rows<C>(sv, v, t0, len, H, h, d, tid);
+    load_rows<C>(sdO, dout, t0, len, H, h, d, tid);
     for (int e = tid; e < cd; e += THREADS) {
-        sZ[e] = ws.Z[wslot * cd + e];
-        sdZ[e] = ws.dZ[wslot * cd + e];
+        const int i = e / d, a = i * dp + (e - i * d);
+        sZ[a] = ws.Z[wslot * cd + e];
+        sdZ[a] = ws.dZ[wslot * cd + e];
     }
     for (int i = tid; i < C; i += THREADS) sb[i] = i < len ? beta[(size_t)(t0 + i) * H + h] : 0.f;
     __syncthreads();
-    cumsum_rows(sG, d, C, tid);
+    cumsum_rows<C>(sG, d, tid);
     __syncthreads();
-    build_T(sKt, sT, sk, sG, sb, d, C, tid);
+    pair_products<C>(sKt, nullptr, sk, sq, sG, scale, d, tid);
+    __syncthreads();
+    solve_T<C>(sT, sKt, sb, tid);
 
     // The products with S and dS', SR channel rows at a time:
     //   dR = -dZ S^T,  dQbar = dO S^T,  dKbar = Z dS'^T,  gc = e^{G_C} rowsum(dS' . S).
     const float *Sg = ws.S + wslot * dd, *dSg = ws.dS + wslot * dd;
     for (int r0 = 0; r0 < d; r0 += SR) {
         for (int e = tid; e < SR * d; e += THREADS) {
-            const int rr = e / d, u = e - rr * d;
-            sS[rr * sp + u] = Sg[(size_t)r0 * d + e];
-            sdS[rr * sp + u] = dSg[(size_t)r0 * d + e];
+            const int rr = e / d, a = rr * dp + (e - rr * d);
+            sS[a] = Sg[(size_t)r0 * d + e];
+            sdS[a] = dSg[(size_t)r0 * d + e];
         }
         __syncthreads();
         for (int e = tid; e < C * SR; e += THREADS) {
             const int x = e / SR, rr = e - x * SR;
             float a = 0.f, b = 0.f, z = 0.f;
             for (int u = 0; u < d; ++u) {
-                const float s = sS[rr * sp + u];
-                a += sdZ[x * d + u] * s;
-                b += sdO[x * d + u] * s;
-                z += sZ[x * d + u] * sdS[rr * sp + u];
+                const float s = sS[rr * dp + u];
+                a += sdZ[x * dp + u] * s;
+                b += sdO[x * dp + u] * s;
+                z += sZ[x * dp + u] * sdS[rr * dp + u];
             }
-            sdR[x * d + r0 + rr] = -a;
-            sdQb[x * d + r0 + rr] = b;
-            sdKb[x * d + r0 + rr] = z;
+            sdR[x * dp + r0 + rr] = -a;
+            sdQb[x * dp + r0 + rr] = b;
+            sdKb[x * dp + r0 + rr] = z;
         }
         for (int rr = tid; rr < SR; rr += THREADS) {
             float a = 0.f;
-            for (int u = 0; u < d; ++u) a += sdS[rr * sp + u] * sS[rr * sp + u];
-            sgc[r0 + rr] = expf(sG[(C - 1) * d + r0 + rr]) * a;
+            for (int u = 0; u < d; ++u) a += sdS[rr * dp + u] * sS[rr * dp + u];
+            sgc[r0 + rr] = fast_exp(sG[(C - 1) * dp + r0 + rr]) * a;
         }
         __syncthreads();
     }
@@ -395,12 +432,12 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_grad_kernel(
         const int i = e / C, j = e - i * C;
         float a = 0.f;
         for (int c2 = 0; c2 < d; ++c2)
-            a += sb[j] * (sdZ[i * d + c2] * sv[j * d + c2] +
-                          sdR[i * d + c2] * sk[j * d + c2] * expf(sG[j * d + c2]));
-        sdT[e] = a;
+            a += sdZ[i * dp + c2] * sv[j * dp + c2] +
+                 sdR[i * dp + c2] * sk[j * dp + c2] * fast_exp(sG[j * dp + c2]);
+        sdT[e] = sb[j] * a;
         float hh = 0.f;
         if (j <= i)
-            for (int c2 = 0; c2 < d; ++c2) hh += sdO[i * d + c2] * sZ[j * d + c2];
+            for (int c2 = 0; c2 < d; ++c2) hh += sdO[i * dp + c2] * sZ[j * dp + c2];
         sHm[e] = hh;
     }
     __syncthreads();
@@ -409,21 +446,13 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_grad_kernel(
         const int j = e / d, c2 = e - j * d;
         float bv = 0.f, bl = 0.f;
         for (int i = j; i < C; ++i) {
-            bv += sT[i * C + j] * sdZ[i * d + c2];
-            bl += sT[i * C + j] * sdR[i * d + c2];
+            bv += sT[i * C + j] * sdZ[i * dp + c2];
+            bl += sT[i * C + j] * sdR[i * dp + c2];
         }
-        sdBV[e] = bv;
-        sdL[e] = bl;
+        sdBV[j * dp + c2] = bv;
+        sdL[j * dp + c2] = bl;
     }
-    __syncthreads();
-    // dbeta_j = dBV_j . v_j + dBL_j . L_j;  M1 = T^T dT
-    for (int j = tid; j < C; j += THREADS) {
-        float s = 0.f;
-        for (int c2 = 0; c2 < d; ++c2)
-            s += sdBV[j * d + c2] * sv[j * d + c2] +
-                 sdL[j * d + c2] * sk[j * d + c2] * expf(sG[j * d + c2]);
-        sdb[j] = s;
-    }
+    // M1 = T^T dT
     for (int e = tid; e < C * C; e += THREADS) {
         const int i = e / C, j = e - i * C;
         float a = 0.f;
@@ -431,23 +460,34 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_grad_kernel(
         sM1[e] = a;
     }
     __syncthreads();
-    // dv = beta dBV;  dL = beta dBL (in place);
-    // dA = M1 T^T (strictly lower), dbeta_i -= sum_j dA_ij K~_ij,
-    // dK~_ij = -beta_i dA_ij into K~'s storage (one thread per row)
+    // dbeta_j = dBV_j . v_j + dBL_j . L_j
+    for (int j = tid; j < C; j += THREADS) {
+        float s = 0.f;
+        for (int c2 = 0; c2 < d; ++c2)
+            s += sdBV[j * dp + c2] * sv[j * dp + c2] +
+                 sdL[j * dp + c2] * sk[j * dp + c2] * fast_exp(sG[j * dp + c2]);
+        sdb[j] = s;
+    }
+    // dA = M1 T^T (strictly lower); dA . K~ into dT's storage (dT is consumed);
+    // dK~_ij = -beta_i dA_ij in place of K~
+    for (int e = tid; e < C * C; e += THREADS) {
+        const int i = e / C, j = e - i * C;
+        float a = 0.f;
+        if (j < i)
+            for (int m = 0; m <= j; ++m) a += sM1[i * C + m] * sT[j * C + m];
+        sAK[e] = a * sKt[e];
+        sKt[e] = -sb[i] * a;
+    }
+    __syncthreads();
+    // dv = beta dBV;  dL = beta dBL (in place);  dbeta_i -= sum_j dA_ij K~_ij
     for (int e = tid; e < cd; e += THREADS) {
-        const int j = e / d;
-        if (j < len) dv[((size_t)(t0 + j) * H + h) * d + (e - j * d)] = sb[j] * sdBV[e];
-        sdL[e] *= sb[j];
+        const int j = e / d, a = j * dp + (e - j * d);
+        if (j < len) dv[((size_t)(t0 + j) * H + h) * d + (e - j * d)] = sb[j] * sdBV[a];
+        sdL[a] *= sb[j];
     }
     for (int i = tid; i < C; i += THREADS) {
         float s = 0.f;
-        for (int j = 0; j < i; ++j) {
-            float a = 0.f;
-            for (int m = 0; m <= j; ++m) a += sM1[i * C + m] * sT[j * C + m];
-            s += a * sKt[i * C + j];
-            sKt[i * C + j] = -sb[i] * a;
-        }
-        for (int j = i; j < C; ++j) sKt[i * C + j] = 0.f;
+        for (int j = 0; j < i; ++j) s += sAK[i * C + j];
         sdb[i] -= s;
     }
     __syncthreads();
@@ -456,41 +496,41 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_grad_kernel(
     //   P3 = sum_{j<=x} dH_xj k_jc E_xj,  P4 = sum_{i>=x} dH_ix (s q_ic) E_ix;
     // then the direct uses of e^{G} in Qbar, L and Kbar.
     for (int e = tid; e < cd; e += THREADS) {
-        const int x = e / d, c2 = e - x * d;
-        const float Gx = sG[e], kx = sk[e], qx = scale * sq[e];
+        const int x = e / d, c2 = e - x * d, ax = x * dp + c2;
+        const float Gx = sG[ax], kx = sk[ax], qx = scale * sq[ax];
         float P1 = 0.f, P2 = 0.f, P3 = 0.f, P4 = 0.f;
         for (int j = 0; j <= x; ++j) {
-            const float E = expf(Gx - sG[j * d + c2]);
-            if (j < x) P1 += sKt[x * C + j] * sk[j * d + c2] * E;
-            P3 += sHm[x * C + j] * sk[j * d + c2] * E;
+            const float E = fast_exp(Gx - sG[j * dp + c2]) * sk[j * dp + c2];
+            if (j < x) P1 += sKt[x * C + j] * E;
+            P3 += sHm[x * C + j] * E;
         }
         for (int i = x; i < C; ++i) {
-            const float E = expf(sG[i * d + c2] - Gx);
-            if (i > x) P2 += sKt[i * C + x] * sk[i * d + c2] * E;
-            P4 += sHm[i * C + x] * scale * sq[i * d + c2] * E;
+            const float E = fast_exp(sG[i * dp + c2] - Gx);
+            if (i > x) P2 += sKt[i * C + x] * sk[i * dp + c2] * E;
+            P4 += sHm[i * C + x] * scale * sq[i * dp + c2] * E;
         }
-        const float dQb = sdQb[e], dKb = sdKb[e];
-        const float eG = expf(Gx), eK = expf(sG[(C - 1) * d + c2] - Gx);
+        const float dQb = sdQb[ax], dKb = sdKb[ax], dLx = sdL[ax];
+        const float eG = fast_exp(Gx), eK = fast_exp(sG[(C - 1) * dp + c2] - Gx);
         const float dqs = P3 + dQb * eG;
-        const float dkx = P1 + P2 + P4 + sdL[e] * eG + dKb * eK;
-        const float dGx = kx * (P1 - P2 - P4) + qx * P3 + dQb * qx * eG + sdL[e] * kx * eG -
+        const float dkx = P1 + P2 + P4 + dLx * eG + dKb * eK;
+        const float dGx = kx * (P1 - P2 - P4) + qx * P3 + dQb * qx * eG + dLx * kx * eG -
                           dKb * kx * eK;
         if (x < len) {
             const size_t a = ((size_t)(t0 + x) * H + h) * d + c2;
             dq[a] = scale * dqs;
             dk[a] = dkx;
         }
-        sdG[e] = dGx;
-        sdL[e] = dKb * kx * eK;   // Kbar-term of dG_C, summed over rows below
+        sdG[ax] = dGx;
+        sdL[ax] = dKb * kx * eK;   // Kbar-term of dG_C, summed over rows below
     }
     __syncthreads();
     // dG_C = gc + sum_x dKbar_x Kbar_x joins the last row; dg is the reverse
     // cumulative sum of dG over the valid rows (padding rows carry nothing).
     for (int c2 = tid; c2 < d; c2 += THREADS) {
         float run = sgc[c2];
-        for (int x = 0; x < C; ++x) run += sdL[x * d + c2];
+        for (int x = 0; x < C; ++x) run += sdL[x * dp + c2];
         for (int x = len - 1; x >= 0; --x) {
-            run += sdG[x * d + c2];
+            run += sdG[x * dp + c2];
             dg[((size_t)(t0 + x) * H + h) * d + c2] = run;
         }
     }
@@ -512,28 +552,39 @@ size_t bwd_workspace_bytes(int64_t total_tokens, int n_seqs, int heads, int d, i
     return slots * heads * (2 * (size_t)d * d + 2 * (size_t)chunk * d) * sizeof(float);
 }
 
-hipError_t launch_chunk_bwd(const ChunkBwdProblem &p) {
+namespace {
+template <int C> hipError_t launch_bwd_c(const ChunkBwdProblem &p, const bwd::Ws &ws, size_t slots) {
     using namespace bwd;
-    const int64_t total = p.cu ? (int64_t)p.seqlen : (int64_t)p.n_seqs * p.seqlen;
-    const size_t slots = n_slots(total, p.n_seqs, p.chunk);
-    const Ws ws = ws_layout(p.work, slots, p.heads, p.d, p.chunk);
-    const size_t lc = (size_t)chain_layout(p.d, p.chunk).total * sizeof(float);
-    const size_t lg = (size_t)grad_layout(p.d, p.chunk).total * sizeof(float);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kda_bwd_chain_kernel),
+    const size_t lc = (size_t)chain_layout(p.d, C).total * sizeof(float);
+    const size_t lg = (size_t)grad_layout(p.d, C).total * sizeof(float);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kda_bwd_chain_kernel<C>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lc);
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kda_bwd_grad_kernel),
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kda_bwd_grad_kernel<C>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lg);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kda_bwd_chain_kernel, dim3(p.n_seqs * p.heads * (p.d / TV)), dim3(THREADS),
-                       lc, p.stream, p.q, p.k, p.v, p.g, p.beta, p.scale, p.heads, p.d, p.chunk,
-                       p.seqlen, p.cu, p.s0, p.dfinal, p.dout, p.ds0, ws);
+    hipLaunchKernelGGL(kda_bwd_chain_kernel<C>, dim3(p.n_seqs * p.heads * (p.d / TV)),
+                       dim3(THREADS), lc, p.stream, p.q, p.k, p.v, p.g, p.beta, p.scale, p.heads,
+                       p.d, p.seqlen, p.cu, p.s0, p.dfinal, p.dout, p.ds0, ws);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kda_bwd_grad_kernel, dim3((unsigned)(slots * p.heads)), dim3(THREADS), lg,
-                       p.stream, p.q, p.k, p.v, p.g, p.beta, p.scale, p.heads, p.d, p.chunk,
-                       p.seqlen, p.cu, p.n_seqs, p.dout, p.dq, p.dk, p.dv, p.dg, p.dbeta, ws);
+    hipLaunchKernelGGL(kda_bwd_grad_kernel<C>, dim3((unsigned)(slots * p.heads)), dim3(THREADS),
+                       lg, p.stream, p.q, p.k, p.v, p.g, p.beta, p.scale, p.heads, p.d, p.seqlen,
+                       p.cu, p.n_seqs, p.dout, p.dq, p.dk, p.dv, p.dg, p.dbeta, ws);
     return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_chunk_bwd(const ChunkBwdProblem &p) {
+    const int64_t total = p.cu ? (int64_t)p.seqlen : (int64_t)p.n_seqs * p.seqlen;
+    const size_t slots = bwd::n_slots(total, p.n_seqs, p.chunk);
+    const bwd::Ws ws = bwd::ws_layout(p.work, slots, p.heads, p.d, p.chunk);
+    switch (p.chunk) {
+    case 16: return launch_bwd_c<16>(p, ws, slots);
+    case 32: return launch_bwd_c<32>(p, ws, slots);
+    case 64: return launch_bwd_c<64>(p, ws, slots);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace kda
