@@ -14,15 +14,18 @@
 // and the decay-weighted products behind A and H hand their gradients to k, q
 // and the cumulative log-decay G, whose reverse cumulative sum is dg.
 //
-// Two kernels.  Only S and dS are carried from chunk to chunk, and each of
-// their value columns evolves on its own (Z and dZ are column-wise too), so
-// the chain kernel runs one workgroup per (sequence, head, 16 value columns):
-// a forward sweep stores each chunk's start state and Z, a reverse sweep
-// stores each chunk's end-state gradient dS' and dZ and leaves dS_0.  Every
-// other gradient is a function of one chunk's inputs and those four stored
-// quantities, so the gradient kernel runs one workgroup per (chunk, head),
-// all in parallel.  fp32 on the vector ALUs, decay factors as e^{G_i - G_j}
-// with exponents <= 0, so any finite log-decay is in range.
+// Three kernels.  Every per-chunk factor that does not depend on the value
+// columns (K~, T, H, R, Kbar, Qbar, e^{G_C}) comes from a prep kernel, one
+// workgroup per (chunk, head), into the workspace.  Only S and dS are carried
+// from chunk to chunk, and each of their value columns evolves on its own (Z
+// and dZ are column-wise too), so the chain kernel runs one workgroup per
+// (sequence, head, 16 value columns) and streams those factors: a forward
+// sweep stores each chunk's start state and Z, a reverse sweep stores each
+// chunk's end-state gradient dS' and dZ and leaves dS_0.  Every other
+// gradient is a function of one chunk's inputs and the stored quantities, so
+// the gradient kernel runs one workgroup per (chunk, head), all in parallel.
+// fp32 on the vector ALUs, decay factors as e^{G_i - G_j} with exponents <= 0
+// (and e^{G_i}, e^{G_C - G_i} <= 1), so any finite log-decay is in range.
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
@@ -33,17 +36,33 @@ constexpr int THREADS = 256;
 constexpr int TV = 16;   // value columns per chain workgroup
 
 // ---- workspace ------------------------------------------------------------------
-// Per (chunk slot, head): S at the chunk start [d][d], dS' at the chunk end
-// [d][d], Z [C][d] and dZ [C][d], fp32, row-major; four regions one after another.
+// Per (chunk slot, head), fp32, row-major, one region per quantity:
+//   S at the chunk start and dS' at the chunk end [d][d]; Z, dZ, R, Kbar,
+//   Qbar [C][d]; T, K~, H [C][C]; e^{G_C} [d].
 __host__ __device__ inline size_t n_slots(int64_t total_tokens, int n_seqs, int chunk) {
     return (size_t)(total_tokens / chunk + n_seqs + 1);
 }
+__host__ __device__ inline size_t ws_floats_per_slot(int d, int C) {
+    return 2 * (size_t)d * d + 5 * (size_t)C * d + 3 * (size_t)C * C + d;
+}
 struct Ws {
-    float *S, *dS, *Z, *dZ;
+    float *S, *dS, *Z, *dZ, *R, *Kb, *Qb, *T, *Kt, *Hm, *gC;
 };
 __host__ __device__ inline Ws ws_layout(float *base, size_t slots, int heads, int d, int C) {
-    const size_t dd = (size_t)slots * heads * d * d, cd = (size_t)slots * heads * C * d;
-    return Ws{base, base + dd, base + 2 * dd, base + 2 * dd + cd};
+    const size_t n = slots * heads, dd = n * d * d, cd = n * C * d, cc = n * C * C;
+    Ws w;
+    w.S = base;
+    w.dS = w.S + dd;
+    w.Z = w.dS + dd;
+    w.dZ = w.Z + cd;
+    w.R = w.dZ + cd;
+    w.Kb = w.R + cd;
+    w.Qb = w.Kb + cd;
+    w.T = w.Qb + cd;
+    w.Kt = w.T + cc;
+    w.Hm = w.Kt + cc;
+    w.gC = w.Hm + cc;
+    return w;
 }
 
 // First chunk slot of sequence n: floor(start / C) + n.  Strictly increasing in
@@ -62,19 +81,63 @@ __device__ __forceinline__ void seq_range(const int32_t *cu, int row_len, int n,
     }
 }
 
+// The chunk held by slot `slot`: its sequence's bounds and the chunk's first
+// token and length.  False for a gap slot (uniform over a workgroup).
+template <int C>
+__device__ __forceinline__ bool slot_chunk(const int32_t *cu, int row_len, int n_seqs, int slot,
+                                           int &t0, int &len) {
+    // the sequence owning the slot: the last n with chunk_base(n) <= slot
+    int lo = 0, hi = n_seqs - 1, ts, te;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        seq_range(cu, row_len, mid, ts, te);
+        if (chunk_base(ts, mid, C) <= slot) lo = mid;
+        else hi = mid - 1;
+    }
+    seq_range(cu, row_len, lo, ts, te);
+    const int c = slot - chunk_base(ts, lo, C);
+    if (c >= (te - ts + C - 1) / C) return false;
+    t0 = ts + c * C;
+    len = min(C, te - t0);
+    return true;
+}
+
 // ---- shared chunk steps (one workgroup, THREADS threads, operands in LDS) ----------
 // [C][d] operands sit in LDS with row stride d + 1, so that lanes walking the
 // rows of one column hit distinct banks.
 __host__ __device__ inline int row_stride(int d) { return d + 1; }
 
-// Loads rows t0 .. t0+len-1 of a [tokens, H, d] tensor into dst[C][dp] (zeros below).
-template <int C>
-__device__ __forceinline__ void load_rows(float *dst, const float *src, int t0, int len, int H,
-                                          int h, int d, int tid) {
+// A [rows][d] block (rows * d <= 2048) moves from global memory to LDS in two
+// steps: fetch_rows issues 16-byte loads into registers, commit_rows stores
+// them, so a chunk's loads can be in flight while the previous chunk computes.
+constexpr int MAXV4 = 2;
+struct Rows4 {
+    float4 x[MAXV4];
+};
+// Row i (< len) of the block starts at src + i * pitch; rows >= len read as 0.
+__device__ __forceinline__ void fetch_rows(Rows4 &r, const float *src, size_t pitch, int rows,
+                                           int len, int d, int tid) {
+#pragma unroll
+    for (int u = 0; u < MAXV4; ++u) {
+        const int e = 4 * (tid + u * THREADS), i = e / d;
+        float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (i < rows && i < len)
+            val = *reinterpret_cast<const float4 *>(src + (size_t)i * pitch + (e - i * d));
+        r.x[u] = val;
+    }
+}
+__device__ __forceinline__ void commit_rows(float *dst, const Rows4 &r, int rows, int d, int tid) {
     const int dp = row_stride(d);
-    for (int e = tid; e < C * d; e += THREADS) {
-        const int i = e / d, c = e - i * d;
-        dst[i * dp + c] = i < len ? src[((size_t)(t0 + i) * H + h) * d + c] : 0.f;
+#pragma unroll
+    for (int u = 0; u < MAXV4; ++u) {
+        const int e = 4 * (tid + u * THREADS), i = e / d;
+        if (i < rows) {
+            float *p = dst + i * dp + (e - i * d);
+            p[0] = r.x[u].x;
+            p[1] = r.x[u].y;
+            p[2] = r.x[u].z;
+            p[3] = r.x[u].w;
+        }
     }
 }
 // In place: G[i][c] <- sum_{r <= i} g[r][c] (padding rows add zero).
@@ -102,12 +165,14 @@ __device__ __forceinline__ void pair_products(float *Kt, float *Hm, const float 
         float a = 0.f, hh = 0.f;
         if (j <= i) {
             if (Hm) {
+#pragma unroll 8
                 for (int c = 0; c < d; ++c) {
                     const float E = fast_exp(G[i * dp + c] - G[j * dp + c]) * k[j * dp + c];
                     a += k[i * dp + c] * E;
                     hh += q[i * dp + c] * E;
                 }
             } else if (j < i) {
+#pragma unroll 8
                 for (int c = 0; c < d; ++c)
                     a += k[i * dp + c] * fast_exp(G[i * dp + c] - G[j * dp + c]) * k[j * dp + c];
             }
@@ -136,90 +201,170 @@ __device__ __forceinline__ void solve_T(float *T, const float *Kt, const float *
     }
 }
 
+// ---- prep kernel ----------------------------------------------------------------
+struct PrepLds {
+    int k, G, q, L, beta, Kt, T, Hm, total;
+};
+__host__ __device__ inline PrepLds prep_layout(int d, int C) {
+    PrepLds L;
+    int o = 0;
+    const int cd = C * row_stride(d), cc = C * C;
+    L.k = o; o += cd;
+    L.G = o; o += cd;
+    L.q = o; o += cd;
+    L.L = o; o += cd;
+    L.beta = o; o += C;
+    L.Kt = o; o += cc;
+    L.T = o; o += cc;
+    L.Hm = o; o += cc;
+    L.total = o;
+    return L;
+}
+
+// One chunk of one head: K~, T, H, R = T Diag(beta) L, Kbar, Qbar and e^{G_C}
+// into the workspace (padding rows come out zero, T's padding block identity).
+template <int C, int D>
+__global__ __launch_bounds__(THREADS) void kda_bwd_prep_kernel(
+    const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ g,
+    const float *__restrict__ beta, float scale, int H, int row_len,
+    const int32_t *__restrict__ cu, int n_seqs, Ws ws) {
+    constexpr int d = D;
+    extern __shared__ float sm[];
+    const PrepLds L = prep_layout(d, C);
+    float *sk = sm + L.k, *sG = sm + L.G, *sq = sm + L.q, *sL = sm + L.L, *sb = sm + L.beta;
+    float *sKt = sm + L.Kt, *sT = sm + L.T, *sHm = sm + L.Hm;
+    const int slot = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H, tid = threadIdx.x;
+    int t0, len;
+    if (!slot_chunk<C>(cu, row_len, n_seqs, slot, t0, len)) return;
+    const int dp = row_stride(d), cd = C * d, cc = C * C;
+    const size_t wslot = (size_t)slot * H + h;
+    {
+        const size_t off = ((size_t)t0 * H + h) * d, pitch = (size_t)H * d;
+        Rows4 rk, rg, rq;
+        fetch_rows(rk, k + off, pitch, C, len, d, tid);
+        fetch_rows(rg, g + off, pitch, C, len, d, tid);
+        fetch_rows(rq, q + off, pitch, C, len, d, tid);
+        const float rb = tid < len ? beta[(size_t)(t0 + tid) * H + h] : 0.f;
+        commit_rows(sk, rk, C, d, tid);
+        commit_rows(sG, rg, C, d, tid);
+        commit_rows(sq, rq, C, d, tid);
+        if (tid < C) sb[tid] = rb;
+    }
+    __syncthreads();
+    cumsum_rows<C>(sG, d, tid);
+    __syncthreads();
+    for (int e = tid; e < cd; e += THREADS) {
+        const int i = e / d, c2 = e - i * d, a = i * dp + c2;
+        const float kk = sk[a], G = sG[a];
+        const float eG = fast_exp(G);
+        sL[a] = kk * eG;
+        ws.Kb[wslot * cd + e] = kk * fast_exp(sG[(C - 1) * dp + c2] - G);
+        ws.Qb[wslot * cd + e] = scale * sq[a] * eG;
+    }
+    for (int c2 = tid; c2 < d; c2 += THREADS) ws.gC[wslot * d + c2] = fast_exp(sG[(C - 1) * dp + c2]);
+    pair_products<C>(sKt, sHm, sk, sq, sG, scale, d, tid);
+    __syncthreads();
+    solve_T<C>(sT, sKt, sb, tid);
+    __syncthreads();
+    for (int e = tid; e < cd; e += THREADS) {
+        const int i = e / d, c2 = e - i * d;
+        float r = 0.f;
+        for (int j = 0; j <= i; ++j) r += sT[i * C + j] * sb[j] * sL[j * dp + c2];
+        ws.R[wslot * cd + e] = r;
+    }
+    for (int e = tid; e < cc; e += THREADS) {
+        ws.T[wslot * cc + e] = sT[e];
+        ws.Kt[wslot * cc + e] = sKt[e];
+        ws.Hm[wslot * cc + e] = sHm[e];
+    }
+}
+
 // ---- chain kernel ---------------------------------------------------------------
 struct ChainLds {
-    int k, G, q, LQ, Kb, R, beta, Kt, T, Hm, vt, zt, A, B, total;
+    int R, Kb, Qb, T, Hm, beta, gC, vt, zt, A, total;
 };
 __host__ __device__ inline ChainLds chain_layout(int d, int C) {
     ChainLds L;
     int o = 0;
     const int cd = C * row_stride(d), cc = C * C, ct = C * TV, dt = d * TV;
-    L.k = o; o += cd;
-    L.G = o; o += cd;
-    L.q = o; o += cd;
-    L.LQ = o; o += cd;   // L = k e^{G} for R, then Qbar = s q e^{G}
-    L.Kb = o; o += cd;   // Kbar = k e^{G_C - G}
     L.R = o; o += cd;
-    L.beta = o; o += C;
-    L.Kt = o; o += cc;
+    L.Kb = o; o += cd;
+    L.Qb = o; o += cd;
     L.T = o; o += cc;
     L.Hm = o; o += cc;
+    L.beta = o; o += C;
+    L.gC = o; o += d;
     L.vt = o; o += ct;   // v tile (forward sweep) or dO tile (reverse sweep)
     L.zt = o; o += ct;   // Z tile or dZ tile
     L.A = o; o += dt;    // S tile or dS tile
-    L.B = o; o += dt;    // its update
     L.total = o;
     return L;
 }
 
-template <int C>
+template <int C, int D>
 __global__ __launch_bounds__(THREADS) void kda_bwd_chain_kernel(
-    const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
-    const float *__restrict__ g, const float *__restrict__ beta, float scale, int H, int d,
-    int row_len, const int32_t *__restrict__ cu, const float *__restrict__ s0,
-    const float *__restrict__ dfinal, const float *__restrict__ dout, float *__restrict__ ds0,
-    Ws ws) {
+    const float *__restrict__ v, const float *__restrict__ beta, int H, int row_len,
+    const int32_t *__restrict__ cu, const float *__restrict__ s0, const float *__restrict__ dfinal,
+    const float *__restrict__ dout, float *__restrict__ ds0, Ws ws) {
+    constexpr int d = D, CC = C * C / THREADS, RPT = D / 16;
     extern __shared__ float sm[];
     const ChainLds L = chain_layout(d, C);
-    float *sk = sm + L.k, *sG = sm + L.G, *sq = sm + L.q, *sLQ = sm + L.LQ, *sKb = sm + L.Kb;
-    float *sR = sm + L.R, *sb = sm + L.beta, *sKt = sm + L.Kt, *sT = sm + L.T, *sHm = sm + L.Hm;
-    float *svt = sm + L.vt, *szt = sm + L.zt, *sA = sm + L.A, *sB = sm + L.B;
+    float *sR = sm + L.R, *sKb = sm + L.Kb, *sQb = sm + L.Qb, *sT = sm + L.T, *sHm = sm + L.Hm;
+    float *sb = sm + L.beta, *sgC = sm + L.gC, *svt = sm + L.vt, *szt = sm + L.zt, *sA = sm + L.A;
 
     const int nt = d / TV;
     const int pid = blockIdx.x / nt, tile = blockIdx.x - pid * nt;
     const int n = pid / H, h = pid - n * H;
     const int v0 = tile * TV, tid = threadIdx.x;
-    const int dd = d * d, dt = d * TV, ct = C * TV, dp = row_stride(d);
+    const int dd = d * d, dt = d * TV, ct = C * TV, cd = C * d, dp = row_stride(d);
+    const int jc = tid % TV, rb0 = tid / TV;   // this thread's column and first row in S updates
     int ts, te;
     seq_range(cu, row_len, n, ts, te);
     const size_t pair = (size_t)n * H + h;
     const int nck = (te - ts + C - 1) / C;
     const int base = chunk_base(ts, n, C);
 
-    // Chunk c: k, G (cumulative), beta and a 16-column tile of v (forward) or of
-    // dO and all of q (reverse); then L, Kbar, K~ (and H), and T.
-    auto prepare_chunk = [&](int c, bool reverse) {
+    // One chunk's factors and a 16-column tile of v (forward) or dO (reverse),
+    // fetched into registers a chunk ahead of their use.
+    Rows4 rR, rKb, rQb;
+    float rT[CC], rH[CC], rv[C / 16], rb = 0.f, rg = 0.f;
+    auto fetch_chunk = [&](int c, bool reverse) {
         const int t0 = ts + c * C, len = min(C, te - t0);
-        load_rows<C>(sk, k, t0, len, H, h, d, tid);
-        load_rows<C>(sG, g, t0, len, H, h, d, tid);
-        if (reverse) load_rows<C>(sq, q, t0, len, H, h, d, tid);
+        const size_t w = (size_t)(base + c) * H + h;
+        fetch_rows(rR, ws.R + w * cd, d, C, C, d, tid);
+        fetch_rows(rKb, ws.Kb + w * cd, d, C, C, d, tid);
+        if (reverse) fetch_rows(rQb, ws.Qb + w * cd, d, C, C, d, tid);
+#pragma unroll
+        for (int u = 0; u < CC; ++u) {
+            rT[u] = ws.T[w * C * C + tid + u * THREADS];
+            if (reverse) rH[u] = ws.Hm[w * C * C + tid + u * THREADS];
+        }
+        const size_t off = ((size_t)t0 * H + h) * d, pitch = (size_t)H * d;
         const float *src = reverse ? dout : v;
-        for (int e = tid; e < ct; e += THREADS) {
-            const int i = e / TV;
-            svt[e] = i < len ? src[((size_t)(t0 + i) * H + h) * d + v0 + (e - i * TV)] : 0.f;
+#pragma unroll
+        for (int u = 0; u < C / 16; ++u) {
+            const int e = tid + u * THREADS, i = e / TV;
+            rv[u] = i < len ? src[off + (size_t)i * pitch + v0 + (e - i * TV)] : 0.f;
         }
-        for (int i = tid; i < C; i += THREADS) sb[i] = i < len ? beta[(size_t)(t0 + i) * H + h] : 0.f;
-        __syncthreads();
-        cumsum_rows<C>(sG, d, tid);
-        __syncthreads();
-        for (int e = tid; e < C * d; e += THREADS) {
-            const int i = e / d, c2 = e - i * d, a = i * dp + c2;
-            const float kk = sk[a], G = sG[a];
-            sLQ[a] = kk * fast_exp(G);
-            sKb[a] = kk * fast_exp(sG[(C - 1) * dp + c2] - G);
+        if (tid < C) rb = tid < len ? beta[(size_t)(t0 + tid) * H + h] : 0.f;
+        if (tid < d) rg = ws.gC[w * d + tid];
+    };
+    // The fetched chunk into LDS, then the next chunk's fetch is issued.
+    auto commit_chunk = [&](bool reverse, int next) {
+        commit_rows(sR, rR, C, d, tid);
+        commit_rows(sKb, rKb, C, d, tid);
+        if (reverse) commit_rows(sQb, rQb, C, d, tid);
+#pragma unroll
+        for (int u = 0; u < CC; ++u) {
+            sT[tid + u * THREADS] = rT[u];
+            if (reverse) sHm[tid + u * THREADS] = rH[u];
         }
-        pair_products<C>(sKt, reverse ? sHm : nullptr, sk, sq, sG, scale, d, tid);
+#pragma unroll
+        for (int u = 0; u < C / 16; ++u) svt[tid + u * THREADS] = rv[u];
+        if (tid < C) sb[tid] = rb;
+        if (tid < d) sgC[tid] = rg;
         __syncthreads();
-        solve_T<C>(sT, sKt, sb, tid);
-        __syncthreads();
-        // R = T Diag(beta) L
-        for (int e = tid; e < C * d; e += THREADS) {
-            const int i = e / d, c2 = e - i * d;
-            float r = 0.f;
-            for (int j = 0; j <= i; ++j) r += sT[i * C + j] * sb[j] * sLQ[j * dp + c2];
-            sR[i * dp + c2] = r;
-        }
-        __syncthreads();
+        if (next >= 0) fetch_chunk(next, reverse);
     };
 
     // ---- forward sweep: S at each chunk start, and Z --------------------------
@@ -227,6 +372,7 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_chain_kernel(
         const int r = e / TV;
         sA[e] = s0 ? s0[pair * dd + (size_t)r * d + v0 + (e - r * TV)] : 0.f;
     }
+    if (nck > 0) fetch_chunk(0, false);
     __syncthreads();
     for (int c = 0; c < nck; ++c) {
         const size_t slot = (size_t)(base + c) * H + h;
@@ -235,28 +381,34 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_chain_kernel(
             const int r = e / TV;
             Sd[(size_t)r * d + v0 + (e - r * TV)] = sA[e];
         }
-        prepare_chunk(c, false);
+        commit_chunk(false, c + 1 < nck ? c + 1 : -1);
         // Z = T Diag(beta) V - R S on this tile
-        float *Zd = ws.Z + slot * C * d;
+        float *Zd = ws.Z + slot * cd;
         for (int e = tid; e < ct; e += THREADS) {
             const int i = e / TV, j = e - i * TV;
             float z = 0.f;
             for (int m = 0; m <= i; ++m) z += sT[i * C + m] * sb[m] * svt[m * TV + j];
+#pragma unroll 8
             for (int r = 0; r < d; ++r) z -= sR[i * dp + r] * sA[r * TV + j];
             szt[e] = z;
             Zd[(size_t)i * d + v0 + j] = z;
         }
         __syncthreads();
-        // S <- Diag(e^{G_C}) S + Kbar^T Z
-        for (int e = tid; e < dt; e += THREADS) {
-            const int r = e / TV, j = e - r * TV;
-            float acc = fast_exp(sG[(C - 1) * dp + r]) * sA[e];
-#pragma unroll 4
-            for (int i = 0; i < C; ++i) acc += sKb[i * dp + r] * szt[i * TV + j];
-            sB[e] = acc;
+        // S <- Diag(e^{G_C}) S + Kbar^T Z, in place: each thread owns its entries
+        float acc[RPT];
+#pragma unroll
+        for (int u = 0; u < RPT; ++u) {
+            const int r = rb0 + 16 * u;
+            acc[u] = sgC[r] * sA[r * TV + jc];
         }
-        __syncthreads();
-        for (int e = tid; e < dt; e += THREADS) sA[e] = sB[e];
+#pragma unroll 4
+        for (int i = 0; i < C; ++i) {
+            const float z = szt[i * TV + jc];
+#pragma unroll
+            for (int u = 0; u < RPT; ++u) acc[u] += sKb[i * dp + rb0 + 16 * u] * z;
+        }
+#pragma unroll
+        for (int u = 0; u < RPT; ++u) sA[(rb0 + 16 * u) * TV + jc] = acc[u];
         __syncthreads();
     }
 
@@ -265,6 +417,7 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_chain_kernel(
         const int r = e / TV;
         sA[e] = dfinal ? dfinal[pair * dd + (size_t)r * d + v0 + (e - r * TV)] : 0.f;
     }
+    if (nck > 0) fetch_chunk(nck - 1, true);
     __syncthreads();
     for (int c = nck - 1; c >= 0; --c) {
         const size_t slot = (size_t)(base + c) * H + h;
@@ -273,33 +426,35 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_chain_kernel(
             const int r = e / TV;
             dSd[(size_t)r * d + v0 + (e - r * TV)] = sA[e];
         }
-        prepare_chunk(c, true);
-        // dZ = Kbar dS' + H^T dO on this tile; L's storage takes Qbar = s q e^{G}
-        float *dZd = ws.dZ + slot * C * d;
+        commit_chunk(true, c > 0 ? c - 1 : -1);
+        // dZ = Kbar dS' + H^T dO on this tile
+        float *dZd = ws.dZ + slot * cd;
         for (int e = tid; e < ct; e += THREADS) {
             const int i = e / TV, j = e - i * TV;
             float z = 0.f;
+#pragma unroll 8
             for (int r = 0; r < d; ++r) z += sKb[i * dp + r] * sA[r * TV + j];
             for (int i2 = i; i2 < C; ++i2) z += sHm[i2 * C + i] * svt[i2 * TV + j];
             szt[e] = z;
             dZd[(size_t)i * d + v0 + j] = z;
         }
-        for (int e = tid; e < C * d; e += THREADS) {
-            const int i = e / d, a = i * dp + (e - i * d);
-            sLQ[a] = scale * sq[a] * fast_exp(sG[a]);
-        }
         __syncthreads();
-        // dS = Diag(e^{G_C}) dS' + Qbar^T dO - R^T dZ
-        for (int e = tid; e < dt; e += THREADS) {
-            const int r = e / TV, j = e - r * TV;
-            float a = fast_exp(sG[(C - 1) * dp + r]) * sA[e];
+        // dS = Diag(e^{G_C}) dS' + Qbar^T dO - R^T dZ, in place
+        float acc[RPT];
+#pragma unroll
+        for (int u = 0; u < RPT; ++u) {
+            const int r = rb0 + 16 * u;
+            acc[u] = sgC[r] * sA[r * TV + jc];
+        }
 #pragma unroll 4
-            for (int i = 0; i < C; ++i)
-                a += sLQ[i * dp + r] * svt[i * TV + j] - sR[i * dp + r] * szt[i * TV + j];
-            sB[e] = a;
+        for (int i = 0; i < C; ++i) {
+            const float o = svt[i * TV + jc], z = szt[i * TV + jc];
+#pragma unroll
+            for (int u = 0; u < RPT; ++u)
+                acc[u] += sQb[i * dp + rb0 + 16 * u] * o - sR[i * dp + rb0 + 16 * u] * z;
         }
-        __syncthreads();
-        for (int e = tid; e < dt; e += THREADS) sA[e] = sB[e];
+#pragma unroll
+        for (int u = 0; u < RPT; ++u) sA[(rb0 + 16 * u) * TV + jc] = acc[u];
         __syncthreads();
     }
     if (ds0)
@@ -345,13 +500,14 @@ __host__ __device__ inline GradLds grad_layout(int d, int C) {
     return L;
 }
 
-template <int C>
+template <int C, int D>
 __global__ __launch_bounds__(THREADS) void kda_bwd_grad_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
-    const float *__restrict__ g, const float *__restrict__ beta, float scale, int H, int d,
+    const float *__restrict__ g, const float *__restrict__ beta, float scale, int H,
     int row_len, const int32_t *__restrict__ cu, int n_seqs, const float *__restrict__ dout,
     float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv,
     float *__restrict__ dg, float *__restrict__ dbeta, Ws ws) {
+    constexpr int d = D;
     extern __shared__ float sm[];
     const GradLds L = grad_layout(d, C);
     float *sq = sm + L.q, *sk = sm + L.k, *sG = sm + L.G, *sv = sm + L.v, *sdO = sm + L.dO;
@@ -363,53 +519,61 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_grad_kernel(
 
     const int slot = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
     const int tid = threadIdx.x;
-    // The sequence owning this slot: the last n with chunk_base(n) <= slot.
-    int lo = 0, hi = n_seqs - 1, ts, te;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        seq_range(cu, row_len, mid, ts, te);
-        if (chunk_base(ts, mid, C) <= slot) lo = mid;
-        else hi = mid - 1;
-    }
-    const int n = lo;
-    seq_range(cu, row_len, n, ts, te);
-    const int c = slot - chunk_base(ts, n, C);
-    if (c >= (te - ts + C - 1) / C) return;   // a gap slot: uniform over the workgroup
-    const int t0 = ts + c * C, len = min(C, te - t0);
+    int t0, len;
+    if (!slot_chunk<C>(cu, row_len, n_seqs, slot, t0, len)) return;
     const int cd = C * d, dd = d * d, SR = slice_rows(d), dp = row_stride(d);
     const size_t wslot = (size_t)slot * H + h;
 
-    load_rows<C>(sq, q, t0, len, H, h, d, tid);
-    load_rows<C>(sk, k, t0, len, H, h, d, tid);
-    load_rows<C>(sG, g, t0, len, H, h, d, tid);
-    load_rows<C>(sv, v, t0, len, H, h, d, tid);
-    load_rows<C>(sdO, dout, t0, len, H, h, d, tid);
-    for (int e = tid; e < cd; e += THREADS) {
-        const int i = e / d, a = i * dp + (e - i * d);
-        sZ[a] = ws.Z[wslot * cd + e];
-        sdZ[a] = ws.dZ[wslot * cd + e];
+    {
+        const size_t off = ((size_t)t0 * H + h) * d, pitch = (size_t)H * d;
+        Rows4 r[7];
+        fetch_rows(r[0], q + off, pitch, C, len, d, tid);
+        fetch_rows(r[1], k + off, pitch, C, len, d, tid);
+        fetch_rows(r[2], g + off, pitch, C, len, d, tid);
+        fetch_rows(r[3], v + off, pitch, C, len, d, tid);
+        fetch_rows(r[4], dout + off, pitch, C, len, d, tid);
+        fetch_rows(r[5], ws.Z + wslot * cd, d, C, C, d, tid);
+        fetch_rows(r[6], ws.dZ + wslot * cd, d, C, C, d, tid);
+        const float rb = tid < len ? beta[(size_t)(t0 + tid) * H + h] : 0.f;
+        constexpr int CC = C * C / THREADS;
+        float rT[CC], rK[CC];
+#pragma unroll
+        for (int u = 0; u < CC; ++u) {
+            rT[u] = ws.T[wslot * C * C + tid + u * THREADS];
+            rK[u] = ws.Kt[wslot * C * C + tid + u * THREADS];
+        }
+        float *dst[7] = {sq, sk, sG, sv, sdO, sZ, sdZ};
+#pragma unroll
+        for (int a = 0; a < 7; ++a) commit_rows(dst[a], r[a], C, d, tid);
+        if (tid < C) sb[tid] = rb;
+#pragma unroll
+        for (int u = 0; u < CC; ++u) {
+            sT[tid + u * THREADS] = rT[u];
+            sKt[tid + u * THREADS] = rK[u];
+        }
     }
-    for (int i = tid; i < C; i += THREADS) sb[i] = i < len ? beta[(size_t)(t0 + i) * H + h] : 0.f;
     __syncthreads();
     cumsum_rows<C>(sG, d, tid);
     __syncthreads();
-    pair_products<C>(sKt, nullptr, sk, sq, sG, scale, d, tid);
-    __syncthreads();
-    solve_T<C>(sT, sKt, sb, tid);
 
     // The products with S and dS', SR channel rows at a time:
     //   dR = -dZ S^T,  dQbar = dO S^T,  dKbar = Z dS'^T,  gc = e^{G_C} rowsum(dS' . S).
     const float *Sg = ws.S + wslot * dd, *dSg = ws.dS + wslot * dd;
+    Rows4 rS, rdS;
+    fetch_rows(rS, Sg, d, SR, SR, d, tid);
+    fetch_rows(rdS, dSg, d, SR, SR, d, tid);
     for (int r0 = 0; r0 < d; r0 += SR) {
-        for (int e = tid; e < SR * d; e += THREADS) {
-            const int rr = e / d, a = rr * dp + (e - rr * d);
-            sS[a] = Sg[(size_t)r0 * d + e];
-            sdS[a] = dSg[(size_t)r0 * d + e];
-        }
+        commit_rows(sS, rS, SR, d, tid);
+        commit_rows(sdS, rdS, SR, d, tid);
         __syncthreads();
+        if (r0 + SR < d) {
+            fetch_rows(rS, Sg + (size_t)(r0 + SR) * d, d, SR, SR, d, tid);
+            fetch_rows(rdS, dSg + (size_t)(r0 + SR) * d, d, SR, SR, d, tid);
+        }
         for (int e = tid; e < C * SR; e += THREADS) {
             const int x = e / SR, rr = e - x * SR;
             float a = 0.f, b = 0.f, z = 0.f;
+#pragma unroll 8
             for (int u = 0; u < d; ++u) {
                 const float s = sS[rr * dp + u];
                 a += sdZ[x * dp + u] * s;
@@ -542,35 +706,47 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_grad_kernel(
 bool bwd_supported(int dk, int dv, int chunk) {
     if (dk != dv || !(dk == 16 || dk == 32 || dk == 64 || dk == 128)) return false;
     if (!(chunk == 16 || chunk == 32 || chunk == 64)) return false;
+    if (chunk * dk > 4 * bwd::MAXV4 * bwd::THREADS) return false;   // one fetch per thread
     const size_t cap = 163840 / sizeof(float);
-    return (size_t)bwd::chain_layout(dk, chunk).total <= cap &&
+    return (size_t)bwd::prep_layout(dk, chunk).total <= cap &&
+           (size_t)bwd::chain_layout(dk, chunk).total <= cap &&
            (size_t)bwd::grad_layout(dk, chunk).total <= cap;
 }
 
 size_t bwd_workspace_bytes(int64_t total_tokens, int n_seqs, int heads, int d, int chunk) {
     const size_t slots = bwd::n_slots(total_tokens, n_seqs, chunk);
-    return slots * heads * (2 * (size_t)d * d + 2 * (size_t)chunk * d) * sizeof(float);
+    return slots * heads * bwd::ws_floats_per_slot(d, chunk) * sizeof(float);
 }
 
 namespace {
-template <int C> hipError_t launch_bwd_c(const ChunkBwdProblem &p, const bwd::Ws &ws, size_t slots) {
+template <int C, int D>
+hipError_t launch_bwd_cd(const ChunkBwdProblem &p, const bwd::Ws &ws, size_t slots) {
     using namespace bwd;
-    const size_t lc = (size_t)chain_layout(p.d, C).total * sizeof(float);
-    const size_t lg = (size_t)grad_layout(p.d, C).total * sizeof(float);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kda_bwd_chain_kernel<C>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lc);
+    const size_t lp = (size_t)prep_layout(D, C).total * sizeof(float);
+    const size_t lc = (size_t)chain_layout(D, C).total * sizeof(float);
+    const size_t lg = (size_t)grad_layout(D, C).total * sizeof(float);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kda_bwd_prep_kernel<C, D>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lp);
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kda_bwd_grad_kernel<C>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kda_bwd_chain_kernel<C, D>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lc);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kda_bwd_grad_kernel<C, D>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lg);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kda_bwd_chain_kernel<C>, dim3(p.n_seqs * p.heads * (p.d / TV)),
-                       dim3(THREADS), lc, p.stream, p.q, p.k, p.v, p.g, p.beta, p.scale, p.heads,
-                       p.d, p.seqlen, p.cu, p.s0, p.dfinal, p.dout, p.ds0, ws);
+    const dim3 per_chunk((unsigned)(slots * p.heads));
+    hipLaunchKernelGGL((kda_bwd_prep_kernel<C, D>), per_chunk, dim3(THREADS), lp, p.stream, p.q,
+                       p.k, p.g, p.beta, p.scale, p.heads, p.seqlen, p.cu, p.n_seqs, ws);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kda_bwd_grad_kernel<C>, dim3((unsigned)(slots * p.heads)), dim3(THREADS),
-                       lg, p.stream, p.q, p.k, p.v, p.g, p.beta, p.scale, p.heads, p.d, p.seqlen,
-                       p.cu, p.n_seqs, p.dout, p.dq, p.dk, p.dv, p.dg, p.dbeta, ws);
+    hipLaunchKernelGGL((kda_bwd_chain_kernel<C, D>), dim3(p.n_seqs * p.heads * (D / TV)),
+                       dim3(THREADS), lc, p.stream, p.v, p.beta, p.heads, p.seqlen, p.cu, p.s0,
+                       p.dfinal, p.dout, p.ds0, ws);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((kda_bwd_grad_kernel<C, D>), per_chunk, dim3(THREADS), lg, p.stream, p.q,
+                       p.k, p.v, p.g, p.beta, p.scale, p.heads, p.seqlen, p.cu, p.n_seqs, p.dout,
+                       p.dq, p.dk, p.dv, p.dg, p.dbeta, ws);
     return hipGetLastError();
 }
 }  // namespace
@@ -579,10 +755,16 @@ hipError_t launch_chunk_bwd(const ChunkBwdProblem &p) {
     const int64_t total = p.cu ? (int64_t)p.seqlen : (int64_t)p.n_seqs * p.seqlen;
     const size_t slots = bwd::n_slots(total, p.n_seqs, p.chunk);
     const bwd::Ws ws = bwd::ws_layout(p.work, slots, p.heads, p.d, p.chunk);
-    switch (p.chunk) {
-    case 16: return launch_bwd_c<16>(p, ws, slots);
-    case 32: return launch_bwd_c<32>(p, ws, slots);
-    case 64: return launch_bwd_c<64>(p, ws, slots);
+    // The (d, chunk) pairs bwd_supported accepts.
+    switch (p.d * 1000 + p.chunk) {
+    case 16016: return launch_bwd_cd<16, 16>(p, ws, slots);
+    case 16032: return launch_bwd_cd<32, 16>(p, ws, slots);
+    case 16064: return launch_bwd_cd<64, 16>(p, ws, slots);
+    case 32016: return launch_bwd_cd<16, 32>(p, ws, slots);
+    case 32032: return launch_bwd_cd<32, 32>(p, ws, slots);
+    case 64016: return launch_bwd_cd<16, 64>(p, ws, slots);
+    case 64032: return launch_bwd_cd<32, 64>(p, ws, slots);
+    case 128016: return launch_bwd_cd<16, 128>(p, ws, slots);
     default: return hipErrorInvalidValue;
     }
 }

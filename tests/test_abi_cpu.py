@@ -205,10 +205,11 @@ def test_backward_rejects_unsupported_problems():
 def test_backward_workspace_query():
     sh = shape(d_k=16, d_v=16, chunk_size=16, dtype_code=K.KDA_F32, seqlen=100, heads=3)
     # (T / C + N + 1) chunk slots per head, each with the chunk-start state and
-    # the end-state gradient (d x d) and Z, dZ (C x d), fp32
+    # the end-state gradient (d x d), Z, dZ, R, Kbar, Qbar (C x d), T, K~, H
+    # (C x C) and e^{G_C} (d), fp32
+    per_slot = lambda d, C: 2 * d * d + 5 * C * d + 3 * C * C + d  # noqa: E731
     slots = 100 // 16 + 1 + 1
-    assert K.lib().kda_chunk_bwd_workspace_bytes(ctypes.byref(sh)) == \
-        slots * 3 * (2 * 16 * 16 + 2 * 16 * 16) * 4
+    assert K.lib().kda_chunk_bwd_workspace_bytes(ctypes.byref(sh)) == slots * 3 * per_slot(16, 16) * 4
     sh = shape(d_k=128, d_v=128, chunk_size=16, dtype_code=K.KDA_F32, seqlen=4096, heads=2)
     assert K.lib().kda_chunk_bwd_workspace_bytes(ctypes.byref(sh)) == \
-        (4096 // 16 + 2) * 2 * (2 * 128 * 128 + 2 * 16 * 128) * 4
+        (4096 // 16 + 2) * 2 * per_slot(128, 16) * 4
