@@ -6,8 +6,8 @@ workload (B=1, H=32, T=131072, d_k=d_v=128, C=64, bf16 storage) with every
 input already resident in HBM.  The same run also times the batched decode
 step (``kda_decode_step``: 128 sessions x 32 heads, 268 MB fp32 state updated
 in place), the same prefill through the scalar-gate entry point, the packed
-varlen workload (8 sequences through cu_seqlens), the backward of the fp32
-small-width path, and the fp64 CPU oracle on a bounded sample of the prefill
+varlen workload (8 sequences through cu_seqlens), the backward (fp32
+storage, d = 128), and the fp64 CPU oracle on a bounded sample of the prefill
 workload.
 
 Prints ONE JSON line.  ``value`` is prefill tokens/s; the ``decode`` object
@@ -372,11 +372,11 @@ def main():
         del d4, inp4, ws4, o4, fs4
 
     if not args.skip_backward:
-        # Gradients through kda_chunk_bwd: the fp32 small-width path (d = 64,
-        # C = 32), one sequence of 4096 tokens per head, 16 heads.
-        print("[bench] backward (fp32, d=64, C=32, B=1 H=16 T=4096)", file=sys.stderr, flush=True)
+        # Gradients through kda_chunk_bwd at the layer's width (fp32 storage,
+        # d = 128, C = 16), one sequence of 8192 tokens per head, 32 heads.
+        print("[bench] backward (fp32, d=128, C=16, B=1 H=32 T=8192)", file=sys.stderr, flush=True)
         gen = torch.Generator(device=dev).manual_seed(7)
-        Tb, Hb, db = 4096, 16, 64
+        Tb, Hb, db, Cb = 8192, 32, 128, 16
         rnd = lambda *sh: torch.randn(*sh, generator=gen, device=dev)  # noqa: E731
         qb = torch.nn.functional.normalize(rnd(1, Tb, Hb, db), dim=-1).contiguous()
         kb = torch.nn.functional.normalize(rnd(1, Tb, Hb, db), dim=-1).contiguous()
@@ -385,11 +385,11 @@ def main():
         bb = torch.sigmoid(rnd(1, Tb, Hb)).contiguous()
         s0b, dfb = 0.1 * rnd(1, Hb, db, db), rnd(1, Hb, db, db)
         wsb = torch.empty(K.lib().kda_chunk_bwd_workspace_bytes(ctypes_byref_shape(
-            K, 1, Tb, Hb, db, 32, 1)), dtype=torch.uint8, device=dev)
+            K, 1, Tb, Hb, db, Cb, 1)), dtype=torch.uint8, device=dev)
 
         def bstep():
             return K.chunk_bwd(qb, kb, vb, gb, bb, dob, initial_state=s0b, d_final_state=dfb,
-                               chunk_size=32, workspace=wsb)
+                               chunk_size=Cb, workspace=wsb)
 
         for _ in range(2):
             bstep()
@@ -409,10 +409,10 @@ def main():
         result["backward"] = {
             "value": round(Tb / (bms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(bms, 4),
             "steps": n_b,
-            "config": {"workload": "gradients of the chunked prefill, B=1 H=16 T=4096 d=64 C=32 "
+            "config": {"workload": "gradients of the chunked prefill, B=1 H=32 T=8192 d=128 C=16 "
                                    "fp32, log-decays U(-0.05, 0), through kda_chunk_bwd"},
-            "roofline": {"bound": "alu", "kernel": "kda_chunk_bwd_f32_kernel (fp32 VALU, "
-                         "operands in LDS; a correctness-first path)",
+            "roofline": {"bound": "alu", "kernel": "kda_bwd_prep_kernel, kda_bwd_chain_kernel, "
+                         "kda_bwd_grad_kernel (fp32 VALU, operands in LDS)",
                          "achieved_hbm_gbs": round(bgbs, 2), "hbm_frac": round(bgbs / HBM_PEAK_GBS, 5),
                          "alg_bytes_per_launch": bbytes},
             "outputs_finite": bool(all(torch.isfinite(t).all().item() for t in grads.values()))}
