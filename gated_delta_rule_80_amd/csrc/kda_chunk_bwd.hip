@@ -32,8 +32,10 @@
 namespace kda {
 namespace bwd {
 
-constexpr int THREADS = 256;
-constexpr int TV = 16;   // value columns per chain workgroup
+constexpr int THREADS = 256;   // prep kernel
+constexpr int CT = 512;        // chain kernel: two waves per SIMD
+constexpr int GT = 512;        // gradient kernel
+constexpr int TV = 16;         // value columns per chain workgroup
 
 // ---- workspace ------------------------------------------------------------------
 // Per (chunk slot, head), fp32, row-major, one region per quantity:
@@ -110,27 +112,31 @@ __host__ __device__ inline int row_stride(int d) { return d + 1; }
 // A [rows][d] block (rows * d <= 2048) moves from global memory to LDS in two
 // steps: fetch_rows issues 16-byte loads into registers, commit_rows stores
 // them, so a chunk's loads can be in flight while the previous chunk computes.
-constexpr int MAXV4 = 2;
-struct Rows4 {
-    float4 x[MAXV4];
+constexpr int MAX_BLOCK = 2048;   // floats in one fetched [rows][d] block
+template <int NT> struct Rows {
+    static constexpr int NV = (MAX_BLOCK / 4 + NT - 1) / NT;   // float4 per thread
+    float4 x[NV];
 };
 // Row i (< len) of the block starts at src + i * pitch; rows >= len read as 0.
-__device__ __forceinline__ void fetch_rows(Rows4 &r, const float *src, size_t pitch, int rows,
+template <int NT>
+__device__ __forceinline__ void fetch_rows(Rows<NT> &r, const float *src, size_t pitch, int rows,
                                            int len, int d, int tid) {
 #pragma unroll
-    for (int u = 0; u < MAXV4; ++u) {
-        const int e = 4 * (tid + u * THREADS), i = e / d;
+    for (int u = 0; u < Rows<NT>::NV; ++u) {
+        const int e = 4 * (tid + u * NT), i = e / d;
         float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
         if (i < rows && i < len)
             val = *reinterpret_cast<const float4 *>(src + (size_t)i * pitch + (e - i * d));
         r.x[u] = val;
     }
 }
-__device__ __forceinline__ void commit_rows(float *dst, const Rows4 &r, int rows, int d, int tid) {
+template <int NT>
+__device__ __forceinline__ void commit_rows(float *dst, const Rows<NT> &r, int rows, int d,
+                                            int tid) {
     const int dp = row_stride(d);
 #pragma unroll
-    for (int u = 0; u < MAXV4; ++u) {
-        const int e = 4 * (tid + u * THREADS), i = e / d;
+    for (int u = 0; u < Rows<NT>::NV; ++u) {
+        const int e = 4 * (tid + u * NT), i = e / d;
         if (i < rows) {
             float *p = dst + i * dp + (e - i * d);
             p[0] = r.x[u].x;
@@ -141,9 +147,9 @@ __device__ __forceinline__ void commit_rows(float *dst, const Rows4 &r, int rows
     }
 }
 // In place: G[i][c] <- sum_{r <= i} g[r][c] (padding rows add zero).
-template <int C> __device__ __forceinline__ void cumsum_rows(float *G, int d, int tid) {
+template <int C, int NT> __device__ __forceinline__ void cumsum_rows(float *G, int d, int tid) {
     const int dp = row_stride(d);
-    for (int c = tid; c < d; c += THREADS) {
+    for (int c = tid; c < d; c += NT) {
         float run = 0.f;
 #pragma unroll 4
         for (int i = 0; i < C; ++i) {
@@ -240,7 +246,7 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_prep_kernel(
     const size_t wslot = (size_t)slot * H + h;
     {
         const size_t off = ((size_t)t0 * H + h) * d, pitch = (size_t)H * d;
-        Rows4 rk, rg, rq;
+        Rows<THREADS> rk, rg, rq;
         fetch_rows(rk, k + off, pitch, C, len, d, tid);
         fetch_rows(rg, g + off, pitch, C, len, d, tid);
         fetch_rows(rq, q + off, pitch, C, len, d, tid);
@@ -251,7 +257,7 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_prep_kernel(
         if (tid < C) sb[tid] = rb;
     }
     __syncthreads();
-    cumsum_rows<C>(sG, d, tid);
+    cumsum_rows<C, THREADS>(sG, d, tid);
     __syncthreads();
     for (int e = tid; e < cd; e += THREADS) {
         const int i = e / d, c2 = e - i * d, a = i * dp + c2;
@@ -302,11 +308,16 @@ __host__ __device__ inline ChainLds chain_layout(int d, int C) {
 }
 
 template <int C, int D>
-__global__ __launch_bounds__(THREADS) void kda_bwd_chain_kernel(
+__global__ __launch_bounds__(CT) void kda_bwd_chain_kernel(
     const float *__restrict__ v, const float *__restrict__ beta, int H, int row_len,
     const int32_t *__restrict__ cu, const float *__restrict__ s0, const float *__restrict__ dfinal,
     const float *__restrict__ dout, float *__restrict__ ds0, Ws ws) {
-    constexpr int d = D, CC = C * C / THREADS, RPT = D / 16;
+    constexpr int d = D;
+    constexpr int NCC = (C * C + CT - 1) / CT;       // T / H entries per thread
+    constexpr int NVT = (C * TV + CT - 1) / CT;      // v or dO tile entries per thread
+    constexpr int RS = CT / TV, RPT = (D + RS - 1) / RS;   // state rows: stride, per thread
+    constexpr int ZS = (C * TV < CT) ? CT / (C * TV) : 1;  // lanes sharing one Z / dZ entry
+    static_assert(ZS == 1 || ZS == 2, "Z entries are split over at most a lane pair");
     extern __shared__ float sm[];
     const ChainLds L = chain_layout(d, C);
     float *sR = sm + L.R, *sKb = sm + L.Kb, *sQb = sm + L.Qb, *sT = sm + L.T, *sHm = sm + L.Hm;
@@ -326,8 +337,8 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_chain_kernel(
 
     // One chunk's factors and a 16-column tile of v (forward) or dO (reverse),
     // fetched into registers a chunk ahead of their use.
-    Rows4 rR, rKb, rQb;
-    float rT[CC], rH[CC], rv[C / 16], rb = 0.f, rg = 0.f;
+    Rows<CT> rR, rKb, rQb;
+    float rT[NCC], rH[NCC], rv[NVT], rb = 0.f, rg = 0.f;
     auto fetch_chunk = [&](int c, bool reverse) {
         const int t0 = ts + c * C, len = min(C, te - t0);
         const size_t w = (size_t)(base + c) * H + h;
@@ -335,16 +346,19 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_chain_kernel(
         fetch_rows(rKb, ws.Kb + w * cd, d, C, C, d, tid);
         if (reverse) fetch_rows(rQb, ws.Qb + w * cd, d, C, C, d, tid);
 #pragma unroll
-        for (int u = 0; u < CC; ++u) {
-            rT[u] = ws.T[w * C * C + tid + u * THREADS];
-            if (reverse) rH[u] = ws.Hm[w * C * C + tid + u * THREADS];
+        for (int u = 0; u < NCC; ++u) {
+            const int e = tid + u * CT;
+            if (e < C * C) {
+                rT[u] = ws.T[w * C * C + e];
+                if (reverse) rH[u] = ws.Hm[w * C * C + e];
+            }
         }
         const size_t off = ((size_t)t0 * H + h) * d, pitch = (size_t)H * d;
         const float *src = reverse ? dout : v;
 #pragma unroll
-        for (int u = 0; u < C / 16; ++u) {
-            const int e = tid + u * THREADS, i = e / TV;
-            rv[u] = i < len ? src[off + (size_t)i * pitch + v0 + (e - i * TV)] : 0.f;
+        for (int u = 0; u < NVT; ++u) {
+            const int e = tid + u * CT, i = e / TV;
+            rv[u] = (i < C && i < len) ? src[off + (size_t)i * pitch + v0 + (e - i * TV)] : 0.f;
         }
         if (tid < C) rb = tid < len ? beta[(size_t)(t0 + tid) * H + h] : 0.f;
         if (tid < d) rg = ws.gC[w * d + tid];
@@ -355,12 +369,16 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_chain_kernel(
         commit_rows(sKb, rKb, C, d, tid);
         if (reverse) commit_rows(sQb, rQb, C, d, tid);
 #pragma unroll
-        for (int u = 0; u < CC; ++u) {
-            sT[tid + u * THREADS] = rT[u];
-            if (reverse) sHm[tid + u * THREADS] = rH[u];
+        for (int u = 0; u < NCC; ++u) {
+            const int e = tid + u * CT;
+            if (e < C * C) {
+                sT[e] = rT[u];
+                if (reverse) sHm[e] = rH[u];
+            }
         }
 #pragma unroll
-        for (int u = 0; u < C / 16; ++u) svt[tid + u * THREADS] = rv[u];
+        for (int u = 0; u < NVT; ++u)
+            if (tid + u * CT < C * TV) svt[tid + u * CT] = rv[u];
         if (tid < C) sb[tid] = rb;
         if (tid < d) sgC[tid] = rg;
         __syncthreads();
@@ -368,7 +386,7 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_chain_kernel(
     };
 
     // ---- forward sweep: S at each chunk start, and Z --------------------------
-    for (int e = tid; e < dt; e += THREADS) {
+    for (int e = tid; e < dt; e += CT) {
         const int r = e / TV;
         sA[e] = s0 ? s0[pair * dd + (size_t)r * d + v0 + (e - r * TV)] : 0.f;
     }
@@ -377,43 +395,51 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_chain_kernel(
     for (int c = 0; c < nck; ++c) {
         const size_t slot = (size_t)(base + c) * H + h;
         float *Sd = ws.S + slot * dd;
-        for (int e = tid; e < dt; e += THREADS) {
+        for (int e = tid; e < dt; e += CT) {
             const int r = e / TV;
             Sd[(size_t)r * d + v0 + (e - r * TV)] = sA[e];
         }
         commit_chunk(false, c + 1 < nck ? c + 1 : -1);
         // Z = T Diag(beta) V - R S on this tile
         float *Zd = ws.Z + slot * cd;
-        for (int e = tid; e < ct; e += THREADS) {
-            const int i = e / TV, j = e - i * TV;
+        for (int e = tid / ZS; e < ct; e += CT / ZS) {
+            const int i = e / TV, j = e - i * TV, part = tid % ZS;
             float z = 0.f;
-            for (int m = 0; m <= i; ++m) z += sT[i * C + m] * sb[m] * svt[m * TV + j];
+            if (part == 0)
+                for (int m = 0; m <= i; ++m) z += sT[i * C + m] * sb[m] * svt[m * TV + j];
 #pragma unroll 8
-            for (int r = 0; r < d; ++r) z -= sR[i * dp + r] * sA[r * TV + j];
-            szt[e] = z;
-            Zd[(size_t)i * d + v0 + j] = z;
+            for (int r = part * (d / ZS); r < (part + 1) * (d / ZS); ++r)
+                z -= sR[i * dp + r] * sA[r * TV + j];
+            if (ZS == 2) z += __shfl_xor(z, 1);
+            if (part == 0) {
+                szt[e] = z;
+                Zd[(size_t)i * d + v0 + j] = z;
+            }
         }
         __syncthreads();
         // S <- Diag(e^{G_C}) S + Kbar^T Z, in place: each thread owns its entries
-        float acc[RPT];
+        if (rb0 < d) {   // rows rb0 + RS u of column jc (RS >= d leaves some threads idle)
+            float acc[RPT];
 #pragma unroll
-        for (int u = 0; u < RPT; ++u) {
-            const int r = rb0 + 16 * u;
-            acc[u] = sgC[r] * sA[r * TV + jc];
-        }
+            for (int u = 0; u < RPT; ++u) {
+                const int r = min(rb0 + RS * u, d - 1);
+                acc[u] = sgC[r] * sA[r * TV + jc];
+            }
 #pragma unroll 4
-        for (int i = 0; i < C; ++i) {
-            const float z = szt[i * TV + jc];
+            for (int i = 0; i < C; ++i) {
+                const float z = szt[i * TV + jc];
 #pragma unroll
-            for (int u = 0; u < RPT; ++u) acc[u] += sKb[i * dp + rb0 + 16 * u] * z;
+                for (int u = 0; u < RPT; ++u) acc[u] += sKb[i * dp + min(rb0 + RS * u, d - 1)] * z;
+            }
+#pragma unroll
+            for (int u = 0; u < RPT; ++u)
+                if (rb0 + RS * u < d) sA[(rb0 + RS * u) * TV + jc] = acc[u];
         }
-#pragma unroll
-        for (int u = 0; u < RPT; ++u) sA[(rb0 + 16 * u) * TV + jc] = acc[u];
         __syncthreads();
     }
 
     // ---- reverse sweep: dS' at each chunk end, and dZ; dS_0 at the end -----------
-    for (int e = tid; e < dt; e += THREADS) {
+    for (int e = tid; e < dt; e += CT) {
         const int r = e / TV;
         sA[e] = dfinal ? dfinal[pair * dd + (size_t)r * d + v0 + (e - r * TV)] : 0.f;
     }
@@ -422,43 +448,53 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_chain_kernel(
     for (int c = nck - 1; c >= 0; --c) {
         const size_t slot = (size_t)(base + c) * H + h;
         float *dSd = ws.dS + slot * dd;
-        for (int e = tid; e < dt; e += THREADS) {
+        for (int e = tid; e < dt; e += CT) {
             const int r = e / TV;
             dSd[(size_t)r * d + v0 + (e - r * TV)] = sA[e];
         }
         commit_chunk(true, c > 0 ? c - 1 : -1);
         // dZ = Kbar dS' + H^T dO on this tile
         float *dZd = ws.dZ + slot * cd;
-        for (int e = tid; e < ct; e += THREADS) {
-            const int i = e / TV, j = e - i * TV;
+        for (int e = tid / ZS; e < ct; e += CT / ZS) {
+            const int i = e / TV, j = e - i * TV, part = tid % ZS;
             float z = 0.f;
 #pragma unroll 8
-            for (int r = 0; r < d; ++r) z += sKb[i * dp + r] * sA[r * TV + j];
-            for (int i2 = i; i2 < C; ++i2) z += sHm[i2 * C + i] * svt[i2 * TV + j];
-            szt[e] = z;
-            dZd[(size_t)i * d + v0 + j] = z;
+            for (int r = part * (d / ZS); r < (part + 1) * (d / ZS); ++r)
+                z += sKb[i * dp + r] * sA[r * TV + j];
+            if (part == 0)
+                for (int i2 = i; i2 < C; ++i2) z += sHm[i2 * C + i] * svt[i2 * TV + j];
+            if (ZS == 2) z += __shfl_xor(z, 1);
+            if (part == 0) {
+                szt[e] = z;
+                dZd[(size_t)i * d + v0 + j] = z;
+            }
         }
         __syncthreads();
         // dS = Diag(e^{G_C}) dS' + Qbar^T dO - R^T dZ, in place
-        float acc[RPT];
+        if (rb0 < d) {
+            float acc[RPT];
 #pragma unroll
-        for (int u = 0; u < RPT; ++u) {
-            const int r = rb0 + 16 * u;
-            acc[u] = sgC[r] * sA[r * TV + jc];
-        }
+            for (int u = 0; u < RPT; ++u) {
+                const int r = min(rb0 + RS * u, d - 1);
+                acc[u] = sgC[r] * sA[r * TV + jc];
+            }
 #pragma unroll 4
-        for (int i = 0; i < C; ++i) {
-            const float o = svt[i * TV + jc], z = szt[i * TV + jc];
+            for (int i = 0; i < C; ++i) {
+                const float o = svt[i * TV + jc], z = szt[i * TV + jc];
+#pragma unroll
+                for (int u = 0; u < RPT; ++u) {
+                    const int r = min(rb0 + RS * u, d - 1);
+                    acc[u] += sQb[i * dp + r] * o - sR[i * dp + r] * z;
+                }
+            }
 #pragma unroll
             for (int u = 0; u < RPT; ++u)
-                acc[u] += sQb[i * dp + rb0 + 16 * u] * o - sR[i * dp + rb0 + 16 * u] * z;
+                if (rb0 + RS * u < d) sA[(rb0 + RS * u) * TV + jc] = acc[u];
         }
-#pragma unroll
-        for (int u = 0; u < RPT; ++u) sA[(rb0 + 16 * u) * TV + jc] = acc[u];
         __syncthreads();
     }
     if (ds0)
-        for (int e = tid; e < dt; e += THREADS) {
+        for (int e = tid; e < dt; e += CT) {
             const int r = e / TV;
             ds0[pair * dd + (size_t)r * d + v0 + (e - r * TV)] = sA[e];
         }
@@ -501,13 +537,16 @@ __host__ __device__ inline GradLds grad_layout(int d, int C) {
 }
 
 template <int C, int D>
-__global__ __launch_bounds__(THREADS) void kda_bwd_grad_kernel(
+__global__ __launch_bounds__(GT) void kda_bwd_grad_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, float scale, int H,
     int row_len, const int32_t *__restrict__ cu, int n_seqs, const float *__restrict__ dout,
     float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv,
     float *__restrict__ dg, float *__restrict__ dbeta, Ws ws) {
     constexpr int d = D;
+    constexpr int XS = (C * (D < 16 ? D : 16) < GT) ? GT / (C * (D < 16 ? D : 16)) : 1;
+    constexpr int PS = (C * C < GT) ? GT / (C * C) : 1;   // lanes sharing one dT / dH entry
+    static_assert((XS == 1 || XS == 2) && (PS == 1 || PS == 2), "at most lane pairs");
     extern __shared__ float sm[];
     const GradLds L = grad_layout(d, C);
     float *sq = sm + L.q, *sk = sm + L.k, *sG = sm + L.G, *sv = sm + L.v, *sdO = sm + L.dO;
@@ -526,7 +565,7 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_grad_kernel(
 
     {
         const size_t off = ((size_t)t0 * H + h) * d, pitch = (size_t)H * d;
-        Rows4 r[7];
+        Rows<GT> r[7];
         fetch_rows(r[0], q + off, pitch, C, len, d, tid);
         fetch_rows(r[1], k + off, pitch, C, len, d, tid);
         fetch_rows(r[2], g + off, pitch, C, len, d, tid);
@@ -535,31 +574,33 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_grad_kernel(
         fetch_rows(r[5], ws.Z + wslot * cd, d, C, C, d, tid);
         fetch_rows(r[6], ws.dZ + wslot * cd, d, C, C, d, tid);
         const float rb = tid < len ? beta[(size_t)(t0 + tid) * H + h] : 0.f;
-        constexpr int CC = C * C / THREADS;
-        float rT[CC], rK[CC];
+        constexpr int NCC = (C * C + GT - 1) / GT;
+        float rT[NCC], rK[NCC];
 #pragma unroll
-        for (int u = 0; u < CC; ++u) {
-            rT[u] = ws.T[wslot * C * C + tid + u * THREADS];
-            rK[u] = ws.Kt[wslot * C * C + tid + u * THREADS];
+        for (int u = 0; u < NCC; ++u) {
+            const int e = min(tid + u * GT, C * C - 1);
+            rT[u] = ws.T[wslot * C * C + e];
+            rK[u] = ws.Kt[wslot * C * C + e];
         }
         float *dst[7] = {sq, sk, sG, sv, sdO, sZ, sdZ};
 #pragma unroll
         for (int a = 0; a < 7; ++a) commit_rows(dst[a], r[a], C, d, tid);
         if (tid < C) sb[tid] = rb;
 #pragma unroll
-        for (int u = 0; u < CC; ++u) {
-            sT[tid + u * THREADS] = rT[u];
-            sKt[tid + u * THREADS] = rK[u];
-        }
+        for (int u = 0; u < NCC; ++u)
+            if (tid + u * GT < C * C) {
+                sT[tid + u * GT] = rT[u];
+                sKt[tid + u * GT] = rK[u];
+            }
     }
     __syncthreads();
-    cumsum_rows<C>(sG, d, tid);
+    cumsum_rows<C, GT>(sG, d, tid);
     __syncthreads();
 
     // The products with S and dS', SR channel rows at a time:
     //   dR = -dZ S^T,  dQbar = dO S^T,  dKbar = Z dS'^T,  gc = e^{G_C} rowsum(dS' . S).
     const float *Sg = ws.S + wslot * dd, *dSg = ws.dS + wslot * dd;
-    Rows4 rS, rdS;
+    Rows<GT> rS, rdS;
     fetch_rows(rS, Sg, d, SR, SR, d, tid);
     fetch_rows(rdS, dSg, d, SR, SR, d, tid);
     for (int r0 = 0; r0 < d; r0 += SR) {
@@ -570,21 +611,28 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_grad_kernel(
             fetch_rows(rS, Sg + (size_t)(r0 + SR) * d, d, SR, SR, d, tid);
             fetch_rows(rdS, dSg + (size_t)(r0 + SR) * d, d, SR, SR, d, tid);
         }
-        for (int e = tid; e < C * SR; e += THREADS) {
-            const int x = e / SR, rr = e - x * SR;
+        for (int e = tid / XS; e < C * SR; e += GT / XS) {
+            const int x = e / SR, rr = e - x * SR, part = tid % XS;
             float a = 0.f, b = 0.f, z = 0.f;
 #pragma unroll 8
-            for (int u = 0; u < d; ++u) {
+            for (int u = part * (d / XS); u < (part + 1) * (d / XS); ++u) {
                 const float s = sS[rr * dp + u];
                 a += sdZ[x * dp + u] * s;
                 b += sdO[x * dp + u] * s;
                 z += sZ[x * dp + u] * sdS[rr * dp + u];
             }
-            sdR[x * dp + r0 + rr] = -a;
-            sdQb[x * dp + r0 + rr] = b;
-            sdKb[x * dp + r0 + rr] = z;
+            if (XS == 2) {
+                a += __shfl_xor(a, 1);
+                b += __shfl_xor(b, 1);
+                z += __shfl_xor(z, 1);
+            }
+            if (part == 0) {
+                sdR[x * dp + r0 + rr] = -a;
+                sdQb[x * dp + r0 + rr] = b;
+                sdKb[x * dp + r0 + rr] = z;
+            }
         }
-        for (int rr = tid; rr < SR; rr += THREADS) {
+        for (int rr = tid; rr < SR; rr += GT) {
             float a = 0.f;
             for (int u = 0; u < d; ++u) a += sdS[rr * dp + u] * sS[rr * dp + u];
             sgc[r0 + rr] = fast_exp(sG[(C - 1) * dp + r0 + rr]) * a;
@@ -592,21 +640,29 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_grad_kernel(
         __syncthreads();
     }
     // dT = dZ (BV)^T + dR (BL)^T;  dH = dO Z^T (j <= i)
-    for (int e = tid; e < C * C; e += THREADS) {
-        const int i = e / C, j = e - i * C;
-        float a = 0.f;
-        for (int c2 = 0; c2 < d; ++c2)
+    for (int e = tid / PS; e < C * C; e += GT / PS) {
+        const int i = e / C, j = e - i * C, part = tid % PS;
+        const int c0 = part * (d / PS), c1 = (part + 1) * (d / PS);
+        float a = 0.f, hh = 0.f;
+#pragma unroll 4
+        for (int c2 = c0; c2 < c1; ++c2)
             a += sdZ[i * dp + c2] * sv[j * dp + c2] +
                  sdR[i * dp + c2] * sk[j * dp + c2] * fast_exp(sG[j * dp + c2]);
-        sdT[e] = sb[j] * a;
-        float hh = 0.f;
         if (j <= i)
-            for (int c2 = 0; c2 < d; ++c2) hh += sdO[i * dp + c2] * sZ[j * dp + c2];
-        sHm[e] = hh;
+#pragma unroll 4
+            for (int c2 = c0; c2 < c1; ++c2) hh += sdO[i * dp + c2] * sZ[j * dp + c2];
+        if (PS == 2) {
+            a += __shfl_xor(a, 1);
+            hh += __shfl_xor(hh, 1);
+        }
+        if (part == 0) {
+            sdT[e] = sb[j] * a;
+            sHm[e] = hh;
+        }
     }
     __syncthreads();
     // dBV = T^T dZ (into dO's storage), dBL = T^T dR
-    for (int e = tid; e < cd; e += THREADS) {
+    for (int e = tid; e < cd; e += GT) {
         const int j = e / d, c2 = e - j * d;
         float bv = 0.f, bl = 0.f;
         for (int i = j; i < C; ++i) {
@@ -617,7 +673,7 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_grad_kernel(
         sdL[j * dp + c2] = bl;
     }
     // M1 = T^T dT
-    for (int e = tid; e < C * C; e += THREADS) {
+    for (int e = tid; e < C * C; e += GT) {
         const int i = e / C, j = e - i * C;
         float a = 0.f;
         for (int m = i; m < C; ++m) a += sT[m * C + i] * sdT[m * C + j];
@@ -625,7 +681,7 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_grad_kernel(
     }
     __syncthreads();
     // dbeta_j = dBV_j . v_j + dBL_j . L_j
-    for (int j = tid; j < C; j += THREADS) {
+    for (int j = tid; j < C; j += GT) {
         float s = 0.f;
         for (int c2 = 0; c2 < d; ++c2)
             s += sdBV[j * dp + c2] * sv[j * dp + c2] +
@@ -634,7 +690,7 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_grad_kernel(
     }
     // dA = M1 T^T (strictly lower); dA . K~ into dT's storage (dT is consumed);
     // dK~_ij = -beta_i dA_ij in place of K~
-    for (int e = tid; e < C * C; e += THREADS) {
+    for (int e = tid; e < C * C; e += GT) {
         const int i = e / C, j = e - i * C;
         float a = 0.f;
         if (j < i)
@@ -644,12 +700,12 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_grad_kernel(
     }
     __syncthreads();
     // dv = beta dBV;  dL = beta dBL (in place);  dbeta_i -= sum_j dA_ij K~_ij
-    for (int e = tid; e < cd; e += THREADS) {
+    for (int e = tid; e < cd; e += GT) {
         const int j = e / d, a = j * dp + (e - j * d);
         if (j < len) dv[((size_t)(t0 + j) * H + h) * d + (e - j * d)] = sb[j] * sdBV[a];
         sdL[a] *= sb[j];
     }
-    for (int i = tid; i < C; i += THREADS) {
+    for (int i = tid; i < C; i += GT) {
         float s = 0.f;
         for (int j = 0; j < i; ++j) s += sAK[i * C + j];
         sdb[i] -= s;
@@ -659,7 +715,7 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_grad_kernel(
     //   P1 = sum_{j<x} dK~_xj k_jc E_xj,  P2 = sum_{i>x} dK~_ix k_ic E_ix,
     //   P3 = sum_{j<=x} dH_xj k_jc E_xj,  P4 = sum_{i>=x} dH_ix (s q_ic) E_ix;
     // then the direct uses of e^{G} in Qbar, L and Kbar.
-    for (int e = tid; e < cd; e += THREADS) {
+    for (int e = tid; e < cd; e += GT) {
         const int x = e / d, c2 = e - x * d, ax = x * dp + c2;
         const float Gx = sG[ax], kx = sk[ax], qx = scale * sq[ax];
         float P1 = 0.f, P2 = 0.f, P3 = 0.f, P4 = 0.f;
@@ -690,7 +746,7 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_grad_kernel(
     __syncthreads();
     // dG_C = gc + sum_x dKbar_x Kbar_x joins the last row; dg is the reverse
     // cumulative sum of dG over the valid rows (padding rows carry nothing).
-    for (int c2 = tid; c2 < d; c2 += THREADS) {
+    for (int c2 = tid; c2 < d; c2 += GT) {
         float run = sgc[c2];
         for (int x = 0; x < C; ++x) run += sdL[x * dp + c2];
         for (int x = len - 1; x >= 0; --x) {
@@ -698,7 +754,7 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_grad_kernel(
             dg[((size_t)(t0 + x) * H + h) * d + c2] = run;
         }
     }
-    for (int j = tid; j < len; j += THREADS) dbeta[(size_t)(t0 + j) * H + h] = sdb[j];
+    for (int j = tid; j < len; j += GT) dbeta[(size_t)(t0 + j) * H + h] = sdb[j];
 }
 
 }  // namespace bwd
@@ -706,7 +762,7 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_grad_kernel(
 bool bwd_supported(int dk, int dv, int chunk) {
     if (dk != dv || !(dk == 16 || dk == 32 || dk == 64 || dk == 128)) return false;
     if (!(chunk == 16 || chunk == 32 || chunk == 64)) return false;
-    if (chunk * dk > 4 * bwd::MAXV4 * bwd::THREADS) return false;   // one fetch per thread
+    if (chunk * dk > bwd::MAX_BLOCK) return false;   // one fetched block per [C][d] operand
     const size_t cap = 163840 / sizeof(float);
     return (size_t)bwd::prep_layout(dk, chunk).total <= cap &&
            (size_t)bwd::chain_layout(dk, chunk).total <= cap &&
@@ -740,11 +796,11 @@ hipError_t launch_bwd_cd(const ChunkBwdProblem &p, const bwd::Ws &ws, size_t slo
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((kda_bwd_chain_kernel<C, D>), dim3(p.n_seqs * p.heads * (D / TV)),
-                       dim3(THREADS), lc, p.stream, p.v, p.beta, p.heads, p.seqlen, p.cu, p.s0,
+                       dim3(CT), lc, p.stream, p.v, p.beta, p.heads, p.seqlen, p.cu, p.s0,
                        p.dfinal, p.dout, p.ds0, ws);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((kda_bwd_grad_kernel<C, D>), per_chunk, dim3(THREADS), lg, p.stream, p.q,
+    hipLaunchKernelGGL((kda_bwd_grad_kernel<C, D>), per_chunk, dim3(GT), lg, p.stream, p.q,
                        p.k, p.v, p.g, p.beta, p.scale, p.heads, p.seqlen, p.cu, p.n_seqs, p.dout,
                        p.dq, p.dk, p.dv, p.dg, p.dbeta, ws);
     return hipGetLastError();
