@@ -354,13 +354,19 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
               workspace: Optional[torch.Tensor] = None) -> dict:
     """Gradients of ``chunk_fwd`` (``kda_chunk_bwd``) for L = <o, d_o> +
     <final states, d_final_state>: a dict with dq, dk, dv, dg, dbeta and, when
-    an initial state is given, dinitial_state.  fp32 tensors only, d_k = d_v =
-    d with (d, chunk_size) in {(16, 16|32|64), (32, 16|32), (64, 16|32)}."""
+    an initial state is given, dinitial_state.  q, k, v and d_o in fp32 or
+    bf16 (one dtype), g, beta and the states fp32; the gradients are fp32.
+    d_k = d_v = d with (d, chunk_size) in {(16, 16|32|64), (32, 16|32),
+    (64, 16|32), (128, 16)}."""
     _need(q.dim() == 4 and k.shape == q.shape and v.shape == q.shape and g.shape == q.shape,
           "q, k, v, g must be [B, T, H, d] (d_k = d_v)")
     B, T, H, d = q.shape
     _need(beta.shape == (B, T, H) and d_o.shape == q.shape, "beta must be [B, T, H], d_o like v")
-    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("d_o", d_o)):
+    _need(q.dtype in (torch.float32, torch.bfloat16) and
+          q.dtype == k.dtype == v.dtype == d_o.dtype, "q, k, v, d_o must share fp32 or bf16")
+    for name, t in (("q", q), ("k", k), ("v", v), ("d_o", d_o)):
+        _need(t.is_cuda and t.is_contiguous(), "%s must be a contiguous device tensor" % name)
+    for name, t in (("g", g), ("beta", beta)):
         _need(t.dtype == torch.float32 and t.is_cuda and t.is_contiguous(),
               "%s must be a contiguous fp32 device tensor" % name)
     if cu_seqlens is not None:
@@ -375,12 +381,12 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
                             and t.is_contiguous()),
               "%s must be a contiguous fp32 device tensor [N, H, d, d]" % name)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    sh = make_shape(B, T, H, d, d, chunk_size, N, KDA_F32)
+    sh = make_shape(B, T, H, d, d, chunk_size, N, _dtype_code(q))
     need = int(lib().kda_chunk_bwd_workspace_bytes(ctypes.byref(sh)))
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    out = {n: torch.empty_like(t) for n, t in (("dq", q), ("dk", k), ("dv", v), ("dg", g),
-                                               ("dbeta", beta))}
+    out = {n: torch.empty(t.shape, dtype=torch.float32, device=q.device)
+           for n, t in (("dq", q), ("dk", k), ("dv", v), ("dg", g), ("dbeta", beta))}
     ds0 = None
     if initial_state is not None:
         ds0 = torch.empty_like(initial_state)

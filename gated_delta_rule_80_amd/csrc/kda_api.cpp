@@ -340,16 +340,16 @@ size_t kda_chunk_bwd_workspace_bytes(const kda_shape *shape) {
                                     shape->chunk_size);
 }
 
-kda_status kda_chunk_bwd(const kda_shape *shape, const float *q, const float *k, const float *v,
+kda_status kda_chunk_bwd(const kda_shape *shape, const void *q, const void *k, const void *v,
                          const float *g_log_decay, const float *beta, float scale,
-                         const float *initial_state, const int32_t *cu_seqlens, const float *d_o,
+                         const float *initial_state, const int32_t *cu_seqlens, const void *d_o,
                          const float *d_final_state, float *dq, float *dk, float *dv, float *dg,
                          float *dbeta, float *d_initial_state, void *workspace,
                          size_t workspace_bytes, void *stream) {
     g_last_error[0] = '\0';
     if (!shape) return fail(KDA_ERR_INVALID_ARGUMENT, "shape is NULL");
-    if (shape->dtype != KDA_F32)
-        return fail(KDA_ERR_UNSUPPORTED, "the backward is built for fp32 storage only");
+    if (shape->dtype != KDA_F32 && shape->dtype != KDA_BF16)
+        return fail(KDA_ERR_UNSUPPORTED, "unknown dtype %d", (int)shape->dtype);
     if (shape->batch <= 0 || shape->seqlen < 0 || shape->num_heads <= 0 || shape->d_k <= 0 ||
         shape->d_v <= 0 || shape->chunk_size <= 0 || shape->num_seqs <= 0)
         return fail(KDA_ERR_INVALID_ARGUMENT, "non-positive size");
@@ -398,6 +398,7 @@ kda_status kda_chunk_bwd(const kda_shape *shape, const float *q, const float *k,
     p.heads = shape->num_heads;
     p.d = shape->d_k;
     p.chunk = shape->chunk_size;
+    p.bf16 = shape->dtype == KDA_BF16;
     p.q = q;
     p.k = k;
     p.v = v;

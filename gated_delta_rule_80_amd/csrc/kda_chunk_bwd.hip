@@ -117,16 +117,23 @@ template <int NT> struct Rows {
     static constexpr int NV = (MAX_BLOCK / 4 + NT - 1) / NT;   // float4 per thread
     float4 x[NV];
 };
+// Four consecutive elements as fp32 (bf16 widens exactly).
+__device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+__device__ __forceinline__ float4 ld4(const bf16_t *p) {
+    const uint2 u = *reinterpret_cast<const uint2 *>(p);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
 // Row i (< len) of the block starts at src + i * pitch; rows >= len read as 0.
-template <int NT>
-__device__ __forceinline__ void fetch_rows(Rows<NT> &r, const float *src, size_t pitch, int rows,
+template <int NT, typename E>
+__device__ __forceinline__ void fetch_rows(Rows<NT> &r, const E *src, size_t pitch, int rows,
                                            int len, int d, int tid) {
 #pragma unroll
     for (int u = 0; u < Rows<NT>::NV; ++u) {
         const int e = 4 * (tid + u * NT), i = e / d;
         float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
         if (i < rows && i < len)
-            val = *reinterpret_cast<const float4 *>(src + (size_t)i * pitch + (e - i * d));
+            val = ld4(src + (size_t)i * pitch + (e - i * d));
         r.x[u] = val;
     }
 }
@@ -229,9 +236,9 @@ __host__ __device__ inline PrepLds prep_layout(int d, int C) {
 
 // One chunk of one head: K~, T, H, R = T Diag(beta) L, Kbar, Qbar and e^{G_C}
 // into the workspace (padding rows come out zero, T's padding block identity).
-template <int C, int D>
+template <int C, int D, typename In>
 __global__ __launch_bounds__(THREADS) void kda_bwd_prep_kernel(
-    const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ g,
+    const In *__restrict__ q, const In *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, float scale, int H, int row_len,
     const int32_t *__restrict__ cu, int n_seqs, Ws ws) {
     constexpr int d = D;
@@ -307,11 +314,11 @@ __host__ __device__ inline ChainLds chain_layout(int d, int C) {
     return L;
 }
 
-template <int C, int D>
+template <int C, int D, typename In>
 __global__ __launch_bounds__(CT) void kda_bwd_chain_kernel(
-    const float *__restrict__ v, const float *__restrict__ beta, int H, int row_len,
+    const In *__restrict__ v, const float *__restrict__ beta, int H, int row_len,
     const int32_t *__restrict__ cu, const float *__restrict__ s0, const float *__restrict__ dfinal,
-    const float *__restrict__ dout, float *__restrict__ ds0, Ws ws) {
+    const In *__restrict__ dout, float *__restrict__ ds0, Ws ws) {
     constexpr int d = D;
     constexpr int NCC = (C * C + CT - 1) / CT;       // T / H entries per thread
     constexpr int NVT = (C * TV + CT - 1) / CT;      // v or dO tile entries per thread
@@ -354,11 +361,12 @@ __global__ __launch_bounds__(CT) void kda_bwd_chain_kernel(
             }
         }
         const size_t off = ((size_t)t0 * H + h) * d, pitch = (size_t)H * d;
-        const float *src = reverse ? dout : v;
+        const In *src = reverse ? dout : v;
 #pragma unroll
         for (int u = 0; u < NVT; ++u) {
             const int e = tid + u * CT, i = e / TV;
-            rv[u] = (i < C && i < len) ? src[off + (size_t)i * pitch + v0 + (e - i * TV)] : 0.f;
+            rv[u] = (i < C && i < len) ? io<In>::load(src, off + (size_t)i * pitch + v0 + (e - i * TV))
+                                       : 0.f;
         }
         if (tid < C) rb = tid < len ? beta[(size_t)(t0 + tid) * H + h] : 0.f;
         if (tid < d) rg = ws.gC[w * d + tid];
@@ -536,11 +544,11 @@ __host__ __device__ inline GradLds grad_layout(int d, int C) {
     return L;
 }
 
-template <int C, int D>
+template <int C, int D, typename In>
 __global__ __launch_bounds__(GT) void kda_bwd_grad_kernel(
-    const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
+    const In *__restrict__ q, const In *__restrict__ k, const In *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, float scale, int H,
-    int row_len, const int32_t *__restrict__ cu, int n_seqs, const float *__restrict__ dout,
+    int row_len, const int32_t *__restrict__ cu, int n_seqs, const In *__restrict__ dout,
     float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv,
     float *__restrict__ dg, float *__restrict__ dbeta, Ws ws) {
     constexpr int d = D;
@@ -775,35 +783,42 @@ size_t bwd_workspace_bytes(int64_t total_tokens, int n_seqs, int heads, int d, i
 }
 
 namespace {
-template <int C, int D>
-hipError_t launch_bwd_cd(const ChunkBwdProblem &p, const bwd::Ws &ws, size_t slots) {
+template <int C, int D, typename In>
+hipError_t launch_bwd_cdt(const ChunkBwdProblem &p, const bwd::Ws &ws, size_t slots) {
     using namespace bwd;
+    const In *q = static_cast<const In *>(p.q), *k = static_cast<const In *>(p.k);
+    const In *v = static_cast<const In *>(p.v), *dout = static_cast<const In *>(p.dout);
     const size_t lp = (size_t)prep_layout(D, C).total * sizeof(float);
     const size_t lc = (size_t)chain_layout(D, C).total * sizeof(float);
     const size_t lg = (size_t)grad_layout(D, C).total * sizeof(float);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kda_bwd_prep_kernel<C, D>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kda_bwd_prep_kernel<C, D, In>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lp);
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kda_bwd_chain_kernel<C, D>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kda_bwd_chain_kernel<C, D, In>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lc);
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kda_bwd_grad_kernel<C, D>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kda_bwd_grad_kernel<C, D, In>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lg);
     if (e != hipSuccess) return e;
     const dim3 per_chunk((unsigned)(slots * p.heads));
-    hipLaunchKernelGGL((kda_bwd_prep_kernel<C, D>), per_chunk, dim3(THREADS), lp, p.stream, p.q,
-                       p.k, p.g, p.beta, p.scale, p.heads, p.seqlen, p.cu, p.n_seqs, ws);
+    hipLaunchKernelGGL((kda_bwd_prep_kernel<C, D, In>), per_chunk, dim3(THREADS), lp, p.stream, q,
+                       k, p.g, p.beta, p.scale, p.heads, p.seqlen, p.cu, p.n_seqs, ws);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((kda_bwd_chain_kernel<C, D>), dim3(p.n_seqs * p.heads * (D / TV)),
-                       dim3(CT), lc, p.stream, p.v, p.beta, p.heads, p.seqlen, p.cu, p.s0,
-                       p.dfinal, p.dout, p.ds0, ws);
+    hipLaunchKernelGGL((kda_bwd_chain_kernel<C, D, In>), dim3(p.n_seqs * p.heads * (D / TV)),
+                       dim3(CT), lc, p.stream, v, p.beta, p.heads, p.seqlen, p.cu, p.s0,
+                       p.dfinal, dout, p.ds0, ws);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((kda_bwd_grad_kernel<C, D>), per_chunk, dim3(GT), lg, p.stream, p.q,
-                       p.k, p.v, p.g, p.beta, p.scale, p.heads, p.seqlen, p.cu, p.n_seqs, p.dout,
+    hipLaunchKernelGGL((kda_bwd_grad_kernel<C, D, In>), per_chunk, dim3(GT), lg, p.stream, q,
+                       k, v, p.g, p.beta, p.scale, p.heads, p.seqlen, p.cu, p.n_seqs, dout,
                        p.dq, p.dk, p.dv, p.dg, p.dbeta, ws);
     return hipGetLastError();
+}
+template <int C, int D>
+hipError_t launch_bwd_cd(const ChunkBwdProblem &p, const bwd::Ws &ws, size_t slots) {
+    return p.bf16 ? launch_bwd_cdt<C, D, bf16_t>(p, ws, slots)
+                  : launch_bwd_cdt<C, D, float>(p, ws, slots);
 }
 }  // namespace
 

@@ -79,15 +79,17 @@ hipError_t launch_chunk_fwd_f32(const ChunkProblem &p);
 // Gradients of the chunked prefill, fp32 storage, d_k = d_v = d.
 struct ChunkBwdProblem {
     int n_seqs, seqlen, heads, d, chunk;   // as ChunkProblem (seqlen = row length)
-    const float *q, *k, *v, *g, *beta;     // per-channel log-decays, plain inputs
+    bool bf16;                             // q, k, v, dout in bf16 (else fp32)
+    const void *q, *k, *v;                 // plain inputs
+    const float *g, *beta;                 // per-channel log-decays, write strengths
     float scale;
     const float *s0;        // may be null (zeros)
     const int32_t *cu;      // may be null (equal rows)
     const float *dfinal;    // gradient of the final states; may be null (zeros)
-    const float *dout;      // gradient of o
+    const void *dout;       // gradient of o, dtype of v
     float *dq, *dk, *dv, *dg, *dbeta;
     float *ds0;             // may be null (not written)
-    float *work;            // workspace: per chunk S, dS', Z and dZ
+    float *work;            // workspace: per chunk states, gradients and factors
     hipStream_t stream;
 };
 bool bwd_supported(int dk, int dv, int chunk);

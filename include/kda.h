@@ -300,15 +300,17 @@ kda_status kda_output_rmsnorm_gate(int64_t rows, int32_t d_v, kda_dtype dtype,
  * and dZ; a second kernel (one workgroup per chunk and head) forms every
  * other gradient from one chunk's inputs and those stored quantities.
  *
- *   shape         as kda_chunk_fwd; dtype KDA_F32 only, d_k = d_v = d with
- *                 (d, chunk) in {(16, 16|32|64), (32, 16|32), (64, 16|32),
- *                 (128, 16)}.
+ *   shape         as kda_chunk_fwd; dtype KDA_F32 or KDA_BF16 (the storage of
+ *                 q, k, v and d_o), d_k = d_v = d with (d, chunk) in
+ *                 {(16, 16|32|64), (32, 16|32), (64, 16|32), (128, 16)}.
  *   q, k, g_log_decay, v, beta, scale, initial_state, cu_seqlens
  *                 the forward's inputs, same layouts (initial_state may be NULL).
- *   d_o           [B, T, H, d_v] fp32: dL/do.
+ *   d_o           [B, T, H, d_v], dtype as v: dL/do.
+ *   All arithmetic is fp32 (bf16 inputs widen exactly); every gradient is
+ *   written in fp32.
  *   d_final_state [N, H, d_k, d_v] fp32 or NULL (zeros).
  *   dq, dk, dv, dg, dbeta
- *                 outputs with the layouts of q, k, v, g_log_decay, beta.
+ *                 fp32 outputs with the layouts of q, k, v, g_log_decay, beta.
  *   d_initial_state [N, H, d_k, d_v] fp32 or NULL (not written).
  *   workspace     at least kda_chunk_bwd_workspace_bytes(shape) bytes,
  *                 256-byte aligned: per chunk slot and head, the chunk-start
@@ -319,11 +321,11 @@ kda_status kda_output_rmsnorm_gate(int64_t rows, int32_t d_v, kda_dtype dtype,
  * library enqueues kernels only.
  */
 size_t kda_chunk_bwd_workspace_bytes(const kda_shape *shape);
-kda_status kda_chunk_bwd(const kda_shape *shape, const float *q, const float *k,
-                         const float *v, const float *g_log_decay,
+kda_status kda_chunk_bwd(const kda_shape *shape, const void *q, const void *k,
+                         const void *v, const float *g_log_decay,
                          const float *beta, float scale,
                          const float *initial_state,
-                         const int32_t *cu_seqlens, const float *d_o,
+                         const int32_t *cu_seqlens, const void *d_o,
                          const float *d_final_state, float *dq, float *dk,
                          float *dv, float *dg, float *dbeta,
                          float *d_initial_state, void *workspace,

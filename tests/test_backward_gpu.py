@@ -40,9 +40,22 @@ def make(B, T, H, d, seed, lengths=None, g_range=(-1.0, 0.0), s0=True, dfin=True
     return x
 
 
+def to_bf16(x):
+    """q, k, v and do rounded to bf16 (RNE); the oracle gets the rounded values."""
+    x = dict(x)
+    for n in ("q", "k", "v", "do"):
+        x[n] = torch.from_numpy(x[n]).to(torch.bfloat16).float().numpy()
+    x["_bf16"] = True
+    return x
+
+
 def check(x, chunk):
     import gated_delta_rule_80_amd as K
+    bf16 = x.pop("_bf16", False)
     dev = {n: (torch.from_numpy(a).cuda() if a is not None else None) for n, a in x.items()}
+    if bf16:
+        for n in ("q", "k", "v", "do"):
+            dev[n] = dev[n].to(torch.bfloat16)   # exact: the values are bf16 already
     got = K.chunk_bwd(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], dev["do"],
                       initial_state=dev["s0"], cu_seqlens=dev["cu"], d_final_state=dev["dfin"],
                       chunk_size=chunk)
@@ -56,6 +69,7 @@ def check(x, chunk):
                                           1.0 / np.sqrt(d), flat(x["do"]), x["s0"], x["dfin"], cu)
     errs = {}
     for name in ("dq", "dk", "dv", "dg", "dbeta"):
+        assert got[name].dtype == torch.float32
         a = got[name].double().cpu().numpy()
         errs[name] = rel_err(a.reshape(-1, *a.shape[2:]), ref[name])
     if x["s0"] is not None:
@@ -90,3 +104,12 @@ def test_backward_d128_packed_sequences():
 
 def test_backward_d128_strong_decays_without_initial_state():
     check(make(1, 37, 1, 128, seed=205, g_range=(-5.0, 0.0), s0=False), 16)
+
+
+@pytest.mark.parametrize("d,C,T", [(128, 16, 45), (64, 32, 70), (16, 64, 130)])
+def test_backward_bf16_storage(d, C, T):
+    check(to_bf16(make(2, T, 2, d, seed=300 + d)), C)
+
+
+def test_backward_bf16_packed_sequences():
+    check(to_bf16(make(1, 0, 2, 128, seed=305, lengths=[20, 0, 37])), 16)
