@@ -76,11 +76,6 @@ def measured_traffic(key):
     return rec["hbm_bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
 
 
-def ctypes_byref_shape(K, B, T, H, d, C, N):
-    import ctypes
-    return ctypes.byref(K.make_shape(B, T, H, d, d, C, N, K.KDA_F32))
-
-
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -372,20 +367,23 @@ def main():
         del d4, inp4, ws4, o4, fs4
 
     if not args.skip_backward:
-        # Gradients through kda_chunk_bwd at the layer's width (fp32 storage,
-        # d = 128, C = 16), one sequence of 8192 tokens per head, 32 heads.
-        print("[bench] backward (fp32, d=128, C=16, B=1 H=32 T=8192)", file=sys.stderr, flush=True)
+        # Gradients through kda_chunk_bwd at the layer's width (bf16 q, k, v and
+        # d_o, fp32 gradients, d = 128, C = 16), one sequence of 8192 tokens
+        # per head, 32 heads.
+        print("[bench] backward (bf16 storage, d=128, C=16, B=1 H=32 T=8192)", file=sys.stderr,
+              flush=True)
         gen = torch.Generator(device=dev).manual_seed(7)
         Tb, Hb, db, Cb = 8192, 32, 128, 16
         rnd = lambda *sh: torch.randn(*sh, generator=gen, device=dev)  # noqa: E731
-        qb = torch.nn.functional.normalize(rnd(1, Tb, Hb, db), dim=-1).contiguous()
-        kb = torch.nn.functional.normalize(rnd(1, Tb, Hb, db), dim=-1).contiguous()
-        vb, dob = rnd(1, Tb, Hb, db), rnd(1, Tb, Hb, db)
+        bf = torch.bfloat16
+        qb = torch.nn.functional.normalize(rnd(1, Tb, Hb, db), dim=-1).to(bf).contiguous()
+        kb = torch.nn.functional.normalize(rnd(1, Tb, Hb, db), dim=-1).to(bf).contiguous()
+        vb, dob = rnd(1, Tb, Hb, db).to(bf), rnd(1, Tb, Hb, db).to(bf)
         gb = (-0.05 * torch.rand(1, Tb, Hb, db, generator=gen, device=dev)).contiguous()
         bb = torch.sigmoid(rnd(1, Tb, Hb)).contiguous()
         s0b, dfb = 0.1 * rnd(1, Hb, db, db), rnd(1, Hb, db, db)
-        wsb = torch.empty(K.lib().kda_chunk_bwd_workspace_bytes(ctypes_byref_shape(
-            K, 1, Tb, Hb, db, Cb, 1)), dtype=torch.uint8, device=dev)
+        wsb = torch.empty(K.workspace_bytes_bwd(1, Tb, Hb, db, Cb, 1, bf), dtype=torch.uint8,
+                          device=dev)
 
         def bstep():
             return K.chunk_bwd(qb, kb, vb, gb, bb, dob, initial_state=s0b, d_final_state=dfb,
@@ -402,15 +400,17 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         bms = e0.elapsed_time(e1) / n_b
-        # inputs q, k, v, g, d_o (fp32 d) and beta read once, gradients written
-        # once, states read (s0, d_final) and written (d_s0) once
-        bbytes = Tb * Hb * (5 * 4 * db + 4) + Tb * Hb * (4 * 4 * db + 4) + 3 * Hb * db * db * 4
+        # inputs q, k, v, d_o (bf16), g (fp32) and beta read once, gradients
+        # (fp32) written once, states read (s0, d_final) and written (d_s0) once
+        bbytes = Tb * Hb * (4 * 2 * db + 4 * db + 4) + Tb * Hb * (4 * 4 * db + 4) + \
+            3 * Hb * db * db * 4
         bgbs = bbytes / (bms * 1e-3) / 1e9
         result["backward"] = {
             "value": round(Tb / (bms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(bms, 4),
             "steps": n_b,
-            "config": {"workload": "gradients of the chunked prefill, B=1 H=32 T=8192 d=128 C=16 "
-                                   "fp32, log-decays U(-0.05, 0), through kda_chunk_bwd"},
+            "config": {"workload": "gradients of the chunked prefill, B=1 H=32 T=8192 d=128 C=16, "
+                                   "bf16 q/k/v/d_o, fp32 gradients, log-decays U(-0.05, 0), "
+                                   "through kda_chunk_bwd"},
             "roofline": {"bound": "alu", "kernel": "kda_bwd_prep_kernel, kda_bwd_chain_kernel, "
                          "kda_bwd_grad_kernel (fp32 VALU, operands in LDS)",
                          "achieved_hbm_gbs": round(bgbs, 2), "hbm_frac": round(bgbs / HBM_PEAK_GBS, 5),

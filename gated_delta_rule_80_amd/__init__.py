@@ -150,6 +150,14 @@ def workspace_bytes(batch, seqlen, heads, d_k, d_v, chunk_size, num_seqs,
     return int(lib().kda_chunk_fwd_workspace_bytes(ctypes.byref(sh)))
 
 
+def workspace_bytes_bwd(batch, seqlen, heads, d, chunk_size, num_seqs,
+                        dtype=torch.float32) -> int:
+    """Workspace kda_chunk_bwd needs for this problem (0 if unsupported)."""
+    code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
+    sh = make_shape(batch, seqlen, heads, d, d, chunk_size, num_seqs, code)
+    return int(lib().kda_chunk_bwd_workspace_bytes(ctypes.byref(sh)))
+
+
 def _prefill(entry, gate, q, k, v, g, beta, scale, initial_state, cu_seqlens,
              chunk_size, output_final_state, workspace, out, final_state, form=None):
     _need(q.dim() == 4 and k.shape == q.shape and v.dim() == 4 and v.shape[:3] == q.shape[:3],
