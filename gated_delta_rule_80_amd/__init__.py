@@ -27,8 +27,8 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["chunk_fwd", "decode_step", "chunk_fwd_scalar_gate", "decode_step_scalar_gate",
-           "chunk_fwd_ex", "decode_step_ex", "output_rmsnorm_gate", "workspace_bytes", "lib",
-           "KdaError", "LIB_PATH"]
+           "chunk_fwd_ex", "decode_step_ex", "output_rmsnorm_gate", "chunk_bwd", "workspace_bytes",
+           "workspace_bytes_bwd", "lib", "KdaError", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
