@@ -59,10 +59,9 @@ def decode_alg_bytes(N, H, dk, dv):
     return N * H * (2 * dk * dv * 4 + 2 * dk + 2 * dk + 2 * dv + 4 * dk + 4 + 2 * dv)
 
 
-def measured_traffic(key):
-    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
-    runs (scaled by a plain copy of known size), or None when the kernel
-    sources have changed since those counters were taken."""
+def _counter_record(key):
+    """The committed rocprofv3 counter record for one workload, or None when it
+    is missing or the kernel sources have changed since it was taken."""
     import hashlib
     try:
         with open(os.path.join(ROOT, "profiles", "hbm_traffic.json")) as f:
@@ -73,7 +72,28 @@ def measured_traffic(key):
                 h.update(f.read())
     except (OSError, KeyError, ValueError):
         return None
-    return rec["hbm_bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
+    return rec if h.hexdigest() == rec["sources_sha256"] else None
+
+
+def measured_traffic(key):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    runs (scaled by a plain copy of known size), or None when the kernel
+    sources have changed since those counters were taken."""
+    rec = _counter_record(key)
+    return rec["hbm_bytes_per_launch"] if rec else None
+
+
+def measured_mfma(key):
+    """Per kernel: the fraction of SIMD cycles with the matrix unit busy
+    (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE per XCD x 1024 SIMDs) and the
+    MFMA FLOPs issued (SQ_INSTS_VALU_MFMA_MOPS_* x 512), from the committed
+    counter run; None when the sources have changed since."""
+    rec = _counter_record(key)
+    if not rec or "mfma_counters" not in rec:
+        return None
+    return {k: {"busy_frac": v["mfma_busy_frac"],
+                "flop": v["mfma_flop_f16"] + v["mfma_flop_bf16"] + v["mfma_flop_f32"]}
+            for k, v in rec["mfma_counters"].items()}
 
 
 def cpu_model():
@@ -186,7 +206,8 @@ def main():
                      "alg_bytes_per_launch": alg_bytes,
                      "avg_launch_ms": round(avg_launch_ms, 4),
                      "mfma_frac_alg": round(alg_flops / (avg_launch_ms * 1e-3) / 1e12
-                                            / BF16_MFMA_PEAK_TFLOPS, 4)},
+                                            / BF16_MFMA_PEAK_TFLOPS, 4),
+                     "mfma_counters": measured_mfma("kda_chunk_fwd:T131072_H32")},
         "outputs_finite": ok,
     }
 
@@ -313,11 +334,13 @@ def main():
                                    "kda_output_rmsnorm_gate on its output"},
             "roofline": {"bound": "hbm", "kernel": "kda_chunk_fwd_ex", "achieved": round(fgbs, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(fgbs / HBM_PEAK_GBS, 4), "alg_bytes_per_launch": alg_bytes},
+                         "frac": round(fgbs / HBM_PEAK_GBS, 4), "alg_bytes_per_launch": alg_bytes,
+                         "traffic": measured_traffic("kda_chunk_fwd_ex:T131072_H32_all_forms")},
             "output_stage": {"ms": round(oms, 4), "achieved": round(ogbs, 1), "unit": "GB/s",
                              "frac": round(ogbs / HBM_PEAK_GBS, 4),
                              "kernel": "kda_output_rmsnorm_gate_kernel",
-                             "alg_bytes_per_launch": obytes}}
+                             "alg_bytes_per_launch": obytes,
+                             "traffic": measured_traffic("kda_output_rmsnorm_gate:T131072_H32")}}
         del z, bl, ogate, wgt, out_stage
 
     if not args.skip_varlen:
@@ -362,7 +385,8 @@ def main():
                                    % (lens, vtok)},
             "roofline": {"bound": "hbm", "kernel": "kda_chunk_fwd (cu_seqlens)",
                          "achieved": round(vgbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(vgbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "frac": round(vgbs / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("kda_chunk_fwd:varlen8_H32"),
                          "alg_bytes_per_launch": vbytes}}
         del d4, inp4, ws4, o4, fs4
 
@@ -414,7 +438,8 @@ def main():
             "roofline": {"bound": "alu", "kernel": "kda_bwd_prep_kernel, kda_bwd_chain_kernel, "
                          "kda_bwd_grad_kernel (fp32 VALU, operands in LDS)",
                          "achieved_hbm_gbs": round(bgbs, 2), "hbm_frac": round(bgbs / HBM_PEAK_GBS, 5),
-                         "alg_bytes_per_launch": bbytes},
+                         "alg_bytes_per_launch": bbytes,
+                         "traffic": measured_traffic("kda_chunk_bwd:T8192_H32_d128_C16")},
             "outputs_finite": bool(all(torch.isfinite(t).all().item() for t in grads.values()))}
         del qb, kb, vb, dob, gb, bb, s0b, dfb, wsb, grads
 
