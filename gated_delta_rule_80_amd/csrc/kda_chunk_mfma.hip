@@ -50,11 +50,11 @@ namespace kda {
 namespace mfma_path {
 
 constexpr int C = 64, DK = 128, DV = 128;
-#ifndef KDA_INTER_NCT
-#define KDA_INTER_NCT 1
-#endif
 #ifndef KDA_INTER_PF
 #define KDA_INTER_PF 3
+#endif
+#ifndef KDA_INTER_PF_WIDE
+#define KDA_INTER_PF_WIDE 2
 #endif
 #ifndef KDA_INTER_L2D
 #define KDA_INTER_L2D 4
@@ -62,10 +62,9 @@ constexpr int C = 64, DK = 128, DV = 128;
 #ifndef KDA_INTER_L2R
 #define KDA_INTER_L2R 4
 #endif
-constexpr int NCT = KDA_INTER_NCT;    // 16-column value tiles per inter workgroup
-constexpr int PF = KDA_INTER_PF;      // chunk records in flight per inter wave
-constexpr int DVT = 16 * NCT;         // value columns per inter workgroup
-constexpr int NTILES = DV / DVT;      // inter workgroups per (sequence, head)
+// Chunk records in flight per inter wave, for 16- and 32-column value tiles.
+template <int NCT>
+constexpr int ring_depth() { return NCT == 1 ? KDA_INTER_PF : KDA_INTER_PF_WIDE; }
 constexpr int L2D = KDA_INTER_L2D;    // L2 prefetch distance in chunks (0: no prefetch wave)
 constexpr int L2R = KDA_INTER_L2R;    // chunks a prefetch load may stay in flight
 constexpr int INTER_THREADS = L2D > 0 ? 576 : 512;   // 4 state + 4 output (+ 1 prefetch) waves
@@ -780,6 +779,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
 // S (fp16) and Z (fp16) are exchanged through LDS with two barriers per chunk.
 // Each operand fragment is reused for the NCT 16-column tiles of the workgroup,
 // and each byte of a chunk record is loaded by exactly one wave of the CU.
+template <int NCT>
 struct StateOps {
     half8 W[4], K[4];
     half4 U[NCT];
@@ -791,7 +791,8 @@ struct OutOps {
 
 // Refills are split by the step that consumes each piece, so a buffer is
 // reloaded for the chunk PF ahead right after each piece's last use.
-__device__ __forceinline__ void load_wu(StateOps &op, const uint8_t *rec, int t, int l, int vt0) {
+template <int NCT>
+__device__ __forceinline__ void load_wu(StateOps<NCT> &op, const uint8_t *rec, int t, int l, int vt0) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
         op.W[kb] = reinterpret_cast<const half8 *>(rec + REC_W)[(t * 4 + kb) * 64 + l];
@@ -799,7 +800,8 @@ __device__ __forceinline__ void load_wu(StateOps &op, const uint8_t *rec, int t,
     for (int ct = 0; ct < NCT; ++ct)
         op.U[ct] = reinterpret_cast<const half4 *>(rec + REC_U)[(t * 8 + vt0 + ct) * 64 + l];
 }
-__device__ __forceinline__ void load_kg(StateOps &op, const uint8_t *rec, int t, int l) {
+template <int NCT>
+__device__ __forceinline__ void load_kg(StateOps<NCT> &op, const uint8_t *rec, int t, int l) {
 #pragma unroll
     for (int cl = 0; cl < 2; ++cl)
 #pragma unroll
@@ -825,7 +827,8 @@ __device__ __forceinline__ void load_h(OutOps &op, const uint8_t *rec, int t, in
 }
 
 // Chunk step of a state wave (token tile / channel block t).
-__device__ __forceinline__ void state_step(float4v (&S)[2][NCT], StateOps &op, half8 *sS,
+template <int NCT>
+__device__ __forceinline__ void state_step(float4v (&S)[2][NCT], StateOps<NCT> &op, half8 *sS,
                                            half8 *sZ, int t, int l, int vt0,
                                            const uint8_t *next) {
     // S -> fp16 B-fragments of channel block t.
@@ -874,6 +877,7 @@ __device__ __forceinline__ void state_step(float4v (&S)[2][NCT], StateOps &op, h
 }
 
 // Chunk step of an output wave (token tile t): O^T = S^T Qbar^T + Z^T H^T.
+template <int NCT>
 __device__ __forceinline__ void output_step(OutOps &op, const half8 *sS, const half8 *sZ,
                                             const Chunk &ch, int H, int h, int t, int l, int vt0,
                                             const uint8_t *next, uint16_t *__restrict__ o) {
@@ -909,10 +913,13 @@ __device__ __forceinline__ void output_step(OutOps &op, const half8 *sS, const h
 // state is read from s_in (NULL = zeros) and written to s_out (NULL = not
 // written).  s_out may equal s_in: each lane reads its state elements before
 // it writes them, and no other lane touches them.
+template <int NCT>
 __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
     const int32_t *__restrict__ off, int n_pairs, int H, int row_len, int ncr,
     const int4 *__restrict__ table, int nc_max, const uint8_t *__restrict__ recs, int jlo,
     int jhi, const float *s_in, float *s_out, uint16_t *__restrict__ o) {
+    constexpr int NTILES = DV / (16 * NCT);   // workgroups per (sequence, head)
+    constexpr int PF = ring_depth<NCT>();
     __shared__ half8 sS[4 * NCT * 64];   // S as fp16 B-fragments [channel block][column tile]
     __shared__ half8 sZ[2 * NCT * 64];   // Z as fp16 B-fragments [token block][column tile]
 
@@ -964,7 +971,7 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
                     S[cl][ct][e] = s_in ? s_in[sbase + (size_t)(32 * t + 16 * cl + 4 * g4 + e) * DV +
                                                16 * (vt0 + ct) + i16]
                                         : 0.f;
-        StateOps buf[PF];
+        StateOps<NCT> buf[PF];
 #pragma unroll
         for (int j = 0; j < PF; ++j) {
             const uint8_t *rec = rbase + (size_t)min(cs + j, clast) * REC_BYTES;
@@ -1008,13 +1015,13 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
         for (; c + PF <= ce; c += PF) {
 #pragma unroll
             for (int j = 0; j < PF; ++j)
-                output_step(buf[j], sS, sZ, chunk_at(c + j, table, row_len, ncr), H, h, t, l,
+                output_step<NCT>(buf[j], sS, sZ, chunk_at(c + j, table, row_len, ncr), H, h, t, l,
                             vt0, rbase + (size_t)min(c + j + PF, clast) * REC_BYTES, o);
         }
 #pragma unroll
         for (int j = 0; j < PF - 1; ++j)
             if (c + j < ce)
-                output_step(buf[j], sS, sZ, chunk_at(c + j, table, row_len, ncr), H, h, t, l,
+                output_step<NCT>(buf[j], sS, sZ, chunk_at(c + j, table, row_len, ncr), H, h, t, l,
                             vt0, rbase + (size_t)min(c + j + PF, clast) * REC_BYTES, o);
     } else if (L2D > 0) {
         // Prefetch wave: touches this tile's share of the 128-byte lines of the
@@ -1098,15 +1105,27 @@ hipError_t launch_chunk_fwd_mfma(const ChunkProblem &p) {
     const bool varlen = p.cu != nullptr;
     const int64_t total = (int64_t)p.batch * p.seqlen;
     const WsLayout L = ws_layout(total, p.n_seqs, p.heads);
+    hipError_t e;
     uint8_t *ws = static_cast<uint8_t *>(p.workspace);
     int32_t *off = reinterpret_cast<int32_t *>(ws + L.off);
     int4 *table = varlen ? reinterpret_cast<int4 *>(ws + L.table) : nullptr;
     uint8_t *recs = ws + L.recs;
     const int ncr = (p.seqlen + C - 1) / C;
     const int n_pairs = p.n_seqs * p.heads;
-    const int inter_grid = (n_pairs + 7) / 8 * 8 * NTILES;
+    // One chain workgroup per CU is resident at a time (its nine waves hold
+    // nearly every VGPR of a SIMD), so chains beyond the CU count wait for whole
+    // earlier chains to finish.  When 16-column tiles would give more chains
+    // than CUs, 32-column tiles halve their number; each step is then slower
+    // (about 1.4 against 1.2 us per chunk), but twice as many (sequence, head)
+    // pairs advance at once.
+    int dev = 0, n_cu = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev)) !=
+        hipSuccess)
+        return e;
+    const bool wide = (int64_t)n_pairs * (DV / 16) > n_cu;
+    const int inter_grid = (n_pairs + 7) / 8 * 8 * (wide ? DV / 32 : DV / 16);
     uint16_t *o = static_cast<uint16_t *>(p.o);
-    hipError_t e;
 
     auto intra = [&](hipStream_t st, int jlo, int jn, int grid) {
         auto kern = p.gate == Gate::PerChannel ? kda_intra_kernel<Gate::PerChannel>
@@ -1120,9 +1139,10 @@ hipError_t launch_chunk_fwd_mfma(const ChunkProblem &p) {
         return hipGetLastError();
     };
     auto inter = [&](int jlo, int jhi, const float *s_in, float *s_out) {
-        hipLaunchKernelGGL(kda_inter_kernel, dim3(inter_grid), dim3(INTER_THREADS), 0, p.stream,
-                           off, n_pairs, p.heads, p.seqlen, ncr, table, (int)L.nc_max, recs, jlo,
-                           jhi, s_in, s_out, o);
+        auto kern = wide ? kda_inter_kernel<2> : kda_inter_kernel<1>;
+        hipLaunchKernelGGL(kern, dim3(inter_grid), dim3(INTER_THREADS), 0, p.stream, off, n_pairs,
+                           p.heads, p.seqlen, ncr, table, (int)L.nc_max, recs, jlo, jhi, s_in,
+                           s_out, o);
         return hipGetLastError();
     };
 

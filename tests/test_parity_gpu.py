@@ -201,6 +201,32 @@ def test_varlen_equals_separate_calls():
         assert np.array_equal(o1, o[a:b]) and np.array_equal(s1[0], fs[n])
 
 
+def test_wide_value_tiles_match_narrow_bitwise():
+    """With more (sequence, head) chains than CUs the chain kernel runs 32-column
+    value tiles instead of 16-column ones; every column sees the same operations
+    in the same order, so a packed call that takes the wide tiles gives the bits
+    of per-sequence calls that take the narrow ones."""
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    lengths = [70, 0, 129, 3, 64, 200, 1, 65]
+    H = -(-(n_cu // 8 + 1) // len(lengths))   # 8 H x 8 value tiles > n_cu chains
+    inp = small(H=H, lengths=lengths)
+    o, fs = gpu_prefill(inp, 64)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    for n in range(len(lengths)):
+        a, b = cu[n], cu[n + 1]
+        sub = dict(inp)
+        for name in ("q", "k", "v", "g", "beta"):
+            sub[name] = inp[name][:, a:b].contiguous()
+        sub["initial_state"] = inp["initial_state"][n:n + 1].contiguous()
+        sub["cu_seqlens"] = None
+        if b == a:
+            assert np.array_equal(fs[n], W.to64(inp["initial_state"][n]).astype(fs.dtype))
+            continue
+        o1, s1 = gpu_prefill(sub, 64)
+        assert np.array_equal(o1, o[a:b]) and np.array_equal(s1[0], fs[n]), n
+    check_prefill(inp, 64)
+
+
 def test_moderate_decay_near_the_old_chunk_bound():
     # per-token log-decay about -0.23: a chunk's cumulative decay near -15,
     # where a single reference row per chunk would already leave fp16's range
