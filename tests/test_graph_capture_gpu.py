@@ -59,12 +59,17 @@ def test_decode_steps_replayed_from_a_graph():
             assert torch.equal(outs[s], o_ref[s]), "replay %d step %d" % (replay, s)
 
 
-@pytest.mark.parametrize("varlen", [False, True])
-def test_prefill_replayed_from_a_graph(varlen):
+@pytest.mark.parametrize("varlen,wide", [(False, False), (True, False), (True, True)])
+def test_prefill_replayed_from_a_graph(varlen, wide):
+    """wide: enough (sequence, head) pairs that the chain kernel takes its
+    32-column value tiles (more 16-column chains than CUs)."""
     import gated_delta_rule_80_amd as K
     if varlen:
-        inp = W.make_prefill(H=2, dk=128, dv=128, dtype="bf16", z_range=(2.0, 9.0), seed=71,
-                             lengths=[0, 130, 64, 257], s0_std=0.05)
+        lengths = [0, 130, 64, 257]
+        n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+        H = -(-(n_cu // 8 + 1) // len(lengths)) if wide else 2
+        inp = W.make_prefill(H=H, dk=128, dv=128, dtype="bf16", z_range=(2.0, 9.0), seed=71,
+                             lengths=lengths, s0_std=0.05)
     else:
         inp = W.make_prefill(H=2, dk=128, dv=128, dtype="bf16", z_range=(2.0, 9.0), seed=71,
                              B=2, T=400, s0_std=0.05)
