@@ -508,6 +508,284 @@ __global__ __launch_bounds__(CT) void kda_bwd_chain_kernel(
         }
 }
 
+// ---- chain kernel on fp32 MFMA (C = 16, d = 128) ------------------------------------
+// The same two sweeps with the state tile in MFMA accumulators.  Four waves;
+// wave w owns state rows (key channels) 32w .. 32w+31 of the 16 value columns
+// as two 16x16 fp32 tiles.  v_mfma_f32_16x16x4f32: lane l gives A[l % 16][k]
+// and B[k][l % 16] and holds D rows 4 (l / 16) + e, column l % 16 (e = 0..3).
+// Step s of a contraction uses k = 4 (l / 16) + s, so an accumulator tile is
+// the B operand of the next product as it stands: S feeds Z = U - R S, Z feeds
+// S <- Diag(e^{G_C}) S + Kbar^T Z, and likewise dS', dZ in the reverse sweep.
+// Each wave forms the part of Z (dZ) over its own 32 channels; the four parts
+// meet in LDS (double-buffered, one barrier per chunk step).  The next chunk's
+// operands are loaded into registers during the current step.
+constexpr int MT = 256;   // MFMA chain kernel: one wave per SIMD
+constexpr int MC = 16, MD = 128;
+
+// Token-row values are kept as loaded (bf16 bits or fp32) and widened where
+// they are used, so that nothing waits on the next chunk's loads early.
+template <typename In> struct Raw {
+    typedef float type;
+    __device__ static float ld(const float *p, size_t i) { return p[i]; }
+    __device__ static float f(float x) { return x; }
+};
+template <> struct Raw<bf16_t> {
+    typedef unsigned short type;
+    __device__ static unsigned short ld(const bf16_t *p, size_t i) { return p[i].bits; }
+    __device__ static float f(unsigned short x) { return bf16_to_f32(x); }
+};
+template <typename In> struct FwdOps {
+    float4 r[2];     // R[i16][32w + 16cl + 4g4 .. +3]        (A of R S)
+    float kb[2][4];  // Kbar[4g4 + s][32w + 16cl + i16]      (A of Kbar^T Z)
+    float4 gc[2];    // e^{G_C}[32w + 16cl + 4g4 .. +3]
+    float4 t;        // T[i16][4g4 .. +3]                     (A of T (beta V))
+    float b[4];      // beta[4g4 + s]                          (B of T (beta V): beta V)
+    typename Raw<In>::type vr[4];   // V[4g4 + s][v0 + i16]
+    int len;         // tokens in the chunk: rows >= len count as zero
+};
+template <typename In> struct RevOps {
+    float4 kb[2];    // Kbar[i16][32w + 16cl + 4g4 .. +3]     (A of Kbar dS')
+    float qb[2][4];  // Qbar[4g4 + s][32w + 16cl + i16]       (A of Qbar^T dO)
+    float rr[2][4];  // R[4g4 + s][32w + 16cl + i16]          (A of R^T dZ)
+    float4 gc[2];
+    float h[4];      // H[4g4 + s][i16]                        (A of H^T dO)
+    typename Raw<In>::type dr[4];   // dO[4g4 + s][v0 + i16]  (B of H^T dO, Qbar^T dO)
+    int len;
+};
+
+__device__ __forceinline__ float4v mfma4(float a, float b, float4v c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float4v as4v(float4 x) { return float4v{x.x, x.y, x.z, x.w}; }
+
+template <typename In>
+__global__ __launch_bounds__(MT) void kda_bwd_chain_mfma_kernel(
+    const In *__restrict__ v, const float *__restrict__ beta, int H, int row_len,
+    const int32_t *__restrict__ cu, int n_pairs, const float *__restrict__ s0,
+    const float *__restrict__ dfinal, const In *__restrict__ dout, float *__restrict__ ds0,
+    Ws ws) {
+    constexpr int C = MC, d = MD, dd = MD * MD, cd = MC * MD;
+    __shared__ float4v sPart[2][4][64];   // [buffer][wave][lane]: one wave's part of Z or dZ
+
+    // Block id -> (pair, value tile) with the 8 tiles of a pair on one XCD.
+    const int bid = blockIdx.x, lane8 = bid & 7, rest = bid >> 3;
+    const int tile = rest & 7, pid = (rest >> 3) * 8 + lane8;
+    if (pid >= n_pairs) return;
+    const int n = pid / H, h = pid - n * H;
+    const int tid = threadIdx.x, l = tid & 63, g4 = l >> 4, i16 = l & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int v0 = tile * TV;
+    int ts, te;
+    seq_range(cu, row_len, n, ts, te);
+    const size_t pair = (size_t)pid;
+    const int nck = (te - ts + C - 1) / C;
+    const int base = chunk_base(ts, n, C);
+    // This lane's state entries: rows 32w + 16cl + 4g4 + e, column v0 + i16.
+    auto srow = [&](int cl, int e) { return 32 * w + 16 * cl + 4 * g4 + e; };
+
+    // Rows past the chunk's end are read at its last token (in bounds) and
+    // zeroed where they are used.
+    auto load_fwd = [&](int c, FwdOps<In> &op) {
+        const size_t slot = (size_t)(base + c) * H + h;
+        const int t0 = ts + c * C, len = min(C, te - t0);
+        const float *R = ws.R + slot * cd, *Kb = ws.Kb + slot * cd, *gC = ws.gC + slot * d;
+#pragma unroll
+        for (int cl = 0; cl < 2; ++cl) {
+            op.r[cl] = *reinterpret_cast<const float4 *>(R + i16 * d + srow(cl, 0));
+            op.gc[cl] = *reinterpret_cast<const float4 *>(gC + srow(cl, 0));
+#pragma unroll
+            for (int s = 0; s < 4; ++s) op.kb[cl][s] = Kb[(4 * g4 + s) * d + 32 * w + 16 * cl + i16];
+        }
+        op.t = *reinterpret_cast<const float4 *>(ws.T + slot * C * C + i16 * C + 4 * g4);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const size_t row = (size_t)(t0 + min(4 * g4 + s, len - 1)) * H + h;
+            op.b[s] = beta[row];
+            op.vr[s] = Raw<In>::ld(v, row * d + v0 + i16);
+        }
+        op.len = len;
+    };
+    auto load_rev = [&](int c, RevOps<In> &op) {
+        const size_t slot = (size_t)(base + c) * H + h;
+        const int t0 = ts + c * C, len = min(C, te - t0);
+        const float *R = ws.R + slot * cd, *Kb = ws.Kb + slot * cd, *Qb = ws.Qb + slot * cd;
+        const float *gC = ws.gC + slot * d;
+#pragma unroll
+        for (int cl = 0; cl < 2; ++cl) {
+            op.kb[cl] = *reinterpret_cast<const float4 *>(Kb + i16 * d + srow(cl, 0));
+            op.gc[cl] = *reinterpret_cast<const float4 *>(gC + srow(cl, 0));
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                op.qb[cl][s] = Qb[(4 * g4 + s) * d + 32 * w + 16 * cl + i16];
+                op.rr[cl][s] = R[(4 * g4 + s) * d + 32 * w + 16 * cl + i16];
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            op.h[s] = ws.Hm[slot * C * C + (4 * g4 + s) * C + i16];
+            op.dr[s] = Raw<In>::ld(dout, ((size_t)(t0 + min(4 * g4 + s, len - 1)) * H + h) * d +
+                                             v0 + i16);
+        }
+        op.len = len;
+    };
+    // The four waves' parts of Z (dZ) summed; buffer b alternates by chunk.
+    // The waves share nothing but LDS, so the barrier waits for LDS only and
+    // the next chunk's operand loads stay in flight across it.
+    auto exchange = [&](float4v part, int b) {
+        sPart[b][w][l] = part;
+        lds_barrier();
+        float4v z = sPart[b][0][l];
+#pragma unroll
+        for (int u = 1; u < 4; ++u) z += sPart[b][u][l];
+        return z;
+    };
+
+    float4v St[2];   // S (forward sweep), dS' (reverse sweep)
+#pragma unroll
+    for (int cl = 0; cl < 2; ++cl)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            St[cl][e] = s0 ? s0[pair * dd + (size_t)srow(cl, e) * d + v0 + i16] : 0.f;
+
+    // ---- forward sweep ----
+    auto fwd_step = [&](int c, const FwdOps<In> &op) {
+        const size_t slot = (size_t)(base + c) * H + h;
+        float *Sd = ws.S + slot * dd;
+#pragma unroll
+        for (int cl = 0; cl < 2; ++cl)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Sd[(size_t)srow(cl, e) * d + v0 + i16] = St[cl][e];
+        // this wave's part of Z: (U if w == 0) - R[:, rows of w] S[rows of w]
+        float4v p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cl = 0; cl < 2; ++cl) {
+            p = mfma4(op.r[cl].x, St[cl][0], p);
+            p = mfma4(op.r[cl].y, St[cl][1], p);
+            p = mfma4(op.r[cl].z, St[cl][2], p);
+            p = mfma4(op.r[cl].w, St[cl][3], p);
+        }
+        p = -p;
+        if (w == 0) {
+            float bv[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                bv[s] = 4 * g4 + s < op.len ? op.b[s] * Raw<In>::f(op.vr[s]) : 0.f;
+            p = mfma4(op.t.x, bv[0], p);
+            p = mfma4(op.t.y, bv[1], p);
+            p = mfma4(op.t.z, bv[2], p);
+            p = mfma4(op.t.w, bv[3], p);
+        }
+        const float4v z = exchange(p, c & 1);
+        if (w == 0) {
+            float *Zd = ws.Z + slot * cd;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Zd[(size_t)(4 * g4 + e) * d + v0 + i16] = z[e];
+        }
+        // S <- Diag(e^{G_C}) S + Kbar^T Z on this wave's rows
+#pragma unroll
+        for (int cl = 0; cl < 2; ++cl) {
+            float4v a = St[cl] * as4v(op.gc[cl]);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) a = mfma4(op.kb[cl][s], z[s], a);
+            St[cl] = a;
+        }
+    };
+    // A ring of three chunks' operands, refilled two chunks ahead.  Loads past
+    // the last chunk re-read it (in bounds, unused), so the loop has no
+    // conditional loads and the wait counts stay exact across it.
+    if (nck > 0) {
+        const int cl = nck - 1;
+        FwdOps<In> A, B, D;
+        load_fwd(0, A);
+        load_fwd(min(1, cl), B);
+        int c = 0;
+        for (; c + 3 <= nck; c += 3) {
+            load_fwd(min(c + 2, cl), D);
+            fwd_step(c, A);
+            load_fwd(min(c + 3, cl), A);
+            fwd_step(c + 1, B);
+            load_fwd(min(c + 4, cl), B);
+            fwd_step(c + 2, D);
+        }
+        if (c < nck) fwd_step(c, A);
+        if (c + 1 < nck) fwd_step(c + 1, B);
+    }
+
+    // ---- reverse sweep ----
+#pragma unroll
+    for (int cl = 0; cl < 2; ++cl)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            St[cl][e] = dfinal ? dfinal[pair * dd + (size_t)srow(cl, e) * d + v0 + i16] : 0.f;
+    auto rev_step = [&](int c, const RevOps<In> &op) {
+        const size_t slot = (size_t)(base + c) * H + h;
+        float *dSd = ws.dS + slot * dd;
+#pragma unroll
+        for (int cl = 0; cl < 2; ++cl)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dSd[(size_t)srow(cl, e) * d + v0 + i16] = St[cl][e];
+        float dO[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) dO[s] = 4 * g4 + s < op.len ? Raw<In>::f(op.dr[s]) : 0.f;
+        // this wave's part of dZ: (H^T dO if w == 0) + Kbar[:, rows of w] dS'[rows of w]
+        float4v p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cl = 0; cl < 2; ++cl) {
+            p = mfma4(op.kb[cl].x, St[cl][0], p);
+            p = mfma4(op.kb[cl].y, St[cl][1], p);
+            p = mfma4(op.kb[cl].z, St[cl][2], p);
+            p = mfma4(op.kb[cl].w, St[cl][3], p);
+        }
+        if (w == 0) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) p = mfma4(op.h[s], dO[s], p);
+        }
+        // Buffers keep alternating across the two sweeps: the forward sweep's
+        // last step (c = nck - 1) used buffer (nck - 1) & 1, so this sweep's
+        // first step, also c = nck - 1, takes the other one.
+        const float4v z = exchange(p, (c + 1) & 1);
+        if (w == 0) {
+            float *dZd = ws.dZ + slot * cd;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dZd[(size_t)(4 * g4 + e) * d + v0 + i16] = z[e];
+        }
+        // dS <- Diag(e^{G_C}) dS' + Qbar^T dO - R^T dZ on this wave's rows
+        const float4v nz = -z;
+#pragma unroll
+        for (int cl = 0; cl < 2; ++cl) {
+            float4v a = St[cl] * as4v(op.gc[cl]);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) a = mfma4(op.qb[cl][s], dO[s], a);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) a = mfma4(op.rr[cl][s], nz[s], a);
+            St[cl] = a;
+        }
+    };
+    if (nck > 0) {
+        RevOps<In> A, B, D;
+        load_rev(nck - 1, A);
+        load_rev(max(nck - 2, 0), B);
+        int c = nck - 1;
+        for (; c - 2 >= 0; c -= 3) {
+            load_rev(max(c - 2, 0), D);
+            rev_step(c, A);
+            load_rev(max(c - 3, 0), A);
+            rev_step(c - 1, B);
+            load_rev(max(c - 4, 0), B);
+            rev_step(c - 2, D);
+        }
+        if (c >= 0) rev_step(c, A);
+        if (c - 1 >= 0) rev_step(c - 1, B);
+    }
+    if (ds0) {
+#pragma unroll
+        for (int cl = 0; cl < 2; ++cl)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                ds0[pair * dd + (size_t)srow(cl, e) * d + v0 + i16] = St[cl][e];
+    }
+}
+
 // ---- gradient kernel ------------------------------------------------------------
 __host__ __device__ inline int slice_rows(int d) { return d < 16 ? d : 16; }
 
@@ -640,10 +918,17 @@ __global__ __launch_bounds__(GT) void kda_bwd_grad_kernel(
                 sdKb[x * dp + r0 + rr] = z;
             }
         }
-        for (int rr = tid; rr < SR; rr += GT) {
+        {
+            // one slice row per LPR lanes of a wave, reduced by shuffles
+            constexpr int LPR = GT / 16;
+            static_assert(LPR <= 64 && 64 % LPR == 0, "a slice row within one wave");
+            const int rr = tid / LPR, part = tid % LPR;
             float a = 0.f;
-            for (int u = 0; u < d; ++u) a += sdS[rr * dp + u] * sS[rr * dp + u];
-            sgc[r0 + rr] = fast_exp(sG[(C - 1) * dp + r0 + rr]) * a;
+            if (rr < SR)
+                for (int u = part; u < d; u += LPR) a += sdS[rr * dp + u] * sS[rr * dp + u];
+#pragma unroll
+            for (int m = LPR / 2; m >= 1; m >>= 1) a += __shfl_xor(a, m, 64);
+            if (part == 0 && rr < SR) sgc[r0 + rr] = fast_exp(sG[(C - 1) * dp + r0 + rr]) * a;
         }
         __syncthreads();
     }
@@ -805,9 +1090,16 @@ hipError_t launch_bwd_cdt(const ChunkBwdProblem &p, const bwd::Ws &ws, size_t sl
                        k, p.g, p.beta, p.scale, p.heads, p.seqlen, p.cu, p.n_seqs, ws);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((kda_bwd_chain_kernel<C, D, In>), dim3(p.n_seqs * p.heads * (D / TV)),
-                       dim3(CT), lc, p.stream, v, p.beta, p.heads, p.seqlen, p.cu, p.s0,
-                       p.dfinal, dout, p.ds0, ws);
+    if constexpr (C == MC && D == MD) {
+        const int n_pairs = p.n_seqs * p.heads;
+        hipLaunchKernelGGL((kda_bwd_chain_mfma_kernel<In>), dim3((n_pairs + 7) / 8 * 8 * (D / TV)),
+                           dim3(MT), 0, p.stream, v, p.beta, p.heads, p.seqlen, p.cu, n_pairs,
+                           p.s0, p.dfinal, dout, p.ds0, ws);
+    } else {
+        hipLaunchKernelGGL((kda_bwd_chain_kernel<C, D, In>), dim3(p.n_seqs * p.heads * (D / TV)),
+                           dim3(CT), lc, p.stream, v, p.beta, p.heads, p.seqlen, p.cu, p.s0,
+                           p.dfinal, dout, p.ds0, ws);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((kda_bwd_grad_kernel<C, D, In>), per_chunk, dim3(GT), lg, p.stream, q,

@@ -106,6 +106,16 @@ def test_backward_d128_strong_decays_without_initial_state():
     check(make(1, 37, 1, 128, seed=205, g_range=(-5.0, 0.0), s0=False), 16)
 
 
+def test_backward_d128_pairs_not_filling_groups_of_eight():
+    """9 (sequence, head) pairs: the chain kernel's last group of 8 pairs is
+    partly empty; 70 tokens are 5 chunks with a ragged tail."""
+    check(make(3, 70, 3, 128, seed=206), 16)
+
+
+def test_backward_d128_odd_and_even_chunk_counts_without_final_gradient():
+    check(make(1, 0, 3, 128, seed=207, lengths=[49, 16, 0, 33], dfin=False), 16)
+
+
 @pytest.mark.parametrize("d,C,T", [(128, 16, 45), (64, 32, 70), (16, 64, 130)])
 def test_backward_bf16_storage(d, C, T):
     check(to_bf16(make(2, T, 2, d, seed=300 + d)), C)
