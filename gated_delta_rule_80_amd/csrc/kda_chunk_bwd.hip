@@ -883,9 +883,64 @@ __global__ __launch_bounds__(GT) void kda_bwd_grad_kernel(
     cumsum_rows<C, GT>(sG, d, tid);
     __syncthreads();
 
-    // The products with S and dS', SR channel rows at a time:
+    // The products with S and dS':
     //   dR = -dZ S^T,  dQbar = dO S^T,  dKbar = Z dS'^T,  gc = e^{G_C} rowsum(dS' . S).
     const float *Sg = ws.S + wslot * dd, *dSg = ws.dS + wslot * dd;
+    if constexpr (C == 16 && D == 128) {
+        // On fp32 MFMA: wave w takes channels 16w .. 16w+15 (the output columns),
+        // token rows are the output rows, and the value index u is the
+        // reduction.  Instruction (T, s) takes u = 16T + 4 (l/16) + s from lane
+        // l, so every operand is a float4 read straight from global memory:
+        // lane l holds row l % 16 of dZ, dO and Z and row 16w + l % 16 of S and
+        // dS' (32 values each).  Rows of dO past the chunk's end are zero.
+        const int l = tid & 63, g4 = l >> 4, i16 = l & 15, w = tid >> 6;
+        const int ch = 16 * w + i16;
+        const float *Zg = ws.Z + wslot * cd, *dZg = ws.dZ + wslot * cd;
+        const size_t orow = ((size_t)(t0 + min(i16, len - 1)) * H + h) * d;
+        float4 rS[8], rdS[8], rZ[8], rdZ[8], rdO[8];
+#pragma unroll
+        for (int T = 0; T < 8; ++T) {
+            const int u = 16 * T + 4 * g4;
+            rS[T] = *reinterpret_cast<const float4 *>(Sg + (size_t)ch * d + u);
+            rdS[T] = *reinterpret_cast<const float4 *>(dSg + (size_t)ch * d + u);
+            rZ[T] = *reinterpret_cast<const float4 *>(Zg + i16 * d + u);
+            rdZ[T] = *reinterpret_cast<const float4 *>(dZg + i16 * d + u);
+            rdO[T] = ld4(dout + orow + u);
+        }
+        const bool live = i16 < len;
+        float4v aR = {0.f, 0.f, 0.f, 0.f}, aQ = aR, aK = aR;
+        float gsum = 0.f;
+#pragma unroll
+        for (int T = 0; T < 8; ++T) {
+            const float4 o4 = live ? rdO[T] : make_float4(0.f, 0.f, 0.f, 0.f);
+            aR = mfma4(rdZ[T].x, rS[T].x, aR);
+            aR = mfma4(rdZ[T].y, rS[T].y, aR);
+            aR = mfma4(rdZ[T].z, rS[T].z, aR);
+            aR = mfma4(rdZ[T].w, rS[T].w, aR);
+            aQ = mfma4(o4.x, rS[T].x, aQ);
+            aQ = mfma4(o4.y, rS[T].y, aQ);
+            aQ = mfma4(o4.z, rS[T].z, aQ);
+            aQ = mfma4(o4.w, rS[T].w, aQ);
+            aK = mfma4(rZ[T].x, rdS[T].x, aK);
+            aK = mfma4(rZ[T].y, rdS[T].y, aK);
+            aK = mfma4(rZ[T].z, rdS[T].z, aK);
+            aK = mfma4(rZ[T].w, rdS[T].w, aK);
+            gsum += rdS[T].x * rS[T].x + rdS[T].y * rS[T].y + rdS[T].z * rS[T].z +
+                    rdS[T].w * rS[T].w;
+        }
+        // accumulator element e: token 4 (l/16) + e, channel ch
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int x = 4 * g4 + e;
+            sdR[x * dp + ch] = -aR[e];
+            sdQb[x * dp + ch] = aQ[e];
+            sdKb[x * dp + ch] = aK[e];
+        }
+        gsum += __shfl_xor(gsum, 16, 64);
+        gsum += __shfl_xor(gsum, 32, 64);
+        if (g4 == 0) sgc[ch] = fast_exp(sG[(C - 1) * dp + ch]) * gsum;
+        __syncthreads();
+    } else {
     Rows<GT> rS, rdS;
     fetch_rows(rS, Sg, d, SR, SR, d, tid);
     fetch_rows(rdS, dSg, d, SR, SR, d, tid);
@@ -932,6 +987,7 @@ __global__ __launch_bounds__(GT) void kda_bwd_grad_kernel(
         }
         __syncthreads();
     }
+    }
     // dT = dZ (BV)^T + dR (BL)^T;  dH = dO Z^T (j <= i)
     for (int e = tid / PS; e < C * C; e += GT / PS) {
         const int i = e / C, j = e - i * C, part = tid % PS;
@@ -973,13 +1029,18 @@ __global__ __launch_bounds__(GT) void kda_bwd_grad_kernel(
         sM1[e] = a;
     }
     __syncthreads();
-    // dbeta_j = dBV_j . v_j + dBL_j . L_j
-    for (int j = tid; j < C; j += GT) {
+    // dbeta_j = dBV_j . v_j + dBL_j . L_j, row j over GT / C lanes of one wave
+    {
+        constexpr int LPR = GT / C;
+        static_assert(LPR <= 64 && 64 % LPR == 0, "a row within one wave");
+        const int j = tid / LPR, part = tid % LPR;
         float s = 0.f;
-        for (int c2 = 0; c2 < d; ++c2)
+        for (int c2 = part; c2 < d; c2 += LPR)
             s += sdBV[j * dp + c2] * sv[j * dp + c2] +
                  sdL[j * dp + c2] * sk[j * dp + c2] * fast_exp(sG[j * dp + c2]);
-        sdb[j] = s;
+#pragma unroll
+        for (int m = LPR / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
+        if (part == 0) sdb[j] = s;
     }
     // dA = M1 T^T (strictly lower); dA . K~ into dT's storage (dT is consumed);
     // dK~_ij = -beta_i dA_ij in place of K~
