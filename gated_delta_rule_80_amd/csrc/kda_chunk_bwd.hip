@@ -806,10 +806,18 @@ __host__ __device__ inline GradLds grad_layout(int d, int C) {
     L.dZ = o; o += cd;
     L.dR = o; o += cd;    // later dG
     L.dL = o; o += cd;
-    L.dQb = o; o += cd;   // dL/dQbar = dO S^T
-    L.dKb = o; o += cd;   // dL/dKbar = Z dS'^T
-    L.Ssl = o; o += sd;   // rows of S
-    L.dSsl = o; o += sd;  // rows of dS'
+    if (d == 128 && C == 16) {
+        // Products on MFMA: no slices of S and dS' in LDS, and dQbar, dKbar
+        // wait in accumulators until v and Z are dead, then take their place.
+        L.dQb = L.v;
+        L.dKb = L.Z;
+        L.Ssl = L.dSsl = 0;
+    } else {
+        L.dQb = o; o += cd;   // dL/dQbar = dO S^T
+        L.dKb = o; o += cd;   // dL/dKbar = Z dS'^T
+        L.Ssl = o; o += sd;   // rows of S
+        L.dSsl = o; o += sd;  // rows of dS'
+    }
     L.beta = o; o += C;
     L.dbeta = o; o += C;
     L.Kt = o; o += cc;    // K~, later its gradient
@@ -886,56 +894,43 @@ __global__ __launch_bounds__(GT) void kda_bwd_grad_kernel(
     // The products with S and dS':
     //   dR = -dZ S^T,  dQbar = dO S^T,  dKbar = Z dS'^T,  gc = e^{G_C} rowsum(dS' . S).
     const float *Sg = ws.S + wslot * dd, *dSg = ws.dS + wslot * dd;
+    // At d = 128, C = 16 (fp32 MFMA): wave w takes channels 16w .. 16w+15 (the
+    // output columns), token rows are the output rows, and the value index u is
+    // the reduction.  Instruction (T, s) takes u = 16T + 4 (l/16) + s from lane
+    // l: its rows 16w + l % 16 of S and dS' are float4 reads from global
+    // memory (32 values each), rows l % 16 of dZ, dO and Z come from LDS.
+    // dQbar and dKbar stay in accumulators until v and Z are dead.
+    float4v aQ = {0.f, 0.f, 0.f, 0.f}, aK = aQ;
     if constexpr (C == 16 && D == 128) {
-        // On fp32 MFMA: wave w takes channels 16w .. 16w+15 (the output columns),
-        // token rows are the output rows, and the value index u is the
-        // reduction.  Instruction (T, s) takes u = 16T + 4 (l/16) + s from lane
-        // l, so every operand is a float4 read straight from global memory:
-        // lane l holds row l % 16 of dZ, dO and Z and row 16w + l % 16 of S and
-        // dS' (32 values each).  Rows of dO past the chunk's end are zero.
         const int l = tid & 63, g4 = l >> 4, i16 = l & 15, w = tid >> 6;
         const int ch = 16 * w + i16;
-        const float *Zg = ws.Z + wslot * cd, *dZg = ws.dZ + wslot * cd;
-        const size_t orow = ((size_t)(t0 + min(i16, len - 1)) * H + h) * d;
-        float4 rS[8], rdS[8], rZ[8], rdZ[8], rdO[8];
+        float4 rS[8], rdS[8];
 #pragma unroll
         for (int T = 0; T < 8; ++T) {
             const int u = 16 * T + 4 * g4;
             rS[T] = *reinterpret_cast<const float4 *>(Sg + (size_t)ch * d + u);
             rdS[T] = *reinterpret_cast<const float4 *>(dSg + (size_t)ch * d + u);
-            rZ[T] = *reinterpret_cast<const float4 *>(Zg + i16 * d + u);
-            rdZ[T] = *reinterpret_cast<const float4 *>(dZg + i16 * d + u);
-            rdO[T] = ld4(dout + orow + u);
         }
-        const bool live = i16 < len;
-        float4v aR = {0.f, 0.f, 0.f, 0.f}, aQ = aR, aK = aR;
+        float4v aR = {0.f, 0.f, 0.f, 0.f};
         float gsum = 0.f;
+        const float *zr = sZ + i16 * dp + 4 * g4, *dzr = sdZ + i16 * dp + 4 * g4;
+        const float *dor = sdO + i16 * dp + 4 * g4;
 #pragma unroll
         for (int T = 0; T < 8; ++T) {
-            const float4 o4 = live ? rdO[T] : make_float4(0.f, 0.f, 0.f, 0.f);
-            aR = mfma4(rdZ[T].x, rS[T].x, aR);
-            aR = mfma4(rdZ[T].y, rS[T].y, aR);
-            aR = mfma4(rdZ[T].z, rS[T].z, aR);
-            aR = mfma4(rdZ[T].w, rS[T].w, aR);
-            aQ = mfma4(o4.x, rS[T].x, aQ);
-            aQ = mfma4(o4.y, rS[T].y, aQ);
-            aQ = mfma4(o4.z, rS[T].z, aQ);
-            aQ = mfma4(o4.w, rS[T].w, aQ);
-            aK = mfma4(rZ[T].x, rdS[T].x, aK);
-            aK = mfma4(rZ[T].y, rdS[T].y, aK);
-            aK = mfma4(rZ[T].z, rdS[T].z, aK);
-            aK = mfma4(rZ[T].w, rdS[T].w, aK);
-            gsum += rdS[T].x * rS[T].x + rdS[T].y * rS[T].y + rdS[T].z * rS[T].z +
-                    rdS[T].w * rS[T].w;
+            const float s4[4] = {rS[T].x, rS[T].y, rS[T].z, rS[T].w};
+            const float ds4[4] = {rdS[T].x, rdS[T].y, rdS[T].z, rdS[T].w};
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+                const int u = 16 * T + s2;
+                aR = mfma4(dzr[u], s4[s2], aR);
+                aQ = mfma4(dor[u], s4[s2], aQ);
+                aK = mfma4(zr[u], ds4[s2], aK);
+                gsum += ds4[s2] * s4[s2];
+            }
         }
         // accumulator element e: token 4 (l/16) + e, channel ch
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int x = 4 * g4 + e;
-            sdR[x * dp + ch] = -aR[e];
-            sdQb[x * dp + ch] = aQ[e];
-            sdKb[x * dp + ch] = aK[e];
-        }
+        for (int e = 0; e < 4; ++e) sdR[(4 * g4 + e) * dp + ch] = -aR[e];
         gsum += __shfl_xor(gsum, 16, 64);
         gsum += __shfl_xor(gsum, 32, 64);
         if (g4 == 0) sgc[ch] = fast_exp(sG[(C - 1) * dp + ch]) * gsum;
@@ -1054,6 +1049,15 @@ __global__ __launch_bounds__(GT) void kda_bwd_grad_kernel(
     }
     __syncthreads();
     // dv = beta dBV;  dL = beta dBL (in place);  dbeta_i -= sum_j dA_ij K~_ij
+    if constexpr (C == 16 && D == 128) {
+        // dQbar and dKbar into the storage of v and Z, which are dead now
+        const int l = tid & 63, g4 = l >> 4, ch = 16 * (tid >> 6) + (l & 15);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sdQb[(4 * g4 + e) * dp + ch] = aQ[e];
+            sdKb[(4 * g4 + e) * dp + ch] = aK[e];
+        }
+    }
     for (int e = tid; e < cd; e += GT) {
         const int j = e / d, a = j * dp + (e - j * d);
         if (j < len) dv[((size_t)(t0 + j) * H + h) * d + (e - j * d)] = sb[j] * sdBV[a];
