@@ -538,9 +538,9 @@ template <typename In> struct FwdOps {
     float4 r[2];     // R[i16][32w + 16cl + 4g4 .. +3]        (A of R S)
     float kb[2][4];  // Kbar[4g4 + s][32w + 16cl + i16]      (A of Kbar^T Z)
     float4 gc[2];    // e^{G_C}[32w + 16cl + 4g4 .. +3]
-    float4 t;        // T[i16][4g4 .. +3]                     (A of T (beta V))
-    float b[4];      // beta[4g4 + s]                          (B of T (beta V): beta V)
-    typename Raw<In>::type vr[4];   // V[4g4 + s][v0 + i16]
+    float t;         // T[i16][4g4 + w]                       (A of T (beta V), step w)
+    float b;         // beta[4g4 + w]                          (B of T (beta V): beta V)
+    typename Raw<In>::type vr;      // V[4g4 + w][v0 + i16]
     int len;         // tokens in the chunk: rows >= len count as zero
 };
 template <typename In> struct RevOps {
@@ -548,7 +548,7 @@ template <typename In> struct RevOps {
     float qb[2][4];  // Qbar[4g4 + s][32w + 16cl + i16]       (A of Qbar^T dO)
     float rr[2][4];  // R[4g4 + s][32w + 16cl + i16]          (A of R^T dZ)
     float4 gc[2];
-    float h[4];      // H[4g4 + s][i16]                        (A of H^T dO)
+    float h;         // H[4g4 + w][i16]                        (A of H^T dO, step w)
     typename Raw<In>::type dr[4];   // dO[4g4 + s][v0 + i16]  (B of H^T dO, Qbar^T dO)
     int len;
 };
@@ -596,13 +596,11 @@ __global__ __launch_bounds__(MT) void kda_bwd_chain_mfma_kernel(
 #pragma unroll
             for (int s = 0; s < 4; ++s) op.kb[cl][s] = Kb[(4 * g4 + s) * d + 32 * w + 16 * cl + i16];
         }
-        op.t = *reinterpret_cast<const float4 *>(ws.T + slot * C * C + i16 * C + 4 * g4);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const size_t row = (size_t)(t0 + min(4 * g4 + s, len - 1)) * H + h;
-            op.b[s] = beta[row];
-            op.vr[s] = Raw<In>::ld(v, row * d + v0 + i16);
-        }
+        // T (beta V) is split over the waves by reduction step: wave w takes k = 4g4 + w
+        op.t = ws.T[slot * C * C + i16 * C + 4 * g4 + w];
+        const size_t row = (size_t)(t0 + min(4 * g4 + w, len - 1)) * H + h;
+        op.b = beta[row];
+        op.vr = Raw<In>::ld(v, row * d + v0 + i16);
         op.len = len;
     };
     auto load_rev = [&](int c, RevOps<In> &op) {
@@ -620,14 +618,22 @@ __global__ __launch_bounds__(MT) void kda_bwd_chain_mfma_kernel(
                 op.rr[cl][s] = R[(4 * g4 + s) * d + 32 * w + 16 * cl + i16];
             }
         }
+        op.h = ws.Hm[slot * C * C + (4 * g4 + w) * C + i16];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            op.h[s] = ws.Hm[slot * C * C + (4 * g4 + s) * C + i16];
+        for (int s = 0; s < 4; ++s)
             op.dr[s] = Raw<In>::ld(dout, ((size_t)(t0 + min(4 * g4 + s, len - 1)) * H + h) * d +
                                              v0 + i16);
-        }
         op.len = len;
     };
+    // This wave's state rows (32w + 16cl + 4g4 + e, column v0 + i16) to dst.
+    auto store_tile = [&](const float4v (&x)[2], float *dst) {
+#pragma unroll
+        for (int cl = 0; cl < 2; ++cl)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[(size_t)srow(cl, e) * d + v0 + i16] = x[cl][e];
+    };
+    // Element w of a 4-vector (w is uniform; no register indexing).
+    auto pick = [&](const float4v &x) { return w == 0 ? x[0] : w == 1 ? x[1] : w == 2 ? x[2] : x[3]; };
     // The four waves' parts of Z (dZ) summed; buffer b alternates by chunk.
     // The waves share nothing but LDS, so the barrier waits for LDS only and
     // the next chunk's operand loads stay in flight across it.
@@ -650,12 +656,8 @@ __global__ __launch_bounds__(MT) void kda_bwd_chain_mfma_kernel(
     // ---- forward sweep ----
     auto fwd_step = [&](int c, const FwdOps<In> &op) {
         const size_t slot = (size_t)(base + c) * H + h;
-        float *Sd = ws.S + slot * dd;
-#pragma unroll
-        for (int cl = 0; cl < 2; ++cl)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Sd[(size_t)srow(cl, e) * d + v0 + i16] = St[cl][e];
-        // this wave's part of Z: (U if w == 0) - R[:, rows of w] S[rows of w]
+        store_tile(St, ws.S + slot * dd);
+        // this wave's part of Z: -R[:, rows of w] S[rows of w], plus step w of U
         float4v p = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int cl = 0; cl < 2; ++cl) {
@@ -665,22 +667,11 @@ __global__ __launch_bounds__(MT) void kda_bwd_chain_mfma_kernel(
             p = mfma4(op.r[cl].w, St[cl][3], p);
         }
         p = -p;
-        if (w == 0) {
-            float bv[4];
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                bv[s] = 4 * g4 + s < op.len ? op.b[s] * Raw<In>::f(op.vr[s]) : 0.f;
-            p = mfma4(op.t.x, bv[0], p);
-            p = mfma4(op.t.y, bv[1], p);
-            p = mfma4(op.t.z, bv[2], p);
-            p = mfma4(op.t.w, bv[3], p);
-        }
+        // reduction step w of U = T (beta V)
+        p = mfma4(op.t, 4 * g4 + w < op.len ? op.b * Raw<In>::f(op.vr) : 0.f, p);
         const float4v z = exchange(p, c & 1);
-        if (w == 0) {
-            float *Zd = ws.Z + slot * cd;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Zd[(size_t)(4 * g4 + e) * d + v0 + i16] = z[e];
-        }
+        // every wave stores one token row of each lane group: 4g4 + w
+        ws.Z[slot * cd + (size_t)(4 * g4 + w) * d + v0 + i16] = pick(z);
         // S <- Diag(e^{G_C}) S + Kbar^T Z on this wave's rows
 #pragma unroll
         for (int cl = 0; cl < 2; ++cl) {
@@ -690,9 +681,10 @@ __global__ __launch_bounds__(MT) void kda_bwd_chain_mfma_kernel(
             St[cl] = a;
         }
     };
-    // A ring of three chunks' operands, refilled two chunks ahead.  Loads past
-    // the last chunk re-read it (in bounds, unused), so the loop has no
-    // conditional loads and the wait counts stay exact across it.
+    // A ring of three chunks' operands, refilled two chunks ahead (a fourth
+    // slot measured no faster).  Loads past the last chunk re-read it (in
+    // bounds, unused), so the loop has no conditional loads and the wait
+    // counts stay exact across it.
     if (nck > 0) {
         const int cl = nck - 1;
         FwdOps<In> A, B, D;
@@ -719,15 +711,11 @@ __global__ __launch_bounds__(MT) void kda_bwd_chain_mfma_kernel(
             St[cl][e] = dfinal ? dfinal[pair * dd + (size_t)srow(cl, e) * d + v0 + i16] : 0.f;
     auto rev_step = [&](int c, const RevOps<In> &op) {
         const size_t slot = (size_t)(base + c) * H + h;
-        float *dSd = ws.dS + slot * dd;
-#pragma unroll
-        for (int cl = 0; cl < 2; ++cl)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dSd[(size_t)srow(cl, e) * d + v0 + i16] = St[cl][e];
+        store_tile(St, ws.dS + slot * dd);
         float dO[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) dO[s] = 4 * g4 + s < op.len ? Raw<In>::f(op.dr[s]) : 0.f;
-        // this wave's part of dZ: (H^T dO if w == 0) + Kbar[:, rows of w] dS'[rows of w]
+        // this wave's part of dZ: Kbar[:, rows of w] dS'[rows of w], plus step w of H^T dO
         float4v p = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int cl = 0; cl < 2; ++cl) {
@@ -736,19 +724,13 @@ __global__ __launch_bounds__(MT) void kda_bwd_chain_mfma_kernel(
             p = mfma4(op.kb[cl].z, St[cl][2], p);
             p = mfma4(op.kb[cl].w, St[cl][3], p);
         }
-        if (w == 0) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) p = mfma4(op.h[s], dO[s], p);
-        }
+        // reduction step w of H^T dO
+        p = mfma4(op.h, w == 0 ? dO[0] : w == 1 ? dO[1] : w == 2 ? dO[2] : dO[3], p);
         // Buffers keep alternating across the two sweeps: the forward sweep's
         // last step (c = nck - 1) used buffer (nck - 1) & 1, so this sweep's
         // first step, also c = nck - 1, takes the other one.
         const float4v z = exchange(p, (c + 1) & 1);
-        if (w == 0) {
-            float *dZd = ws.dZ + slot * cd;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dZd[(size_t)(4 * g4 + e) * d + v0 + i16] = z[e];
-        }
+        ws.dZ[slot * cd + (size_t)(4 * g4 + w) * d + v0 + i16] = pick(z);
         // dS <- Diag(e^{G_C}) dS' + Qbar^T dO - R^T dZ on this wave's rows
         const float4v nz = -z;
 #pragma unroll
