@@ -317,8 +317,9 @@ __host__ __device__ inline ChainLds chain_layout(int d, int C) {
 template <int C, int D, typename In>
 __global__ __launch_bounds__(CT) void kda_bwd_chain_kernel(
     const In *__restrict__ v, const float *__restrict__ beta, int H, int row_len,
-    const int32_t *__restrict__ cu, const float *__restrict__ s0, const float *__restrict__ dfinal,
-    const In *__restrict__ dout, float *__restrict__ ds0, Ws ws) {
+    const int32_t *__restrict__ cu, int n_pairs, const float *__restrict__ s0,
+    const float *__restrict__ dfinal, const In *__restrict__ dout, float *__restrict__ ds0,
+    Ws ws) {
     constexpr int d = D;
     constexpr int NCC = (C * C + CT - 1) / CT;       // T / H entries per thread
     constexpr int NVT = (C * TV + CT - 1) / CT;      // v or dO tile entries per thread
@@ -330,8 +331,12 @@ __global__ __launch_bounds__(CT) void kda_bwd_chain_kernel(
     float *sR = sm + L.R, *sKb = sm + L.Kb, *sQb = sm + L.Qb, *sT = sm + L.T, *sHm = sm + L.Hm;
     float *sb = sm + L.beta, *sgC = sm + L.gC, *svt = sm + L.vt, *szt = sm + L.zt, *sA = sm + L.A;
 
+    // Block id -> (pair, value tile) with the tiles of a pair on one XCD
+    // (consecutive ids go round-robin over the 8 XCDs), so they share its L2.
     const int nt = d / TV;
-    const int pid = blockIdx.x / nt, tile = blockIdx.x - pid * nt;
+    const int lane8 = blockIdx.x & 7, rest = blockIdx.x >> 3;
+    const int tile = rest % nt, pid = (rest / nt) * 8 + lane8;
+    if (pid >= n_pairs) return;
     const int n = pid / H, h = pid - n * H;
     const int v0 = tile * TV, tid = threadIdx.x;
     const int dd = d * d, dt = d * TV, ct = C * TV, cd = C * d, dp = row_stride(d);
@@ -1143,9 +1148,10 @@ hipError_t launch_bwd_cdt(const ChunkBwdProblem &p, const bwd::Ws &ws, size_t sl
                            dim3(MT), 0, p.stream, v, p.beta, p.heads, p.seqlen, p.cu, n_pairs,
                            p.s0, p.dfinal, dout, p.ds0, ws);
     } else {
-        hipLaunchKernelGGL((kda_bwd_chain_kernel<C, D, In>), dim3(p.n_seqs * p.heads * (D / TV)),
-                           dim3(CT), lc, p.stream, v, p.beta, p.heads, p.seqlen, p.cu, p.s0,
-                           p.dfinal, dout, p.ds0, ws);
+        const int n_pairs = p.n_seqs * p.heads;
+        hipLaunchKernelGGL((kda_bwd_chain_kernel<C, D, In>), dim3((n_pairs + 7) / 8 * 8 * (D / TV)),
+                           dim3(CT), lc, p.stream, v, p.beta, p.heads, p.seqlen, p.cu, n_pairs,
+                           p.s0, p.dfinal, dout, p.ds0, ws);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
