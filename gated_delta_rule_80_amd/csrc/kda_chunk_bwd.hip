@@ -971,24 +971,62 @@ __global__ __launch_bounds__(GT) void kda_bwd_grad_kernel(
     }
     }
     // dT = dZ (BV)^T + dR (BL)^T;  dH = dO Z^T (j <= i)
-    for (int e = tid / PS; e < C * C; e += GT / PS) {
-        const int i = e / C, j = e - i * C, part = tid % PS;
-        const int c0 = part * (d / PS), c1 = (part + 1) * (d / PS);
-        float a = 0.f, hh = 0.f;
-#pragma unroll 4
-        for (int c2 = c0; c2 < c1; ++c2)
-            a += sdZ[i * dp + c2] * sv[j * dp + c2] +
-                 sdR[i * dp + c2] * sk[j * dp + c2] * fast_exp(sG[j * dp + c2]);
-        if (j <= i)
-#pragma unroll 4
-            for (int c2 = c0; c2 < c1; ++c2) hh += sdO[i * dp + c2] * sZ[j * dp + c2];
-        if (PS == 2) {
-            a += __shfl_xor(a, 1);
-            hh += __shfl_xor(hh, 1);
+    if constexpr (C == 16 && D == 128) {
+        // On fp32 MFMA, one 16 x 16 tile each: waves 0-3 take dT, waves 4-7 dH,
+        // each wave 32 of the 128 channels (the reduction).  Lane l gives row
+        // l % 16 of both operands at channel 32 (w % 4) + 4 (l/16) + s in step
+        // s; L = k e^{G} is formed on the fly.  The four parts of each tile meet
+        // in dL's storage, which is written only in the next phase.
+        const int l = tid & 63, g4 = l >> 4, i16 = l & 15, w = tid >> 6;
+        const int cb0 = 32 * (w & 3) + 4 * g4, r = i16 * dp;
+        float4v acc = {0.f, 0.f, 0.f, 0.f};
+        if (w < 4) {
+#pragma unroll
+            for (int t8 = 0; t8 < 8; ++t8) {
+                const int c2 = cb0 + 16 * (t8 >> 2) + (t8 & 3);
+                acc = mfma4(sdZ[r + c2], sv[r + c2], acc);
+                acc = mfma4(sdR[r + c2], sk[r + c2] * fast_exp(sG[r + c2]), acc);
+            }
+        } else {
+#pragma unroll
+            for (int t8 = 0; t8 < 8; ++t8) {
+                const int c2 = cb0 + 16 * (t8 >> 2) + (t8 & 3);
+                acc = mfma4(sdO[r + c2], sZ[r + c2], acc);
+            }
         }
-        if (part == 0) {
-            sdT[e] = sb[j] * a;
-            sHm[e] = hh;
+        // accumulator element e: row i = 4 (l/16) + e, column j = l % 16
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sdL[w * C * C + (4 * g4 + e) * C + i16] = acc[e];
+        __syncthreads();
+        {
+            const int which = tid / (C * C), e = tid - which * (C * C);
+            const int i = e / C, j = e - i * C;
+            float a = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < 4; ++ww) a += sdL[(4 * which + ww) * C * C + e];
+            if (which == 0) sdT[e] = sb[j] * a;
+            else sHm[e] = j <= i ? a : 0.f;
+        }
+    } else {
+        for (int e = tid / PS; e < C * C; e += GT / PS) {
+            const int i = e / C, j = e - i * C, part = tid % PS;
+            const int c0 = part * (d / PS), c1 = (part + 1) * (d / PS);
+            float a = 0.f, hh = 0.f;
+#pragma unroll 4
+            for (int c2 = c0; c2 < c1; ++c2)
+                a += sdZ[i * dp + c2] * sv[j * dp + c2] +
+                     sdR[i * dp + c2] * sk[j * dp + c2] * fast_exp(sG[j * dp + c2]);
+            if (j <= i)
+#pragma unroll 4
+                for (int c2 = c0; c2 < c1; ++c2) hh += sdO[i * dp + c2] * sZ[j * dp + c2];
+            if (PS == 2) {
+                a += __shfl_xor(a, 1);
+                hh += __shfl_xor(hh, 1);
+            }
+            if (part == 0) {
+                sdT[e] = sb[j] * a;
+                sHm[e] = hh;
+            }
         }
     }
     __syncthreads();
