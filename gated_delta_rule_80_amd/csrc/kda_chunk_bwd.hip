@@ -1030,23 +1030,53 @@ __global__ __launch_bounds__(GT) void kda_bwd_grad_kernel(
         }
     }
     __syncthreads();
-    // dBV = T^T dZ (into dO's storage), dBL = T^T dR
-    for (int e = tid; e < cd; e += GT) {
-        const int j = e / d, c2 = e - j * d;
-        float bv = 0.f, bl = 0.f;
-        for (int i = j; i < C; ++i) {
-            bv += sT[i * C + j] * sdZ[i * dp + c2];
-            bl += sT[i * C + j] * sdR[i * dp + c2];
+    // dBV = T^T dZ (into dO's storage), dBL = T^T dR;  M1 = T^T dT
+    if constexpr (C == 16 && D == 128) {
+        // On fp32 MFMA with the C tokens as the reduction: wave w takes channel
+        // tile w of dBV and dBL, wave 0 also M1.  Lane l gives T[4 (l/16) + s][l % 16]
+        // (A, transposed) and row 4 (l/16) + s of dZ, dR or dT (B) in step s.
+        const int l = tid & 63, g4 = l >> 4, i16 = l & 15, w = tid >> 6;
+        const int cc = 16 * w + i16;
+        float4v bv = {0.f, 0.f, 0.f, 0.f}, bl = bv;
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+            const int i = 4 * g4 + s2;
+            const float t = sT[i * C + i16];
+            bv = mfma4(t, sdZ[i * dp + cc], bv);
+            bl = mfma4(t, sdR[i * dp + cc], bl);
         }
-        sdBV[j * dp + c2] = bv;
-        sdL[j * dp + c2] = bl;
-    }
-    // M1 = T^T dT
-    for (int e = tid; e < C * C; e += GT) {
-        const int i = e / C, j = e - i * C;
-        float a = 0.f;
-        for (int m = i; m < C; ++m) a += sT[m * C + i] * sdT[m * C + j];
-        sM1[e] = a;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sdBV[(4 * g4 + e) * dp + cc] = bv[e];
+            sdL[(4 * g4 + e) * dp + cc] = bl[e];
+        }
+        if (w == 0) {
+            float4v m1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+                const int i = 4 * g4 + s2;
+                m1 = mfma4(sT[i * C + i16], sdT[i * C + i16], m1);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sM1[(4 * g4 + e) * C + i16] = m1[e];
+        }
+    } else {
+        for (int e = tid; e < cd; e += GT) {
+            const int j = e / d, c2 = e - j * d;
+            float bv = 0.f, bl = 0.f;
+            for (int i = j; i < C; ++i) {
+                bv += sT[i * C + j] * sdZ[i * dp + c2];
+                bl += sT[i * C + j] * sdR[i * dp + c2];
+            }
+            sdBV[j * dp + c2] = bv;
+            sdL[j * dp + c2] = bl;
+        }
+        for (int e = tid; e < C * C; e += GT) {
+            const int i = e / C, j = e - i * C;
+            float a = 0.f;
+            for (int m = i; m < C; ++m) a += sT[m * C + i] * sdT[m * C + j];
+            sM1[e] = a;
+        }
     }
     __syncthreads();
     // dbeta_j = dBV_j . v_j + dBL_j . L_j, row j over GT / C lanes of one wave
