@@ -754,9 +754,20 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
 
     // ---- stage 6: T Diag(beta) to fp16, then W^T = L^T (T B)^T and U = (T B) V -------
     _Float16 *sT16 = reinterpret_cast<_Float16 *>(smem + L_T16);
-    for (int e = tid; e < C * C; e += 256) {
-        const int i = e >> 6, jj = e & 63;
-        sT16[i * TP + jj] = (_Float16)((jj <= i) ? sTf[i * AP + jj] * sBeta[jj] : 0.f);
+    {
+        // thread: row i, columns j0 .. j0+15; all reads before the two 16-byte writes
+        const int i = tid >> 2, j0 = 16 * (tid & 3);
+        float tv[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) tv[j] = sTf[i * AP + j0 + j];
+        half8 h0, h1;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            h0[j] = (_Float16)((j0 + j <= i) ? tv[j] * sBeta[j0 + j] : 0.f);
+            h1[j] = (_Float16)((j0 + 8 + j <= i) ? tv[8 + j] * sBeta[j0 + 8 + j] : 0.f);
+        }
+        *reinterpret_cast<half8 *>(sT16 + i * TP + j0) = h0;
+        *reinterpret_cast<half8 *>(sT16 + i * TP + j0 + 8) = h1;
     }
     lds_barrier();
 #pragma unroll
