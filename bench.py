@@ -126,8 +126,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build runs the whole KDA path on a single "
-              "MI355X (no sharding or collectives); --gpus %d is not supported" % args.gpus,
+        print("bench.py measures one GPU only: the whole KDA path runs on a single MI355X "
+              "(no sharding or collectives); --gpus %d is not supported" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
 
