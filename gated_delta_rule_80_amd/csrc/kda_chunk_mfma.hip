@@ -137,48 +137,59 @@ __device__ __forceinline__ float row_scan16(float x) {
 // sequences and at most T / C + N chunks: every later access stays in bounds.
 // For a valid cu_seqlens (starting at 0, non-decreasing, ending at T) b' = cu.
 // ------------------------------------------------------------------------------------
+// Exclusive scan over the 1024 threads of the workgroup, by sum or by max
+// (inputs >= 0, so 0 is the identity of both); also returns the total.
+template <bool MAX>
+__device__ __forceinline__ int block_exclusive_scan(int x, int *s_wave, int &total) {
+    auto op = [](int a, int b) { return MAX ? max(a, b) : a + b; };
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    int incl = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl = op(incl, y);
+    }
+    const int prev = __shfl_up(incl, 1, 64);
+    if (lane == 63) s_wave[w] = incl;
+    __syncthreads();
+    if (w == 0) {
+        int v = lane < 16 ? s_wave[lane] : 0;
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            const int y = __shfl_up(v, o, 64);
+            if (lane >= o) v = op(v, y);
+        }
+        if (lane < 16) s_wave[16 + lane] = v;   // inclusive over waves 0..lane
+    }
+    __syncthreads();
+    total = s_wave[31];
+    const int before = w == 0 ? 0 : s_wave[16 + w - 1];
+    const int r = op(before, lane == 0 ? 0 : prev);
+    __syncthreads();   // s_wave is reused by the next scan
+    return r;
+}
+
 __global__ __launch_bounds__(1024) void kda_chunk_index_kernel(const int32_t *__restrict__ cu,
                                                                int n_seqs, int total_tokens,
                                                                int32_t *__restrict__ off,
                                                                int4 *__restrict__ table) {
-    __shared__ int s_max[1024], s_cnt[1024];
+    __shared__ int s_wave[32];
     const int t = threadIdx.x;
     const int per = (n_seqs + 1023) / 1024;
     const int s0 = min(n_seqs, t * per), s1 = min(n_seqs, s0 + per);
     auto clampT = [&](int x) { return min(total_tokens, max(0, x)); };
     int mx = 0;
     for (int n = s0; n < s1; ++n) mx = max(mx, clampT(cu[n + 1]));
-    s_max[t] = mx;
-    __syncthreads();
-    if (t == 0) {
-        int run = 0;
-        for (int i = 0; i < 1024; ++i) {
-            const int x = s_max[i];
-            s_max[i] = run;
-            run = max(run, x);
-        }
-    }
-    __syncthreads();
-    const int start = s_max[t];   // b'_{s0}
+    int tot;
+    const int start = block_exclusive_scan<true>(mx, s_wave, tot);   // b'_{s0}
     int a = start, cnt = 0;
     for (int n = s0; n < s1; ++n) {
         const int b = max(a, clampT(cu[n + 1]));
         cnt += (b - a + C - 1) / C;
         a = b;
     }
-    s_cnt[t] = cnt;
-    __syncthreads();
-    if (t == 0) {
-        int run = 0;
-        for (int i = 0; i < 1024; ++i) {
-            const int x = s_cnt[i];
-            s_cnt[i] = run;
-            run += x;
-        }
-        off[n_seqs] = run;
-    }
-    __syncthreads();
-    int run = s_cnt[t];
+    int run = block_exclusive_scan<false>(cnt, s_wave, tot);
+    if (t == 0) off[n_seqs] = tot;
     a = start;
     for (int n = s0; n < s1; ++n) {
         const int b = max(a, clampT(cu[n + 1])), L = b - a;

@@ -359,6 +359,13 @@ def test_many_short_packed_sequences():
     check_prefill(small(H=3, lengths=lengths), 64)
 
 
+def test_thousands_of_packed_sequences():
+    """More sequences than the chunk-table kernel has threads (1024): each
+    thread of its scans then takes several sequences; many are empty."""
+    lengths = np.random.default_rng(78).integers(0, 9, size=1500).tolist()
+    check_prefill(small(H=2, lengths=lengths), 64)
+
+
 # ---------------------------------------------------------------- fp32 path
 @pytest.mark.parametrize("d,C,T", [(16, 16, 64), (16, 32, 77), (16, 64, 130), (32, 16, 50),
                                    (32, 32, 96), (32, 64, 150), (64, 16, 40), (64, 64, 129)])
