@@ -138,6 +138,30 @@ def _need(cond: bool, msg: str):
         raise ValueError(msg)
 
 
+def _on_device(ref: torch.Tensor, **tensors):
+    """Every given tensor lives on ref's device, which is the current one (the
+    library launches on the current device's current stream)."""
+    _need(ref.is_cuda, "tensors must be on a HIP device")
+    _need(ref.device.index == torch.cuda.current_device(),
+          "tensors are on %s but the current device is %d" % (ref.device,
+                                                               torch.cuda.current_device()))
+    for name, t in tensors.items():
+        _need(t is None or t.device == ref.device, "%s must be on %s" % (name, ref.device))
+
+
+def _check_out(name: str, t: Optional[torch.Tensor], shape, dtype):
+    """A caller-supplied output buffer must be exactly what the kernels write."""
+    _need(t is None or (tuple(t.shape) == tuple(shape) and t.dtype == dtype and t.is_cuda
+                        and t.is_contiguous()),
+          "%s must be a contiguous %s device tensor %s" % (name, dtype, list(shape)))
+
+
+def _check_workspace(t: Optional[torch.Tensor]):
+    _need(t is None or (t.dtype == torch.uint8 and t.dim() == 1 and t.is_cuda
+                        and t.is_contiguous()),
+          "workspace must be a contiguous 1-D uint8 device tensor")
+
+
 def make_shape(batch, seqlen, heads, d_k, d_v, chunk_size, num_seqs, dtype_code) -> KdaShape:
     return KdaShape(batch, seqlen, heads, d_k, d_v, chunk_size, num_seqs, dtype_code)
 
@@ -189,6 +213,11 @@ def _prefill(entry, gate, q, k, v, g, beta, scale, initial_state, cu_seqlens,
         _need(initial_state.shape == (N, H, dk, dv) and initial_state.dtype == torch.float32
               and initial_state.is_cuda and initial_state.is_contiguous(),
               "initial_state must be a contiguous fp32 device tensor [N, H, d_k, d_v]")
+    _check_out("out", out, (B, T, H, dv), q.dtype)
+    _check_out("final_state", final_state, (N, H, dk, dv), torch.float32)
+    _check_workspace(workspace)
+    _on_device(q, k=k, v=v, g=g, beta=beta, initial_state=initial_state, cu_seqlens=cu_seqlens,
+               out=out, final_state=final_state, workspace=workspace)
     scale = 1.0 / math.sqrt(dk) if scale is None else float(scale)
     sh = make_shape(B, T, H, dk, dv, chunk_size, N, code)
     need = int(lib().kda_chunk_fwd_workspace_bytes(ctypes.byref(sh)))
@@ -292,6 +321,8 @@ def _decode(entry, gate, q, k, v, g, beta, state, scale, out, form=None):
         _need(t is None or (t.is_cuda and t.is_contiguous()),
               "%s must be a contiguous device tensor" % name)
     code = _dtype_code(q)
+    _check_out("out", out, (N, H, dv), q.dtype)
+    _on_device(q, k=k, v=v, g=g, beta=beta, state=state, out=out)
     scale = 1.0 / math.sqrt(dk) if scale is None else float(scale)
     o = out if out is not None else torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
     extra = () if form is None else (ctypes.byref(form),)
@@ -345,9 +376,9 @@ def output_rmsnorm_gate(o: torch.Tensor, gate: torch.Tensor, weight: torch.Tenso
     for name, t in (("o", o), ("gate", gate), ("weight", weight)):
         _need(t.is_cuda and t.is_contiguous(), "%s must be a contiguous device tensor" % name)
     code = _dtype_code(o)
+    _check_out("out", out, o.shape, o.dtype)
+    _on_device(o, gate=gate, weight=weight, out=out)
     res = out if out is not None else torch.empty_like(o)
-    _need(res.shape == o.shape and res.dtype == o.dtype and res.is_contiguous(),
-          "out must match o")
     st = lib().kda_output_rmsnorm_gate(o.numel() // dv, dv, code, _ptr(o), _ptr(gate), _ptr(weight),
                                        ctypes.c_float(eps), _ptr(res), _stream())
     _check(st)
@@ -388,6 +419,9 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
         _need(t is None or (t.shape == (N, H, d, d) and t.dtype == torch.float32 and t.is_cuda
                             and t.is_contiguous()),
               "%s must be a contiguous fp32 device tensor [N, H, d, d]" % name)
+    _check_workspace(workspace)
+    _on_device(q, k=k, v=v, g=g, beta=beta, d_o=d_o, initial_state=initial_state,
+               cu_seqlens=cu_seqlens, d_final_state=d_final_state, workspace=workspace)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     sh = make_shape(B, T, H, d, d, chunk_size, N, _dtype_code(q))
     need = int(lib().kda_chunk_bwd_workspace_bytes(ctypes.byref(sh)))
