@@ -27,6 +27,9 @@ kda_status fail(kda_status st, const char *fmt, ...) {
 }
 
 kda_status hip_fail(hipError_t e, const char *what) {
+    if (e == hipErrorInvalidConfiguration)
+        return fail(KDA_ERR_HIP, "%s: %s (a kernel grid for this problem would exceed 2^32 - 1 "
+                    "threads)", what, hipGetErrorString(e));
     return fail(KDA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 

@@ -1205,20 +1205,23 @@ hipError_t launch_bwd_cdt(const ChunkBwdProblem &p, const bwd::Ws &ws, size_t sl
     e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kda_bwd_grad_kernel<C, D, In>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lg);
     if (e != hipSuccess) return e;
+    const int64_t n_pairs = (int64_t)p.n_seqs * p.heads;
+    const int64_t chain_blocks = (n_pairs + 7) / 8 * 8 * (D / TV);
+    if (!launch_fits((int64_t)slots * p.heads, GT) ||
+        !launch_fits(chain_blocks, (C == MC && D == MD) ? MT : CT))
+        return hipErrorInvalidConfiguration;
     const dim3 per_chunk((unsigned)(slots * p.heads));
     hipLaunchKernelGGL((kda_bwd_prep_kernel<C, D, In>), per_chunk, dim3(THREADS), lp, p.stream, q,
                        k, p.g, p.beta, p.scale, p.heads, p.seqlen, p.cu, p.n_seqs, ws);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if constexpr (C == MC && D == MD) {
-        const int n_pairs = p.n_seqs * p.heads;
-        hipLaunchKernelGGL((kda_bwd_chain_mfma_kernel<In>), dim3((n_pairs + 7) / 8 * 8 * (D / TV)),
-                           dim3(MT), 0, p.stream, v, p.beta, p.heads, p.seqlen, p.cu, n_pairs,
+        hipLaunchKernelGGL((kda_bwd_chain_mfma_kernel<In>), dim3((unsigned)chain_blocks),
+                           dim3(MT), 0, p.stream, v, p.beta, p.heads, p.seqlen, p.cu, (int)n_pairs,
                            p.s0, p.dfinal, dout, p.ds0, ws);
     } else {
-        const int n_pairs = p.n_seqs * p.heads;
-        hipLaunchKernelGGL((kda_bwd_chain_kernel<C, D, In>), dim3((n_pairs + 7) / 8 * 8 * (D / TV)),
-                           dim3(CT), lc, p.stream, v, p.beta, p.heads, p.seqlen, p.cu, n_pairs,
+        hipLaunchKernelGGL((kda_bwd_chain_kernel<C, D, In>), dim3((unsigned)chain_blocks),
+                           dim3(CT), lc, p.stream, v, p.beta, p.heads, p.seqlen, p.cu, (int)n_pairs,
                            p.s0, p.dfinal, dout, p.ds0, ws);
     }
     e = hipGetLastError();

@@ -215,6 +215,7 @@ hipError_t launch_chunk_fwd_f32(const ChunkProblem &p) {
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
+    if (!launch_fits((int64_t)p.n_seqs * p.heads, THREADS)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(kda_chunk_f32_kernel, dim3(p.n_seqs * p.heads), dim3(THREADS), lds,
                        p.stream, static_cast<const float *>(p.q), static_cast<const float *>(p.k),
                        static_cast<const float *>(p.v), p.g, (int)p.gate, p.beta, p.scale,

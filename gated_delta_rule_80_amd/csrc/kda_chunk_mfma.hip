@@ -68,6 +68,7 @@ constexpr int ring_depth() { return NCT == 1 ? KDA_INTER_PF : KDA_INTER_PF_WIDE;
 constexpr int L2D = KDA_INTER_L2D;    // L2 prefetch distance in chunks (0: no prefetch wave)
 constexpr int L2R = KDA_INTER_L2R;    // chunks a prefetch load may stay in flight
 constexpr int INTER_THREADS = L2D > 0 ? 576 : 512;   // 4 state + 4 output (+ 1 prefetch) waves
+constexpr int INTER_MAX_PAIRS = 1 << 19;               // (sequence, head) pairs per chain launch
 
 // One chunk-head record in the workspace (bytes).  Fragment index -> 1 KB
 // (64 lanes x 16 B) unless noted.
@@ -962,7 +963,7 @@ __device__ __forceinline__ void output_step(OutOps &op, const half8 *sS, const h
 // it writes them, and no other lane touches them.
 template <int NCT>
 __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
-    const int32_t *__restrict__ off, int n_pairs, int H, int row_len, int ncr,
+    const int32_t *__restrict__ off, int pair0, int n_pairs, int H, int row_len, int ncr,
     const int4 *__restrict__ table, int nc_max, const uint8_t *__restrict__ recs, int jlo,
     int jhi, const float *s_in, float *s_out, uint16_t *__restrict__ o) {
     constexpr int NTILES = DV / (16 * NCT);   // workgroups per (sequence, head)
@@ -975,7 +976,7 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
     const int bid = blockIdx.x;
     const int lane8 = bid & 7, rest = bid >> 3;
     const int tile = rest % NTILES, grp = rest / NTILES;
-    const int pair = grp * 8 + lane8;
+    const int pair = pair0 + grp * 8 + lane8;
     if (pair >= n_pairs) return;
     const int n = pair / H, h = pair - n * H;
 
@@ -1171,7 +1172,11 @@ hipError_t launch_chunk_fwd_mfma(const ChunkProblem &p) {
         hipSuccess)
         return e;
     const bool wide = (int64_t)n_pairs * (DV / 16) > n_cu;
-    const int inter_grid = (n_pairs + 7) / 8 * 8 * (wide ? DV / 32 : DV / 16);
+    const int tiles = wide ? DV / 32 : DV / 16;
+    // A launch holds at most 2^32 threads, so the chains go out in launches of
+    // at most INTER_MAX_PAIRS (sequence, head) pairs (a multiple of 8, so the
+    // XCD placement is the same in every launch).
+    static_assert((uint64_t)INTER_MAX_PAIRS * (DV / 16) * INTER_THREADS <= 0xFFFFFFFFull, "");
     uint16_t *o = static_cast<uint16_t *>(p.o);
 
     auto intra = [&](hipStream_t st, int jlo, int jn, int grid) {
@@ -1187,15 +1192,21 @@ hipError_t launch_chunk_fwd_mfma(const ChunkProblem &p) {
     };
     auto inter = [&](int jlo, int jhi, const float *s_in, float *s_out) {
         auto kern = wide ? kda_inter_kernel<2> : kda_inter_kernel<1>;
-        hipLaunchKernelGGL(kern, dim3(inter_grid), dim3(INTER_THREADS), 0, p.stream, off, n_pairs,
-                           p.heads, p.seqlen, ncr, table, (int)L.nc_max, recs, jlo, jhi, s_in,
-                           s_out, o);
-        return hipGetLastError();
+        hipError_t err = hipSuccess;
+        for (int p0 = 0; p0 < n_pairs && err == hipSuccess; p0 += INTER_MAX_PAIRS) {
+            const int np = min(INTER_MAX_PAIRS, n_pairs - p0);
+            hipLaunchKernelGGL(kern, dim3((np + 7) / 8 * 8 * tiles), dim3(INTER_THREADS), 0,
+                               p.stream, off, p0, n_pairs, p.heads, p.seqlen, ncr, table,
+                               (int)L.nc_max, recs, jlo, jhi, s_in, s_out, o);
+            err = hipGetLastError();
+        }
+        return err;
     };
 
     if (varlen || total == 0) {
         // Packed sequences: chunk table, all intra-chunk work, then the chunk chain.
         if (varlen) {
+            if (!launch_fits((int64_t)p.heads * L.nc_max, 256)) return hipErrorInvalidConfiguration;
             hipLaunchKernelGGL(kda_chunk_index_kernel, dim3(1), dim3(1024), 0, p.stream, p.cu,
                                p.n_seqs, (int)total, off, table);
             if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1206,6 +1217,7 @@ hipError_t launch_chunk_fwd_mfma(const ChunkProblem &p) {
     }
 
     // Equal rows: all intra-chunk work, then the chunk chain, on the caller's stream.
+    if (!launch_fits((int64_t)p.heads * p.batch * ncr, 256)) return hipErrorInvalidConfiguration;
     if ((e = intra(p.stream, 0, ncr, p.heads * p.batch * ncr)) != hipSuccess) return e;
     return inter(0, ncr, p.s0, p.s_final);
 }

@@ -167,6 +167,7 @@ static hipError_t launch_decode_g(int n_pairs, InputForm f, const void *q, const
                                   const void *v, const float *g, const float *beta, float scale,
                                   float *state, void *o, hipStream_t stream) {
     using Cfg = DecodeCfg<DK, DV>;
+    if (!launch_fits(n_pairs, Cfg::THREADS)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((kda_decode_kernel<DK, DV, T, GATE>), dim3(n_pairs), dim3(Cfg::THREADS),
                        0, stream, static_cast<const T *>(q), static_cast<const T *>(k),
                        static_cast<const T *>(v), g, beta, scale, f.flags(), f.eps, state,

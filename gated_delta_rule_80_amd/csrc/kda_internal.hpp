@@ -62,6 +62,12 @@ struct ChunkProblem {
 
 // Upper bound on the number of chunks over all sequences: each sequence of
 // L tokens has ceil(L / C) <= L / C + 1 chunks.
+// One kernel launch holds at most 2^32 - 1 threads; launchers whose grid would
+// exceed that return hipErrorInvalidConfiguration before launching.
+inline bool launch_fits(int64_t blocks, int64_t threads) {
+    return blocks >= 0 && blocks * threads <= (int64_t)0xFFFFFFFF;
+}
+
 inline int64_t max_chunks(int64_t total_tokens, int64_t n_seqs, int64_t chunk) {
     return total_tokens / chunk + n_seqs;
 }

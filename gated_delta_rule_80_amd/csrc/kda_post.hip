@@ -90,6 +90,7 @@ static hipError_t launch_post(int64_t rows, const void *o, const void *gate, con
     constexpr int RPB = 256 / (DV / 4) * POST_RPT;   // rows per workgroup
     const int64_t blocks = (rows + RPB - 1) / RPB;
     if (blocks == 0) return hipSuccess;
+    if (!launch_fits(blocks, 256)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((kda_output_rmsnorm_gate_kernel<T, DV>), dim3((unsigned)blocks), dim3(256),
                        0, stream, rows, static_cast<const T *>(o), static_cast<const T *>(gate), w,
                        eps, static_cast<T *>(out));

@@ -31,6 +31,11 @@
  *     error nothing is enqueued, no output is touched, and a status other than
  *     KDA_OK is returned; kda_last_error() then describes the cause (the text
  *     is thread-local and valid until the next call on the same thread).
+ *   - A problem whose kernel grid would exceed 2^32 - 1 threads in one launch
+ *     returns KDA_ERR_HIP (hipErrorInvalidConfiguration) before anything is
+ *     enqueued.  The prefill's chunk chain is launched in batches of (sequence,
+ *     head) pairs, so it never reaches that limit.  Any other KDA_ERR_HIP may
+ *     leave kernels of the same call enqueued before the one that failed.
  *   - Device-side faults, if any, surface at the caller's next
  *     synchronisation, as for any HIP kernel.
  *   - No C++ exception crosses this boundary.  The library holds no global

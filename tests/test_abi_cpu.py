@@ -118,6 +118,16 @@ def test_decode_rejects_bad_arguments():
     assert b"aligned" in lib.kda_last_error()
 
 
+def test_decode_grid_above_32_bit_threads_is_an_error_not_a_launch():
+    """2^20 sessions x 2047 heads fits the pair count but not one launch's 2^32
+    threads at d = 128: the call reports it before launching anything."""
+    lib = K.lib()
+    P, O, f = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000), ctypes.c_float(0.1)
+    assert lib.kda_decode_step(1 << 20, 2047, 128, 128, K.KDA_BF16, P, P, P, P, P, f, P, O,
+                               None) == 4
+    assert b"2^32" in lib.kda_last_error()
+
+
 def test_last_error_is_cleared_on_entry():
     lib = K.lib()
     call_chunk(shape(heads=0))

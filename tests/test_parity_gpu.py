@@ -366,6 +366,38 @@ def test_thousands_of_packed_sequences():
     check_prefill(small(H=2, lengths=lengths), 64)
 
 
+def test_chain_launches_split_over_pair_batches():
+    """16,500 packed sequences x 32 heads = 528,000 (sequence, head) pairs, more
+    than one chain launch takes (2^19 pairs, to stay within 2^32 threads), so
+    the chain goes out in two launches.  Sequences on both sides of the split
+    are checked one by one against the oracle (all heads, o and final state)."""
+    import gated_delta_rule_80_amd as K
+    H, N = 32, 16500
+    split = (1 << 19) // H                       # first sequence of the second launch
+    lengths = np.random.default_rng(79).integers(0, 5, size=N)
+    lengths[[0, split - 1, split, N - 1]] = [3, 4, 2, 4]
+    inp = small(H=H, lengths=lengths.tolist(), s0_std=None)
+    d = to_dev(inp)
+    o, fs = K.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], scale=d["scale"],
+                        cu_seqlens=d["cu_seqlens"])
+    torch.cuda.synchronize()
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    picks = [0, 1, 777, split - 2, split - 1, split, split + 1, split + 50, N - 1]
+    errs = []
+    for n in picks:
+        t0, t1 = int(cu[n]), int(cu[n + 1])
+        args = [W.to64(inp[x])[0, t0:t1] for x in ("q", "k", "v", "g", "beta")]
+        o_ref, s_ref = oracle.prefill(*args, inp["scale"], None, [0, t1 - t0])
+        got_s = fs[n].double().cpu().numpy()
+        if t1 > t0:
+            errs.append(rel_err(o[0, t0:t1].double().cpu().numpy(), o_ref))
+            errs.append(rel_err(got_s, s_ref[0]))
+        else:
+            assert not got_s.any()               # no tokens, no initial state: zeros
+    print("pair-batch split: max err %.3e over %d sequences" % (max(errs), len(picks)), flush=True)
+    assert max(errs) <= TOL["bf16"]
+
+
 # ---------------------------------------------------------------- fp32 path
 @pytest.mark.parametrize("d,C,T", [(16, 16, 64), (16, 32, 77), (16, 64, 130), (32, 16, 50),
                                    (32, 32, 96), (32, 64, 150), (64, 16, 40), (64, 64, 129)])
