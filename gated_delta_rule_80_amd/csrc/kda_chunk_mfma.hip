@@ -137,7 +137,12 @@ __device__ __forceinline__ float row_scan16(float x) {
 // 0, T)) -- so that even a malformed cu_seqlens yields disjoint in-range
 // sequences and at most T / C + N chunks: every later access stays in bounds.
 // For a valid cu_seqlens (starting at 0, non-decreasing, ending at T) b' = cu.
+// It also writes order[0..N): the sequences by chunk count, longest first (ties
+// by index), so that the chain kernel starts the longest chains first and the
+// short ones fill in behind them.  Beyond ORDER_MAX sequences the order is the
+// identity (ranking costs O(N) per sequence).
 // ------------------------------------------------------------------------------------
+constexpr int ORDER_MAX = 1024;
 // Exclusive scan over the 1024 threads of the workgroup, by sum or by max
 // (inputs >= 0, so 0 is the identity of both); also returns the total.
 template <bool MAX>
@@ -173,8 +178,10 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int *s_wave, int &tot
 __global__ __launch_bounds__(1024) void kda_chunk_index_kernel(const int32_t *__restrict__ cu,
                                                                int n_seqs, int total_tokens,
                                                                int32_t *__restrict__ off,
+                                                               int32_t *__restrict__ order,
                                                                int4 *__restrict__ table) {
     __shared__ int s_wave[32];
+    __shared__ int s_cnt[ORDER_MAX];
     const int t = threadIdx.x;
     const int per = (n_seqs + 1023) / 1024;
     const int s0 = min(n_seqs, t * per), s1 = min(n_seqs, s0 + per);
@@ -198,6 +205,21 @@ __global__ __launch_bounds__(1024) void kda_chunk_index_kernel(const int32_t *__
         for (int j = 0; j * C < L; ++j) table[run + j] = make_int4(n, a + j * C, min(C, L - j * C), 0);
         run += (L + C - 1) / C;
         a = b;
+    }
+    if (n_seqs > ORDER_MAX) {
+        for (int n = s0; n < s1; ++n) order[n] = n;
+        return;
+    }
+    // One sequence per thread here (per == 1): its rank among all counts.
+    if (t < n_seqs) s_cnt[t] = cnt;
+    __syncthreads();
+    if (t < n_seqs) {
+        int rank = 0;
+        for (int m = 0; m < n_seqs; ++m) {
+            const int cm = s_cnt[m];
+            rank += (cm > cnt) || (cm == cnt && m < t);
+        }
+        order[rank] = t;
     }
 }
 
@@ -963,7 +985,8 @@ __device__ __forceinline__ void output_step(OutOps &op, const half8 *sS, const h
 // it writes them, and no other lane touches them.
 template <int NCT>
 __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
-    const int32_t *__restrict__ off, int pair0, int n_pairs, int H, int row_len, int ncr,
+    const int32_t *__restrict__ off, const int32_t *__restrict__ order, int pair0, int n_pairs,
+    int H, int row_len, int ncr,
     const int4 *__restrict__ table, int nc_max, const uint8_t *__restrict__ recs, int jlo,
     int jhi, const float *s_in, float *s_out, uint16_t *__restrict__ o) {
     constexpr int NTILES = DV / (16 * NCT);   // workgroups per (sequence, head)
@@ -978,7 +1001,9 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
     const int tile = rest % NTILES, grp = rest / NTILES;
     const int pair = pair0 + grp * 8 + lane8;
     if (pair >= n_pairs) return;
-    const int n = pair / H, h = pair - n * H;
+    // Launch position -> sequence: longest chains first for packed sequences.
+    const int pos = pair / H, h = pair - pos * H;
+    const int n = table ? order[pos] : pos;
 
     const int tid = threadIdx.x, l = tid & 63, g4 = l >> 4, i16 = l & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
@@ -998,7 +1023,7 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
     cs = min(ce, cs + jlo);
     const uint8_t *rbase = recs + (size_t)h * nc_max * REC_BYTES;
     const int clast = max(cs, ce - 1);
-    const size_t sbase = (size_t)pair * DK * DV;
+    const size_t sbase = ((size_t)n * H + h) * DK * DV;
 
     // The loads are unconditional -- past the last chunk they re-read the last
     // record (in bounds, unused) -- so the compiler's wait-count tracking stays
@@ -1120,10 +1145,10 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
     }
 }
 
-// Workspace: [off int32 (N+1)][chunk table int4 x nc_max][records], each region
+// Workspace: [off int32 (N+1)][order int32 N][chunk table int4 x nc_max][records], each region
 // 256-byte aligned.
 struct WsLayout {
-    size_t off, table, recs, total;
+    size_t off, order, table, recs, total;
     int64_t nc_max;
 };
 
@@ -1132,7 +1157,8 @@ static WsLayout ws_layout(int64_t total_tokens, int64_t n_seqs, int heads) {
     L.nc_max = max_chunks(total_tokens, n_seqs, C);
     auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
     L.off = 0;
-    L.table = up((size_t)(n_seqs + 1) * 4);
+    L.order = up((size_t)(n_seqs + 1) * 4);
+    L.table = L.order + up((size_t)n_seqs * 4);
     L.recs = L.table + up((size_t)L.nc_max * 16);
     L.total = L.recs + (size_t)heads * L.nc_max * REC_BYTES;
     return L;
@@ -1156,6 +1182,7 @@ hipError_t launch_chunk_fwd_mfma(const ChunkProblem &p) {
     hipError_t e;
     uint8_t *ws = static_cast<uint8_t *>(p.workspace);
     int32_t *off = reinterpret_cast<int32_t *>(ws + L.off);
+    int32_t *order = reinterpret_cast<int32_t *>(ws + L.order);
     int4 *table = varlen ? reinterpret_cast<int4 *>(ws + L.table) : nullptr;
     uint8_t *recs = ws + L.recs;
     const int ncr = (p.seqlen + C - 1) / C;
@@ -1196,7 +1223,7 @@ hipError_t launch_chunk_fwd_mfma(const ChunkProblem &p) {
         for (int p0 = 0; p0 < n_pairs && err == hipSuccess; p0 += INTER_MAX_PAIRS) {
             const int np = min(INTER_MAX_PAIRS, n_pairs - p0);
             hipLaunchKernelGGL(kern, dim3((np + 7) / 8 * 8 * tiles), dim3(INTER_THREADS), 0,
-                               p.stream, off, p0, n_pairs, p.heads, p.seqlen, ncr, table,
+                               p.stream, off, order, p0, n_pairs, p.heads, p.seqlen, ncr, table,
                                (int)L.nc_max, recs, jlo, jhi, s_in, s_out, o);
             err = hipGetLastError();
         }
@@ -1208,7 +1235,7 @@ hipError_t launch_chunk_fwd_mfma(const ChunkProblem &p) {
         if (varlen) {
             if (!launch_fits((int64_t)p.heads * L.nc_max, 256)) return hipErrorInvalidConfiguration;
             hipLaunchKernelGGL(kda_chunk_index_kernel, dim3(1), dim3(1024), 0, p.stream, p.cu,
-                               p.n_seqs, (int)total, off, table);
+                               p.n_seqs, (int)total, off, order, table);
             if ((e = hipGetLastError()) != hipSuccess) return e;
             if (L.nc_max > 0 && (e = intra(p.stream, 0, 0, p.heads * (int)L.nc_max)) != hipSuccess)
                 return e;
