@@ -366,6 +366,31 @@ def test_thousands_of_packed_sequences():
     check_prefill(small(H=2, lengths=lengths), 64)
 
 
+def test_packed_position_does_not_change_a_sequence_bitwise():
+    """Each packed sequence is chunked from its own first token and the chain
+    kernel starts the longest sequences first, whatever their place in the
+    pack: the same sequences packed in another order, each with its own
+    initial state, give bitwise the same outputs and final states."""
+    import gated_delta_rule_80_amd as K
+    lengths = [40, 300, 0, 129, 64, 300, 1, 200]
+    inp = small(H=3, lengths=lengths, s0_std=0.05, seed=81)
+    d = to_dev(inp)
+    o, fs = K.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], scale=d["scale"],
+                        initial_state=d["initial_state"], cu_seqlens=d["cu_seqlens"])
+    perm = [5, 2, 7, 0, 3, 6, 1, 4]
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    rows = torch.cat([torch.arange(int(cu[n]), int(cu[n + 1])) for n in perm]).cuda()
+    lp = [lengths[n] for n in perm]
+    cu_p = torch.tensor(np.concatenate([[0], np.cumsum(lp)]).astype(np.int32)).cuda()
+    take = lambda t: t[:, rows].contiguous()  # noqa: E731
+    o2, fs2 = K.chunk_fwd(take(d["q"]), take(d["k"]), take(d["v"]), take(d["g"]),
+                          take(d["beta"]), scale=d["scale"],
+                          initial_state=d["initial_state"][perm].contiguous(), cu_seqlens=cu_p)
+    torch.cuda.synchronize()
+    assert torch.equal(o[:, rows], o2)
+    assert torch.equal(fs[perm], fs2)
+
+
 def test_chain_launches_split_over_pair_batches():
     """16,500 packed sequences x 32 heads = 528,000 (sequence, head) pairs, more
     than one chain launch takes (2^19 pairs, to stay within 2^32 threads), so
