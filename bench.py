@@ -3,9 +3,11 @@
 
 One step = one chunkwise prefill (``kda_chunk_fwd``) of the long-context
 workload (B=1, H=32, T=131072, d_k=d_v=128, C=64, bf16 storage) with every
-input already resident in HBM.  The same run also times the batched decode
-step (``kda_decode_step``: 128 sessions x 32 heads, 268 MB fp32 state updated
-in place), the same prefill through the scalar-gate entry point, the packed
+input already resident in HBM.  The same run also times the small prefill
+workload (B=2, H=8, T=2048, report only), the batched decode step
+(``kda_decode_step``: 128 sessions x 32 heads, 268 MB fp32 state updated in
+place, a fresh seeded token set every step), the same prefill through the
+scalar-gate entry point, the packed
 varlen workload (8 sequences through cu_seqlens), the backward (fp32
 storage, d = 128), and the fp64 CPU oracle on a bounded sample of the prefill
 workload.
@@ -97,14 +99,25 @@ def measured_mfma(key):
 
 
 def cpu_model():
+    """The host CPU as /proc/cpuinfo names it, with its family / model /
+    stepping numbers (some hosts report only a generic model name) and the
+    logical CPU count."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" not in line:
+                    if fields:
+                        break           # the first processor's block is enough
+                    continue
+                key, val = (x.strip() for x in line.split(":", 1))
+                fields.setdefault(key, val)
     except OSError:
         pass
-    return platform.processor()
+    name = fields.get("model name") or platform.processor() or "unknown"
+    ids = ", ".join("%s %s" % (k, fields[k]) for k in ("vendor_id", "cpu family", "model",
+                                                        "stepping") if k in fields)
+    return "%s (%s; %d logical CPUs)" % (name, ids or "no cpuinfo ids", os.cpu_count() or 0)
 
 
 def main():
@@ -116,6 +129,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=32768)
     ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--skip-small-prefill", action="store_true")
     ap.add_argument("--skip-scalar-gate", action="store_true")
     ap.add_argument("--skip-varlen", action="store_true")
     ap.add_argument("--skip-backward", action="store_true")
@@ -211,11 +225,55 @@ def main():
         "outputs_finite": ok,
     }
 
+    if not args.skip_small_prefill:
+        # Workload 2, report only: B=2 rows of 2048 tokens, H=8.  Sixteen chains
+        # of 32 chunks cannot fill the chip; this leg shows the latency floor.
+        w2 = W.WORKLOADS[2]
+        print("[bench] small prefill: %s" % w2.description, file=sys.stderr, flush=True)
+        inp2 = W.make_workload(2)
+        d2 = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp2.items()}
+        B2, T2, H2, dk2 = d2["q"].shape
+        ws2 = torch.empty(K.workspace_bytes(B2, T2, H2, dk2, dv, w2.chunk, B2), dtype=torch.uint8,
+                          device=dev)
+        o2 = torch.empty((B2, T2, H2, dv), dtype=torch.bfloat16, device=dev)
+        fs2 = torch.empty((B2, H2, dk2, dv), dtype=torch.float32, device=dev)
+
+        def pstep():
+            K.chunk_fwd(d2["q"], d2["k"], d2["v"], d2["g"], d2["beta"], scale=d2["scale"],
+                        initial_state=d2["initial_state"], chunk_size=w2.chunk, workspace=ws2,
+                        out=o2, final_state=fs2)
+
+        for _ in range(5):
+            pstep()
+        torch.cuda.synchronize()
+        n_p = 50
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n_p):
+            pstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        pms = e0.elapsed_time(e1) / n_p
+        ptok = B2 * T2
+        pbytes = prefill_alg_bytes(ptok, H2, dk2, dv, B2)
+        pgbs = pbytes / (pms * 1e-3) / 1e9
+        result["small_prefill"] = {
+            "value": round(ptok / (pms * 1e-3), 1), "unit": "tokens/s",
+            "ms_per_step": round(pms, 4), "steps": n_p,
+            "config": {"workload": "prefill B=2 H=8 T=2048 d_k=d_v=128 C=64 bf16, "
+                                   "S0~N(0,0.01^2) (report only)"},
+            "roofline": {"bound": "hbm", "kernel": "kda_chunk_fwd", "achieved": round(pgbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(pgbs / HBM_PEAK_GBS, 4), "alg_bytes_per_launch": pbytes}}
+        del d2, inp2, ws2, o2, fs2
+
     if not args.skip_decode:
         w3 = W.WORKLOADS[3]
         print("[bench] decode: %s" % w3.description, file=sys.stderr, flush=True)
         state = W.make_decode_state(w3).to(dev)
-        n_tok = 8
+        # Fresh seeded tokens for every one of the workload's steps, drawn on the
+        # host and held on the device (about 5 MB per step) before the timing.
+        n_tok = w3.steps
         toks = [{k: (v.to(dev) if isinstance(v, torch.Tensor) else v)
                  for k, v in W.make_decode_step(s, w3).items()} for s in range(n_tok)]
         od = torch.empty((w3.n_sessions, w3.H, w3.dv), dtype=torch.bfloat16, device=dev)
@@ -241,7 +299,8 @@ def main():
             "value": round(dgbs, 1), "unit": "GB/s", "ms_per_step": round(dms, 5),
             "steps": args.decode_steps,
             "config": {"workload": "batched decode 128 sessions x 32 heads d=128, fp32 state "
-                                   "268 MB in place, bf16 tokens"},
+                                   "268 MB in place, bf16 tokens, a fresh seeded token set for "
+                                   "each of the %d steps (cycled beyond that)" % n_tok},
             "roofline": {"bound": "hbm", "kernel": "kda_decode_kernel<128,128,bf16>",
                          "achieved": round(dgbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(dgbs / HBM_PEAK_GBS, 4),

@@ -23,7 +23,7 @@ SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_chunk_mfma.hip", "kda_chunk_f32
            "kda_chunk_bwd.hip",
            "kda_post.hip"]
 
-COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
+COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wextra", "-Werror",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 

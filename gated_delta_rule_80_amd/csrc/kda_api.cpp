@@ -33,14 +33,25 @@ kda_status hip_fail(hipError_t e, const char *what) {
     return fail(KDA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// The integer a caller stored in a kda_dtype.  A C caller may store any int
+// there; in C++ reading an enum object whose value lies outside the enum's
+// range is undefined, so its bytes are read as an int32_t instead.
+int dtype_code(const kda_dtype &d) {
+    static_assert(sizeof(kda_dtype) == sizeof(int32_t), "kda_dtype is an int-sized enum");
+    int32_t v;
+    std::memcpy(&v, &d, sizeof(v));
+    return v;
+}
+bool known_dtype(int dt) { return dt == KDA_F32 || dt == KDA_BF16; }
+
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 // Checks the fields every prefill call needs; on success fills the token count.
 kda_status check_shape(const kda_shape *s, int64_t *total_tokens) {
     if (!s) return fail(KDA_ERR_INVALID_ARGUMENT, "shape is NULL");
-    if (s->dtype != KDA_F32 && s->dtype != KDA_BF16)
-        return fail(KDA_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)s->dtype);
+    if (!known_dtype(dtype_code(s->dtype)))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype_code(s->dtype));
     if (s->batch <= 0 || s->seqlen < 0 || s->num_heads <= 0 || s->d_k <= 0 || s->d_v <= 0 ||
         s->chunk_size <= 0 || s->num_seqs <= 0)
         return fail(KDA_ERR_INVALID_ARGUMENT,
@@ -48,7 +59,7 @@ kda_status check_shape(const kda_shape *s, int64_t *total_tokens) {
                     "num_seqs %d)",
                     s->batch, s->seqlen, s->num_heads, s->d_k, s->d_v, s->chunk_size,
                     s->num_seqs);
-    const bool bf16 = s->dtype == KDA_BF16;
+    const bool bf16 = dtype_code(s->dtype) == KDA_BF16;
     if (!kda::mfma_path_supported(s->d_k, s->d_v, s->chunk_size, bf16) &&
         !kda::f32_path_supported(s->d_k, s->d_v, s->chunk_size, bf16))
         return fail(KDA_ERR_UNSUPPORTED,
@@ -67,7 +78,7 @@ kda_status check_shape(const kda_shape *s, int64_t *total_tokens) {
 // The workspace is sized for the packed-sequence chunk bound T/C + N, which
 // is never below the equal-rows count B * ceil(T/C); one size fits both.
 size_t workspace_for(const kda_shape *s, int64_t total) {
-    const bool bf16 = s->dtype == KDA_BF16;
+    const bool bf16 = dtype_code(s->dtype) == KDA_BF16;
     if (kda::mfma_path_supported(s->d_k, s->d_v, s->chunk_size, bf16))
         return kda::mfma_workspace_bytes(total, s->num_seqs, s->num_heads, s->chunk_size);
     return kda::f32_workspace_bytes(total, s->num_seqs, s->num_heads, s->chunk_size);
@@ -143,7 +154,7 @@ kda_status chunk_fwd(kda::Gate gate, kda::InputForm form, const kda_shape *shape
     p.dk = shape->d_k;
     p.dv = shape->d_v;
     p.chunk = shape->chunk_size;
-    p.bf16 = shape->dtype == KDA_BF16;
+    p.bf16 = dtype_code(shape->dtype) == KDA_BF16;
     p.q = q;
     p.k = k;
     p.v = v;
@@ -170,15 +181,15 @@ kda_status chunk_fwd(kda::Gate gate, kda::InputForm form, const kda_shape *shape
 // Shared body of the two decode entry points (gate layouts as for chunk_fwd,
 // per pair instead of per token).
 kda_status decode_step(kda::Gate gate, kda::InputForm form, int32_t num_sessions,
-                       int32_t num_heads, int32_t d_k, int32_t d_v, kda_dtype dtype,
+                       int32_t num_heads, int32_t d_k, int32_t d_v, int dtype,
                        const void *q, const void *k, const void *v, const float *g,
                        const float *beta, float scale, float *state_inout, void *o,
                        void *stream) {
     if (gate == kda::Gate::Scalar && !g) gate = kda::Gate::None;
     if (gate == kda::Gate::None && g)
         return fail(KDA_ERR_INVALID_ARGUMENT, "g must be NULL when there is no gate");
-    if (dtype != KDA_F32 && dtype != KDA_BF16)
-        return fail(KDA_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)dtype);
+    if (!known_dtype(dtype))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
     if (num_sessions <= 0 || num_heads <= 0 || d_k <= 0 || d_v <= 0)
         return fail(KDA_ERR_INVALID_ARGUMENT, "non-positive size (sessions %d heads %d d_k %d "
                     "d_v %d)", num_sessions, num_heads, d_k, d_v);
@@ -278,7 +289,7 @@ kda_status kda_decode_step(int32_t num_sessions, int32_t num_heads, int32_t d_k,
                            void *o, void *stream) {
     g_last_error[0] = '\0';
     return decode_step(kda::Gate::PerChannel, kda::InputForm(), num_sessions, num_heads, d_k, d_v,
-                       dtype, q, k, v, g, beta, scale, state_inout, o, stream);
+                       dtype_code(dtype), q, k, v, g, beta, scale, state_inout, o, stream);
 }
 
 kda_status kda_decode_step_scalar_gate(int32_t num_sessions, int32_t num_heads, int32_t d_k,
@@ -288,7 +299,7 @@ kda_status kda_decode_step_scalar_gate(int32_t num_sessions, int32_t num_heads, 
                                        void *o, void *stream) {
     g_last_error[0] = '\0';
     return decode_step(kda::Gate::Scalar, kda::InputForm(), num_sessions, num_heads, d_k, d_v,
-                       dtype, q, k, v, g, beta, scale, state_inout, o, stream);
+                       dtype_code(dtype), q, k, v, g, beta, scale, state_inout, o, stream);
 }
 
 kda_status kda_decode_step_ex(int32_t num_sessions, int32_t num_heads, int32_t d_k, int32_t d_v,
@@ -302,7 +313,8 @@ kda_status kda_decode_step_ex(int32_t num_sessions, int32_t num_heads, int32_t d
     if (st != KDA_OK) return st;
     if (gate == kda::Gate::Scalar && !g)
         return fail(KDA_ERR_INVALID_ARGUMENT, "KDA_GATE_SCALAR needs g (use KDA_GATE_NONE)");
-    return decode_step(gate, f, num_sessions, num_heads, d_k, d_v, dtype, q, k, v, g, beta, scale,
+    return decode_step(gate, f, num_sessions, num_heads, d_k, d_v, dtype_code(dtype), q, k, v, g,
+                       beta, scale,
                        state_inout, o, stream);
 }
 
@@ -310,8 +322,8 @@ kda_status kda_output_rmsnorm_gate(int64_t rows, int32_t d_v, kda_dtype dtype, c
                                    const void *gate, const float *weight, float eps, void *out,
                                    void *stream) {
     g_last_error[0] = '\0';
-    if (dtype != KDA_F32 && dtype != KDA_BF16)
-        return fail(KDA_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)dtype);
+    const int dt = dtype_code(dtype);
+    if (!known_dtype(dt)) return fail(KDA_ERR_INVALID_ARGUMENT, "unknown dtype %d", dt);
     if (rows < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "negative rows (%lld)", (long long)rows);
     if (!kda::output_stage_supported(d_v))
         return fail(KDA_ERR_UNSUPPORTED, "no output-stage kernel for d_v %d (built: 16, 32, 64, "
@@ -323,12 +335,12 @@ kda_status kda_output_rmsnorm_gate(int64_t rows, int32_t d_v, kda_dtype dtype, c
         return fail(KDA_ERR_INVALID_ARGUMENT, "too many rows (%lld)", (long long)rows);
     if (!o || !gate || !weight || !out)
         return fail(KDA_ERR_INVALID_ARGUMENT, "a required tensor pointer is NULL");
-    const uintptr_t mask = dtype == KDA_F32 ? 15u : 7u;
+    const uintptr_t mask = dt == KDA_F32 ? 15u : 7u;
     if ((reinterpret_cast<uintptr_t>(o) & mask) || (reinterpret_cast<uintptr_t>(gate) & mask) ||
         (reinterpret_cast<uintptr_t>(out) & mask) || !aligned16(weight))
         return fail(KDA_ERR_INVALID_ARGUMENT, "o / gate / out / weight are misaligned");
     if (out == gate) return fail(KDA_ERR_INVALID_ARGUMENT, "out must not alias gate");
-    hipError_t e = kda::launch_output_rmsnorm_gate(rows, d_v, dtype == KDA_BF16, o, gate, weight,
+    hipError_t e = kda::launch_output_rmsnorm_gate(rows, d_v, dt == KDA_BF16, o, gate, weight,
                                                    eps, out, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "output stage launch");
     return KDA_OK;
@@ -351,8 +363,8 @@ kda_status kda_chunk_bwd(const kda_shape *shape, const void *q, const void *k, c
                          size_t workspace_bytes, void *stream) {
     g_last_error[0] = '\0';
     if (!shape) return fail(KDA_ERR_INVALID_ARGUMENT, "shape is NULL");
-    if (shape->dtype != KDA_F32 && shape->dtype != KDA_BF16)
-        return fail(KDA_ERR_UNSUPPORTED, "unknown dtype %d", (int)shape->dtype);
+    if (!known_dtype(dtype_code(shape->dtype)))
+        return fail(KDA_ERR_UNSUPPORTED, "unknown dtype %d", dtype_code(shape->dtype));
     if (shape->batch <= 0 || shape->seqlen < 0 || shape->num_heads <= 0 || shape->d_k <= 0 ||
         shape->d_v <= 0 || shape->chunk_size <= 0 || shape->num_seqs <= 0)
         return fail(KDA_ERR_INVALID_ARGUMENT, "non-positive size");
@@ -401,7 +413,7 @@ kda_status kda_chunk_bwd(const kda_shape *shape, const void *q, const void *k, c
     p.heads = shape->num_heads;
     p.d = shape->d_k;
     p.chunk = shape->chunk_size;
-    p.bf16 = shape->dtype == KDA_BF16;
+    p.bf16 = dtype_code(shape->dtype) == KDA_BF16;
     p.q = q;
     p.k = k;
     p.v = v;

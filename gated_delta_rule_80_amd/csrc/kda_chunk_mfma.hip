@@ -19,7 +19,10 @@
 // own reference point, so no factor ever divides by the decay of more than
 // half a sub-chunk.  Qbar, L and Ktil only ever scale by e^{x} with x <= 0.
 // Exponents are differences of cumulative logs, as the derivation
-// recommends.  Supported: per-token log-decays down to about -10.9.
+// recommends.  Per-token log-decays below MIN_LOG_DECAY = -10 (down to -inf)
+// are taken as -10: a retention of e^-10 = 4.5e-5 instead of less, which
+// keeps every factor in range and changes o and S by at most that fraction of
+// the state being forgotten.
 //
 // Kernels
 //   kda_chunk_index  packed sequences -> chunk table (device side, no sync)
@@ -50,6 +53,10 @@ namespace kda {
 namespace mfma_path {
 
 constexpr int C = 64, DK = 128, DV = 128;
+// Floor of the per-token log-decay (natural log) on this path.  Within a
+// 16-token sub-chunk the mid-point split factors then stay below e^{8 * 10},
+// and a sub-chunk's whole decay below e^{160}: inside the fp32 / bf16 range.
+constexpr float MIN_LOG_DECAY = -10.f;
 #ifndef KDA_INTER_PF
 #define KDA_INTER_PF 3
 #endif
@@ -371,8 +378,12 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
         nq[r] = scale;   // the query scale rides on the per-row factor
     }
     // Gate as a logit: log a = log sigmoid(x) on the valid rows (padding rows
-    // keep log a = 0).  A scalar gate is broadcast over the channels.  Log-decays
-    // are then kept in base 2 (g log2 e), so every factor below is one exp2.
+    // keep log a = 0).  A scalar gate is broadcast over the channels.  Each
+    // per-token log-decay is then floored at MIN_LOG_DECAY (NaN passes through):
+    // a channel that keeps less than e^-10 of its state over one token keeps
+    // e^-10 instead, which bounds every split factor below (see the secondary
+    // chunking comment) whatever the gate, -inf included.  Log-decays are then
+    // kept in base 2 (g log2 e), so every factor below is one exp2.
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const bool ok = 16 * r + i16 < len;
@@ -388,7 +399,10 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
             }
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) G[r][j] *= 1.4426950408889634f;
+        for (int j = 0; j < 8; ++j) {
+            const float x = G[r][j];
+            G[r][j] = (x < MIN_LOG_DECAY ? MIN_LOG_DECAY : x) * 1.4426950408889634f;
+        }
     }
     if (tid < C) {
         const int i = tid;
@@ -444,7 +458,8 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
     // whatever the decay.  Inside a sub-chunk the split is taken at the
     // mid-point M_a = (E_a + E_{a+1}) / 2, so each factor lies within
     // e^{+-(E_a - E_{a+1}) / 2}: in range for fp32 and bf16 while the decay of
-    // 16 tokens stays above about -175 (-10.9 per token).
+    // 16 tokens stays above about -175, which the floor of -10 per token
+    // guarantees (-160 at most).
     float E[5][8];
     float gcmin = 0.f;   // the strongest whole-chunk decay (log2) among this lane's channels
 #pragma unroll

@@ -167,13 +167,15 @@ size_t kda_chunk_fwd_workspace_bytes(const kda_shape *shape);
  *                 kda_chunk_fwd_workspace_bytes(shape) bytes, 256-byte aligned.
  * Each sequence is cut into chunks of C tokens from its first token; the last
  * chunk may be shorter.  Chunks never straddle sequences.
- * Supported decay range: any cumulative decay; on the MFMA path every
- * per-token log-decay must be finite and >= -10 (the kernels split each 64-token chunk
- * into 16-token sub-chunks, "Kimi Delta Attention: a half-life per channel",
- * section "What changes in the kernel"; within a sub-chunk the decay-scaled
- * operands then stay inside the fp32 / bf16 range).  The fp32 path takes any
- * finite value.  Smaller values (a channel that forgets within one token) give
- * non-finite outputs on the MFMA path.  Keys
+ * Decay range: any cumulative decay and any per-token log-decay, -inf
+ * included.  The MFMA path (bf16 storage) splits each 64-token chunk into
+ * 16-token sub-chunks ("Kimi Delta Attention: a half-life per channel",
+ * section "What changes in the kernel") and floors each per-token log-decay at
+ * -10: a channel told to keep less than e^-10 (4.5e-5) of its state over one
+ * token keeps e^-10 of it, which moves o and the state by at most that
+ * fraction of the forgotten state (far inside the bf16 tolerance) and keeps
+ * every decay-scaled operand inside the fp32 / bf16 range.  The fp32 path
+ * uses the exact factors and takes any finite value.  Keys
  * and queries are expected L2-normalised (|k|, |q| <= 1) and |v| well below
  * the fp16 range, as the layer that calls this operator produces them.
  * Pointers to q, k, v, o, g and the states must be 16-byte aligned; beta and

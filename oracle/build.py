@@ -18,7 +18,7 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     # -ffp-contract=off keeps every multiply and add a separately rounded fp64
     # operation, so the oracle's arithmetic is exactly what its source says.
-    cmd = ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+    cmd = ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off", "-Werror",
            "-std=c99", "-Wall", "-Wextra", "-o", tmp, SRC, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)

@@ -41,40 +41,66 @@ def test_workload2_prefill_full():
     check_prefill(inp, 64)
 
 
-def test_workload4_varlen_sampled():
+def test_workload4_varlen_full():
+    """Every head, sequence and value column of the packed workload, with the
+    per-(sequence, head) and per-chunk maxima."""
     inp = W.make_workload(4)
-    check_prefill(inp, 64, heads=[0, 17, 31], cols=list(range(0, 128, 4)))
+    check_prefill(inp, 64)
 
 
-def test_workload5_long_sampled():
+# Four columns of every 16-column value tile, at a different place in each tile,
+# so every chain workgroup of the long workload is compared.
+WORKLOAD5_COLS = sorted(16 * t + a for t in range(8) for a in {t % 16, (5 * t + 3) % 16,
+                                                                 (11 * t + 7) % 16, 15 - t})
+
+
+def test_workload5_long_all_heads():
+    """All 32 heads of the T = 131072 workload on a column subset (columns of
+    the value space are independent, so the subset is exact), with the
+    per-head and per-chunk maxima over all 2048 chunks of every head."""
+    assert len({c // 16 for c in WORKLOAD5_COLS}) == 8
     inp = W.make_workload(5)
-    check_prefill(inp, 64, heads=[3, 28], cols=[0, 1, 31, 32, 63, 64, 95, 127])
+    check_prefill(inp, 64, cols=WORKLOAD5_COLS)
 
 
-def test_workload3_decode_256_steps_sampled():
+# Sixteen value columns, one from each group of eight (the decode kernel's
+# threads own four columns each), at varied places in the group.
+DECODE_COLS = [8 * i + (3 * i) % 8 for i in range(16)]
+
+
+def test_workload3_decode_256_steps_all_pairs():
+    """All 128 x 32 (session, head) pairs at every one of the 256 steps, on a
+    column subset: o stacked over the steps and the state after step 256, as a
+    whole and per pair."""
     import gated_delta_rule_80_amd as K
+    from kda_harness import state_pair_errors
     w = W.WORKLOADS[3]
+    cols = DECODE_COLS
     state = W.make_decode_state(w)
-    pairs = [(n, h) for n in (0, 37, 127) for h in (0, 9, 31)]
-    ref_state = np.stack([W.to64(state[n, h]) for n, h in pairs])
+    ref_state = W.to64(state[..., cols])
     st_dev = state.to("cuda")
+    del state
     o_gpu, o_ref = [], []
     for s in range(w.steps):
         tok = W.make_decode_step(s, w)
         d = to_dev(tok)
         o = K.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], st_dev, scale=w.scale)
-        o_gpu.append(o.double().cpu().numpy()[[p[0] for p in pairs], [p[1] for p in pairs]])
-        sel = lambda t: W.to64(t)[[p[0] for p in pairs], [p[1] for p in pairs]][None]  # noqa
-        orr, ref_state = oracle.decode_step(sel(tok["q"]), sel(tok["k"]), sel(tok["v"]),
-                                            sel(tok["g"]), sel(tok["beta"]), w.scale,
-                                            ref_state[None])
-        ref_state = ref_state[0]
-        o_ref.append(orr[0])
+        o_gpu.append(o[..., cols].double().cpu().numpy())
+        orr, ref_state = oracle.decode_step(W.to64(tok["q"]), W.to64(tok["k"]),
+                                            W.to64(tok["v"])[..., cols], W.to64(tok["g"]),
+                                            W.to64(tok["beta"]), w.scale, ref_state)
+        o_ref.append(orr)
     torch.cuda.synchronize()
-    st = st_dev.double().cpu().numpy()[[p[0] for p in pairs], [p[1] for p in pairs]]
-    eo, es = rel_err(np.stack(o_gpu), np.stack(o_ref)), rel_err(st, ref_state)
-    print("decode err o %.3e S %.3e" % (eo, es))
-    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+    st = st_dev[..., cols].double().cpu().numpy()
+    og, orf = np.stack(o_gpu), np.stack(o_ref)           # [steps, N, H, cols]
+    eo, es = rel_err(og, orf), rel_err(st, ref_state)
+    pair_o = np.sqrt(((og - orf) ** 2).sum(axis=(0, 3)) / (orf ** 2).sum(axis=(0, 3)))
+    pair_s = state_pair_errors(st, ref_state)
+    print("decode err o %.3e S %.3e  per pair max o %.3e S %.3e"
+          % (eo, es, pair_o.max(), pair_s.max()), flush=True)
+    tol = TOL["bf16"]
+    assert np.all(np.isfinite(og)) and np.all(np.isfinite(st))
+    assert eo <= tol and es <= tol and pair_o.max() <= tol and pair_s.max() <= tol
 
 
 # ---------------------------------------------------------------- MFMA path edge cases
@@ -255,6 +281,30 @@ def test_strong_decay_sub_chunks(lo, hi, mixed):
     chunk's cumulative decay reaches -640, far outside any single-reference
     range, and the 16-token sub-chunks keep every factor finite."""
     inp = _strong_gate(small(T=333, H=2, s0_std=0.05), lo, hi, seed=61, mixed=mixed)
+    check_prefill(inp, 64)
+
+
+@pytest.mark.parametrize("lo,hi", [(-20.0, -10.0), (-100.0, -20.0), (-12.0, 0.0)])
+def test_decay_below_the_floor(lo, hi):
+    """Per-token log-decays below -10, which the MFMA path floors at -10 (a
+    retention of e^-10 instead of less): the outputs stay finite and within the
+    tolerance of the exact recurrence."""
+    inp = _strong_gate(small(T=333, H=2, s0_std=0.05), lo, hi, seed=68)
+    check_prefill(inp, 64)
+
+
+def test_decay_minus_inf_on_channels_and_tokens():
+    """log a = -inf (a channel that forgets everything in one token) on 5% of
+    the (token, channel) entries, on every channel of some tokens, and on a
+    whole channel of a head, among the workload's weak decays; packed
+    sequences with ragged tails."""
+    inp = small(H=2, lengths=[70, 1, 200, 64, 17, 130], s0_std=0.05, seed=69)
+    g = inp["g"].clone()
+    gen = torch.Generator().manual_seed(70)
+    g[torch.rand(g.shape, generator=gen) < 0.05] = float("-inf")
+    g[:, [3, 100, 101, 250], :, :] = float("-inf")
+    g[:, :, 1, 77] = float("-inf")
+    inp["g"] = g.contiguous()
     check_prefill(inp, 64)
 
 

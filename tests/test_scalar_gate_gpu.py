@@ -12,7 +12,7 @@ import torch
 
 import kda_workloads as W
 import oracle
-from kda_harness import TOL, oracle_prefill, rel_err, to_dev
+from kda_harness import TOL, assert_close, cu_list, oracle_prefill, rel_err, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -55,10 +55,7 @@ def check(inp, gs, chunk):
               else gs[..., None].expand_as(inp["g"]).contiguous())
     o, fs = run_scalar(inp, gs, chunk)
     o_ref, s_ref = oracle_prefill(with_gate(inp, g_full))
-    eo, es = rel_err(o, o_ref), rel_err(fs, s_ref)
-    print("scalar gate err o %.3e S %.3e" % (eo, es))
-    tol = TOL[inp["dtype"]]
-    assert eo <= tol and es <= tol
+    assert_close(o, o_ref, fs, s_ref, cu_list(inp), TOL[inp["dtype"]], label="scalar gate")
 
 
 @pytest.mark.parametrize("T,B", [(300, 2), (64, 1), (1000, 1)])
