@@ -7,6 +7,8 @@ device pointers and the current HIP stream.  There is no fallback: if the
 library is missing or cannot be loaded, every call raises.
 
   chunk_fwd(q, k, v, g, beta, ...)      chunkwise prefill  -> (o, final_state)
+  chunk_fwd_noalloc(...)                the same on the library's own device
+                                        buffer (no workspace allocation)
   decode_step(q, k, v, g, beta, state)  one recurrent step -> o (state in place)
   chunk_fwd_scalar_gate, decode_step_scalar_gate
                                         the same with one log-decay per (token,
@@ -26,7 +28,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["chunk_fwd", "decode_step", "chunk_fwd_scalar_gate", "decode_step_scalar_gate",
+__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "decode_step", "chunk_fwd_scalar_gate", "decode_step_scalar_gate",
            "chunk_fwd_ex", "decode_step_ex", "output_rmsnorm_gate", "chunk_bwd", "workspace_bytes",
            "workspace_bytes_bwd", "lib", "KdaError", "LIB_PATH"]
 
@@ -84,6 +86,9 @@ def lib():
     L.kda_chunk_fwd.restype = ctypes.c_int
     L.kda_chunk_fwd.argtypes = [ctypes.POINTER(KdaShape), vp, vp, vp, fp, fp, ctypes.c_float,
                                 fp, ip, vp, fp, vp, ctypes.c_size_t, vp]
+    L.kda_chunk_fwd_noalloc.restype = ctypes.c_int
+    L.kda_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(KdaShape), vp, vp, vp, fp, fp,
+                                        ctypes.c_float, fp, ip, vp, fp, vp]
     L.kda_chunk_fwd_scalar_gate.restype = ctypes.c_int
     L.kda_chunk_fwd_scalar_gate.argtypes = L.kda_chunk_fwd.argtypes
     L.kda_decode_step.restype = ctypes.c_int
@@ -183,7 +188,8 @@ def workspace_bytes_bwd(batch, seqlen, heads, d, chunk_size, num_seqs,
 
 
 def _prefill(entry, gate, q, k, v, g, beta, scale, initial_state, cu_seqlens,
-             chunk_size, output_final_state, workspace, out, final_state, form=None):
+             chunk_size, output_final_state, workspace, out, final_state, form=None,
+             noalloc=False):
     _need(q.dim() == 4 and k.shape == q.shape and v.dim() == 4 and v.shape[:3] == q.shape[:3],
           "q, k must be [B, T, H, d_k] and v [B, T, H, d_v]")
     B, T, H, dk = q.shape
@@ -220,18 +226,20 @@ def _prefill(entry, gate, q, k, v, g, beta, scale, initial_state, cu_seqlens,
                out=out, final_state=final_state, workspace=workspace)
     scale = 1.0 / math.sqrt(dk) if scale is None else float(scale)
     sh = make_shape(B, T, H, dk, dv, chunk_size, N, code)
-    need = int(lib().kda_chunk_fwd_workspace_bytes(ctypes.byref(sh)))
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if not noalloc:
+        need = int(lib().kda_chunk_fwd_workspace_bytes(ctypes.byref(sh)))
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     o = out if out is not None else torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
     fs = None
     if output_final_state:
         fs = final_state if final_state is not None else torch.empty(
             (N, H, dk, dv), dtype=torch.float32, device=q.device)
     extra = () if form is None else (ctypes.byref(form),)
+    ws_args = () if noalloc else (_ptr(workspace), ctypes.c_size_t(workspace.numel()))
     st = entry(ctypes.byref(sh), *extra, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                ctypes.c_float(scale), _ptr(initial_state), _ptr(cu_seqlens), _ptr(o), _ptr(fs),
-               _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream())
+               *ws_args, _stream())
     _check(st)
     return o, fs
 
@@ -253,6 +261,23 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     """
     return _prefill(lib().kda_chunk_fwd, "per_channel", q, k, v, g, beta, scale, initial_state,
                     cu_seqlens, chunk_size, output_final_state, workspace, out, final_state)
+
+
+def chunk_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                      beta: torch.Tensor, scale: Optional[float] = None,
+                      initial_state: Optional[torch.Tensor] = None,
+                      cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = 64,
+                      output_final_state: bool = True, out: Optional[torch.Tensor] = None,
+                      final_state: Optional[torch.Tensor] = None
+                      ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """``chunk_fwd`` through ``kda_chunk_fwd_noalloc``: the library's own
+    device buffer (``KDA_NOALLOC_SCRATCH_BYTES`` per device) is the workspace,
+    so the call allocates no device memory when ``out`` (and ``final_state``,
+    if wanted) are given.  Problems whose workspace would exceed that buffer
+    raise ``KdaError`` (KDA_ERR_WORKSPACE_TOO_SMALL)."""
+    return _prefill(lib().kda_chunk_fwd_noalloc, "per_channel", q, k, v, g, beta, scale,
+                    initial_state, cu_seqlens, chunk_size, output_final_state, None, out,
+                    final_state, noalloc=True)
 
 
 def chunk_fwd_scalar_gate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

@@ -21,7 +21,7 @@ ARCH = "gfx950"
 
 SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_chunk_mfma.hip", "kda_chunk_f32.hip",
            "kda_chunk_bwd.hip",
-           "kda_post.hip"]
+           "kda_post.hip", "kda_scratch.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wextra", "-Werror",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -104,11 +104,32 @@ kda_status read_form(const kda_inputs_form *f, kda::Gate *gate, kda::InputForm *
     return KDA_OK;
 }
 
+// Finds the no-allocation workspace of the current device once every argument
+// has been validated; `stream` must belong to that device.
+kda_status noalloc_workspace(void *stream, void **ws) {
+    int dev = -1, sdev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "current device");
+    if (stream) {
+        e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev);
+        if (e != hipSuccess) return hip_fail(e, "device of the stream");
+        if (sdev != dev)
+            return fail(KDA_ERR_INVALID_ARGUMENT,
+                        "the stream belongs to device %d but the current device is %d; the "
+                        "no-allocation workspace is the current device's", sdev, dev);
+    }
+    e = kda::noalloc_scratch(dev, ws);
+    if (e != hipSuccess) return hip_fail(e, "no-allocation workspace");
+    return KDA_OK;
+}
+
+// Shared body of the prefill entry points.  With `noalloc` the workspace
+// arguments are ignored and the library's own device buffer is used.
 kda_status chunk_fwd(kda::Gate gate, kda::InputForm form, const kda_shape *shape, const void *q,
                      const void *k, const void *v, const float *g, const float *beta,
                      float scale, const float *initial_state, const int32_t *cu_seqlens,
                      void *o, float *final_state, void *workspace, size_t workspace_bytes,
-                     void *stream) {
+                     void *stream, bool noalloc = false) {
     if (gate == kda::Gate::Scalar && !g) gate = kda::Gate::None;
     if (gate == kda::Gate::None && g)
         return fail(KDA_ERR_INVALID_ARGUMENT, "g must be NULL when there is no gate");
@@ -138,6 +159,19 @@ kda_status chunk_fwd(kda::Gate gate, kda::InputForm form, const kda_shape *shape
               o == (const void *)beta))
         return fail(KDA_ERR_INVALID_ARGUMENT, "o must not alias an input");
     const size_t need = workspace_for(shape, total);
+    if (noalloc) {
+        if (need > KDA_NOALLOC_SCRATCH_BYTES)
+            return fail(KDA_ERR_WORKSPACE_TOO_SMALL,
+                        "this problem needs %zu bytes of workspace; kda_chunk_fwd_noalloc has %zu "
+                        "(KDA_NOALLOC_SCRATCH_BYTES): call kda_chunk_fwd with a workspace instead",
+                        need, (size_t)KDA_NOALLOC_SCRATCH_BYTES);
+        workspace = nullptr;
+        workspace_bytes = KDA_NOALLOC_SCRATCH_BYTES;
+        if (need > 0) {
+            st = noalloc_workspace(stream, &workspace);
+            if (st != KDA_OK) return st;
+        }
+    }
     if (need > 0 && !workspace)
         return fail(KDA_ERR_INVALID_ARGUMENT, "workspace is NULL (%zu bytes needed)", need);
     if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u))
@@ -254,6 +288,17 @@ kda_status kda_chunk_fwd(const kda_shape *shape, const void *q, const void *k, c
     return chunk_fwd(kda::Gate::PerChannel, kda::InputForm(), shape, q, k, v, g_log_decay, beta,
                      scale, initial_state, cu_seqlens, o, final_state, workspace,
                      workspace_bytes, stream);
+}
+
+kda_status kda_chunk_fwd_noalloc(const kda_shape *shape, const void *q, const void *k,
+                                 const void *v, const float *g_log_decay, const float *beta,
+                                 float scale, const float *initial_state,
+                                 const int32_t *cu_seqlens, void *o, float *final_state,
+                                 void *stream) {
+    g_last_error[0] = '\0';
+    return chunk_fwd(kda::Gate::PerChannel, kda::InputForm(), shape, q, k, v, g_log_decay, beta,
+                     scale, initial_state, cu_seqlens, o, final_state, nullptr, 0, stream,
+                     /*noalloc=*/true);
 }
 
 kda_status kda_chunk_fwd_scalar_gate(const kda_shape *shape, const void *q, const void *k,

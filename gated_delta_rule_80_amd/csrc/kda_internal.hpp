@@ -72,6 +72,11 @@ inline int64_t max_chunks(int64_t total_tokens, int64_t n_seqs, int64_t chunk) {
     return total_tokens / chunk + n_seqs;
 }
 
+// The device address of the no-allocation workspace (KDA_NOALLOC_SCRATCH_BYTES)
+// on `device`, which must be the current device; looked up on the first call
+// per device and kept.
+hipError_t noalloc_scratch(int device, void **ptr);
+
 // MFMA path: (128, 128, 64) with bf16 storage.
 bool mfma_path_supported(int dk, int dv, int chunk, bool bf16);
 size_t mfma_workspace_bytes(int64_t total_tokens, int64_t n_seqs, int heads, int chunk);

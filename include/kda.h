@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 4
+#define KDA_ABI_VERSION 5
 
 typedef enum kda_status {
     KDA_OK = 0,
@@ -187,6 +187,38 @@ kda_status kda_chunk_fwd(const kda_shape *shape, const void *q, const void *k,
                          const float *initial_state, const int32_t *cu_seqlens,
                          void *o, float *final_state, void *workspace,
                          size_t workspace_bytes, void *stream);
+
+/*
+ * Size of the device buffer behind kda_chunk_fwd_noalloc (256 MiB per device).
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+
+/*
+ * kda_chunk_fwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, hosts that forbid hipMalloc.  Same
+ * arguments, semantics and results (bit for bit) as kda_chunk_fwd, without the
+ * workspace: the workspace is a buffer of KDA_NOALLOC_SCRATCH_BYTES that the
+ * library holds in device memory from the moment it is loaded onto a device
+ * until the process ends (each device has its own).  Nothing is allocated or
+ * freed by this call.
+ *   - Problems whose kda_chunk_fwd_workspace_bytes exceeds
+ *     KDA_NOALLOC_SCRATCH_BYTES return KDA_ERR_WORKSPACE_TOO_SMALL before
+ *     anything is enqueued; at d_k = d_v = 128 with bf16 storage the buffer
+ *     holds about 3,700 (chunk, head) records (for example H = 32 heads over
+ *     about 7,300 tokens).  The fp32 path needs no workspace.
+ *   - The buffer belongs to the CURRENT device; `stream` must be a stream of
+ *     that device (NULL = its null stream), else KDA_ERR_INVALID_ARGUMENT.
+ *   - All calls on one device share the buffer, and it keeps the last call's
+ *     contents.  Calls that may overlap on one device (different streams,
+ *     different host threads) race on it; serialise them, for example on one
+ *     stream.  Each call writes every part of the buffer it later reads, so
+ *     nothing needs clearing between calls.
+ */
+kda_status kda_chunk_fwd_noalloc(const kda_shape *shape, const void *q, const void *k,
+                                 const void *v, const float *g_log_decay, const float *beta,
+                                 float scale, const float *initial_state,
+                                 const int32_t *cu_seqlens, void *o, float *final_state,
+                                 void *stream);
 
 /*
  * The same prefill with a scalar gate: one log-decay per (token, head), shared

@@ -14,9 +14,21 @@
 StubRecord g_stub;
 hipError_t g_stub_status = hipSuccess;
 
+int g_stub_device = 0;          // the current device the stub reports
+int g_stub_stream_device = 0;   // the device every non-null stream belongs to
+
 extern "C" const char *hipGetErrorString(hipError_t e) {
     return e == hipSuccess ? "hipSuccess" : "stub launch failure";
 }
+extern "C" hipError_t hipGetDevice(int *device) {
+    *device = g_stub_device;
+    return hipSuccess;
+}
+extern "C" hipError_t hipStreamGetDevice(hipStream_t, hipDevice_t *device) {
+    *device = g_stub_stream_device;
+    return hipSuccess;
+}
+
 namespace kda {
 
 bool decode_supported(int dk, int dv) {
@@ -55,6 +67,12 @@ hipError_t launch_output_rmsnorm_gate(int64_t rows, int dv, bool bf16, const voi
     g_stub.o = out;
     g_stub.q = o;
     return g_stub_status;
+}
+
+// A fake device address per device (never dereferenced).
+hipError_t noalloc_scratch(int device, void **ptr) {
+    *ptr = reinterpret_cast<void *>(uintptr_t(0x7f0000000000ull) + (uintptr_t(device) << 32));
+    return hipSuccess;
 }
 
 bool mfma_path_supported(int dk, int dv, int chunk, bool bf16) {

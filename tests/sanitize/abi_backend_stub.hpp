@@ -19,3 +19,4 @@ struct StubRecord {
 
 extern StubRecord g_stub;
 extern hipError_t g_stub_status;
+extern int g_stub_device, g_stub_stream_device;

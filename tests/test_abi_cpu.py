@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = K.lib()
-    assert lib.kda_abi_version() == 4
+    assert lib.kda_abi_version() == 5
     for code, name in K.STATUS.items():
         assert lib.kda_status_string(code).decode() == name
 
@@ -223,3 +223,23 @@ def test_backward_workspace_query():
     sh = shape(d_k=128, d_v=128, chunk_size=16, dtype_code=K.KDA_F32, seqlen=4096, heads=2)
     assert K.lib().kda_chunk_bwd_workspace_bytes(ctypes.byref(sh)) == \
         (4096 // 16 + 2) * 2 * per_slot(128, 16) * 4
+
+
+def test_noalloc_refuses_before_touching_the_gpu():
+    """kda_chunk_fwd_noalloc validates like kda_chunk_fwd and refuses problems
+    whose workspace exceeds its buffer before any HIP call."""
+    lib = K.lib()
+    P = ctypes.c_void_p(0x100000)
+    O = ctypes.c_void_p(0x200000)
+    f = ctypes.c_float(0.1)
+
+    def call(sh, o=O):
+        return lib.kda_chunk_fwd_noalloc(ctypes.byref(sh) if sh is not None else None, P, P, P,
+                                         P, P, f, None, None, o, None, None)
+    big = shape(seqlen=131072)
+    assert ws(big) > (256 << 20)
+    assert call(big) == 3
+    assert b"kda_chunk_fwd with a workspace" in lib.kda_last_error()
+    assert call(None) == 1
+    assert call(shape(d_k=96, d_v=96)) == 2
+    assert call(shape(), o=P) == 1                     # o aliases an input
