@@ -64,7 +64,7 @@ kda_status check_shape(const kda_shape *s, int64_t *total_tokens) {
         !kda::f32_path_supported(s->d_k, s->d_v, s->chunk_size, bf16))
         return fail(KDA_ERR_UNSUPPORTED,
                     "no kernel for d_k %d d_v %d chunk %d dtype %s (built: 128/128/64 bf16; "
-                    "d in {16,32,64} with chunk in {16,32,64} fp32)",
+                    "d in {16,32,64,128} with chunk in {16,32,64} fp32)",
                     s->d_k, s->d_v, s->chunk_size, bf16 ? "bf16" : "f32");
     *total_tokens = (int64_t)s->batch * s->seqlen;
     if (*total_tokens > INT32_MAX / 2)

@@ -1,13 +1,24 @@
-// kda_chunk_f32.hip -- chunkwise KDA prefill in fp32 for fp32 storage and
-// small widths (d_k = d_v = d in {16, 32, 64}, C in {16, 32, 64}; up to 148 KB
-// of LDS, within gfx950's 160 KB per workgroup).
+// kda_chunk_f32.hip -- chunkwise KDA prefill in fp32 for fp32 storage:
+// d_k = d_v = d in {16, 32, 64} with C in {16, 32, 64}, and d = 128 with
+// C in {16, 32, 64} (up to about 150 KB of LDS, within gfx950's 160 KB per
+// workgroup).
 //
 // Same chunk algebra as the MFMA path ("Understanding Kimi Delta Attention",
 // sections "The triangular system" and "Putting the chunks together", with
 // A = -A_page so that (I + A) T = I), evaluated entirely in fp32 on the vector
 // ALUs with every chunk operand resident in LDS.  This is the path whose
 // accuracy budget is 1e-4; its speed is not a target.  One workgroup handles
-// one (sequence, head) and walks its chunks in order with the state in LDS.
+// one (sequence, head, value tile) and walks its chunks in order with its
+// columns of the state in LDS.  Value columns evolve independently, so the
+// tiles need no communication; each recomputes the value-independent chunk
+// factors (A, T, H) for itself.
+//
+// Per chunk, with L_j = k_j e^{G_j}:  Z = U - W S = T Diag(beta) (V - L S),
+// so neither W nor U is ever formed: Y = V - L S overwrites the value tile,
+// then Z = T Diag(beta) Y, O = (s Q e^{G}) S + H Z, and
+// S <- Diag(e^{G_C}) S + (K e^{G_C - G})^T Z.  Every decay factor is the
+// exponential of a difference of cumulative logs (or of G itself), as the
+// derivation recommends, so any finite log-decay stays in range.
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
@@ -16,24 +27,34 @@ namespace f32_path {
 
 constexpr int THREADS = 256;
 
+// Value columns per workgroup: the whole width up to 64, else 16 (so the
+// q, k, G rows of a 64-token chunk at d = 128 still fit in LDS).
+__host__ __device__ inline int value_tile(int dv) { return dv <= 64 ? dv : 16; }
+
 struct Lds {
-    int q, k, G, v, beta, nrm, A, T, W, U, S, total;   // offsets in floats (H reuses A)
+    int P, VP, CP;                                      // row pitches (floats)
+    int q, k, G, v, z, beta, nrm, A, T, S, total;       // offsets in floats (H reuses A)
 };
 
+// Rows are padded by one float so that threads walking different rows of the
+// same column hit different LDS banks.
 __host__ __device__ inline Lds lds_layout(int dk, int dv, int C) {
     Lds L;
+    const int VT = value_tile(dv);
+    L.P = dk + 1;
+    L.VP = VT + 1;
+    L.CP = C + 1;
     int o = 0;
-    L.q = o; o += C * dk;
-    L.k = o; o += C * dk;
-    L.G = o; o += C * dk;
-    L.v = o; o += C * dv;
+    L.q = o; o += C * L.P;
+    L.k = o; o += C * L.P;
+    L.G = o; o += C * L.P;
+    L.v = o; o += C * L.VP;   // v, then Y = V - L S
+    L.z = o; o += C * L.VP;   // Z = T Diag(beta) Y
     L.beta = o; o += C;
-    L.nrm = o; o += 2 * C;   // inverse L2 norms of the rows of k and q
-    L.A = o; o += C * C;
-    L.T = o; o += C * C;
-    L.W = o; o += C * dk;
-    L.U = o; o += C * dv;
-    L.S = o; o += dk * dv;
+    L.nrm = o; o += 2 * C;    // inverse L2 norms of the rows of k and q
+    L.A = o; o += C * L.CP;
+    L.T = o; o += C * L.CP;
+    L.S = o; o += dk * L.VP;
     L.total = o;
     return L;
 }
@@ -45,13 +66,16 @@ __global__ __launch_bounds__(THREADS) void kda_chunk_f32_kernel(
     const float *__restrict__ s0, float *__restrict__ s_final, float *__restrict__ o) {
     extern __shared__ float sm[];
     const Lds L = lds_layout(dk, dv, C);
-    float *sq = sm + L.q, *sk = sm + L.k, *sG = sm + L.G, *sv = sm + L.v, *sb = sm + L.beta;
-    float *snrm = sm + L.nrm;
-    float *sA = sm + L.A, *sT = sm + L.T, *sW = sm + L.W, *sU = sm + L.U;
+    const int P = L.P, VP = L.VP, CP = L.CP;
+    const int VT = value_tile(dv), n_vt = dv / VT;
+    float *sq = sm + L.q, *sk = sm + L.k, *sG = sm + L.G, *sv = sm + L.v, *sz = sm + L.z;
+    float *sb = sm + L.beta, *snrm = sm + L.nrm;
+    float *sA = sm + L.A, *sT = sm + L.T, *sS = sm + L.S;
     float *sH = sA;   // H is built once T no longer needs A
-    float *sS = sm + L.S;
 
-    const int n = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
+    const int vt = blockIdx.x % n_vt, pair_id = blockIdx.x / n_vt;
+    const int n = pair_id / H, h = pair_id - n * H;
+    const int c0 = vt * VT;   // first value column of this tile
     const int tid = threadIdx.x;
     int ts, te;
     if (cu) {
@@ -64,7 +88,10 @@ __global__ __launch_bounds__(THREADS) void kda_chunk_f32_kernel(
         te = ts + row_len;
     }
     const size_t pair = (size_t)n * H + h;
-    for (int e = tid; e < dk * dv; e += THREADS) sS[e] = s0 ? s0[pair * dk * dv + e] : 0.f;
+    for (int e = tid; e < dk * VT; e += THREADS) {
+        const int r = e / VT, c = e - r * VT;
+        sS[r * VP + c] = s0 ? s0[pair * dk * dv + (size_t)r * dv + c0 + c] : 0.f;
+    }
     __syncthreads();
 
     for (int t0 = ts; t0 < te; t0 += C) {
@@ -74,19 +101,19 @@ __global__ __launch_bounds__(THREADS) void kda_chunk_f32_kernel(
             const int i = e / dk, c = e - i * dk;
             const bool ok = i < len;
             const size_t a = ((size_t)(t0 + i) * H + h) * dk + c;
-            sq[e] = ok ? q[a] : 0.f;
-            sk[e] = ok ? k[a] : 0.f;
+            sq[i * P + c] = ok ? q[a] : 0.f;
+            sk[i * P + c] = ok ? k[a] : 0.f;
             // gate 0: log-decay per channel; 1: one per (token, head); 2: none
             float gv = 0.f;
             if (ok && gate != 2) {
                 gv = gate == 0 ? g[a] : g[(size_t)(t0 + i) * H + h];
                 if (form & kFormGateLogit) gv = log_sigmoid(gv);
             }
-            sG[e] = gv;
+            sG[i * P + c] = gv;
         }
-        for (int e = tid; e < C * dv; e += THREADS) {
-            const int i = e / dv, c = e - i * dv;
-            sv[e] = i < len ? v[((size_t)(t0 + i) * H + h) * dv + c] : 0.f;
+        for (int e = tid; e < C * VT; e += THREADS) {
+            const int i = e / VT, c = e - i * VT;
+            sv[i * VP + c] = i < len ? v[((size_t)(t0 + i) * H + h) * dv + c0 + c] : 0.f;
         }
         for (int i = tid; i < C; i += THREADS) {
             float b = i < len ? beta[(size_t)(t0 + i) * H + h] : 0.f;
@@ -96,16 +123,16 @@ __global__ __launch_bounds__(THREADS) void kda_chunk_f32_kernel(
         __syncthreads();
         if (form & kFormL2Norm) {   // q, k rows divided by sqrt(sum of squares + eps)
             for (int x = tid; x < 2 * C; x += THREADS) {
-                const float *row = (x < C ? sk : sq) + (x % C) * dk;
+                const float *row = (x < C ? sk : sq) + (x % C) * P;
                 float ss = 0.f;
                 for (int c = 0; c < dk; ++c) ss += row[c] * row[c];
                 snrm[x] = 1.f / sqrtf(ss + eps);
             }
             __syncthreads();
             for (int e = tid; e < C * dk; e += THREADS) {
-                const int i = e / dk;
-                sk[e] *= snrm[i];
-                sq[e] *= snrm[C + i];
+                const int i = e / dk, c = e - i * dk;
+                sk[i * P + c] *= snrm[i];
+                sq[i * P + c] *= snrm[C + i];
             }
             __syncthreads();
         }
@@ -113,8 +140,8 @@ __global__ __launch_bounds__(THREADS) void kda_chunk_f32_kernel(
         for (int c = tid; c < dk; c += THREADS) {
             float run = 0.f;
             for (int i = 0; i < C; ++i) {
-                run += sG[i * dk + c];
-                sG[i * dk + c] = run;
+                run += sG[i * P + c];
+                sG[i * P + c] = run;
             }
         }
         __syncthreads();
@@ -124,83 +151,78 @@ __global__ __launch_bounds__(THREADS) void kda_chunk_f32_kernel(
             float a = 0.f;
             if (j < i)
                 for (int c = 0; c < dk; ++c)
-                    a += sk[i * dk + c] * expf(sG[i * dk + c] - sG[j * dk + c]) * sk[j * dk + c];
-            sA[e] = (j < i) ? sb[i] * a : 0.f;
+                    a += sk[i * P + c] * expf(sG[i * P + c] - sG[j * P + c]) * sk[j * P + c];
+            sA[i * CP + j] = (j < i) ? sb[i] * a : 0.f;
         }
         __syncthreads();
         // T = (I + A)^{-1}: column j by forward substitution (one thread per column).
         for (int j = tid; j < C; j += THREADS) {
             for (int i = 0; i < C; ++i) {
                 float s = (i == j) ? 1.f : 0.f;
-                for (int kk = j; kk < i; ++kk) s -= sA[i * C + kk] * sT[kk * C + j];
-                sT[i * C + j] = (i < j) ? 0.f : s;
+                for (int kk = j; kk < i; ++kk) s -= sA[i * CP + kk] * sT[kk * CP + j];
+                sT[i * CP + j] = (i < j) ? 0.f : s;
             }
         }
+        // Y = V - L S (in place of V), L_j = k_j e^{G_j}: independent of A and T.
+        for (int e = tid; e < C * VT; e += THREADS) {
+            const int j = e / VT, c = e - j * VT;
+            float acc = sv[j * VP + c];
+            for (int r = 0; r < dk; ++r)
+                acc -= sk[j * P + r] * expf(sG[j * P + r]) * sS[r * VP + c];
+            sv[j * VP + c] = acc;
+        }
         __syncthreads();
-        // H_ij = s sum_c q_ic k_jc e^{G_ic - G_jc}  (j <= i), into A's storage.
+        // H_ij = s sum_c q_ic k_jc e^{G_ic - G_jc}  (j <= i), into A's storage;
+        // Z = T Diag(beta) Y alongside (it reads T and Y only).
         for (int e = tid; e < C * C; e += THREADS) {
             const int i = e / C, j = e - i * C;
             float hh = 0.f;
             if (j <= i)
                 for (int c = 0; c < dk; ++c)
-                    hh += sq[i * dk + c] * expf(sG[i * dk + c] - sG[j * dk + c]) * sk[j * dk + c];
-            sH[e] = (j <= i) ? scale * hh : 0.f;
+                    hh += sq[i * P + c] * expf(sG[i * P + c] - sG[j * P + c]) * sk[j * P + c];
+            sH[i * CP + j] = (j <= i) ? scale * hh : 0.f;
         }
-        __syncthreads();
-        // W = T Diag(beta) (K e^{G}),  U = T Diag(beta) V.
-        for (int e = tid; e < C * dk; e += THREADS) {
-            const int i = e / dk, c = e - i * dk;
+        for (int e = tid; e < C * VT; e += THREADS) {
+            const int i = e / VT, c = e - i * VT;
             float acc = 0.f;
-            for (int j = 0; j <= i; ++j)
-                acc += sT[i * C + j] * sb[j] * sk[j * dk + c] * expf(sG[j * dk + c]);
-            sW[e] = acc;
-        }
-        for (int e = tid; e < C * dv; e += THREADS) {
-            const int i = e / dv, c = e - i * dv;
-            float acc = 0.f;
-            for (int j = 0; j <= i; ++j) acc += sT[i * C + j] * sb[j] * sv[j * dv + c];
-            sU[e] = acc;
-        }
-        __syncthreads();
-        // Z = U - W S (into sU).
-        for (int e = tid; e < C * dv; e += THREADS) {
-            const int i = e / dv, c = e - i * dv;
-            float acc = sU[e];
-            for (int r = 0; r < dk; ++r) acc -= sW[i * dk + r] * sS[r * dv + c];
-            sU[e] = acc;
+            for (int j = 0; j <= i; ++j) acc += sT[i * CP + j] * sb[j] * sv[j * VP + c];
+            sz[i * VP + c] = acc;
         }
         __syncthreads();
         // O = (s Q e^{G}) S + H Z.
-        for (int e = tid; e < C * dv; e += THREADS) {
-            const int i = e / dv, c = e - i * dv;
+        for (int e = tid; e < C * VT; e += THREADS) {
+            const int i = e / VT, c = e - i * VT;
             if (i >= len) continue;
             float acc = 0.f;
             for (int r = 0; r < dk; ++r)
-                acc += scale * sq[i * dk + r] * expf(sG[i * dk + r]) * sS[r * dv + c];
-            for (int j = 0; j <= i; ++j) acc += sH[i * C + j] * sU[j * dv + c];
-            o[((size_t)(t0 + i) * H + h) * dv + c] = acc;
+                acc += scale * sq[i * P + r] * expf(sG[i * P + r]) * sS[r * VP + c];
+            for (int j = 0; j <= i; ++j) acc += sH[i * CP + j] * sz[j * VP + c];
+            o[((size_t)(t0 + i) * H + h) * dv + c0 + c] = acc;
         }
         __syncthreads();
         // S <- Diag(e^{G_C}) S + (K e^{G_C - G})^T Z.
-        for (int e = tid; e < dk * dv; e += THREADS) {
-            const int r = e / dv, c = e - r * dv;
-            const float gl = sG[(C - 1) * dk + r];
-            float acc = expf(gl) * sS[e];
+        for (int e = tid; e < dk * VT; e += THREADS) {
+            const int r = e / VT, c = e - r * VT;
+            const float gl = sG[(C - 1) * P + r];
+            float acc = expf(gl) * sS[r * VP + c];
             for (int j = 0; j < C; ++j)
-                acc += sk[j * dk + r] * expf(gl - sG[j * dk + r]) * sU[j * dv + c];
-            sS[e] = acc;
+                acc += sk[j * P + r] * expf(gl - sG[j * P + r]) * sz[j * VP + c];
+            sS[r * VP + c] = acc;
         }
         __syncthreads();
     }
     if (s_final)
-        for (int e = tid; e < dk * dv; e += THREADS) s_final[pair * dk * dv + e] = sS[e];
+        for (int e = tid; e < dk * VT; e += THREADS) {
+            const int r = e / VT, c = e - r * VT;
+            s_final[pair * dk * dv + (size_t)r * dv + c0 + c] = sS[r * VP + c];
+        }
 }
 
 }  // namespace f32_path
 
 bool f32_path_supported(int dk, int dv, int chunk, bool bf16) {
     if (bf16 || dk != dv) return false;
-    if (!(dk == 16 || dk == 32 || dk == 64)) return false;
+    if (!(dk == 16 || dk == 32 || dk == 64 || dk == 128)) return false;
     if (!(chunk == 16 || chunk == 32 || chunk == 64)) return false;
     return (size_t)f32_path::lds_layout(dk, dv, chunk).total * sizeof(float) <= 163840;
 }
@@ -215,8 +237,9 @@ hipError_t launch_chunk_fwd_f32(const ChunkProblem &p) {
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    if (!launch_fits((int64_t)p.n_seqs * p.heads, THREADS)) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(kda_chunk_f32_kernel, dim3(p.n_seqs * p.heads), dim3(THREADS), lds,
+    const int64_t blocks = (int64_t)p.n_seqs * p.heads * (p.dv / value_tile(p.dv));
+    if (!launch_fits(blocks, THREADS)) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(kda_chunk_f32_kernel, dim3((unsigned)blocks), dim3(THREADS), lds,
                        p.stream, static_cast<const float *>(p.q), static_cast<const float *>(p.k),
                        static_cast<const float *>(p.v), p.g, (int)p.gate, p.beta, p.scale,
                        p.form.flags(), p.form.eps, p.heads, p.dk, p.dv, p.chunk, p.seqlen, p.cu,

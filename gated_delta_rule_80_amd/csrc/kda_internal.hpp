@@ -82,7 +82,7 @@ bool mfma_path_supported(int dk, int dv, int chunk, bool bf16);
 size_t mfma_workspace_bytes(int64_t total_tokens, int64_t n_seqs, int heads, int chunk);
 hipError_t launch_chunk_fwd_mfma(const ChunkProblem &p);
 
-// fp32 path: d_k == d_v in {16, 32, 64}, C in {16, 32, 64}, fp32 storage.
+// fp32 path: d_k == d_v in {16, 32, 64, 128}, C in {16, 32, 64}, fp32 storage.
 bool f32_path_supported(int dk, int dv, int chunk, bool bf16);
 size_t f32_workspace_bytes(int64_t total_tokens, int64_t n_seqs, int heads, int chunk);
 hipError_t launch_chunk_fwd_f32(const ChunkProblem &p);

@@ -76,7 +76,8 @@ typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  *   dtype      storage type of q, k, v, o
  * Built combinations (d_k, d_v, C, dtype):
  *   (128, 128, 64, KDA_BF16)  MFMA path (fp16 operands, fp32 accumulation)
- *   (d, d, C, KDA_F32) with d in {16, 32, 64}, C in {16, 32, 64}: fp32 path
+ *   (d, d, C, KDA_F32) with d in {16, 32, 64, 128}, C in {16, 32, 64}: fp32
+ *                             path (fp32 arithmetic throughout)
  * Everything else returns KDA_ERR_UNSUPPORTED.
  */
 typedef struct kda_shape {

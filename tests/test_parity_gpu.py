@@ -480,6 +480,28 @@ def test_fp32_path(d, C, T):
     check_prefill(small(H=2, T=T, dk=d, dv=d, dtype="f32"), C)
 
 
+def test_fp32_d128_prefill_workload2_shape():
+    """fp32 storage at d_k = d_v = 128, C = 64 on the shape of workload 2
+    (B = 2, H = 8, T = 2048, S0 ~ N(0, 0.01^2)): the fp32 path, 1e-4."""
+    inp = W.make_prefill(H=8, dk=128, dv=128, dtype="f32", z_range=(2.0, 9.0), seed=1002, B=2,
+                         T=2048, s0_std=0.01)
+    check_prefill(inp, 64)
+
+
+def test_fp32_d128_packed_ragged_strong_decay():
+    """fp32 at d = 128, C = 64: packed sequences with ragged tails (and an
+    empty one), log-decays in [-10, 0] on every other channel among weak ones."""
+    inp = small(H=3, dk=128, dv=128, dtype="f32", lengths=[1, 63, 64, 65, 0, 200, 333],
+                s0_std=0.05, seed=71)
+    inp = _strong_gate(inp, -10.0, 0.0, seed=72, mixed=True)
+    check_prefill(inp, 64)
+
+
+@pytest.mark.parametrize("C", [16, 32])
+def test_fp32_d128_smaller_chunks(C):
+    check_prefill(small(H=2, T=150, dk=128, dv=128, dtype="f32"), C)
+
+
 def test_fp32_varlen():
     check_prefill(small(H=2, dk=16, dv=16, dtype="f32", lengths=[5, 0, 33, 16, 1]), 16)
 
