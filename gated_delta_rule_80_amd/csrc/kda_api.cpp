@@ -106,12 +106,12 @@ kda_status read_form(const kda_inputs_form *f, kda::Gate *gate, kda::InputForm *
 
 // Finds the no-allocation workspace of the current device once every argument
 // has been validated; `stream` must belong to that device.
-kda_status noalloc_workspace(void *stream, void **ws) {
+kda_status noalloc_workspace(hipStream_t stream, void **ws) {
     int dev = -1, sdev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "current device");
     if (stream) {
-        e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev);
+        e = hipStreamGetDevice(stream, &sdev);
         if (e != hipSuccess) return hip_fail(e, "device of the stream");
         if (sdev != dev)
             return fail(KDA_ERR_INVALID_ARGUMENT,
@@ -129,7 +129,7 @@ kda_status chunk_fwd(kda::Gate gate, kda::InputForm form, const kda_shape *shape
                      const void *k, const void *v, const float *g, const float *beta,
                      float scale, const float *initial_state, const int32_t *cu_seqlens,
                      void *o, float *final_state, void *workspace, size_t workspace_bytes,
-                     void *stream, bool noalloc = false) {
+                     hipStream_t stream, bool noalloc = false) {
     if (gate == kda::Gate::Scalar && !g) gate = kda::Gate::None;
     if (gate == kda::Gate::None && g)
         return fail(KDA_ERR_INVALID_ARGUMENT, "g must be NULL when there is no gate");
@@ -203,7 +203,7 @@ kda_status chunk_fwd(kda::Gate gate, kda::InputForm form, const kda_shape *shape
     p.s_final = final_state;
     p.workspace = workspace;
     p.workspace_bytes = workspace_bytes;
-    p.stream = static_cast<hipStream_t>(stream);
+    p.stream = stream;
 
     hipError_t e = kda::mfma_path_supported(p.dk, p.dv, p.chunk, p.bf16)
                        ? kda::launch_chunk_fwd_mfma(p)
@@ -218,7 +218,7 @@ kda_status decode_step(kda::Gate gate, kda::InputForm form, int32_t num_sessions
                        int32_t num_heads, int32_t d_k, int32_t d_v, int dtype,
                        const void *q, const void *k, const void *v, const float *g,
                        const float *beta, float scale, float *state_inout, void *o,
-                       void *stream) {
+                       hipStream_t stream) {
     if (gate == kda::Gate::Scalar && !g) gate = kda::Gate::None;
     if (gate == kda::Gate::None && g)
         return fail(KDA_ERR_INVALID_ARGUMENT, "g must be NULL when there is no gate");
@@ -245,7 +245,7 @@ kda_status decode_step(kda::Gate gate, kda::InputForm form, int32_t num_sessions
         return fail(KDA_ERR_INVALID_ARGUMENT, "o must not alias state_inout");
     hipError_t e = kda::launch_decode((int)pairs, d_k, d_v, dtype == KDA_BF16, gate, form, q, k, v,
                                       gate == kda::Gate::None ? nullptr : g, beta, scale,
-                                      state_inout, o, static_cast<hipStream_t>(stream));
+                                      state_inout, o, stream);
     if (e != hipSuccess) return hip_fail(e, "decode step launch");
     return KDA_OK;
 }
@@ -283,7 +283,7 @@ kda_status kda_chunk_fwd(const kda_shape *shape, const void *q, const void *k, c
                          const float *g_log_decay, const float *beta, float scale,
                          const float *initial_state, const int32_t *cu_seqlens, void *o,
                          float *final_state, void *workspace, size_t workspace_bytes,
-                         void *stream) {
+                         hipStream_t stream) {
     g_last_error[0] = '\0';
     return chunk_fwd(kda::Gate::PerChannel, kda::InputForm(), shape, q, k, v, g_log_decay, beta,
                      scale, initial_state, cu_seqlens, o, final_state, workspace,
@@ -294,7 +294,7 @@ kda_status kda_chunk_fwd_noalloc(const kda_shape *shape, const void *q, const vo
                                  const void *v, const float *g_log_decay, const float *beta,
                                  float scale, const float *initial_state,
                                  const int32_t *cu_seqlens, void *o, float *final_state,
-                                 void *stream) {
+                                 hipStream_t stream) {
     g_last_error[0] = '\0';
     return chunk_fwd(kda::Gate::PerChannel, kda::InputForm(), shape, q, k, v, g_log_decay, beta,
                      scale, initial_state, cu_seqlens, o, final_state, nullptr, 0, stream,
@@ -305,7 +305,7 @@ kda_status kda_chunk_fwd_scalar_gate(const kda_shape *shape, const void *q, cons
                                      const void *v, const float *g_log_decay, const float *beta,
                                      float scale, const float *initial_state,
                                      const int32_t *cu_seqlens, void *o, float *final_state,
-                                     void *workspace, size_t workspace_bytes, void *stream) {
+                                     void *workspace, size_t workspace_bytes, hipStream_t stream) {
     g_last_error[0] = '\0';
     return chunk_fwd(kda::Gate::Scalar, kda::InputForm(), shape, q, k, v, g_log_decay, beta,
                      scale, initial_state, cu_seqlens, o, final_state, workspace,
@@ -316,7 +316,7 @@ kda_status kda_chunk_fwd_ex(const kda_shape *shape, const kda_inputs_form *form,
                             const void *k, const void *v, const float *g_log_decay,
                             const float *beta, float scale, const float *initial_state,
                             const int32_t *cu_seqlens, void *o, float *final_state,
-                            void *workspace, size_t workspace_bytes, void *stream) {
+                            void *workspace, size_t workspace_bytes, hipStream_t stream) {
     g_last_error[0] = '\0';
     kda::Gate gate = kda::Gate::PerChannel;
     kda::InputForm f;
@@ -331,7 +331,7 @@ kda_status kda_chunk_fwd_ex(const kda_shape *shape, const kda_inputs_form *form,
 kda_status kda_decode_step(int32_t num_sessions, int32_t num_heads, int32_t d_k, int32_t d_v,
                            kda_dtype dtype, const void *q, const void *k, const void *v,
                            const float *g, const float *beta, float scale, float *state_inout,
-                           void *o, void *stream) {
+                           void *o, hipStream_t stream) {
     g_last_error[0] = '\0';
     return decode_step(kda::Gate::PerChannel, kda::InputForm(), num_sessions, num_heads, d_k, d_v,
                        dtype_code(dtype), q, k, v, g, beta, scale, state_inout, o, stream);
@@ -341,7 +341,7 @@ kda_status kda_decode_step_scalar_gate(int32_t num_sessions, int32_t num_heads, 
                                        int32_t d_v, kda_dtype dtype, const void *q,
                                        const void *k, const void *v, const float *g,
                                        const float *beta, float scale, float *state_inout,
-                                       void *o, void *stream) {
+                                       void *o, hipStream_t stream) {
     g_last_error[0] = '\0';
     return decode_step(kda::Gate::Scalar, kda::InputForm(), num_sessions, num_heads, d_k, d_v,
                        dtype_code(dtype), q, k, v, g, beta, scale, state_inout, o, stream);
@@ -350,7 +350,7 @@ kda_status kda_decode_step_scalar_gate(int32_t num_sessions, int32_t num_heads, 
 kda_status kda_decode_step_ex(int32_t num_sessions, int32_t num_heads, int32_t d_k, int32_t d_v,
                               kda_dtype dtype, const kda_inputs_form *form, const void *q,
                               const void *k, const void *v, const float *g, const float *beta,
-                              float scale, float *state_inout, void *o, void *stream) {
+                              float scale, float *state_inout, void *o, hipStream_t stream) {
     g_last_error[0] = '\0';
     kda::Gate gate = kda::Gate::PerChannel;
     kda::InputForm f;
@@ -365,7 +365,7 @@ kda_status kda_decode_step_ex(int32_t num_sessions, int32_t num_heads, int32_t d
 
 kda_status kda_output_rmsnorm_gate(int64_t rows, int32_t d_v, kda_dtype dtype, const void *o,
                                    const void *gate, const float *weight, float eps, void *out,
-                                   void *stream) {
+                                   hipStream_t stream) {
     g_last_error[0] = '\0';
     const int dt = dtype_code(dtype);
     if (!known_dtype(dt)) return fail(KDA_ERR_INVALID_ARGUMENT, "unknown dtype %d", dt);
@@ -386,7 +386,7 @@ kda_status kda_output_rmsnorm_gate(int64_t rows, int32_t d_v, kda_dtype dtype, c
         return fail(KDA_ERR_INVALID_ARGUMENT, "o / gate / out / weight are misaligned");
     if (out == gate) return fail(KDA_ERR_INVALID_ARGUMENT, "out must not alias gate");
     hipError_t e = kda::launch_output_rmsnorm_gate(rows, d_v, dt == KDA_BF16, o, gate, weight,
-                                                   eps, out, static_cast<hipStream_t>(stream));
+                                                   eps, out, stream);
     if (e != hipSuccess) return hip_fail(e, "output stage launch");
     return KDA_OK;
 }
@@ -405,7 +405,7 @@ kda_status kda_chunk_bwd(const kda_shape *shape, const void *q, const void *k, c
                          const float *initial_state, const int32_t *cu_seqlens, const void *d_o,
                          const float *d_final_state, float *dq, float *dk, float *dv, float *dg,
                          float *dbeta, float *d_initial_state, void *workspace,
-                         size_t workspace_bytes, void *stream) {
+                         size_t workspace_bytes, hipStream_t stream) {
     g_last_error[0] = '\0';
     if (!shape) return fail(KDA_ERR_INVALID_ARGUMENT, "shape is NULL");
     if (!known_dtype(dtype_code(shape->dtype)))
@@ -476,7 +476,7 @@ kda_status kda_chunk_bwd(const kda_shape *shape, const void *q, const void *k, c
     p.dbeta = dbeta;
     p.ds0 = d_initial_state;
     p.work = static_cast<float *>(workspace);
-    p.stream = static_cast<hipStream_t>(stream);
+    p.stream = stream;
     hipError_t e = kda::launch_chunk_bwd(p);
     if (e != hipSuccess) return hip_fail(e, "chunk backward launch");
     return KDA_OK;

@@ -25,8 +25,10 @@
  *     row-major and contiguous in the layouts stated below; the library never
  *     allocates, frees or retains them.  They must stay valid until the work
  *     enqueued on `stream` has completed.
- *   - `stream` is a hipStream_t (NULL = the null stream).  All work is
- *     enqueued on it in order; calls return without synchronising.
+ *   - `stream` is a hipStream_t, declared here by its underlying type
+ *     `struct ihipStream_t *` so that this header needs no HIP header
+ *     (NULL = the null stream).  All work is enqueued on it in order; calls
+ *     return without synchronising.
  *   - Arguments are validated on the host before anything is enqueued.  On any
  *     error nothing is enqueued, no output is touched, and a status other than
  *     KDA_OK is returned; kda_last_error() then describes the cause (the text
@@ -51,6 +53,9 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* The HIP stream type: hipStream_t is a pointer to this (opaque) struct. */
+struct ihipStream_t;
 
 #define KDA_ABI_VERSION 5
 
@@ -187,7 +192,7 @@ kda_status kda_chunk_fwd(const kda_shape *shape, const void *q, const void *k,
                          const float *beta, float scale,
                          const float *initial_state, const int32_t *cu_seqlens,
                          void *o, float *final_state, void *workspace,
-                         size_t workspace_bytes, void *stream);
+                         size_t workspace_bytes, struct ihipStream_t *stream);
 
 /*
  * Size of the device buffer behind kda_chunk_fwd_noalloc (256 MiB per device).
@@ -219,7 +224,7 @@ kda_status kda_chunk_fwd_noalloc(const kda_shape *shape, const void *q, const vo
                                  const void *v, const float *g_log_decay, const float *beta,
                                  float scale, const float *initial_state,
                                  const int32_t *cu_seqlens, void *o, float *final_state,
-                                 void *stream);
+                                 struct ihipStream_t *stream);
 
 /*
  * The same prefill with a scalar gate: one log-decay per (token, head), shared
@@ -244,7 +249,7 @@ kda_status kda_chunk_fwd_scalar_gate(const kda_shape *shape, const void *q,
                                      const float *initial_state,
                                      const int32_t *cu_seqlens, void *o,
                                      float *final_state, void *workspace,
-                                     size_t workspace_bytes, void *stream);
+                                     size_t workspace_bytes, struct ihipStream_t *stream);
 
 /*
  * One recurrent decode step for num_sessions x num_heads independent pairs
@@ -264,7 +269,7 @@ kda_status kda_decode_step(int32_t num_sessions, int32_t num_heads, int32_t d_k,
                            int32_t d_v, kda_dtype dtype, const void *q,
                            const void *k, const void *v, const float *g,
                            const float *beta, float scale, float *state_inout,
-                           void *o, void *stream);
+                           void *o, struct ihipStream_t *stream);
 
 /*
  * kda_decode_step with a scalar gate (see kda_chunk_fwd_scalar_gate):
@@ -278,7 +283,7 @@ kda_status kda_decode_step_scalar_gate(int32_t num_sessions, int32_t num_heads,
                                        const void *v, const float *g,
                                        const float *beta, float scale,
                                        float *state_inout, void *o,
-                                       void *stream);
+                                       struct ihipStream_t *stream);
 
 /*
  * kda_chunk_fwd with the inputs in the form `form` describes (see
@@ -292,7 +297,7 @@ kda_status kda_chunk_fwd_ex(const kda_shape *shape, const kda_inputs_form *form,
                             float scale, const float *initial_state,
                             const int32_t *cu_seqlens, void *o,
                             float *final_state, void *workspace,
-                            size_t workspace_bytes, void *stream);
+                            size_t workspace_bytes, struct ihipStream_t *stream);
 
 /*
  * kda_decode_step with the inputs in the form `form` describes; g is
@@ -303,7 +308,7 @@ kda_status kda_decode_step_ex(int32_t num_sessions, int32_t num_heads,
                               const kda_inputs_form *form, const void *q,
                               const void *k, const void *v, const float *g,
                               const float *beta, float scale,
-                              float *state_inout, void *o, void *stream);
+                              float *state_inout, void *o, struct ihipStream_t *stream);
 
 /*
  * Output stage of a KDA layer after the recurrence: RMS normalisation of each
@@ -325,7 +330,7 @@ kda_status kda_decode_step_ex(int32_t num_sessions, int32_t num_heads,
 kda_status kda_output_rmsnorm_gate(int64_t rows, int32_t d_v, kda_dtype dtype,
                                    const void *o, const void *gate,
                                    const float *weight, float eps, void *out,
-                                   void *stream);
+                                   struct ihipStream_t *stream);
 
 /*
  * Gradients of kda_chunk_fwd (per-channel log-decays, plain inputs) for the
@@ -369,7 +374,7 @@ kda_status kda_chunk_bwd(const kda_shape *shape, const void *q, const void *k,
                          const float *d_final_state, float *dq, float *dk,
                          float *dv, float *dg, float *dbeta,
                          float *d_initial_state, void *workspace,
-                         size_t workspace_bytes, void *stream);
+                         size_t workspace_bytes, struct ihipStream_t *stream);
 
 #ifdef __cplusplus
 }

@@ -196,20 +196,20 @@ static void prefill_checks() {
 
 static void noalloc_checks() {
     kda_shape s = bf16_shape(1, 2000, 8);
-    auto call = [](const kda_shape &sh, void *stream) {
+    auto call = [](const kda_shape &sh, hipStream_t stream) {
         return kda_chunk_fwd_noalloc(&sh, dev(1), dev(2), dev(3), devf(4), devf(5), 0.1f,
                                      nullptr, nullptr, dev(7), devf(9), stream);
     };
     // Fits: the launcher receives the device's scratch address as its workspace.
     CHECK(kda_chunk_fwd_workspace_bytes(&s) <= KDA_NOALLOC_SCRATCH_BYTES);
     g_stub_device = g_stub_stream_device = 3;
-    CHECK(call(s, dev(30)) == KDA_OK && g_stub.kind == StubRecord::PrefillMfma);
+    CHECK(call(s, static_cast<hipStream_t>(dev(30))) == KDA_OK && g_stub.kind == StubRecord::PrefillMfma);
     CHECK(g_stub.prefill.workspace == reinterpret_cast<void *>(0x7f0000000000ull + (3ull << 32)));
     CHECK(g_stub.prefill.workspace_bytes == KDA_NOALLOC_SCRATCH_BYTES);
     CHECK(call(s, nullptr) == KDA_OK);
     // A stream of another device is refused (the buffer is the current device's).
     g_stub_stream_device = 1;
-    CHECK(call(s, dev(30)) == KDA_ERR_INVALID_ARGUMENT);
+    CHECK(call(s, static_cast<hipStream_t>(dev(30))) == KDA_ERR_INVALID_ARGUMENT);
     CHECK(std::strstr(kda_last_error(), "device 1") != nullptr);
     g_stub_device = g_stub_stream_device = 0;
     // Too large for the buffer: refused with a clear message, nothing enqueued.

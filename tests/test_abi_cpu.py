@@ -243,3 +243,24 @@ def test_noalloc_refuses_before_touching_the_gpu():
     assert call(None) == 1
     assert call(shape(d_k=96, d_v=96)) == 2
     assert call(shape(), o=P) == 1                     # o aliases an input
+
+
+@pytest.mark.parametrize("hip_first", [True, False])
+def test_header_compiles_as_c_next_to_the_hip_headers(tmp_path, hip_first):
+    """kda.h is plain C99, and a hipStream_t passes as its stream argument
+    whichever header is included first."""
+    if not os.path.exists("/opt/rocm/include/hip/hip_runtime_api.h"):
+        pytest.skip("HIP headers not available")
+    inc = ['#include <hip/hip_runtime_api.h>', '#include "kda.h"']
+    src = "\n".join(inc if hip_first else inc[::-1]) + """
+kda_status f(hipStream_t s) {
+    return kda_decode_step(1, 1, 128, 128, KDA_BF16, 0, 0, 0, 0, 0, 1.f, 0, 0, s);
+}
+"""
+    c = tmp_path / "use.c"
+    c.write_text(src)
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic",
+                        "-D__HIP_PLATFORM_AMD__", "-isystem", "/opt/rocm/include", "-I" + ROOT + "/include",
+                        "-c", str(c), "-o", str(tmp_path / "use.o")], capture_output=True,
+                       text=True)
+    assert r.returncode == 0, r.stderr
