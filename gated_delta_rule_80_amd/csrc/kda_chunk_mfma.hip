@@ -69,11 +69,15 @@ constexpr float MIN_LOG_DECAY = -10.f;
 #ifndef KDA_INTER_L2R
 #define KDA_INTER_L2R 4
 #endif
+#ifndef KDA_INTER_TOUCH
+#define KDA_INTER_TOUCH 128
+#endif
 // Chunk records in flight per inter wave, for 16- and 32-column value tiles.
 template <int NCT>
 constexpr int ring_depth() { return NCT == 1 ? KDA_INTER_PF : KDA_INTER_PF_WIDE; }
 constexpr int L2D = KDA_INTER_L2D;    // L2 prefetch distance in chunks (0: no prefetch wave)
 constexpr int L2R = KDA_INTER_L2R;    // chunks a prefetch load may stay in flight
+constexpr int TOUCH = KDA_INTER_TOUCH;  // bytes of a record between two prefetch touches
 constexpr int INTER_THREADS = L2D > 0 ? 576 : 512;   // 4 state + 4 output (+ 1 prefetch) waves
 constexpr int INTER_MAX_PAIRS = 1 << 19;               // (sequence, head) pairs per chain launch
 
@@ -1112,12 +1116,14 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
                 output_step<NCT>(buf[j], sS, sZ, chunk_at(c + j, table, row_len, ncr), H, h, t, l,
                             vt0, rbase + (size_t)min(c + j + PF, clast) * REC_BYTES, o);
     } else if (L2D > 0) {
-        // Prefetch wave: touches this tile's share of the 128-byte lines of the
-        // record L2D chunks ahead, so that the record sits in L2 when the other
-        // waves' register rings load it (the value tiles of a pair share that
-        // L2).  A touch is consumed -- waited for -- L2R chunks after it was
-        // issued, so this wave never stalls the chunk barriers on memory.
-        constexpr int LINES = REC_BYTES / 128;
+        // Prefetch wave: touches this tile's share of the record L2D chunks
+        // ahead, one 4-byte load every TOUCH bytes, so that the record sits in
+        // L2 when the other waves' register rings load it (the value tiles of a
+        // pair share that L2).  A touch is consumed -- waited for -- L2R chunks
+        // after it was issued, so this wave never stalls the chunk barriers on
+        // memory.
+        static_assert(REC_BYTES % TOUCH == 0 && TOUCH >= 4, "touch stride");
+        constexpr int LINES = REC_BYTES / TOUCH;
 #ifdef KDA_INTER_L2ALL
         constexpr int SHARE = LINES;
         const int tile0 = 0;
@@ -1129,7 +1135,7 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
         int lofs[NLD];
 #pragma unroll
         for (int i = 0; i < NLD; ++i)
-            lofs[i] = min(tile0 * SHARE + min(64 * i + l, SHARE - 1), LINES - 1) * 128;
+            lofs[i] = min(tile0 * SHARE + min(64 * i + l, SHARE - 1), LINES - 1) * TOUCH;
         uint32_t ring[L2R][NLD];
 #pragma unroll
         for (int j = 0; j < L2R; ++j)
