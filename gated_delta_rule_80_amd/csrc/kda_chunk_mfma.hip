@@ -293,6 +293,140 @@ __device__ __forceinline__ void offdiag_column(const float *sA, float *sTf, int 
     }
 }
 
+// Diagonal block w of T = (I + A)^{-1} by one wave, into the same block of
+// sTf.  Ad holds the block of A in accumulator layout (rows 4 (l/16) + e,
+// column l % 16); sA holds it too (row-major, pitch AP).
+__device__ __forceinline__ void diag_inverse(const float *sA, float *sTf, int w, int g4, int i16,
+                                             float4v Ad) {
+    // A is strictly lower triangular, so A^16 = 0 and
+    //   (I + A)^{-1} = (I - A)(I + A^2)(I + A^4)(I + A^8),
+    // factors that commute.  On fp32 MFMA: the running product Y stays in
+    // accumulator layout and is the B operand of each step (Y <- Y + P Y);
+    // each power P is read as the A operand (row l % 16, column 4 (l/16) + s)
+    // from LDS, A from sA and the higher powers from this wave's diagonal
+    // block of sTf, which T overwrites at the end.  Every entry of A is at
+    // most beta_i |k_i| |k_j| in size (its decay factor is <= 1), so the
+    // powers stay small.  The reads follow writes by other lanes of this
+    // wave: LDS executes a wave's operations in order; the waits keep the
+    // compiler from moving the reads above the writes.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    float *blk = sTf + (16 * w) * AP + 16 * w;
+    const float *arow = sA + (16 * w + i16) * AP + 16 * w + 4 * g4;
+    const float *prow = blk + i16 * AP + 4 * g4;
+    float4v Y, P = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Y[e] = (4 * g4 + e == i16 ? 1.f : 0.f) - Ad[e];
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2)
+        P = __builtin_amdgcn_mfma_f32_16x16x4f32(arow[s2], Ad[s2], P, 0, 0, 0);   // A^2
+#pragma unroll
+    for (int q2 = 0; q2 < 3; ++q2) {   // P = A^2, A^4, A^8
+#pragma unroll
+        for (int e = 0; e < 4; ++e) blk[(4 * g4 + e) * AP + i16] = P[e];
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        float pa[4];
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) pa[s2] = prow[s2];
+        float4v Yn = Y, Pn = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+            Yn = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[s2], Y[s2], Yn, 0, 0, 0);
+            if (q2 < 2) Pn = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[s2], P[s2], Pn, 0, 0, 0);
+        }
+        Y = Yn;
+        P = Pn;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) blk[(4 * g4 + e) * AP + i16] = Y[e];
+}
+
+// Stages 5, 3 and 6 of the intra-chunk kernels, after the diagonal inverses:
+// the off-diagonal blocks of T, L^T and V^T transposed into LDS, then
+// T Diag(beta) in fp16 and the WY factors W^T = L^T (T B)^T and U = (T B) V
+// into the record.  hL holds L = K e^{G} in fp16 and vra, vrb the bf16 values
+// of v for this lane's rows 16 r + l % 16 and channels ca.., cb...
+__device__ __forceinline__ void finish_wy(uint8_t *smem, uint8_t *__restrict__ rec, int tid, int l,
+                                          int w, int g4, int i16, int ca, int cb,
+                                          const half8 (&hL)[4], const uint2 (&vra)[4],
+                                          const uint2 (&vrb)[4], const float *sA, float *sTf,
+                                          const float *sBeta) {
+    // ---- stage 5: off-diagonal blocks of T, block column j by wave j (fp32 MFMA); ----
+    // ---- stage 3 alongside: L^T and V^T transposed into LDS (over the dead partials)
+    // beta is applied to the columns of T in stage 6 (W = (T Diag(beta)) L and
+    // U = (T Diag(beta)) V), so L and V go to LDS unscaled.
+    switch (w) {
+    case 0: offdiag_column<0>(sA, sTf, g4, i16); break;
+    case 1: offdiag_column<1>(sA, sTf, g4, i16); break;
+    case 2: offdiag_column<2>(sA, sTf, g4, i16); break;
+    default: break;
+    }
+    _Float16 *sBL = reinterpret_cast<_Float16 *>(smem + L_BL);
+    _Float16 *sBV = reinterpret_cast<_Float16 *>(smem + L_BV);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int i = 16 * r + i16;   // rows past the end hold zeros (masked loads)
+        const uint32_t vw[4] = {vra[r].x, vra[r].y, vrb[r].x, vrb[r].y};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int cc = j < 4 ? ca + j : cb + j - 4;
+            sBL[cc * TP + i] = hL[r][j];
+            const float vv = bf((j & 1) ? (vw[j >> 1] >> 16) : (vw[j >> 1] & 0xffff));
+            sBV[cc * TP + i] = (_Float16)vv;
+        }
+    }
+    lds_barrier();
+
+    // ---- stage 6: T Diag(beta) to fp16, then W^T = L^T (T B)^T and U = (T B) V -------
+    _Float16 *sT16 = reinterpret_cast<_Float16 *>(smem + L_T16);
+    {
+        // thread: row i, columns j0 .. j0+15; all reads before the two 16-byte writes
+        const int i = tid >> 2, j0 = 16 * (tid & 3);
+        float tv[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) tv[j] = sTf[i * AP + j0 + j];
+        half8 h0, h1;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            h0[j] = (_Float16)((j0 + j <= i) ? tv[j] * sBeta[j0 + j] : 0.f);
+            h1[j] = (_Float16)((j0 + 8 + j <= i) ? tv[8 + j] * sBeta[j0 + 8 + j] : 0.f);
+        }
+        *reinterpret_cast<half8 *>(sT16 + i * TP + j0) = h0;
+        *reinterpret_cast<half8 *>(sT16 + i * TP + j0 + 8) = h1;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int cl = 0; cl < 2; ++cl) {
+        const int ct = 2 * w + cl;   // channel tile for W^T, value tile for U
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            float4v aw = {0, 0, 0, 0}, au = {0, 0, 0, 0};
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                if (kb > (it >> 1)) continue;
+                const half8 tfrag =
+                    *reinterpret_cast<const half8 *>(sT16 + (16 * it + i16) * TP + 32 * kb + 8 * g4);
+                const half8 lfrag =
+                    *reinterpret_cast<const half8 *>(sBL + (16 * ct + i16) * TP + 32 * kb + 8 * g4);
+                const half8 vfrag =
+                    *reinterpret_cast<const half8 *>(sBV + (16 * ct + i16) * TP + 32 * kb + 8 * g4);
+                aw = mfma16(lfrag, tfrag, aw);   // rows: channels, cols: tokens
+                au = mfma16(tfrag, vfrag, au);   // rows: tokens, cols: value columns
+            }
+            half4 hw, hu;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                hw[e] = (_Float16)aw[e];
+                hu[e] = (_Float16)au[e];
+            }
+            // W A-frag (token tile it, channel block w): channel tile 2w -> bytes 0..7,
+            // channel tile 2w+1 -> bytes 8..15.
+            *reinterpret_cast<half4 *>(rec + REC_W + ((it * 4 + w) * 64 + l) * 16 + cl * 8) = hw;
+            reinterpret_cast<half4 *>(rec + REC_U)[(it * 8 + ct) * 64 + l] = hu;
+        }
+    }
+}
+
 // Grid: one workgroup per (head, chunk).  With a chunk table (packed sequences)
 // block b covers global chunk b / H.  Without one (B equal rows of ncr chunks)
 // it covers local chunk jlo + (b / H) % jn of row (b / H) / jn, so a launch can
@@ -735,124 +869,286 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
             const half4 z = {0, 0, 0, 0};
             *reinterpret_cast<half4 *>(dst + 8) = z;
         }
-        // A is strictly lower triangular, so A^16 = 0 and
-        //   (I + A)^{-1} = (I - A)(I + A^2)(I + A^4)(I + A^8),
-        // factors that commute.  On fp32 MFMA: the running product Y stays in
-        // accumulator layout and is the B operand of each step (Y <- Y + P Y);
-        // each power P is read as the A operand (row l % 16, column 4 (l/16) + s)
-        // from LDS, A from sA and the higher powers from this wave's diagonal
-        // block of sTf, which T overwrites at the end.  Every entry of A is at
-        // most beta_i |k_i| |k_j| in size (its decay factor is <= 1), so the
-        // powers stay small.  The reads follow writes by other lanes of this
-        // wave: LDS executes a wave's operations in order; the waits keep the
-        // compiler from moving the reads above the writes.
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        float *blk = sTf + (16 * w) * AP + 16 * w;
-        const float *arow = sA + (16 * w + i16) * AP + 16 * w + 4 * g4;
-        const float *prow = blk + i16 * AP + 4 * g4;
-        float4v Y, P = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) Y[e] = (4 * g4 + e == i16 ? 1.f : 0.f) - Ad[e];
-#pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2)
-            P = __builtin_amdgcn_mfma_f32_16x16x4f32(arow[s2], Ad[s2], P, 0, 0, 0);   // A^2
-#pragma unroll
-        for (int q2 = 0; q2 < 3; ++q2) {   // P = A^2, A^4, A^8
-#pragma unroll
-            for (int e = 0; e < 4; ++e) blk[(4 * g4 + e) * AP + i16] = P[e];
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            float pa[4];
-#pragma unroll
-            for (int s2 = 0; s2 < 4; ++s2) pa[s2] = prow[s2];
-            float4v Yn = Y, Pn = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s2 = 0; s2 < 4; ++s2) {
-                Yn = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[s2], Y[s2], Yn, 0, 0, 0);
-                if (q2 < 2) Pn = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[s2], P[s2], Pn, 0, 0, 0);
-            }
-            Y = Yn;
-            P = Pn;
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) blk[(4 * g4 + e) * AP + i16] = Y[e];
+        diag_inverse(sA, sTf, w, g4, i16, Ad);
     }
     lds_barrier();
 
-    // ---- stage 5: off-diagonal blocks of T, block column j by wave j (fp32 MFMA); ----
-    // ---- stage 3 alongside: L^T and V^T transposed into LDS (over the dead partials)
-    // beta is applied to the columns of T in stage 6 (W = (T Diag(beta)) L and
-    // U = (T Diag(beta)) V), so L and V go to LDS unscaled.
-    switch (w) {
-    case 0: offdiag_column<0>(sA, sTf, g4, i16); break;
-    case 1: offdiag_column<1>(sA, sTf, g4, i16); break;
-    case 2: offdiag_column<2>(sA, sTf, g4, i16); break;
-    default: break;
+    finish_wy(smem, rec, tid, l, w, g4, i16, ca, cb, hL, vra, vrb, sA, sTf, sBeta);
+}
+
+// ------------------------------------------------------------------------------------
+// Intra-chunk kernel for a scalar gate (one log-decay per token and head, Gated
+// DeltaNet's gate) or none (DeltaNet).  With the same decay on every key channel
+// the factor e^{G_i - G_j} leaves the sum over channels:
+//   A_ij = beta_i e^{G_i - G_j} (k_i . k_j)   (j < i)
+//   H_ij = e^{G_i - G_j} (s q_i . k_j)        (j <= i)
+// so K K^T and (s Q) K^T are plain MFMA products of fp16 k and q, and the decay
+// is a C x C mask applied in fp32 to the accumulators, every factor <= 1 ("Kimi
+// Delta Attention: a half-life per channel", section "What changes in the
+// kernel": the scalar gate's C x C mask).  No split points and no per-element
+// exponentials: L = K e^{G}, Qbar = s Q e^{G} and Ktil = K e^{G_C - G} scale
+// whole rows by one factor each.  The record written is the one kda_intra_kernel
+// writes, so the chunk chain is shared.  Per-token log-decays are floored at
+// MIN_LOG_DECAY as there, so cumulative logs stay finite (-inf included).
+// ------------------------------------------------------------------------------------
+constexpr int LS_K = 0;        // K fp16 A/B-fragments [row tile 4][channel block 4][lane]  16384
+constexpr int LS_Q = 16384;    // s Q fp16 fragments, same layout                            16384
+constexpr int LS_G = 32768;    // G (log2 units) fp32 [64]                                   256
+static_assert(LS_G + 256 <= L_KT && L_NRM + 2048 <= L_BETA, "scalar-gate stage 1 LDS map");
+
+// Lower-triangle tile u = 0..9 of a 4 x 4 tile grid: (a, b) with b <= a.
+__device__ __forceinline__ void lower_tile(int u, int &a, int &b) {
+    a = u >= 6 ? 3 : (u >= 3 ? 2 : (u >= 1 ? 1 : 0));
+    b = u - (a * (a + 1)) / 2;
+}
+// Strictly-lower tile t = 0..5: (1,0), (2,0), (2,1), (3,0), (3,1), (3,2).
+__device__ __forceinline__ void offdiag_tile(int t, int &a, int &b) {
+    a = t >= 3 ? 3 : (t >= 1 ? 2 : 1);
+    b = t - (a * (a - 1)) / 2;
+}
+
+template <bool HAS_GATE>
+__global__ __launch_bounds__(256, 2) void kda_intra_scalar_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+    const uint16_t *__restrict__ v, const float *__restrict__ g,
+    const float *__restrict__ beta, float scale, int form, float eps, int H, int row_len,
+    int ncr, const int4 *__restrict__ table, const int32_t *__restrict__ n_chunks, int nc_max,
+    int jlo, int jn, uint8_t *__restrict__ recs) {
+#pragma clang fp contract(off)
+    __shared__ __attribute__((aligned(16))) uint8_t smem[L_BYTES];
+    const int h = blockIdx.x % H, b = blockIdx.x / H;
+    int c;
+    if (table) {
+        c = b;
+        if (c >= *n_chunks) return;
+    } else {
+        const int row = b / jn, j = jlo + (b - row * jn);
+        if (j >= ncr) return;
+        c = row * ncr + j;
     }
-    _Float16 *sBL = reinterpret_cast<_Float16 *>(smem + L_BL);
-    _Float16 *sBV = reinterpret_cast<_Float16 *>(smem + L_BV);
+    const Chunk ch = chunk_at(c, table, row_len, ncr);
+    uint8_t *rec = recs + ((size_t)h * nc_max + c) * REC_BYTES;
+
+    const int tid = threadIdx.x, l = tid & 63, g4 = l >> 4, i16 = l & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int len = ch.len;
+    const int ca = 32 * w + 4 * g4, cb = ca + 16;   // this lane's 8 channels
+
+    half8 *sK = reinterpret_cast<half8 *>(smem + LS_K);
+    half8 *sQ = reinterpret_cast<half8 *>(smem + LS_Q);
+    float *sG = reinterpret_cast<float *>(smem + LS_G);
+    _Float16 *sKt = reinterpret_cast<_Float16 *>(smem + L_KT);
+    float *sBeta = reinterpret_cast<float *>(smem + L_BETA);
+
+    // ---- stage 1: loads, cumulative decay, fp16 operands ------------------------------
+    float gr[4], nk[4], nq[4];
+    uint32_t kw[4][4], qw[4][4];
+    uint2 vra[4], vrb[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const int i = 16 * r + i16;   // rows past the end hold zeros (masked loads)
-        const uint32_t vw[4] = {vra[r].x, vra[r].y, vrb[r].x, vrb[r].y};
+        const int i = 16 * r + i16;
+        const bool ok = i < len;
+        const size_t row = (size_t)(ch.t0 + (ok ? i : 0)) * H + h;
+        uint2 ka = {0, 0}, kb2 = {0, 0}, qa = {0, 0}, qb = {0, 0};
+        vra[r] = uint2{0, 0};
+        vrb[r] = uint2{0, 0};
+        gr[r] = 0.f;
+        if (ok) {
+            if constexpr (HAS_GATE) gr[r] = g[row];
+            ka = *reinterpret_cast<const uint2 *>(k + row * DK + ca);
+            kb2 = *reinterpret_cast<const uint2 *>(k + row * DK + cb);
+            qa = *reinterpret_cast<const uint2 *>(q + row * DK + ca);
+            qb = *reinterpret_cast<const uint2 *>(q + row * DK + cb);
+            vra[r] = *reinterpret_cast<const uint2 *>(v + row * DV + ca);
+            vrb[r] = *reinterpret_cast<const uint2 *>(v + row * DV + cb);
+        }
+        kw[r][0] = ka.x, kw[r][1] = ka.y, kw[r][2] = kb2.x, kw[r][3] = kb2.y;
+        qw[r][0] = qa.x, qw[r][1] = qa.y, qw[r][2] = qb.x, qw[r][3] = qb.y;
+        nk[r] = 1.f;
+        nq[r] = scale;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        float x = gr[r];
+        if (HAS_GATE && (form & kFormGateLogit) && 16 * r + i16 < len) x = log_sigmoid(x);
+        gr[r] = (x < MIN_LOG_DECAY ? MIN_LOG_DECAY : x) * 1.4426950408889634f;
+    }
+    if (tid < C) {
+        const int i = tid;
+        float bt = i < len ? beta[(size_t)(ch.t0 + i) * H + h] : 0.f;
+        if ((form & kFormBetaLogit) && i < len) bt = sigmoid(bt);
+        sBeta[i] = bt;
+    }
+    if (form & kFormL2Norm) {
+        float *sNrm = reinterpret_cast<float *>(smem + L_NRM);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float a = 0.f, bb = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float kx = bf_at(kw[r], j), qx = bf_at(qw[r], j);
+                a += kx * kx;
+                bb += qx * qx;
+            }
+            a += __shfl_xor(a, 16, 64);
+            a += __shfl_xor(a, 32, 64);
+            bb += __shfl_xor(bb, 16, 64);
+            bb += __shfl_xor(bb, 32, 64);
+            if (g4 == 0) {
+                sNrm[(w * 64 + 16 * r + i16) * 2 + 0] = a;
+                sNrm[(w * 64 + 16 * r + i16) * 2 + 1] = bb;
+            }
+        }
+        lds_barrier();
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * r + i16;
+            float a = 0.f, bb = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < 4; ++ww) {
+                a += sNrm[(ww * 64 + i) * 2 + 0];
+                bb += sNrm[(ww * 64 + i) * 2 + 1];
+            }
+            nk[r] = rsqrtf(a + eps);
+            nq[r] = scale * rsqrtf(bb + eps);
+        }
+    }
+    // Inclusive cumulative log-decay of the token rows (log2 units): a scan over
+    // the 16 lanes of each row tile, carried across the tiles.
+    float G2[4], carry = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float x = row_scan16(gr[r]);
+        G2[r] = carry + x;
+        carry += __shfl(x, (l & 48) | 15, 64);
+    }
+    const float G2C = carry;   // G at the chunk's last row (padding rows add 0)
+    if (w == 0 && g4 == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sG[16 * r + i16] = G2[r];
+    }
+    if (i16 == 0) {
+        float *ge = reinterpret_cast<float *>(rec + REC_GE);
+        const float eC = __builtin_amdgcn_exp2f(G2C);
+        const float4v e4 = {eC, eC, eC, eC};
+        *reinterpret_cast<float4v *>(ge + ca) = e4;
+        *reinterpret_cast<float4v *>(ge + cb) = e4;
+    }
+    half8 hL[4];   // L = K e^{G} in fp16, for stage 3
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int i = 16 * r + i16;
+        const float eG = __builtin_amdgcn_exp2f(G2[r]), eK = __builtin_amdgcn_exp2f(G2C - G2[r]);
+        half8 hk, hq, hqb;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
+            const float kk = bf_at(kw[r], j) * nk[r], qq = bf_at(qw[r], j) * nq[r];
+            hk[j] = (_Float16)kk;
+            hq[j] = (_Float16)qq;
+            hL[r][j] = (_Float16)(kk * eG);    // L = K e^{G}
+            hqb[j] = (_Float16)(qq * eG);      // Qbar = s Q e^{G}
             const int cc = j < 4 ? ca + j : cb + j - 4;
-            sBL[cc * TP + i] = hL[r][j];
-            const float vv = bf((j & 1) ? (vw[j >> 1] >> 16) : (vw[j >> 1] & 0xffff));
-            sBV[cc * TP + i] = (_Float16)vv;
+            sKt[cc * TP + i] = (_Float16)(kk * eK);   // Ktil = K e^{G_C - G}
+        }
+        sK[(r * 4 + w) * 64 + l] = hk;
+        sQ[(r * 4 + w) * 64 + l] = hq;
+        reinterpret_cast<half8 *>(rec + REC_Q)[(r * 4 + w) * 64 + l] = hqb;
+    }
+    lds_barrier();
+
+    // ---- stage 2: K K^T and (s Q) K^T tiles on MFMA, masked by the decay --------------
+    // Wave w takes diagonal tile (w, w) of A, then 4 of the other 16 tiles: the 6
+    // off-diagonal A tiles and the 10 lower H^T tiles (list entries 0..5 and 6..15).
+    float4v accA[2];   // this wave's off-diagonal A tiles (waves 0, 1 have two, 2, 3 one)
+    float4v Ad;        // diagonal tile (w, w) of A
+    {
+        float4v acc = {0, 0, 0, 0};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+            acc = mfma16(sK[(w * 4 + kb) * 64 + l], sK[(w * 4 + kb) * 64 + l], acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * w + 4 * g4 + e, j = 16 * w + i16;
+            Ad[e] = (j < i) ? acc[e] * sBeta[i] * __builtin_amdgcn_exp2f(sG[i] - sG[j]) : 0.f;
+        }
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+        const int t = w + 4 * s2;
+        int a, bt;
+        if (t < 6) {
+            // off-diagonal A tile t of (1,0), (2,0), (2,1), (3,0), (3,1), (3,2)
+            offdiag_tile(t, a, bt);
+            float4v acc = {0, 0, 0, 0};
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                acc = mfma16(sK[(a * 4 + kb) * 64 + l], sK[(bt * 4 + kb) * 64 + l], acc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * a + 4 * g4 + e, j = 16 * bt + i16;
+                acc[e] = acc[e] * sBeta[i] * __builtin_amdgcn_exp2f(sG[i] - sG[j]);
+            }
+            accA[s2] = acc;   // s2 is 0 or 1 here (t < 6)
+        } else {
+            // H^T tile (bt, a) of lower tile u = t - 6: rows tokens j, columns tokens i
+            lower_tile(t - 6, a, bt);
+            float4v acc = {0, 0, 0, 0};
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                acc = mfma16(sK[(bt * 4 + kb) * 64 + l], sQ[(a * 4 + kb) * 64 + l], acc);
+            half4 hv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 16 * bt + 4 * g4 + e, i = 16 * a + i16;
+                hv[e] = (_Float16)((j <= i) ? acc[e] * __builtin_amdgcn_exp2f(sG[i] - sG[j]) : 0.f);
+            }
+            uint8_t *dst = rec + REC_H + (h_slot(a, bt >> 1) * 64 + l) * 16;
+            *reinterpret_cast<half4 *>(dst + (bt & 1) * 8) = hv;
+            if (a == bt && !(a & 1)) {   // tile (a, a + 1) above the diagonal shares the slot
+                const half4 z = {0, 0, 0, 0};
+                *reinterpret_cast<half4 *>(dst + 8) = z;
+            }
+        }
+    }
+    // Ktil^T fragments: channel tiles 2w, 2w+1, token blocks 0, 1.
+#pragma unroll
+    for (int cl = 0; cl < 2; ++cl) {
+        const int ct = 2 * w + cl;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const _Float16 *rowp = sKt + (16 * ct + i16) * TP + 32 * kb + 4 * g4;
+            const half4 lo = *reinterpret_cast<const half4 *>(rowp);
+            const half4 hi = *reinterpret_cast<const half4 *>(rowp + 16);
+            half8 f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                f[e] = lo[e];
+                f[4 + e] = hi[e];
+            }
+            reinterpret_cast<half8 *>(rec + REC_K)[(ct * 2 + kb) * 64 + l] = f;
         }
     }
     lds_barrier();
 
-    // ---- stage 6: T Diag(beta) to fp16, then W^T = L^T (T B)^T and U = (T B) V -------
-    _Float16 *sT16 = reinterpret_cast<_Float16 *>(smem + L_T16);
-    {
-        // thread: row i, columns j0 .. j0+15; all reads before the two 16-byte writes
-        const int i = tid >> 2, j0 = 16 * (tid & 3);
-        float tv[16];
+    // ---- stage 2b and 4: A tiles into sA; each wave inverts its diagonal block --------
+    float *sA = reinterpret_cast<float *>(smem + L_A);
+    float *sTf = reinterpret_cast<float *>(smem + L_TF);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) tv[j] = sTf[i * AP + j0 + j];
-        half8 h0, h1;
+    for (int s2 = 0; s2 < 2; ++s2) {
+        const int t = w + 4 * s2;
+        if (t < 6) {
+            int a, bt;
+            offdiag_tile(t, a, bt);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            h0[j] = (_Float16)((j0 + j <= i) ? tv[j] * sBeta[j0 + j] : 0.f);
-            h1[j] = (_Float16)((j0 + 8 + j <= i) ? tv[8 + j] * sBeta[j0 + 8 + j] : 0.f);
+            for (int e = 0; e < 4; ++e) sA[(16 * a + 4 * g4 + e) * AP + 16 * bt + i16] = accA[s2][e];
         }
-        *reinterpret_cast<half8 *>(sT16 + i * TP + j0) = h0;
-        *reinterpret_cast<half8 *>(sT16 + i * TP + j0 + 8) = h1;
     }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sA[(16 * w + 4 * g4 + e) * AP + 16 * w + i16] = Ad[e];
+    diag_inverse(sA, sTf, w, g4, i16, Ad);
     lds_barrier();
-#pragma unroll
-    for (int cl = 0; cl < 2; ++cl) {
-        const int ct = 2 * w + cl;   // channel tile for W^T, value tile for U
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            float4v aw = {0, 0, 0, 0}, au = {0, 0, 0, 0};
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                if (kb > (it >> 1)) continue;
-                const half8 tfrag =
-                    *reinterpret_cast<const half8 *>(sT16 + (16 * it + i16) * TP + 32 * kb + 8 * g4);
-                const half8 lfrag =
-                    *reinterpret_cast<const half8 *>(sBL + (16 * ct + i16) * TP + 32 * kb + 8 * g4);
-                const half8 vfrag =
-                    *reinterpret_cast<const half8 *>(sBV + (16 * ct + i16) * TP + 32 * kb + 8 * g4);
-                aw = mfma16(lfrag, tfrag, aw);   // rows: channels, cols: tokens
-                au = mfma16(tfrag, vfrag, au);   // rows: tokens, cols: value columns
-            }
-            half4 hw, hu;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                hw[e] = (_Float16)aw[e];
-                hu[e] = (_Float16)au[e];
-            }
-            // W A-frag (token tile it, channel block w): channel tile 2w -> bytes 0..7,
-            // channel tile 2w+1 -> bytes 8..15.
-            *reinterpret_cast<half4 *>(rec + REC_W + ((it * 4 + w) * 64 + l) * 16 + cl * 8) = hw;
-            reinterpret_cast<half4 *>(rec + REC_U)[(it * 8 + ct) * 64 + l] = hu;
-        }
-    }
+
+    finish_wy(smem, rec, tid, l, w, g4, i16, ca, cb, hL, vra, vrb, sA, sTf, sBeta);
 }
 
 // ------------------------------------------------------------------------------------
@@ -1229,8 +1525,8 @@ hipError_t launch_chunk_fwd_mfma(const ChunkProblem &p) {
 
     auto intra = [&](hipStream_t st, int jlo, int jn, int grid) {
         auto kern = p.gate == Gate::PerChannel ? kda_intra_kernel<Gate::PerChannel>
-                    : p.gate == Gate::Scalar   ? kda_intra_kernel<Gate::Scalar>
-                                               : kda_intra_kernel<Gate::None>;
+                    : p.gate == Gate::Scalar   ? kda_intra_scalar_kernel<true>
+                                               : kda_intra_scalar_kernel<false>;
         hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st,
                            static_cast<const uint16_t *>(p.q), static_cast<const uint16_t *>(p.k),
                            static_cast<const uint16_t *>(p.v), p.g, p.beta, p.scale,

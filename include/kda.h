@@ -238,9 +238,15 @@ kda_status kda_chunk_fwd_noalloc(const kda_shape *shape, const void *q, const vo
  *                 NULL for a_t = 1.  4-byte aligned.
  * Every other argument, the workspace (kda_chunk_fwd_workspace_bytes, same
  * shape), the built combinations, the decay range and the alignment rules are
- * those of kda_chunk_fwd.  The kernels are the same ones; only the gate is
- * read differently, so a scalar gate g gives bit-for-bit the result of
- * kda_chunk_fwd with g repeated over the d_k channels.
+ * those of kda_chunk_fwd.  With bf16 storage the intra-chunk work has a kernel
+ * of its own: with one decay per token, the pairwise factor e^{G_i - G_j}
+ * leaves the sum over key channels, so K K^T and (s Q) K^T are plain MFMA
+ * products and the decay is a chunk x chunk mask (every factor <= 1) applied
+ * to them ("Kimi Delta Attention: a half-life per channel", section "What
+ * changes in the kernel"); the chunk chain is shared.  Its results agree with
+ * kda_chunk_fwd fed g on every channel to within the bf16 tolerance, not bit
+ * for bit.  With fp32 storage one kernel serves both gate layouts and the
+ * results are bit for bit those of kda_chunk_fwd with g repeated.
  */
 kda_status kda_chunk_fwd_scalar_gate(const kda_shape *shape, const void *q,
                                      const void *k, const void *v,

@@ -80,19 +80,55 @@ def test_scalar_gate_fp32_path(d, C):
     check(inp, gs, C)
 
 
-def test_scalar_gate_equals_repeated_per_channel_gate_bitwise():
-    """The kernels are shared: a scalar gate gives exactly the bits of the
-    per-channel entry point fed the same gate on every channel."""
+def test_scalar_gate_kernel_matches_the_per_channel_kernel_on_a_repeated_gate():
+    """bf16 storage: the scalar gate has an intra-chunk kernel of its own (the
+    C x C decay mask on K K^T and Q K^T); fed the same gate on every channel,
+    the per-channel kernel computes the same operator by another route.  Both
+    meet the oracle's tolerance, and they agree with each other to within it."""
     import gated_delta_rule_80_amd as K
     inp, gs = inputs(T=700, B=2)
     d = to_dev(inp)
-    g_full = gs[..., None].expand_as(inp["g"]).contiguous().cuda()
+    g_full = gs[..., None].expand_as(inp["g"]).contiguous()
     o1, s1 = K.chunk_fwd_scalar_gate(d["q"], d["k"], d["v"], gs.cuda(), d["beta"],
                                      initial_state=d["initial_state"])
-    o2, s2 = K.chunk_fwd(d["q"], d["k"], d["v"], g_full, d["beta"],
+    o2, s2 = K.chunk_fwd(d["q"], d["k"], d["v"], g_full.cuda(), d["beta"],
                          initial_state=d["initial_state"])
     torch.cuda.synchronize()
+    o_ref, s_ref = oracle_prefill(with_gate(inp, g_full))
+    for o, st in ((o1, s1), (o2, s2)):
+        o64 = o.double().cpu().numpy()
+        assert_close(o64.reshape(-1, *o64.shape[2:]), o_ref, st.double().cpu().numpy(), s_ref,
+                     cu_list(inp), TOL["bf16"], label="scalar vs per-channel kernel")
+    assert rel_err(o1.double().cpu(), o2.double().cpu()) <= TOL["bf16"]
+    assert rel_err(s1.double().cpu(), s2.double().cpu()) <= TOL["bf16"]
+
+
+def test_scalar_gate_fp32_equals_repeated_per_channel_gate_bitwise():
+    """fp32 storage: one kernel serves both gate layouts, so a scalar gate gives
+    exactly the bits of the per-channel entry point fed it on every channel."""
+    import gated_delta_rule_80_amd as K
+    inp, gs = inputs(d=32, dtype="f32", T=150, B=2)
+    d = to_dev(inp)
+    g_full = gs[..., None].expand_as(inp["g"]).contiguous().cuda()
+    o1, s1 = K.chunk_fwd_scalar_gate(d["q"], d["k"], d["v"], gs.cuda(), d["beta"],
+                                     initial_state=d["initial_state"], chunk_size=32)
+    o2, s2 = K.chunk_fwd(d["q"], d["k"], d["v"], g_full, d["beta"],
+                         initial_state=d["initial_state"], chunk_size=32)
+    torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+@pytest.mark.parametrize("lo,hi", [(-0.4, 0.0), (-5.0, 0.0), (-30.0, -5.0)])
+def test_scalar_gate_strong_decays_and_minus_inf(lo, hi):
+    """Scalar log-decays from weak to far below the floor of -10, with -inf on
+    some tokens, over packed sequences with ragged tails: the mask factors
+    e^{G_i - G_j} are at most 1 whatever the decay."""
+    inp, _ = inputs(H=2, lengths=[70, 1, 200, 64, 17, 130])
+    gen = torch.Generator().manual_seed(73)
+    gs = (lo + (hi - lo) * torch.rand(inp["beta"].shape, generator=gen,
+                                      dtype=torch.float64)).to(torch.float32)
+    gs[:, [5, 71, 150, 300], :] = float("-inf")
+    check(inp, gs.contiguous(), 64)
 
 
 @pytest.mark.parametrize("gated", [True, False])
