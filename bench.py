@@ -264,7 +264,8 @@ def main():
                                    "S0~N(0,0.01^2) (report only)"},
             "roofline": {"bound": "hbm", "kernel": "kda_chunk_fwd", "achieved": round(pgbs, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(pgbs / HBM_PEAK_GBS, 4), "alg_bytes_per_launch": pbytes}}
+                         "frac": round(pgbs / HBM_PEAK_GBS, 4), "alg_bytes_per_launch": pbytes,
+                         "traffic": measured_traffic("kda_chunk_fwd:B2_T2048_H8")}}
         del d2, inp2, ws2, o2, fs2
 
     if not args.skip_decode:
@@ -273,7 +274,7 @@ def main():
         state = W.make_decode_state(w3).to(dev)
         # Fresh seeded tokens for every one of the workload's steps, drawn on the
         # host and held on the device (about 5 MB per step) before the timing.
-        n_tok = w3.steps
+        n_tok = max(1, min(w3.steps, args.decode_steps))
         toks = [{k: (v.to(dev) if isinstance(v, torch.Tensor) else v)
                  for k, v in W.make_decode_step(s, w3).items()} for s in range(n_tok)]
         od = torch.empty((w3.n_sessions, w3.H, w3.dv), dtype=torch.bfloat16, device=dev)
