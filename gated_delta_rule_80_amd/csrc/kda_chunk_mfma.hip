@@ -83,16 +83,18 @@ constexpr int INTER_MAX_PAIRS = 1 << 19;               // (sequence, head) pairs
 
 // One chunk-head record in the workspace (bytes).  Fragment index -> 1 KB
 // (64 lanes x 16 B) unless noted.
+// U = T Diag(beta) V is not stored: the chain forms it from v and the T
+// fragments, so the intra-chunk kernel neither reads v nor writes U.
 constexpr int REC_W = 0;        // W   A-frags [token tile 4][channel block 4]
 constexpr int REC_Q = 16384;    // Qbar A-frags [token tile 4][channel block 4]
 constexpr int REC_K = 32768;    // Ktil^T A-frags [channel tile 8][token block 2]
-constexpr int REC_U = 49152;    // U accumulator tiles [token tile 4][value tile 8], 512 B each
-constexpr int REC_H = 65536;    // H A-frags, 6 nonzero (token tile, token block) pairs
-constexpr int REC_GE = 71680;   // e^{G_C} fp32 [128]
-constexpr int REC_BYTES = 72192;
+constexpr int REC_H = 49152;    // H A-frags, 6 nonzero (token tile, token block) pairs
+constexpr int REC_T = 55296;    // T Diag(beta) A-frags, the same 6 pairs
+constexpr int REC_GE = 61440;   // e^{G_C} fp32 [128]
+constexpr int REC_BYTES = 61952;
 static_assert(REC_BYTES % 256 == 0, "record alignment");
 
-// H fragment slot of (token tile it, token block kb), kb <= it / 2.
+// H and T fragment slot of (token tile it, token block kb), kb <= it / 2.
 __device__ __forceinline__ int h_slot(int it, int kb) { return it < 2 ? it : 2 * it - 2 + kb; }
 
 struct Chunk {
@@ -250,7 +252,6 @@ constexpr int L_DP = 16640;       // 32768 -> 49408, over dead fragment buffers,
 // Stages 3-6 (the fragment buffers are dead by then).
 constexpr int L_A = 0;            // fp32 [64][65]   16640
 constexpr int L_BL = 16640;       // fp16 [128][72]  18432  L^T = (K e^{G})^T
-constexpr int L_BV = 35072;       // fp16 [128][72]  18432  V^T
 constexpr int L_TF = 53504;       // fp32 [64][65]   16640  T
 constexpr int L_T16 = 0;          // fp16 [64][72]    9216  T (after A is dead)
 constexpr int L_BETA = 70144;     // fp32 [64]
@@ -259,8 +260,8 @@ constexpr int TP = 72;            // fp16 pitch of transposed [channel][token] b
 constexpr int AP = 65;            // fp32 pitch of A and T
 static_assert(L_KT == L_RD + 12288 && L_KT + 128 * TP * 2 == L_NRM && L_NRM + 2048 <= L_BETA,
               "stage 1 LDS map");
-static_assert(L_DP >= L_A + 64 * AP * 4 && L_DP + 32768 <= L_BV + 128 * TP * 2,
-              "diagonal partials sit clear of sA and inside the stage 3 buffers");
+static_assert(L_DP >= L_A + 64 * AP * 4 && L_DP + 32768 <= L_TF && L_BL + 128 * TP * 2 <= L_TF,
+              "diagonal partials sit clear of sA and sTf; L^T clear of sTf");
 
 // Block column J of T = (I + A)^{-1} below the diagonal, by one wave:
 //   X_J = T_JJ;  X_b = -T_bb sum_{k=J}^{b-1} A_bk X_k  for b > J.
@@ -342,19 +343,18 @@ __device__ __forceinline__ void diag_inverse(const float *sA, float *sTf, int w,
 }
 
 // Stages 5, 3 and 6 of the intra-chunk kernels, after the diagonal inverses:
-// the off-diagonal blocks of T, L^T and V^T transposed into LDS, then
-// T Diag(beta) in fp16 and the WY factors W^T = L^T (T B)^T and U = (T B) V
-// into the record.  hL holds L = K e^{G} in fp16 and vra, vrb the bf16 values
-// of v for this lane's rows 16 r + l % 16 and channels ca.., cb...
+// the off-diagonal blocks of T and L^T transposed into LDS, then T Diag(beta)
+// in fp16 and the WY factor W^T = L^T (T B)^T into the record, with the
+// fragments of T B from which the chain forms U = (T B) V.  hL holds
+// L = K e^{G} in fp16 for this lane's rows 16 r + l % 16 and channels ca.., cb...
 __device__ __forceinline__ void finish_wy(uint8_t *smem, uint8_t *__restrict__ rec, int tid, int l,
                                           int w, int g4, int i16, int ca, int cb,
-                                          const half8 (&hL)[4], const uint2 (&vra)[4],
-                                          const uint2 (&vrb)[4], const float *sA, float *sTf,
+                                          const half8 (&hL)[4], const float *sA, float *sTf,
                                           const float *sBeta) {
     // ---- stage 5: off-diagonal blocks of T, block column j by wave j (fp32 MFMA); ----
-    // ---- stage 3 alongside: L^T and V^T transposed into LDS (over the dead partials)
-    // beta is applied to the columns of T in stage 6 (W = (T Diag(beta)) L and
-    // U = (T Diag(beta)) V), so L and V go to LDS unscaled.
+    // ---- stage 3 alongside: L^T transposed into LDS (over the dead partials) ------
+    // beta is applied to the columns of T in stage 6 (W = (T Diag(beta)) L), so L
+    // goes to LDS unscaled.
     switch (w) {
     case 0: offdiag_column<0>(sA, sTf, g4, i16); break;
     case 1: offdiag_column<1>(sA, sTf, g4, i16); break;
@@ -362,22 +362,15 @@ __device__ __forceinline__ void finish_wy(uint8_t *smem, uint8_t *__restrict__ r
     default: break;
     }
     _Float16 *sBL = reinterpret_cast<_Float16 *>(smem + L_BL);
-    _Float16 *sBV = reinterpret_cast<_Float16 *>(smem + L_BV);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int i = 16 * r + i16;   // rows past the end hold zeros (masked loads)
-        const uint32_t vw[4] = {vra[r].x, vra[r].y, vrb[r].x, vrb[r].y};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int cc = j < 4 ? ca + j : cb + j - 4;
-            sBL[cc * TP + i] = hL[r][j];
-            const float vv = bf((j & 1) ? (vw[j >> 1] >> 16) : (vw[j >> 1] & 0xffff));
-            sBV[cc * TP + i] = (_Float16)vv;
-        }
+        for (int j = 0; j < 8; ++j) sBL[(j < 4 ? ca + j : cb + j - 4) * TP + i] = hL[r][j];
     }
     lds_barrier();
 
-    // ---- stage 6: T Diag(beta) to fp16, then W^T = L^T (T B)^T and U = (T B) V -------
+    // ---- stage 6: T Diag(beta) to fp16, then W^T = L^T (T B)^T ------------------------
     _Float16 *sT16 = reinterpret_cast<_Float16 *>(smem + L_T16);
     {
         // thread: row i, columns j0 .. j0+15; all reads before the two 16-byte writes
@@ -397,10 +390,10 @@ __device__ __forceinline__ void finish_wy(uint8_t *smem, uint8_t *__restrict__ r
     lds_barrier();
 #pragma unroll
     for (int cl = 0; cl < 2; ++cl) {
-        const int ct = 2 * w + cl;   // channel tile for W^T, value tile for U
+        const int ct = 2 * w + cl;   // channel tile of W^T
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
-            float4v aw = {0, 0, 0, 0}, au = {0, 0, 0, 0};
+            float4v aw = {0, 0, 0, 0};
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 if (kb > (it >> 1)) continue;
@@ -408,21 +401,17 @@ __device__ __forceinline__ void finish_wy(uint8_t *smem, uint8_t *__restrict__ r
                     *reinterpret_cast<const half8 *>(sT16 + (16 * it + i16) * TP + 32 * kb + 8 * g4);
                 const half8 lfrag =
                     *reinterpret_cast<const half8 *>(sBL + (16 * ct + i16) * TP + 32 * kb + 8 * g4);
-                const half8 vfrag =
-                    *reinterpret_cast<const half8 *>(sBV + (16 * ct + i16) * TP + 32 * kb + 8 * g4);
                 aw = mfma16(lfrag, tfrag, aw);   // rows: channels, cols: tokens
-                au = mfma16(tfrag, vfrag, au);   // rows: tokens, cols: value columns
+                // Wave w stores the T B fragments of token tile w.
+                if (cl == 0 && it == w)
+                    reinterpret_cast<half8 *>(rec + REC_T)[h_slot(it, kb) * 64 + l] = tfrag;
             }
-            half4 hw, hu;
+            half4 hw;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                hw[e] = (_Float16)aw[e];
-                hu[e] = (_Float16)au[e];
-            }
+            for (int e = 0; e < 4; ++e) hw[e] = (_Float16)aw[e];
             // W A-frag (token tile it, channel block w): channel tile 2w -> bytes 0..7,
             // channel tile 2w+1 -> bytes 8..15.
             *reinterpret_cast<half4 *>(rec + REC_W + ((it * 4 + w) * 64 + l) * 16 + cl * 8) = hw;
-            reinterpret_cast<half4 *>(rec + REC_U)[(it * 8 + ct) * 64 + l] = hu;
         }
     }
 }
@@ -437,8 +426,7 @@ __device__ __forceinline__ void finish_wy(uint8_t *smem, uint8_t *__restrict__ r
 // absent (no decay).
 template <Gate GATE>
 __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-    const uint16_t *__restrict__ v, const float *__restrict__ g,
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, float scale, int form, float eps, int H, int row_len,
     int ncr, const int4 *__restrict__ table, const int32_t *__restrict__ n_chunks, int nc_max,
     int jlo, int jn, uint8_t *__restrict__ recs) {
@@ -478,7 +466,6 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
     // (nq also carries the query scale s).
     float G[4][8], nk[4], nq[4];
     uint32_t kw[4][4], qw[4][4];
-    uint2 vra[4], vrb[4];   // this lane's v values (value channels ca.., cb..), used in stage 3
     // All loads are issued before any of them is used, so the four row tiles
     // cost one memory round trip; the gate's elementwise form is applied after.
 #pragma unroll
@@ -486,11 +473,8 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
         const int i = 16 * r + i16;
         const bool ok = i < len;
         const size_t base = ((size_t)(ch.t0 + (ok ? i : 0)) * H + h) * DK;
-        const size_t vbase = ((size_t)(ch.t0 + (ok ? i : 0)) * H + h) * DV;
         float4v ga = {0, 0, 0, 0}, gb = {0, 0, 0, 0};
         uint2 ka = {0, 0}, kb2 = {0, 0}, qa = {0, 0}, qb = {0, 0};
-        vra[r] = uint2{0, 0};
-        vrb[r] = uint2{0, 0};
         if (ok) {
             if constexpr (GATE == Gate::PerChannel) {
                 ga = *reinterpret_cast<const float4v *>(g + base + ca);
@@ -502,8 +486,6 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
             kb2 = *reinterpret_cast<const uint2 *>(k + base + cb);
             qa = *reinterpret_cast<const uint2 *>(q + base + ca);
             qb = *reinterpret_cast<const uint2 *>(q + base + cb);
-            vra[r] = *reinterpret_cast<const uint2 *>(v + vbase + ca);
-            vrb[r] = *reinterpret_cast<const uint2 *>(v + vbase + cb);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -873,7 +855,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
     }
     lds_barrier();
 
-    finish_wy(smem, rec, tid, l, w, g4, i16, ca, cb, hL, vra, vrb, sA, sTf, sBeta);
+    finish_wy(smem, rec, tid, l, w, g4, i16, ca, cb, hL, sA, sTf, sBeta);
 }
 
 // ------------------------------------------------------------------------------------
@@ -909,8 +891,7 @@ __device__ __forceinline__ void offdiag_tile(int t, int &a, int &b) {
 
 template <bool HAS_GATE>
 __global__ __launch_bounds__(256, 2) void kda_intra_scalar_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-    const uint16_t *__restrict__ v, const float *__restrict__ g,
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, float scale, int form, float eps, int H, int row_len,
     int ncr, const int4 *__restrict__ table, const int32_t *__restrict__ n_chunks, int nc_max,
     int jlo, int jn, uint8_t *__restrict__ recs) {
@@ -943,15 +924,12 @@ __global__ __launch_bounds__(256, 2) void kda_intra_scalar_kernel(
     // ---- stage 1: loads, cumulative decay, fp16 operands ------------------------------
     float gr[4], nk[4], nq[4];
     uint32_t kw[4][4], qw[4][4];
-    uint2 vra[4], vrb[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int i = 16 * r + i16;
         const bool ok = i < len;
         const size_t row = (size_t)(ch.t0 + (ok ? i : 0)) * H + h;
         uint2 ka = {0, 0}, kb2 = {0, 0}, qa = {0, 0}, qb = {0, 0};
-        vra[r] = uint2{0, 0};
-        vrb[r] = uint2{0, 0};
         gr[r] = 0.f;
         if (ok) {
             if constexpr (HAS_GATE) gr[r] = g[row];
@@ -959,8 +937,6 @@ __global__ __launch_bounds__(256, 2) void kda_intra_scalar_kernel(
             kb2 = *reinterpret_cast<const uint2 *>(k + row * DK + cb);
             qa = *reinterpret_cast<const uint2 *>(q + row * DK + ca);
             qb = *reinterpret_cast<const uint2 *>(q + row * DK + cb);
-            vra[r] = *reinterpret_cast<const uint2 *>(v + row * DV + ca);
-            vrb[r] = *reinterpret_cast<const uint2 *>(v + row * DV + cb);
         }
         kw[r][0] = ka.x, kw[r][1] = ka.y, kw[r][2] = kb2.x, kw[r][3] = kb2.y;
         qw[r][0] = qa.x, qw[r][1] = qa.y, qw[r][2] = qb.x, qw[r][3] = qb.y;
@@ -1148,7 +1124,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_scalar_kernel(
     diag_inverse(sA, sTf, w, g4, i16, Ad);
     lds_barrier();
 
-    finish_wy(smem, rec, tid, l, w, g4, i16, ca, cb, hL, vra, vrb, sA, sTf, sBeta);
+    finish_wy(smem, rec, tid, l, w, g4, i16, ca, cb, hL, sA, sTf, sBeta);
 }
 
 // ------------------------------------------------------------------------------------
@@ -1160,30 +1136,43 @@ __global__ __launch_bounds__(256, 2) void kda_intra_scalar_kernel(
 //                         applies S <- Diag(e^{G_C}) S + Ktil^T Z.  This is the
 //                         serial chain from chunk to chunk.
 //   output wave t (0..3)  computes token tile t of O = Qbar S + H Z and stores it,
-//                         off the chain.
-// S (fp16) and Z (fp16) are exchanged through LDS with two barriers per chunk.
-// Each operand fragment is reused for the NCT 16-column tiles of the workgroup,
-// and each byte of a chunk record is loaded by exactly one wave of the CU.
+//                         off the chain.  It also forms token tile t of
+//                         U = (T Diag(beta)) V one chunk ahead, from the value
+//                         rows it staged in LDS (transposed, fp16) the step before.
+// S and Z (fp16) and U (fp32) are exchanged through LDS with two barriers per
+// chunk.  Each operand fragment is reused for the NCT 16-column tiles of the
+// workgroup, and each byte of a chunk record is loaded by exactly one wave of
+// the CU.
 template <int NCT>
 struct StateOps {
     half8 W[4], K[4];
-    half4 U[NCT];
     float4v ge[2];
 };
+// Ring slot of an output wave for chunk x: Qbar and H of x, T Diag(beta) of
+// x + 1 and the value rows of x + 2 (each is used that many steps earlier).
+template <int NCT>
 struct OutOps {
-    half8 Q[4], H[2];
+    half8 Q[4], H[2], T[2];
+    uint32_t V[2 * NCT];   // bf16 pairs: row 16 t + l / 4, columns 4 NCT (l % 4) .. of the tile
 };
+
+// Value rows of one (sequence, head, value tile) as this lane loads them: local
+// chunk x - first covers rows (x - first) C .. of the sequence's len rows.
+struct VRows {
+    const uint16_t *p;   // row 0 of the sequence, at this lane's columns
+    size_t stride;       // elements from one row to the next
+    int first, len;
+};
+
+constexpr int VTP = 72;   // fp16 pitch (tokens) of the transposed value rows in LDS
 
 // Refills are split by the step that consumes each piece, so a buffer is
 // reloaded for the chunk PF ahead right after each piece's last use.
 template <int NCT>
-__device__ __forceinline__ void load_wu(StateOps<NCT> &op, const uint8_t *rec, int t, int l, int vt0) {
+__device__ __forceinline__ void load_w(StateOps<NCT> &op, const uint8_t *rec, int t, int l) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
         op.W[kb] = reinterpret_cast<const half8 *>(rec + REC_W)[(t * 4 + kb) * 64 + l];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-        op.U[ct] = reinterpret_cast<const half4 *>(rec + REC_U)[(t * 8 + vt0 + ct) * 64 + l];
 }
 template <int NCT>
 __device__ __forceinline__ void load_kg(StateOps<NCT> &op, const uint8_t *rec, int t, int l) {
@@ -1198,23 +1187,57 @@ __device__ __forceinline__ void load_kg(StateOps<NCT> &op, const uint8_t *rec, i
     for (int cl = 0; cl < 2; ++cl)
         op.ge[cl] = *reinterpret_cast<const float4v *>(ge + 16 * (2 * t + cl) + 4 * (l >> 4));
 }
-__device__ __forceinline__ void load_q(OutOps &op, const uint8_t *rec, int t, int l) {
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-        op.Q[kb] = reinterpret_cast<const half8 *>(rec + REC_Q)[(t * 4 + kb) * 64 + l];
-}
-__device__ __forceinline__ void load_h(OutOps &op, const uint8_t *rec, int t, int l) {
+// Fragments of token tile t in the 6-slot layout of H and T B (zero above the diagonal).
+__device__ __forceinline__ void load_tri(half8 (&f)[2], const uint8_t *src, int t, int l) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
-        op.H[kb] = (kb <= (t >> 1))
-                       ? reinterpret_cast<const half8 *>(rec + REC_H)[h_slot(t, kb) * 64 + l]
-                       : half8{0, 0, 0, 0, 0, 0, 0, 0};
+        f[kb] = (kb <= (t >> 1)) ? reinterpret_cast<const half8 *>(src)[h_slot(t, kb) * 64 + l]
+                                 : half8{0, 0, 0, 0, 0, 0, 0, 0};
+}
+template <int NCT>
+__device__ __forceinline__ void load_v(uint32_t (&V)[2 * NCT], const VRows &vr, int x, int t, int l) {
+    const int rel = (x - vr.first) * C + 16 * t + (l >> 2);
+    const bool ok = rel < vr.len;   // rows past the sequence's end are zeros
+    const uint16_t *src = vr.p + (size_t)(ok ? rel : 0) * vr.stride;
+    if constexpr (NCT == 1) {
+        const uint2 u = ok ? *reinterpret_cast<const uint2 *>(src) : uint2{0, 0};
+        V[0] = u.x, V[1] = u.y;
+    } else {
+        const uint4 u = ok ? *reinterpret_cast<const uint4 *>(src) : uint4{0, 0, 0, 0};
+        V[0] = u.x, V[1] = u.y, V[2] = u.z, V[3] = u.w;
+    }
+}
+// Value rows 16 t .. 16 t + 15 of one chunk into LDS as fp16 [column][token].
+template <int NCT>
+__device__ __forceinline__ void stage_v(const uint32_t (&V)[2 * NCT], _Float16 *sVt, int t, int l) {
+    const int tok = 16 * t + (l >> 2), col0 = 4 * NCT * (l & 3);
+#pragma unroll
+    for (int j = 0; j < 4 * NCT; ++j)
+        sVt[(col0 + j) * VTP + tok] = (_Float16)bf((j & 1) ? (V[j >> 1] >> 16) : (V[j >> 1] & 0xffff));
+}
+// Token tile t of U = (T B) V for one chunk, from its staged value rows, into
+// sU in the accumulator layout of Z (rows 16 t + 4 (l/16) + e, column l % 16).
+template <int NCT>
+__device__ __forceinline__ void form_u(const half8 (&T)[2], const _Float16 *sVt, float4v *sU, int t,
+                                       int l) {
+    const int g4 = l >> 4, i16 = l & 15;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        float4v u = {0, 0, 0, 0};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+            if (kb <= (t >> 1))
+                u = mfma16(T[kb],
+                           *reinterpret_cast<const half8 *>(sVt + (16 * ct + i16) * VTP + 32 * kb + 8 * g4),
+                           u);
+        sU[(t * NCT + ct) * 64 + l] = u;
+    }
 }
 
-// Chunk step of a state wave (token tile / channel block t).
+// Chunk step of a state wave (token tile / channel block t); sU holds this chunk's U.
 template <int NCT>
 __device__ __forceinline__ void state_step(float4v (&S)[2][NCT], StateOps<NCT> &op, half8 *sS,
-                                           half8 *sZ, int t, int l, int vt0,
+                                           half8 *sZ, const float4v *sU, int t, int l,
                                            const uint8_t *next) {
     // S -> fp16 B-fragments of channel block t.
 #pragma unroll
@@ -1229,9 +1252,12 @@ __device__ __forceinline__ void state_step(float4v (&S)[2][NCT], StateOps<NCT> &
     }
     lds_barrier();
     // Z = U - W S for token tile t (rows: tokens).
-    float4v p[NCT];
+    float4v u[NCT], p[NCT];
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) p[ct] = float4v{0, 0, 0, 0};
+    for (int ct = 0; ct < NCT; ++ct) {
+        u[ct] = sU[(t * NCT + ct) * 64 + l];
+        p[ct] = float4v{0, 0, 0, 0};
+    }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -1240,11 +1266,11 @@ __device__ __forceinline__ void state_step(float4v (&S)[2][NCT], StateOps<NCT> &
     for (int ct = 0; ct < NCT; ++ct) {
         half4 zh;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) zh[e] = (_Float16)((float)op.U[ct][e] - p[ct][e]);
+        for (int e = 0; e < 4; ++e) zh[e] = (_Float16)(u[ct][e] - p[ct][e]);
         *reinterpret_cast<half4 *>(reinterpret_cast<uint8_t *>(&sZ[((t >> 1) * NCT + ct) * 64 + l]) +
                                    (t & 1) * 8) = zh;
     }
-    load_wu(op, next, t, l, vt0);
+    load_w(op, next, t, l);
     lds_barrier();
     // S <- Diag(e^{G_C}) S + Ktil^T Z for channel rows 32t .. 32t+31.
 #pragma unroll
@@ -1261,11 +1287,16 @@ __device__ __forceinline__ void state_step(float4v (&S)[2][NCT], StateOps<NCT> &
     load_kg(op, next, t, l);
 }
 
-// Chunk step of an output wave (token tile t): O^T = S^T Qbar^T + Z^T H^T.
+// Chunk step of an output wave (token tile t) for chunk c: O^T = S^T Qbar^T +
+// Z^T H^T; after the second barrier also U of chunk c + 1 into sU1 from the
+// value rows in sVt1, and the value rows of chunk c + 2 into sVt2.  The ring
+// slot is refilled for chunk c + PF (x below).
 template <int NCT>
-__device__ __forceinline__ void output_step(OutOps &op, const half8 *sS, const half8 *sZ,
+__device__ __forceinline__ void output_step(OutOps<NCT> &op, const half8 *sS, const half8 *sZ,
+                                            const _Float16 *sVt1, float4v *sU1, _Float16 *sVt2,
                                             const Chunk &ch, int H, int h, int t, int l, int vt0,
-                                            const uint8_t *next, uint16_t *__restrict__ o) {
+                                            const uint8_t *rbase, int x, int clast,
+                                            const VRows &vr, uint16_t *__restrict__ o) {
     const int g4 = l >> 4, i16 = l & 15;
     lds_barrier();
     float4v O[NCT];
@@ -1275,7 +1306,12 @@ __device__ __forceinline__ void output_step(OutOps &op, const half8 *sS, const h
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) O[ct] = mfma16(sS[(kb * NCT + ct) * 64 + l], op.Q[kb], O[ct]);
-    load_q(op, next, t, l);
+    {
+        const uint8_t *rq = rbase + (size_t)min(x, clast) * REC_BYTES;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+            op.Q[kb] = reinterpret_cast<const half8 *>(rq + REC_Q)[(t * 4 + kb) * 64 + l];
+    }
     lds_barrier();
     const int tok = 16 * t + i16;
 #pragma unroll
@@ -1291,7 +1327,11 @@ __device__ __forceinline__ void output_step(OutOps &op, const half8 *sS, const h
             *reinterpret_cast<uint2 *>(o + ob) = pk;
         }
     }
-    load_h(op, next, t, l);
+    form_u<NCT>(op.T, sVt1, sU1, t, l);
+    stage_v<NCT>(op.V, sVt2, t, l);
+    load_tri(op.H, rbase + (size_t)min(x, clast) * REC_BYTES + REC_H, t, l);
+    load_tri(op.T, rbase + (size_t)min(x + 1, clast) * REC_BYTES + REC_T, t, l);
+    load_v<NCT>(op.V, vr, min(x + 2, clast), t, l);
 }
 
 // Processes local chunks [jlo, jhi) of every (sequence, head, value tile): the
@@ -1303,11 +1343,17 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
     const int32_t *__restrict__ off, const int32_t *__restrict__ order, int pair0, int n_pairs,
     int H, int row_len, int ncr,
     const int4 *__restrict__ table, int nc_max, const uint8_t *__restrict__ recs, int jlo,
-    int jhi, const float *s_in, float *s_out, uint16_t *__restrict__ o) {
+    int jhi, const uint16_t *__restrict__ v, const float *s_in, float *s_out,
+    uint16_t *__restrict__ o) {
     constexpr int NTILES = DV / (16 * NCT);   // workgroups per (sequence, head)
     constexpr int PF = ring_depth<NCT>();
+    constexpr int U_SLOT = 4 * NCT * 64, VT_SLOT = 16 * NCT * VTP;
     __shared__ half8 sS[4 * NCT * 64];   // S as fp16 B-fragments [channel block][column tile]
     __shared__ half8 sZ[2 * NCT * 64];   // Z as fp16 B-fragments [token block][column tile]
+    // By chunk parity: U [token tile][column tile] in accumulator layout, and
+    // value rows transposed, fp16 [column][token].
+    __shared__ float4v sU[2 * U_SLOT];
+    __shared__ __attribute__((aligned(16))) _Float16 sVt[2 * VT_SLOT];
 
     // Block id -> (pair, tile) so the value tiles of one (sequence, head) run on one XCD
     // (consecutive ids go round-robin over the 8 XCDs) and share its L2.
@@ -1334,6 +1380,7 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
         cs = n * ncr;
         ce = cs + ncr;
     }
+    const int first = cs, n_chunks = ce - cs;
     ce = min(ce, cs + jhi);
     cs = min(ce, cs + jlo);
     const uint8_t *rbase = recs + (size_t)h * nc_max * REC_BYTES;
@@ -1363,9 +1410,10 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
 #pragma unroll
         for (int j = 0; j < PF; ++j) {
             const uint8_t *rec = rbase + (size_t)min(cs + j, clast) * REC_BYTES;
-            load_wu(buf[j], rec, t, l, vt0);
+            load_w(buf[j], rec, t, l);
             load_kg(buf[j], rec, t, l);
         }
+        lds_barrier();   // the output waves' U of the first chunk
         // Whole groups of PF chunks run without per-step conditions, so the
         // compiler's wait counts see the same load sequence on every path and
         // wait only for the ring slot in use; the last < PF chunks follow.
@@ -1373,13 +1421,13 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
         for (; c + PF <= ce; c += PF) {
 #pragma unroll
             for (int j = 0; j < PF; ++j)
-                state_step(S, buf[j], sS, sZ, t, l, vt0,
+                state_step(S, buf[j], sS, sZ, sU + ((c + j) & 1) * U_SLOT, t, l,
                            rbase + (size_t)min(c + j + PF, clast) * REC_BYTES);
         }
 #pragma unroll
         for (int j = 0; j < PF - 1; ++j)
             if (c + j < ce)
-                state_step(S, buf[j], sS, sZ, t, l, vt0,
+                state_step(S, buf[j], sS, sZ, sU + ((c + j) & 1) * U_SLOT, t, l,
                            rbase + (size_t)min(c + j + PF, clast) * REC_BYTES);
         if (s_out) {
 #pragma unroll
@@ -1392,25 +1440,70 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
                               16 * (vt0 + ct) + i16] = S[cl][ct][e];
         }
     } else if (w < 8) {
-        OutOps buf[PF];
+        // The sequence's value rows at this lane's columns (row 16 t + l / 4 of
+        // each chunk, 4 NCT columns from 16 vt0 + 4 NCT (l % 4)).
+        VRows vr;
+        vr.stride = (size_t)H * DV;
+        vr.first = first;
+        vr.len = 0;
+        size_t tok0 = 0;
+        if (n_chunks > 0) {
+            if (table) {
+                const int4 e0 = table[first], e1 = table[first + n_chunks - 1];
+                tok0 = (size_t)e0.y;
+                vr.len = e1.y + e1.z - e0.y;
+            } else {
+                tok0 = (size_t)n * row_len;
+                vr.len = row_len;
+            }
+        }
+        vr.p = v + (tok0 * H + h) * DV + 16 * vt0 + 4 * NCT * (l & 3);
+        OutOps<NCT> buf[PF];
+        if (cs < ce) {
+            // U of the first chunk needs its rows and T B now; the rows of the
+            // second go to LDS for the first step.
+            half8 T0[2];
+            uint32_t V0[2 * NCT], V1[2 * NCT];
+            load_v<NCT>(V0, vr, cs, t, l);
+            load_v<NCT>(V1, vr, min(cs + 1, clast), t, l);
+            load_tri(T0, rbase + (size_t)cs * REC_BYTES + REC_T, t, l);
 #pragma unroll
-        for (int j = 0; j < PF; ++j) {
-            const uint8_t *rec = rbase + (size_t)min(cs + j, clast) * REC_BYTES;
-            load_q(buf[j], rec, t, l);
-            load_h(buf[j], rec, t, l);
+            for (int j = 0; j < PF; ++j) {
+                const uint8_t *rec = rbase + (size_t)min(cs + j, clast) * REC_BYTES;
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+                    buf[j].Q[kb] = reinterpret_cast<const half8 *>(rec + REC_Q)[(t * 4 + kb) * 64 + l];
+                load_tri(buf[j].H, rec + REC_H, t, l);
+                load_tri(buf[j].T, rbase + (size_t)min(cs + j + 1, clast) * REC_BYTES + REC_T, t, l);
+                load_v<NCT>(buf[j].V, vr, min(cs + j + 2, clast), t, l);
+            }
+            stage_v<NCT>(V0, sVt + (cs & 1) * VT_SLOT, t, l);
+            stage_v<NCT>(V1, sVt + ((cs + 1) & 1) * VT_SLOT, t, l);
+            lds_barrier();
+            form_u<NCT>(T0, sVt + (cs & 1) * VT_SLOT, sU + (cs & 1) * U_SLOT, t, l);
+        } else {
+            lds_barrier();
         }
         int c = cs;
         for (; c + PF <= ce; c += PF) {
 #pragma unroll
-            for (int j = 0; j < PF; ++j)
-                output_step<NCT>(buf[j], sS, sZ, chunk_at(c + j, table, row_len, ncr), H, h, t, l,
-                            vt0, rbase + (size_t)min(c + j + PF, clast) * REC_BYTES, o);
+            for (int j = 0; j < PF; ++j) {
+                const int cc = c + j;
+                output_step<NCT>(buf[j], sS, sZ, sVt + ((cc + 1) & 1) * VT_SLOT,
+                                 sU + ((cc + 1) & 1) * U_SLOT, sVt + (cc & 1) * VT_SLOT,
+                                 chunk_at(cc, table, row_len, ncr), H, h, t, l, vt0, rbase,
+                                 cc + PF, clast, vr, o);
+            }
         }
 #pragma unroll
-        for (int j = 0; j < PF - 1; ++j)
-            if (c + j < ce)
-                output_step<NCT>(buf[j], sS, sZ, chunk_at(c + j, table, row_len, ncr), H, h, t, l,
-                            vt0, rbase + (size_t)min(c + j + PF, clast) * REC_BYTES, o);
+        for (int j = 0; j < PF - 1; ++j) {
+            const int cc = c + j;
+            if (cc < ce)
+                output_step<NCT>(buf[j], sS, sZ, sVt + ((cc + 1) & 1) * VT_SLOT,
+                                 sU + ((cc + 1) & 1) * U_SLOT, sVt + (cc & 1) * VT_SLOT,
+                                 chunk_at(cc, table, row_len, ncr), H, h, t, l, vt0, rbase,
+                                 cc + PF, clast, vr, o);
+        }
     } else if (L2D > 0) {
         // Prefetch wave: touches this tile's share of the record L2D chunks
         // ahead, one 4-byte load every TOUCH bytes, so that the record sits in
@@ -1447,6 +1540,7 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
             }
             lds_barrier();
         };
+        lds_barrier();   // the output waves' U of the first chunk
         int c = cs;
         for (; c + L2R <= ce; c += L2R) {
 #pragma unroll
@@ -1529,7 +1623,7 @@ hipError_t launch_chunk_fwd_mfma(const ChunkProblem &p) {
                                                : kda_intra_scalar_kernel<false>;
         hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st,
                            static_cast<const uint16_t *>(p.q), static_cast<const uint16_t *>(p.k),
-                           static_cast<const uint16_t *>(p.v), p.g, p.beta, p.scale,
+                           p.g, p.beta, p.scale,
                            p.form.flags(), p.form.eps, p.heads, p.seqlen, ncr, table,
                            off + p.n_seqs, (int)L.nc_max, jlo, jn, recs);
         return hipGetLastError();
@@ -1541,7 +1635,8 @@ hipError_t launch_chunk_fwd_mfma(const ChunkProblem &p) {
             const int np = min(INTER_MAX_PAIRS, n_pairs - p0);
             hipLaunchKernelGGL(kern, dim3((np + 7) / 8 * 8 * tiles), dim3(INTER_THREADS), 0,
                                p.stream, off, order, p0, n_pairs, p.heads, p.seqlen, ncr, table,
-                               (int)L.nc_max, recs, jlo, jhi, s_in, s_out, o);
+                               (int)L.nc_max, recs, jlo, jhi, static_cast<const uint16_t *>(p.v),
+                               s_in, s_out, o);
             err = hipGetLastError();
         }
         return err;

@@ -210,8 +210,8 @@ kda_status kda_chunk_fwd(const kda_shape *shape, const void *q, const void *k,
  *   - Problems whose kda_chunk_fwd_workspace_bytes exceeds
  *     KDA_NOALLOC_SCRATCH_BYTES return KDA_ERR_WORKSPACE_TOO_SMALL before
  *     anything is enqueued; at d_k = d_v = 128 with bf16 storage the buffer
- *     holds about 3,700 (chunk, head) records (for example H = 32 heads over
- *     about 7,300 tokens).  The fp32 path needs no workspace.
+ *     holds about 4,300 (chunk, head) records (for example H = 32 heads over
+ *     about 8,600 tokens).  The fp32 path needs no workspace.
  *   - The buffer belongs to the CURRENT device; `stream` must be a stream of
  *     that device (NULL = its null stream), else KDA_ERR_INVALID_ARGUMENT.
  *   - All calls on one device share the buffer, and it keeps the last call's

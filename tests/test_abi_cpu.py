@@ -58,16 +58,16 @@ def ws(sh):
 
 
 def test_workspace_query():
-    # records of 72192 bytes per (chunk, head) plus chunk table and offsets
+    # records of 61952 bytes per (chunk, head) plus chunk table and offsets
     n = ws(shape())
-    assert n >= 32 * (2048 // 64) * 72192
-    assert ws(shape(seqlen=131072)) >= 32 * 2048 * 72192
+    assert n >= 32 * (2048 // 64) * 61952
+    assert ws(shape(seqlen=131072)) >= 32 * 2048 * 61952
     assert ws(shape(d_k=64)) == 0                       # unsupported
     assert ws(shape(batch=0)) == 0                      # invalid
     assert ws(shape(d_k=16, d_v=16, chunk_size=16, dtype_code=K.KDA_F32)) == 0  # fp32 path: none
     # varlen bound T/C + N chunks never below B * ceil(T/C)
     for B, T in [(1, 1), (3, 65), (2, 64), (5, 127)]:
-        assert ws(shape(batch=B, seqlen=T, num_seqs=B)) >= B * ((T + 63) // 64) * 32 * 72192
+        assert ws(shape(batch=B, seqlen=T, num_seqs=B)) >= B * ((T + 63) // 64) * 32 * 61952
 
 
 FAKE = ctypes.c_void_p(0x100000)   # aligned, never dereferenced: validation fails first
