@@ -28,14 +28,17 @@
 //   kda_chunk_index  packed sequences -> chunk table (device side, no sync)
 //   kda_intra        one workgroup per (chunk, head), fully parallel: the
 //                    cumulative decay, A and H on MFMA (fp16 for the blocks
-//                    between sub-chunks, split bf16 inside them), (I + A)^{-1} (diagonal
-//                    16x16 blocks by forward substitution, off-diagonal blocks
-//                    by fp32 MFMA), then W and U on MFMA.  Its outputs go to
+//                    between sub-chunks, fp16 or split bf16 inside them),
+//                    (I + A)^{-1} (diagonal 16x16 blocks as the product
+//                    (I - A)(I + A^2)(I + A^4)(I + A^8), off-diagonal blocks by
+//                    block substitution, all on fp32 MFMA), then W on MFMA.
+//                    Its outputs, with the fragments of T Diag(beta), go to
 //                    the workspace already in the register-fragment order the
-//                    inter kernel consumes.
-//   kda_inter        one workgroup per (sequence, head, 16-column value
+//                    inter kernel consumes.  It does not read v.
+//   kda_inter        one workgroup per (sequence, head, 16- or 32-column value
 //                    tile): the sequential chunk loop with the fp32 state
-//                    resident in registers.  Columns of the value space evolve
+//                    resident in registers; it forms U = T Diag(beta) V from
+//                    v one chunk ahead.  Columns of the value space evolve
 //                    independently, so value tiles need no communication.
 //
 // MFMA fragments (v_mfma_f32_16x16x32_f16): lane l gives row/column l % 16
