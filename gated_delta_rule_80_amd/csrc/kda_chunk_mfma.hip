@@ -392,30 +392,31 @@ __device__ __forceinline__ void finish_wy(uint8_t *smem, uint8_t *__restrict__ r
     }
     lds_barrier();
 #pragma unroll
-    for (int cl = 0; cl < 2; ++cl) {
-        const int ct = 2 * w + cl;   // channel tile of W^T
+    for (int it = 0; it < 4; ++it) {
+        float4v aw[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            float4v aw = {0, 0, 0, 0};
+        for (int kb = 0; kb < 2; ++kb) {
+            if (kb > (it >> 1)) continue;
+            const half8 tfrag =
+                *reinterpret_cast<const half8 *>(sT16 + (16 * it + i16) * TP + 32 * kb + 8 * g4);
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                if (kb > (it >> 1)) continue;
-                const half8 tfrag =
-                    *reinterpret_cast<const half8 *>(sT16 + (16 * it + i16) * TP + 32 * kb + 8 * g4);
-                const half8 lfrag =
-                    *reinterpret_cast<const half8 *>(sBL + (16 * ct + i16) * TP + 32 * kb + 8 * g4);
-                aw = mfma16(lfrag, tfrag, aw);   // rows: channels, cols: tokens
-                // Wave w stores the T B fragments of token tile w.
-                if (cl == 0 && it == w)
-                    reinterpret_cast<half8 *>(rec + REC_T)[h_slot(it, kb) * 64 + l] = tfrag;
+            for (int cl = 0; cl < 2; ++cl) {   // channel tiles 2w, 2w + 1 of W^T
+                const half8 lfrag = *reinterpret_cast<const half8 *>(
+                    sBL + (16 * (2 * w + cl) + i16) * TP + 32 * kb + 8 * g4);
+                aw[cl] = mfma16(lfrag, tfrag, aw[cl]);   // rows: channels, cols: tokens
             }
-            half4 hw;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) hw[e] = (_Float16)aw[e];
-            // W A-frag (token tile it, channel block w): channel tile 2w -> bytes 0..7,
-            // channel tile 2w+1 -> bytes 8..15.
-            *reinterpret_cast<half4 *>(rec + REC_W + ((it * 4 + w) * 64 + l) * 16 + cl * 8) = hw;
+            // Wave w stores the T B fragments of token tile w.
+            if (it == w) reinterpret_cast<half8 *>(rec + REC_T)[h_slot(it, kb) * 64 + l] = tfrag;
         }
+        // W A-frag (token tile it, channel block w): channel tile 2w in bytes
+        // 0..7, channel tile 2w+1 in bytes 8..15.
+        half8 hw;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            hw[e] = (_Float16)aw[0][e];
+            hw[4 + e] = (_Float16)aw[1][e];
+        }
+        reinterpret_cast<half8 *>(rec + REC_W)[(it * 4 + w) * 64 + l] = hw;
     }
 }
 
