@@ -61,7 +61,7 @@ constexpr int C = 64, DK = 128, DV = 128;
 // and a sub-chunk's whole decay below e^{160}: inside the fp32 / bf16 range.
 constexpr float MIN_LOG_DECAY = -10.f;
 #ifndef KDA_INTER_PF
-#define KDA_INTER_PF 3
+#define KDA_INTER_PF 2
 #endif
 #ifndef KDA_INTER_PF_WIDE
 #define KDA_INTER_PF_WIDE 2
