@@ -126,3 +126,52 @@ def test_noalloc_binding_reuses_caller_outputs():
     assert o_b.data_ptr() == o.data_ptr() and f_b.data_ptr() == fs.data_ptr()
     assert torch.equal(o_b, o_r) and torch.equal(f_b, f_r)
     assert np.isfinite(o_b.float().cpu().numpy()).all()
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("varlen", [False, True], ids=["rows", "packed"])
+def test_noalloc_replayed_from_a_graph(varlen):
+    """kda_chunk_fwd_noalloc captured in a HIP graph (the callers it is for):
+    every replay gives the eager result bit for bit, also after an eager call
+    on another problem has overwritten the shared device buffer in between."""
+    import gated_delta_rule_80_amd as K
+    if varlen:
+        inp = W.make_prefill(H=2, dk=128, dv=128, dtype="bf16", z_range=(2.0, 9.0), seed=95,
+                             lengths=[0, 130, 64, 257], s0_std=0.05)
+    else:
+        inp = W.make_prefill(H=2, dk=128, dv=128, dtype="bf16", z_range=(2.0, 9.0), seed=95,
+                             B=2, T=400, s0_std=0.05)
+    other = to_dev(W.make_prefill(H=3, dk=128, dv=128, dtype="bf16", z_range=(2.0, 9.0),
+                                  seed=96, B=1, T=700, s0_std=0.05))
+    d = to_dev(inp)
+    B, T, H, dk = d["q"].shape
+    N = inp["n_seqs"]
+
+    def call(o, fs):
+        K.chunk_fwd_noalloc(d["q"], d["k"], d["v"], d["g"], d["beta"], scale=d["scale"],
+                            initial_state=d["initial_state"], cu_seqlens=d["cu_seqlens"],
+                            out=o, final_state=fs)
+
+    o_ref = torch.empty((B, T, H, 128), dtype=torch.bfloat16, device="cuda")
+    fs_ref = torch.empty((N, H, dk, 128), dtype=torch.float32, device="cuda")
+    call(o_ref, fs_ref)
+    torch.cuda.synchronize()
+    o, fs = torch.empty_like(o_ref), torch.empty_like(fs_ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(torch.empty_like(o_ref), torch.empty_like(fs_ref))
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(o, fs)
+    for replay in range(3):
+        K.chunk_fwd_noalloc(other["q"], other["k"], other["v"], other["g"], other["beta"],
+                            initial_state=other["initial_state"])
+        o.zero_()
+        fs.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(fs, fs_ref), "replay %d" % replay
