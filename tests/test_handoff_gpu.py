@@ -4,7 +4,9 @@ tests/handoff_model/).  Producers stream records through a ring; R consumers
 per stream check every word.  Every wait in the kernel is bounded by a poll
 count and by a wall-clock deadline and polls a shared abort word, so each run
 ends on its own; the abort path is exercised by streams whose producer the
-host leaves out.
+host leaves out.  Mode 2 keeps each stream's roles on one XCD and hands the
+records over through its L2 alone; the tests check the placement the kernel
+reports as well as every word.
 """
 import ctypes
 import os
@@ -22,7 +24,7 @@ def _lib():
     lib = ctypes.CDLL(LIB)
     f = lib.ring_probe_launch
     f.restype = ctypes.c_int
-    f.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] * 6 + [ctypes.c_uint32, ctypes.c_double,
+    f.argtypes = [ctypes.c_void_p] * 7 + [ctypes.c_int] * 6 + [ctypes.c_uint32, ctypes.c_double,
                                                                ctypes.c_int, ctypes.c_void_p]
     return lib
 
@@ -30,9 +32,12 @@ def _lib():
 def test_probe_library_exports_and_validates_on_the_host():
     f = _lib().ring_probe_launch
     fake = ctypes.c_void_p(0x100000)   # never dereferenced: validation fails first
-    args = [fake] * 6 + [4, 8, 4, 16, 1024, 4, 1000, 1.0, 0, None]
+    args = [fake] * 7 + [4, 8, 4, 16, 1024, 4, 1000, 1.0, 0, None]
     assert f(*([None] + args[1:])) == -1                       # null buffer
-    for i, bad in [(6, 0), (7, 17), (8, 65), (10, 24), (11, 5), (13, 0.0), (13, 11.0), (14, 2)]:
+    # P = 0, R = 17, S = 65, 24-byte records, more producers than streams,
+    # bounds of 0 and 11 s, mode 2 with P = 4 (not a multiple of 8), mode 3
+    for i, bad in [(7, 0), (8, 17), (9, 65), (11, 24), (12, 5), (14, 0.0), (14, 11.0), (15, 2),
+                   (15, 3)]:
         a = list(args)
         a[i] = bad
         assert f(*a) == -1, (i, bad)
@@ -46,6 +51,7 @@ def _run(P, R, S, n, rec_bytes, active, spin, max_s, mode=0):
     done = torch.zeros(P * S, dtype=torch.int32, device=dev)
     words = torch.zeros(2, dtype=torch.int32, device=dev)      # abort, bad
     progress = torch.full((P * (1 + R),), -1, dtype=torch.int32, device=dev)
+    xcc = torch.full((P * (1 + R),), -1, dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
     st = torch.cuda.current_stream().cuda_stream
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -53,16 +59,25 @@ def _run(P, R, S, n, rec_bytes, active, spin, max_s, mode=0):
     e0.record()
     rc = _lib().ring_probe_launch(ring.data_ptr(), ready.data_ptr(), done.data_ptr(),
                                   words.data_ptr(), words.data_ptr() + 4, progress.data_ptr(),
-                                  P, R, S, n, rec_bytes, active, spin, max_s, mode, st)
+                                  xcc.data_ptr(), P, R, S, n, rec_bytes, active, spin, max_s, mode, st)
     e1.record()
     torch.cuda.synchronize()
     wall = time.time() - t0
     assert rc == 0
+    _run.xcc = xcc.cpu().tolist()
     return (int(words[0]), int(words[1]), progress.cpu().tolist(), e0.elapsed_time(e1), wall)
 
 
+def _one_xcd_per_stream(P, R):
+    """Every role of a stream ran on the XCD of its producer, and the streams
+    spread over all 8 XCDs."""
+    x = _run.xcc
+    ok = all(x[P + p * R + r] == x[p] for p in range(P) for r in range(R))
+    return ok and sorted(set(x[:P])) == list(range(8))
+
+
 @pytest.mark.gpu
-@pytest.mark.parametrize("mode", [0, 1], ids=["acquire_polls", "one_fence"])
+@pytest.mark.parametrize("mode", [0, 1, 2], ids=["acquire_polls", "one_fence", "one_xcd"])
 def test_ring_handoff_delivers_every_record(mode):
     P, R, S, n = 8, 8, 4, 512
     print("ring handoff P=%d R=%d S=%d chunks=%d rec=61952 B mode %d" % (P, R, S, n, mode),
@@ -70,6 +85,8 @@ def test_ring_handoff_delivers_every_record(mode):
     abort, bad, prog, ms, _ = _run(P, R, S, n, 61952, P, 1 << 22, 5.0, mode)
     assert abort == 0 and bad == 0
     assert prog == [n] * (P * (1 + R))
+    if mode == 2:
+        assert _one_xcd_per_stream(P, R), _run.xcc
     print("  %.3f ms, %.3f us per record per stream" % (ms, 1e3 * ms / n), flush=True)
 
 
@@ -91,9 +108,9 @@ def test_ring_handoff_abort_ends_every_wait():
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("mode,rec,S", [(0, 61952, 4), (1, 61952, 4), (1, 1024, 4), (1, 1024, 16),
-                                        (1, 61952, 16)],
+                                        (1, 61952, 16), (2, 61952, 4), (2, 1024, 4), (2, 61952, 16)],
                          ids=["acquire_polls", "one_fence", "one_fence_1KB", "one_fence_1KB_16slots",
-                              "one_fence_16slots"])
+                              "one_fence_16slots", "one_xcd", "one_xcd_1KB", "one_xcd_16slots"])
 def test_ring_handoff_at_the_prefill_shape(mode, rec, S):
     # 32 streams (heads) x 8 consumers (value tiles) x 2048 records of the
     # prefill's record size (and of 1 KB, for the round trip alone), 4 or 16
@@ -104,5 +121,7 @@ def test_ring_handoff_at_the_prefill_shape(mode, rec, S):
     abort, bad, prog, ms, _ = _run(P, R, S, n, rec, P, 1 << 22, 8.0, mode)
     assert abort == 0 and bad == 0
     assert prog == [n] * (P * (1 + R))
+    if mode == 2:
+        assert _one_xcd_per_stream(P, R), _run.xcc
     print("  %.3f ms, %.3f us per record per stream, %.1f GB/s written, %.1f GB/s read"
           % (ms, 1e3 * ms / n, P * n * rec / ms / 1e6, R * P * n * rec / ms / 1e6), flush=True)
