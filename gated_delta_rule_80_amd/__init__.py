@@ -77,6 +77,8 @@ def lib():
     vp, fp, ip = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
     L.kda_abi_version.restype = ctypes.c_int
     L.kda_abi_version.argtypes = []
+    L.kda_set_prefill_overlap.restype = ctypes.c_int
+    L.kda_set_prefill_overlap.argtypes = [ctypes.c_int]
     L.kda_status_string.restype = ctypes.c_char_p
     L.kda_status_string.argtypes = [ctypes.c_int]
     L.kda_last_error.restype = ctypes.c_char_p
@@ -242,6 +244,19 @@ def _prefill(entry, gate, q, k, v, g, beta, scale, initial_state, cu_seqlens,
                *ws_args, _stream())
     _check(st)
     return o, fs
+
+
+def set_prefill_overlap(mode: int) -> int:
+    """Process-wide order of the bf16 prefill's two kernels
+    (``kda_set_prefill_overlap``): 1 overlapped where it applies (the default),
+    0 one after the other, 2 overlapped with every chunk's factors refused by
+    the chain, 3 overlapped with chains that give up at once when their first
+    chunks are not ready (2 and 3 make the repair pass run; for tests).
+    Returns the previous mode."""
+    prev = lib().kda_set_prefill_overlap(int(mode))
+    if prev < 0:
+        raise ValueError("unknown prefill order %r (0, 1, 2 or 3)" % (mode,))
+    return prev
 
 
 def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,

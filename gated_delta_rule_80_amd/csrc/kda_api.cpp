@@ -7,6 +7,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -17,6 +18,9 @@
 namespace {
 
 thread_local char g_last_error[512] = "";
+
+// The prefill order chosen by kda_set_prefill_overlap (1 = overlapped where it applies).
+std::atomic<int> g_prefill_overlap{1};
 
 kda_status fail(kda_status st, const char *fmt, ...) {
     va_list ap;
@@ -204,6 +208,7 @@ kda_status chunk_fwd(kda::Gate gate, kda::InputForm form, const kda_shape *shape
     p.workspace = workspace;
     p.workspace_bytes = workspace_bytes;
     p.stream = stream;
+    p.allow_overlap = !noalloc;
 
     hipError_t e = kda::mfma_path_supported(p.dk, p.dv, p.chunk, p.bf16)
                        ? kda::launch_chunk_fwd_mfma(p)
@@ -252,9 +257,16 @@ kda_status decode_step(kda::Gate gate, kda::InputForm form, int32_t num_sessions
 
 }  // namespace
 
+int kda::prefill_overlap_mode() { return g_prefill_overlap.load(std::memory_order_relaxed); }
+
 extern "C" {
 
 int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+int kda_set_prefill_overlap(int mode) {
+    if (mode < 0 || mode > 3) return -1;
+    return g_prefill_overlap.exchange(mode);
+}
 
 const char *kda_status_string(kda_status status) {
     switch (status) {

@@ -49,6 +49,8 @@
 //   slot s < 4  -> index 4 (l/16) + s,   slot s >= 4 -> index 16 + 4 (l/16) + s - 4
 // which is exactly what two vertically adjacent 16x16 accumulator tiles hold,
 // so an MFMA result feeds the next MFMA without leaving registers.
+#include <mutex>
+
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
@@ -75,9 +77,17 @@ constexpr float MIN_LOG_DECAY = -10.f;
 #ifndef KDA_INTER_TOUCH
 #define KDA_INTER_TOUCH 128
 #endif
-// Chunk records in flight per inter wave, for 16- and 32-column value tiles.
+#ifndef KDA_INTER_PF_W4
+#define KDA_INTER_PF_W4 1
+#endif
+#ifndef KDA_OVERLAP_NCT
+#define KDA_OVERLAP_NCT 2
+#endif
+// Chunk records in flight per inter wave, for 16-, 32- and 64-column value tiles.
 template <int NCT>
-constexpr int ring_depth() { return NCT == 1 ? KDA_INTER_PF : KDA_INTER_PF_WIDE; }
+constexpr int ring_depth() {
+    return NCT == 1 ? KDA_INTER_PF : NCT == 2 ? KDA_INTER_PF_WIDE : KDA_INTER_PF_W4;
+}
 constexpr int L2D = KDA_INTER_L2D;    // L2 prefetch distance in chunks (0: no prefetch wave)
 constexpr int L2R = KDA_INTER_L2R;    // chunks a prefetch load may stay in flight
 constexpr int TOUCH = KDA_INTER_TOUCH;  // bytes of a record between two prefetch touches
@@ -99,6 +109,64 @@ static_assert(REC_BYTES % 256 == 0, "record alignment");
 
 // H and T fragment slot of (token tile it, token block kb), kb <= it / 2.
 __device__ __forceinline__ int h_slot(int it, int kb) { return it < 2 ? it : 2 * it - 2 + kb; }
+
+// ---- Record handoff between the two kernels when they run side by side ------------
+// In the overlapped prefill the chain kernel starts beside the intra-chunk
+// kernel and reads each record as soon as it is published, instead of after
+// the whole intra-chunk launch.  The records are handed over through the L2 of
+// one XCD (accelerator die), with no cache write-back or invalidation: the
+// producer's stores of a record are acknowledged by L2 (the vector L1 writes
+// through) before it stores the record's flag, and the chain reads flags and
+// records through its own XCD's L2.  That holds only when producer and chain
+// share an XCD.  Workgroups are dispatched to the 8 XCDs round-robin by id and
+// both kernels place head h on XCD h mod 8 when H is a multiple of 8, but the
+// flag carries the XCD the producer actually ran on, and the chain accepts a
+// record only from its own XCD; anything else (another XCD, or a flag not seen
+// in time) marks the call for a repair pass, which reruns the chain after both
+// kernels have ended, as the serial order would.
+
+// Flag value of a published record: nonzero, with the producer's XCD.
+constexpr uint32_t REC_READY = 0x100u;
+
+// The XCD this wave runs on (the XCC_ID hardware register).
+__device__ __forceinline__ uint32_t xcc_id() {
+    return __builtin_amdgcn_s_getreg((3 << 11) | 20) & 15u;   // HW_REG_XCC_ID, bits 3:0
+}
+
+// Work placement by XCD.  A dispatch does not always start on XCD 0, so two
+// kernels on different queues cannot agree on a placement by workgroup id.  In
+// the overlapped order every workgroup reads the XCD it runs on and claims the
+// next item of that XCD's pool instead: n_items items, pool x holding those
+// whose head is x mod 8, `per` consecutive pool items (the heads x, x + 8, ...
+// of one position) at a time.  A workgroup whose pool is empty takes the next
+// item of the following pools; there are exactly as many workgroups as items,
+// so every item is taken once.  ctr: 8 zeroed counters.  Returns the pool and
+// the rank of the item in it.  Called by one thread.
+__device__ __forceinline__ void claim_item(uint32_t *ctr, int n_items, int *pool, int *rank) {
+    const int x0 = (int)xcc_id() & 7, cap = n_items / 8;
+    for (int d = 0; d < 8; ++d) {
+        const int x = (x0 + d) & 7;
+        const uint32_t k = __hip_atomic_fetch_add(ctr + x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((int)k < cap) {
+            *pool = x;
+            *rank = (int)k;
+            return;
+        }
+    }
+    *pool = x0;   // unreachable while the grid has n_items workgroups
+    *rank = cap;
+}
+
+// Producer side, after the workgroup's last record store: every wave waits
+// until its stores are acknowledged, then one thread stores the flag.
+__device__ __forceinline__ void publish_record(uint32_t *flag, int tid) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt and lgkmcnt left at their maxima
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __syncthreads();
+    if (tid == 0)
+        __hip_atomic_store(flag, REC_READY | xcc_id(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 struct Chunk {
     int seq, t0, len;
@@ -433,13 +501,27 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, float scale, int form, float eps, int H, int row_len,
     int ncr, const int4 *__restrict__ table, const int32_t *__restrict__ n_chunks, int nc_max,
-    int jlo, int jn, uint8_t *__restrict__ recs) {
+    int jlo, int jn, uint8_t *__restrict__ recs, uint32_t *__restrict__ ready,
+    uint32_t *__restrict__ claim) {
     // No FMA contraction in this kernel: the compiler would fuse differently in
     // each gate layout's instantiation, and a scalar gate would then no longer
     // give the bits of the same gate repeated over the channels.
 #pragma clang fp contract(off)
     __shared__ __attribute__((aligned(16))) uint8_t smem[L_BYTES];
-    const int h = blockIdx.x % H, b = blockIdx.x / H;
+    int item = blockIdx.x;   // b H + h
+    if (claim) {
+        // Overlapped order: the item comes from this XCD's pool (heads = XCD mod 8).
+        __shared__ int s_item;
+        if (threadIdx.x == 0) {
+            int x, k;
+            claim_item(claim, (int)gridDim.x, &x, &k);
+            const int per = H / 8;
+            s_item = (k / per) * H + x + 8 * (k % per);
+        }
+        __syncthreads();
+        item = s_item;
+    }
+    const int h = item % H, b = item / H;
     int c;
     if (table) {
         c = b;
@@ -860,6 +942,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
     lds_barrier();
 
     finish_wy(smem, rec, tid, l, w, g4, i16, ca, cb, hL, sA, sTf, sBeta);
+    if (ready) publish_record(ready + (size_t)h * nc_max + c, tid);
 }
 
 // ------------------------------------------------------------------------------------
@@ -898,10 +981,24 @@ __global__ __launch_bounds__(256, 2) void kda_intra_scalar_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, float scale, int form, float eps, int H, int row_len,
     int ncr, const int4 *__restrict__ table, const int32_t *__restrict__ n_chunks, int nc_max,
-    int jlo, int jn, uint8_t *__restrict__ recs) {
+    int jlo, int jn, uint8_t *__restrict__ recs, uint32_t *__restrict__ ready,
+    uint32_t *__restrict__ claim) {
 #pragma clang fp contract(off)
     __shared__ __attribute__((aligned(16))) uint8_t smem[L_BYTES];
-    const int h = blockIdx.x % H, b = blockIdx.x / H;
+    int item = blockIdx.x;   // b H + h
+    if (claim) {
+        // Overlapped order: the item comes from this XCD's pool (heads = XCD mod 8).
+        __shared__ int s_item;
+        if (threadIdx.x == 0) {
+            int x, k;
+            claim_item(claim, (int)gridDim.x, &x, &k);
+            const int per = H / 8;
+            s_item = (k / per) * H + x + 8 * (k % per);
+        }
+        __syncthreads();
+        item = s_item;
+    }
+    const int h = item % H, b = item / H;
     int c;
     if (table) {
         c = b;
@@ -1129,6 +1226,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_scalar_kernel(
     lds_barrier();
 
     finish_wy(smem, rec, tid, l, w, g4, i16, ca, cb, hL, sA, sTf, sBeta);
+    if (ready) publish_record(ready + (size_t)h * nc_max + c, tid);
 }
 
 // ------------------------------------------------------------------------------------
@@ -1207,8 +1305,11 @@ __device__ __forceinline__ void load_v(uint32_t (&V)[2 * NCT], const VRows &vr, 
         const uint2 u = ok ? *reinterpret_cast<const uint2 *>(src) : uint2{0, 0};
         V[0] = u.x, V[1] = u.y;
     } else {
-        const uint4 u = ok ? *reinterpret_cast<const uint4 *>(src) : uint4{0, 0, 0, 0};
-        V[0] = u.x, V[1] = u.y, V[2] = u.z, V[3] = u.w;
+#pragma unroll
+        for (int i = 0; i < NCT / 2; ++i) {   // 8 columns per 16-byte load
+            const uint4 u = ok ? reinterpret_cast<const uint4 *>(src)[i] : uint4{0, 0, 0, 0};
+            V[4 * i] = u.x, V[4 * i + 1] = u.y, V[4 * i + 2] = u.z, V[4 * i + 3] = u.w;
+        }
     }
 }
 // Value rows 16 t .. 16 t + 15 of one chunk into LDS as fp16 [column][token].
@@ -1342,13 +1443,22 @@ __device__ __forceinline__ void output_step(OutOps<NCT> &op, const half8 *sS, co
 // state is read from s_in (NULL = zeros) and written to s_out (NULL = not
 // written).  s_out may equal s_in: each lane reads its state elements before
 // it writes them, and no other lane touches them.
+// With `ready` the records are still being produced by an intra-chunk kernel
+// running beside this one: the prefetch wave waits for each record's flag
+// (at most `spin_limit` polls each, and until `max_ticks` of the wall clock
+// from the workgroup's start in all) instead of touching records, and notes in
+// *status any record it could not accept.  If the first records are not there
+// within `start_ticks`, the intra-chunk kernel is taken to be queued behind
+// this one and the whole workgroup ends at once.  With `run_if` the launch is
+// the repair pass: every workgroup ends at once unless *run_if is nonzero.
 template <int NCT>
 __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
     const int32_t *__restrict__ off, const int32_t *__restrict__ order, int pair0, int n_pairs,
     int H, int row_len, int ncr,
     const int4 *__restrict__ table, int nc_max, const uint8_t *__restrict__ recs, int jlo,
     int jhi, const uint16_t *__restrict__ v, const float *s_in, float *s_out,
-    uint16_t *__restrict__ o) {
+    uint16_t *__restrict__ o, const uint32_t *ready, uint32_t *status, uint32_t spin_limit,
+    uint64_t max_ticks, uint64_t start_ticks, const uint32_t *run_if, uint32_t *claim) {
     constexpr int NTILES = DV / (16 * NCT);   // workgroups per (sequence, head)
     constexpr int PF = ring_depth<NCT>();
     constexpr int U_SLOT = 4 * NCT * 64, VT_SLOT = 16 * NCT * VTP;
@@ -1358,14 +1468,31 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
     // value rows transposed, fp16 [column][token].
     __shared__ float4v sU[2 * U_SLOT];
     __shared__ __attribute__((aligned(16))) _Float16 sVt[2 * VT_SLOT];
+    __shared__ int s_quit;   // overlapped order: the first records never came
 
     // Block id -> (pair, tile) so the value tiles of one (sequence, head) run on one XCD
-    // (consecutive ids go round-robin over the 8 XCDs) and share its L2.
-    const int bid = blockIdx.x;
-    const int lane8 = bid & 7, rest = bid >> 3;
+    // (consecutive ids go round-robin over the 8 XCDs) and share its L2.  In the
+    // overlapped order the pair comes from this XCD's pool instead (pairs, and
+    // so heads, = XCD mod 8), the XCD the intra-chunk kernel produces its
+    // records on.
+    int lane8 = blockIdx.x & 7, rest = blockIdx.x >> 3;
+    if (claim) {
+        __shared__ int s_slot;
+        if (threadIdx.x == 0) {
+            int x, k;
+            claim_item(claim, (int)gridDim.x, &x, &k);
+            s_slot = k * 8 + x;
+        }
+        __syncthreads();
+        lane8 = s_slot & 7;
+        rest = s_slot >> 3;
+    }
     const int tile = rest % NTILES, grp = rest / NTILES;
     const int pair = pair0 + grp * 8 + lane8;
     if (pair >= n_pairs) return;
+    // The repair pass runs only when the overlapped launch marked the call.
+    if (run_if && __hip_atomic_load(run_if, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u)
+        return;
     // Launch position -> sequence: longest chains first for packed sequences.
     const int pos = pair / H, h = pair - pos * H;
     const int n = table ? order[pos] : pos;
@@ -1410,6 +1537,10 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
                     S[cl][ct][e] = s_in ? s_in[sbase + (size_t)(32 * t + 16 * cl + 4 * g4 + e) * DV +
                                                16 * (vt0 + ct) + i16]
                                         : 0.f;
+        if (ready) {
+            lds_barrier();   // the records of the first chunks are published (or never will be)
+            if (s_quit) return;
+        }
         StateOps<NCT> buf[PF];
 #pragma unroll
         for (int j = 0; j < PF; ++j) {
@@ -1463,6 +1594,10 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
         }
         vr.p = v + (tok0 * H + h) * DV + 16 * vt0 + 4 * NCT * (l & 3);
         OutOps<NCT> buf[PF];
+        if (ready) {
+            lds_barrier();   // the records of the first chunks are published (or never will be)
+            if (s_quit) return;
+        }
         if (cs < ce) {
             // U of the first chunk needs its rows and T B now; the rows of the
             // second go to LDS for the first step.
@@ -1507,6 +1642,72 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
                                  sU + ((cc + 1) & 1) * U_SLOT, sVt + (cc & 1) * VT_SLOT,
                                  chunk_at(cc, table, row_len, ncr), H, h, t, l, vt0, rbase,
                                  cc + PF, clast, vr, o);
+        }
+    } else if (ready) {
+        // Handoff wave: the records come from an intra-chunk kernel running
+        // beside this one, through this XCD's L2, so nothing is touched ahead.
+        // The other waves load record x at step x - PF (the T Diag(beta)
+        // fragments at step x - PF - 1, after that step's second barrier), and
+        // the first PF + 1 records before the loop; this wave accepts each
+        // record before the barrier that precedes its first load.  A record's
+        // flag is read one step before it is needed, so a record that is
+        // already published costs no wait.
+        static_assert(L2D > 0, "the overlapped chain needs its ninth wave");
+        const uint32_t *fl = ready + (size_t)h * nc_max;
+        const uint32_t me = xcc_id();
+        const uint64_t t_start = (uint64_t)wall_clock64();
+        uint64_t deadline = t_start + start_ticks;   // for the first records, then t_start + max_ticks
+        bool bad = false;
+        // Marks the call for the repair pass.  The first refusal of the call
+        // also leaves its details in status[1..5]: why (1 not seen in time,
+        // 2 from another XCD, 3 refused by request), the flag seen, this XCD,
+        // the chunk and the head.
+        auto mark = [&](uint32_t why, uint32_t seen, int cc) {
+            bad = true;
+            if (l == 0) {
+                __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (atomicCAS(status + 1, 0u, why) == 0u) {
+                    status[2] = seen;
+                    status[3] = me;
+                    status[4] = (uint32_t)cc;
+                    status[5] = (uint32_t)h;
+                }
+            }
+        };
+        if (spin_limit == 0) mark(3u, 0u, cs);   // accept nothing: the repair pass recomputes the call
+        auto peek = [&](int cc) -> uint32_t {
+            return (bad || cc >= ce)
+                       ? 0u
+                       : __hip_atomic_load(fl + cc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        };
+        // Waits until record cc is published; a flag from another XCD, or none
+        // within the limits, marks the call and ends every later wait.
+        auto accept = [&](int cc, uint32_t x) {
+            if (bad || cc >= ce) return;
+            x = __builtin_amdgcn_readfirstlane(x);
+            for (uint32_t it = 0; x == 0u; ++it) {
+                if (it >= spin_limit || (uint64_t)wall_clock64() > deadline) break;
+                __builtin_amdgcn_s_sleep(1);
+                x = __builtin_amdgcn_readfirstlane(
+                    __hip_atomic_load(fl + cc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            }
+            if (x != (REC_READY | me)) mark(x == 0u ? 1u : 2u, x, cc);
+        };
+#pragma unroll 1
+        for (int j = 0; j <= PF; ++j) accept(cs + j, peek(cs + j));
+        const bool quit = bad && spin_limit != 0;   // not refused by request: never came
+        if (l == 0) s_quit = quit ? 1 : 0;
+        lds_barrier();   // the records of the first chunks are published (or never will be)
+        if (quit) return;
+        deadline = t_start + max_ticks;
+        uint32_t next = peek(cs + PF + 1);
+        lds_barrier();   // the output waves' U of the first chunk
+#pragma unroll 1
+        for (int c = cs; c < ce; ++c) {
+            lds_barrier();
+            accept(c + PF + 1, next);
+            next = peek(c + PF + 2);
+            lds_barrier();
         }
     } else if (L2D > 0) {
         // Prefetch wave: touches this tile's share of the record L2D chunks
@@ -1560,10 +1761,18 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
     }
 }
 
-// Workspace: [off int32 (N+1)][order int32 N][chunk table int4 x nc_max][records], each region
-// 256-byte aligned.
+// Zeroes n words (the overlapped prefill's status word and record flags).
+__global__ __launch_bounds__(256) void kda_clear_words_kernel(uint32_t *__restrict__ p, int64_t n) {
+    const int64_t step = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += step) p[i] = 0u;
+}
+
+// Workspace: [status word, 256 B][off int32 (N+1)][order int32 N][chunk table
+// int4 x nc_max][record flags uint32 x H x nc_max][records], each region
+// 256-byte aligned.  The status word (nonzero after an overlapped call that
+// needed its repair pass) and the flags serve the overlapped prefill.
 struct WsLayout {
-    size_t off, order, table, recs, total;
+    size_t off, order, table, status, flags, recs, total;
     int64_t nc_max;
 };
 
@@ -1571,12 +1780,47 @@ static WsLayout ws_layout(int64_t total_tokens, int64_t n_seqs, int heads) {
     WsLayout L;
     L.nc_max = max_chunks(total_tokens, n_seqs, C);
     auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
-    L.off = 0;
-    L.order = up((size_t)(n_seqs + 1) * 4);
+    L.status = 0;
+    L.off = 256;
+    L.order = L.off + up((size_t)(n_seqs + 1) * 4);
     L.table = L.order + up((size_t)n_seqs * 4);
-    L.recs = L.table + up((size_t)L.nc_max * 16);
+    L.flags = L.table + up((size_t)L.nc_max * 16);
+    L.recs = L.flags + up((size_t)heads * L.nc_max * 4);
     L.total = L.recs + (size_t)heads * L.nc_max * REC_BYTES;
     return L;
+}
+
+// The side stream and the two events of the overlapped prefill, one set per
+// device, created on first use and kept until the process ends.  The mutex
+// also keeps the fork / join of one call from interleaving with another
+// thread's.
+struct SideStream {
+    hipStream_t stream = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+static std::mutex g_side_mu;
+static SideStream g_side[64];
+
+static hipError_t side_stream(int dev, SideStream **out) {
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    SideStream &s = g_side[dev];
+    hipError_t e;
+    if (!s.stream) {
+        hipStream_t st = nullptr;
+        hipEvent_t f = nullptr, j = nullptr;
+        if ((e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) != hipSuccess) return e;
+        if ((e = hipEventCreateWithFlags(&f, hipEventDisableTiming)) != hipSuccess ||
+            (e = hipEventCreateWithFlags(&j, hipEventDisableTiming)) != hipSuccess) {
+            if (f) (void)hipEventDestroy(f);
+            (void)hipStreamDestroy(st);
+            return e;
+        }
+        s.stream = st;
+        s.fork = f;
+        s.join = j;
+    }
+    *out = &s;
+    return hipSuccess;
 }
 
 }  // namespace mfma_path
@@ -1614,14 +1858,18 @@ hipError_t launch_chunk_fwd_mfma(const ChunkProblem &p) {
         hipSuccess)
         return e;
     const bool wide = (int64_t)n_pairs * (DV / 16) > n_cu;
-    const int tiles = wide ? DV / 32 : DV / 16;
     // A launch holds at most 2^32 threads, so the chains go out in launches of
     // at most INTER_MAX_PAIRS (sequence, head) pairs (a multiple of 8, so the
     // XCD placement is the same in every launch).
     static_assert((uint64_t)INTER_MAX_PAIRS * (DV / 16) * INTER_THREADS <= 0xFFFFFFFFull, "");
     uint16_t *o = static_cast<uint16_t *>(p.o);
 
-    auto intra = [&](hipStream_t st, int jlo, int jn, int grid) {
+    // Status region: [0] repair needed, [1..5] the first refusal, [8..15] and
+    // [16..23] the intra-chunk and chain kernels' XCD pool counters.
+    uint32_t *status = reinterpret_cast<uint32_t *>(ws + L.status);
+    uint32_t *flags = reinterpret_cast<uint32_t *>(ws + L.flags);
+
+    auto intra = [&](hipStream_t st, int jlo, int jn, int grid, uint32_t *ready, uint32_t *claim) {
         auto kern = p.gate == Gate::PerChannel ? kda_intra_kernel<Gate::PerChannel>
                     : p.gate == Gate::Scalar   ? kda_intra_scalar_kernel<true>
                                                : kda_intra_scalar_kernel<false>;
@@ -1629,21 +1877,30 @@ hipError_t launch_chunk_fwd_mfma(const ChunkProblem &p) {
                            static_cast<const uint16_t *>(p.q), static_cast<const uint16_t *>(p.k),
                            p.g, p.beta, p.scale,
                            p.form.flags(), p.form.eps, p.heads, p.seqlen, ncr, table,
-                           off + p.n_seqs, (int)L.nc_max, jlo, jn, recs);
+                           off + p.n_seqs, (int)L.nc_max, jlo, jn, recs, ready, claim);
         return hipGetLastError();
     };
-    auto inter = [&](int jlo, int jhi, const float *s_in, float *s_out) {
-        auto kern = wide ? kda_inter_kernel<2> : kda_inter_kernel<1>;
+    // The chunk chain over local chunks [jlo, jhi), with 32-column tiles when
+    // `wide_tiles`.  `ready` etc.: the overlapped launch and its repair pass.
+    auto inter = [&](int nct, int jlo, int jhi, const float *s_in, float *s_out,
+                     const uint32_t *ready, uint32_t spin_limit, uint64_t max_ticks,
+                     uint64_t start_ticks, const uint32_t *run_if, uint32_t *claim) {
+        auto kern = nct == 4 ? kda_inter_kernel<4> : nct == 2 ? kda_inter_kernel<2> : kda_inter_kernel<1>;
+        const int n_tiles = DV / (16 * nct);
         hipError_t err = hipSuccess;
         for (int p0 = 0; p0 < n_pairs && err == hipSuccess; p0 += INTER_MAX_PAIRS) {
             const int np = min(INTER_MAX_PAIRS, n_pairs - p0);
-            hipLaunchKernelGGL(kern, dim3((np + 7) / 8 * 8 * tiles), dim3(INTER_THREADS), 0,
+            hipLaunchKernelGGL(kern, dim3((np + 7) / 8 * 8 * n_tiles), dim3(INTER_THREADS), 0,
                                p.stream, off, order, p0, n_pairs, p.heads, p.seqlen, ncr, table,
                                (int)L.nc_max, recs, jlo, jhi, static_cast<const uint16_t *>(p.v),
-                               s_in, s_out, o);
+                               s_in, s_out, o, ready, status, spin_limit, max_ticks,
+                               start_ticks, run_if, claim);
             err = hipGetLastError();
         }
         return err;
+    };
+    auto serial_inter = [&](int jlo, int jhi, const float *s_in, float *s_out) {
+        return inter(wide ? 2 : 1, jlo, jhi, s_in, s_out, nullptr, 0u, 0, 0, nullptr, nullptr);
     };
 
     if (varlen || total == 0) {
@@ -1653,16 +1910,88 @@ hipError_t launch_chunk_fwd_mfma(const ChunkProblem &p) {
             hipLaunchKernelGGL(kda_chunk_index_kernel, dim3(1), dim3(1024), 0, p.stream, p.cu,
                                p.n_seqs, (int)total, off, order, table);
             if ((e = hipGetLastError()) != hipSuccess) return e;
-            if (L.nc_max > 0 && (e = intra(p.stream, 0, 0, p.heads * (int)L.nc_max)) != hipSuccess)
+            if (L.nc_max > 0 &&
+                (e = intra(p.stream, 0, 0, p.heads * (int)L.nc_max, nullptr, nullptr)) != hipSuccess)
                 return e;
         }
-        return inter(0, INT32_MAX / 2, p.s0, p.s_final);
+        return serial_inter(0, INT32_MAX / 2, p.s0, p.s_final);
     }
 
-    // Equal rows: all intra-chunk work, then the chunk chain, on the caller's stream.
     if (!launch_fits((int64_t)p.heads * p.batch * ncr, 256)) return hipErrorInvalidConfiguration;
-    if ((e = intra(p.stream, 0, ncr, p.heads * p.batch * ncr)) != hipSuccess) return e;
-    return inter(0, ncr, p.s0, p.s_final);
+    // Overlapped order, for equal rows of at least OVERLAP_MIN_CHUNKS chunks
+    // whose chains fit on half the CUs as 32-column tiles: the chain kernel
+    // starts at once on the caller's stream and reads each record as the
+    // intra-chunk kernel, on a side stream, publishes it (both kernels take
+    // the heads of their own XCD, h mod 8, so H must be a multiple of 8).  The
+    // intra-chunk work then shares the device with the chains instead of
+    // preceding them, and the records are read from L2 instead of HBM.  Left
+    // out: calls that cannot create a stream (the no-allocation entry point,
+    // stream capture), an initial state that the chain overwrites (the repair
+    // pass needs it), and a mode set to serial.  Measured at H = 32: 7% faster
+    // from 32768 tokens per row up, even at 8192, 10% slower at 4096 (the
+    // side stream's fork and join and the extra launches cost about 30 us).
+    // Side by side, the intra-chunk work has about half the CUs and bounds the
+    // call, so the overlap pays only while that work is lighter than the chain:
+    // with the logit gate and the in-kernel L2 norms it is not (4.43 against
+    // 4.36 ms at T = 131072), and those forms keep the serial order.
+    constexpr int OVERLAP_MIN_CHUNKS = 128;
+    const int mode = prefill_overlap_mode();
+    const bool light_intra = (p.form.flags() & (kFormGateLogit | kFormL2Norm)) == 0;
+    bool overlap = mode != 0 && p.allow_overlap && light_intra && p.heads % 8 == 0 &&
+                   (int64_t)n_pairs * (DV / (16 * KDA_OVERLAP_NCT)) * 2 <= n_cu &&
+                   ncr >= OVERLAP_MIN_CHUNKS && !(p.s_final && p.s_final == p.s0);
+    if (overlap) {
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        if ((e = hipStreamIsCapturing(p.stream, &cap)) != hipSuccess) return e;
+        overlap = cap == hipStreamCaptureStatusNone;
+    }
+    if (!overlap) {
+        // Serial order: all intra-chunk work, then the chunk chain, on the caller's stream.
+        if ((e = intra(p.stream, 0, ncr, p.heads * p.batch * ncr, nullptr, nullptr)) != hipSuccess)
+            return e;
+        return serial_inter(0, ncr, p.s0, p.s_final);
+    }
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStream *side = nullptr;
+    if ((e = side_stream(dev, &side)) != hipSuccess) return e;
+    int khz = 0;
+    if ((e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev)) != hipSuccess)
+        return e;
+    // A chain waits at most 10 ms plus 20 us per chunk in all (a chunk row of
+    // the intra-chunk kernel takes about 2 us beside the chains), then stops
+    // waiting and leaves the call to the repair pass.
+    const uint64_t max_ticks = (uint64_t)((10.0 + 0.02 * ncr) * (double)(khz > 0 ? khz : 100000));
+    const uint32_t spin_limit = mode == 2 ? 0u : 0xFFFFFFFFu;
+    // Clear the status word and every record flag.
+    const int64_t n_flags = (int64_t)(L.recs - L.flags) / 4;
+    const int64_t clear_blocks = (n_flags + 255) / 256;
+    hipLaunchKernelGGL(kda_clear_words_kernel, dim3(1), dim3(256), 0, p.stream, status, (int64_t)64);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(kda_clear_words_kernel,
+                       dim3((unsigned)(clear_blocks < 1024 ? clear_blocks : 1024)), dim3(256), 0,
+                       p.stream, flags, n_flags);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // The chain is enqueued first, so that its workgroups find whole CUs free
+    // (enqueued second, they wait for the intra-chunk workgroups to drain a
+    // CU: 3% slower).  Should the side stream share a hardware queue with the
+    // caller's stream (a process has a few, and streams beyond that share
+    // them), the intra-chunk kernel cannot start before the chain ends: each
+    // chain workgroup then gives up within START_US and the repair pass runs.
+    constexpr double START_US = 250.0;
+    const uint64_t start_ticks =
+        mode == 3 ? 0 : (uint64_t)(START_US * 1e-3 * (double)(khz > 0 ? khz : 100000));
+    if ((e = hipEventRecord(side->fork, p.stream)) != hipSuccess) return e;
+    if ((e = inter(KDA_OVERLAP_NCT, 0, ncr, p.s0, p.s_final, flags, spin_limit, max_ticks,
+                   start_ticks, nullptr, status + 16)) != hipSuccess)
+        return e;
+    if ((e = hipStreamWaitEvent(side->stream, side->fork, 0)) != hipSuccess) return e;
+    if ((e = intra(side->stream, 0, ncr, p.heads * p.batch * ncr, flags, status + 8)) !=
+        hipSuccess)
+        return e;
+    if ((e = hipEventRecord(side->join, side->stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(p.stream, side->join, 0)) != hipSuccess) return e;
+    // Repair pass: reruns the chain in the serial order if any record was not accepted.
+    return inter(wide ? 2 : 1, 0, ncr, p.s0, p.s_final, nullptr, 0u, 0, 0, status, nullptr);
 }
 
 }  // namespace kda

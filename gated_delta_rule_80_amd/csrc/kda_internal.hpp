@@ -58,7 +58,13 @@ struct ChunkProblem {
     void *workspace;
     size_t workspace_bytes;
     hipStream_t stream;
+    bool allow_overlap = true;   // false: never the overlapped prefill (creates no stream)
 };
+
+// Process-wide choice of the prefill order (kda_set_prefill_overlap): 0 serial,
+// 1 overlapped where it applies, 2 overlapped with every record refused, 3
+// overlapped with no wait for the first records (2 and 3 test the repair pass).
+int prefill_overlap_mode();
 
 // Upper bound on the number of chunks over all sequences: each sequence of
 // L tokens has ceil(L / C) <= L / C + 1 chunks.

@@ -28,7 +28,10 @@
  *   - `stream` is a hipStream_t, declared here by its underlying type
  *     `struct ihipStream_t *` so that this header needs no HIP header
  *     (NULL = the null stream).  All work is enqueued on it in order; calls
- *     return without synchronising.
+ *     return without synchronising.  (The overlapped prefill of
+ *     kda_chunk_fwd also runs one kernel on a side stream of the library's,
+ *     which waits for `stream` and which `stream` waits for, so the call
+ *     still starts and completes in order on `stream`.)
  *   - Arguments are validated on the host before anything is enqueued.  On any
  *     error nothing is enqueued, no output is touched, and a status other than
  *     KDA_OK is returned; kda_last_error() then describes the cause (the text
@@ -40,8 +43,11 @@
  *     leave kernels of the same call enqueued before the one that failed.
  *   - Device-side faults, if any, surface at the caller's next
  *     synchronisation, as for any HIP kernel.
- *   - No C++ exception crosses this boundary.  The library holds no global
- *     mutable state; concurrent calls on different streams are safe.
+ *   - No C++ exception crosses this boundary.  The library's only global
+ *     state is the prefill order (kda_set_prefill_overlap) and, per device,
+ *     the side stream and two events of the overlapped prefill, created by
+ *     its first use on the device and kept until the process ends;
+ *     concurrent calls on different streams are safe.
  *   - Values are not checked: NaN / Inf in, NaN / Inf out.
  */
 #ifndef KDA_H
@@ -57,7 +63,7 @@ extern "C" {
 /* The HIP stream type: hipStream_t is a pointer to this (opaque) struct. */
 struct ihipStream_t;
 
-#define KDA_ABI_VERSION 5
+#define KDA_ABI_VERSION 6
 
 typedef enum kda_status {
     KDA_OK = 0,
@@ -134,6 +140,23 @@ typedef struct kda_inputs_form {
 /* ABI version of the loaded library (KDA_ABI_VERSION it was built with). */
 int kda_abi_version(void);
 
+/*
+ * Chooses, for the whole process, the order in which kda_chunk_fwd (and the
+ * scalar-gate and _ex prefills) run their two bf16 kernels, and returns the
+ * previous choice, or -1 for an unknown mode (nothing changes then).
+ *   1  overlapped where it applies (the default; see kda_chunk_fwd)
+ *   0  always one after the other
+ *   2  overlapped, but the chain accepts no chunk's factors and runs on
+ *      whatever the workspace holds, so every overlapped call ends with the
+ *      repair pass: for testing that pass.
+ *   3  overlapped, but a chain whose first chunks' factors are not already
+ *      published gives up at once (as it does after 250 us in mode 1, when
+ *      the intra-chunk kernel is queued behind it), and the repair pass runs:
+ *      for testing that path.
+ * Calls already enqueued keep the order they were enqueued with.
+ */
+int kda_set_prefill_overlap(int mode);
+
 /* Static text for a status code. */
 const char *kda_status_string(kda_status status);
 
@@ -144,7 +167,8 @@ const char *kda_last_error(void);
  * Bytes of device workspace kda_chunk_fwd needs for `shape`, or 0 if the
  * shape is invalid or unsupported (kda_chunk_fwd then reports why).  The
  * workspace holds the per-chunk WY factors between the intra-chunk and the
- * inter-chunk kernels, and the chunk table of packed sequences.
+ * inter-chunk kernels, the chunk table of packed sequences, and one flag per
+ * (chunk, head) for the overlapped order.
  */
 size_t kda_chunk_fwd_workspace_bytes(const kda_shape *shape);
 
@@ -186,6 +210,26 @@ size_t kda_chunk_fwd_workspace_bytes(const kda_shape *shape);
  * the fp16 range, as the layer that calls this operator produces them.
  * Pointers to q, k, v, o, g and the states must be 16-byte aligned; beta and
  * cu_seqlens 4-byte aligned.
+ * Order of the two kernels (bf16 storage).  The intra-chunk kernel computes
+ * every chunk's factors independently and the chain kernel carries the state
+ * across chunks.  By default, for equal rows (no cu_seqlens) of at least 128
+ * chunks (8192 tokens at C = 64) with H a multiple of 8, at most n_cu / 8
+ * (sequence, head) pairs (32 on MI355X), an initial state that final_state
+ * does not overwrite and (through kda_chunk_fwd_ex) neither the logit gate nor
+ * the in-kernel L2 norms, whose intra-chunk work is as long as the chain, the
+ * two run side by side: the chain starts at once and
+ * takes each chunk's factors as soon as they are published, through the L2 of
+ * the XCD (accelerator die) on which both kernels place the head.  Should the chain fail to accept a chunk's factors (they came through
+ * another XCD, or did not arrive within about 10 ms plus 20 us per chunk),
+ * a repair pass reruns the chain after both kernels have ended (a chain
+ * that finds its first chunks' factors missing for 250 us gives up at once:
+ * the intra-chunk kernel is then queued behind it, as when the library's side
+ * stream shares a hardware queue with `stream`).  Every
+ * other call, and every call under stream capture, runs the kernels one after
+ * the other.  Both orders give the same bits.  An overlapped call leaves the
+ * first 32-bit word of the workspace nonzero if it needed its repair pass and
+ * 0 if not (a diagnostic, valid once the call has completed); a call run in
+ * the serial order does not write it.
  */
 kda_status kda_chunk_fwd(const kda_shape *shape, const void *q, const void *k,
                          const void *v, const float *g_log_decay,
@@ -219,6 +263,7 @@ kda_status kda_chunk_fwd(const kda_shape *shape, const void *q, const void *k,
  *     different host threads) race on it; serialise them, for example on one
  *     stream.  Each call writes every part of the buffer it later reads, so
  *     nothing needs clearing between calls.
+ *   - The two kernels always run one after the other (no side stream).
  */
 kda_status kda_chunk_fwd_noalloc(const kda_shape *shape, const void *q, const void *k,
                                  const void *v, const float *g_log_decay, const float *beta,

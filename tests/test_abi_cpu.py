@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = K.lib()
-    assert lib.kda_abi_version() == 5
+    assert lib.kda_abi_version() == 6
     for code, name in K.STATUS.items():
         assert lib.kda_status_string(code).decode() == name
 
