@@ -77,17 +77,9 @@ constexpr float MIN_LOG_DECAY = -10.f;
 #ifndef KDA_INTER_TOUCH
 #define KDA_INTER_TOUCH 128
 #endif
-#ifndef KDA_INTER_PF_W4
-#define KDA_INTER_PF_W4 1
-#endif
-#ifndef KDA_OVERLAP_NCT
-#define KDA_OVERLAP_NCT 2
-#endif
-// Chunk records in flight per inter wave, for 16-, 32- and 64-column value tiles.
+// Chunk records in flight per inter wave, for 16- and 32-column value tiles.
 template <int NCT>
-constexpr int ring_depth() {
-    return NCT == 1 ? KDA_INTER_PF : NCT == 2 ? KDA_INTER_PF_WIDE : KDA_INTER_PF_W4;
-}
+constexpr int ring_depth() { return NCT == 1 ? KDA_INTER_PF : KDA_INTER_PF_WIDE; }
 constexpr int L2D = KDA_INTER_L2D;    // L2 prefetch distance in chunks (0: no prefetch wave)
 constexpr int L2R = KDA_INTER_L2R;    // chunks a prefetch load may stay in flight
 constexpr int TOUCH = KDA_INTER_TOUCH;  // bytes of a record between two prefetch touches
@@ -1439,6 +1431,94 @@ __device__ __forceinline__ void output_step(OutOps<NCT> &op, const half8 *sS, co
     load_v<NCT>(op.V, vr, min(x + 2, clast), t, l);
 }
 
+// The chain's side of the record handoff in the overlapped order, run by the
+// ninth wave of the workgroup.  The other waves load record x at step x - PF
+// (the T Diag(beta) fragments at step x - PF - 1, after that step's second
+// barrier), and the first PF + 1 records before the loop; the handoff wave
+// accepts each record before the barrier that precedes its first load.  A record's flag is
+// read one step before it is needed, so a record already published costs no
+// wait.  A flag from another XCD, or none within the limits, marks the call
+// for the repair pass and ends every later wait (the chain then runs on
+// whatever the records hold, in bounds, and its results are overwritten).
+struct Handoff {
+    const uint32_t *fl;   // the head's record flags
+    uint32_t *status;
+    uint32_t me, spin_limit, next;
+    uint64_t t_start, deadline, max_ticks;
+    int cs, ce, h, l;
+    bool bad;
+
+    __device__ void init(const uint32_t *ready, int nc_max_, uint32_t *status_, uint32_t spin,
+                         uint64_t max_t, uint64_t start_t, int cs_, int ce_, int h_, int l_) {
+        fl = ready + (size_t)h_ * nc_max_;
+        status = status_;
+        me = xcc_id();
+        spin_limit = spin;
+        t_start = (uint64_t)wall_clock64();
+        deadline = t_start + start_t;   // for the first records; then t_start + max_t
+        max_ticks = max_t;
+        cs = cs_;
+        ce = ce_;
+        h = h_;
+        l = l_;
+        bad = false;
+        next = 0;
+        if (spin_limit == 0) mark(3u, 0u, cs);   // accept nothing: the repair pass recomputes
+    }
+    // Marks the call for the repair pass.  The first refusal of the call also
+    // leaves its details in status[1..5]: why (1 not seen in time, 2 from
+    // another XCD, 3 refused by request), the flag seen, this XCD, the chunk
+    // and the head.
+    __device__ void mark(uint32_t why, uint32_t seen, int cc) {
+        bad = true;
+        if (l == 0) {
+            __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (atomicCAS(status + 1, 0u, why) == 0u) {
+                status[2] = seen;
+                status[3] = me;
+                status[4] = (uint32_t)cc;
+                status[5] = (uint32_t)h;
+            }
+        }
+    }
+    __device__ uint32_t peek(int cc) const {
+        return (bad || cc >= ce) ? 0u
+                                 : __hip_atomic_load(fl + cc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __device__ void accept(int cc, uint32_t x) {
+        if (bad || cc >= ce) return;
+        x = __builtin_amdgcn_readfirstlane(x);
+        for (uint32_t it = 0; x == 0u; ++it) {
+            if (it >= spin_limit || (uint64_t)wall_clock64() > deadline) break;
+            __builtin_amdgcn_s_sleep(1);
+            x = __builtin_amdgcn_readfirstlane(
+                __hip_atomic_load(fl + cc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        }
+        if (x != (REC_READY | me)) mark(x == 0u ? 1u : 2u, x, cc);
+    }
+    // With rings PF records deep, step c accepts chunk c + A, A = PF + 1, and
+    // the records before the loop are cs .. cs + A - 1.
+    // Before the first barrier: the records of chunks cs .. cs + A - 1.
+    // Returns true when the workgroup must end at once: they did not come in
+    // time (the intra-chunk kernel is then queued behind this one) or not from
+    // this XCD.
+    template <int A>
+    __device__ bool begin() {
+#pragma unroll 1
+        for (int j = 0; j < A; ++j) accept(cs + j, peek(cs + j));
+        const bool quit = bad && spin_limit != 0;
+        deadline = t_start + max_ticks;
+        next = peek(cs + A);
+        return quit;
+    }
+    // Between the two barriers of step c: the record of chunk c + A.
+    template <int A>
+    __device__ void step(int c) {
+        accept(c + A, next);
+        next = peek(c + A + 1);
+    }
+};
+
 // Processes local chunks [jlo, jhi) of every (sequence, head, value tile): the
 // state is read from s_in (NULL = zeros) and written to s_out (NULL = not
 // written).  s_out may equal s_in: each lane reads its state elements before
@@ -1461,6 +1541,7 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
     uint64_t max_ticks, uint64_t start_ticks, const uint32_t *run_if, uint32_t *claim) {
     constexpr int NTILES = DV / (16 * NCT);   // workgroups per (sequence, head)
     constexpr int PF = ring_depth<NCT>();
+    constexpr int ACC = PF + 1;   // the handoff accepts record c + ACC at step c
     constexpr int U_SLOT = 4 * NCT * 64, VT_SLOT = 16 * NCT * VTP;
     __shared__ half8 sS[4 * NCT * 64];   // S as fp16 B-fragments [channel block][column tile]
     __shared__ half8 sZ[2 * NCT * 64];   // Z as fp16 B-fragments [token block][column tile]
@@ -1646,67 +1727,18 @@ __global__ __launch_bounds__(INTER_THREADS, 1) void kda_inter_kernel(
     } else if (ready) {
         // Handoff wave: the records come from an intra-chunk kernel running
         // beside this one, through this XCD's L2, so nothing is touched ahead.
-        // The other waves load record x at step x - PF (the T Diag(beta)
-        // fragments at step x - PF - 1, after that step's second barrier), and
-        // the first PF + 1 records before the loop; this wave accepts each
-        // record before the barrier that precedes its first load.  A record's
-        // flag is read one step before it is needed, so a record that is
-        // already published costs no wait.
         static_assert(L2D > 0, "the overlapped chain needs its ninth wave");
-        const uint32_t *fl = ready + (size_t)h * nc_max;
-        const uint32_t me = xcc_id();
-        const uint64_t t_start = (uint64_t)wall_clock64();
-        uint64_t deadline = t_start + start_ticks;   // for the first records, then t_start + max_ticks
-        bool bad = false;
-        // Marks the call for the repair pass.  The first refusal of the call
-        // also leaves its details in status[1..5]: why (1 not seen in time,
-        // 2 from another XCD, 3 refused by request), the flag seen, this XCD,
-        // the chunk and the head.
-        auto mark = [&](uint32_t why, uint32_t seen, int cc) {
-            bad = true;
-            if (l == 0) {
-                __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (atomicCAS(status + 1, 0u, why) == 0u) {
-                    status[2] = seen;
-                    status[3] = me;
-                    status[4] = (uint32_t)cc;
-                    status[5] = (uint32_t)h;
-                }
-            }
-        };
-        if (spin_limit == 0) mark(3u, 0u, cs);   // accept nothing: the repair pass recomputes the call
-        auto peek = [&](int cc) -> uint32_t {
-            return (bad || cc >= ce)
-                       ? 0u
-                       : __hip_atomic_load(fl + cc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        };
-        // Waits until record cc is published; a flag from another XCD, or none
-        // within the limits, marks the call and ends every later wait.
-        auto accept = [&](int cc, uint32_t x) {
-            if (bad || cc >= ce) return;
-            x = __builtin_amdgcn_readfirstlane(x);
-            for (uint32_t it = 0; x == 0u; ++it) {
-                if (it >= spin_limit || (uint64_t)wall_clock64() > deadline) break;
-                __builtin_amdgcn_s_sleep(1);
-                x = __builtin_amdgcn_readfirstlane(
-                    __hip_atomic_load(fl + cc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-            }
-            if (x != (REC_READY | me)) mark(x == 0u ? 1u : 2u, x, cc);
-        };
-#pragma unroll 1
-        for (int j = 0; j <= PF; ++j) accept(cs + j, peek(cs + j));
-        const bool quit = bad && spin_limit != 0;   // not refused by request: never came
+        Handoff hand;
+        hand.init(ready, nc_max, status, spin_limit, max_ticks, start_ticks, cs, ce, h, l);
+        const bool quit = hand.begin<ACC>();
         if (l == 0) s_quit = quit ? 1 : 0;
         lds_barrier();   // the records of the first chunks are published (or never will be)
         if (quit) return;
-        deadline = t_start + max_ticks;
-        uint32_t next = peek(cs + PF + 1);
         lds_barrier();   // the output waves' U of the first chunk
 #pragma unroll 1
         for (int c = cs; c < ce; ++c) {
             lds_barrier();
-            accept(c + PF + 1, next);
-            next = peek(c + PF + 2);
+            hand.step<ACC>(c);
             lds_barrier();
         }
     } else if (L2D > 0) {
@@ -1885,7 +1917,7 @@ hipError_t launch_chunk_fwd_mfma(const ChunkProblem &p) {
     auto inter = [&](int nct, int jlo, int jhi, const float *s_in, float *s_out,
                      const uint32_t *ready, uint32_t spin_limit, uint64_t max_ticks,
                      uint64_t start_ticks, const uint32_t *run_if, uint32_t *claim) {
-        auto kern = nct == 4 ? kda_inter_kernel<4> : nct == 2 ? kda_inter_kernel<2> : kda_inter_kernel<1>;
+        auto kern = nct == 2 ? kda_inter_kernel<2> : kda_inter_kernel<1>;
         const int n_tiles = DV / (16 * nct);
         hipError_t err = hipSuccess;
         for (int p0 = 0; p0 < n_pairs && err == hipSuccess; p0 += INTER_MAX_PAIRS) {
@@ -1938,7 +1970,7 @@ hipError_t launch_chunk_fwd_mfma(const ChunkProblem &p) {
     const int mode = prefill_overlap_mode();
     const bool light_intra = (p.form.flags() & (kFormGateLogit | kFormL2Norm)) == 0;
     bool overlap = mode != 0 && p.allow_overlap && light_intra && p.heads % 8 == 0 &&
-                   (int64_t)n_pairs * (DV / (16 * KDA_OVERLAP_NCT)) * 2 <= n_cu &&
+                   (int64_t)n_pairs * (DV / 32) * 2 <= n_cu &&
                    ncr >= OVERLAP_MIN_CHUNKS && !(p.s_final && p.s_final == p.s0);
     if (overlap) {
         hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
@@ -1981,8 +2013,8 @@ hipError_t launch_chunk_fwd_mfma(const ChunkProblem &p) {
     const uint64_t start_ticks =
         mode == 3 ? 0 : (uint64_t)(START_US * 1e-3 * (double)(khz > 0 ? khz : 100000));
     if ((e = hipEventRecord(side->fork, p.stream)) != hipSuccess) return e;
-    if ((e = inter(KDA_OVERLAP_NCT, 0, ncr, p.s0, p.s_final, flags, spin_limit, max_ticks,
-                   start_ticks, nullptr, status + 16)) != hipSuccess)
+    if ((e = inter(2, 0, ncr, p.s0, p.s_final, flags, spin_limit, max_ticks, start_ticks, nullptr,
+                   status + 16)) != hipSuccess)
         return e;
     if ((e = hipStreamWaitEvent(side->stream, side->fork, 0)) != hipSuccess) return e;
     if ((e = intra(side->stream, 0, ncr, p.heads * p.batch * ncr, flags, status + 8)) !=
