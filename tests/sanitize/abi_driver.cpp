@@ -71,6 +71,7 @@ static void prefill_checks() {
     CHECK(fwd(s, dev(20), need) == KDA_OK);
     CHECK(g_stub.kind == StubRecord::PrefillMfma);
     CHECK(g_stub.prefill.batch == 2 && g_stub.prefill.seqlen == 300 && g_stub.prefill.heads == 4);
+    CHECK(g_stub.prefill.allow_overlap);
     CHECK(g_stub.prefill.q == dev(1) && g_stub.prefill.o == dev(7) && g_stub.prefill.cu == nullptr);
     CHECK(g_stub.prefill.gate == kda::Gate::PerChannel && g_stub.prefill.form.flags() == 0);
     CHECK(std::strcmp(kda_last_error(), "") == 0);
@@ -206,6 +207,7 @@ static void noalloc_checks() {
     CHECK(call(s, static_cast<hipStream_t>(dev(30))) == KDA_OK && g_stub.kind == StubRecord::PrefillMfma);
     CHECK(g_stub.prefill.workspace == reinterpret_cast<void *>(0x7f0000000000ull + (3ull << 32)));
     CHECK(g_stub.prefill.workspace_bytes == KDA_NOALLOC_SCRATCH_BYTES);
+    CHECK(!g_stub.prefill.allow_overlap);   // the no-allocation path never creates a stream
     CHECK(call(s, nullptr) == KDA_OK);
     // A stream of another device is refused (the buffer is the current device's).
     g_stub_stream_device = 1;
@@ -297,6 +299,13 @@ static void backward_checks() {
 
 static void misc_checks() {
     CHECK(kda_abi_version() == KDA_ABI_VERSION);
+    // The prefill order: modes 0-3, the previous mode returned, unknown modes refused.
+    const int prev = kda_set_prefill_overlap(0);
+    CHECK(prev == 1 && kda::prefill_overlap_mode() == 0);
+    CHECK(kda_set_prefill_overlap(3) == 0 && kda::prefill_overlap_mode() == 3);
+    CHECK(kda_set_prefill_overlap(4) == -1 && kda_set_prefill_overlap(-1) == -1);
+    CHECK(kda::prefill_overlap_mode() == 3);
+    CHECK(kda_set_prefill_overlap(prev) == 3 && kda::prefill_overlap_mode() == 1);
     for (int st = 0; st <= 6; ++st) CHECK(kda_status_string(static_cast<kda_status>(st)) != nullptr);
     CHECK(std::strcmp(kda_status_string(KDA_ERR_HIP), "KDA_ERR_HIP") == 0);
     // The last-error text is per thread: a failure on another thread leaves this one's alone.
