@@ -1973,9 +1973,13 @@ hipError_t launch_chunk_fwd_mfma(const ChunkProblem &p) {
                    (int64_t)n_pairs * (DV / 32) * 2 <= n_cu &&
                    ncr >= OVERLAP_MIN_CHUNKS && !(p.s_final && p.s_final == p.s0);
     if (overlap) {
+        // The side stream is the current device's: a caller's stream of another
+        // device keeps the serial order (its kernels run on the stream's device).
+        int sdev = dev;
+        if (p.stream && (e = hipStreamGetDevice(p.stream, &sdev)) != hipSuccess) return e;
         hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
         if ((e = hipStreamIsCapturing(p.stream, &cap)) != hipSuccess) return e;
-        overlap = cap == hipStreamCaptureStatusNone;
+        overlap = sdev == dev && cap == hipStreamCaptureStatusNone;
     }
     if (!overlap) {
         // Serial order: all intra-chunk work, then the chunk chain, on the caller's stream.
@@ -1994,7 +1998,8 @@ hipError_t launch_chunk_fwd_mfma(const ChunkProblem &p) {
     // waiting and leaves the call to the repair pass.
     const uint64_t max_ticks = (uint64_t)((10.0 + 0.02 * ncr) * (double)(khz > 0 ? khz : 100000));
     const uint32_t spin_limit = mode == 2 ? 0u : 0xFFFFFFFFu;
-    // Clear the status word and every record flag.
+    // Clear the status words (repair flag, refusal details, work counters) and
+    // every record flag.
     const int64_t n_flags = (int64_t)(L.recs - L.flags) / 4;
     const int64_t clear_blocks = (n_flags + 255) / 256;
     hipLaunchKernelGGL(kda_clear_words_kernel, dim3(1), dim3(256), 0, p.stream, status, (int64_t)64);

@@ -212,24 +212,26 @@ size_t kda_chunk_fwd_workspace_bytes(const kda_shape *shape);
  * cu_seqlens 4-byte aligned.
  * Order of the two kernels (bf16 storage).  The intra-chunk kernel computes
  * every chunk's factors independently and the chain kernel carries the state
- * across chunks.  By default, for equal rows (no cu_seqlens) of at least 128
- * chunks (8192 tokens at C = 64) with H a multiple of 8, at most n_cu / 8
- * (sequence, head) pairs (32 on MI355X), an initial state that final_state
- * does not overwrite and (through kda_chunk_fwd_ex) neither the logit gate nor
- * the in-kernel L2 norms, whose intra-chunk work is as long as the chain, the
- * two run side by side: the chain starts at once and
- * takes each chunk's factors as soon as they are published, through the L2 of
- * the XCD (accelerator die) on which both kernels place the head.  Should the chain fail to accept a chunk's factors (they came through
- * another XCD, or did not arrive within about 10 ms plus 20 us per chunk),
- * a repair pass reruns the chain after both kernels have ended (a chain
- * that finds its first chunks' factors missing for 250 us gives up at once:
- * the intra-chunk kernel is then queued behind it, as when the library's side
- * stream shares a hardware queue with `stream`).  Every
- * other call, and every call under stream capture, runs the kernels one after
- * the other.  Both orders give the same bits.  An overlapped call leaves the
- * first 32-bit word of the workspace nonzero if it needed its repair pass and
- * 0 if not (a diagnostic, valid once the call has completed); a call run in
- * the serial order does not write it.
+ * across chunks.  By default the two run side by side for equal rows (no
+ * cu_seqlens) of at least 128 chunks (8192 tokens at C = 64) with H a
+ * multiple of 8, at most n_cu / 8 (sequence, head) pairs (32 on MI355X), an
+ * initial state that final_state does not overwrite, and (through
+ * kda_chunk_fwd_ex) neither the logit gate nor the in-kernel L2 norms, whose
+ * intra-chunk work is as long as the chain.  The chain then starts at once
+ * and takes each chunk's factors as soon as they are published, through the
+ * L2 of the XCD (accelerator die) on which both kernels place the head.
+ * Should the chain fail to accept a chunk's factors (they came through
+ * another XCD, or did not arrive within about 10 ms plus 20 us per chunk), a
+ * repair pass reruns the chain after both kernels have ended.  A chain that
+ * finds its first chunks' factors missing for 250 us gives up at once: the
+ * intra-chunk kernel is then queued behind it, as when the library's side
+ * stream shares a hardware queue with `stream`.  Every other call, every call
+ * under stream capture and every call whose `stream` belongs to another
+ * device than the current one runs the kernels one after the other.  Both
+ * orders give the same bits.  An overlapped call leaves the first 32-bit word
+ * of the workspace nonzero if it needed its repair pass and 0 if not (a
+ * diagnostic, valid once the call has completed); a call run in the serial
+ * order does not write it.
  */
 kda_status kda_chunk_fwd(const kda_shape *shape, const void *q, const void *k,
                          const void *v, const float *g_log_decay,
