@@ -83,13 +83,14 @@ __device__ __forceinline__ void seq_range(const int32_t *cu, int row_len, int n,
     }
 }
 
-// The chunk held by slot `slot`: its sequence's bounds and the chunk's first
-// token and length.  False for a gap slot (uniform over a workgroup).
+// The chunk held by slot `slot`: its first token and length, its index c
+// within its sequence and the sequence's end te.  False for a gap slot
+// (uniform over a workgroup).
 template <int C>
 __device__ __forceinline__ bool slot_chunk(const int32_t *cu, int row_len, int n_seqs, int slot,
-                                           int &t0, int &len) {
+                                           int &t0, int &len, int &c, int &te) {
     // the sequence owning the slot: the last n with chunk_base(n) <= slot
-    int lo = 0, hi = n_seqs - 1, ts, te;
+    int lo = 0, hi = n_seqs - 1, ts;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         seq_range(cu, row_len, mid, ts, te);
@@ -97,11 +98,17 @@ __device__ __forceinline__ bool slot_chunk(const int32_t *cu, int row_len, int n
         else hi = mid - 1;
     }
     seq_range(cu, row_len, lo, ts, te);
-    const int c = slot - chunk_base(ts, lo, C);
+    c = slot - chunk_base(ts, lo, C);
     if (c >= (te - ts + C - 1) / C) return false;
     t0 = ts + c * C;
     len = min(C, te - t0);
     return true;
+}
+template <int C>
+__device__ __forceinline__ bool slot_chunk(const int32_t *cu, int row_len, int n_seqs, int slot,
+                                           int &t0, int &len) {
+    int c, te;
+    return slot_chunk<C>(cu, row_len, n_seqs, slot, t0, len, c, te);
 }
 
 // ---- shared chunk steps (one workgroup, THREADS threads, operands in LDS) ----------
@@ -659,9 +666,13 @@ __global__ __launch_bounds__(MT) void kda_bwd_chain_mfma_kernel(
             St[cl][e] = s0 ? s0[pair * dd + (size_t)srow(cl, e) * d + v0 + i16] : 0.f;
 
     // ---- forward sweep ----
+    // The state is stored at the start of even chunks only, and dS' at the end
+    // of odd chunks and of the last one: the gradient kernel rebuilds the
+    // other from its neighbour's with one chunk step, which costs less than
+    // the stores saved.
     auto fwd_step = [&](int c, const FwdOps<In> &op) {
         const size_t slot = (size_t)(base + c) * H + h;
-        store_tile(St, ws.S + slot * dd);
+        if (!(c & 1)) store_tile(St, ws.S + slot * dd);
         // this wave's part of Z: -R[:, rows of w] S[rows of w], plus step w of U
         float4v p = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -716,7 +727,7 @@ __global__ __launch_bounds__(MT) void kda_bwd_chain_mfma_kernel(
             St[cl][e] = dfinal ? dfinal[pair * dd + (size_t)srow(cl, e) * d + v0 + i16] : 0.f;
     auto rev_step = [&](int c, const RevOps<In> &op) {
         const size_t slot = (size_t)(base + c) * H + h;
-        store_tile(St, ws.dS + slot * dd);
+        if ((c & 1) || c == nck - 1) store_tile(St, ws.dS + slot * dd);
         float dO[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) dO[s] = 4 * g4 + s < op.len ? Raw<In>::f(op.dr[s]) : 0.f;
@@ -839,10 +850,22 @@ __global__ __launch_bounds__(GT) void kda_bwd_grad_kernel(
 
     const int slot = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
     const int tid = threadIdx.x;
-    int t0, len;
-    if (!slot_chunk<C>(cu, row_len, n_seqs, slot, t0, len)) return;
+    int t0, len, cix, te;
+    if (!slot_chunk<C>(cu, row_len, n_seqs, slot, t0, len, cix, te)) return;
     const int cd = C * d, dd = d * d, SR = slice_rows(d), dp = row_stride(d);
     const size_t wslot = (size_t)slot * H + h;
+    // At d = 128, C = 16 the chain kernel stores S only at the start of even
+    // chunks and dS' only at the end of odd chunks and of the last one.  An
+    // odd chunk rebuilds its S from chunk c - 1: S = Diag(e^{G_C}) S_prev +
+    // Kbar^T Z of that chunk.  An even chunk that is not the last rebuilds its
+    // dS' from chunk c + 1: dS' = Diag(e^{G_C}) dS'_next + Qbar^T dO - R^T dZ
+    // of that chunk.  Both are the chain's own steps (the chunk recurrence and
+    // its reverse), with operands from the workspace.  The staged operands sit
+    // in the storage of dL (Z or dZ of the neighbour) and dR (dO of the next
+    // chunk), both written only after the products with S and dS'.
+    constexpr bool HALF = C == MC && D == MD;
+    const bool s_rebuild = HALF && (cix & 1);
+    const bool ds_rebuild = HALF && !(cix & 1) && t0 + C < te;
 
     {
         const size_t off = ((size_t)t0 * H + h) * d, pitch = (size_t)H * d;
@@ -863,9 +886,18 @@ __global__ __launch_bounds__(GT) void kda_bwd_grad_kernel(
             rT[u] = ws.T[wslot * C * C + e];
             rK[u] = ws.Kt[wslot * C * C + e];
         }
+        Rows<GT> rx, ry;
+        if (s_rebuild) {
+            fetch_rows(rx, ws.Z + (wslot - H) * cd, d, C, C, d, tid);
+        } else if (ds_rebuild) {
+            fetch_rows(rx, ws.dZ + (wslot + H) * cd, d, C, C, d, tid);
+            fetch_rows(ry, dout + off + C * pitch, pitch, C, min(C, te - t0 - C), d, tid);
+        }
         float *dst[7] = {sq, sk, sG, sv, sdO, sZ, sdZ};
 #pragma unroll
         for (int a = 0; a < 7; ++a) commit_rows(dst[a], r[a], C, d, tid);
+        if (s_rebuild || ds_rebuild) commit_rows(sdL, rx, C, d, tid);
+        if (ds_rebuild) commit_rows(sdR, ry, C, d, tid);
         if (tid < C) sb[tid] = rb;
 #pragma unroll
         for (int u = 0; u < NCC; ++u)
@@ -880,7 +912,8 @@ __global__ __launch_bounds__(GT) void kda_bwd_grad_kernel(
 
     // The products with S and dS':
     //   dR = -dZ S^T,  dQbar = dO S^T,  dKbar = Z dS'^T,  gc = e^{G_C} rowsum(dS' . S).
-    const float *Sg = ws.S + wslot * dd, *dSg = ws.dS + wslot * dd;
+    const float *Sg = ws.S + (s_rebuild ? wslot - H : wslot) * dd;
+    const float *dSg = ws.dS + (ds_rebuild ? wslot + H : wslot) * dd;
     // At d = 128, C = 16 (fp32 MFMA): wave w takes channels 16w .. 16w+15 (the
     // output columns), token rows are the output rows, and the value index u is
     // the reduction.  Instruction (T, s) takes u = 16T + 4 (l/16) + s from lane
@@ -897,6 +930,37 @@ __global__ __launch_bounds__(GT) void kda_bwd_grad_kernel(
             const int u = 16 * T + 4 * g4;
             rS[T] = *reinterpret_cast<const float4 *>(Sg + (size_t)ch * d + u);
             rdS[T] = *reinterpret_cast<const float4 *>(dSg + (size_t)ch * d + u);
+        }
+        // The rebuilt tile in the layout of rS: computed transposed, value
+        // rows 16T + l % 16 (A, from LDS) by channels (B), token 4 (l/16) + s in
+        // step s, so accumulator element e is value 16T + 4 (l/16) + e of
+        // channel ch.
+        auto rebuild = [&](float4 (&X)[8], size_t nb, const float *A1, const float *B1,
+                           const float *A2, const float *B2) {
+            const float gc = ws.gC[nb * d + ch];
+            float b1[4], b2[4];
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+                b1[s2] = B1[nb * cd + (4 * g4 + s2) * d + ch];
+                b2[s2] = B2 ? -B2[nb * cd + (4 * g4 + s2) * d + ch] : 0.f;
+            }
+#pragma unroll
+            for (int T = 0; T < 8; ++T) {
+                float4v a = as4v(X[T]) * gc;
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2) {
+                    const int x = (4 * g4 + s2) * dp + 16 * T + i16;
+                    a = mfma4(A1[x], b1[s2], a);
+                    if (A2) a = mfma4(A2[x], b2[s2], a);
+                }
+                X[T] = make_float4(a[0], a[1], a[2], a[3]);
+            }
+        };
+        if (s_rebuild) {
+            rebuild(rS, wslot - H, sdL, ws.Kb, nullptr, nullptr);
+        } else if (ds_rebuild) {
+            rebuild(rdS, wslot + H, sdR, ws.Qb, sdL, ws.R);
+            __syncthreads();   // dR's storage is written below
         }
         float4v aR = {0.f, 0.f, 0.f, 0.f};
         float gsum = 0.f;

@@ -116,6 +116,15 @@ def test_backward_d128_odd_and_even_chunk_counts_without_final_gradient():
     check(make(1, 0, 3, 128, seed=207, lengths=[49, 16, 0, 33], dfin=False), 16)
 
 
+def test_backward_d128_rebuilt_states_along_long_sequences():
+    """At d = 128, chunk 16, the chain stores S at even chunks and dS' at odd
+    ones and the last; the gradient kernel rebuilds the rest.  Sequences of
+    11 (ragged), 2, 1, 6 and 2 (ragged) chunks put the last chunk at both
+    parities, full and ragged, and chain rebuilds over many chunks."""
+    check(make(1, 0, 2, 128, seed=208, lengths=[161, 32, 15, 96, 17]), 16)
+    check(to_bf16(make(1, 0, 2, 128, seed=209, lengths=[17, 15, 160])), 16)
+
+
 @pytest.mark.parametrize("d,C,T", [(128, 16, 45), (64, 32, 70), (16, 64, 130)])
 def test_backward_bf16_storage(d, C, T):
     check(to_bf16(make(2, T, 2, d, seed=300 + d)), C)
