@@ -1191,11 +1191,12 @@ __global__ __launch_bounds__(GT) void kda_bwd_grad_kernel(
     // Per (row x, channel c), with E_ij = e^{G_ic - G_jc}:
     //   P1 = sum_{j<x} dK~_xj k_jc E_xj,  P2 = sum_{i>x} dK~_ix k_ic E_ix,
     //   P3 = sum_{j<=x} dH_xj k_jc E_xj,  P4 = sum_{i>=x} dH_ix (s q_ic) E_ix;
-    // then the direct uses of e^{G} in Qbar, L and Kbar.
-    for (int e = tid; e < cd; e += GT) {
-        const int x = e / d, c2 = e - x * d, ax = x * dp + c2;
-        const float Gx = sG[ax], kx = sk[ax], qx = scale * sq[ax];
-        float P1 = 0.f, P2 = 0.f, P3 = 0.f, P4 = 0.f;
+    // then the direct uses of e^{G} in Qbar, L and Kbar.  dK~ is zero on and
+    // above its diagonal and dH above it, so the bounds on j and i hold by
+    // themselves wherever the sums run over all rows.
+    auto pairwise = [&](int x, int c2, float &P1, float &P2, float &P3, float &P4) {
+        const float Gx = sG[x * dp + c2];
+        P1 = P2 = P3 = P4 = 0.f;
         for (int j = 0; j <= x; ++j) {
             const float E = fast_exp(Gx - sG[j * dp + c2]) * sk[j * dp + c2];
             if (j < x) P1 += sKt[x * C + j] * E;
@@ -1206,6 +1207,13 @@ __global__ __launch_bounds__(GT) void kda_bwd_grad_kernel(
             if (i > x) P2 += sKt[i * C + x] * sk[i * dp + c2] * E;
             P4 += sHm[i * C + x] * scale * sq[i * dp + c2] * E;
         }
+    };
+    // dq and dk of row x, channel c2 to global memory; dG and the Kbar-term
+    // of dG_C (summed over the rows below) into dR's and dL's storage, where
+    // only this element's own thread reads them before the barrier.
+    auto finish = [&](int x, int c2, float P1, float P2, float P3, float P4) {
+        const int ax = x * dp + c2;
+        const float Gx = sG[ax], kx = sk[ax], qx = scale * sq[ax];
         const float dQb = sdQb[ax], dKb = sdKb[ax], dLx = sdL[ax];
         const float eG = fast_exp(Gx), eK = fast_exp(sG[(C - 1) * dp + c2] - Gx);
         const float dqs = P3 + dQb * eG;
@@ -1218,7 +1226,55 @@ __global__ __launch_bounds__(GT) void kda_bwd_grad_kernel(
             dk[a] = dkx;
         }
         sdG[ax] = dGx;
-        sdL[ax] = dKb * kx * eK;   // Kbar-term of dG_C, summed over rows below
+        sdL[ax] = dKb * kx * eK;
+    };
+    if constexpr (C == 16 && D == 128) {
+        // On fp32 MFMA.  With row r = 7 of the cumulative decays as reference,
+        // e^{G_x - G_j} = e^{G_x - G_r} e^{G_r - G_j} in each channel, so every
+        // sum is a C x C by C x d product between two row scalings:
+        //   P1, P3 = e^{G_x - G_r} (dK~, dH) (k e^{G_r - G}),
+        //   P2 = e^{G_r - G_x} dK~^T (k e^{G - G_r}),  P4 = e^{G_r - G_x} dH^T (s q e^{G - G_r}).
+        // A channel that decays by at most 40 over the chunk keeps both factors
+        // within e^{+-40}; a wave with a channel beyond that takes the pairwise
+        // factors instead.  Wave w takes channels 16w .. 16w+15; lane l gives
+        // token 4s + l/16 in step s, and accumulator element e is row 4 (l/16) + e.
+        const int l = tid & 63, g4 = l >> 4, i16 = l & 15, ch = 16 * (tid >> 6) + i16;
+        float P1[4], P2[4], P3[4], P4[4];
+        if (__all(sG[ch] - sG[(C - 1) * dp + ch] <= 40.f)) {
+            const float Gr = sG[7 * dp + ch];
+            float4v a1 = {0.f, 0.f, 0.f, 0.f}, a2 = a1, a3 = a1, a4 = a1;
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+                const int j = 4 * s2 + g4, aj = j * dp + ch;
+                const float Gj = sG[aj], kj = sk[aj], qj = scale * sq[aj];
+                const float up = fast_exp(Gj - Gr), dn = fast_exp(Gr - Gj);
+                a1 = mfma4(sKt[i16 * C + j], kj * dn, a1);
+                a3 = mfma4(sHm[i16 * C + j], kj * dn, a3);
+                a2 = mfma4(sKt[j * C + i16], kj * up, a2);
+                a4 = mfma4(sHm[j * C + i16], qj * up, a4);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float Gx = sG[(4 * g4 + e) * dp + ch];
+                const float up = fast_exp(Gx - Gr), dn = fast_exp(Gr - Gx);
+                P1[e] = a1[e] * up;
+                P3[e] = a3[e] * up;
+                P2[e] = a2[e] * dn;
+                P4[e] = a4[e] * dn;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pairwise(4 * g4 + e, ch, P1[e], P2[e], P3[e], P4[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) finish(4 * g4 + e, ch, P1[e], P2[e], P3[e], P4[e]);
+    } else {
+        for (int e = tid; e < cd; e += GT) {
+            const int x = e / d, c2 = e - x * d;
+            float P1, P2, P3, P4;
+            pairwise(x, c2, P1, P2, P3, P4);
+            finish(x, c2, P1, P2, P3, P4);
+        }
     }
     __syncthreads();
     // dG_C = gc + sum_x dKbar_x Kbar_x joins the last row; dg is the reverse

@@ -125,6 +125,19 @@ def test_backward_d128_rebuilt_states_along_long_sequences():
     check(to_bf16(make(1, 0, 2, 128, seed=209, lengths=[17, 15, 160])), 16)
 
 
+def test_backward_d128_pairwise_and_factored_decay_paths():
+    """At d = 128, chunk 16, a wave whose 16 channels all decay by at most 40
+    over a chunk forms the decay-weighted sums as matrix products between
+    row scalings; any other wave takes the pairwise factors.  Channels 0-47
+    decay by 3-4 per token (spans of 45-60 over a full chunk), 48-127 weakly,
+    so waves 0-2 take the pairwise factors and waves 3-7 the products,
+    except in the short last chunk."""
+    x = make(1, 70, 2, 128, seed=210)
+    rng = np.random.default_rng(211)
+    x["g"][..., :48] = rng.uniform(-4.0, -3.0, size=x["g"][..., :48].shape).astype(np.float32)
+    check(x, 16)
+
+
 @pytest.mark.parametrize("d,C,T", [(128, 16, 45), (64, 32, 70), (16, 64, 130)])
 def test_backward_bf16_storage(d, C, T):
     check(to_bf16(make(2, T, 2, d, seed=300 + d)), C)
