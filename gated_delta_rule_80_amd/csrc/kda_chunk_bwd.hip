@@ -221,6 +221,13 @@ __device__ __forceinline__ void solve_T(float *T, const float *Kt, const float *
     }
 }
 
+// One fp32 MFMA step, 16 x 16 x 4: lane l gives A[l % 16][l / 16] and
+// B[l / 16][l % 16]; accumulator element e is D[4 (l / 16) + e][l % 16].
+__device__ __forceinline__ float4v mfma4(float a, float b, float4v c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float4v as4v(float4 x) { return float4v{x.x, x.y, x.z, x.w}; }
+
 // ---- prep kernel ----------------------------------------------------------------
 struct PrepLds {
     int k, G, q, L, beta, Kt, T, Hm, total;
@@ -273,6 +280,52 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_prep_kernel(
     __syncthreads();
     cumsum_rows<C, THREADS>(sG, d, tid);
     __syncthreads();
+    bool products = false;   // K~ and H formed on MFMA
+    if constexpr (C == 16 && D == 128) {
+        // With row r = 7 of the cumulative decays as reference,
+        // e^{G_i - G_j} = e^{G_i - G_r} e^{G_r - G_j} in each channel, so
+        //   K~ = (k e^{G - G_r}) (k e^{G_r - G})^T,  H = s (q e^{G - G_r}) (k e^{G_r - G})^T
+        // are plain products over the channels (then masked to j < i and
+        // j <= i).  Every channel must decay by at most 40 over the chunk so
+        // that both factors stay within e^{+-40}; else the pairwise factors.
+        // Wave w takes channels 32w .. 32w+31, channel 32w + 4s + l/16 in step
+        // s from lane l (row l % 16 for both operands); the four waves' parts
+        // meet in L's storage, written only afterwards.
+        static_assert(THREADS == C * C, "one K~ and H entry per thread");
+        const int wide = tid < d && !(sG[tid] - sG[(C - 1) * dp + tid] <= 40.f);
+        if (!__syncthreads_or(wide)) {
+            products = true;
+            const int l = tid & 63, g4 = l >> 4, i16 = l & 15, w = tid >> 6;
+            float4v ak = {0.f, 0.f, 0.f, 0.f}, ah = ak;
+#pragma unroll
+            for (int s2 = 0; s2 < 8; ++s2) {
+                const int c2 = 32 * w + 4 * s2 + g4, a = i16 * dp + c2;
+                const float Gr = sG[7 * dp + c2], G = sG[a], kk = sk[a];
+                const float up = fast_exp(G - Gr), dn = kk * fast_exp(Gr - G);
+                ak = mfma4(kk * up, dn, ak);
+                ah = mfma4(sq[a] * up, dn, ah);
+            }
+            // accumulator element e: row i = 4 (l/16) + e, column j = l % 16
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sL[w * 2 * cc + (4 * g4 + e) * C + i16] = ak[e];
+                sL[w * 2 * cc + cc + (4 * g4 + e) * C + i16] = ah[e];
+            }
+            __syncthreads();
+            {
+                const int e = tid, i = e / C, j = e - i * C;   // THREADS == C * C
+                float a = 0.f, hh = 0.f;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    a += sL[u * 2 * cc + e];
+                    hh += sL[u * 2 * cc + cc + e];
+                }
+                sKt[e] = j < i ? a : 0.f;
+                sHm[e] = j <= i ? scale * hh : 0.f;
+            }
+            __syncthreads();
+        }
+    }
     for (int e = tid; e < cd; e += THREADS) {
         const int i = e / d, c2 = e - i * d, a = i * dp + c2;
         const float kk = sk[a], G = sG[a];
@@ -282,15 +335,33 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_prep_kernel(
         ws.Qb[wslot * cd + e] = scale * sq[a] * eG;
     }
     for (int c2 = tid; c2 < d; c2 += THREADS) ws.gC[wslot * d + c2] = fast_exp(sG[(C - 1) * dp + c2]);
-    pair_products<C>(sKt, sHm, sk, sq, sG, scale, d, tid);
+    if (!products) pair_products<C>(sKt, sHm, sk, sq, sG, scale, d, tid);
     __syncthreads();
     solve_T<C>(sT, sKt, sb, tid);
     __syncthreads();
-    for (int e = tid; e < cd; e += THREADS) {
-        const int i = e / d, c2 = e - i * d;
-        float r = 0.f;
-        for (int j = 0; j <= i; ++j) r += sT[i * C + j] * sb[j] * sL[j * dp + c2];
-        ws.R[wslot * cd + e] = r;
+    if constexpr (C == 16 && D == 128) {
+        // R = T Diag(beta) L on fp32 MFMA: wave w takes channel tiles 2w and
+        // 2w + 1, token 4s + l/16 in step s (T is zero above its diagonal).
+        const int l = tid & 63, g4 = l >> 4, i16 = l & 15, w = tid >> 6;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int c0 = 16 * (2 * w + t);
+            float4v r = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+                const int j = 4 * s2 + g4;
+                r = mfma4(sT[i16 * C + j] * sb[j], sL[j * dp + c0 + i16], r);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ws.R[wslot * cd + (4 * g4 + e) * d + c0 + i16] = r[e];
+        }
+    } else {
+        for (int e = tid; e < cd; e += THREADS) {
+            const int i = e / d, c2 = e - i * d;
+            float r = 0.f;
+            for (int j = 0; j <= i; ++j) r += sT[i * C + j] * sb[j] * sL[j * dp + c2];
+            ws.R[wslot * cd + e] = r;
+        }
     }
     for (int e = tid; e < cc; e += THREADS) {
         ws.T[wslot * cc + e] = sT[e];
@@ -565,10 +636,6 @@ template <typename In> struct RevOps {
     int len;
 };
 
-__device__ __forceinline__ float4v mfma4(float a, float b, float4v c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ float4v as4v(float4 x) { return float4v{x.x, x.y, x.z, x.w}; }
 
 template <typename In>
 __global__ __launch_bounds__(MT) void kda_bwd_chain_mfma_kernel(

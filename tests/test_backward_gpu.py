@@ -131,7 +131,9 @@ def test_backward_d128_pairwise_and_factored_decay_paths():
     row scalings; any other wave takes the pairwise factors.  Channels 0-47
     decay by 3-4 per token (spans of 45-60 over a full chunk), 48-127 weakly,
     so waves 0-2 take the pairwise factors and waves 3-7 the products,
-    except in the short last chunk."""
+    except in the short last chunk.  The prep kernel makes that choice for
+    all 128 channels of a chunk at once (K~ and H), so here it takes the
+    pairwise factors except in the last chunk."""
     x = make(1, 70, 2, 128, seed=210)
     rng = np.random.default_rng(211)
     x["g"][..., :48] = rng.uniform(-4.0, -3.0, size=x["g"][..., :48].shape).astype(np.float32)
