@@ -934,6 +934,7 @@ __global__ __launch_bounds__(GT) void kda_bwd_grad_kernel(
     const bool s_rebuild = HALF && (cix & 1);
     const bool ds_rebuild = HALF && !(cix & 1) && t0 + C < te;
 
+    float4 rS[8], rdS[8];   // rows of S and dS' (d = 128, C = 16)
     {
         const size_t off = ((size_t)t0 * H + h) * d, pitch = (size_t)H * d;
         Rows<GT> r[7];
@@ -952,6 +953,19 @@ __global__ __launch_bounds__(GT) void kda_bwd_grad_kernel(
             const int e = min(tid + u * GT, C * C - 1);
             rT[u] = ws.T[wslot * C * C + e];
             rK[u] = ws.Kt[wslot * C * C + e];
+        }
+        // Rows of S and dS' for the products below, issued after the inputs so
+        // that committing those waits for them alone.
+        if constexpr (C == 16 && D == 128) {
+            const int l = tid & 63, g4 = l >> 4, ch = 16 * (tid >> 6) + (l & 15);
+            const float *Sg = ws.S + (s_rebuild ? wslot - H : wslot) * dd;
+            const float *dSg = ws.dS + (ds_rebuild ? wslot + H : wslot) * dd;
+#pragma unroll
+            for (int T = 0; T < 8; ++T) {
+                const int u = 16 * T + 4 * g4;
+                rS[T] = *reinterpret_cast<const float4 *>(Sg + (size_t)ch * d + u);
+                rdS[T] = *reinterpret_cast<const float4 *>(dSg + (size_t)ch * d + u);
+            }
         }
         Rows<GT> rx, ry;
         if (s_rebuild) {
@@ -979,25 +993,17 @@ __global__ __launch_bounds__(GT) void kda_bwd_grad_kernel(
 
     // The products with S and dS':
     //   dR = -dZ S^T,  dQbar = dO S^T,  dKbar = Z dS'^T,  gc = e^{G_C} rowsum(dS' . S).
-    const float *Sg = ws.S + (s_rebuild ? wslot - H : wslot) * dd;
-    const float *dSg = ws.dS + (ds_rebuild ? wslot + H : wslot) * dd;
+    const float *Sg = ws.S + wslot * dd, *dSg = ws.dS + wslot * dd;
     // At d = 128, C = 16 (fp32 MFMA): wave w takes channels 16w .. 16w+15 (the
     // output columns), token rows are the output rows, and the value index u is
     // the reduction.  Instruction (T, s) takes u = 16T + 4 (l/16) + s from lane
-    // l: its rows 16w + l % 16 of S and dS' are float4 reads from global
-    // memory (32 values each), rows l % 16 of dZ, dO and Z come from LDS.
+    // l: its rows 16w + l % 16 of S and dS' are the float4 reads issued with
+    // the inputs (32 values each), rows l % 16 of dZ, dO and Z come from LDS.
     // dQbar and dKbar stay in accumulators until v and Z are dead.
     float4v aQ = {0.f, 0.f, 0.f, 0.f}, aK = aQ;
     if constexpr (C == 16 && D == 128) {
         const int l = tid & 63, g4 = l >> 4, i16 = l & 15, w = tid >> 6;
         const int ch = 16 * w + i16;
-        float4 rS[8], rdS[8];
-#pragma unroll
-        for (int T = 0; T < 8; ++T) {
-            const int u = 16 * T + 4 * g4;
-            rS[T] = *reinterpret_cast<const float4 *>(Sg + (size_t)ch * d + u);
-            rdS[T] = *reinterpret_cast<const float4 *>(dSg + (size_t)ch * d + u);
-        }
         // The rebuilt tile in the layout of rS: computed transposed, value
         // rows 16T + l % 16 (A, from LDS) by channels (B), token 4 (l/16) + s in
         // step s, so accumulator element e is value 16T + 4 (l/16) + e of
