@@ -602,8 +602,17 @@ __global__ __launch_bounds__(CT) void kda_bwd_chain_kernel(
 // Each wave forms the part of Z (dZ) over its own 32 channels; the four parts
 // meet in LDS (double-buffered, one barrier per chunk step).  The next chunk's
 // operands are loaded into registers during the current step.
-constexpr int MT = 256;   // MFMA chain kernel: one wave per SIMD
+constexpr int MT = 256;   // MFMA chain kernel: one compute wave per SIMD
+constexpr int MTP = MT + 64;   // and a prefetch wave
 constexpr int MC = 16, MD = 128;
+#ifndef KDA_BWD_PD
+#define KDA_BWD_PD 5
+#endif
+#ifndef KDA_BWD_PR
+#define KDA_BWD_PR 3
+#endif
+constexpr int BWD_PD = KDA_BWD_PD;   // prefetch distance in chunk steps
+constexpr int BWD_PR = KDA_BWD_PR;   // chunk steps between a touch and its wait
 
 // Token-row values are kept as loaded (bf16 bits or fp32) and widened where
 // they are used, so that nothing waits on the next chunk's loads early.
@@ -638,7 +647,7 @@ template <typename In> struct RevOps {
 
 
 template <typename In>
-__global__ __launch_bounds__(MT) void kda_bwd_chain_mfma_kernel(
+__global__ __launch_bounds__(MTP) void kda_bwd_chain_mfma_kernel(
     const In *__restrict__ v, const float *__restrict__ beta, int H, int row_len,
     const int32_t *__restrict__ cu, int n_pairs, const float *__restrict__ s0,
     const float *__restrict__ dfinal, const In *__restrict__ dout, float *__restrict__ ds0,
@@ -659,6 +668,61 @@ __global__ __launch_bounds__(MT) void kda_bwd_chain_mfma_kernel(
     const size_t pair = (size_t)pid;
     const int nck = (te - ts + C - 1) / C;
     const int base = chunk_base(ts, n, C);
+    if (w == 4) {
+        // Prefetch wave.  Step q of the 2 nck chunk steps (forward, then
+        // reverse) touches the operand lines of the step BWD_PD later: one
+        // 4-byte load per 128-byte line, every eighth line from this tile's
+        // offset, so the eight value tiles of a pair together bring each
+        // line into their XCD's L2 before the compute waves' register rings
+        // load it.  A touch is waited for BWD_PR steps after it was issued,
+        // and this wave meets the compute waves at their one barrier per
+        // step, so it never holds that barrier up on memory.
+        constexpr int RL = MD * (int)sizeof(In) / 128;   // lines per token row
+        static_assert(MD * sizeof(In) % 128 == 0 && (C * MD * 4) % 128 == 0, "whole lines");
+        auto line = [&](bool rev, int c, int li) -> const uint32_t * {
+            const size_t slot = (size_t)(base + c) * H + h;
+            const int t0 = ts + c * C, len = min(C, te - t0);
+            const int nb = rev ? 3 : 2, nl = 64 * nb + 4 + 8 + C * RL;
+            li = min(li, nl - 1);
+            if (li < 64 * nb) {
+                const float *blk = rev ? (li < 64 ? ws.Kb : li < 128 ? ws.Qb : ws.R)
+                                       : (li < 64 ? ws.R : ws.Kb);
+                return reinterpret_cast<const uint32_t *>(blk + slot * cd) + 32 * (li & 63);
+            }
+            li -= 64 * nb;
+            if (li < 4) return reinterpret_cast<const uint32_t *>(ws.gC + slot * d) + 32 * li;
+            li -= 4;
+            if (li < 8)
+                return reinterpret_cast<const uint32_t *>((rev ? ws.Hm : ws.T) + slot * C * C) +
+                       32 * li;
+            li -= 8;
+            const int row = min(li / RL, len - 1);
+            const In *src = (rev ? dout : v) + ((size_t)(t0 + row) * H + h) * d;
+            return reinterpret_cast<const uint32_t *>(src) + 32 * (li % RL);
+        };
+        uint32_t ring[BWD_PR];
+#pragma unroll
+        for (int j = 0; j < BWD_PR; ++j) ring[j] = 0u;
+        const int nq = 2 * nck;
+        auto touch = [&](int j, int q) {
+            const int p = q + BWD_PD;
+            const bool rev = p >= nck;
+            const int c = !rev ? p : max(nq - 1 - p, 0);
+            asm volatile("" ::"v"(ring[j]));
+            ring[j] = *line(rev, c, 8 * l + tile);
+            lds_barrier();
+        };
+        int q = 0;
+        for (; q + BWD_PR <= nq; q += BWD_PR)
+#pragma unroll
+            for (int j = 0; j < BWD_PR; ++j) touch(j, q + j);
+#pragma unroll
+        for (int j = 0; j < BWD_PR - 1; ++j)
+            if (q + j < nq) touch(j, q + j);
+#pragma unroll
+        for (int j = 0; j < BWD_PR; ++j) asm volatile("" ::"v"(ring[j]));
+        return;
+    }
     // This lane's state entries: rows 32w + 16cl + 4g4 + e, column v0 + i16.
     auto srow = [&](int cl, int e) { return 32 * w + 16 * cl + 4 * g4 + e; };
 
@@ -1401,7 +1465,7 @@ hipError_t launch_bwd_cdt(const ChunkBwdProblem &p, const bwd::Ws &ws, size_t sl
     const int64_t n_pairs = (int64_t)p.n_seqs * p.heads;
     const int64_t chain_blocks = (n_pairs + 7) / 8 * 8 * (D / TV);
     if (!launch_fits((int64_t)slots * p.heads, GT) ||
-        !launch_fits(chain_blocks, (C == MC && D == MD) ? MT : CT))
+        !launch_fits(chain_blocks, (C == MC && D == MD) ? MTP : CT))
         return hipErrorInvalidConfiguration;
     const dim3 per_chunk((unsigned)(slots * p.heads));
     hipLaunchKernelGGL((kda_bwd_prep_kernel<C, D, In>), per_chunk, dim3(THREADS), lp, p.stream, q,
@@ -1410,7 +1474,7 @@ hipError_t launch_bwd_cdt(const ChunkBwdProblem &p, const bwd::Ws &ws, size_t sl
     if (e != hipSuccess) return e;
     if constexpr (C == MC && D == MD) {
         hipLaunchKernelGGL((kda_bwd_chain_mfma_kernel<In>), dim3((unsigned)chain_blocks),
-                           dim3(MT), 0, p.stream, v, p.beta, p.heads, p.seqlen, p.cu, (int)n_pairs,
+                           dim3(MTP), 0, p.stream, v, p.beta, p.heads, p.seqlen, p.cu, (int)n_pairs,
                            p.s0, p.dfinal, dout, p.ds0, ws);
     } else {
         hipLaunchKernelGGL((kda_bwd_chain_kernel<C, D, In>), dim3((unsigned)chain_blocks),
