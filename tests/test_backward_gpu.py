@@ -147,3 +147,50 @@ def test_backward_bf16_storage(d, C, T):
 
 def test_backward_bf16_packed_sequences():
     check(to_bf16(make(1, 0, 2, 128, seed=305, lengths=[20, 0, 37])), 16)
+
+
+def test_backward_bench_workload_sampled_heads():
+    """The backward at the benchmark's size and launch shape: B = 1, H = 32,
+    T = 8192, d = 128, chunk 16, bf16 q, k, v and dO, log-decays U(-0.05, 0).
+    The chain kernel walks 512 chunks each way in the same 256 workgroups (its
+    prefetch wave included), and the gradient kernel rebuilds every other
+    state.  Heads are independent, so three of the 32 are compared in full
+    with the oracle's chunkwise backward (pinned to autograd of the
+    recurrence to 1e-10 in the CPU tests)."""
+    import gated_delta_rule_80_amd as K
+    T, H, d, C = 8192, 32, 128, 16
+    rng = np.random.default_rng(212)
+    shp = (1, T, H, d)
+    bf = lambda a: torch.from_numpy(a).to(torch.bfloat16)  # noqa: E731
+    q = rng.standard_normal(size=shp, dtype=np.float32)
+    k = rng.standard_normal(size=shp, dtype=np.float32)
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    x = dict(q=bf(q), k=bf(k), v=bf(rng.standard_normal(size=shp, dtype=np.float32)),
+             do=bf(rng.standard_normal(size=shp, dtype=np.float32)))
+    del q, k
+    g = (-0.05 * rng.random(size=shp, dtype=np.float32))
+    beta = (1.0 / (1.0 + np.exp(-rng.standard_normal(size=shp[:3])))).astype(np.float32)
+    s0 = (0.1 * rng.standard_normal(size=(1, H, d, d))).astype(np.float32)
+    dfin = rng.standard_normal(size=(1, H, d, d)).astype(np.float32)
+    got = K.chunk_bwd(x["q"].cuda(), x["k"].cuda(), x["v"].cuda(), torch.from_numpy(g).cuda(),
+                      torch.from_numpy(beta).cuda(), x["do"].cuda(),
+                      initial_state=torch.from_numpy(s0).cuda(),
+                      d_final_state=torch.from_numpy(dfin).cuda(), chunk_size=C)
+    torch.cuda.synchronize()
+    got = {n: t.cpu().numpy() for n, t in got.items()}
+    for hh in (0, 13, 31):
+        one = lambda a: a[0, :, hh:hh + 1].astype(np.float64)  # noqa: E731
+        ref = oracle.backward.chunkwise_grads(
+            one(x["q"].float().numpy()), one(x["k"].float().numpy()),
+            one(x["v"].float().numpy()), one(g), beta[0, :, hh:hh + 1].astype(np.float64),
+            1.0 / np.sqrt(d), C, one(x["do"].float().numpy()), s0[:, hh:hh + 1],
+            dfin[:, hh:hh + 1], [0, T])
+        errs = {n: rel_err(got[n][0, :, hh:hh + 1], ref[n]) for n in ("dq", "dk", "dv", "dg")}
+        errs["dbeta"] = rel_err(got["dbeta"][0, :, hh:hh + 1], ref["dbeta"])
+        errs["dinitial_state"] = rel_err(got["dinitial_state"][:, hh:hh + 1],
+                                         ref["dinitial_state"])
+        print("head %d backward errors: " % hh + "  ".join("%s %.2e" % kv for kv in errs.items()),
+              flush=True)
+        for name, e in errs.items():
+            assert np.isfinite(e) and e <= TOL, (hh, name, e)
