@@ -26,6 +26,17 @@
 // the gradient kernel runs one workgroup per (chunk, head), all in parallel.
 // fp32 on the vector ALUs, decay factors as e^{G_i - G_j} with exponents <= 0
 // (and e^{G_i}, e^{G_C - G_i} <= 1), so any finite log-decay is in range.
+//
+// At d = 128, C = 16 the contractions run on fp32 MFMA (16 x 16 x 4), so the
+// arithmetic stays fp32: the chain kernel keeps its state tiles in
+// accumulators and has a fifth wave that prefetches each chunk's operands
+// into L2 a few steps ahead; it stores S only at even chunks and dS' only at
+// odd chunks and the last one, and the gradient kernel rebuilds the other
+// with one chunk step from its neighbour's.  The decay-weighted sums of the
+// prep kernel (K~, H) and of the gradient kernel (P1-P4) become products
+// between row scalings, e^{G_i - G_j} = e^{G_i - G_r} e^{G_r - G_j}, where
+// every channel decays by at most 40 over the chunk (both factors then stay
+// within e^{+-40}); elsewhere the pairwise factors above are kept.
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
@@ -39,8 +50,9 @@ constexpr int TV = 16;         // value columns per chain workgroup
 
 // ---- workspace ------------------------------------------------------------------
 // Per (chunk slot, head), fp32, row-major, one region per quantity:
-//   S at the chunk start and dS' at the chunk end [d][d]; Z, dZ, R, Kbar,
-//   Qbar [C][d]; T, K~, H [C][C]; e^{G_C} [d].
+//   S at the chunk start and dS' at the chunk end [d][d] (at d = 128, C = 16
+//   only S of even and dS' of odd and last chunks are written); Z, dZ, R,
+//   Kbar, Qbar [C][d]; T, K~, H [C][C]; e^{G_C} [d].
 __host__ __device__ inline size_t n_slots(int64_t total_tokens, int n_seqs, int chunk) {
     return (size_t)(total_tokens / chunk + n_seqs + 1);
 }
