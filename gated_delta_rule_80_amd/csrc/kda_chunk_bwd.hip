@@ -1428,12 +1428,44 @@ __global__ __launch_bounds__(GT) void kda_bwd_grad_kernel(
     __syncthreads();
     // dG_C = gc + sum_x dKbar_x Kbar_x joins the last row; dg is the reverse
     // cumulative sum of dG over the valid rows (padding rows carry nothing).
-    for (int c2 = tid; c2 < d; c2 += GT) {
+    if constexpr (C == 16 && D == 128) {
+        // Four threads per channel, each over four rows: the sums of its rows
+        // (dG over the valid ones) meet in q's storage (q is dead after the
+        // barrier above), then each thread adds the rows below its own.
+        static_assert(GT == 4 * D, "four row quarters per channel");
+        const int c2 = tid & (D - 1), qd = tid >> 7, x0 = 4 * qd;
+        float sl = 0.f, sg = 0.f;
+#pragma unroll
+        for (int x = x0; x < x0 + 4; ++x) {
+            sl += sdL[x * dp + c2];
+            if (x < len) sg += sdG[x * dp + c2];
+        }
+        float *part = sq;   // [2][4][D] floats
+        static_assert(2 * 4 * D <= C * (D + 1), "room for the row-quarter sums");
+        part[qd * D + c2] = sl;
+        part[4 * D + qd * D + c2] = sg;
+        __syncthreads();
         float run = sgc[c2];
-        for (int x = 0; x < C; ++x) run += sdL[x * dp + c2];
-        for (int x = len - 1; x >= 0; --x) {
-            run += sdG[x * dp + c2];
-            dg[((size_t)(t0 + x) * H + h) * d + c2] = run;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            run += part[u * D + c2];
+            if (u > qd) run += part[4 * D + u * D + c2];
+        }
+#pragma unroll
+        for (int x = x0 + 3; x >= x0; --x) {
+            if (x < len) {
+                run += sdG[x * dp + c2];
+                dg[((size_t)(t0 + x) * H + h) * d + c2] = run;
+            }
+        }
+    } else {
+        for (int c2 = tid; c2 < d; c2 += GT) {
+            float run = sgc[c2];
+            for (int x = 0; x < C; ++x) run += sdL[x * dp + c2];
+            for (int x = len - 1; x >= 0; --x) {
+                run += sdG[x * dp + c2];
+                dg[((size_t)(t0 + x) * H + h) * d + c2] = run;
+            }
         }
     }
     for (int j = tid; j < len; j += GT) dbeta[(size_t)(t0 + j) * H + h] = sdb[j];
