@@ -149,9 +149,11 @@ def test_backward_bf16_packed_sequences():
     check(to_bf16(make(1, 0, 2, 128, seed=305, lengths=[20, 0, 37])), 16)
 
 
-def test_backward_bench_workload_sampled_heads():
+@pytest.mark.parametrize("storage", ["bf16", "f32"])
+def test_backward_bench_workload_sampled_heads(storage):
     """The backward at the benchmark's size and launch shape: B = 1, H = 32,
-    T = 8192, d = 128, chunk 16, bf16 q, k, v and dO, log-decays U(-0.05, 0).
+    T = 8192, d = 128, chunk 16, bf16 (as benchmarked) or fp32 q, k, v and dO,
+    log-decays U(-0.05, 0).
     The chain kernel walks 512 chunks each way in the same 256 workgroups (its
     prefetch wave included), and the gradient kernel rebuilds every other
     state.  Heads are independent, so three of the 32 are compared in full
@@ -161,7 +163,8 @@ def test_backward_bench_workload_sampled_heads():
     T, H, d, C = 8192, 32, 128, 16
     rng = np.random.default_rng(212)
     shp = (1, T, H, d)
-    bf = lambda a: torch.from_numpy(a).to(torch.bfloat16)  # noqa: E731
+    dt = torch.bfloat16 if storage == "bf16" else torch.float32
+    bf = lambda a: torch.from_numpy(a).to(dt)  # noqa: E731
     q = rng.standard_normal(size=shp, dtype=np.float32)
     k = rng.standard_normal(size=shp, dtype=np.float32)
     q /= np.linalg.norm(q, axis=-1, keepdims=True)
