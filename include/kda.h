@@ -391,12 +391,16 @@ kda_status kda_output_rmsnorm_gate(int64_t rows, int32_t d_v, kda_dtype dtype,
  * gradients ("Kimi Delta Attention: How It Works, Step by Step" motivates the
  * chunkwise form by training); this reverses the chunk algebra of
  * "Understanding Kimi Delta Attention", sections "The triangular system" and
- * "Putting the chunks together", step by step.  A chain kernel (one
- * workgroup per sequence, head and 16 value columns) walks the chunks forward
- * storing each chunk's start state and Z = U - R S, then in reverse carrying
- * dL/dS across chunk boundaries and storing each chunk's end-state gradient
- * and dZ; a second kernel (one workgroup per chunk and head) forms every
- * other gradient from one chunk's inputs and those stored quantities.
+ * "Putting the chunks together", step by step.  A first kernel (one
+ * workgroup per chunk and head) stores every per-chunk factor that does not
+ * depend on the values.  A chain kernel (one workgroup per sequence, head and
+ * 16 value columns) walks the chunks forward storing each chunk's start
+ * state and Z = U - R S, then in reverse carrying dL/dS across chunk
+ * boundaries and storing each chunk's end-state gradient and dZ (at d = 128
+ * only every other state and end-state gradient); a last kernel (one
+ * workgroup per chunk and head) forms every other gradient from one chunk's
+ * inputs and those stored quantities, rebuilding a state or gradient that
+ * was not stored with one chunk step from its neighbour's.
  *
  *   shape         as kda_chunk_fwd; dtype KDA_F32 or KDA_BF16 (the storage of
  *                 q, k, v and d_o), d_k = d_v = d with (d, chunk) in
@@ -411,9 +415,11 @@ kda_status kda_output_rmsnorm_gate(int64_t rows, int32_t d_v, kda_dtype dtype,
  *                 fp32 outputs with the layouts of q, k, v, g_log_decay, beta.
  *   d_initial_state [N, H, d_k, d_v] fp32 or NULL (not written).
  *   workspace     at least kda_chunk_bwd_workspace_bytes(shape) bytes,
- *                 256-byte aligned: per chunk slot and head, the chunk-start
- *                 state and end-state gradient (d x d) and Z, dZ (chunk x d),
- *                 fp32, with T_total / chunk + N + 1 slots.
+ *                 256-byte aligned: per chunk slot and head, fp32, the
+ *                 chunk-start state and end-state gradient (d x d); Z, dZ
+ *                 and the factors R, Kbar, Qbar (chunk x d); T, K~, H
+ *                 (chunk x chunk); e^{G_C} (d); with T_total / chunk + N + 1
+ *                 slots.  Its contents are scratch between calls.
  * Tensors 16-byte aligned (beta, dbeta, cu_seqlens 4-byte); outputs must not
  * alias inputs.  Log-decays must be finite.  Asynchronous on `stream`; the
  * library enqueues kernels only.
