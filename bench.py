@@ -510,9 +510,8 @@ def main():
                                    "bf16 q/k/v/d_o, fp32 gradients, log-decays U(-0.05, 0), "
                                    "through kda_chunk_bwd"},
             "roofline": {"bound": "hbm", "kernel": "kda_bwd_prep_kernel, kda_bwd_chain_mfma_kernel "
-                         "and kda_bwd_grad_kernel (fp32 MFMA for every contraction but T's "
-                         "forward substitution); the states stored at every other chunk "
-                         "boundary dominate the traffic",
+                         "and kda_bwd_grad_kernel (fp32 MFMA for every contraction); the "
+                         "states stored at every other chunk boundary dominate the traffic",
                          "achieved_hbm_gbs": round(bgbs, 2), "hbm_frac": round(bgbs / HBM_PEAK_GBS, 5),
                          "alg_bytes_per_launch": bbytes,
                          "traffic": measured_traffic("kda_chunk_bwd:T8192_H32_d128_C16")},
