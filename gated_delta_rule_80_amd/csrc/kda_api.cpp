@@ -81,10 +81,15 @@ kda_status check_shape(const kda_shape *s, int64_t *total_tokens) {
 
 // The workspace is sized for the packed-sequence chunk bound T/C + N, which
 // is never below the equal-rows count B * ceil(T/C); one size fits both.
+// For fp32 storage at d = 128 it is what the MFMA factors path needs, which
+// covers the gate layouts and input forms that take the other fp32 kernel
+// (that one needs none).
 size_t workspace_for(const kda_shape *s, int64_t total) {
     const bool bf16 = dtype_code(s->dtype) == KDA_BF16;
     if (kda::mfma_path_supported(s->d_k, s->d_v, s->chunk_size, bf16))
         return kda::mfma_workspace_bytes(total, s->num_seqs, s->num_heads, s->chunk_size);
+    if (kda::f32_mfma_applies(s->d_k, s->d_v, bf16, kda::Gate::PerChannel, kda::InputForm()))
+        return kda::f32_mfma_workspace_bytes(total, s->num_seqs, s->num_heads);
     return kda::f32_workspace_bytes(total, s->num_seqs, s->num_heads, s->chunk_size);
 }
 
@@ -162,7 +167,12 @@ kda_status chunk_fwd(kda::Gate gate, kda::InputForm form, const kda_shape *shape
     if (o && (o == q || o == k || o == v || (g && o == (const void *)g) ||
               o == (const void *)beta))
         return fail(KDA_ERR_INVALID_ARGUMENT, "o must not alias an input");
-    const size_t need = workspace_for(shape, total);
+    // fp32 at d = 128 takes the MFMA factors path for a per-channel gate and
+    // plain inputs, except without allocation: the other fp32 kernel needs
+    // no workspace, so the no-allocation entry point keeps every fp32 size.
+    const bool bf16 = dtype_code(shape->dtype) == KDA_BF16;
+    const bool mfma_f32 = !noalloc && kda::f32_mfma_applies(shape->d_k, shape->d_v, bf16, gate, form);
+    const size_t need = (bf16 || mfma_f32) ? workspace_for(shape, total) : 0;
     if (noalloc) {
         if (need > KDA_NOALLOC_SCRATCH_BYTES)
             return fail(KDA_ERR_WORKSPACE_TOO_SMALL,
@@ -212,7 +222,8 @@ kda_status chunk_fwd(kda::Gate gate, kda::InputForm form, const kda_shape *shape
 
     hipError_t e = kda::mfma_path_supported(p.dk, p.dv, p.chunk, p.bf16)
                        ? kda::launch_chunk_fwd_mfma(p)
-                       : kda::launch_chunk_fwd_f32(p);
+                       : mfma_f32 ? kda::launch_chunk_fwd_f32_mfma(p)
+                                  : kda::launch_chunk_fwd_f32(p);
     if (e != hipSuccess) return hip_fail(e, "chunk prefill launch");
     return KDA_OK;
 }

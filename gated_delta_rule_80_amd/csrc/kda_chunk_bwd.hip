@@ -968,6 +968,195 @@ __global__ __launch_bounds__(MTP) void kda_bwd_chain_mfma_kernel(
     }
 }
 
+// ---- fp32 prefill at d = 128 on the prep kernel's factors -------------------------
+// The forward pass of the same chunk algebra for fp32 storage at d = 128, with
+// 16-token chunks: the prep kernel above writes K~, T, H, R, Kbar, Qbar and
+// e^{G_C} per (chunk, head); this chain kernel then walks the chunks with the
+// state tile in MFMA accumulators, as the backward's forward sweep does, and
+// also forms the output:
+//   Z = U - R S,  O = Qbar S + H Z,  S <- Diag(e^{G_C}) S + Kbar^T Z.
+// Each wave adds its 32 channels' parts of R S and of Qbar S; the four parts
+// of both meet in one double-buffered LDS exchange per chunk.  Every wave
+// then adds H Z over the whole chunk (4 MFMAs) and stores one token row of
+// each lane group of O.  A fifth wave prefetches, as in the backward chain.
+struct FwdOutOps {
+    float4 r[2];     // R[i16][32w + 16cl + 4g4 .. +3]        (A of R S)
+    float4 qb[2];    // Qbar[i16][32w + 16cl + 4g4 .. +3]     (A of Qbar S)
+    float kb[2][4];  // Kbar[4g4 + s][32w + 16cl + i16]      (A of Kbar^T Z)
+    float4 gc[2];    // e^{G_C}[32w + 16cl + 4g4 .. +3]
+    float hm[4];     // H[i16][4g4 + s]                        (A of H Z)
+    float t;         // T[i16][4g4 + w]                        (A of T (beta V), step w)
+    float b;         // beta[4g4 + w]
+    float vr;        // V[4g4 + w][v0 + i16]
+    int len;
+};
+
+__global__ __launch_bounds__(MTP) void kda_fwd_f32_chain_kernel(
+    const float *__restrict__ v, const float *__restrict__ beta, int H, int row_len,
+    const int32_t *__restrict__ cu, int n_pairs, const float *__restrict__ s0,
+    float *__restrict__ o, float *__restrict__ s_final, Ws ws) {
+    constexpr int C = MC, d = MD, dd = MD * MD, cd = MC * MD;
+    __shared__ float4v sPart[2][2][4][64];   // [buffer][R S or Qbar S][wave][lane]
+
+    // Block id -> (pair, value tile) with the 8 tiles of a pair on one XCD.
+    const int bid = blockIdx.x, lane8 = bid & 7, rest = bid >> 3;
+    const int tile = rest & 7, pid = (rest >> 3) * 8 + lane8;
+    if (pid >= n_pairs) return;
+    const int n = pid / H, h = pid - n * H;
+    const int tid = threadIdx.x, l = tid & 63, g4 = l >> 4, i16 = l & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int v0 = tile * TV;
+    int ts, te;
+    seq_range(cu, row_len, n, ts, te);
+    const size_t pair = (size_t)pid;
+    const int nck = (te - ts + C - 1) / C;
+    const int base = chunk_base(ts, n, C);
+    if (w == 4) {
+        // Prefetch wave: one line in eight of chunk c + BWD_PD's operands at
+        // step c (R, Kbar, Qbar, e^{G_C}, T, H, the value rows), each tile of
+        // the pair taking a different eighth; a touch is waited for BWD_PR
+        // steps after it was issued.
+        constexpr int RL = MD * 4 / 128;   // lines per value row
+        constexpr int NL = 3 * 64 + 4 + 8 + 8 + C * RL;
+        auto line = [&](int c, int li) -> const uint32_t * {
+            const size_t slot = (size_t)(base + c) * H + h;
+            const int t0 = ts + c * C, len = min(C, te - t0);
+            li = min(li, NL - 1);
+            if (li < 192) {
+                const float *blk = li < 64 ? ws.R : li < 128 ? ws.Kb : ws.Qb;
+                return reinterpret_cast<const uint32_t *>(blk + slot * cd) + 32 * (li & 63);
+            }
+            li -= 192;
+            if (li < 4) return reinterpret_cast<const uint32_t *>(ws.gC + slot * d) + 32 * li;
+            li -= 4;
+            if (li < 16)
+                return reinterpret_cast<const uint32_t *>((li < 8 ? ws.T : ws.Hm) + slot * C * C) +
+                       32 * (li & 7);
+            li -= 16;
+            const int row = min(li / RL, len - 1);
+            return reinterpret_cast<const uint32_t *>(v + ((size_t)(t0 + row) * H + h) * d) +
+                   32 * (li % RL);
+        };
+        uint32_t ring[BWD_PR];
+#pragma unroll
+        for (int j = 0; j < BWD_PR; ++j) ring[j] = 0u;
+        auto touch = [&](int j, int c) {
+            asm volatile("" ::"v"(ring[j]));
+            ring[j] = *line(min(c + BWD_PD, nck - 1), 8 * l + tile);
+            lds_barrier();
+        };
+        int c = 0;
+        for (; c + BWD_PR <= nck; c += BWD_PR)
+#pragma unroll
+            for (int j = 0; j < BWD_PR; ++j) touch(j, c + j);
+#pragma unroll
+        for (int j = 0; j < BWD_PR - 1; ++j)
+            if (c + j < nck) touch(j, c + j);
+#pragma unroll
+        for (int j = 0; j < BWD_PR; ++j) asm volatile("" ::"v"(ring[j]));
+        return;
+    }
+    auto srow = [&](int cl, int e) { return 32 * w + 16 * cl + 4 * g4 + e; };
+    // Rows past the chunk's end are read at its last token (in bounds) and
+    // zeroed where they are used.
+    auto load = [&](int c, FwdOutOps &op) {
+        const size_t slot = (size_t)(base + c) * H + h;
+        const int t0 = ts + c * C, len = min(C, te - t0);
+        const float *R = ws.R + slot * cd, *Kb = ws.Kb + slot * cd, *Qb = ws.Qb + slot * cd;
+        const float *gC = ws.gC + slot * d, *Hm = ws.Hm + slot * C * C;
+#pragma unroll
+        for (int cl = 0; cl < 2; ++cl) {
+            op.r[cl] = *reinterpret_cast<const float4 *>(R + i16 * d + srow(cl, 0));
+            op.qb[cl] = *reinterpret_cast<const float4 *>(Qb + i16 * d + srow(cl, 0));
+            op.gc[cl] = *reinterpret_cast<const float4 *>(gC + srow(cl, 0));
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) op.kb[cl][s2] = Kb[(4 * g4 + s2) * d + 32 * w + 16 * cl + i16];
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) op.hm[s2] = Hm[i16 * C + 4 * g4 + s2];
+        op.t = ws.T[slot * C * C + i16 * C + 4 * g4 + w];
+        const size_t row = (size_t)(t0 + min(4 * g4 + w, len - 1)) * H + h;
+        op.b = beta[row];
+        op.vr = v[row * d + v0 + i16];
+        op.len = len;
+    };
+    auto pick = [&](const float4v &x) { return w == 0 ? x[0] : w == 1 ? x[1] : w == 2 ? x[2] : x[3]; };
+
+    float4v St[2];
+#pragma unroll
+    for (int cl = 0; cl < 2; ++cl)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            St[cl][e] = s0 ? s0[pair * dd + (size_t)srow(cl, e) * d + v0 + i16] : 0.f;
+
+    auto step = [&](int c, const FwdOutOps &op) {
+        // this wave's parts of -R S (plus step w of U) and of Qbar S
+        float4v p = {0.f, 0.f, 0.f, 0.f}, po = p;
+#pragma unroll
+        for (int cl = 0; cl < 2; ++cl) {
+            p = mfma4(op.r[cl].x, St[cl][0], p);
+            p = mfma4(op.r[cl].y, St[cl][1], p);
+            p = mfma4(op.r[cl].z, St[cl][2], p);
+            p = mfma4(op.r[cl].w, St[cl][3], p);
+            po = mfma4(op.qb[cl].x, St[cl][0], po);
+            po = mfma4(op.qb[cl].y, St[cl][1], po);
+            po = mfma4(op.qb[cl].z, St[cl][2], po);
+            po = mfma4(op.qb[cl].w, St[cl][3], po);
+        }
+        p = -p;
+        p = mfma4(op.t, 4 * g4 + w < op.len ? op.b * op.vr : 0.f, p);
+        const int b = c & 1;
+        sPart[b][0][w][l] = p;
+        sPart[b][1][w][l] = po;
+        lds_barrier();
+        float4v z = sPart[b][0][0][l], oz = sPart[b][1][0][l];
+#pragma unroll
+        for (int u = 1; u < 4; ++u) {
+            z += sPart[b][0][u][l];
+            oz += sPart[b][1][u][l];
+        }
+        // O = Qbar S + H Z, token rows 4g4 + e of this lane group
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) oz = mfma4(op.hm[s2], z[s2], oz);
+        if (4 * g4 + w < op.len)
+            o[((size_t)(ts + c * C + 4 * g4 + w) * H + h) * d + v0 + i16] = pick(oz);
+        // S <- Diag(e^{G_C}) S + Kbar^T Z on this wave's rows
+#pragma unroll
+        for (int cl = 0; cl < 2; ++cl) {
+            float4v a = St[cl] * as4v(op.gc[cl]);
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) a = mfma4(op.kb[cl][s2], z[s2], a);
+            St[cl] = a;
+        }
+    };
+    // A ring of three chunks' operands, refilled two chunks ahead; loads past
+    // the last chunk re-read it (in bounds, unused).
+    if (nck > 0) {
+        const int cl = nck - 1;
+        FwdOutOps A, B, D;
+        load(0, A);
+        load(min(1, cl), B);
+        int c = 0;
+        for (; c + 3 <= nck; c += 3) {
+            load(min(c + 2, cl), D);
+            step(c, A);
+            load(min(c + 3, cl), A);
+            step(c + 1, B);
+            load(min(c + 4, cl), B);
+            step(c + 2, D);
+        }
+        if (c < nck) step(c, A);
+        if (c + 1 < nck) step(c + 1, B);
+    }
+    if (s_final) {
+#pragma unroll
+        for (int cl = 0; cl < 2; ++cl)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                s_final[pair * dd + (size_t)srow(cl, e) * d + v0 + i16] = St[cl][e];
+    }
+}
+
 // ---- gradient kernel ------------------------------------------------------------
 __host__ __device__ inline int slice_rows(int d) { return d < 16 ? d : 16; }
 
@@ -1522,6 +1711,62 @@ bool bwd_supported(int dk, int dv, int chunk) {
     return (size_t)bwd::prep_layout(dk, chunk).total <= cap &&
            (size_t)bwd::chain_layout(dk, chunk).total <= cap &&
            (size_t)bwd::grad_layout(dk, chunk).total <= cap;
+}
+
+bool f32_mfma_applies(int dk, int dv, bool bf16, Gate gate, InputForm form) {
+    return !bf16 && dk == bwd::MD && dv == bwd::MD && gate == Gate::PerChannel &&
+           form.flags() == 0;
+}
+
+namespace bwd {
+// The fp32 prefill's workspace per (chunk slot, head): R, Kbar, Qbar [C][d];
+// T, K~, H [C][C]; e^{G_C} [d], as the prep kernel writes them.
+__host__ __device__ inline size_t fwd_floats_per_slot() {
+    return 3 * (size_t)MC * MD + 3 * (size_t)MC * MC + MD;
+}
+inline Ws fwd_ws_layout(float *base, size_t slots, int heads) {
+    const size_t n = slots * heads, cd = n * MC * MD, cc = n * MC * MC;
+    Ws w;
+    w.S = w.dS = w.Z = w.dZ = nullptr;   // the prep kernel writes none of these
+    w.R = base;
+    w.Kb = w.R + cd;
+    w.Qb = w.Kb + cd;
+    w.T = w.Qb + cd;
+    w.Kt = w.T + cc;
+    w.Hm = w.Kt + cc;
+    w.gC = w.Hm + cc;
+    return w;
+}
+}  // namespace bwd
+
+size_t f32_mfma_workspace_bytes(int64_t total_tokens, int64_t n_seqs, int heads) {
+    return bwd::n_slots(total_tokens, (int)n_seqs, bwd::MC) * heads * bwd::fwd_floats_per_slot() *
+           sizeof(float);
+}
+
+hipError_t launch_chunk_fwd_f32_mfma(const ChunkProblem &p) {
+    using namespace bwd;
+    const int64_t total = p.cu ? (int64_t)p.seqlen : (int64_t)p.n_seqs * p.seqlen;
+    const size_t slots = n_slots(total, p.n_seqs, MC);
+    const Ws ws = fwd_ws_layout(static_cast<float *>(p.workspace), slots, p.heads);
+    const size_t lp = (size_t)prep_layout(MD, MC).total * sizeof(float);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kda_bwd_prep_kernel<MC, MD, float>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lp);
+    if (e != hipSuccess) return e;
+    const int64_t n_pairs = (int64_t)p.n_seqs * p.heads;
+    const int64_t chain_blocks = (n_pairs + 7) / 8 * 8 * (MD / TV);
+    if (!launch_fits((int64_t)(slots * p.heads), THREADS) || !launch_fits(chain_blocks, MTP))
+        return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((kda_bwd_prep_kernel<MC, MD, float>), dim3((unsigned)(slots * p.heads)),
+                       dim3(THREADS), lp, p.stream, static_cast<const float *>(p.q),
+                       static_cast<const float *>(p.k), p.g, p.beta, p.scale, p.heads, p.seqlen,
+                       p.cu, p.n_seqs, ws);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kda_fwd_f32_chain_kernel, dim3((unsigned)chain_blocks), dim3(MTP), 0,
+                       p.stream, static_cast<const float *>(p.v), p.beta, p.heads, p.seqlen, p.cu,
+                       (int)n_pairs, p.s0, static_cast<float *>(p.o), p.s_final, ws);
+    return hipGetLastError();
 }
 
 size_t bwd_workspace_bytes(int64_t total_tokens, int n_seqs, int heads, int d, int chunk) {

@@ -4,7 +4,7 @@
 #include "kda_internal.hpp"
 
 struct StubRecord {
-    enum Kind { None, Decode, Output, PrefillMfma, PrefillF32, Backward } kind = None;
+    enum Kind { None, Decode, Output, PrefillMfma, PrefillF32, PrefillF32Mfma, Backward } kind = None;
     int n_pairs = 0, dk = 0, dv = 0, gate = -1, form_flags = 0;
     int64_t rows = 0;
     bool bf16 = false;

@@ -146,15 +146,32 @@ static void prefill_checks() {
                         nullptr, nullptr, dev(20), kda_chunk_fwd_workspace_bytes(&e),
                         nullptr) == KDA_OK);
 
-    // fp32 storage goes to the fp32 path, including d = 128 with 64-token chunks.
+    // fp32 storage goes to the fp32 path; at d = 128 with a per-channel gate and
+    // plain inputs to the MFMA factors path, which needs a workspace.
     kda_shape f = bf16_shape(1, 50, 2);
     f.dtype = KDA_F32;
     f.d_k = f.d_v = 32;
     f.chunk_size = 16;
+    CHECK(kda_chunk_fwd_workspace_bytes(&f) == 0);
     CHECK(fwd(f, nullptr, 0) == KDA_OK && g_stub.kind == StubRecord::PrefillF32);
     f.d_k = f.d_v = 128;
     f.chunk_size = 64;
-    CHECK(fwd(f, nullptr, 0) == KDA_OK && g_stub.kind == StubRecord::PrefillF32);
+    const size_t fneed = kda_chunk_fwd_workspace_bytes(&f);
+    CHECK(fneed > 0);
+    CHECK(fwd(f, nullptr, 0) == KDA_ERR_INVALID_ARGUMENT);
+    CHECK(fwd(f, dev(20), fneed - 1) == KDA_ERR_WORKSPACE_TOO_SMALL);
+    CHECK(fwd(f, dev(20), fneed) == KDA_OK && g_stub.kind == StubRecord::PrefillF32Mfma);
+    CHECK(g_stub.prefill.workspace == dev(20) && g_stub.prefill.chunk == 64);
+    // Other gate layouts and input forms at d = 128 keep the fp32 kernel.
+    CHECK(kda_chunk_fwd_scalar_gate(&f, dev(1), dev(2), dev(3), nullptr, devf(5), 1.f, nullptr,
+                                    nullptr, dev(7), nullptr, nullptr, 0, nullptr) == KDA_OK &&
+          g_stub.kind == StubRecord::PrefillF32);
+    {
+        kda_inputs_form lf = {KDA_GATE_PER_CHANNEL, 1, 0, 0, 0.f};
+        CHECK(kda_chunk_fwd_ex(&f, &lf, dev(1), dev(2), dev(3), devf(4), devf(5), 1.f, nullptr,
+                               nullptr, dev(7), nullptr, nullptr, 0, nullptr) == KDA_OK &&
+              g_stub.kind == StubRecord::PrefillF32);
+    }
 
     // Scalar gate: NULL g is "no gate"; the ex form descriptor.
     CHECK(kda_chunk_fwd_scalar_gate(&s, dev(1), dev(2), dev(3), nullptr, devf(5), 1.f, nullptr,
@@ -221,6 +238,10 @@ static void noalloc_checks() {
     CHECK(call(big, nullptr) == KDA_ERR_WORKSPACE_TOO_SMALL);
     CHECK(g_stub.kind == StubRecord::None);
     CHECK(std::strstr(kda_last_error(), "kda_chunk_fwd with a workspace") != nullptr);
+    // fp32 at d = 128 keeps the fp32 kernel here (no workspace), at any size.
+    kda_shape f = bf16_shape(1, 1 << 20, 32);
+    f.dtype = KDA_F32;
+    CHECK(call(f, nullptr) == KDA_OK && g_stub.kind == StubRecord::PrefillF32);
     // The usual validation still applies.
     CHECK(kda_chunk_fwd_noalloc(nullptr, dev(1), dev(2), dev(3), devf(4), devf(5), 0.1f, nullptr,
                                 nullptr, dev(7), nullptr, nullptr) == KDA_ERR_INVALID_ARGUMENT);
