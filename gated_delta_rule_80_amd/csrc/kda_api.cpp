@@ -168,11 +168,16 @@ kda_status chunk_fwd(kda::Gate gate, kda::InputForm form, const kda_shape *shape
               o == (const void *)beta))
         return fail(KDA_ERR_INVALID_ARGUMENT, "o must not alias an input");
     // fp32 at d = 128 takes the MFMA factors path for a per-channel gate and
-    // plain inputs, except without allocation: the other fp32 kernel needs
-    // no workspace, so the no-allocation entry point keeps every fp32 size.
+    // plain inputs.  Without allocation it does so while its workspace fits
+    // the library's buffer; beyond that the other fp32 kernel, which needs no
+    // workspace, keeps every fp32 size available.
     const bool bf16 = dtype_code(shape->dtype) == KDA_BF16;
-    const bool mfma_f32 = !noalloc && kda::f32_mfma_applies(shape->d_k, shape->d_v, bf16, gate, form);
-    const size_t need = (bf16 || mfma_f32) ? workspace_for(shape, total) : 0;
+    bool mfma_f32 = kda::f32_mfma_applies(shape->d_k, shape->d_v, bf16, gate, form);
+    size_t need = (bf16 || mfma_f32) ? workspace_for(shape, total) : 0;
+    if (noalloc && mfma_f32 && need > KDA_NOALLOC_SCRATCH_BYTES) {
+        mfma_f32 = false;
+        need = 0;
+    }
     if (noalloc) {
         if (need > KDA_NOALLOC_SCRATCH_BYTES)
             return fail(KDA_ERR_WORKSPACE_TOO_SMALL,

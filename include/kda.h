@@ -88,7 +88,11 @@ typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  * Built combinations (d_k, d_v, C, dtype):
  *   (128, 128, 64, KDA_BF16)  MFMA path (fp16 operands, fp32 accumulation)
  *   (d, d, C, KDA_F32) with d in {16, 32, 64, 128}, C in {16, 32, 64}: fp32
- *                             path (fp32 arithmetic throughout)
+ *                             path (fp32 arithmetic throughout).  At d = 128
+ *                             with a per-channel gate and plain inputs it
+ *                             forms the chunk factors and carries the state
+ *                             on fp32 MFMA in 16-token chunks whatever C is
+ *                             (C changes only the rounding order).
  * Everything else returns KDA_ERR_UNSUPPORTED.
  */
 typedef struct kda_shape {
@@ -168,7 +172,10 @@ const char *kda_last_error(void);
  * shape is invalid or unsupported (kda_chunk_fwd then reports why).  The
  * workspace holds the per-chunk WY factors between the intra-chunk and the
  * inter-chunk kernels, the chunk table of packed sequences, and one flag per
- * (chunk, head) for the overlapped order.
+ * (chunk, head) for the overlapped order.  With fp32 storage it is 0 below
+ * d = 128; at d = 128 it holds the fp32 chunk factors (27.5 KB per 16-token
+ * chunk slot and head), which the other gate layouts and input forms leave
+ * unused.
  */
 size_t kda_chunk_fwd_workspace_bytes(const kda_shape *shape);
 
@@ -257,7 +264,12 @@ kda_status kda_chunk_fwd(const kda_shape *shape, const void *q, const void *k,
  *     KDA_NOALLOC_SCRATCH_BYTES return KDA_ERR_WORKSPACE_TOO_SMALL before
  *     anything is enqueued; at d_k = d_v = 128 with bf16 storage the buffer
  *     holds about 4,300 (chunk, head) records (for example H = 32 heads over
- *     about 8,600 tokens).  The fp32 path needs no workspace.
+ *     about 8,600 tokens).  With fp32 storage at d = 128 a problem whose
+ *     factors fit (about 9,500 16-token chunk slots x heads) takes the same
+ *     path as kda_chunk_fwd; a larger one takes the fp32 kernel that needs no
+ *     workspace, whose results agree with kda_chunk_fwd's to within the fp32
+ *     tolerance rather than bit for bit.  Below d = 128 the fp32 path needs no
+ *     workspace.
  *   - The buffer belongs to the CURRENT device; `stream` must be a stream of
  *     that device (NULL = its null stream), else KDA_ERR_INVALID_ARGUMENT.
  *   - All calls on one device share the buffer, and it keeps the last call's
@@ -292,8 +304,10 @@ kda_status kda_chunk_fwd_noalloc(const kda_shape *shape, const void *q, const vo
  * to them ("Kimi Delta Attention: a half-life per channel", section "What
  * changes in the kernel"); the chunk chain is shared.  Its results agree with
  * kda_chunk_fwd fed g on every channel to within the bf16 tolerance, not bit
- * for bit.  With fp32 storage one kernel serves both gate layouts and the
- * results are bit for bit those of kda_chunk_fwd with g repeated.
+ * for bit.  With fp32 storage below d = 128 one kernel serves both gate
+ * layouts and the results are bit for bit those of kda_chunk_fwd with g
+ * repeated; at d = 128 kda_chunk_fwd takes the MFMA factors path and the two
+ * agree to within the fp32 tolerance.
  */
 kda_status kda_chunk_fwd_scalar_gate(const kda_shape *shape, const void *q,
                                      const void *k, const void *v,

@@ -238,9 +238,16 @@ static void noalloc_checks() {
     CHECK(call(big, nullptr) == KDA_ERR_WORKSPACE_TOO_SMALL);
     CHECK(g_stub.kind == StubRecord::None);
     CHECK(std::strstr(kda_last_error(), "kda_chunk_fwd with a workspace") != nullptr);
-    // fp32 at d = 128 keeps the fp32 kernel here (no workspace), at any size.
-    kda_shape f = bf16_shape(1, 1 << 20, 32);
+    // fp32 at d = 128: the MFMA factors path while its workspace fits the
+    // buffer, else the fp32 kernel (no workspace), so every size runs.
+    kda_shape f = bf16_shape(1, 2000, 8);
     f.dtype = KDA_F32;
+    CHECK(kda_chunk_fwd_workspace_bytes(&f) <= KDA_NOALLOC_SCRATCH_BYTES);
+    CHECK(call(f, nullptr) == KDA_OK && g_stub.kind == StubRecord::PrefillF32Mfma);
+    CHECK(g_stub.prefill.workspace == reinterpret_cast<void *>(0x7f0000000000ull));
+    f = bf16_shape(1, 1 << 20, 32);
+    f.dtype = KDA_F32;
+    CHECK(kda_chunk_fwd_workspace_bytes(&f) > KDA_NOALLOC_SCRATCH_BYTES);
     CHECK(call(f, nullptr) == KDA_OK && g_stub.kind == StubRecord::PrefillF32);
     // The usual validation still applies.
     CHECK(kda_chunk_fwd_noalloc(nullptr, dev(1), dev(2), dev(3), devf(4), devf(5), 0.1f, nullptr,

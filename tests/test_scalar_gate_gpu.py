@@ -74,7 +74,7 @@ def test_scalar_gate_packed_sequences():
     check(inp, gs, 64)
 
 
-@pytest.mark.parametrize("d,C", [(16, 16), (32, 32), (64, 64)])
+@pytest.mark.parametrize("d,C", [(16, 16), (32, 32), (64, 64), (128, 64)])
 def test_scalar_gate_fp32_path(d, C):
     inp, gs = inputs(d=d, dtype="f32", T=3 * C + 5)
     check(inp, gs, C)

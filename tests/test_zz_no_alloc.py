@@ -99,6 +99,9 @@ def test_noalloc_fp32_path_and_refusal_of_oversize_problems():
     L = K.lib()
     _check(W.make_prefill(H=2, dk=16, dv=16, dtype="f32", z_range=(2.0, 9.0), seed=93, B=1, T=77,
                           s0_std=0.05))
+    # fp32 at d = 128: the chunk factors fit the buffer, so the same MFMA path
+    _check(W.make_prefill(H=2, dk=128, dv=128, dtype="f32", z_range=(2.0, 9.0), seed=94,
+                          lengths=[150, 0, 33], s0_std=0.05))
     # 32 heads x 131072 tokens need about 4.7 GB of records: refused, nothing run
     sh = K.make_shape(1, 131072, 32, 128, 128, 64, 1, K.KDA_BF16)
     assert L.kda_chunk_fwd_workspace_bytes(ctypes.byref(sh)) > (256 << 20)
