@@ -42,6 +42,13 @@ def prefill_alg_bytes(T_total, H, dk, dv, n_seqs, has_s0=True):
     return T_total * H * per_th + state * (2 if has_s0 else 1)
 
 
+def prefill_f32_alg_bytes(T_total, H, dk, dv, n_seqs, has_s0=True):
+    """As prefill_alg_bytes with q, k, v and o stored in fp32."""
+    per_th = 4 * dk + 4 * dk + 4 * dv + 4 * dk + 4 + 4 * dv
+    state = n_seqs * H * dk * dv * 4
+    return T_total * H * per_th + state * (2 if has_s0 else 1)
+
+
 def scalar_gate_alg_bytes(T_total, H, dk, dv, n_seqs, has_s0=True):
     """As prefill_alg_bytes with one fp32 log-decay per (token, head)."""
     per_th = 2 * dk + 2 * dk + 2 * dv + 4 + 4 + 2 * dv
@@ -130,6 +137,7 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=32768)
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-small-prefill", action="store_true")
+    ap.add_argument("--skip-fp32-prefill", action="store_true")
     ap.add_argument("--skip-scalar-gate", action="store_true")
     ap.add_argument("--skip-varlen", action="store_true")
     ap.add_argument("--skip-backward", action="store_true")
@@ -281,6 +289,50 @@ def main():
                          "frac": round(pgbs / HBM_PEAK_GBS, 4), "alg_bytes_per_launch": pbytes,
                          "traffic": measured_traffic("kda_chunk_fwd:B2_T2048_H8")}}
         del d2, inp2, ws2, o2, fs2
+
+    if not args.skip_fp32_prefill:
+        # Workload 2's shape with fp32 storage, report only: the fp32 path at
+        # d = 128 (chunk factors and state chain on fp32 MFMA).
+        print("[bench] fp32 prefill: B=2 H=8 T=2048 d=128, fp32 storage", file=sys.stderr,
+              flush=True)
+        inpf = W.make_prefill(H=8, dk=128, dv=128, dtype="f32", z_range=(2.0, 9.0), seed=1002,
+                              B=2, T=2048, s0_std=0.01)
+        df = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inpf.items()}
+        Bf, Tf, Hf, dkf = df["q"].shape
+        wsf = torch.empty(K.workspace_bytes(Bf, Tf, Hf, dkf, dkf, 64, Bf, torch.float32),
+                          dtype=torch.uint8, device=dev)
+        of = torch.empty((Bf, Tf, Hf, dkf), dtype=torch.float32, device=dev)
+        fsf = torch.empty((Bf, Hf, dkf, dkf), dtype=torch.float32, device=dev)
+
+        def fstep():
+            K.chunk_fwd(df["q"], df["k"], df["v"], df["g"], df["beta"], scale=df["scale"],
+                        initial_state=df["initial_state"], chunk_size=64, workspace=wsf,
+                        out=of, final_state=fsf)
+
+        for _ in range(3):
+            fstep()
+        torch.cuda.synchronize()
+        n_f = 20
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n_f):
+            fstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        fms = e0.elapsed_time(e1) / n_f
+        fbytes = prefill_f32_alg_bytes(Bf * Tf, Hf, dkf, dkf, Bf)
+        fgbs = fbytes / (fms * 1e-3) / 1e9
+        result["fp32_prefill"] = {
+            "value": round(Bf * Tf / (fms * 1e-3), 1), "unit": "tokens/s",
+            "ms_per_step": round(fms, 4), "steps": n_f,
+            "config": {"workload": "prefill B=2 H=8 T=2048 d_k=d_v=128 C=64 fp32 storage, "
+                                   "S0~N(0,0.01^2) (report only)"},
+            "roofline": {"bound": "hbm", "kernel": "kda_bwd_prep_kernel (chunk factors) and "
+                         "kda_fwd_f32_chain_kernel, fp32 MFMA", "achieved": round(fgbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(fgbs / HBM_PEAK_GBS, 4), "alg_bytes_per_launch": fbytes,
+                         "traffic": measured_traffic("kda_chunk_fwd:f32_B2_T2048_H8")}}
+        del df, inpf, wsf, of, fsf
 
     if not args.skip_decode:
         w3 = W.WORKLOADS[3]

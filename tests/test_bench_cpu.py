@@ -33,6 +33,13 @@ def test_prefill_byte_model():
     assert bench.scalar_gate_alg_bytes(1, 1, 128, 128, 0) == 1540 - 512 + 4
 
 
+def test_fp32_prefill_byte_model():
+    # q, k, v, o in fp32 (512 B each at d = 128), g in fp32 (512 B), beta (4 B)
+    assert bench.prefill_f32_alg_bytes(1, 1, 128, 128, 0) == 5 * 512 + 4 == 2564
+    assert bench.prefill_f32_alg_bytes(4096, 8, 128, 128, 2) == \
+        4096 * 8 * 2564 + 2 * 2 * 8 * 128 * 128 * 4
+
+
 def test_prefill_flop_model():
     # 2 (5 C d + 3 d^2) = 180,224 FLOP per token-head at C = 64, d = 128
     assert bench.prefill_alg_flops(1, 1, 64, 128) == 180224
