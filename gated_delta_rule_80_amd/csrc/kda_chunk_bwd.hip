@@ -1,5 +1,6 @@
 // kda_chunk_bwd.hip -- gradients of the chunkwise KDA prefill in fp32, for
-// fp32 storage and d_k = d_v = d in {16, 32, 64, 128}.
+// fp32 storage and d_k = d_v = d in {16, 32, 64, 128}; and, sharing the prep
+// kernel's chunk factors, the fp32 prefill itself at d = 128 (near the end).
 //
 // The pages derive no gradients.  These kernels reverse the chunk algebra of
 // "Understanding Kimi Delta Attention" (A. Flores), sections "The triangular
