@@ -264,7 +264,9 @@ __host__ __device__ inline PrepLds prep_layout(int d, int C) {
 
 // One chunk of one head: K~, T, H, R = T Diag(beta) L, Kbar, Qbar and e^{G_C}
 // into the workspace (padding rows come out zero, T's padding block identity).
-template <int C, int D, typename In>
+// GL is the layout of g (Gate): per channel [T, H, d], one log-decay per
+// (token, head) [T, H] broadcast over the channels, or none (g unused).
+template <int C, int D, typename In, int GL = 0>
 __global__ __launch_bounds__(THREADS) void kda_bwd_prep_kernel(
     const In *__restrict__ q, const In *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, float scale, int H, int row_len,
@@ -283,7 +285,16 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_prep_kernel(
         const size_t off = ((size_t)t0 * H + h) * d, pitch = (size_t)H * d;
         Rows<THREADS> rk, rg, rq;
         fetch_rows(rk, k + off, pitch, C, len, d, tid);
-        fetch_rows(rg, g + off, pitch, C, len, d, tid);
+        if constexpr (GL == 0) {
+            fetch_rows(rg, g + off, pitch, C, len, d, tid);
+        } else {
+#pragma unroll
+            for (int u = 0; u < Rows<THREADS>::NV; ++u) {
+                const int i = 4 * (tid + u * THREADS) / d;
+                const float gi = (GL == 1 && i < C && i < len) ? g[(size_t)(t0 + i) * H + h] : 0.f;
+                rg.x[u] = make_float4(gi, gi, gi, gi);
+            }
+        }
         fetch_rows(rq, q + off, pitch, C, len, d, tid);
         const float rb = tid < len ? beta[(size_t)(t0 + tid) * H + h] : 0.f;
         commit_rows(sk, rk, C, d, tid);
@@ -1714,9 +1725,8 @@ bool bwd_supported(int dk, int dv, int chunk) {
            (size_t)bwd::grad_layout(dk, chunk).total <= cap;
 }
 
-bool f32_mfma_applies(int dk, int dv, bool bf16, Gate gate, InputForm form) {
-    return !bf16 && dk == bwd::MD && dv == bwd::MD && gate == Gate::PerChannel &&
-           form.flags() == 0;
+bool f32_mfma_applies(int dk, int dv, bool bf16, Gate, InputForm form) {
+    return !bf16 && dk == bwd::MD && dv == bwd::MD && form.flags() == 0;
 }
 
 namespace bwd {
@@ -1751,17 +1761,31 @@ hipError_t launch_chunk_fwd_f32_mfma(const ChunkProblem &p) {
     const size_t slots = n_slots(total, p.n_seqs, MC);
     const Ws ws = fwd_ws_layout(static_cast<float *>(p.workspace), slots, p.heads);
     const size_t lp = (size_t)prep_layout(MD, MC).total * sizeof(float);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kda_bwd_prep_kernel<MC, MD, float>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lp);
+    const void *prep = p.gate == Gate::PerChannel
+                           ? reinterpret_cast<const void *>(&kda_bwd_prep_kernel<MC, MD, float, 0>)
+                       : p.gate == Gate::Scalar
+                           ? reinterpret_cast<const void *>(&kda_bwd_prep_kernel<MC, MD, float, 1>)
+                           : reinterpret_cast<const void *>(&kda_bwd_prep_kernel<MC, MD, float, 2>);
+    hipError_t e = hipFuncSetAttribute(prep, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lp);
     if (e != hipSuccess) return e;
     const int64_t n_pairs = (int64_t)p.n_seqs * p.heads;
     const int64_t chain_blocks = (n_pairs + 7) / 8 * 8 * (MD / TV);
     if (!launch_fits((int64_t)(slots * p.heads), THREADS) || !launch_fits(chain_blocks, MTP))
         return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((kda_bwd_prep_kernel<MC, MD, float>), dim3((unsigned)(slots * p.heads)),
-                       dim3(THREADS), lp, p.stream, static_cast<const float *>(p.q),
-                       static_cast<const float *>(p.k), p.g, p.beta, p.scale, p.heads, p.seqlen,
-                       p.cu, p.n_seqs, ws);
+    const dim3 grid((unsigned)(slots * p.heads));
+    const float *q = static_cast<const float *>(p.q), *k = static_cast<const float *>(p.k);
+    if (p.gate == Gate::PerChannel)
+        hipLaunchKernelGGL((kda_bwd_prep_kernel<MC, MD, float, 0>), grid, dim3(THREADS), lp,
+                           p.stream, q, k, p.g, p.beta, p.scale, p.heads, p.seqlen, p.cu,
+                           p.n_seqs, ws);
+    else if (p.gate == Gate::Scalar)
+        hipLaunchKernelGGL((kda_bwd_prep_kernel<MC, MD, float, 1>), grid, dim3(THREADS), lp,
+                           p.stream, q, k, p.g, p.beta, p.scale, p.heads, p.seqlen, p.cu,
+                           p.n_seqs, ws);
+    else
+        hipLaunchKernelGGL((kda_bwd_prep_kernel<MC, MD, float, 2>), grid, dim3(THREADS), lp,
+                           p.stream, q, k, nullptr, p.beta, p.scale, p.heads, p.seqlen, p.cu,
+                           p.n_seqs, ws);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kda_fwd_f32_chain_kernel, dim3((unsigned)chain_blocks), dim3(MTP), 0,

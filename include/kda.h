@@ -89,7 +89,7 @@ typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  *   (128, 128, 64, KDA_BF16)  MFMA path (fp16 operands, fp32 accumulation)
  *   (d, d, C, KDA_F32) with d in {16, 32, 64, 128}, C in {16, 32, 64}: fp32
  *                             path (fp32 arithmetic throughout).  At d = 128
- *                             with a per-channel gate and plain inputs it
+ *                             with plain inputs (any gate layout) it
  *                             forms the chunk factors and carries the state
  *                             on fp32 MFMA in 16-token chunks whatever C is
  *                             (C changes only the rounding order).
@@ -174,7 +174,7 @@ const char *kda_last_error(void);
  * inter-chunk kernels, the chunk table of packed sequences, and one flag per
  * (chunk, head) for the overlapped order.  With fp32 storage it is 0 below
  * d = 128; at d = 128 it holds the fp32 chunk factors (27.5 KB per 16-token
- * chunk slot and head), which the other gate layouts and input forms leave
+ * chunk slot and head), which the input forms of kda_chunk_fwd_ex leave
  * unused.
  */
 size_t kda_chunk_fwd_workspace_bytes(const kda_shape *shape);
@@ -304,10 +304,8 @@ kda_status kda_chunk_fwd_noalloc(const kda_shape *shape, const void *q, const vo
  * to them ("Kimi Delta Attention: a half-life per channel", section "What
  * changes in the kernel"); the chunk chain is shared.  Its results agree with
  * kda_chunk_fwd fed g on every channel to within the bf16 tolerance, not bit
- * for bit.  With fp32 storage below d = 128 one kernel serves both gate
- * layouts and the results are bit for bit those of kda_chunk_fwd with g
- * repeated; at d = 128 kda_chunk_fwd takes the MFMA factors path and the two
- * agree to within the fp32 tolerance.
+ * for bit.  With fp32 storage one path serves both gate layouts and the
+ * results are bit for bit those of kda_chunk_fwd with g repeated.
  */
 kda_status kda_chunk_fwd_scalar_gate(const kda_shape *shape, const void *q,
                                      const void *k, const void *v,

@@ -64,8 +64,9 @@ def test_scalar_gate_prefill(T, B):
     check(inp, gs, 64)
 
 
-def test_no_gate_prefill_is_deltanet():
-    inp, _ = inputs(T=500)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_no_gate_prefill_is_deltanet(dtype):
+    inp, _ = inputs(T=500, dtype=dtype)
     check(inp, None, 64)
 
 
@@ -103,11 +104,13 @@ def test_scalar_gate_kernel_matches_the_per_channel_kernel_on_a_repeated_gate():
     assert rel_err(s1.double().cpu(), s2.double().cpu()) <= TOL["bf16"]
 
 
-def test_scalar_gate_fp32_equals_repeated_per_channel_gate_bitwise():
-    """fp32 storage: one kernel serves both gate layouts, so a scalar gate gives
-    exactly the bits of the per-channel entry point fed it on every channel."""
+@pytest.mark.parametrize("d", [32, 128])
+def test_scalar_gate_fp32_equals_repeated_per_channel_gate_bitwise(d):
+    """fp32 storage: one path serves both gate layouts (at d = 128 the MFMA
+    chunk factors, below it one VALU kernel), so a scalar gate gives exactly
+    the bits of the per-channel entry point fed it on every channel."""
     import gated_delta_rule_80_amd as K
-    inp, gs = inputs(d=32, dtype="f32", T=150, B=2)
+    inp, gs = inputs(d=d, dtype="f32", T=150, B=2)
     d = to_dev(inp)
     g_full = gs[..., None].expand_as(inp["g"]).contiguous().cuda()
     o1, s1 = K.chunk_fwd_scalar_gate(d["q"], d["k"], d["v"], gs.cuda(), d["beta"],
