@@ -81,9 +81,7 @@ kda_status check_shape(const kda_shape *s, int64_t *total_tokens) {
 
 // The workspace is sized for the packed-sequence chunk bound T/C + N, which
 // is never below the equal-rows count B * ceil(T/C); one size fits both.
-// For fp32 storage at d = 128 it is what the MFMA factors path needs, which
-// covers the input forms that take the other fp32 kernel (that one needs
-// none).
+// For fp32 storage at d = 128 it is what the MFMA factors path needs.
 size_t workspace_for(const kda_shape *s, int64_t total) {
     const bool bf16 = dtype_code(s->dtype) == KDA_BF16;
     if (kda::mfma_path_supported(s->d_k, s->d_v, s->chunk_size, bf16))
@@ -167,8 +165,8 @@ kda_status chunk_fwd(kda::Gate gate, kda::InputForm form, const kda_shape *shape
     if (o && (o == q || o == k || o == v || (g && o == (const void *)g) ||
               o == (const void *)beta))
         return fail(KDA_ERR_INVALID_ARGUMENT, "o must not alias an input");
-    // fp32 at d = 128 takes the MFMA factors path for plain inputs (any gate
-    // layout).  Without allocation it does so while its workspace fits
+    // fp32 at d = 128 takes the MFMA factors path (any gate layout and input
+    // form).  Without allocation it does so while its workspace fits
     // the library's buffer; beyond that the other fp32 kernel, which needs no
     // workspace, keeps every fp32 size available.
     const bool bf16 = dtype_code(shape->dtype) == KDA_BF16;

@@ -266,11 +266,14 @@ __host__ __device__ inline PrepLds prep_layout(int d, int C) {
 // into the workspace (padding rows come out zero, T's padding block identity).
 // GL is the layout of g (Gate): per channel [T, H, d], one log-decay per
 // (token, head) [T, H] broadcast over the channels, or none (g unused).
+// `form` (fp32 prefill only; 0 for the backward) applies the layer's input
+// steps as the rows are read: log a = log sigmoid(g), beta = sigmoid(beta)
+// and q, k divided by sqrt(sum of squares + eps), on the valid rows.
 template <int C, int D, typename In, int GL = 0>
 __global__ __launch_bounds__(THREADS) void kda_bwd_prep_kernel(
     const In *__restrict__ q, const In *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, float scale, int H, int row_len,
-    const int32_t *__restrict__ cu, int n_seqs, Ws ws) {
+    const int32_t *__restrict__ cu, int n_seqs, Ws ws, int form = 0, float eps = 0.f) {
     constexpr int d = D;
     extern __shared__ float sm[];
     const PrepLds L = prep_layout(d, C);
@@ -296,13 +299,36 @@ __global__ __launch_bounds__(THREADS) void kda_bwd_prep_kernel(
             }
         }
         fetch_rows(rq, q + off, pitch, C, len, d, tid);
-        const float rb = tid < len ? beta[(size_t)(t0 + tid) * H + h] : 0.f;
+        float rb = tid < len ? beta[(size_t)(t0 + tid) * H + h] : 0.f;
+        if (GL != 2 && (form & kFormGateLogit)) {
+#pragma unroll
+            for (int u = 0; u < Rows<THREADS>::NV; ++u)
+                if (4 * (tid + u * THREADS) / d < len) {
+                    float4 &x = rg.x[u];
+                    x = make_float4(log_sigmoid(x.x), log_sigmoid(x.y), log_sigmoid(x.z),
+                                    log_sigmoid(x.w));
+                }
+        }
+        if ((form & kFormBetaLogit) && tid < len) rb = sigmoid(rb);
         commit_rows(sk, rk, C, d, tid);
         commit_rows(sG, rg, C, d, tid);
         commit_rows(sq, rq, C, d, tid);
         if (tid < C) sb[tid] = rb;
     }
     __syncthreads();
+    if (form & kFormL2Norm) {
+        // one k or q row per THREADS / (2 C) lanes of a wave, reduced by shuffles
+        constexpr int LPR = THREADS / (2 * C);
+        static_assert(LPR <= 64 && 64 % LPR == 0 && D % LPR == 0, "a row within one wave");
+        const int x = tid / LPR, part = tid % LPR;
+        float *row = (x < C ? sk : sq) + (x % C) * dp;
+        float ss = 0.f;
+        for (int c2 = part; c2 < d; c2 += LPR) ss += row[c2] * row[c2];
+#pragma unroll
+        for (int m = LPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+        const float inv = 1.f / sqrtf(ss + eps);
+        for (int c2 = part; c2 < d; c2 += LPR) row[c2] *= inv;
+    }
     cumsum_rows<C, THREADS>(sG, d, tid);
     __syncthreads();
     bool products = false;   // K~ and H formed on MFMA
@@ -1006,7 +1032,7 @@ struct FwdOutOps {
 __global__ __launch_bounds__(MTP) void kda_fwd_f32_chain_kernel(
     const float *__restrict__ v, const float *__restrict__ beta, int H, int row_len,
     const int32_t *__restrict__ cu, int n_pairs, const float *__restrict__ s0,
-    float *__restrict__ o, float *__restrict__ s_final, Ws ws) {
+    float *__restrict__ o, float *__restrict__ s_final, Ws ws, int form) {
     constexpr int C = MC, d = MD, dd = MD * MD, cd = MC * MD;
     __shared__ float4v sPart[2][2][4][64];   // [buffer][R S or Qbar S][wave][lane]
 
@@ -1093,6 +1119,7 @@ __global__ __launch_bounds__(MTP) void kda_fwd_f32_chain_kernel(
         op.len = len;
     };
     auto pick = [&](const float4v &x) { return w == 0 ? x[0] : w == 1 ? x[1] : w == 2 ? x[2] : x[3]; };
+    const bool beta_logit = form & kFormBetaLogit;
 
     float4v St[2];
 #pragma unroll
@@ -1116,7 +1143,8 @@ __global__ __launch_bounds__(MTP) void kda_fwd_f32_chain_kernel(
             po = mfma4(op.qb[cl].w, St[cl][3], po);
         }
         p = -p;
-        p = mfma4(op.t, 4 * g4 + w < op.len ? op.b * op.vr : 0.f, p);
+        const float bw = beta_logit ? sigmoid(op.b) : op.b;
+        p = mfma4(op.t, 4 * g4 + w < op.len ? bw * op.vr : 0.f, p);
         const int b = c & 1;
         sPart[b][0][w][l] = p;
         sPart[b][1][w][l] = po;
@@ -1725,8 +1753,8 @@ bool bwd_supported(int dk, int dv, int chunk) {
            (size_t)bwd::grad_layout(dk, chunk).total <= cap;
 }
 
-bool f32_mfma_applies(int dk, int dv, bool bf16, Gate, InputForm form) {
-    return !bf16 && dk == bwd::MD && dv == bwd::MD && form.flags() == 0;
+bool f32_mfma_applies(int dk, int dv, bool bf16, Gate, InputForm) {
+    return !bf16 && dk == bwd::MD && dv == bwd::MD;
 }
 
 namespace bwd {
@@ -1774,23 +1802,25 @@ hipError_t launch_chunk_fwd_f32_mfma(const ChunkProblem &p) {
         return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)(slots * p.heads));
     const float *q = static_cast<const float *>(p.q), *k = static_cast<const float *>(p.k);
+    const int form = p.form.flags();
+    const float eps = p.form.eps;
     if (p.gate == Gate::PerChannel)
         hipLaunchKernelGGL((kda_bwd_prep_kernel<MC, MD, float, 0>), grid, dim3(THREADS), lp,
                            p.stream, q, k, p.g, p.beta, p.scale, p.heads, p.seqlen, p.cu,
-                           p.n_seqs, ws);
+                           p.n_seqs, ws, form, eps);
     else if (p.gate == Gate::Scalar)
         hipLaunchKernelGGL((kda_bwd_prep_kernel<MC, MD, float, 1>), grid, dim3(THREADS), lp,
                            p.stream, q, k, p.g, p.beta, p.scale, p.heads, p.seqlen, p.cu,
-                           p.n_seqs, ws);
+                           p.n_seqs, ws, form, eps);
     else
         hipLaunchKernelGGL((kda_bwd_prep_kernel<MC, MD, float, 2>), grid, dim3(THREADS), lp,
                            p.stream, q, k, nullptr, p.beta, p.scale, p.heads, p.seqlen, p.cu,
-                           p.n_seqs, ws);
+                           p.n_seqs, ws, form, eps);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kda_fwd_f32_chain_kernel, dim3((unsigned)chain_blocks), dim3(MTP), 0,
                        p.stream, static_cast<const float *>(p.v), p.beta, p.heads, p.seqlen, p.cu,
-                       (int)n_pairs, p.s0, static_cast<float *>(p.o), p.s_final, ws);
+                       (int)n_pairs, p.s0, static_cast<float *>(p.o), p.s_final, ws, form);
     return hipGetLastError();
 }
 
@@ -1824,7 +1854,7 @@ hipError_t launch_bwd_cdt(const ChunkBwdProblem &p, const bwd::Ws &ws, size_t sl
         return hipErrorInvalidConfiguration;
     const dim3 per_chunk((unsigned)(slots * p.heads));
     hipLaunchKernelGGL((kda_bwd_prep_kernel<C, D, In>), per_chunk, dim3(THREADS), lp, p.stream, q,
-                       k, p.g, p.beta, p.scale, p.heads, p.seqlen, p.cu, p.n_seqs, ws);
+                       k, p.g, p.beta, p.scale, p.heads, p.seqlen, p.cu, p.n_seqs, ws, 0, 0.f);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if constexpr (C == MC && D == MD) {

@@ -92,7 +92,7 @@ hipError_t launch_chunk_fwd_mfma(const ChunkProblem &p);
 bool f32_path_supported(int dk, int dv, int chunk, bool bf16);
 size_t f32_workspace_bytes(int64_t total_tokens, int64_t n_seqs, int heads, int chunk);
 hipError_t launch_chunk_fwd_f32(const ChunkProblem &p);
-// fp32 storage at d_k = d_v = 128 with plain inputs (any gate layout):
+// fp32 storage at d_k = d_v = 128 (any gate layout and input form):
 // 16-token chunks whatever p.chunk says (the chunk size changes only the
 // rounding order), the per-chunk factors on fp32 MFMA, then a chain kernel.
 bool f32_mfma_applies(int dk, int dv, bool bf16, Gate gate, InputForm form);

@@ -89,7 +89,7 @@ typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  *   (128, 128, 64, KDA_BF16)  MFMA path (fp16 operands, fp32 accumulation)
  *   (d, d, C, KDA_F32) with d in {16, 32, 64, 128}, C in {16, 32, 64}: fp32
  *                             path (fp32 arithmetic throughout).  At d = 128
- *                             with plain inputs (any gate layout) it
+ *                             (any gate layout and input form) it
  *                             forms the chunk factors and carries the state
  *                             on fp32 MFMA in 16-token chunks whatever C is
  *                             (C changes only the rounding order).
@@ -174,8 +174,7 @@ const char *kda_last_error(void);
  * inter-chunk kernels, the chunk table of packed sequences, and one flag per
  * (chunk, head) for the overlapped order.  With fp32 storage it is 0 below
  * d = 128; at d = 128 it holds the fp32 chunk factors (27.5 KB per 16-token
- * chunk slot and head), which the input forms of kda_chunk_fwd_ex leave
- * unused.
+ * chunk slot and head).
  */
 size_t kda_chunk_fwd_workspace_bytes(const kda_shape *shape);
 

@@ -101,8 +101,8 @@ hipError_t launch_chunk_fwd_f32(const ChunkProblem &p) {
     g_stub.prefill = p;
     return g_stub_status;
 }
-bool f32_mfma_applies(int dk, int dv, bool bf16, Gate, InputForm form) {
-    return !bf16 && dk == 128 && dv == 128 && form.flags() == 0;
+bool f32_mfma_applies(int dk, int dv, bool bf16, Gate, InputForm) {
+    return !bf16 && dk == 128 && dv == 128;
 }
 size_t f32_mfma_workspace_bytes(int64_t total_tokens, int64_t n_seqs, int heads) {
     return (size_t)(total_tokens / 16 + n_seqs + 1) * heads * 2048;

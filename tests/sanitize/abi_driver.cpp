@@ -146,8 +146,8 @@ static void prefill_checks() {
                         nullptr, nullptr, dev(20), kda_chunk_fwd_workspace_bytes(&e),
                         nullptr) == KDA_OK);
 
-    // fp32 storage goes to the fp32 path; at d = 128 with plain inputs to the
-    // MFMA factors path, which needs a workspace.
+    // fp32 storage goes to the fp32 path; at d = 128 to the MFMA factors path,
+    // which needs a workspace.
     kda_shape f = bf16_shape(1, 50, 2);
     f.dtype = KDA_F32;
     f.d_k = f.d_v = 32;
@@ -162,15 +162,15 @@ static void prefill_checks() {
     CHECK(fwd(f, dev(20), fneed - 1) == KDA_ERR_WORKSPACE_TOO_SMALL);
     CHECK(fwd(f, dev(20), fneed) == KDA_OK && g_stub.kind == StubRecord::PrefillF32Mfma);
     CHECK(g_stub.prefill.workspace == dev(20) && g_stub.prefill.chunk == 64);
-    // Any gate layout with plain inputs too; input forms keep the fp32 kernel.
+    // Every gate layout and input form too.
     CHECK(kda_chunk_fwd_scalar_gate(&f, dev(1), dev(2), dev(3), nullptr, devf(5), 1.f, nullptr,
                                     nullptr, dev(7), nullptr, dev(20), fneed, nullptr) == KDA_OK &&
           g_stub.kind == StubRecord::PrefillF32Mfma && g_stub.prefill.gate == kda::Gate::None);
     {
-        kda_inputs_form lf = {KDA_GATE_PER_CHANNEL, 1, 0, 0, 0.f};
+        kda_inputs_form lf = {KDA_GATE_PER_CHANNEL, 1, 1, 1, 1e-6f};
         CHECK(kda_chunk_fwd_ex(&f, &lf, dev(1), dev(2), dev(3), devf(4), devf(5), 1.f, nullptr,
-                               nullptr, dev(7), nullptr, nullptr, 0, nullptr) == KDA_OK &&
-              g_stub.kind == StubRecord::PrefillF32);
+                               nullptr, dev(7), nullptr, dev(20), fneed, nullptr) == KDA_OK &&
+              g_stub.kind == StubRecord::PrefillF32Mfma && g_stub.prefill.form.flags() == 7);
     }
 
     // Scalar gate: NULL g is "no gate"; the ex form descriptor.

@@ -75,21 +75,24 @@ def check(inp, gate, chunk, form):
                  label="form %s %s" % (gate, form))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("gate", ["per_channel", "scalar", "none"])
-def test_prefill_with_every_input_step(gate):
-    inp = raw_inputs(gate, T=300, B=2)
+def test_prefill_with_every_input_step(gate, dtype):
+    inp = raw_inputs(gate, T=300, B=2, dtype=dtype)
     form = dict(ALL)
     if gate == "none":
         form.pop("gate_is_logit")
     check(inp, gate, 64, form)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("gate", ["per_channel", "scalar"])
-def test_logit_gate_down_to_minus_50(gate):
+def test_logit_gate_down_to_minus_50(gate, dtype):
     """Decay logits anywhere in [-50, 9]: log sigmoid(x) is about x below -10,
-    where the MFMA path floors the log-decay at -10; outputs stay finite and
-    within the tolerance of the exact recurrence on the same logits."""
-    inp = raw_inputs(gate, T=260, B=1, seed=43)
+    where the bf16 MFMA path floors the log-decay at -10 and the fp32 path
+    keeps the exact factors; outputs stay finite and within the tolerance of
+    the exact recurrence on the same logits."""
+    inp = raw_inputs(gate, T=260, B=1, seed=43, dtype=dtype)
     rng = np.random.default_rng([43, 78])
     inp["g"] = torch.from_numpy(rng.uniform(-50.0, 9.0, size=inp["g"].shape).astype(np.float32))
     check(inp, gate, 64, dict(ALL))
@@ -110,20 +113,22 @@ def test_prefill_one_step_at_a_time(form):
     check(inp, "per_channel", 64, form)
 
 
-def test_prefill_forms_packed_sequences():
-    inp = raw_inputs("scalar", H=3, lengths=[0, 65, 1, 300, 129])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_forms_packed_sequences(dtype):
+    inp = raw_inputs("scalar", H=3, lengths=[0, 65, 1, 300, 129], dtype=dtype)
     check(inp, "scalar", 64, ALL)
 
 
-@pytest.mark.parametrize("d,C", [(16, 16), (32, 32), (64, 64)])
+@pytest.mark.parametrize("d,C", [(16, 16), (32, 32), (64, 64), (128, 64)])
 def test_prefill_forms_fp32_path(d, C):
     inp = raw_inputs("per_channel", d=d, dtype="f32", T=3 * C + 7)
     check(inp, "per_channel", C, ALL)
 
 
-def test_plain_form_is_the_plain_entry_point_bitwise():
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_plain_form_is_the_plain_entry_point_bitwise(dtype):
     import gated_delta_rule_80_amd as K
-    inp = W.make_prefill(H=2, dk=128, dv=128, dtype="bf16", z_range=(2.0, 9.0), seed=43, B=2,
+    inp = W.make_prefill(H=2, dk=128, dv=128, dtype=dtype, z_range=(2.0, 9.0), seed=43, B=2,
                          T=500, s0_std=0.05)
     d = {k_: (v_.cuda() if isinstance(v_, torch.Tensor) else v_) for k_, v_ in inp.items()}
     o1, s1 = K.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"],
