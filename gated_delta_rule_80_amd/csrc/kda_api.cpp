@@ -419,7 +419,8 @@ kda_status kda_output_rmsnorm_gate(int64_t rows, int32_t d_v, kda_dtype dtype, c
 
 size_t kda_chunk_bwd_workspace_bytes(const kda_shape *shape) {
     if (!shape || shape->batch <= 0 || shape->seqlen < 0 || shape->num_heads <= 0 ||
-        shape->d_k <= 0 || shape->chunk_size <= 0 || shape->num_seqs <= 0)
+        shape->d_k <= 0 || shape->chunk_size <= 0 || shape->num_seqs <= 0 ||
+        !kda::bwd_supported(shape->d_k, shape->d_v, shape->chunk_size))
         return 0;
     const int64_t total = (int64_t)shape->batch * shape->seqlen;
     return kda::bwd_workspace_bytes(total, shape->num_seqs, shape->num_heads, shape->d_k,

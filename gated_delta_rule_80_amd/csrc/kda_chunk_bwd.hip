@@ -1743,9 +1743,19 @@ __global__ __launch_bounds__(GT) void kda_bwd_grad_kernel(
 
 }  // namespace bwd
 
-bool bwd_supported(int dk, int dv, int chunk) {
+namespace {
+// The chunk the backward runs for a requested one.  At d = 128 it is always
+// 16 tokens (the fp32 MFMA kernels): the chunkwise form is exact for any
+// chunk, so the requested size changes only the rounding order.
+int bwd_run_chunk(int d, int chunk) {
+    return d == bwd::MD && (chunk == 16 || chunk == 32 || chunk == 64) ? bwd::MC : chunk;
+}
+}  // namespace
+
+bool bwd_supported(int dk, int dv, int chunk_requested) {
     if (dk != dv || !(dk == 16 || dk == 32 || dk == 64 || dk == 128)) return false;
-    if (!(chunk == 16 || chunk == 32 || chunk == 64)) return false;
+    if (!(chunk_requested == 16 || chunk_requested == 32 || chunk_requested == 64)) return false;
+    const int chunk = bwd_run_chunk(dk, chunk_requested);
     if (chunk * dk > bwd::MAX_BLOCK) return false;   // one fetched block per [C][d] operand
     const size_t cap = 163840 / sizeof(float);
     return (size_t)bwd::prep_layout(dk, chunk).total <= cap &&
@@ -1824,7 +1834,9 @@ hipError_t launch_chunk_fwd_f32_mfma(const ChunkProblem &p) {
     return hipGetLastError();
 }
 
-size_t bwd_workspace_bytes(int64_t total_tokens, int n_seqs, int heads, int d, int chunk) {
+size_t bwd_workspace_bytes(int64_t total_tokens, int n_seqs, int heads, int d,
+                           int chunk_requested) {
+    const int chunk = bwd_run_chunk(d, chunk_requested);
     const size_t slots = bwd::n_slots(total_tokens, n_seqs, chunk);
     return slots * heads * bwd::ws_floats_per_slot(d, chunk) * sizeof(float);
 }
@@ -1882,10 +1894,11 @@ hipError_t launch_bwd_cd(const ChunkBwdProblem &p, const bwd::Ws &ws, size_t slo
 
 hipError_t launch_chunk_bwd(const ChunkBwdProblem &p) {
     const int64_t total = p.cu ? (int64_t)p.seqlen : (int64_t)p.n_seqs * p.seqlen;
-    const size_t slots = bwd::n_slots(total, p.n_seqs, p.chunk);
-    const bwd::Ws ws = bwd::ws_layout(p.work, slots, p.heads, p.d, p.chunk);
-    // The (d, chunk) pairs bwd_supported accepts.
-    switch (p.d * 1000 + p.chunk) {
+    const int chunk = bwd_run_chunk(p.d, p.chunk);
+    const size_t slots = bwd::n_slots(total, p.n_seqs, chunk);
+    const bwd::Ws ws = bwd::ws_layout(p.work, slots, p.heads, p.d, chunk);
+    // The (d, chunk) pairs bwd_supported accepts, as they run.
+    switch (p.d * 1000 + chunk) {
     case 16016: return launch_bwd_cd<16, 16>(p, ws, slots);
     case 16032: return launch_bwd_cd<32, 16>(p, ws, slots);
     case 16064: return launch_bwd_cd<64, 16>(p, ws, slots);

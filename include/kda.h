@@ -415,7 +415,10 @@ kda_status kda_output_rmsnorm_gate(int64_t rows, int32_t d_v, kda_dtype dtype,
  *
  *   shape         as kda_chunk_fwd; dtype KDA_F32 or KDA_BF16 (the storage of
  *                 q, k, v and d_o), d_k = d_v = d with (d, chunk) in
- *                 {(16, 16|32|64), (32, 16|32), (64, 16|32), (128, 16)}.
+ *                 {(16, 16|32|64), (32, 16|32), (64, 16|32), (128, 16|32|64)};
+ *                 at d = 128 the gradients are formed over 16-token chunks
+ *                 whatever the chunk (the chunkwise form is exact for any
+ *                 chunk, so it changes only the rounding order).
  *   q, k, g_log_decay, v, beta, scale, initial_state, cu_seqlens
  *                 the forward's inputs, same layouts (initial_state may be NULL).
  *   d_o           [B, T, H, d_v], dtype as v: dL/do.
@@ -425,8 +428,9 @@ kda_status kda_output_rmsnorm_gate(int64_t rows, int32_t d_v, kda_dtype dtype,
  *   dq, dk, dv, dg, dbeta
  *                 fp32 outputs with the layouts of q, k, v, g_log_decay, beta.
  *   d_initial_state [N, H, d_k, d_v] fp32 or NULL (not written).
- *   workspace     at least kda_chunk_bwd_workspace_bytes(shape) bytes,
- *                 256-byte aligned: per chunk slot and head, fp32, the
+ *   workspace     at least kda_chunk_bwd_workspace_bytes(shape) bytes (0 for
+ *                 an invalid or unsupported shape), 256-byte aligned: per
+ *                 chunk slot and head (16-token slots at d = 128), fp32, the
  *                 chunk-start state and end-state gradient (d x d); Z, dZ
  *                 and the factors R, Kbar, Qbar (chunk x d); T, K~, H
  *                 (chunk x chunk); e^{G_C} (d); with T_total / chunk + N + 1

@@ -118,7 +118,7 @@ bool bwd_supported(int dk, int dv, int chunk) {
     if (dk != dv) return false;
     if (dk == 16) return chunk == 16 || chunk == 32 || chunk == 64;
     if (dk == 32 || dk == 64) return chunk == 16 || chunk == 32;
-    return dk == 128 && chunk == 16;
+    return dk == 128 && (chunk == 16 || chunk == 32 || chunk == 64);
 }
 size_t bwd_workspace_bytes(int64_t total_tokens, int n_seqs, int heads, int d, int chunk) {
     return (size_t)(total_tokens / chunk + n_seqs + 1) * heads * d * 8;

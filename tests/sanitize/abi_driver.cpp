@@ -317,7 +317,9 @@ static void backward_checks() {
     CHECK(bwd(s, dev(20), need, devf(1)) == KDA_ERR_INVALID_ARGUMENT);   // dq aliases q
     CHECK(bwd(s, nullptr, need, devf(10)) == KDA_ERR_INVALID_ARGUMENT);
     kda_shape u = s;
-    u.chunk_size = 64;
+    u.chunk_size = 64;   // at d = 128 run as 16-token chunks by the backend
+    CHECK(bwd(u, dev(20), need, devf(10)) == KDA_OK && g_stub.bwd.chunk == 64);
+    u.chunk_size = 48;
     CHECK(bwd(u, dev(20), need, devf(10)) == KDA_ERR_UNSUPPORTED);
     CHECK(c_bwd_with_dtype(&s, 9) == KDA_ERR_UNSUPPORTED);
     CHECK(kda_chunk_bwd(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0.f, nullptr,

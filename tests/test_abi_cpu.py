@@ -196,11 +196,19 @@ def call_bwd(sh, **kw):
                              args["db"], args["ds0"], args["ws"], args["wsb"], None)
 
 
+def test_backward_workspace_at_d128_is_that_of_16_token_chunks():
+    """At d = 128 the backward runs 16-token chunks for a requested 16, 32 or
+    64, so the workspace it asks for is the same."""
+    sizes = {C: K.workspace_bytes_bwd(1, 4096, 8, 128, C, 1) for C in (16, 32, 64)}
+    assert sizes[16] > 0 and sizes[16] == sizes[32] == sizes[64]
+    assert K.workspace_bytes_bwd(1, 4096, 8, 128, 48, 1) == 0
+
+
 def test_backward_rejects_unsupported_problems():
     f32 = dict(d_k=32, d_v=32, chunk_size=32, dtype_code=K.KDA_F32, seqlen=64, heads=2)
     assert call_bwd(shape(**dict(f32, dtype_code=5))) == 2                # unknown dtype
-    assert call_bwd(shape(**dict(f32, d_k=128, d_v=128))) == 2          # d = 128 needs chunk 16
-    assert call_bwd(shape(**dict(f32, d_k=128, d_v=128, chunk_size=64))) == 2
+    assert call_bwd(shape(**dict(f32, d_k=128, d_v=128, chunk_size=48))) == 2   # not 16/32/64
+    assert call_bwd(shape(**dict(f32, d_k=128, d_v=128, chunk_size=8))) == 2
     assert call_bwd(shape(**dict(f32, d_k=96, d_v=96, chunk_size=16))) == 2
     assert call_bwd(shape(**dict(f32, d_k=64, d_v=32, chunk_size=16))) == 2
     assert call_bwd(shape(**dict(f32, chunk_size=64))) == 2

@@ -125,6 +125,24 @@ def test_backward_d128_rebuilt_states_along_long_sequences():
     check(to_bf16(make(1, 0, 2, 128, seed=209, lengths=[17, 15, 160])), 16)
 
 
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_backward_d128_requested_chunks_run_as_16_token_chunks(chunk):
+    """At d = 128 a requested chunk of 32 or 64 tokens (the forward's) gives
+    the gradients of the 16-token computation, bit for bit, and so within the
+    tolerance of the oracle."""
+    import gated_delta_rule_80_amd as K
+    x = make(1, 0, 2, 128, seed=213, lengths=[150, 0, 47])
+    check(dict(x), chunk)
+    dev = {n: (torch.from_numpy(a).cuda() if a is not None else None) for n, a in x.items()}
+    run = lambda c: K.chunk_bwd(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], dev["do"],  # noqa: E731
+                                initial_state=dev["s0"], cu_seqlens=dev["cu"],
+                                d_final_state=dev["dfin"], chunk_size=c)
+    a, b = run(16), run(chunk)
+    torch.cuda.synchronize()
+    for name in a:
+        assert torch.equal(a[name], b[name]), name
+
+
 def test_backward_d128_pairwise_and_factored_decay_paths():
     """At d = 128, chunk 16, a wave whose 16 channels all decay by at most 40
     over a chunk forms the decay-weighted sums as matrix products between
