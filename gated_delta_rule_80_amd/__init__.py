@@ -436,7 +436,8 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     an initial state is given, dinitial_state.  q, k, v and d_o in fp32 or
     bf16 (one dtype), g, beta and the states fp32; the gradients are fp32.
     d_k = d_v = d with (d, chunk_size) in {(16, 16|32|64), (32, 16|32),
-    (64, 16|32), (128, 16)}."""
+    (64, 16|32), (128, 16|32|64)}; at d = 128 the gradients are formed over
+    16-token chunks whatever chunk_size is (it changes only the rounding)."""
     _need(q.dim() == 4 and k.shape == q.shape and v.shape == q.shape and g.shape == q.shape,
           "q, k, v, g must be [B, T, H, d] (d_k = d_v)")
     B, T, H, d = q.shape
