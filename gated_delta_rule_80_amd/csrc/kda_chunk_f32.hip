@@ -7,7 +7,10 @@
 // sections "The triangular system" and "Putting the chunks together", with
 // A = -A_page so that (I + A) T = I), evaluated entirely in fp32 on the vector
 // ALUs with every chunk operand resident in LDS.  This is the path whose
-// accuracy budget is 1e-4; its speed is not a target.  One workgroup handles
+// accuracy budget is 1e-4; its speed is not a target.  At d = 128 it serves
+// only the no-allocation entry point on problems whose fp32 MFMA factors
+// would not fit its buffer (it needs no workspace); every other fp32 call at
+// d = 128 takes the MFMA path in kda_chunk_bwd.hip.  One workgroup handles
 // one (sequence, head, value tile) and walks its chunks in order with its
 // columns of the state in LDS.  Value columns evolve independently, so the
 // tiles need no communication; each recomputes the value-independent chunk
